@@ -1,0 +1,149 @@
+"""Seeded synthetic inputs for the attention op and its KV-cache companion.
+
+This module only draws numbers and names shapes. It holds none of the
+attention arithmetic, so both sides of a parity check (the CPU oracle and
+the HIP library) can take their inputs from here without sharing any of
+the method.
+
+Recipe: every tensor is drawn from its own stream,
+``numpy.random.default_rng(SeedSequence([seed, tensor_id]))``, as float32
+standard normal values times a standard deviation. Stream ids: q = 0, k = 1,
+v = 2, bias = 3, bias mask = 4. A bias mask sets an entry to -1e9 with the
+stated probability, which is how the op catalogue says to mask a score with
+its bias input (graph protocol op catalogue, `attention` inputs).
+
+The pages name no dataset; these Gaussian tensors stand in for activations.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+STREAM_Q, STREAM_K, STREAM_V, STREAM_BIAS, STREAM_BIAS_MASK = 0, 1, 2, 3, 4
+MASK_VALUE = -1e9
+
+
+def rng(seed: int, stream: int) -> np.random.Generator:
+    return np.random.default_rng(np.random.SeedSequence([int(seed), int(stream)]))
+
+
+def normal(shape, seed: int, stream: int, std: float = 1.0) -> np.ndarray:
+    """float32 i.i.d. N(0, std^2) of the given shape."""
+    x = rng(seed, stream).standard_normal(size=shape, dtype=np.float32)
+    if std != 1.0:
+        x *= np.float32(std)
+    return np.ascontiguousarray(x, dtype=np.float32)
+
+
+def masked_bias(shape, seed: int, mask_prob: float, std: float = 1.0) -> np.ndarray:
+    """N(0, std^2) bias with each entry set to -1e9 with probability mask_prob."""
+    b = normal(shape, seed, STREAM_BIAS, std)
+    if mask_prob > 0.0:
+        drop = rng(seed, STREAM_BIAS_MASK).random(size=shape) < mask_prob
+        b[drop] = np.float32(MASK_VALUE)
+    return b
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """One attention call: shapes, op parameters and the input recipe.
+
+    Parameter names follow the op catalogue's `attention` entry (heads,
+    headDim, kvHeads, vHeadDim, causal, posOffset, scale, softcap, window,
+    alibi, alibiMax, alibiSlopes) plus the input tensor shapes.
+    """
+
+    name: str
+    T: int
+    S: int
+    heads: int
+    headDim: int
+    kvHeads: Optional[int] = None
+    vHeadDim: Optional[int] = None
+    causal: bool = True
+    posOffset: int = 0
+    scale: Optional[float] = None
+    softcap: Optional[float] = None
+    window: Optional[int] = None
+    alibi: Optional[bool] = None
+    alibiMax: Optional[float] = None
+    alibiSlopes: Optional[tuple] = None
+    bias: Optional[str] = None  # None, "TS" ([T,S]) or "HTS" ([heads,T,S])
+    bias_mask_prob: float = 0.0
+    std: float = 1.0
+    cache_rows: Optional[int] = None  # KV rows in the cache (S) that hold data; None = all
+    seed: int = 0
+
+    @property
+    def G(self) -> int:
+        return self.kvHeads if self.kvHeads else self.heads
+
+    @property
+    def Dv(self) -> int:
+        return self.vHeadDim if self.vHeadDim else self.headDim
+
+    def params(self) -> dict:
+        """The op parameters as keyword arguments (absent ones omitted)."""
+        out = {"heads": self.heads, "headDim": self.headDim}
+        for key in ("kvHeads", "vHeadDim", "posOffset", "scale", "softcap",
+                    "window", "alibi", "alibiMax", "alibiSlopes"):
+            val = getattr(self, key)
+            if val is not None:
+                out[key] = val
+        out["causal"] = self.causal
+        return out
+
+    def tensors(self):
+        """(q, k, v, bias or None) as float32 host arrays."""
+        H, G, D, Dv = self.heads, self.G, self.headDim, self.Dv
+        q = normal((self.T, H * D), self.seed, STREAM_Q, self.std)
+        k = normal((self.S, G * D), self.seed, STREAM_K, self.std)
+        v = normal((self.S, G * Dv), self.seed, STREAM_V, self.std)
+        if self.bias is None:
+            bias = None
+        elif self.bias == "TS":
+            bias = masked_bias((self.T, self.S), self.seed, self.bias_mask_prob)
+        elif self.bias == "HTS":
+            bias = masked_bias((H, self.T, self.S), self.seed, self.bias_mask_prob)
+        else:
+            raise ValueError(f"unknown bias layout {self.bias!r}")
+        return q, k, v, bias
+
+    def replace(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+# The workloads the measurements and the full-size parity tests use.
+TINY = Workload("tiny causal prefill T=S=8 H=4 G=2 D=16",
+                T=8, S=8, heads=4, kvHeads=2, headDim=16)
+
+LLAMA_DECODE = Workload("llama3-8b-shaped GQA decode T=1 S=32768 H=32 G=8 D=128",
+                        T=1, S=32768, heads=32, kvHeads=8, headDim=128,
+                        posOffset=32767)
+
+LLAMA_PREFILL = Workload("llama3-8b-shaped causal prefill T=S=4096 H=32 G=8 D=128",
+                         T=4096, S=4096, heads=32, kvHeads=8, headDim=128)
+
+LLAMA_CHUNKED = Workload("llama3-8b-shaped chunked prefill T=512 at 3584, S=4096",
+                         T=512, S=4096, heads=32, kvHeads=8, headDim=128,
+                         posOffset=3584)
+
+GEMMA2_SWA = Workload("gemma2-shaped sliding-window prefill T=S=8192 H=16 G=8 D=256",
+                      T=8192, S=8192, heads=16, kvHeads=8, headDim=256,
+                      scale=256 ** -0.5, softcap=50.0, window=4096, std=2.0)
+
+LATENT_DECODE = Workload("latent-shaped ALiBi+bias decode T=1 S=8192 H=16 D=192 Dv=128",
+                         T=1, S=8192, heads=16, kvHeads=16, headDim=192,
+                         vHeadDim=128, posOffset=8191, alibi=True, bias="HTS",
+                         bias_mask_prob=0.1)
+
+LATENT_NONCAUSAL = Workload("latent-shaped ALiBi+bias non-causal T=S=1024 H=16 D=192 Dv=128",
+                            T=1024, S=1024, heads=16, kvHeads=16, headDim=192,
+                            vHeadDim=128, causal=False, alibi=True, bias="HTS",
+                            bias_mask_prob=0.1)
+
+ALL = (TINY, LLAMA_DECODE, LLAMA_PREFILL, LLAMA_CHUNKED, GEMMA2_SWA,
+       LATENT_DECODE, LATENT_NONCAUSAL)
