@@ -1,0 +1,233 @@
+#!/usr/bin/env python3
+"""Benchmark of the attention op's hot path on one MI355X.
+
+One step is one decode step of the Llama-3-8B-shaped GQA workload (T=1,
+S=32768, heads 32, kvHeads 8, headDim 128, causal, posOffset 32767): two
+cache_write calls append the new K and V rows at row 32767, then
+attn_forward attends over the whole cache (decode_split + decode_combine).
+K/V caches rotate over two copies (512 MiB together) so no step finds its
+working set in the 256 MB Infinity Cache.
+
+`value` is the decode's algorithmic KV bandwidth: the bytes attention must
+move (every visible K and V row once, plus q and out) per step time, in
+GB/s. `roofline` rates the dominant kernel, decode_split, on its own: the
+same algorithmic bytes over its average duration, timed with HIP events
+recorded around each of its launches on the stream it runs on, against the
+8 TB/s HBM peak. `cpu_baseline` times the CPU oracle on the same inputs.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode KV GB/s + prefill TFLOP/s (f32), % of MI355X roofline, 1 GPU"
+HBM_PEAK_GBS = 8000.0
+FP32_PEAK_TFLOPS = 157.3
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = {
+    "decode_split": ["gqa_scaled_dot_amd/csrc/decode.hip", "gqa_scaled_dot_amd/csrc/device_common.h",
+                     "gqa_scaled_dot_amd/csrc/kernels.h"],
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash(kernel: str) -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from rocprofv3 counters, if taken on this very kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(kernel)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha256") != source_hash(kernel) or rec.get("workload") != workload:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def decode_algorithmic_bytes(w) -> int:
+    """Every visible K and V row once, plus q, out and the visible bias entries."""
+    lo = max(0, w.posOffset - (w.window or 0) + 1) if w.window else 0
+    hi = min(w.S, w.posOffset + w.T)
+    rows = hi - lo
+    b = rows * w.G * (w.headDim + w.Dv) * 4
+    b += w.T * w.heads * w.headDim * 4 + w.T * w.heads * w.Dv * 4
+    if w.bias == "HTS":
+        b += w.heads * w.T * rows * 4
+    elif w.bias == "TS":
+        b += w.T * rows * 4
+    return b
+
+
+def cpu_threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def run_decode(args):
+    import numpy as np
+    import torch
+
+    import gqa_scaled_dot_amd as ga
+    import workloads
+
+    w = workloads.LLAMA_DECODE
+    params = w.params()
+    dev = torch.device("cuda:0")
+    q, k, v, _ = w.tensors()
+    log(f"[bench] workload: {w.name}")
+    plan = ga.attn_plan(w.T, w.S, **params)
+    log(f"[bench] plan: {plan}")
+
+    n_buf = 2
+    qd = torch.from_numpy(q).to(dev)
+    kd = torch.from_numpy(k).to(dev)
+    vd = torch.from_numpy(v).to(dev)
+    kc = [torch.empty_like(kd) for _ in range(n_buf)]
+    vc = [torch.empty_like(vd) for _ in range(n_buf)]
+    for b in range(n_buf):  # the past rows, through cache_write
+        ga.attn_cache_write(kc[b], kd[:w.S - 1], 0)
+        ga.attn_cache_write(vc[b], vd[:w.S - 1], 0)
+    new_k, new_v = kd[w.S - 1:], vd[w.S - 1:]
+    del kd, vd
+    out = torch.empty((w.T, w.heads * w.Dv), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(ga.attn_workspace_size(w.T, w.S, **params), 256), dtype=torch.uint8, device=dev)
+
+    steps = []
+    for b in range(n_buf):
+        steps.append((ga.prepare_cache_write(kc[b], new_k, w.S - 1),
+                      ga.prepare_cache_write(vc[b], new_v, w.S - 1),
+                      ga.prepare_forward(qd, kc[b], vc[b], out=out, workspace=ws, **params)))
+
+    def step(i):
+        a, b, c = steps[i % n_buf]
+        a()
+        b()
+        c()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # Timed region: K steps between two events on the stream the kernels run on.
+    ga.attn_timing_enable(True)
+    for name in ("decode_split", "decode_combine", "cache_write"):
+        ga.attn_timing_collect(name)
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_timed = e0.elapsed_time(e1) / args.steps
+    split_ms, split_n = ga.attn_timing_collect("decode_split")
+    comb_ms, comb_n = ga.attn_timing_collect("decode_combine")
+    cw_ms, cw_n = ga.attn_timing_collect("cache_write")
+    ga.attn_timing_enable(False)
+
+    # The same loop without per-kernel events, for the step time itself.
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    log(f"[bench] step {ms_per_step * 1e3:.2f} us (with kernel events {ms_timed * 1e3:.2f} us); "
+        f"decode_split {split_ms / max(split_n, 1) * 1e3:.2f} us x{split_n}, "
+        f"decode_combine {comb_ms / max(comb_n, 1) * 1e3:.2f} us x{comb_n}, "
+        f"cache_write {cw_ms / max(cw_n, 1) * 1e3:.2f} us x{cw_n}")
+
+    alg_bytes = decode_algorithmic_bytes(w)
+    value = alg_bytes / (ms_per_step * 1e-3) / 1e9
+    split_avg_s = split_ms / split_n * 1e-3
+    achieved = alg_bytes / split_avg_s / 1e9
+    traffic = measured_traffic("decode_split", w.name)
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "kernel": "decode_split", "bytes_per_launch": alg_bytes,
+                "avg_launch_us": round(split_avg_s * 1e6, 3)}
+
+    # Parity of the benchmarked output against the oracle (same seeded inputs).
+    import oracle
+    threads = cpu_threads()
+    got = out.cpu().numpy().astype(np.float64)
+    cpu_baseline = None
+    t0 = time.perf_counter()
+    ref = oracle.attention(q, k, v, threads=threads, **params)
+    t_one = time.perf_counter() - t0
+    err = np.abs(got - ref)
+    parity_ok = bool(np.all(err <= 1e-4 + 1e-4 * np.abs(ref)))
+    log(f"[bench] parity vs oracle: max |err| {err.max():.3e} ok={parity_ok}")
+    if not args.no_cpu:
+        reps, total = 1, t_one
+        budget = 10.0
+        while total < budget and reps < 1000:
+            t0 = time.perf_counter()
+            oracle.attention(q, k, v, threads=threads, **params)
+            total += time.perf_counter() - t0
+            reps += 1
+        cpu_baseline = {"value": round(alg_bytes * reps / total / 1e9, 4), "unit": "GB/s",
+                        "cores": threads, "kind": "oracle",
+                        "sample": f"the full decode step (1 query row, 32 heads, 32768 keys), "
+                                  f"{reps} runs in {total:.1f} s, f64"}
+
+    return {
+        "metric": METRIC, "value": round(value, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "T": w.T, "S": w.S, "heads": w.heads, "kvHeads": w.G,
+                   "headDim": w.headDim, "vHeadDim": w.Dv, "posOffset": w.posOffset,
+                   "causal": True, "kv_buffers": n_buf, "splits": plan["splits"],
+                   "step": "2x cache_write (new K/V row) + attn_forward"},
+        "roofline": roofline,
+        "cpu_baseline": cpu_baseline,
+        "parity": {"max_abs_err": float(err.max()), "ok": parity_ok},
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle timing")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the op has no multi-GPU path in this library)", file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 1 or args.warmup < 0:
+        ap.error("--steps must be >= 1 and --warmup >= 0")
+    rec = run_decode(args)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

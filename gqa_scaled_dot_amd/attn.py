@@ -1,0 +1,281 @@
+"""Python binding of libattn.so, with the C ABI's names.
+
+Argument marshalling only: every step of the op runs in the library's HIP
+kernels. PyTorch supplies device memory (the output and workspace tensors)
+and the current stream. Parameters take the op catalogue's names for the
+`attention` op (heads, headDim, kvHeads, vHeadDim, causal, posOffset, scale,
+softcap, window, alibi, alibiMax, alibiSlopes).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+from typing import Optional, Sequence
+
+from . import _lib
+from ._lib import AttnParams, AttnPlanInfo
+
+
+class AttnError(RuntimeError):
+    """A call the library refused (code and message from attn_last_error)."""
+
+    def __init__(self, code: int, message: str):
+        super().__init__(f"[{code}] {message}")
+        self.code = code
+        self.message = message
+
+
+def attn_last_error() -> str:
+    return _lib.lib().attn_last_error().decode()
+
+
+def _check(rc: int) -> None:
+    if rc != _lib.ATTN_OK:
+        raise AttnError(rc, attn_last_error())
+
+
+def make_params(T: int, S: int, *, heads: int, headDim: int, kvHeads: Optional[int] = None,
+                vHeadDim: Optional[int] = None, causal: Optional[bool] = None,
+                posOffset: Optional[int] = None, scale: Optional[float] = None,
+                softcap: Optional[float] = None, window: Optional[int] = None,
+                alibi: Optional[bool] = None, alibiMax: Optional[float] = None,
+                alibiSlopes: Optional[Sequence[float]] = None, bias_kind: int = 0):
+    """attn_params for one call. Returns (params, keepalive) - keep the second
+    alive until the call returns (it owns the explicit slope array)."""
+    L = _lib.lib()
+    p = AttnParams()
+    L.attn_params_init(ctypes.byref(p))
+    p.T, p.S = int(T), int(S)
+    p.heads, p.head_dim = int(heads), int(headDim)
+    p.kv_heads = int(kvHeads) if kvHeads else 0
+    p.v_head_dim = int(vHeadDim) if vHeadDim else 0
+    if causal is not None:
+        p.causal = 1 if causal else 0
+    if posOffset is not None:
+        p.pos_offset = int(posOffset)
+    if scale is not None:
+        p.has_scale, p.scale = 1, float(scale)
+    if softcap is not None:
+        p.softcap = float(softcap)
+    if window is not None:
+        p.window = int(window)
+    keep = None
+    if alibiSlopes is not None:
+        # The C ABI takes `heads` floats; only the caller knows the list's length.
+        if len(alibiSlopes) != int(heads):
+            raise AttnError(_lib.ATTN_ERR_INVALID,
+                            f"alibiSlopes: {len(alibiSlopes)} slopes for {heads} heads")
+        keep = (ctypes.c_float * len(alibiSlopes))(*[float(x) for x in alibiSlopes])
+        p.alibi = _lib.ATTN_ALIBI_EXPLICIT
+        p.alibi_slopes = ctypes.cast(keep, ctypes.POINTER(ctypes.c_float))
+    elif alibiMax is not None:
+        p.alibi, p.alibi_max = _lib.ATTN_ALIBI_MPT, float(alibiMax)
+    elif alibi:
+        p.alibi = _lib.ATTN_ALIBI_BLOOM
+    p.bias_kind = int(bias_kind)
+    return p, keep
+
+
+def attn_validate(T: int, S: int, bias_kind: int = 0, **params) -> None:
+    p, keep = make_params(T, S, bias_kind=bias_kind, **params)
+    _check(_lib.lib().attn_validate(ctypes.byref(p)))
+    del keep
+
+
+def attn_workspace_size(T: int, S: int, bias_kind: int = 0, **params) -> int:
+    p, keep = make_params(T, S, bias_kind=bias_kind, **params)
+    n = _lib.lib().attn_workspace_size(ctypes.byref(p))
+    del keep
+    return int(n)
+
+
+def attn_plan(T: int, S: int, bias_kind: int = 0, **params) -> dict:
+    p, keep = make_params(T, S, bias_kind=bias_kind, **params)
+    info = AttnPlanInfo()
+    _check(_lib.lib().attn_plan(ctypes.byref(p), ctypes.byref(info)))
+    del keep
+    return {"path": _lib.PATH_NAMES.get(info.path, str(info.path)), "splits": info.splits,
+            "tile_q": info.tile_q}
+
+
+def attn_set_option(name: str, value: int) -> None:
+    _check(_lib.lib().attn_set_option(name.encode(), int(value)))
+
+
+def attn_timing_enable(on: bool) -> None:
+    _check(_lib.lib().attn_timing_enable(1 if on else 0))
+
+
+def attn_timing_collect(kernel: str):
+    """(total milliseconds, launches) for `kernel` since the last collect."""
+    ms = ctypes.c_double()
+    n = ctypes.c_int64()
+    _check(_lib.lib().attn_timing_collect(kernel.encode(), ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
+
+
+# -- device calls --------------------------------------------------------------
+
+_workspaces = {}
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dev_tensor(x, name: str):
+    torch = _torch()
+    if not isinstance(x, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if x.device.type != "cuda":
+        raise ValueError(f"{name}: must be a GPU tensor (got {x.device})")
+    if x.dtype != torch.float32:
+        raise ValueError(f"{name}: must be float32 (got {x.dtype})")
+    if not x.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous row-major")
+    return x
+
+
+def _stream_ptr(stream, device):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def workspace_for(nbytes: int, device):
+    """A cached device buffer of at least nbytes (None for 0)."""
+    if nbytes <= 0:
+        return None
+    torch = _torch()
+    key = (device.type, device.index)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def _check_forward(q, k, v, bias, out, params):
+    """Shape, dtype and device checks; returns (T, S, heads, vHeadDim, bias_kind)."""
+    _dev_tensor(q, "q")
+    _dev_tensor(k, "k")
+    _dev_tensor(v, "v")
+    if q.dim() != 2 or k.dim() != 2 or v.dim() != 2:
+        raise ValueError("q, k and v are flat 2-D tensors [rows, heads*width]")
+    T, S = q.shape[0], k.shape[0]
+    H = int(params["heads"])
+    D = int(params["headDim"])
+    G = int(params.get("kvHeads") or H)
+    Dv = int(params.get("vHeadDim") or D)
+    if q.shape[1] != H * D:
+        raise ValueError(f"q: {tuple(q.shape)} is not [T, heads*headDim] = [T, {H * D}]")
+    if k.shape[1] != G * D:
+        raise ValueError(f"k: {tuple(k.shape)} is not [S, kvHeads*headDim] = [S, {G * D}]")
+    if tuple(v.shape) != (S, G * Dv):
+        raise ValueError(f"v: {tuple(v.shape)} is not [S, kvHeads*vHeadDim] = [{S}, {G * Dv}]")
+    bias_kind = _lib.ATTN_BIAS_NONE
+    if bias is not None:
+        _dev_tensor(bias, "bias")
+        if tuple(bias.shape) == (T, S):
+            bias_kind = _lib.ATTN_BIAS_TS
+        elif tuple(bias.shape) == (H, T, S):
+            bias_kind = _lib.ATTN_BIAS_HTS
+        else:
+            raise ValueError(f"bias: {tuple(bias.shape)} is neither [T, S] nor [heads, T, S]")
+    if out is not None:
+        _dev_tensor(out, "out")
+        if tuple(out.shape) != (T, H * Dv):
+            raise ValueError(f"out: {tuple(out.shape)} is not [T, heads*vHeadDim] = [{T}, {H * Dv}]")
+    return T, S, H, Dv, bias_kind
+
+
+def attn_forward(q, k, v, bias=None, *, out=None, workspace=None, stream=None, **params):
+    """Op `attention`: returns out [T, heads*vHeadDim] (float32, on q's device).
+
+    q [T, heads*headDim], k [S, kvHeads*headDim], v [S, kvHeads*vHeadDim] and the
+    optional bias [T, S] or [heads, T, S] are contiguous float32 GPU tensors.
+    """
+    torch = _torch()
+    T, S, H, Dv, bias_kind = _check_forward(q, k, v, bias, out, params)
+    p, keep = make_params(T, S, bias_kind=bias_kind, **params)
+    L = _lib.lib()
+    if out is None:
+        out = torch.empty((T, H * Dv), dtype=torch.float32, device=q.device)
+    need = int(L.attn_workspace_size(ctypes.byref(p)))
+    if workspace is None:
+        workspace = workspace_for(need, q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = L.attn_forward(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                        bias.data_ptr() if bias is not None else None, out.data_ptr(),
+                        ws_ptr, ws_bytes, _stream_ptr(stream, q.device))
+    del keep
+    _check(rc)
+    return out
+
+
+def prepare_forward(q, k, v, bias=None, *, out, workspace=None, stream=None, **params):
+    """Marshal one attn_forward call once and return a zero-argument callable
+    that repeats it (same tensors, same stream). For timing loops, where
+    rebuilding the ctypes arguments on every call would cost more host time
+    than the kernels take. The tensors must outlive the callable."""
+    T, S, _, _, bias_kind = _check_forward(q, k, v, bias, out, params)
+    p, keep = make_params(T, S, bias_kind=bias_kind, **params)
+    L = _lib.lib()
+    need = int(L.attn_workspace_size(ctypes.byref(p)))
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = workspace_for(need, q.device)
+    args = (ctypes.byref(p), ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
+            ctypes.c_void_p(v.data_ptr()),
+            ctypes.c_void_p(bias.data_ptr() if bias is not None else None),
+            ctypes.c_void_p(out.data_ptr()),
+            ctypes.c_void_p(workspace.data_ptr() if workspace is not None else None),
+            ctypes.c_size_t(workspace.numel() * workspace.element_size() if workspace is not None else 0),
+            _stream_ptr(stream, q.device))
+    fn = L.attn_forward
+    held = (p, keep, q, k, v, bias, out, workspace)
+
+    def call():
+        rc = fn(*args)
+        if rc != _lib.ATTN_OK:
+            raise AttnError(rc, attn_last_error())
+
+    call.held = held
+    return call
+
+
+def prepare_cache_write(cache, values, offset: int, *, stream=None):
+    """Like prepare_forward, for attn_cache_write."""
+    _dev_tensor(cache, "cache")
+    _dev_tensor(values, "values")
+    args = (ctypes.c_void_p(cache.data_ptr()), ctypes.c_int64(cache.shape[0]),
+            ctypes.c_int64(cache.shape[1]), ctypes.c_void_p(values.data_ptr()),
+            ctypes.c_int64(values.shape[0]), ctypes.c_int64(int(offset)),
+            _stream_ptr(stream, cache.device))
+    fn = _lib.lib().attn_cache_write
+    held = (cache, values)
+
+    def call():
+        rc = fn(*args)
+        if rc != _lib.ATTN_OK:
+            raise AttnError(rc, attn_last_error())
+
+    call.held = held
+    return call
+
+
+def attn_cache_write(cache, values, offset: int, *, stream=None):
+    """Op `cache_write`: rows [offset, offset+rows) of `cache` become `values`, in place.
+    Returns the cache."""
+    _dev_tensor(cache, "cache")
+    _dev_tensor(values, "values")
+    if cache.dim() != 2 or values.dim() != 2 or cache.shape[1] != values.shape[1]:
+        raise ValueError("cache [maxRows, width] and values [rows, width] must share width")
+    rc = _lib.lib().attn_cache_write(cache.data_ptr(), cache.shape[0], cache.shape[1],
+                                     values.data_ptr(), values.shape[0], int(offset),
+                                     _stream_ptr(stream, cache.device))
+    _check(rc)
+    return cache

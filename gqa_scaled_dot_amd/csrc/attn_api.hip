@@ -1,0 +1,543 @@
+// Host side of libattn.so: the C ABI declared in attn.h. Resolves the op's
+// defaults, checks every argument before anything runs (refusing by name,
+// as the op catalogue's feature convention asks), builds the ALiBi slope
+// table, chooses a kernel path and launches it on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "attn.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return code;
+}
+
+int ok() {
+    g_last_error.clear();
+    return ATTN_OK;
+}
+
+// Process-wide tuning overrides (attn_set_option).
+int64_t g_opt_decode_splits = 0;
+int64_t g_opt_force_path = 0;
+
+constexpr int kCUs = 256;                 // MI355X compute units
+constexpr int kDecodeWgPerCU = 2;         // decode_split occupancy target
+constexpr int64_t kDecodeMinKeys = 256;   // smallest key chunk worth a workgroup
+constexpr int64_t kDecodeChunkAlign = 64; // key chunk granularity (a multiple of 16 row groups x 2 rows)
+constexpr int64_t kDecodeMaxSplits = 1024;
+constexpr int64_t kMaxDim = 1 << 16;
+
+// ---------------------------------------------------------------------------
+// ALiBi slope tables (op `attention`, params alibi / alibiMax / alibiSlopes).
+// BLOOM, as in the ALiBi paper: with p the largest power of two <= H, head
+// i = 1..p gets 2^(-8i/p); further heads take 2^(-4j/p) for odd j = 1, 3, ...
+// MPT with alibi_bias_max b: with n the smallest power of two >= H, head
+// i = 1..n gets 2^(-ib/n); when n != H the even-numbered ones come first,
+// then the odd-numbered ones, and the first H are kept.
+// Computed in double and rounded once to f32, the op's number type.
+// ---------------------------------------------------------------------------
+void slopes_bloom(int64_t H, float* out) {
+    int64_t p = 1;
+    while (p * 2 <= H) p *= 2;
+    int64_t n = 0;
+    for (int64_t i = 1; i <= p; ++i) out[n++] = (float)exp2(-8.0 * (double)i / (double)p);
+    for (int64_t j = 1; n < H; j += 2) out[n++] = (float)exp2(-4.0 * (double)j / (double)p);
+}
+
+void slopes_mpt(int64_t H, double b, float* out) {
+    int64_t n = 1;
+    while (n < H) n *= 2;
+    int64_t k = 0;
+    if (n == H) {
+        for (int64_t i = 1; i <= n; ++i) out[k++] = (float)exp2(-(double)i * b / (double)n);
+        return;
+    }
+    for (int64_t i = 2; i <= n && k < H; i += 2) out[k++] = (float)exp2(-(double)i * b / (double)n);
+    for (int64_t i = 1; i <= n && k < H; i += 2) out[k++] = (float)exp2(-(double)i * b / (double)n);
+}
+
+// Resolved view of attn_params.
+struct Resolved {
+    int64_t T, S, H, G, D, Dv, P0, window;
+    bool causal;
+    int bias_kind;
+    attn::Epilogue ep;
+};
+
+int resolve(const attn_params* p, Resolved* r) {
+    if (!p) return fail(ATTN_ERR_INVALID, "params: NULL pointer");
+    if (p->T < 0) return fail(ATTN_ERR_INVALID, "T: must be >= 0 (got %lld)", (long long)p->T);
+    if (p->S < 0) return fail(ATTN_ERR_INVALID, "S: must be >= 0 (got %lld)", (long long)p->S);
+    if (p->heads <= 0 || p->heads > kMaxDim)
+        return fail(ATTN_ERR_INVALID, "heads: must be in 1..%lld (got %lld)", (long long)kMaxDim,
+                    (long long)p->heads);
+    if (p->kv_heads < 0 || p->kv_heads > p->heads)
+        return fail(ATTN_ERR_INVALID, "kvHeads: must be in 1..heads or 0 for absent (got %lld)",
+                    (long long)p->kv_heads);
+    const int64_t G = p->kv_heads ? p->kv_heads : p->heads;
+    if (p->heads % G)
+        return fail(ATTN_ERR_INVALID, "kvHeads: heads (%lld) is not a multiple of kvHeads (%lld)",
+                    (long long)p->heads, (long long)G);
+    if (p->head_dim <= 0 || p->head_dim > kMaxDim)
+        return fail(ATTN_ERR_INVALID, "headDim: must be in 1..%lld (got %lld)", (long long)kMaxDim,
+                    (long long)p->head_dim);
+    if (p->v_head_dim < 0 || p->v_head_dim > kMaxDim)
+        return fail(ATTN_ERR_INVALID, "vHeadDim: must be in 1..%lld or 0 for absent (got %lld)",
+                    (long long)kMaxDim, (long long)p->v_head_dim);
+    if (p->causal != 0 && p->causal != 1)
+        return fail(ATTN_ERR_INVALID, "causal: must be 0 or 1 (got %d)", p->causal);
+    if (p->pos_offset < 0)
+        return fail(ATTN_ERR_INVALID, "posOffset: must be >= 0 (got %lld)", (long long)p->pos_offset);
+    if (p->has_scale != 0 && p->has_scale != 1)
+        return fail(ATTN_ERR_INVALID, "scale: has_scale must be 0 or 1 (got %d)", p->has_scale);
+    if (p->has_scale && !isfinite(p->scale))
+        return fail(ATTN_ERR_INVALID, "scale: must be finite");
+    if (!(p->softcap >= 0.0f) || !isfinite(p->softcap))
+        return fail(ATTN_ERR_INVALID, "softcap: must be finite and >= 0 (0 = off)");
+    if (p->window < 0)
+        return fail(ATTN_ERR_INVALID, "window: must be >= 0 (0 = off; got %lld)", (long long)p->window);
+    if (p->bias_kind < ATTN_BIAS_NONE || p->bias_kind > ATTN_BIAS_HTS)
+        return fail(ATTN_ERR_INVALID, "bias: bias_kind must be 0, 1 ([T,S]) or 2 ([heads,T,S])");
+    if (p->alibi < ATTN_ALIBI_NONE || p->alibi > ATTN_ALIBI_EXPLICIT)
+        return fail(ATTN_ERR_INVALID, "alibi: mode must be 0..3 (got %d)", p->alibi);
+    if (p->alibi == ATTN_ALIBI_MPT && !(isfinite(p->alibi_max) && p->alibi_max > 0.0f))
+        return fail(ATTN_ERR_INVALID, "alibiMax: must be finite and > 0");
+    if (p->alibi == ATTN_ALIBI_EXPLICIT && !p->alibi_slopes)
+        return fail(ATTN_ERR_INVALID, "alibiSlopes: NULL pointer");
+    if (p->alibi != ATTN_ALIBI_NONE && p->heads > ATTN_ALIBI_MAX_HEADS)
+        return fail(ATTN_ERR_UNSUPPORTED, "attention.alibi: at most %d heads (got %lld)",
+                    ATTN_ALIBI_MAX_HEADS, (long long)p->heads);
+
+    Resolved& o = *r;
+    o.T = p->T;
+    o.S = p->S;
+    o.H = p->heads;
+    o.G = G;
+    o.D = p->head_dim;
+    o.Dv = p->v_head_dim ? p->v_head_dim : p->head_dim;
+    o.P0 = p->pos_offset;
+    o.window = p->window;
+    o.causal = p->causal != 0;
+    o.bias_kind = p->bias_kind;
+    // Sizes of every tensor must stay far below 2^62 bytes.
+    const double elems = (double)o.T * o.H * (double)(o.D > o.Dv ? o.D : o.Dv) +
+                         (double)o.S * o.G * (double)(o.D + o.Dv) +
+                         (o.bias_kind ? (double)o.H * o.T * o.S : 0.0);
+    if (elems > 1e17) return fail(ATTN_ERR_INVALID, "sizes: tensors too large");
+    // Positions (query rows at posOffset + t, key rows at s) are kept in 32 bits.
+    if (o.S > INT32_MAX) return fail(ATTN_ERR_UNSUPPORTED, "S: more than 2^31-1 key rows");
+    if (o.P0 > INT32_MAX || o.T > INT32_MAX - o.P0)
+        return fail(ATTN_ERR_UNSUPPORTED, "posOffset: query positions past 2^31-1");
+
+    attn::Epilogue& e = o.ep;
+    memset(&e, 0, sizeof e);
+    e.scale = p->has_scale ? p->scale : (float)(1.0 / sqrt((double)o.D));
+    e.softcap = p->softcap;
+    e.inv_softcap = p->softcap > 0.0f ? (float)(1.0 / (double)p->softcap) : 0.0f;
+    e.causal = o.causal;
+    e.bias_kind = o.bias_kind;
+    e.pos_offset = (int32_t)o.P0;
+    // Every position is below 2^31, so a wider window sees every key a window
+    // of 2^31-1 sees.
+    e.window = (int32_t)(o.window < INT32_MAX ? o.window : INT32_MAX);
+    e.has_alibi = p->alibi != ATTN_ALIBI_NONE;
+    if (p->alibi == ATTN_ALIBI_BLOOM) slopes_bloom(o.H, e.slopes);
+    if (p->alibi == ATTN_ALIBI_MPT) slopes_mpt(o.H, (double)p->alibi_max, e.slopes);
+    if (p->alibi == ATTN_ALIBI_EXPLICIT) {
+        for (int64_t h = 0; h < o.H; ++h) {
+            if (!isfinite(p->alibi_slopes[h]))
+                return fail(ATTN_ERR_INVALID, "alibiSlopes: entry %lld is not finite", (long long)h);
+            e.slopes[h] = p->alibi_slopes[h];
+        }
+    }
+    return ok();
+}
+
+// Keys any query row can see (op `attention`, params causal and window).
+attn::KeyRange key_range(const Resolved& r) {
+    attn::KeyRange kr{0, r.S};
+    const int64_t first = r.P0, last = r.P0 + r.T - 1;
+    if (r.causal) {
+        kr.hi = last + 1 < r.S ? last + 1 : r.S;
+        if (r.window > 0) kr.lo = first - r.window + 1 > 0 ? first - r.window + 1 : 0;
+    } else if (r.window > 0) {
+        kr.lo = first - r.window > 0 ? first - r.window : 0;
+        kr.hi = last + r.window + 1 < r.S ? last + r.window + 1 : r.S;
+    }
+    if (kr.lo > kr.hi) kr.lo = kr.hi;
+    return kr;
+}
+
+int next_pow2_nq(int64_t n) {
+    int q = 1;
+    while (q < n) q *= 2;
+    return q;
+}
+
+struct Plan {
+    int path;
+    attn::DecodePlan decode;
+    attn::PrefillPlan prefill;
+    size_t workspace;
+};
+
+int make_plan(const Resolved& r, Plan* plan) {
+    memset(plan, 0, sizeof *plan);
+    plan->decode.splits = 1;
+    if (r.T == 0) {
+        plan->path = ATTN_PATH_EMPTY;
+        return ok();
+    }
+    const attn::KeyRange kr = key_range(r);
+    if (r.S == 0 || kr.hi <= kr.lo) {
+        plan->path = ATTN_PATH_ZERO;
+        return ok();
+    }
+    const int64_t hpg = r.H / r.G;
+    const int64_t nrows = r.T * hpg;
+    const bool dec_ok = nrows <= 16 && attn::decode_supported((int)r.D, (int)r.Dv, next_pow2_nq(nrows));
+    const bool pre_ok = attn::prefill_supported((int)r.D, (int)r.Dv);
+    int path;
+    if (g_opt_force_path) {
+        path = (int)g_opt_force_path;
+        if ((path == ATTN_PATH_DECODE && !dec_ok) || (path == ATTN_PATH_PREFILL && !pre_ok))
+            return fail(ATTN_ERR_UNSUPPORTED, "force_path: path %d cannot serve this shape", path);
+        if (path != ATTN_PATH_DECODE && path != ATTN_PATH_PREFILL && path != ATTN_PATH_GENERIC)
+            return fail(ATTN_ERR_INVALID, "force_path: unknown path %d", path);
+    } else if (dec_ok) {
+        path = ATTN_PATH_DECODE;
+    } else if (pre_ok) {
+        path = ATTN_PATH_PREFILL;
+    } else {
+        path = ATTN_PATH_GENERIC;
+    }
+    if (path == ATTN_PATH_GENERIC && (r.D + r.Dv > 16000 || r.H > 65535))
+        return fail(ATTN_ERR_UNSUPPORTED,
+                    "headDim/vHeadDim: no kernel for headDim %lld with vHeadDim %lld and %lld heads",
+                    (long long)r.D, (long long)r.Dv, (long long)r.H);
+    plan->path = path;
+    if (path == ATTN_PATH_DECODE) {
+        attn::DecodePlan& d = plan->decode;
+        d.nq = next_pow2_nq(nrows);
+        d.range = kr;
+        const int64_t n = kr.hi - kr.lo;
+        int64_t splits = g_opt_decode_splits;
+        if (splits <= 0) {
+            const int64_t target = ((int64_t)kCUs * kDecodeWgPerCU + r.G - 1) / r.G;
+            const int64_t most = (n + kDecodeMinKeys - 1) / kDecodeMinKeys;
+            splits = target < most ? target : most;
+        }
+        if (splits < 1) splits = 1;
+        if (splits > kDecodeMaxSplits) splits = kDecodeMaxSplits;
+        int64_t chunk = (n + splits - 1) / splits;
+        chunk = (chunk + kDecodeChunkAlign - 1) / kDecodeChunkAlign * kDecodeChunkAlign;
+        // The kernel addresses a chunk with 32-bit offsets from its first row.
+        const int64_t row_floats = r.G * (r.D > r.Dv ? r.D : r.Dv);
+        const int64_t max_chunk = (INT32_MAX - row_floats) / row_floats / kDecodeChunkAlign * kDecodeChunkAlign;
+        if (max_chunk < kDecodeChunkAlign || (n + max_chunk - 1) / max_chunk > kDecodeMaxSplits)
+            return fail(ATTN_ERR_UNSUPPORTED, "S: key range too long for the decode path at this width");
+        if (chunk > max_chunk) chunk = max_chunk;
+        d.chunk = chunk;
+        d.splits = (int32_t)((n + chunk - 1) / chunk);
+        if (d.splits > 1)
+            plan->workspace = sizeof(float) * (size_t)(r.T * r.H) * (size_t)d.splits * (size_t)(r.Dv + 2);
+    }
+    if (path == ATTN_PATH_PREFILL) {
+        plan->prefill.tile_q = 128;
+        plan->prefill.tile_k = 32;
+    }
+    return ok();
+}
+
+// ---------------------------------------------------------------------------
+// Kernel timing (attn_timing_enable / attn_timing_collect).
+// ---------------------------------------------------------------------------
+struct TimingRecord {
+    const char* name;
+    int slot;
+};
+
+struct Timing {
+    std::mutex mu;
+    bool on = false;
+    bool created = false;
+    std::vector<hipEvent_t> start, stop;
+    std::vector<int> free_slots;
+    std::vector<TimingRecord> records;
+};
+
+Timing& timing() {
+    static Timing t;
+    return t;
+}
+
+constexpr int kTimingSlots = 4096;
+
+// Runs launch(L) with L carrying a pair of events from the pool when timing is
+// on; the dispatch stamps them with the kernel's own start and end.
+template <typename F>
+hipError_t timed(const char* name, hipStream_t stream, F&& launch) {
+    Timing& tm = timing();
+    attn::Launch L{stream, nullptr, nullptr};
+    if (!tm.on) return launch(L);
+    int slot = -1;
+    {
+        std::lock_guard<std::mutex> lock(tm.mu);
+        if (!tm.free_slots.empty()) {
+            slot = tm.free_slots.back();
+            tm.free_slots.pop_back();
+        }
+    }
+    if (slot < 0) return launch(L);
+    L.start = tm.start[slot];
+    L.stop = tm.stop[slot];
+    const hipError_t err = launch(L);
+    std::lock_guard<std::mutex> lock(tm.mu);
+    if (err == hipSuccess) tm.records.push_back({name, slot});
+    else tm.free_slots.push_back(slot);
+    return err;
+}
+
+bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
+    if (!a || !b || !an || !bn) return false;
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + bn && y < x + an;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+void attn_params_init(attn_params* p) {
+    if (!p) return;
+    memset(p, 0, sizeof *p);
+    p->causal = 1;
+}
+
+int attn_validate(const attn_params* p) {
+    Resolved r;
+    int rc = resolve(p, &r);
+    if (rc) return rc;
+    Plan plan;
+    return make_plan(r, &plan);
+}
+
+size_t attn_workspace_size(const attn_params* p) {
+    Resolved r;
+    if (resolve(p, &r)) return 0;
+    Plan plan;
+    if (make_plan(r, &plan)) return 0;
+    return plan.workspace;
+}
+
+int attn_plan(const attn_params* p, attn_plan_info* info) {
+    if (!info) return fail(ATTN_ERR_INVALID, "info: NULL pointer");
+    Resolved r;
+    int rc = resolve(p, &r);
+    if (rc) return rc;
+    Plan plan;
+    rc = make_plan(r, &plan);
+    if (rc) return rc;
+    info->path = plan.path;
+    info->splits = plan.path == ATTN_PATH_DECODE ? plan.decode.splits : 1;
+    info->tile_q = plan.path == ATTN_PATH_PREFILL ? plan.prefill.tile_q : 0;
+    info->reserved = 0;
+    return ok();
+}
+
+int attn_forward(const attn_params* p, const float* q, const float* k, const float* v,
+                 const float* bias, float* out, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+    Resolved r;
+    int rc = resolve(p, &r);
+    if (rc) return rc;
+    Plan plan;
+    rc = make_plan(r, &plan);
+    if (rc) return rc;
+    if (plan.path == ATTN_PATH_EMPTY) return ok();
+
+    const size_t qn = sizeof(float) * (size_t)(r.T * r.H * r.D);
+    const size_t kn = sizeof(float) * (size_t)(r.S * r.G * r.D);
+    const size_t vn = sizeof(float) * (size_t)(r.S * r.G * r.Dv);
+    const size_t on = sizeof(float) * (size_t)(r.T * r.H * r.Dv);
+    const size_t bn = r.bias_kind == ATTN_BIAS_TS    ? sizeof(float) * (size_t)(r.T * r.S)
+                      : r.bias_kind == ATTN_BIAS_HTS ? sizeof(float) * (size_t)(r.H * r.T * r.S)
+                                                     : 0;
+    if (!out) return fail(ATTN_ERR_INVALID, "out: NULL pointer");
+    if (!q) return fail(ATTN_ERR_INVALID, "q: NULL pointer");
+    if (r.S > 0 && (!k || !v)) return fail(ATTN_ERR_INVALID, "%s: NULL pointer", k ? "v" : "k");
+    if (r.bias_kind && !bias) return fail(ATTN_ERR_INVALID, "bias: NULL pointer with bias_kind %d", r.bias_kind);
+    if (!r.bias_kind && bias) return fail(ATTN_ERR_INVALID, "bias: pointer given with bias_kind 0");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(bias) || !aligned16(out))
+        return fail(ATTN_ERR_INVALID, "q/k/v/bias/out: pointers must be 16-byte aligned");
+    if (overlaps(out, on, q, qn) || overlaps(out, on, k, kn) || overlaps(out, on, v, vn) ||
+        overlaps(out, on, bias, bn))
+        return fail(ATTN_ERR_INVALID, "out: overlaps an input");
+    if (plan.workspace) {
+        if (!workspace || workspace_bytes < plan.workspace)
+            return fail(ATTN_ERR_INVALID, "workspace: %zu bytes needed, %zu given", plan.workspace,
+                        workspace ? workspace_bytes : (size_t)0);
+        if (((uintptr_t)workspace & 255u) != 0)
+            return fail(ATTN_ERR_INVALID, "workspace: must be 256-byte aligned");
+        if (overlaps(workspace, plan.workspace, out, on) || overlaps(workspace, plan.workspace, q, qn) ||
+            overlaps(workspace, plan.workspace, k, kn) || overlaps(workspace, plan.workspace, v, vn) ||
+            overlaps(workspace, plan.workspace, bias, bn))
+            return fail(ATTN_ERR_INVALID, "workspace: overlaps a tensor");
+    }
+
+    attn::Problem prob;
+    prob.q = q;
+    prob.k = k;
+    prob.v = v;
+    prob.bias = bias;
+    prob.out = out;
+    prob.T = r.T;
+    prob.S = r.S;
+    prob.H = (int32_t)r.H;
+    prob.G = (int32_t)r.G;
+    prob.D = (int32_t)r.D;
+    prob.Dv = (int32_t)r.Dv;
+    prob.ep = r.ep;
+    hipStream_t s = (hipStream_t)stream;
+
+    hipError_t err = hipSuccess;
+    switch (plan.path) {
+        case ATTN_PATH_ZERO:
+            err = timed("zero_fill", s, [&](const attn::Launch& L) {
+                return attn::launch_zero_fill(out, r.T * r.H * r.Dv, L);
+            });
+            break;
+        case ATTN_PATH_GENERIC:
+            err = timed("generic", s, [&](const attn::Launch& L) { return attn::launch_generic(prob, L); });
+            break;
+        case ATTN_PATH_DECODE:
+            err = timed("decode_split", s, [&](const attn::Launch& L) {
+                return attn::launch_decode_split(prob, plan.decode, (float*)workspace, L);
+            });
+            if (err == hipSuccess && plan.decode.splits > 1)
+                err = timed("decode_combine", s, [&](const attn::Launch& L) {
+                    return attn::launch_decode_combine(prob, plan.decode, (const float*)workspace, L);
+                });
+            break;
+        case ATTN_PATH_PREFILL:
+            err = timed("prefill", s, [&](const attn::Launch& L) {
+                return attn::launch_prefill(prob, plan.prefill, L);
+            });
+            break;
+        default:
+            return fail(ATTN_ERR_INVALID, "internal: unknown path %d", plan.path);
+    }
+    if (err != hipSuccess) return fail(ATTN_ERR_DEVICE, "launch: %s", hipGetErrorString(err));
+    return ok();
+}
+
+int attn_cache_write(float* cache, int64_t max_rows, int64_t width, const float* values,
+                     int64_t rows, int64_t offset, void* stream) {
+    if (max_rows < 0) return fail(ATTN_ERR_INVALID, "maxRows: must be >= 0");
+    if (width <= 0) return fail(ATTN_ERR_INVALID, "width: must be > 0");
+    if (rows < 0) return fail(ATTN_ERR_INVALID, "rows: must be >= 0");
+    if (offset < 0) return fail(ATTN_ERR_INVALID, "offset: must be >= 0 (got %lld)", (long long)offset);
+    if (offset > max_rows || rows > max_rows - offset)
+        return fail(ATTN_ERR_INVALID, "offset: rows %lld..%lld run past the cache's %lld rows",
+                    (long long)offset, (long long)(offset + rows), (long long)max_rows);
+    if ((double)max_rows * (double)width > 1e17) return fail(ATTN_ERR_INVALID, "cache: too large");
+    if (rows == 0) return ok();
+    if (!cache) return fail(ATTN_ERR_INVALID, "cache: NULL pointer");
+    if (!values) return fail(ATTN_ERR_INVALID, "values: NULL pointer");
+    float* dst = cache + offset * width;
+    const size_t n = sizeof(float) * (size_t)(rows * width);
+    if (overlaps(dst, n, values, n)) return fail(ATTN_ERR_INVALID, "values: overlap the rows being written");
+    hipStream_t s = (hipStream_t)stream;
+    const hipError_t err = timed("cache_write", s, [&](const attn::Launch& L) {
+        return attn::launch_cache_write(dst, values, rows * width, L);
+    });
+    if (err != hipSuccess) return fail(ATTN_ERR_DEVICE, "launch: %s", hipGetErrorString(err));
+    return ok();
+}
+
+const char* attn_last_error(void) { return g_last_error.c_str(); }
+
+int attn_set_option(const char* name, int64_t value) {
+    if (!name) return fail(ATTN_ERR_INVALID, "option: NULL name");
+    if (!strcmp(name, "decode_splits")) {
+        if (value < 0 || value > kDecodeMaxSplits)
+            return fail(ATTN_ERR_INVALID, "decode_splits: must be in 0..%lld", (long long)kDecodeMaxSplits);
+        g_opt_decode_splits = value;
+        return ok();
+    }
+    if (!strcmp(name, "force_path")) {
+        if (value != 0 && value != ATTN_PATH_GENERIC && value != ATTN_PATH_DECODE && value != ATTN_PATH_PREFILL)
+            return fail(ATTN_ERR_INVALID, "force_path: must be 0, %d, %d or %d", ATTN_PATH_GENERIC,
+                        ATTN_PATH_DECODE, ATTN_PATH_PREFILL);
+        g_opt_force_path = value;
+        return ok();
+    }
+    return fail(ATTN_ERR_INVALID, "option: unknown name '%s'", name);
+}
+
+int attn_timing_enable(int on) {
+    Timing& tm = timing();
+    std::lock_guard<std::mutex> lock(tm.mu);
+    if (on && !tm.created) {
+        tm.start.resize(kTimingSlots);
+        tm.stop.resize(kTimingSlots);
+        for (int i = 0; i < kTimingSlots; ++i) {
+            if (hipEventCreate(&tm.start[i]) != hipSuccess || hipEventCreate(&tm.stop[i]) != hipSuccess)
+                return fail(ATTN_ERR_DEVICE, "timing: hipEventCreate failed");
+            tm.free_slots.push_back(kTimingSlots - 1 - i);
+        }
+        tm.created = true;
+    }
+    tm.on = on != 0;
+    return ok();
+}
+
+int attn_timing_collect(const char* kernel, double* total_ms, int64_t* launches) {
+    if (!kernel || !total_ms || !launches) return fail(ATTN_ERR_INVALID, "timing: NULL argument");
+    Timing& tm = timing();
+    std::lock_guard<std::mutex> lock(tm.mu);
+    double sum = 0.0;
+    int64_t n = 0;
+    std::vector<TimingRecord> keep;
+    for (const TimingRecord& rec : tm.records) {
+        if (strcmp(rec.name, kernel)) {
+            keep.push_back(rec);
+            continue;
+        }
+        if (hipEventSynchronize(tm.stop[rec.slot]) != hipSuccess)
+            return fail(ATTN_ERR_DEVICE, "timing: hipEventSynchronize failed");
+        float ms = 0.0f;
+        if (hipEventElapsedTime(&ms, tm.start[rec.slot], tm.stop[rec.slot]) != hipSuccess)
+            return fail(ATTN_ERR_DEVICE, "timing: hipEventElapsedTime failed");
+        sum += ms;
+        ++n;
+        tm.free_slots.push_back(rec.slot);
+    }
+    tm.records.swap(keep);
+    *total_ms = sum;
+    *launches = n;
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,421 @@
+// Decode path of op `attention`: few query rows against a long key/value
+// range (a KV cache). HBM-bound: every visible K and V row of a KV head is
+// read exactly once, for all the query rows of that head's group.
+//
+// decode_split: grid (splits, kv_heads), 256 threads. The workgroup of KV
+// head g walks its share of the key range. Its 256 lanes form 16 row groups
+// of 16 lanes (one DPP row each); a row group takes U consecutive key rows
+// at a time, and each lane of it loads a 4-float slice of every 64-float
+// stretch of the K and V rows (128-bit loads, a whole row per 16 lanes).
+// The loads of the next U rows are issued before the current ones are
+// used, so two batches are in flight per lane. Dot products are partial per
+// lane and summed across the row with DPP rotations, so every lane of the
+// row group holds every score. The score epilogue and an online softmax
+// follow, and the lane accumulates its V slice for all query rows of the
+// group. At the end the 16 row groups' partial states are merged (lane
+// shuffles, then LDS) into one (max, sum, acc) per query row and split.
+//
+// The running maximum is moved lazily: weights are taken against a
+// reference that may trail the true maximum by up to 2^8 (so a weight is at
+// most 256, far from f32 overflow), and the accumulator is rescaled only
+// when a score passes the reference by more than that. Maxima live in the
+// base-2 domain (scores times log2 e), so every exponential is one exp2.
+//
+// decode_combine: grid (T*heads), merges the splits' partial states:
+// M = max m_i, L = sum l_i 2^(m_i - M), out = sum acc_i 2^(m_i - M) / L.
+#include "device_common.h"
+
+namespace attn {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kRowGroups = kThreads / 16;
+constexpr int kWaves = kThreads / 64;
+constexpr float kLazy = 8.0f;  // log2 of the largest weight before the reference moves
+constexpr int kMaxSplits = 1024;
+
+template <int D, int DV, int NQ>
+struct DecodeShape {
+    static constexpr int KJ = D / 64;   // float4 per lane per K row
+    static constexpr int VJ = DV / 64;  // float4 per lane per V row
+    // Key rows per row group per batch. Two batches of two rows are in flight
+    // per lane (16 (KJ+VJ) registers); measured on the Llama- and
+    // latent-shaped decodes, four-row batches ran slower (more registers, no
+    // more bandwidth).
+    static constexpr int U = 2;
+};
+
+__device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ float4 zero4() { return make_float4(0.f, 0.f, 0.f, 0.f); }
+
+// Whether every query row of positions [pos_first, pos_last] sees every key
+// of [k0, k1) (graph protocol op catalogue, op `attention`, window rule).
+__device__ __forceinline__ bool chunk_all_visible(const Epilogue& e, int pos_first, int pos_last,
+                                                  int k0, int k1) {
+    if (k1 <= k0) return true;
+    if (e.causal) return k1 - 1 <= pos_first && (e.window == 0 || k0 > pos_last - e.window);
+    if (e.window == 0) return true;
+    const int d = max(max(abs(pos_first - k0), abs(pos_first - (k1 - 1))),
+                      max(abs(pos_last - k0), abs(pos_last - (k1 - 1))));
+    return d <= e.window;
+}
+
+// EPI: whether softcap, ALiBi or a bias can be on; without them the score
+// is the scaled dot product and the code for the rest is left out.
+template <int D, int DV, int NQ, bool EPI>
+__global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, DecodePlan plan,
+                                                                   float* __restrict__ ws) {
+    using Sh = DecodeShape<D, DV, NQ>;
+    constexpr int KJ = Sh::KJ, VJ = Sh::VJ, U = Sh::U;
+    constexpr int kStep = kRowGroups * U;
+
+    const int tid = threadIdx.x;
+    const int ln = tid & 15;
+    const int rg = tid >> 4;
+    const int sp = blockIdx.x;
+    const int g = blockIdx.y;
+    const int hpg = p.H / p.G;
+    const int nrows = (int)p.T * hpg;
+
+    // Query rows of this KV group: row r is query row t = r / hpg of head
+    // h = g*hpg + r % hpg. Rows past nrows are padding and never written.
+    float4 qr[NQ][KJ];
+    int pos[NQ];
+    int hh[NQ];
+    int tt[NQ];
+    bool live[NQ];
+#pragma unroll
+    for (int r = 0; r < NQ; ++r) {
+        live[r] = r < nrows;
+        tt[r] = live[r] ? r / hpg : 0;
+        hh[r] = g * hpg + (live[r] ? r % hpg : 0);
+        pos[r] = p.ep.pos_offset + tt[r];
+        const float* qrow = p.q + (int64_t)tt[r] * p.H * D + (int64_t)hh[r] * D + 4 * ln;
+#pragma unroll
+        for (int j = 0; j < KJ; ++j) qr[r][j] = live[r] ? ld4(qrow + 64 * j) : zero4();
+    }
+
+    float m[NQ], l[NQ];
+    float4 acc[NQ][VJ];
+#pragma unroll
+    for (int r = 0; r < NQ; ++r) {
+        m[r] = -INFINITY;
+        l[r] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < VJ; ++j) acc[r][j] = zero4();
+    }
+
+    const int k0 = (int)(plan.range.lo + (int64_t)sp * plan.chunk);
+    const int k1 = (int)min(plan.range.hi, (int64_t)k0 + plan.chunk);
+    // Workgroup-uniform bases; per-lane offsets stay in 32 bits (the host
+    // keeps chunk * row stride below 2^31 floats).
+    const uint32_t kstride = (uint32_t)(p.G * D), vstride = (uint32_t)(p.G * DV);
+    const float* kwg = p.k + (int64_t)k0 * kstride + (int64_t)g * D + 4 * ln;
+    const float* vwg = p.v + (int64_t)k0 * vstride + (int64_t)g * DV + 4 * ln;
+    // With every key of the chunk visible to every row, only the chunk's end
+    // needs checking.
+    const bool dense = chunk_all_visible(p.ep, p.ep.pos_offset, p.ep.pos_offset + (int)p.T - 1, k0, k1);
+
+    // Rows past the chunk's end are clamped to its last row (in bounds) and
+    // their scores masked, so the loads need no branches.
+    auto load = [&](float4 (&kf)[U][KJ], float4 (&vf)[U][VJ], int s0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t row = (uint32_t)(min(s0 + u, k1 - 1) - k0);
+#pragma unroll
+            for (int j = 0; j < KJ; ++j) kf[u][j] = load_stream4(kwg + row * kstride + 64 * j);
+#pragma unroll
+            for (int j = 0; j < VJ; ++j) vf[u][j] = load_stream4(vwg + row * vstride + 64 * j);
+        }
+    };
+
+    auto process = [&](const float4 (&kf)[U][KJ], const float4 (&vf)[U][VJ], int s0) {
+        const bool check = !(dense && s0 + U <= k1);
+        float x[NQ][U];
+#pragma unroll
+        for (int r = 0; r < NQ; ++r) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                float dot = 0.0f;
+#pragma unroll
+                for (int j = 0; j < KJ; ++j) dot = dot4(qr[r][j], kf[u][j], dot);
+                dot = row16_sum(dot);
+                const int s = s0 + u;
+                float xs;
+                if constexpr (EPI) {
+                    const int sc = min(s, k1 - 1);  // in bounds for the bias read
+                    float b = 0.0f;
+                    if (p.ep.bias_kind == ATTN_BIAS_TS) b = p.bias[(int64_t)tt[r] * p.S + sc];
+                    else if (p.ep.bias_kind == ATTN_BIAS_HTS)
+                        b = p.bias[((int64_t)hh[r] * p.T + tt[r]) * p.S + sc];
+                    xs = score_epilogue(dot, p.ep, hh[r], pos[r], s, b) * kLog2e;
+                } else {
+                    xs = dot * (p.ep.scale * kLog2e);
+                }
+                const bool vis = !check | (live[r] & (s < k1) & key_visible(p.ep, pos[r], s));
+                x[r][u] = vis ? xs : -INFINITY;
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < NQ; ++r) {
+            float mx = x[r][0];
+#pragma unroll
+            for (int u = 1; u < U; ++u) mx = fmaxf(mx, x[r][u]);
+            if (mx > m[r] + kLazy) {
+                const float alpha = fast_exp2(m[r] - mx);
+                l[r] *= alpha;
+#pragma unroll
+                for (int j = 0; j < VJ; ++j) {
+                    acc[r][j].x *= alpha; acc[r][j].y *= alpha;
+                    acc[r][j].z *= alpha; acc[r][j].w *= alpha;
+                }
+                m[r] = mx;
+            }
+            const float mu = m[r] == -INFINITY ? 0.0f : m[r];
+            float pu[U];
+            float psum = 0.0f;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                pu[u] = fast_exp2(x[r][u] - mu);
+                psum += pu[u];
+            }
+            l[r] += psum;
+#pragma unroll
+            for (int j = 0; j < VJ; ++j) {
+                float4 a = acc[r][j];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    a.x = fmaf(pu[u], vf[u][j].x, a.x);
+                    a.y = fmaf(pu[u], vf[u][j].y, a.y);
+                    a.z = fmaf(pu[u], vf[u][j].z, a.z);
+                    a.w = fmaf(pu[u], vf[u][j].w, a.w);
+                }
+                acc[r][j] = a;
+            }
+        }
+    };
+
+    {
+        float4 ka[U][KJ], va[U][VJ], kb[U][KJ], vb[U][VJ];
+        int s = k0 + rg * U;
+        if (s < k1) load(ka, va, s);
+        for (; s < k1; s += 2 * kStep) {
+            if (s + kStep < k1) load(kb, vb, s + kStep);
+            process(ka, va, s);
+            if (s + kStep >= k1) break;
+            if (s + 2 * kStep < k1) load(ka, va, s + 2 * kStep);
+            process(kb, vb, s + kStep);
+        }
+    }
+
+    // Merge the four row groups of each wave (lanes 16 and 32 apart hold the
+    // same V slice of another row group).
+#pragma unroll
+    for (int off = 16; off <= 32; off <<= 1) {
+#pragma unroll
+        for (int r = 0; r < NQ; ++r) {
+            const float mo = __shfl_xor(m[r], off, 64);
+            const float lo = __shfl_xor(l[r], off, 64);
+            const float M = fmaxf(m[r], mo);
+            const float Mu = M == -INFINITY ? 0.0f : M;
+            const float a = fast_exp2(m[r] - Mu), b = fast_exp2(mo - Mu);
+            l[r] = l[r] * a + lo * b;
+            m[r] = M;
+#pragma unroll
+            for (int j = 0; j < VJ; ++j) {
+                float4& c = acc[r][j];
+                c.x = c.x * a + __shfl_xor(c.x, off, 64) * b;
+                c.y = c.y * a + __shfl_xor(c.y, off, 64) * b;
+                c.z = c.z * a + __shfl_xor(c.z, off, 64) * b;
+                c.w = c.w * a + __shfl_xor(c.w, off, 64) * b;
+            }
+        }
+    }
+
+    // Then the four waves, through LDS.
+    __shared__ float s_m[kWaves][NQ], s_l[kWaves][NQ];
+    __shared__ float4 s_acc[kWaves][NQ][DV / 4];
+    const int wave = tid >> 6;
+    if ((tid & 63) < 16) {
+#pragma unroll
+        for (int r = 0; r < NQ; ++r) {
+            if (ln == 0) {
+                s_m[wave][r] = m[r];
+                s_l[wave][r] = l[r];
+            }
+#pragma unroll
+            for (int j = 0; j < VJ; ++j) s_acc[wave][r][j * 16 + ln] = acc[r][j];
+        }
+    }
+    __syncthreads();
+
+    const int nsplit = plan.splits;
+    float* ws_acc = ws;
+    float* ws_ml = ws + (int64_t)p.T * p.H * nsplit * DV;
+    for (int idx = tid; idx < NQ * (DV / 4); idx += kThreads) {
+        const int r = idx / (DV / 4), e4 = idx % (DV / 4);
+        if (r >= nrows) continue;
+        float M = s_m[0][r];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][r]);
+        const float Mu = M == -INFINITY ? 0.0f : M;
+        float L = 0.0f;
+        float4 A = zero4();
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float f = fast_exp2(s_m[w][r] - Mu);
+            L += s_l[w][r] * f;
+            const float4 c = s_acc[w][r][e4];
+            A.x += c.x * f; A.y += c.y * f; A.z += c.z * f; A.w += c.w * f;
+        }
+        const int64_t th = (int64_t)(r / hpg) * p.H + (g * hpg + r % hpg);
+        if (nsplit == 1) {
+            const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+            *reinterpret_cast<float4*>(p.out + th * DV + 4 * e4) =
+                make_float4(A.x * inv, A.y * inv, A.z * inv, A.w * inv);
+        } else {
+            *reinterpret_cast<float4*>(ws_acc + (th * nsplit + sp) * DV + 4 * e4) = A;
+            if (e4 == 0) {
+                ws_ml[(th * nsplit + sp) * 2 + 0] = M;
+                ws_ml[(th * nsplit + sp) * 2 + 1] = L;
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ float block_max(float x, float* red) {
+    for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+    __syncthreads();
+    x = red[0];
+    for (int w = 1; w < kWaves; ++w) x = fmaxf(x, red[w]);
+    return x;
+}
+
+__device__ __forceinline__ float block_sum(float x, float* red) {
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+    __syncthreads();
+    x = red[0];
+    for (int w = 1; w < kWaves; ++w) x += red[w];
+    return x;
+}
+
+// One workgroup per (query row, head). Every split's (max, sum) is read at
+// once, one per thread; the accumulators are read as float4 with the splits
+// spread over thread groups and summed through LDS.
+template <int DV>
+__global__ __launch_bounds__(kThreads) void decode_combine_kernel(Problem p, int nsplit,
+                                                                  const float* __restrict__ ws) {
+    constexpr int E4 = DV / 4;
+    constexpr int kGroups = kThreads / E4;
+    __shared__ float s_w[kMaxSplits];
+    __shared__ float s_red[kWaves];
+    __shared__ float4 s_part[kGroups][E4];
+
+    const int tid = threadIdx.x;
+    const int64_t th = blockIdx.x;  // t * H + h
+    const float4* acc4 = reinterpret_cast<const float4*>(ws + th * nsplit * DV);
+    const float* ml = ws + (int64_t)p.T * p.H * nsplit * DV + th * nsplit * 2;
+    float4* orow = reinterpret_cast<float4*>(p.out + th * DV);
+
+    float m = -INFINITY;
+    for (int i = tid; i < nsplit; i += kThreads) m = fmaxf(m, ml[2 * i]);
+    const float M = block_max(m, s_red);
+    if (M == -INFINITY) {  // no visible key in any split
+        for (int e = tid; e < E4; e += kThreads) orow[e] = zero4();
+        return;
+    }
+    float lsum = 0.0f;
+    for (int i = tid; i < nsplit; i += kThreads) {
+        const float w = fast_exp2(ml[2 * i] - M);
+        s_w[i] = w;
+        lsum += ml[2 * i + 1] * w;
+    }
+    const float L = block_sum(lsum, s_red);  // ends with a barrier, so s_w is complete
+
+    const int e4 = tid % E4, grp = tid / E4;
+    float4 a = zero4();
+    for (int i = grp; i < nsplit; i += kGroups) {
+        const float w = s_w[i];
+        const float4 c = acc4[(int64_t)i * E4 + e4];
+        a.x = fmaf(c.x, w, a.x); a.y = fmaf(c.y, w, a.y);
+        a.z = fmaf(c.z, w, a.z); a.w = fmaf(c.w, w, a.w);
+    }
+    s_part[grp][e4] = a;
+    __syncthreads();
+    if (grp == 0) {
+        float4 t = s_part[0][e4];
+        for (int q = 1; q < kGroups; ++q) {
+            const float4 c = s_part[q][e4];
+            t.x += c.x; t.y += c.y; t.z += c.z; t.w += c.w;
+        }
+        const float inv = 1.0f / L;
+        orow[e4] = make_float4(t.x * inv, t.y * inv, t.z * inv, t.w * inv);
+    }
+}
+
+template <int D, int DV, int NQ>
+hipError_t launch_split_t(const Problem& p, const DecodePlan& plan, float* ws, const Launch& L) {
+    const dim3 grid((unsigned)plan.splits, (unsigned)p.G);
+    const bool epi = p.ep.softcap > 0.0f || p.ep.has_alibi || p.ep.bias_kind != ATTN_BIAS_NONE;
+    if (epi) return launch_kernel(decode_split_kernel<D, DV, NQ, true>, grid, dim3(kThreads), 0, L, p, plan, ws);
+    return launch_kernel(decode_split_kernel<D, DV, NQ, false>, grid, dim3(kThreads), 0, L, p, plan, ws);
+}
+
+template <int D, int DV>
+hipError_t launch_split_nq(const Problem& p, const DecodePlan& plan, float* ws, const Launch& L) {
+    constexpr int KV = D / 64 + DV / 64;
+    switch (plan.nq) {
+        case 1: return launch_split_t<D, DV, 1>(p, plan, ws, L);
+        case 2: return launch_split_t<D, DV, 2>(p, plan, ws, L);
+        case 4:
+            if constexpr (KV <= 5) return launch_split_t<D, DV, 4>(p, plan, ws, L);
+            break;
+        case 8:
+            if constexpr (KV <= 2) return launch_split_t<D, DV, 8>(p, plan, ws, L);
+            break;
+        default: break;
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+// (D, Dv) pairs with a decode instance, and the most query rows per KV group
+// each holds in registers without spilling.
+static int decode_max_nq(int D, int Dv) {
+    if (D == 64 && Dv == 64) return 8;
+    if (D == 128 && Dv == 128) return 4;
+    if (D == 192 && Dv == 128) return 4;
+    if (D == 256 && Dv == 256) return 2;
+    return 0;
+}
+
+bool decode_supported(int D, int Dv, int nq) { return nq >= 1 && nq <= decode_max_nq(D, Dv); }
+
+hipError_t launch_decode_split(const Problem& p, const DecodePlan& plan, float* ws, const Launch& L) {
+    if (plan.splits < 1 || plan.splits > kMaxSplits) return hipErrorInvalidValue;
+    if (p.D == 64 && p.Dv == 64) return launch_split_nq<64, 64>(p, plan, ws, L);
+    if (p.D == 128 && p.Dv == 128) return launch_split_nq<128, 128>(p, plan, ws, L);
+    if (p.D == 192 && p.Dv == 128) return launch_split_nq<192, 128>(p, plan, ws, L);
+    if (p.D == 256 && p.Dv == 256) return launch_split_nq<256, 256>(p, plan, ws, L);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_combine(const Problem& p, const DecodePlan& plan, const float* ws,
+                                 const Launch& L) {
+    if (plan.splits < 1 || plan.splits > kMaxSplits) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)(p.T * p.H)), block(kThreads);
+    switch (p.Dv) {
+        case 64: return launch_kernel(decode_combine_kernel<64>, grid, block, 0, L, p, plan.splits, ws);
+        case 128: return launch_kernel(decode_combine_kernel<128>, grid, block, 0, L, p, plan.splits, ws);
+        case 256: return launch_kernel(decode_combine_kernel<256>, grid, block, 0, L, p, plan.splits, ws);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace attn

@@ -1,0 +1,79 @@
+// Device-side pieces shared by the attention kernels: the visibility rule,
+// the score epilogue and a few CDNA lane-exchange helpers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.h"
+
+namespace attn {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Graph protocol op catalogue, op `attention`, params causal and window:
+// causal keys are visible when pos - window < s <= pos, non-causal keys when
+// |pos - s| <= window; window 0 means no window.
+// Positions are non-negative and below 2^31, so none of this overflows.
+__device__ __forceinline__ bool key_visible(const Epilogue& e, int pos, int s) {
+    if (e.causal) return s <= pos && (e.window == 0 || s > pos - e.window);
+    if (e.window == 0) return true;
+    return abs(pos - s) <= e.window;
+}
+
+// The score of one visible (query, key) pair, in the order the op fixes:
+// scale the dot product, softcap it (feature attention.softcap: before the
+// mask), then add the ALiBi penalty -slope*|pos - s| and the bias input.
+__device__ __forceinline__ float score_epilogue(float dot, const Epilogue& e, int h, int pos, int s,
+                                                float bias) {
+    float x = dot * e.scale;
+    if (e.softcap > 0.0f) x = e.softcap * tanhf(x * e.inv_softcap);
+    if (e.has_alibi) x -= e.slopes[h] * (float)abs(pos - s);
+    return x + bias;
+}
+
+// 2^x with the hardware exponential (v_exp_f32; about 1 ulp). Inputs here are
+// differences from a running maximum, so results below 2^-126 are weights
+// too small to matter.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// A 128-bit load that bypasses the caches' normal retention: K and V rows
+// are read once per call, so keeping them would only evict other data.
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 load_stream4(const float* p) {
+    const f32x4_t t = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
+    return make_float4(t.x, t.y, t.z, t.w);
+}
+
+// Row-of-16 all-reduce with DPP row rotations: after the four steps every
+// lane of each 16-lane DPP row holds the row's sum.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float row16_sum(float x) {
+    x += dpp_f32<0x128>(x);  // row_ror:8
+    x += dpp_f32<0x124>(x);  // row_ror:4
+    x += dpp_f32<0x122>(x);  // row_ror:2
+    x += dpp_f32<0x121>(x);  // row_ror:1
+    return x;
+}
+
+__device__ __forceinline__ float row16_max(float x) {
+    x = fmaxf(x, dpp_f32<0x128>(x));
+    x = fmaxf(x, dpp_f32<0x124>(x));
+    x = fmaxf(x, dpp_f32<0x122>(x));
+    x = fmaxf(x, dpp_f32<0x121>(x));
+    return x;
+}
+
+__device__ __forceinline__ float dot4(const float4& a, const float4& b, float acc) {
+    acc = fmaf(a.x, b.x, acc);
+    acc = fmaf(a.y, b.y, acc);
+    acc = fmaf(a.z, b.z, acc);
+    acc = fmaf(a.w, b.w, acc);
+    return acc;
+}
+
+}  // namespace attn

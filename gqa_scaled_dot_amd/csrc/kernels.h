@@ -1,0 +1,83 @@
+// Internal interface between the host dispatch (attn_api.hip) and the HIP
+// kernels. Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "attn.h"
+
+namespace attn {
+
+// Everything the score epilogue needs (op `attention`: scale, softcap,
+// ALiBi, bias, causal/window mask), resolved on the host.
+struct Epilogue {
+    float scale;        // multiplies q.k
+    float softcap;      // 0: off
+    float inv_softcap;  // 1/softcap when on
+    int32_t causal;
+    int32_t has_alibi;
+    int32_t bias_kind;  // ATTN_BIAS_*
+    int32_t pos_offset; // positions are below 2^31 (checked on the host)
+    int32_t window;     // 0: off
+    float slopes[ATTN_ALIBI_MAX_HEADS];
+};
+
+struct Problem {
+    const float* q;
+    const float* k;
+    const float* v;
+    const float* bias;
+    float* out;
+    int64_t T, S;
+    int32_t H, G, D, Dv;
+    Epilogue ep;
+};
+
+// Key rows [lo, hi) that any query row of the call can see. Rows outside
+// are never read (a KV cache past the current position may hold anything).
+struct KeyRange {
+    int64_t lo, hi;
+};
+
+struct DecodePlan {
+    int32_t nq;       // query rows per KV group this instance holds (template value)
+    int32_t splits;   // key-range splits per KV group
+    int64_t chunk;    // keys per split (multiple of the row-group step)
+    KeyRange range;
+};
+
+struct PrefillPlan {
+    int32_t tile_q;   // query rows per workgroup
+    int32_t tile_k;   // key rows per LDS tile
+};
+
+// Where and how one kernel launch goes: the caller's stream, and optionally
+// a pair of events that the dispatch itself stamps with the kernel's start
+// and end (hipExtLaunchKernel), used only when timing is switched on.
+struct Launch {
+    hipStream_t stream;
+    hipEvent_t start;
+    hipEvent_t stop;
+};
+
+template <typename... KArgs, typename... Args>
+inline hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32_t lds,
+                                const Launch& L, Args... args) {
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, L.stream, L.start, L.stop, 0, args...);
+    return hipGetLastError();
+}
+
+// Launchers. Each returns hipSuccess or the launch error.
+hipError_t launch_cache_write(float* dst, const float* src, int64_t count, const Launch& L);
+hipError_t launch_zero_fill(float* dst, int64_t count, const Launch& L);
+hipError_t launch_generic(const Problem& p, const Launch& L);
+bool decode_supported(int D, int Dv, int nq);
+hipError_t launch_decode_split(const Problem& p, const DecodePlan& plan, float* ws, const Launch& L);
+hipError_t launch_decode_combine(const Problem& p, const DecodePlan& plan, const float* ws,
+                                 const Launch& L);
+bool prefill_supported(int D, int Dv);
+hipError_t launch_prefill(const Problem& p, const PrefillPlan& plan, const Launch& L);
+
+}  // namespace attn

@@ -1,0 +1,203 @@
+/*
+ * attn.h - f32 grouped-query scaled dot-product attention on MI355X (gfx950).
+ *
+ * The C ABI of libattn.so. It implements two ops of the graph protocol's op
+ * catalogue (page "https://vtmu.mpakt.dev/api/ops"):
+ *
+ *   attention    "Scaled dot-product attention with grouped-query support";
+ *                q, k and v are flat row-major f32, the score matrix is never
+ *                written to memory (op `attention`: summary, inputs, params,
+ *                features attention.alibi/.bias/.scale/.softcap/.window).
+ *   cache_write  writes rows into a preallocated cache in place (op
+ *                `cache_write`: inputs cache [maxRows, width] and values
+ *                [rows, width], param offset, mutatesInput 0).
+ *
+ * Conventions for every entry point:
+ *   - Tensors are dense row-major f32 (catalogue convention: tensors are
+ *     row-major f32), passed as DEVICE pointers that the caller owns. The
+ *     library keeps no pointer after a call returns, allocates nothing,
+ *     copies nothing between host and device and never synchronises.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream)
+ *     and runs asynchronously: a device fault shows at the caller's next
+ *     synchronisation, not in the return code.
+ *   - Every argument is checked before anything is launched, so a call that
+ *     returns an error has written nothing. Errors name the parameter or the
+ *     feature, following the catalogue's rule that a graph needing a missing
+ *     feature is refused with the feature named; attn_last_error() returns
+ *     that text for the calling thread.
+ *   - Calls that write overlapping memory on one stream are ordered by the
+ *     stream; on different streams they race.
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define ATTN_OK 0
+#define ATTN_ERR_INVALID 1     /* a shape, size, pointer or parameter value is wrong */
+#define ATTN_ERR_UNSUPPORTED 2 /* a valid request this library has no kernel for */
+#define ATTN_ERR_DEVICE 3      /* the HIP runtime refused a launch */
+
+/* attn_params.alibi: which ALiBi slope table (op `attention`, params alibi,
+ * alibiMax, alibiSlopes; feature attention.alibi). */
+#define ATTN_ALIBI_NONE 0
+#define ATTN_ALIBI_BLOOM 1    /* `alibi: true`: BLOOM / ALiBi-paper slopes */
+#define ATTN_ALIBI_MPT 2      /* `alibiMax`: MPT slopes with alibi_bias_max = alibi_max */
+#define ATTN_ALIBI_EXPLICIT 3 /* `alibiSlopes`: alibi_slopes[heads], host memory */
+#define ATTN_ALIBI_MAX_HEADS 256
+
+/* attn_params.bias_kind: the optional fourth input (feature attention.bias). */
+#define ATTN_BIAS_NONE 0
+#define ATTN_BIAS_TS 1  /* bias [T, S], shared by all heads */
+#define ATTN_BIAS_HTS 2 /* bias [heads, T, S] */
+
+/*
+ * One field per parameter of the catalogue's `attention` op. Call
+ * attn_params_init() first: it sets every optional field to "absent".
+ *
+ *   T, S         query rows and key/value rows (>= 0).
+ *   heads        num_attention_heads (> 0).
+ *   kv_heads     num_key_value_heads; 0 = absent = heads. heads must be a
+ *                multiple of it; query head h reads key/value head
+ *                floor(h * kv_heads / heads) (contiguous groups).
+ *   head_dim     query/key width per head (> 0).
+ *   v_head_dim   value width per head; 0 = absent = head_dim.
+ *   causal       default 1. Causal: key s is visible to query row t when
+ *                s <= pos with pos = pos_offset + t.
+ *   pos_offset   absolute position of the first query row (>= 0, default 0);
+ *                key row s sits at position s. With a KV cache, k and v are
+ *                the whole caches (S = maxRows) and causal masking hides the
+ *                rows past the current position, which are never read.
+ *   has_scale, scale
+ *                the score scale; absent = 1/sqrt(head_dim). It multiplies
+ *                q.k only, never the ALiBi or bias terms.
+ *   softcap      0 = off, > 0: x = softcap * tanh(x / softcap), applied to the
+ *                scaled score before ALiBi, bias and the mask (feature
+ *                attention.softcap: "before the mask").
+ *   window       0 = off, > 0: sliding window. Causal: pos - window < s <= pos.
+ *                Non-causal: |pos - s| <= window.
+ *   alibi, alibi_max, alibi_slopes
+ *                ALiBi; adds -slope[h] * |pos - s| to the score. alibi_slopes
+ *                is a HOST pointer to `heads` floats, read during the call and
+ *                not kept. At most ATTN_ALIBI_MAX_HEADS heads.
+ *   bias_kind    ATTN_BIAS_*; the bias is added after softcap and ALiBi (a
+ *                -1e9 entry masks its key, as the catalogue suggests).
+ *
+ * A query row with no visible key outputs zeros.
+ */
+typedef struct attn_params {
+    int64_t T, S;
+    int64_t heads, kv_heads;
+    int64_t head_dim, v_head_dim;
+    int64_t pos_offset;
+    int64_t window;
+    int32_t causal;
+    int32_t has_scale;
+    float scale;
+    float softcap;
+    int32_t alibi;
+    float alibi_max;
+    const float* alibi_slopes;
+    int32_t bias_kind;
+    int32_t reserved;
+} attn_params;
+
+/* Fill *p with the catalogue's defaults: causal = 1, everything optional
+ * absent, sizes 0. */
+void attn_params_init(attn_params* p);
+
+/* Check *p without touching any device: ATTN_OK, ATTN_ERR_INVALID or
+ * ATTN_ERR_UNSUPPORTED, with attn_last_error() naming the field. */
+int attn_validate(const attn_params* p);
+
+/* Bytes of device workspace attn_forward needs for *p (0 if none; also 0
+ * for an invalid *p). The workspace holds per-split partial softmax state. */
+size_t attn_workspace_size(const attn_params* p);
+
+/*
+ * out[T, heads*v_head_dim] = attention(q, k, v, bias) (op `attention`).
+ *   q    [T, heads*head_dim]        device, read-only
+ *   k    [S, kv_heads*head_dim]     device, read-only
+ *   v    [S, kv_heads*v_head_dim]   device, read-only
+ *   bias [T, S] or [heads, T, S]    device, read-only; NULL iff bias_kind = 0
+ *   out  [T, heads*v_head_dim]      device, written; must not overlap inputs
+ *   workspace, workspace_bytes
+ *        device scratch of at least attn_workspace_size(p) bytes (NULL when
+ *        that is 0), 256-byte aligned; its contents need no initialisation
+ *        and mean nothing after the call. Two calls in flight at once must
+ *        not share a workspace.
+ * q, k, v, bias and out must be 16-byte aligned. T = 0 is a no-op; S = 0
+ * writes zeros.
+ */
+int attn_forward(const attn_params* p, const float* q, const float* k, const float* v,
+                 const float* bias, float* out, void* workspace, size_t workspace_bytes,
+                 void* stream);
+
+/*
+ * Op `cache_write`: cache[offset + r, :] = values[r, :] for r < rows, in
+ * place; the rest of the cache is untouched. An exact bit copy.
+ *   cache   [max_rows, width]  device, written
+ *   values  [rows, width]      device, read-only; must not overlap the rows
+ *                              being written
+ * Requires 0 <= offset and offset + rows <= max_rows. rows = 0 is a no-op.
+ */
+int attn_cache_write(float* cache, int64_t max_rows, int64_t width, const float* values,
+                     int64_t rows, int64_t offset, void* stream);
+
+/* Text of the calling thread's last error ("" if the last call succeeded). */
+const char* attn_last_error(void);
+
+/*
+ * Which kernels attn_forward would launch for *p (host only). Lets tests
+ * and measurement tools name the path; not needed to run the op.
+ *   path    ATTN_PATH_*
+ *   splits  key-range splits of the decode path (1 elsewhere)
+ *   tile_q  query rows per workgroup on the prefill path
+ */
+#define ATTN_PATH_EMPTY 0   /* T = 0 or no work */
+#define ATTN_PATH_ZERO 1    /* S = 0: zero fill */
+#define ATTN_PATH_GENERIC 2 /* any shape; correctness path */
+#define ATTN_PATH_DECODE 3  /* few query rows: split-S + combine */
+#define ATTN_PATH_PREFILL 4 /* fp32 MFMA flash kernel */
+typedef struct attn_plan_info {
+    int32_t path;
+    int32_t splits;
+    int32_t tile_q;
+    int32_t reserved;
+} attn_plan_info;
+int attn_plan(const attn_params* p, attn_plan_info* info);
+
+/*
+ * Tuning overrides for tests and sweeps (process-wide, not thread-safe):
+ *   "decode_splits"  force the decode split count (0 = automatic)
+ *   "force_path"     force ATTN_PATH_GENERIC / _DECODE / _PREFILL (0 = automatic);
+ *                    a forced path that cannot serve *p is refused
+ * Returns ATTN_ERR_INVALID for an unknown name.
+ */
+int attn_set_option(const char* name, int64_t value);
+
+/*
+ * Kernel timing for measurement harnesses. While enabled, every kernel the
+ * library launches is bracketed by a pair of HIP events recorded on the
+ * stream it runs on. attn_timing_collect() waits for the recorded events and
+ * returns, for the kernel named `kernel`, the summed duration and the launch
+ * count since the last collect (then clears them). Off by default; the hot
+ * path records nothing when off. Event pairs come from a fixed pool of 4096,
+ * created on the first enable; launches beyond the pool are not timed.
+ * Kernel names: "cache_write", "decode_split", "decode_combine", "prefill",
+ * "generic", "zero_fill".
+ */
+int attn_timing_enable(int on);
+int attn_timing_collect(const char* kernel, double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */

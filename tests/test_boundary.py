@@ -1,0 +1,183 @@
+"""The C-ABI boundary, checked on the CPU (no device calls).
+
+The library must load, export every entry point include/attn.h declares,
+resolve the op's defaults, and refuse bad arguments by name before any
+launch (the catalogue refuses a graph "with the feature named").
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import gqa_scaled_dot_amd as ga
+from gqa_scaled_dot_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = set(re.findall(r"\b(attn_[a-z_]+)\s*\(", text))
+    return sorted(names)
+
+
+def test_header_declares_the_binding_exports():
+    assert set(_declared_functions()) == set(_lib.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib.lib()
+    for name in _declared_functions():
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (attn_\w+)", out))
+    assert set(_declared_functions()) <= exported
+
+
+def test_params_init_defaults():
+    p = _lib.AttnParams()
+    ctypes.memset(ctypes.byref(p), 0xFF, ctypes.sizeof(p))
+    _lib.lib().attn_params_init(ctypes.byref(p))
+    assert p.causal == 1
+    assert (p.T, p.S, p.heads, p.kv_heads, p.head_dim, p.v_head_dim) == (0, 0, 0, 0, 0, 0)
+    assert (p.pos_offset, p.window, p.has_scale, p.softcap, p.alibi, p.bias_kind) == (0, 0, 0, 0, 0, 0)
+    assert not p.alibi_slopes
+
+
+BASE = dict(heads=8, kvHeads=2, headDim=64)
+
+
+@pytest.mark.parametrize("bad, code, word", [
+    (dict(heads=0), 1, "heads"),
+    (dict(kvHeads=3), 1, "kvHeads"),
+    (dict(kvHeads=16), 1, "kvHeads"),
+    (dict(headDim=0), 1, "headDim"),
+    (dict(vHeadDim=-1), 1, "vHeadDim"),
+    (dict(posOffset=-1), 1, "posOffset"),
+    (dict(window=-1), 1, "window"),
+    (dict(softcap=-1.0), 1, "softcap"),
+    (dict(softcap=float("inf")), 1, "softcap"),
+    (dict(softcap=float("nan")), 1, "softcap"),
+    (dict(scale=float("nan")), 1, "scale"),
+    (dict(alibiMax=0.0), 1, "alibiMax"),
+    (dict(alibiSlopes=[0.5] * 3), 1, "alibiSlopes"),
+    (dict(alibiSlopes=[float("inf")] * 8), 1, "alibiSlopes"),
+    (dict(heads=512, kvHeads=512, alibi=True), 2, "attention.alibi"),
+])
+def test_invalid_params_are_named(bad, code, word):
+    kw = dict(BASE)
+    kw.update(bad)
+    with pytest.raises(ga.AttnError) as ei:
+        ga.attn_validate(4, 16, **kw)
+    assert ei.value.code == code
+    assert word in ei.value.message
+
+
+def test_negative_sizes_and_bad_bias_kind():
+    for T, S in ((-1, 4), (4, -1)):
+        with pytest.raises(ga.AttnError) as ei:
+            ga.attn_validate(T, S, **BASE)
+        assert ei.value.code == 1
+    with pytest.raises(ga.AttnError) as ei:
+        ga.attn_validate(4, 4, bias_kind=3, **BASE)
+    assert "bias" in ei.value.message
+
+
+def test_valid_params_pass_and_clear_the_error():
+    with pytest.raises(ga.AttnError):
+        ga.attn_validate(4, 16, heads=0, headDim=8)
+    ga.attn_validate(4, 16, **BASE)
+    assert ga.attn_last_error() == ""
+
+
+def test_plans():
+    dec = ga.attn_plan(1, 32768, heads=32, kvHeads=8, headDim=128, posOffset=32767)
+    assert dec["path"] == "decode" and dec["splits"] > 1
+    assert ga.attn_plan(0, 16, **BASE)["path"] == "empty"
+    assert ga.attn_plan(4, 0, **BASE)["path"] == "zero"
+    # Every row's window lies past the keys: nothing visible, zero fill.
+    assert ga.attn_plan(2, 4, posOffset=10, window=2, **BASE)["path"] == "zero"
+    # Odd widths have no tuned kernel.
+    assert ga.attn_plan(8, 8, heads=4, kvHeads=2, headDim=16)["path"] == "generic"
+    assert ga.attn_plan(3, 9, heads=2, headDim=3, vHeadDim=5)["path"] == "generic"
+
+
+def test_decode_workspace_matches_plan():
+    kw = dict(heads=32, kvHeads=8, headDim=128, posOffset=32767)
+    plan = ga.attn_plan(1, 32768, **kw)
+    assert ga.attn_workspace_size(1, 32768, **kw) == 4 * 32 * plan["splits"] * (128 + 2)
+    assert ga.attn_workspace_size(8, 8, heads=4, kvHeads=2, headDim=16) == 0
+
+
+def test_options():
+    kw = dict(heads=32, kvHeads=8, headDim=128, posOffset=32767)
+    try:
+        ga.attn_set_option("decode_splits", 7)
+        assert ga.attn_plan(1, 32768, **kw)["splits"] == 7
+        ga.attn_set_option("force_path", _lib.ATTN_PATH_GENERIC)
+        assert ga.attn_plan(1, 32768, **kw)["path"] == "generic"
+    finally:
+        ga.attn_set_option("decode_splits", 0)
+        ga.attn_set_option("force_path", 0)
+    with pytest.raises(ga.AttnError):
+        ga.attn_set_option("no_such_option", 1)
+    with pytest.raises(ga.AttnError):
+        ga.attn_set_option("force_path", 99)
+
+
+def _forward_raw(p, q, k, v, bias, out, ws=None, ws_bytes=0):
+    return _lib.lib().attn_forward(ctypes.byref(p), q, k, v, bias, out, ws, ws_bytes, None)
+
+
+def test_forward_refuses_before_launch():
+    # Fake, never-dereferenced addresses: every case is refused on the host.
+    L = _lib.lib()
+    p, _ = ga.make_params(4, 16, **BASE)
+    A = 1 << 32
+    q, k, v, out = A, 2 * A, 3 * A, 4 * A
+    assert _forward_raw(p, q, k, v, None, None) == 1 and "out" in ga.attn_last_error()
+    assert _forward_raw(p, None, k, v, None, out) == 1 and "q" in ga.attn_last_error()
+    assert _forward_raw(p, q, None, v, None, out) == 1 and "k" in ga.attn_last_error()
+    assert _forward_raw(p, q, k, v, 5 * A, out) == 1 and "bias" in ga.attn_last_error()
+    assert _forward_raw(p, q + 4, k, v, None, out) == 1 and "aligned" in ga.attn_last_error()
+    assert _forward_raw(p, q, k, v, None, q + 64) == 1 and "overlaps" in ga.attn_last_error()
+    pb, _ = ga.make_params(4, 16, bias_kind=2, **BASE)
+    assert _forward_raw(pb, q, k, v, None, out) == 1 and "bias" in ga.attn_last_error()
+    # Decode shapes need a workspace.
+    pd, _ = ga.make_params(1, 32768, heads=32, kvHeads=8, headDim=128, posOffset=32767)
+    assert _forward_raw(pd, q, k, v, None, out) == 1 and "workspace" in ga.attn_last_error()
+    assert _forward_raw(pd, q, k, v, None, out, 5 * A + 8, 1 << 30) == 1
+    assert "aligned" in ga.attn_last_error()
+    # T = 0 is a no-op that succeeds without touching anything.
+    p0, _ = ga.make_params(0, 16, **BASE)
+    assert _forward_raw(p0, None, None, None, None, None) == 0
+    del L
+
+
+def test_cache_write_refuses_before_launch():
+    L = _lib.lib()
+    A = 1 << 20
+    assert L.attn_cache_write(A, 10, 4, 2 * A, 3, 8, None) == 1
+    assert "offset" in ga.attn_last_error()
+    assert L.attn_cache_write(A, 10, 4, 2 * A, 1, -1, None) == 1
+    assert L.attn_cache_write(A, 10, 0, 2 * A, 1, 0, None) == 1
+    assert "width" in ga.attn_last_error()
+    assert L.attn_cache_write(A, 10, 4, 2 * A, -1, 0, None) == 1
+    assert L.attn_cache_write(None, 10, 4, 2 * A, 1, 0, None) == 1
+    assert "cache" in ga.attn_last_error()
+    assert L.attn_cache_write(A, 10, 4, A + 16, 2, 1, None) == 1
+    assert "overlap" in ga.attn_last_error()
+    assert L.attn_cache_write(A, 10, 4, 2 * A, 0, 10, None) == 0  # rows = 0: no-op
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 64)
+    with pytest.raises(ValueError):
+        ga.attn_forward(q, q, q, heads=1, headDim=64)
