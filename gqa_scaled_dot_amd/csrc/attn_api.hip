@@ -262,8 +262,13 @@ int make_plan(const Resolved& r, Plan* plan) {
             plan->workspace = sizeof(float) * (size_t)(r.T * r.H) * (size_t)d.splits * (size_t)(r.Dv + 2);
     }
     if (path == ATTN_PATH_PREFILL) {
-        plan->prefill.tile_q = 128;
+        // Four waves of 32 query rows; heads of a KV group side by side
+        // (up to 4), the rest of the workgroup's waves on further query rows.
+        const int64_t nh = hpg % 4 == 0 ? 4 : (hpg % 2 == 0 ? 2 : 1);
+        plan->prefill.tile_q = (int32_t)(4 / nh * 32);
         plan->prefill.tile_k = 32;
+        if (r.G * (hpg / nh) > 65535)
+            return fail(ATTN_ERR_UNSUPPORTED, "kvHeads: too many heads for the prefill grid");
     }
     return ok();
 }

@@ -1,12 +1,366 @@
-// Prefill path of op `attention` (fp32 MFMA flash kernel): not built yet;
-// every shape goes to the decode or generic path until it is.
-#include "kernels.h"
+// Prefill path of op `attention`: many query rows, flash-style, with both
+// contractions on fp32 matrix cores (v_mfma_f32_32x32x2f32).
+//
+// A workgroup is 4 waves; each wave owns 32 query rows of one head, and the
+// waves of a workgroup share one KV head (heads of the same group side by
+// side, or consecutive query blocks of one head). K and V tiles of 32 key rows
+// are staged in LDS (double-buffered; the next tile's global loads are in
+// flight while the current one is used) and read by all four waves.
+//
+// Lane layouts of v_mfma_f32_32x32x2f32 (A 32x2, B 2x32, D 32x32, 64 lanes):
+// A[i][k] sits in lane i + 32k, B[k][j] in lane j + 32k, and D[i][j] in lane
+// j + 32*((i/4)%2), register 4*(i/8) + i%4.
+//
+// Scores are formed transposed, S^T = K Q^T, so a lane holds one query
+// (column l%32) and 16 keys. That accumulator is then used as it stands as
+// the B operand of O^T = V^T P^T: register r of lane l is P^T[key f(r, l/32)]
+// [query l%32] with f(r, h) = 8(r/4) + 4h + r%4, and the V operand is read
+// for exactly those keys. No score ever moves between lanes, and the score
+// matrix never leaves registers.
+//
+// Contraction orders are chosen for wide LDS reads: in QK^T, k-step kk of
+// half h uses d = h*D/2 + kk, so a lane reads D/2 consecutive floats of its
+// key row (and holds the matching D/2 of its query row in registers); in PV,
+// row i of output block b is dv = (DV/32) i + b, so a lane reads DV/32
+// consecutive floats of a V row per k-step and writes DV/32 consecutive
+// output floats per accumulator register.
+//
+// Online softmax per query in the base-2 domain with a lazily moved
+// reference maximum (as in the decode path). Key tiles a workgroup cannot see
+// are skipped; tiles that every query of a wave sees skip the mask. Rows of a
+// tile outside the workgroup's visible key range are zero-filled, never read.
+#include "device_common.h"
 
 namespace attn {
 
-bool prefill_supported(int, int) { return false; }
+namespace {
 
-hipError_t launch_prefill(const Problem&, const PrefillPlan&, const Launch&) {
+constexpr int kThreads = 256;
+constexpr int kWaves = 4;
+constexpr int kBQ = 32;  // query rows per wave
+constexpr int kBK = 32;  // key rows per tile
+constexpr int kPad = 4;  // floats of padding per LDS row (bank spread)
+constexpr float kLazy = 8.0f;
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ f32x16 mfma32(float a, float b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// NB consecutive floats from LDS (NB = 2 or a multiple of 4).
+template <int NB>
+__device__ __forceinline__ void lds_read(const float* src, float (&dst)[NB]) {
+    if constexpr (NB % 4 == 0) {
+#pragma unroll
+        for (int b = 0; b < NB; b += 4) {
+            const float4 w = *reinterpret_cast<const float4*>(src + b);
+            dst[b] = w.x;
+            dst[b + 1] = w.y;
+            dst[b + 2] = w.z;
+            dst[b + 3] = w.w;
+        }
+    } else {
+        static_assert(NB == 2, "vHeadDim must be 64 or a multiple of 128");
+        const float2 w = *reinterpret_cast<const float2*>(src);
+        dst[0] = w.x;
+        dst[1] = w.y;
+    }
+}
+
+// Waves per SIMD the register budget allows (two while q, o and staging fit
+// in 256 registers per lane).
+constexpr int prefill_min_waves(int D, int DV) { return D + DV <= 256 ? 2 : 1; }
+
+template <int D, int DV>
+struct PrefillShape {
+    static constexpr int KLD = D + kPad;    // LDS row stride of a K tile
+    static constexpr int VLD = DV + kPad;   // LDS row stride of a V tile
+    static constexpr int KF4 = kBK * D / 4 / kThreads;   // float4 per thread per K tile
+    static constexpr int VF4 = kBK * DV / 4 / kThreads;  // float4 per thread per V tile
+    static constexpr int NB = DV / 32;      // output blocks (and V floats per lane per k-step)
+    static constexpr size_t lds_bytes = sizeof(float) * 2 * kBK * (size_t)(KLD + VLD);
+};
+
+// Workgroup layout chosen on the host: nh heads of one KV group side by side,
+// each with 4/nh consecutive 32-row query blocks.
+struct PrefillArgs {
+    int nh;        // heads per workgroup (1, 2 or 4)
+    int hgroups;   // head groups per KV head = (heads/kvHeads) / nh
+    int qblocks;   // workgroups along the query rows
+    int causal_order;  // 1: heaviest query blocks first
+};
+
+template <int D, int DV, bool EPI>
+__global__ __launch_bounds__(kThreads, prefill_min_waves(D, DV)) void prefill_kernel(
+    Problem p, PrefillArgs a) {
+    using Sh = PrefillShape<D, DV>;
+    constexpr int KLD = Sh::KLD, VLD = Sh::VLD, NB = Sh::NB;
+    extern __shared__ float lds[];
+    float* ktile = lds;                       // [2][kBK][KLD]
+    float* vtile = lds + 2 * kBK * KLD;       // [2][kBK][VLD]
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int half = lane >> 5;
+    const int col = lane & 31;
+
+    const int hpg = p.H / p.G;
+    const int qsub = kWaves / a.nh;
+    const int qb = a.causal_order ? (a.qblocks - 1 - (int)blockIdx.x) : (int)blockIdx.x;
+    const int g = (int)blockIdx.y / a.hgroups;
+    const int hgi = (int)blockIdx.y % a.hgroups;
+    const int h = g * hpg + hgi * a.nh + wave % a.nh;
+    const int qwg0 = qb * qsub * kBQ;                 // first query row of the workgroup
+    const int q0 = qwg0 + (wave / a.nh) * kBQ;        // first query row of this wave
+    const int T = (int)p.T, S = (int)p.S;
+    const int t = q0 + col;                           // this lane's query row
+    const bool trow = t < T;
+    const int pos = p.ep.pos_offset + t;
+
+    // This lane's half of its query row: q[t, h*D + half*D/2 + kk], kk < D/2.
+    float qreg[D / 2];
+    {
+        const float* qrow = p.q + (int64_t)t * p.H * D + (int64_t)h * D + half * (D / 2);
+#pragma unroll
+        for (int kk = 0; kk < D / 2; kk += 4) {
+            const float4 v = trow ? *reinterpret_cast<const float4*>(qrow + kk) : make_float4(0.f, 0.f, 0.f, 0.f);
+            qreg[kk] = v.x;
+            qreg[kk + 1] = v.y;
+            qreg[kk + 2] = v.z;
+            qreg[kk + 3] = v.w;
+        }
+    }
+
+    // Keys any query row of the workgroup can see.
+    const int wg_last = min(qwg0 + qsub * kBQ, T) - 1;
+    const int pf = p.ep.pos_offset + qwg0, pl = p.ep.pos_offset + wg_last;
+    int klo = 0, khi = S;
+    if (p.ep.causal) {
+        khi = min(S, pl + 1);
+        if (p.ep.window > 0) klo = max(0, pf - p.ep.window + 1);
+    } else if (p.ep.window > 0) {
+        klo = max(0, pf - p.ep.window);
+        khi = min(S, pl + p.ep.window + 1);
+    }
+    // This wave's own query positions (for whole-tile visibility checks).
+    const int wq_last = min(q0 + kBQ, T) - 1;
+    const int wpf = p.ep.pos_offset + q0, wpl = p.ep.pos_offset + max(wq_last, q0);
+
+    f32x16 o[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[b][r] = 0.0f;
+    float m = -INFINITY, l = 0.0f;
+
+    const int kt0 = klo / kBK;
+    const int kt1 = khi > klo ? (khi + kBK - 1) / kBK : kt0;
+    const int64_t kstride = (int64_t)p.G * D, vstride = (int64_t)p.G * DV;
+    const float* kg = p.k + (int64_t)g * D;
+    const float* vg = p.v + (int64_t)g * DV;
+
+    // Global -> registers -> LDS staging of one K/V tile.
+    float4 kst[Sh::KF4], vst[Sh::VF4];
+    auto fetch = [&](int kt) {
+#pragma unroll
+        for (int j = 0; j < Sh::KF4; ++j) {
+            const int f = tid + j * kThreads;
+            const int row = f / (D / 4), c4 = f % (D / 4);
+            const int s = kt * kBK + row;
+            kst[j] = (s >= klo && s < khi) ? *reinterpret_cast<const float4*>(kg + s * kstride + 4 * c4)
+                                           : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+#pragma unroll
+        for (int j = 0; j < Sh::VF4; ++j) {
+            const int f = tid + j * kThreads;
+            const int row = f / (DV / 4), c4 = f % (DV / 4);
+            const int s = kt * kBK + row;
+            vst[j] = (s >= klo && s < khi) ? *reinterpret_cast<const float4*>(vg + s * vstride + 4 * c4)
+                                           : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    };
+    auto stage = [&](int buf) {
+        float* kt_ = ktile + buf * kBK * KLD;
+        float* vt_ = vtile + buf * kBK * VLD;
+#pragma unroll
+        for (int j = 0; j < Sh::KF4; ++j) {
+            const int f = tid + j * kThreads;
+            const int row = f / (D / 4), c4 = f % (D / 4);
+            *reinterpret_cast<float4*>(kt_ + row * KLD + 4 * c4) = kst[j];
+        }
+#pragma unroll
+        for (int j = 0; j < Sh::VF4; ++j) {
+            const int f = tid + j * kThreads;
+            const int row = f / (DV / 4), c4 = f % (DV / 4);
+            *reinterpret_cast<float4*>(vt_ + row * VLD + 4 * c4) = vst[j];
+        }
+    };
+
+    const float qk_scale = p.ep.scale * kLog2e;
+    if (kt0 < kt1) {
+        fetch(kt0);
+        stage(0);
+    }
+    for (int kt = kt0; kt < kt1; ++kt) {
+        const int buf = (kt - kt0) & 1;
+        __syncthreads();  // tile `kt` is in LDS; everyone is done with the other buffer
+        if (kt + 1 < kt1) fetch(kt + 1);
+
+        const int s_first = kt * kBK, s_last = s_first + kBK - 1;
+        // Does any query of this wave see any key of the tile?
+        bool any_vis;
+        bool all_vis;
+        if (p.ep.causal) {
+            any_vis = s_first <= wpl && (p.ep.window == 0 || s_last > wpf - p.ep.window);
+            all_vis = s_last <= wpf && (p.ep.window == 0 || s_first > wpl - p.ep.window);
+        } else if (p.ep.window > 0) {
+            any_vis = s_first <= wpl + p.ep.window && s_last >= wpf - p.ep.window;
+            all_vis = max(max(abs(wpf - s_first), abs(wpf - s_last)),
+                          max(abs(wpl - s_first), abs(wpl - s_last))) <= p.ep.window;
+        } else {
+            any_vis = true;
+            all_vis = true;
+        }
+        all_vis = all_vis && s_first >= klo && s_last < khi;
+
+        if (any_vis) {
+            const float* kt_ = ktile + buf * kBK * KLD;
+            const float* vt_ = vtile + buf * kBK * VLD;
+            // S^T = K Q^T for 32 keys x 32 queries.
+            f32x16 sacc;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[r] = 0.0f;
+            const float* krow = kt_ + col * KLD + half * (D / 2);
+#pragma unroll
+            for (int kk = 0; kk < D / 2; kk += 4) {
+                const float4 kv = *reinterpret_cast<const float4*>(krow + kk);
+                sacc = mfma32(kv.x, qreg[kk], sacc);
+                sacc = mfma32(kv.y, qreg[kk + 1], sacc);
+                sacc = mfma32(kv.z, qreg[kk + 2], sacc);
+                sacc = mfma32(kv.w, qreg[kk + 3], sacc);
+            }
+
+            // Score epilogue and mask; keys of register r: f(r, half).
+            float x[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int s = s_first + 8 * (r >> 2) + 4 * half + (r & 3);
+                float xs;
+                if constexpr (EPI) {
+                    float b = 0.0f;
+                    const int sc = min(s, S - 1), tc = min(t, T - 1);
+                    if (p.ep.bias_kind == ATTN_BIAS_TS) b = p.bias[(int64_t)tc * S + sc];
+                    else if (p.ep.bias_kind == ATTN_BIAS_HTS) b = p.bias[((int64_t)h * T + tc) * S + sc];
+                    xs = score_epilogue(sacc[r], p.ep, h, pos, s, b) * kLog2e;
+                } else {
+                    xs = sacc[r] * qk_scale;
+                }
+                if (!all_vis) {
+                    const bool vis = s >= klo && s < khi && key_visible(p.ep, pos, s);
+                    xs = vis ? xs : -INFINITY;
+                }
+                x[r] = xs;
+            }
+
+            // Online softmax for this lane's query (both halves share the max).
+            float mx = x[0];
+#pragma unroll
+            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, x[r]);
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            if (mx > m + kLazy) {
+                const float alpha = fast_exp2(m - mx);
+                l *= alpha;
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) o[b][r] *= alpha;
+                m = mx;
+            }
+            const float mu = m == -INFINITY ? 0.0f : m;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                x[r] = fast_exp2(x[r] - mu);
+                l += x[r];
+            }
+
+            // O^T += V^T P^T: k-step r uses keys f(r, half) and P from register r.
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = 8 * (r >> 2) + 4 * half + (r & 3);
+                float vv[NB];
+                lds_read<NB>(vt_ + key * VLD + NB * col, vv);
+#pragma unroll
+                for (int b = 0; b < NB; ++b) o[b] = mfma32(vv[b], x[r], o[b]);
+            }
+        }
+
+        if (kt + 1 < kt1) stage(buf ^ 1);
+    }
+
+    // Normalise and store: register r of block b is dv = NB*(8(r/4) + 4 half + r%4) + b.
+    const float lt = l + __shfl_xor(l, 32, 64);
+    const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+    if (trow) {
+        float* orow = p.out + (int64_t)t * p.H * DV + (int64_t)h * DV;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int i = 8 * (r >> 2) + 4 * half + (r & 3);
+            if constexpr (NB % 4 == 0) {
+#pragma unroll
+                for (int b = 0; b < NB; b += 4)
+                    *reinterpret_cast<float4*>(orow + NB * i + b) =
+                        make_float4(o[b][r] * inv, o[b + 1][r] * inv, o[b + 2][r] * inv, o[b + 3][r] * inv);
+            } else {
+                *reinterpret_cast<float2*>(orow + NB * i) = make_float2(o[0][r] * inv, o[1][r] * inv);
+            }
+        }
+    }
+}
+
+template <int D, int DV, bool EPI>
+hipError_t launch_t(const Problem& p, const PrefillArgs& a, const Launch& L) {
+    auto kern = prefill_kernel<D, DV, EPI>;
+    constexpr size_t lds = PrefillShape<D, DV>::lds_bytes;
+    static bool configured = false;
+    if (!configured) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        configured = true;
+    }
+    return launch_kernel(kern, dim3((unsigned)a.qblocks, (unsigned)(p.G * a.hgroups)), dim3(kThreads),
+                         (uint32_t)lds, L, p, a);
+}
+
+template <int D, int DV>
+hipError_t launch_dims(const Problem& p, const PrefillArgs& a, const Launch& L) {
+    const bool epi = p.ep.softcap > 0.0f || p.ep.has_alibi || p.ep.bias_kind != ATTN_BIAS_NONE;
+    return epi ? launch_t<D, DV, true>(p, a, L) : launch_t<D, DV, false>(p, a, L);
+}
+
+}  // namespace
+
+bool prefill_supported(int D, int Dv) {
+    return (D == 64 && Dv == 64) || (D == 128 && Dv == 128) || (D == 192 && Dv == 128) ||
+           (D == 256 && Dv == 256);
+}
+
+hipError_t launch_prefill(const Problem& p, const PrefillPlan& plan, const Launch& L) {
+    const int hpg = p.H / p.G;
+    PrefillArgs a;
+    a.nh = hpg % 4 == 0 ? 4 : (hpg % 2 == 0 ? 2 : 1);
+    a.hgroups = hpg / a.nh;
+    const int rows_per_wg = (kWaves / a.nh) * kBQ;
+    a.qblocks = (int)((p.T + rows_per_wg - 1) / rows_per_wg);
+    a.causal_order = p.ep.causal ? 1 : 0;
+    (void)plan;
+    if ((int64_t)p.G * a.hgroups > 65535) return hipErrorInvalidValue;
+    if (p.D == 64 && p.Dv == 64) return launch_dims<64, 64>(p, a, L);
+    if (p.D == 128 && p.Dv == 128) return launch_dims<128, 128>(p, a, L);
+    if (p.D == 192 && p.Dv == 128) return launch_dims<192, 128>(p, a, L);
+    if (p.D == 256 && p.Dv == 256) return launch_dims<256, 256>(p, a, L);
     return hipErrorInvalidValue;
 }
 
