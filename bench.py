@@ -134,7 +134,7 @@ def run_decode(args):
 
     # Timed region: K steps between two events on the stream the kernels run on.
     ga.attn_timing_enable(True)
-    for name in ("decode_split", "decode_combine", "cache_write"):
+    for name in ("decode_split", "combine", "cache_write"):
         ga.attn_timing_collect(name)
     stream = torch.cuda.current_stream(dev)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -146,7 +146,7 @@ def run_decode(args):
     torch.cuda.synchronize()
     ms_timed = e0.elapsed_time(e1) / args.steps
     split_ms, split_n = ga.attn_timing_collect("decode_split")
-    comb_ms, comb_n = ga.attn_timing_collect("decode_combine")
+    comb_ms, comb_n = ga.attn_timing_collect("combine")
     cw_ms, cw_n = ga.attn_timing_collect("cache_write")
     ga.attn_timing_enable(False)
 

@@ -37,6 +37,7 @@ int ok() {
 
 // Process-wide tuning overrides (attn_set_option).
 int64_t g_opt_decode_splits = 0;
+int64_t g_opt_prefill_splits = 0;
 int64_t g_opt_force_path = 0;
 
 constexpr int kCUs = 256;                 // MI355X compute units
@@ -44,6 +45,8 @@ constexpr int kDecodeWgPerCU = 2;         // decode_split occupancy target
 constexpr int64_t kDecodeMinKeys = 256;   // smallest key chunk worth a workgroup
 constexpr int64_t kDecodeChunkAlign = 64; // key chunk granularity (a multiple of 16 row groups x 2 rows)
 constexpr int64_t kDecodeMaxSplits = 1024;
+constexpr int64_t kPrefillMaxSplits = 16;
+constexpr int64_t kPrefillMinTilesPerSplit = 4;
 constexpr int64_t kMaxDim = 1 << 16;
 
 // ---------------------------------------------------------------------------
@@ -264,11 +267,27 @@ int make_plan(const Resolved& r, Plan* plan) {
     if (path == ATTN_PATH_PREFILL) {
         // Four waves of 32 query rows; heads of a KV group side by side
         // (up to 4), the rest of the workgroup's waves on further query rows.
-        const int64_t nh = hpg % 4 == 0 ? 4 : (hpg % 2 == 0 ? 2 : 1);
-        plan->prefill.tile_q = (int32_t)(4 / nh * 32);
-        plan->prefill.tile_k = 32;
-        if (r.G * (hpg / nh) > 65535)
-            return fail(ATTN_ERR_UNSUPPORTED, "kvHeads: too many heads for the prefill grid");
+        attn::PrefillPlan& pp = plan->prefill;
+        pp.nh = hpg % 4 == 0 ? 4 : (hpg % 2 == 0 ? 2 : 1);
+        pp.tile_q = 4 / pp.nh * 32;
+        const int64_t qblocks = (r.T + pp.tile_q - 1) / pp.tile_q;
+        const int64_t nwg = qblocks * r.G * (hpg / pp.nh);
+        if (nwg > INT32_MAX / kPrefillMaxSplits)
+            return fail(ATTN_ERR_UNSUPPORTED, "T: too many query rows for the prefill grid");
+        pp.qblocks = (int32_t)qblocks;
+        // Too few workgroups to fill the chip: split each one's key range.
+        const int64_t slots = (int64_t)kCUs * attn::prefill_waves_per_simd((int)r.D, (int)r.Dv);
+        const int64_t tiles = (kr.hi - kr.lo + 31) / 32;
+        int64_t ks = g_opt_prefill_splits;
+        if (ks <= 0) {
+            ks = nwg >= slots ? 1 : (slots + nwg - 1) / nwg;
+            const int64_t most = tiles / kPrefillMinTilesPerSplit;
+            if (ks > most) ks = most;
+        }
+        if (ks < 1) ks = 1;
+        if (ks > kPrefillMaxSplits) ks = kPrefillMaxSplits;
+        pp.ksplit = (int32_t)ks;
+        if (ks > 1) plan->workspace = sizeof(float) * (size_t)(r.T * r.H) * (size_t)ks * (size_t)(r.Dv + 2);
     }
     return ok();
 }
@@ -365,7 +384,9 @@ int attn_plan(const attn_params* p, attn_plan_info* info) {
     rc = make_plan(r, &plan);
     if (rc) return rc;
     info->path = plan.path;
-    info->splits = plan.path == ATTN_PATH_DECODE ? plan.decode.splits : 1;
+    info->splits = plan.path == ATTN_PATH_DECODE    ? plan.decode.splits
+                   : plan.path == ATTN_PATH_PREFILL ? plan.prefill.ksplit
+                                                    : 1;
     info->tile_q = plan.path == ATTN_PATH_PREFILL ? plan.prefill.tile_q : 0;
     info->reserved = 0;
     return ok();
@@ -441,14 +462,21 @@ int attn_forward(const attn_params* p, const float* q, const float* k, const flo
                 return attn::launch_decode_split(prob, plan.decode, (float*)workspace, L);
             });
             if (err == hipSuccess && plan.decode.splits > 1)
-                err = timed("decode_combine", s, [&](const attn::Launch& L) {
+                err = timed("combine", s, [&](const attn::Launch& L) {
                     return attn::launch_decode_combine(prob, plan.decode, (const float*)workspace, L);
                 });
             break;
         case ATTN_PATH_PREFILL:
             err = timed("prefill", s, [&](const attn::Launch& L) {
-                return attn::launch_prefill(prob, plan.prefill, L);
+                return attn::launch_prefill(prob, plan.prefill, (float*)workspace, L);
             });
+            if (err == hipSuccess && plan.prefill.ksplit > 1) {
+                attn::DecodePlan merge{};
+                merge.splits = plan.prefill.ksplit;
+                err = timed("combine", s, [&](const attn::Launch& L) {
+                    return attn::launch_decode_combine(prob, merge, (const float*)workspace, L);
+                });
+            }
             break;
         default:
             return fail(ATTN_ERR_INVALID, "internal: unknown path %d", plan.path);
@@ -489,6 +517,12 @@ int attn_set_option(const char* name, int64_t value) {
         if (value < 0 || value > kDecodeMaxSplits)
             return fail(ATTN_ERR_INVALID, "decode_splits: must be in 0..%lld", (long long)kDecodeMaxSplits);
         g_opt_decode_splits = value;
+        return ok();
+    }
+    if (!strcmp(name, "prefill_splits")) {
+        if (value < 0 || value > kPrefillMaxSplits)
+            return fail(ATTN_ERR_INVALID, "prefill_splits: must be in 0..%lld", (long long)kPrefillMaxSplits);
+        g_opt_prefill_splits = value;
         return ok();
     }
     if (!strcmp(name, "force_path")) {

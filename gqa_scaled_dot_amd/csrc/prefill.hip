@@ -4,8 +4,10 @@
 // A workgroup is 4 waves; each wave owns 32 query rows of one head, and the
 // waves of a workgroup share one KV head (heads of the same group side by
 // side, or consecutive query blocks of one head). K and V tiles of 32 key rows
-// are staged in LDS (double-buffered; the next tile's global loads are in
-// flight while the current one is used) and read by all four waves.
+// are staged in LDS, double-buffered, and read by all four waves. The next
+// tile's K rows are fetched from global memory while QK^T runs and written to
+// LDS after it; its V rows likewise around PV, so only one of the two is ever
+// held in registers.
 //
 // Lane layouts of v_mfma_f32_32x32x2f32 (A 32x2, B 2x32, D 32x32, 64 lanes):
 // A[i][k] sits in lane i + 32k, B[k][j] in lane j + 32k, and D[i][j] in lane
@@ -29,6 +31,11 @@
 // reference maximum (as in the decode path). Key tiles a workgroup cannot see
 // are skipped; tiles that every query of a wave sees skip the mask. Rows of a
 // tile outside the workgroup's visible key range are zero-filled, never read.
+//
+// When the grid would be too small to fill the chip (few query rows, as in
+// chunked prefill), each workgroup's key range is split into `ksplit` parts;
+// every part writes its unnormalised partial state to the workspace in the
+// decode path's layout, and the decode combine kernel merges them.
 #include "device_common.h"
 
 namespace attn {
@@ -41,6 +48,7 @@ constexpr int kBQ = 32;  // query rows per wave
 constexpr int kBK = 32;  // key rows per tile
 constexpr int kPad = 4;  // floats of padding per LDS row (bank spread)
 constexpr float kLazy = 8.0f;
+constexpr int kXcds = 8;  // MI355X: 8 XCDs of 32 CUs
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -83,13 +91,47 @@ struct PrefillShape {
 };
 
 // Workgroup layout chosen on the host: nh heads of one KV group side by side,
-// each with 4/nh consecutive 32-row query blocks.
+// each with 4/nh consecutive 32-row query blocks, and ksplit key-range parts.
 struct PrefillArgs {
-    int nh;        // heads per workgroup (1, 2 or 4)
-    int hgroups;   // head groups per KV head = (heads/kvHeads) / nh
-    int qblocks;   // workgroups along the query rows
+    int nh;            // heads per workgroup (1, 2 or 4)
+    int hgroups;       // head groups per KV head = (heads/kvHeads) / nh
+    int qblocks;       // workgroups along the query rows
+    int ksplit;        // parts of each workgroup's key range (1: write out directly)
     int causal_order;  // 1: heaviest query blocks first
+    float* ws;         // partial states when ksplit > 1
 };
+
+// Global -> registers -> LDS staging of the rows [kt*kBK, kt*kBK + kBK) of a
+// K or V tile (width W floats, global row stride `stride`). Rows outside
+// [klo, khi) are loaded from a clamped, in-bounds row and replaced by zeros,
+// so the loads need no branches.
+template <int W>
+__device__ __forceinline__ void fetch_rows(float4 (&st)[kBK * W / 4 / kThreads], const float* base,
+                                           int64_t stride, int kt, int klo, int khi) {
+#pragma unroll
+    for (int j = 0; j < kBK * W / 4 / kThreads; ++j) {
+        const int f = (int)threadIdx.x + j * kThreads;
+        const int row = f / (W / 4), c4 = f % (W / 4);
+        const int s = kt * kBK + row;
+        const int sc = min(max(s, klo), khi - 1);
+        const float4 x = *reinterpret_cast<const float4*>(base + sc * stride + 4 * c4);
+        const bool ok = (s >= klo) & (s < khi);
+        st[j].x = ok ? x.x : 0.0f;
+        st[j].y = ok ? x.y : 0.0f;
+        st[j].z = ok ? x.z : 0.0f;
+        st[j].w = ok ? x.w : 0.0f;
+    }
+}
+
+template <int W>
+__device__ __forceinline__ void stage_rows(const float4 (&st)[kBK * W / 4 / kThreads], float* tile) {
+#pragma unroll
+    for (int j = 0; j < kBK * W / 4 / kThreads; ++j) {
+        const int f = (int)threadIdx.x + j * kThreads;
+        const int row = f / (W / 4), c4 = f % (W / 4);
+        *reinterpret_cast<float4*>(tile + row * (W + kPad) + 4 * c4) = st[j];
+    }
+}
 
 template <int D, int DV, bool EPI>
 __global__ __launch_bounds__(kThreads, prefill_min_waves(D, DV)) void prefill_kernel(
@@ -108,9 +150,19 @@ __global__ __launch_bounds__(kThreads, prefill_min_waves(D, DV)) void prefill_ke
 
     const int hpg = p.H / p.G;
     const int qsub = kWaves / a.nh;
-    const int qb = a.causal_order ? (a.qblocks - 1 - (int)blockIdx.x) : (int)blockIdx.x;
-    const int g = (int)blockIdx.y / a.hgroups;
-    const int hgi = (int)blockIdx.y % a.hgroups;
+    // Workgroups are dealt round-robin to the 8 XCDs (each with its own L2).
+    // Renumber them so that each XCD gets a contiguous run of (KV head, query
+    // block, key part) work: the K/V of a KV head then stays in one L2.
+    // Within a run, the heaviest (latest, for causal) query blocks start first.
+    const int nwg = (int)gridDim.x;
+    int wid = (int)blockIdx.x;
+    if (nwg % kXcds == 0) wid = (wid % kXcds) * (nwg / kXcds) + wid / kXcds;
+    const int ks = wid % a.ksplit;
+    const int yq = wid / a.ksplit / a.qblocks;
+    const int xq = wid / a.ksplit % a.qblocks;
+    const int qb = a.causal_order ? (a.qblocks - 1 - xq) : xq;
+    const int g = yq / a.hgroups;
+    const int hgi = yq % a.hgroups;
     const int h = g * hpg + hgi * a.nh + wave % a.nh;
     const int qwg0 = qb * qsub * kBQ;                 // first query row of the workgroup
     const int q0 = qwg0 + (wave / a.nh) * kBQ;        // first query row of this wave
@@ -122,14 +174,14 @@ __global__ __launch_bounds__(kThreads, prefill_min_waves(D, DV)) void prefill_ke
     // This lane's half of its query row: q[t, h*D + half*D/2 + kk], kk < D/2.
     float qreg[D / 2];
     {
-        const float* qrow = p.q + (int64_t)t * p.H * D + (int64_t)h * D + half * (D / 2);
+        const float* qrow = p.q + (int64_t)min(t, T - 1) * p.H * D + (int64_t)h * D + half * (D / 2);
 #pragma unroll
         for (int kk = 0; kk < D / 2; kk += 4) {
-            const float4 v = trow ? *reinterpret_cast<const float4*>(qrow + kk) : make_float4(0.f, 0.f, 0.f, 0.f);
-            qreg[kk] = v.x;
-            qreg[kk + 1] = v.y;
-            qreg[kk + 2] = v.z;
-            qreg[kk + 3] = v.w;
+            const float4 v = *reinterpret_cast<const float4*>(qrow + kk);
+            qreg[kk] = trow ? v.x : 0.0f;
+            qreg[kk + 1] = trow ? v.y : 0.0f;
+            qreg[kk + 2] = trow ? v.z : 0.0f;
+            qreg[kk + 3] = trow ? v.w : 0.0f;
         }
     }
 
@@ -155,61 +207,33 @@ __global__ __launch_bounds__(kThreads, prefill_min_waves(D, DV)) void prefill_ke
         for (int r = 0; r < 16; ++r) o[b][r] = 0.0f;
     float m = -INFINITY, l = 0.0f;
 
-    const int kt0 = klo / kBK;
-    const int kt1 = khi > klo ? (khi + kBK - 1) / kBK : kt0;
+    // This workgroup's part of its key tiles.
+    const int kt_all0 = klo / kBK;
+    const int kt_all1 = khi > klo ? (khi + kBK - 1) / kBK : kt_all0;
+    const int per = (kt_all1 - kt_all0 + a.ksplit - 1) / a.ksplit;
+    const int kt0 = min(kt_all1, kt_all0 + ks * per);
+    const int kt1 = min(kt_all1, kt0 + per);
+
     const int64_t kstride = (int64_t)p.G * D, vstride = (int64_t)p.G * DV;
     const float* kg = p.k + (int64_t)g * D;
     const float* vg = p.v + (int64_t)g * DV;
-
-    // Global -> registers -> LDS staging of one K/V tile.
     float4 kst[Sh::KF4], vst[Sh::VF4];
-    auto fetch = [&](int kt) {
-#pragma unroll
-        for (int j = 0; j < Sh::KF4; ++j) {
-            const int f = tid + j * kThreads;
-            const int row = f / (D / 4), c4 = f % (D / 4);
-            const int s = kt * kBK + row;
-            kst[j] = (s >= klo && s < khi) ? *reinterpret_cast<const float4*>(kg + s * kstride + 4 * c4)
-                                           : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-#pragma unroll
-        for (int j = 0; j < Sh::VF4; ++j) {
-            const int f = tid + j * kThreads;
-            const int row = f / (DV / 4), c4 = f % (DV / 4);
-            const int s = kt * kBK + row;
-            vst[j] = (s >= klo && s < khi) ? *reinterpret_cast<const float4*>(vg + s * vstride + 4 * c4)
-                                           : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-    };
-    auto stage = [&](int buf) {
-        float* kt_ = ktile + buf * kBK * KLD;
-        float* vt_ = vtile + buf * kBK * VLD;
-#pragma unroll
-        for (int j = 0; j < Sh::KF4; ++j) {
-            const int f = tid + j * kThreads;
-            const int row = f / (D / 4), c4 = f % (D / 4);
-            *reinterpret_cast<float4*>(kt_ + row * KLD + 4 * c4) = kst[j];
-        }
-#pragma unroll
-        for (int j = 0; j < Sh::VF4; ++j) {
-            const int f = tid + j * kThreads;
-            const int row = f / (DV / 4), c4 = f % (DV / 4);
-            *reinterpret_cast<float4*>(vt_ + row * VLD + 4 * c4) = vst[j];
-        }
-    };
 
     const float qk_scale = p.ep.scale * kLog2e;
     if (kt0 < kt1) {
-        fetch(kt0);
-        stage(0);
+        fetch_rows<D>(kst, kg, kstride, kt0, klo, khi);
+        fetch_rows<DV>(vst, vg, vstride, kt0, klo, khi);
+        stage_rows<D>(kst, ktile);
+        stage_rows<DV>(vst, vtile);
     }
     for (int kt = kt0; kt < kt1; ++kt) {
         const int buf = (kt - kt0) & 1;
+        const bool more = kt + 1 < kt1;
         __syncthreads();  // tile `kt` is in LDS; everyone is done with the other buffer
-        if (kt + 1 < kt1) fetch(kt + 1);
+        if (more) fetch_rows<D>(kst, kg, kstride, kt + 1, klo, khi);
 
         const int s_first = kt * kBK, s_last = s_first + kBK - 1;
-        // Does any query of this wave see any key of the tile?
+        // Does any query of this wave see any key of the tile? Do all see all?
         bool any_vis;
         bool all_vis;
         if (p.ep.causal) {
@@ -225,9 +249,10 @@ __global__ __launch_bounds__(kThreads, prefill_min_waves(D, DV)) void prefill_ke
         }
         all_vis = all_vis && s_first >= klo && s_last < khi;
 
+        const float* kt_ = ktile + buf * kBK * KLD;
+        const float* vt_ = vtile + buf * kBK * VLD;
+        float x[16];
         if (any_vis) {
-            const float* kt_ = ktile + buf * kBK * KLD;
-            const float* vt_ = vtile + buf * kBK * VLD;
             // S^T = K Q^T for 32 keys x 32 queries.
             f32x16 sacc;
 #pragma unroll
@@ -240,10 +265,12 @@ __global__ __launch_bounds__(kThreads, prefill_min_waves(D, DV)) void prefill_ke
                 sacc = mfma32(kv.y, qreg[kk + 1], sacc);
                 sacc = mfma32(kv.z, qreg[kk + 2], sacc);
                 sacc = mfma32(kv.w, qreg[kk + 3], sacc);
+                // Keep the scheduler from hoisting every LDS read of the tile
+                // at once (it would need D/2 registers for them).
+                if (kk % 16 == 12) __builtin_amdgcn_sched_barrier(0);
             }
 
             // Score epilogue and mask; keys of register r: f(r, half).
-            float x[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int s = s_first + 8 * (r >> 2) + 4 * half + (r & 3);
@@ -258,12 +285,15 @@ __global__ __launch_bounds__(kThreads, prefill_min_waves(D, DV)) void prefill_ke
                     xs = sacc[r] * qk_scale;
                 }
                 if (!all_vis) {
-                    const bool vis = s >= klo && s < khi && key_visible(p.ep, pos, s);
+                    const bool vis = (s >= klo) & (s < khi) & key_visible(p.ep, pos, s);
                     xs = vis ? xs : -INFINITY;
                 }
                 x[r] = xs;
             }
+        }
+        if (more) stage_rows<D>(kst, ktile + (buf ^ 1) * kBK * KLD);
 
+        if (any_vis) {
             // Online softmax for this lane's query (both halves share the max).
             float mx = x[0];
 #pragma unroll
@@ -284,7 +314,10 @@ __global__ __launch_bounds__(kThreads, prefill_min_waves(D, DV)) void prefill_ke
                 x[r] = fast_exp2(x[r] - mu);
                 l += x[r];
             }
+        }
+        if (more) fetch_rows<DV>(vst, vg, vstride, kt + 1, klo, khi);
 
+        if (any_vis) {
             // O^T += V^T P^T: k-step r uses keys f(r, half) and P from register r.
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -293,28 +326,41 @@ __global__ __launch_bounds__(kThreads, prefill_min_waves(D, DV)) void prefill_ke
                 lds_read<NB>(vt_ + key * VLD + NB * col, vv);
 #pragma unroll
                 for (int b = 0; b < NB; ++b) o[b] = mfma32(vv[b], x[r], o[b]);
+                if (NB * (r + 1) % 16 == 0) __builtin_amdgcn_sched_barrier(0);
             }
         }
-
-        if (kt + 1 < kt1) stage(buf ^ 1);
+        if (more) stage_rows<DV>(vst, vtile + (buf ^ 1) * kBK * VLD);
     }
 
-    // Normalise and store: register r of block b is dv = NB*(8(r/4) + 4 half + r%4) + b.
+    // Register r of block b is dv = NB*(8(r/4) + 4 half + r%4) + b.
     const float lt = l + __shfl_xor(l, 32, 64);
-    const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-    if (trow) {
-        float* orow = p.out + (int64_t)t * p.H * DV + (int64_t)h * DV;
+    if (!trow) return;
+    const int64_t th = (int64_t)t * p.H + h;
+    float* dst;
+    float sc;
+    if (a.ksplit == 1) {
+        dst = p.out + th * DV;
+        sc = lt > 0.0f ? 1.0f / lt : 0.0f;
+    } else {
+        // Unnormalised partial state (max in the base-2 domain, sum, acc).
+        dst = a.ws + (th * a.ksplit + ks) * DV;
+        sc = 1.0f;
+        if (half == 0) {
+            float* ml = a.ws + (int64_t)T * p.H * a.ksplit * DV + (th * a.ksplit + ks) * 2;
+            ml[0] = m;
+            ml[1] = lt;
+        }
+    }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int i = 8 * (r >> 2) + 4 * half + (r & 3);
-            if constexpr (NB % 4 == 0) {
+    for (int r = 0; r < 16; ++r) {
+        const int i = 8 * (r >> 2) + 4 * half + (r & 3);
+        if constexpr (NB % 4 == 0) {
 #pragma unroll
-                for (int b = 0; b < NB; b += 4)
-                    *reinterpret_cast<float4*>(orow + NB * i + b) =
-                        make_float4(o[b][r] * inv, o[b + 1][r] * inv, o[b + 2][r] * inv, o[b + 3][r] * inv);
-            } else {
-                *reinterpret_cast<float2*>(orow + NB * i) = make_float2(o[0][r] * inv, o[1][r] * inv);
-            }
+            for (int b = 0; b < NB; b += 4)
+                *reinterpret_cast<float4*>(dst + NB * i + b) =
+                    make_float4(o[b][r] * sc, o[b + 1][r] * sc, o[b + 2][r] * sc, o[b + 3][r] * sc);
+        } else {
+            *reinterpret_cast<float2*>(dst + NB * i) = make_float2(o[0][r] * sc, o[1][r] * sc);
         }
     }
 }
@@ -330,8 +376,8 @@ hipError_t launch_t(const Problem& p, const PrefillArgs& a, const Launch& L) {
         if (e != hipSuccess) return e;
         configured = true;
     }
-    return launch_kernel(kern, dim3((unsigned)a.qblocks, (unsigned)(p.G * a.hgroups)), dim3(kThreads),
-                         (uint32_t)lds, L, p, a);
+    const int64_t nwg = (int64_t)a.qblocks * p.G * a.hgroups * a.ksplit;
+    return launch_kernel(kern, dim3((unsigned)nwg), dim3(kThreads), (uint32_t)lds, L, p, a);
 }
 
 template <int D, int DV>
@@ -347,16 +393,19 @@ bool prefill_supported(int D, int Dv) {
            (D == 256 && Dv == 256);
 }
 
-hipError_t launch_prefill(const Problem& p, const PrefillPlan& plan, const Launch& L) {
-    const int hpg = p.H / p.G;
+int prefill_waves_per_simd(int D, int Dv) { return prefill_min_waves(D, Dv); }
+
+hipError_t launch_prefill(const Problem& p, const PrefillPlan& plan, float* ws, const Launch& L) {
     PrefillArgs a;
-    a.nh = hpg % 4 == 0 ? 4 : (hpg % 2 == 0 ? 2 : 1);
-    a.hgroups = hpg / a.nh;
-    const int rows_per_wg = (kWaves / a.nh) * kBQ;
-    a.qblocks = (int)((p.T + rows_per_wg - 1) / rows_per_wg);
+    a.nh = plan.nh;
+    a.hgroups = (p.H / p.G) / plan.nh;
+    a.qblocks = plan.qblocks;
+    a.ksplit = plan.ksplit;
     a.causal_order = p.ep.causal ? 1 : 0;
-    (void)plan;
-    if ((int64_t)p.G * a.hgroups > 65535) return hipErrorInvalidValue;
+    a.ws = ws;
+    if (a.nh < 1 || a.hgroups < 1 || a.qblocks < 1 || a.ksplit < 1) return hipErrorInvalidValue;
+    if (a.ksplit > 1 && !ws) return hipErrorInvalidValue;
+    if ((int64_t)a.qblocks * p.G * a.hgroups * a.ksplit > INT32_MAX) return hipErrorInvalidValue;
     if (p.D == 64 && p.Dv == 64) return launch_dims<64, 64>(p, a, L);
     if (p.D == 128 && p.Dv == 128) return launch_dims<128, 128>(p, a, L);
     if (p.D == 192 && p.Dv == 128) return launch_dims<192, 128>(p, a, L);

@@ -129,9 +129,10 @@ size_t attn_workspace_size(const attn_params* p);
  *   out  [T, heads*v_head_dim]      device, written; must not overlap inputs
  *   workspace, workspace_bytes
  *        device scratch of at least attn_workspace_size(p) bytes (NULL when
- *        that is 0), 256-byte aligned; its contents need no initialisation
- *        and mean nothing after the call. Two calls in flight at once must
- *        not share a workspace.
+ *        that is 0), 256-byte aligned; it holds the partial softmax states
+ *        of key-range splits. Its contents need no initialisation and mean
+ *        nothing after the call. Two calls in flight at once must not share
+ *        a workspace.
  * q, k, v, bias and out must be 16-byte aligned. T = 0 is a no-op; S = 0
  * writes zeros.
  */
@@ -157,7 +158,8 @@ const char* attn_last_error(void);
  * Which kernels attn_forward would launch for *p (host only). Lets tests
  * and measurement tools name the path; not needed to run the op.
  *   path    ATTN_PATH_*
- *   splits  key-range splits of the decode path (1 elsewhere)
+ *   splits  key-range splits (decode path, or prefill on a small grid; the
+ *           partial states are merged by a combine kernel); 1 elsewhere
  *   tile_q  query rows per workgroup on the prefill path
  */
 #define ATTN_PATH_EMPTY 0   /* T = 0 or no work */
@@ -176,6 +178,7 @@ int attn_plan(const attn_params* p, attn_plan_info* info);
 /*
  * Tuning overrides for tests and sweeps (process-wide, not thread-safe):
  *   "decode_splits"  force the decode split count (0 = automatic)
+ *   "prefill_splits" force the prefill key-range split count (0 = automatic, max 16)
  *   "force_path"     force ATTN_PATH_GENERIC / _DECODE / _PREFILL (0 = automatic);
  *                    a forced path that cannot serve *p is refused
  * Returns ATTN_ERR_INVALID for an unknown name.
@@ -190,8 +193,8 @@ int attn_set_option(const char* name, int64_t value);
  * count since the last collect (then clears them). Off by default; the hot
  * path records nothing when off. Event pairs come from a fixed pool of 4096,
  * created on the first enable; launches beyond the pool are not timed.
- * Kernel names: "cache_write", "decode_split", "decode_combine", "prefill",
- * "generic", "zero_fill".
+ * Kernel names: "cache_write", "decode_split", "prefill", "combine" (merges
+ * key-range splits after either), "generic", "zero_fill".
  */
 int attn_timing_enable(int on);
 int attn_timing_collect(const char* kernel, double* total_ms, int64_t* launches);

@@ -129,3 +129,17 @@ def test_gemma2_swa_full_size_sampled():
 def test_latent_noncausal_full_size():
     w = workloads.LATENT_NONCAUSAL
     _check(w, rows=sample_rows(w.T, seed=4, n_random=64))
+
+
+@pytest.mark.parametrize("splits", [2, 3, 7])
+def test_prefill_key_splits_match(splits):
+    # Forced key-range splits (merged by the combine kernel) give the same result.
+    w = workloads.Workload("split prefill", T=70, S=500, heads=8, kvHeads=2, headDim=128, posOffset=430,
+                           alibi=True)
+    q, k, v, _ = w.tensors()
+    try:
+        ga.attn_set_option("prefill_splits", splits)
+        assert ga.attn_plan(w.T, w.S, **w.params())["splits"] == splits
+        compare(q, k, v, None, w.params(), what=f"prefill splits={splits}")
+    finally:
+        ga.attn_set_option("prefill_splits", 0)
