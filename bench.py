@@ -4,18 +4,24 @@
 One step is one decode step of the Llama-3-8B-shaped GQA workload (T=1,
 S=32768, heads 32, kvHeads 8, headDim 128, causal, posOffset 32767): two
 cache_write calls append the new K and V rows at row 32767, then
-attn_forward attends over the whole cache (decode_split + decode_combine).
-K/V caches rotate over two copies (512 MiB together) so no step finds its
+attn_forward attends over the whole cache (decode_split + combine). K/V
+caches rotate over two copies (512 MiB together) so no step finds its
 working set in the 256 MB Infinity Cache.
 
 `value` is the decode's algorithmic KV bandwidth: the bytes attention must
 move (every visible K and V row once, plus q and out) per step time, in
 GB/s. `roofline` rates the dominant kernel, decode_split, on its own: the
 same algorithmic bytes over its average duration, timed with HIP events
-recorded around each of its launches on the stream it runs on, against the
+that each launch's dispatch stamps on the stream it runs on, against the
 8 TB/s HBM peak. `cpu_baseline` times the CPU oracle on the same inputs.
 
+The same line carries `prefill`: the Llama-3-8B-shaped causal prefill
+(T=S=4096), whose algorithmic flops (heads x visible (query, key) pairs x
+(2 headDim + 2 vHeadDim)) over the call time give TFLOP/s, rated against the
+157.3 TFLOP/s fp32 matrix peak.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+       [--prefill-steps K]
 """
 
 from __future__ import annotations
@@ -38,6 +44,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
     "decode_split": ["gqa_scaled_dot_amd/csrc/decode.hip", "gqa_scaled_dot_amd/csrc/device_common.h",
                      "gqa_scaled_dot_amd/csrc/kernels.h"],
+    "prefill": ["gqa_scaled_dot_amd/csrc/prefill.hip", "gqa_scaled_dot_amd/csrc/device_common.h",
+                "gqa_scaled_dot_amd/csrc/kernels.h"],
 }
 
 
@@ -77,6 +85,19 @@ def decode_algorithmic_bytes(w) -> int:
     elif w.bias == "TS":
         b += w.T * rows * 4
     return b
+
+
+def visible_pairs(w) -> int:
+    """Visible (query, key) pairs of one head under the causal/window rule."""
+    import numpy as np
+    pos = (w.posOffset or 0) + np.arange(w.T, dtype=np.int64)
+    if w.causal:
+        hi = np.minimum(pos, w.S - 1)
+        lo = np.maximum(0, pos - w.window + 1) if w.window else np.zeros_like(pos)
+    else:
+        hi = np.minimum(pos + w.window, w.S - 1) if w.window else np.full_like(pos, w.S - 1)
+        lo = np.maximum(0, pos - w.window) if w.window else np.zeros_like(pos)
+    return int(np.maximum(hi - lo + 1, 0).sum())
 
 
 def cpu_threads() -> int:
@@ -160,7 +181,7 @@ def run_decode(args):
     ms_per_step = e0.elapsed_time(e1) / args.steps
     log(f"[bench] step {ms_per_step * 1e3:.2f} us (with kernel events {ms_timed * 1e3:.2f} us); "
         f"decode_split {split_ms / max(split_n, 1) * 1e3:.2f} us x{split_n}, "
-        f"decode_combine {comb_ms / max(comb_n, 1) * 1e3:.2f} us x{comb_n}, "
+        f"combine {comb_ms / max(comb_n, 1) * 1e3:.2f} us x{comb_n}, "
         f"cache_write {cw_ms / max(cw_n, 1) * 1e3:.2f} us x{cw_n}")
 
     alg_bytes = decode_algorithmic_bytes(w)
@@ -212,20 +233,86 @@ def run_decode(args):
     }
 
 
+def run_prefill(args):
+    import numpy as np
+    import torch
+
+    import gqa_scaled_dot_amd as ga
+    import oracle
+    import workloads
+
+    w = workloads.LLAMA_PREFILL
+    params = w.params()
+    dev = torch.device("cuda:0")
+    q, k, v, _ = w.tensors()
+    plan = ga.attn_plan(w.T, w.S, **params)
+    log(f"[bench] prefill workload: {w.name}; plan {plan}")
+    qd, kd, vd = (torch.from_numpy(x).to(dev) for x in (q, k, v))
+    out = torch.empty((w.T, w.heads * w.Dv), dtype=torch.float32, device=dev)
+    call = ga.prepare_forward(qd, kd, vd, out=out, **params)
+    for _ in range(max(2, args.warmup // 5)):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # Kernel durations from dispatch-stamped events ...
+    ga.attn_timing_enable(True)
+    for name in ("prefill", "combine"):
+        ga.attn_timing_collect(name)
+    for _ in range(args.prefill_steps):
+        call()
+    torch.cuda.synchronize()
+    k_ms, k_n = ga.attn_timing_collect("prefill")
+    ga.attn_timing_collect("combine")
+    ga.attn_timing_enable(False)
+    # ... and the call time from a loop without them.
+    e0.record(stream)
+    for _ in range(args.prefill_steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_call = e0.elapsed_time(e1) / args.prefill_steps
+    flops = w.heads * visible_pairs(w) * (2 * w.headDim + 2 * w.Dv)
+    kern_s = k_ms / k_n * 1e-3
+    achieved = flops / kern_s / 1e12
+    log(f"[bench] prefill call {ms_call * 1e3:.1f} us, kernel {kern_s * 1e6:.1f} us x{k_n}, "
+        f"{achieved:.2f} TFLOP/s")
+    rows = sorted(set([0, 1, 2, 31, 32, 2047, 2048, 4094, 4095] +
+                      [int(x) for x in np.random.default_rng(7).integers(0, w.T, 24)]))
+    ref = oracle.attention(q, k, v, rows=rows, threads=cpu_threads(), **params)
+    got = out.cpu().numpy()[rows].astype(np.float64)
+    err = np.abs(got - ref)
+    ok = bool(np.all(err <= 1e-4 + 1e-4 * np.abs(ref)))
+    log(f"[bench] prefill parity on {len(rows)} sampled rows: max |err| {err.max():.3e} ok={ok}")
+    return {
+        "workload": w.name, "value": round(flops / (ms_call * 1e-3) / 1e12, 3), "unit": "TFLOP/s",
+        "ms_per_call": round(ms_call, 6), "calls": args.prefill_steps,
+        "flops_per_call": flops,
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": FP32_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / FP32_PEAK_TFLOPS, 4),
+                     "traffic": measured_traffic("prefill", w.name),
+                     "kernel": "prefill", "flops_per_launch": flops,
+                     "avg_launch_us": round(kern_s * 1e6, 3)},
+        "parity": {"rows": len(rows), "max_abs_err": float(err.max()), "ok": ok},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--prefill-steps", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle timing")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the op has no multi-GPU path in this library)", file=sys.stderr)
         sys.exit(2)
-    if args.steps < 1 or args.warmup < 0:
-        ap.error("--steps must be >= 1 and --warmup >= 0")
+    if args.steps < 1 or args.warmup < 0 or args.prefill_steps < 1:
+        ap.error("--steps and --prefill-steps must be >= 1 and --warmup >= 0")
     rec = run_decode(args)
+    rec["prefill"] = run_prefill(args)
     print(json.dumps(rec), flush=True)
 
 
