@@ -38,6 +38,7 @@ int ok() {
 // Process-wide tuning overrides (attn_set_option).
 int64_t g_opt_decode_splits = 0;
 int64_t g_opt_prefill_splits = 0;
+int64_t g_opt_prefill_variant = 0;
 int64_t g_opt_force_path = 0;
 
 constexpr int kCUs = 256;                 // MI355X compute units
@@ -268,15 +269,21 @@ int make_plan(const Resolved& r, Plan* plan) {
         // Four waves of 32 query rows; heads of a KV group side by side
         // (up to 4), the rest of the workgroup's waves on further query rows.
         attn::PrefillPlan& pp = plan->prefill;
-        pp.nh = hpg % 4 == 0 ? 4 : (hpg % 2 == 0 ? 2 : 1);
-        pp.tile_q = 4 / pp.nh * 32;
+        // Heads of one KV group side by side in a workgroup; its other waves
+        // on further query blocks. Wide heads take the 16-row-wave variant.
+        pp.variant = g_opt_prefill_variant ? (int32_t)g_opt_prefill_variant : (r.D + r.Dv > 256 ? 16 : 32);
+        const int64_t waves = pp.variant == 16 ? 8 : 4, rows_per_wave = pp.variant == 16 ? 16 : 32;
+        int64_t nh = 1;
+        while (nh * 2 <= waves && hpg % (nh * 2) == 0) nh *= 2;
+        pp.nh = (int32_t)nh;
+        pp.tile_q = (int32_t)(waves / nh * rows_per_wave);
         const int64_t qblocks = (r.T + pp.tile_q - 1) / pp.tile_q;
-        const int64_t nwg = qblocks * r.G * (hpg / pp.nh);
+        const int64_t nwg = qblocks * r.G * (hpg / nh);
         if (nwg > INT32_MAX / kPrefillMaxSplits)
             return fail(ATTN_ERR_UNSUPPORTED, "T: too many query rows for the prefill grid");
         pp.qblocks = (int32_t)qblocks;
         // Too few workgroups to fill the chip: split each one's key range.
-        const int64_t slots = (int64_t)kCUs * attn::prefill_waves_per_simd((int)r.D, (int)r.Dv);
+        const int64_t slots = (int64_t)kCUs * attn::prefill_wgs_per_cu(pp.variant, (int)r.D, (int)r.Dv);
         const int64_t tiles = (kr.hi - kr.lo + 31) / 32;
         int64_t ks = g_opt_prefill_splits;
         if (ks <= 0) {
@@ -523,6 +530,12 @@ int attn_set_option(const char* name, int64_t value) {
         if (value < 0 || value > kPrefillMaxSplits)
             return fail(ATTN_ERR_INVALID, "prefill_splits: must be in 0..%lld", (long long)kPrefillMaxSplits);
         g_opt_prefill_splits = value;
+        return ok();
+    }
+    if (!strcmp(name, "prefill_variant")) {
+        if (value != 0 && value != 16 && value != 32)
+            return fail(ATTN_ERR_INVALID, "prefill_variant: must be 0, 16 or 32");
+        g_opt_prefill_variant = value;
         return ok();
     }
     if (!strcmp(name, "force_path")) {

@@ -23,6 +23,8 @@
 //
 // decode_combine: grid (T*heads), merges the splits' partial states:
 // M = max m_i, L = sum l_i 2^(m_i - M), out = sum acc_i 2^(m_i - M) / L.
+// combine_few: the same merge for up to 16 splits (prefill key-range parts),
+// one thread per 4 output floats.
 #include "device_common.h"
 
 namespace attn {
@@ -34,6 +36,7 @@ constexpr int kRowGroups = kThreads / 16;
 constexpr int kWaves = kThreads / 64;
 constexpr float kLazy = 8.0f;  // log2 of the largest weight before the reference moves
 constexpr int kMaxSplits = 1024;
+constexpr int kFewSplits = 16;  // up to this many splits, combine_few_kernel merges them
 
 template <int D, int DV, int NQ>
 struct DecodeShape {
@@ -358,6 +361,40 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(Problem p, int
     }
 }
 
+// Few splits (key-range parts of a prefill): one thread per (query row,
+// head, 4 output floats) reads every split's (max, sum) itself and its four
+// accumulator floats; no reduction across threads is needed.
+template <int DV>
+__global__ __launch_bounds__(kThreads) void combine_few_kernel(Problem p, int nsplit,
+                                                               const float* __restrict__ ws) {
+    constexpr int E4 = DV / 4;
+    const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const int64_t rows = p.T * p.H;
+    if (idx >= rows * E4) return;
+    const int64_t th = idx / E4;
+    const int e4 = (int)(idx % E4);
+    const float* ml = ws + rows * nsplit * DV + th * nsplit * 2;
+    const float4* acc4 = reinterpret_cast<const float4*>(ws + th * nsplit * DV) + e4;
+    float M = -INFINITY;
+    for (int i = 0; i < nsplit; ++i) M = fmaxf(M, ml[2 * i]);
+    float4* orow = reinterpret_cast<float4*>(p.out + th * DV) + e4;
+    if (M == -INFINITY) {
+        *orow = zero4();
+        return;
+    }
+    float L = 0.0f;
+    float4 a = zero4();
+    for (int i = 0; i < nsplit; ++i) {
+        const float w = fast_exp2(ml[2 * i] - M);
+        L = fmaf(ml[2 * i + 1], w, L);
+        const float4 c = acc4[(int64_t)i * E4];
+        a.x = fmaf(c.x, w, a.x); a.y = fmaf(c.y, w, a.y);
+        a.z = fmaf(c.z, w, a.z); a.w = fmaf(c.w, w, a.w);
+    }
+    const float inv = 1.0f / L;
+    *orow = make_float4(a.x * inv, a.y * inv, a.z * inv, a.w * inv);
+}
+
 template <int D, int DV, int NQ>
 hipError_t launch_split_t(const Problem& p, const DecodePlan& plan, float* ws, const Launch& L) {
     const dim3 grid((unsigned)plan.splits, (unsigned)p.G);
@@ -409,6 +446,16 @@ hipError_t launch_decode_split(const Problem& p, const DecodePlan& plan, float* 
 hipError_t launch_decode_combine(const Problem& p, const DecodePlan& plan, const float* ws,
                                  const Launch& L) {
     if (plan.splits < 1 || plan.splits > kMaxSplits) return hipErrorInvalidValue;
+    if (plan.splits <= kFewSplits) {
+        const int64_t n = p.T * p.H * (p.Dv / 4);
+        const dim3 g((unsigned)((n + kThreads - 1) / kThreads)), b(kThreads);
+        switch (p.Dv) {
+            case 64: return launch_kernel(combine_few_kernel<64>, g, b, 0, L, p, plan.splits, ws);
+            case 128: return launch_kernel(combine_few_kernel<128>, g, b, 0, L, p, plan.splits, ws);
+            case 256: return launch_kernel(combine_few_kernel<256>, g, b, 0, L, p, plan.splits, ws);
+            default: return hipErrorInvalidValue;
+        }
+    }
     const dim3 grid((unsigned)(p.T * p.H)), block(kThreads);
     switch (p.Dv) {
         case 64: return launch_kernel(decode_combine_kernel<64>, grid, block, 0, L, p, plan.splits, ws);

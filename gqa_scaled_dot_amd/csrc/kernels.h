@@ -49,8 +49,9 @@ struct DecodePlan {
 };
 
 struct PrefillPlan {
-    int32_t tile_q;   // query rows per workgroup
-    int32_t nh;       // heads of one KV group per workgroup (1, 2 or 4)
+    int32_t variant;  // 32: 32x32x2 MFMA, 4 waves of 32 rows; 16: 16x16x4, 8 waves of 16 rows
+    int32_t tile_q;   // query rows per workgroup and head
+    int32_t nh;       // heads of one KV group per workgroup
     int32_t qblocks;  // workgroups along the query rows
     int32_t ksplit;   // key-range parts per workgroup (partials merged by the combine kernel)
 };
@@ -80,7 +81,7 @@ hipError_t launch_decode_split(const Problem& p, const DecodePlan& plan, float* 
 hipError_t launch_decode_combine(const Problem& p, const DecodePlan& plan, const float* ws,
                                  const Launch& L);
 bool prefill_supported(int D, int Dv);
-int prefill_waves_per_simd(int D, int Dv);
+int prefill_wgs_per_cu(int variant, int D, int Dv);
 hipError_t launch_prefill(const Problem& p, const PrefillPlan& plan, float* ws, const Launch& L);
 
 }  // namespace attn

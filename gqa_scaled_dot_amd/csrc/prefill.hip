@@ -36,19 +36,20 @@
 // chunked prefill), each workgroup's key range is split into `ksplit` parts;
 // every part writes its unnormalised partial state to the workspace in the
 // decode path's layout, and the decode combine kernel merges them.
-#include "device_common.h"
+//
+// A 16x16x4 variant with 16 query rows per wave (prefill16.hip) serves wide
+// heads; the host picks one per shape.
+#include "prefill_common.h"
 
 namespace attn {
 
 namespace {
 
+using namespace pf;
+
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
 constexpr int kBQ = 32;  // query rows per wave
-constexpr int kBK = 32;  // key rows per tile
-constexpr int kPad = 4;  // floats of padding per LDS row (bank spread)
-constexpr float kLazy = 8.0f;
-constexpr int kXcds = 8;  // MI355X: 8 XCDs of 32 CUs
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -90,52 +91,9 @@ struct PrefillShape {
     static constexpr size_t lds_bytes = sizeof(float) * 2 * kBK * (size_t)(KLD + VLD);
 };
 
-// Workgroup layout chosen on the host: nh heads of one KV group side by side,
-// each with 4/nh consecutive 32-row query blocks, and ksplit key-range parts.
-struct PrefillArgs {
-    int nh;            // heads per workgroup (1, 2 or 4)
-    int hgroups;       // head groups per KV head = (heads/kvHeads) / nh
-    int qblocks;       // workgroups along the query rows
-    int ksplit;        // parts of each workgroup's key range (1: write out directly)
-    int causal_order;  // 1: heaviest query blocks first
-    float* ws;         // partial states when ksplit > 1
-};
-
-// Global -> registers -> LDS staging of the rows [kt*kBK, kt*kBK + kBK) of a
-// K or V tile (width W floats, global row stride `stride`). Rows outside
-// [klo, khi) are loaded from a clamped, in-bounds row and replaced by zeros,
-// so the loads need no branches.
-template <int W>
-__device__ __forceinline__ void fetch_rows(float4 (&st)[kBK * W / 4 / kThreads], const float* base,
-                                           int64_t stride, int kt, int klo, int khi) {
-#pragma unroll
-    for (int j = 0; j < kBK * W / 4 / kThreads; ++j) {
-        const int f = (int)threadIdx.x + j * kThreads;
-        const int row = f / (W / 4), c4 = f % (W / 4);
-        const int s = kt * kBK + row;
-        const int sc = min(max(s, klo), khi - 1);
-        const float4 x = *reinterpret_cast<const float4*>(base + sc * stride + 4 * c4);
-        const bool ok = (s >= klo) & (s < khi);
-        st[j].x = ok ? x.x : 0.0f;
-        st[j].y = ok ? x.y : 0.0f;
-        st[j].z = ok ? x.z : 0.0f;
-        st[j].w = ok ? x.w : 0.0f;
-    }
-}
-
-template <int W>
-__device__ __forceinline__ void stage_rows(const float4 (&st)[kBK * W / 4 / kThreads], float* tile) {
-#pragma unroll
-    for (int j = 0; j < kBK * W / 4 / kThreads; ++j) {
-        const int f = (int)threadIdx.x + j * kThreads;
-        const int row = f / (W / 4), c4 = f % (W / 4);
-        *reinterpret_cast<float4*>(tile + row * (W + kPad) + 4 * c4) = st[j];
-    }
-}
-
 template <int D, int DV, bool EPI>
 __global__ __launch_bounds__(kThreads, prefill_min_waves(D, DV)) void prefill_kernel(
-    Problem p, PrefillArgs a) {
+    Problem p, Args a) {
     using Sh = PrefillShape<D, DV>;
     constexpr int KLD = Sh::KLD, VLD = Sh::VLD, NB = Sh::NB;
     extern __shared__ float lds[];
@@ -150,19 +108,8 @@ __global__ __launch_bounds__(kThreads, prefill_min_waves(D, DV)) void prefill_ke
 
     const int hpg = p.H / p.G;
     const int qsub = kWaves / a.nh;
-    // Workgroups are dealt round-robin to the 8 XCDs (each with its own L2).
-    // Renumber them so that each XCD gets a contiguous run of (KV head, query
-    // block, key part) work: the K/V of a KV head then stays in one L2.
-    // Within a run, the heaviest (latest, for causal) query blocks start first.
-    const int nwg = (int)gridDim.x;
-    int wid = (int)blockIdx.x;
-    if (nwg % kXcds == 0) wid = (wid % kXcds) * (nwg / kXcds) + wid / kXcds;
-    const int ks = wid % a.ksplit;
-    const int yq = wid / a.ksplit / a.qblocks;
-    const int xq = wid / a.ksplit % a.qblocks;
-    const int qb = a.causal_order ? (a.qblocks - 1 - xq) : xq;
-    const int g = yq / a.hgroups;
-    const int hgi = yq % a.hgroups;
+    const Coords c = wg_coords(a);
+    const int ks = c.ks, qb = c.qb, g = c.g, hgi = c.hgi;
     const int h = g * hpg + hgi * a.nh + wave % a.nh;
     const int qwg0 = qb * qsub * kBQ;                 // first query row of the workgroup
     const int q0 = qwg0 + (wave / a.nh) * kBQ;        // first query row of this wave
@@ -187,15 +134,8 @@ __global__ __launch_bounds__(kThreads, prefill_min_waves(D, DV)) void prefill_ke
 
     // Keys any query row of the workgroup can see.
     const int wg_last = min(qwg0 + qsub * kBQ, T) - 1;
-    const int pf = p.ep.pos_offset + qwg0, pl = p.ep.pos_offset + wg_last;
-    int klo = 0, khi = S;
-    if (p.ep.causal) {
-        khi = min(S, pl + 1);
-        if (p.ep.window > 0) klo = max(0, pf - p.ep.window + 1);
-    } else if (p.ep.window > 0) {
-        klo = max(0, pf - p.ep.window);
-        khi = min(S, pl + p.ep.window + 1);
-    }
+    int klo, khi;
+    visible_keys(p.ep, S, p.ep.pos_offset + qwg0, p.ep.pos_offset + wg_last, klo, khi);
     // This wave's own query positions (for whole-tile visibility checks).
     const int wq_last = min(q0 + kBQ, T) - 1;
     const int wpf = p.ep.pos_offset + q0, wpl = p.ep.pos_offset + max(wq_last, q0);
@@ -221,33 +161,20 @@ __global__ __launch_bounds__(kThreads, prefill_min_waves(D, DV)) void prefill_ke
 
     const float qk_scale = p.ep.scale * kLog2e;
     if (kt0 < kt1) {
-        fetch_rows<D>(kst, kg, kstride, kt0, klo, khi);
-        fetch_rows<DV>(vst, vg, vstride, kt0, klo, khi);
-        stage_rows<D>(kst, ktile);
-        stage_rows<DV>(vst, vtile);
+        fetch_rows<D, kThreads>(kst, kg, kstride, kt0, klo, khi);
+        fetch_rows<DV, kThreads>(vst, vg, vstride, kt0, klo, khi);
+        stage_rows<D, kThreads>(kst, ktile);
+        stage_rows<DV, kThreads>(vst, vtile);
     }
     for (int kt = kt0; kt < kt1; ++kt) {
         const int buf = (kt - kt0) & 1;
         const bool more = kt + 1 < kt1;
         __syncthreads();  // tile `kt` is in LDS; everyone is done with the other buffer
-        if (more) fetch_rows<D>(kst, kg, kstride, kt + 1, klo, khi);
+        if (more) fetch_rows<D, kThreads>(kst, kg, kstride, kt + 1, klo, khi);
 
-        const int s_first = kt * kBK, s_last = s_first + kBK - 1;
-        // Does any query of this wave see any key of the tile? Do all see all?
-        bool any_vis;
-        bool all_vis;
-        if (p.ep.causal) {
-            any_vis = s_first <= wpl && (p.ep.window == 0 || s_last > wpf - p.ep.window);
-            all_vis = s_last <= wpf && (p.ep.window == 0 || s_first > wpl - p.ep.window);
-        } else if (p.ep.window > 0) {
-            any_vis = s_first <= wpl + p.ep.window && s_last >= wpf - p.ep.window;
-            all_vis = max(max(abs(wpf - s_first), abs(wpf - s_last)),
-                          max(abs(wpl - s_first), abs(wpl - s_last))) <= p.ep.window;
-        } else {
-            any_vis = true;
-            all_vis = true;
-        }
-        all_vis = all_vis && s_first >= klo && s_last < khi;
+        const int s_first = kt * kBK;
+        bool any_vis, all_vis;
+        tile_visibility(p.ep, s_first, s_first + kBK - 1, wpf, wpl, klo, khi, any_vis, all_vis);
 
         const float* kt_ = ktile + buf * kBK * KLD;
         const float* vt_ = vtile + buf * kBK * VLD;
@@ -274,16 +201,7 @@ __global__ __launch_bounds__(kThreads, prefill_min_waves(D, DV)) void prefill_ke
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int s = s_first + 8 * (r >> 2) + 4 * half + (r & 3);
-                float xs;
-                if constexpr (EPI) {
-                    float b = 0.0f;
-                    const int sc = min(s, S - 1), tc = min(t, T - 1);
-                    if (p.ep.bias_kind == ATTN_BIAS_TS) b = p.bias[(int64_t)tc * S + sc];
-                    else if (p.ep.bias_kind == ATTN_BIAS_HTS) b = p.bias[((int64_t)h * T + tc) * S + sc];
-                    xs = score_epilogue(sacc[r], p.ep, h, pos, s, b) * kLog2e;
-                } else {
-                    xs = sacc[r] * qk_scale;
-                }
+                float xs = score2<EPI>(p, sacc[r], qk_scale, h, t, pos, s);
                 if (!all_vis) {
                     const bool vis = (s >= klo) & (s < khi) & key_visible(p.ep, pos, s);
                     xs = vis ? xs : -INFINITY;
@@ -291,7 +209,7 @@ __global__ __launch_bounds__(kThreads, prefill_min_waves(D, DV)) void prefill_ke
                 x[r] = xs;
             }
         }
-        if (more) stage_rows<D>(kst, ktile + (buf ^ 1) * kBK * KLD);
+        if (more) stage_rows<D, kThreads>(kst, ktile + (buf ^ 1) * kBK * KLD);
 
         if (any_vis) {
             // Online softmax for this lane's query (both halves share the max).
@@ -315,7 +233,7 @@ __global__ __launch_bounds__(kThreads, prefill_min_waves(D, DV)) void prefill_ke
                 l += x[r];
             }
         }
-        if (more) fetch_rows<DV>(vst, vg, vstride, kt + 1, klo, khi);
+        if (more) fetch_rows<DV, kThreads>(vst, vg, vstride, kt + 1, klo, khi);
 
         if (any_vis) {
             // O^T += V^T P^T: k-step r uses keys f(r, half) and P from register r.
@@ -329,7 +247,7 @@ __global__ __launch_bounds__(kThreads, prefill_min_waves(D, DV)) void prefill_ke
                 if (NB * (r + 1) % 16 == 0) __builtin_amdgcn_sched_barrier(0);
             }
         }
-        if (more) stage_rows<DV>(vst, vtile + (buf ^ 1) * kBK * VLD);
+        if (more) stage_rows<DV, kThreads>(vst, vtile + (buf ^ 1) * kBK * VLD);
     }
 
     // Register r of block b is dv = NB*(8(r/4) + 4 half + r%4) + b.
@@ -366,13 +284,12 @@ __global__ __launch_bounds__(kThreads, prefill_min_waves(D, DV)) void prefill_ke
 }
 
 template <int D, int DV, bool EPI>
-hipError_t launch_t(const Problem& p, const PrefillArgs& a, const Launch& L) {
+hipError_t launch_t(const Problem& p, const Args& a, const Launch& L) {
     auto kern = prefill_kernel<D, DV, EPI>;
     constexpr size_t lds = PrefillShape<D, DV>::lds_bytes;
     static bool configured = false;
     if (!configured) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        const hipError_t e = set_lds_limit(kern, lds);
         if (e != hipSuccess) return e;
         configured = true;
     }
@@ -381,22 +298,28 @@ hipError_t launch_t(const Problem& p, const PrefillArgs& a, const Launch& L) {
 }
 
 template <int D, int DV>
-hipError_t launch_dims(const Problem& p, const PrefillArgs& a, const Launch& L) {
+hipError_t launch_dims(const Problem& p, const Args& a, const Launch& L) {
     const bool epi = p.ep.softcap > 0.0f || p.ep.has_alibi || p.ep.bias_kind != ATTN_BIAS_NONE;
     return epi ? launch_t<D, DV, true>(p, a, L) : launch_t<D, DV, false>(p, a, L);
 }
 
 }  // namespace
 
+hipError_t launch_prefill16(const Problem& p, const pf::Args& a, const Launch& L);
+
 bool prefill_supported(int D, int Dv) {
     return (D == 64 && Dv == 64) || (D == 128 && Dv == 128) || (D == 192 && Dv == 128) ||
            (D == 256 && Dv == 256);
 }
 
-int prefill_waves_per_simd(int D, int Dv) { return prefill_min_waves(D, Dv); }
+// Workgroups per CU the prefill kernels reach (registers and LDS).
+int prefill_wgs_per_cu(int variant, int D, int Dv) {
+    if (variant == 16) return D + Dv <= 256 ? 2 : 1;
+    return prefill_min_waves(D, Dv);
+}
 
 hipError_t launch_prefill(const Problem& p, const PrefillPlan& plan, float* ws, const Launch& L) {
-    PrefillArgs a;
+    Args a;
     a.nh = plan.nh;
     a.hgroups = (p.H / p.G) / plan.nh;
     a.qblocks = plan.qblocks;
@@ -406,6 +329,8 @@ hipError_t launch_prefill(const Problem& p, const PrefillPlan& plan, float* ws, 
     if (a.nh < 1 || a.hgroups < 1 || a.qblocks < 1 || a.ksplit < 1) return hipErrorInvalidValue;
     if (a.ksplit > 1 && !ws) return hipErrorInvalidValue;
     if ((int64_t)a.qblocks * p.G * a.hgroups * a.ksplit > INT32_MAX) return hipErrorInvalidValue;
+    if (plan.variant == 16) return launch_prefill16(p, a, L);
+    if (plan.variant != 32) return hipErrorInvalidValue;
     if (p.D == 64 && p.Dv == 64) return launch_dims<64, 64>(p, a, L);
     if (p.D == 128 && p.Dv == 128) return launch_dims<128, 128>(p, a, L);
     if (p.D == 192 && p.Dv == 128) return launch_dims<192, 128>(p, a, L);

@@ -1,0 +1,143 @@
+// Pieces shared by the two prefill kernels (prefill.hip: 32x32x2 MFMA,
+// 4 waves of 32 query rows; prefill16.hip: 16x16x4 MFMA, 8 waves of 16 query
+// rows): workgroup numbering, the visible key range, tile visibility, and
+// the global -> LDS staging of K/V tiles.
+#pragma once
+
+#include "device_common.h"
+
+namespace attn {
+namespace pf {
+
+constexpr int kBK = 32;       // key rows per LDS tile
+constexpr int kPad = 4;       // floats of padding per LDS row (bank spread)
+constexpr float kLazy = 8.0f; // log2 of the largest weight before the reference max moves
+constexpr int kXcds = 8;      // MI355X: 8 XCDs of 32 CUs, each with its own L2
+
+// Workgroup layout chosen on the host: nh heads of one KV group side by side,
+// each with the rest of the workgroup's waves on consecutive query blocks, and
+// ksplit key-range parts per workgroup.
+struct Args {
+    int nh;            // heads per workgroup
+    int hgroups;       // head groups per KV head = (heads/kvHeads) / nh
+    int qblocks;       // workgroups along the query rows
+    int ksplit;        // parts of each workgroup's key range (1: write out directly)
+    int causal_order;  // 1: heaviest query blocks first
+    float* ws;         // partial states when ksplit > 1
+};
+
+struct Coords {
+    int ks;   // key-range part
+    int g;    // KV head
+    int hgi;  // head group within the KV head
+    int qb;   // query block
+};
+
+// Workgroups are dealt round-robin to the XCDs. Renumber them so that each
+// XCD gets a contiguous run of (KV head, query block, key part) work: the K/V
+// of a KV head then stays in one L2. Within a run the heaviest (latest, for
+// causal) query blocks start first.
+__device__ __forceinline__ Coords wg_coords(const Args& a) {
+    const int nwg = (int)gridDim.x;
+    int wid = (int)blockIdx.x;
+    if (nwg % kXcds == 0) wid = (wid % kXcds) * (nwg / kXcds) + wid / kXcds;
+    Coords c;
+    c.ks = wid % a.ksplit;
+    const int yq = wid / a.ksplit / a.qblocks;
+    const int xq = wid / a.ksplit % a.qblocks;
+    c.qb = a.causal_order ? (a.qblocks - 1 - xq) : xq;
+    c.g = yq / a.hgroups;
+    c.hgi = yq % a.hgroups;
+    return c;
+}
+
+// Keys that any query row at positions [pf, pl] can see (graph protocol op
+// catalogue, op `attention`, params causal and window).
+__device__ __forceinline__ void visible_keys(const Epilogue& e, int S, int pf, int pl, int& klo,
+                                             int& khi) {
+    klo = 0;
+    khi = S;
+    if (e.causal) {
+        khi = min(S, pl + 1);
+        if (e.window > 0) klo = max(0, pf - e.window + 1);
+    } else if (e.window > 0) {
+        klo = max(0, pf - e.window);
+        khi = min(S, pl + e.window + 1);
+    }
+}
+
+// Whether any / every query at positions [wpf, wpl] sees any / every key of
+// [s_first, s_last] (every key also inside [klo, khi)).
+__device__ __forceinline__ void tile_visibility(const Epilogue& e, int s_first, int s_last, int wpf,
+                                                int wpl, int klo, int khi, bool& any_vis,
+                                                bool& all_vis) {
+    if (e.causal) {
+        any_vis = s_first <= wpl && (e.window == 0 || s_last > wpf - e.window);
+        all_vis = s_last <= wpf && (e.window == 0 || s_first > wpl - e.window);
+    } else if (e.window > 0) {
+        any_vis = s_first <= wpl + e.window && s_last >= wpf - e.window;
+        all_vis = max(max(abs(wpf - s_first), abs(wpf - s_last)),
+                      max(abs(wpl - s_first), abs(wpl - s_last))) <= e.window;
+    } else {
+        any_vis = true;
+        all_vis = true;
+    }
+    all_vis = all_vis && s_first >= klo && s_last < khi;
+}
+
+// Global -> registers -> LDS staging of the rows [kt*kBK, kt*kBK + kBK) of a
+// K or V tile (width W floats, global row stride `stride`) by NT threads.
+// Rows outside [klo, khi) are loaded from a clamped, in-bounds row and
+// replaced by zeros, so the loads need no branches.
+template <int W, int NT>
+__device__ __forceinline__ void fetch_rows(float4 (&st)[kBK * W / 4 / NT], const float* base,
+                                           int64_t stride, int kt, int klo, int khi) {
+#pragma unroll
+    for (int j = 0; j < kBK * W / 4 / NT; ++j) {
+        const int f = (int)threadIdx.x + j * NT;
+        const int row = f / (W / 4), c4 = f % (W / 4);
+        const int s = kt * kBK + row;
+        const int sc = min(max(s, klo), khi - 1);
+        const float4 x = *reinterpret_cast<const float4*>(base + sc * stride + 4 * c4);
+        const bool ok = (s >= klo) & (s < khi);
+        st[j].x = ok ? x.x : 0.0f;
+        st[j].y = ok ? x.y : 0.0f;
+        st[j].z = ok ? x.z : 0.0f;
+        st[j].w = ok ? x.w : 0.0f;
+    }
+}
+
+template <int W, int NT>
+__device__ __forceinline__ void stage_rows(const float4 (&st)[kBK * W / 4 / NT], float* tile) {
+#pragma unroll
+    for (int j = 0; j < kBK * W / 4 / NT; ++j) {
+        const int f = (int)threadIdx.x + j * NT;
+        const int row = f / (W / 4), c4 = f % (W / 4);
+        *reinterpret_cast<float4*>(tile + row * (W + kPad) + 4 * c4) = st[j];
+    }
+}
+
+// Score of register value `dot` for key s and query row t of head h, in the
+// base-2 domain: the full epilogue when EPI, else just the scale.
+template <bool EPI>
+__device__ __forceinline__ float score2(const Problem& p, float dot, float qk_scale, int h, int t,
+                                        int pos, int s) {
+    if constexpr (EPI) {
+        float b = 0.0f;
+        const int sc = min(s, (int)p.S - 1), tc = min(t, (int)p.T - 1);
+        if (p.ep.bias_kind == ATTN_BIAS_TS) b = p.bias[(int64_t)tc * p.S + sc];
+        else if (p.ep.bias_kind == ATTN_BIAS_HTS) b = p.bias[((int64_t)h * p.T + tc) * p.S + sc];
+        return score_epilogue(dot, p.ep, h, pos, s, b) * kLog2e;
+    } else {
+        return dot * qk_scale;
+    }
+}
+
+template <typename K>
+hipError_t set_lds_limit(K kern, size_t bytes) {
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+}  // namespace pf
+}  // namespace attn

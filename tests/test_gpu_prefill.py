@@ -14,6 +14,14 @@ pytestmark = pytest.mark.gpu
 BIAS_KIND = {None: 0, "TS": 1, "HTS": 2}
 
 
+@pytest.fixture(params=[32, 16], ids=["mfma32", "mfma16"])
+def variant(request):
+    """Run a test on both prefill kernels (32x32x2 and 16x16x4 MFMA)."""
+    ga.attn_set_option("prefill_variant", request.param)
+    yield request.param
+    ga.attn_set_option("prefill_variant", 0)
+
+
 def _check(w, rows=None, what=None, path="prefill"):
     q, k, v, bias = w.tensors()
     params = w.params()
@@ -26,7 +34,7 @@ def _check(w, rows=None, what=None, path="prefill"):
 # groups), 2 (2 heads x 2 query blocks), 1 (4 query blocks), 3 (1 head x 4).
 @pytest.mark.parametrize("D, Dv", [(64, 64), (128, 128), (192, 128), (256, 256)])
 @pytest.mark.parametrize("H, G", [(8, 2), (8, 1), (4, 2), (4, 4), (6, 2)])
-def test_prefill_shapes_ragged(D, Dv, H, G):
+def test_prefill_shapes_ragged(D, Dv, H, G, variant):
     w = workloads.Workload("prefill shape", T=100, S=100, heads=H, kvHeads=G, headDim=D, vHeadDim=Dv,
                            seed=D + 7 * H + G)
     _check(w)
@@ -41,7 +49,7 @@ def test_prefill_shapes_ragged(D, Dv, H, G):
     dict(softcap=10.0, window=50, alibi=True, bias="HTS", bias_mask_prob=0.1, std=2.0),
 ])
 @pytest.mark.parametrize("D, Dv", [(128, 128), (256, 256), (192, 128)])
-def test_prefill_features(feature, D, Dv):
+def test_prefill_features(feature, D, Dv, variant):
     w = workloads.Workload("prefill features", T=150, S=150, heads=8, kvHeads=2, headDim=D, vHeadDim=Dv,
                            **feature)
     q, k, v, bias = w.tensors()
@@ -52,7 +60,7 @@ def test_prefill_features(feature, D, Dv):
 
 @pytest.mark.parametrize("T, S, P0", [(64, 200, 136), (33, 90, 57), (1, 300, 299), (200, 64, 0),
                                       (70, 400, 100)])
-def test_prefill_pos_offset_and_rectangles(T, S, P0):
+def test_prefill_pos_offset_and_rectangles(T, S, P0, variant):
     # Chunked prefill against a longer cache (rows past P0+T-1 may hold anything).
     w = workloads.Workload("chunked", T=T, S=S, heads=8, kvHeads=2, headDim=128, posOffset=P0)
     q, k, v, _ = w.tensors()
@@ -67,7 +75,7 @@ def test_prefill_pos_offset_and_rectangles(T, S, P0):
     assert np.isfinite(got).all()
 
 
-def test_prefill_window_never_reads_outside():
+def test_prefill_window_never_reads_outside(variant):
     # Keys before every row's window are NaN: they must not be read.
     w = workloads.Workload("window", T=64, S=300, heads=8, kvHeads=2, headDim=128, posOffset=236,
                            window=40)
@@ -77,7 +85,7 @@ def test_prefill_window_never_reads_outside():
     compare(q, k, v, None, w.params(), what="window with NaN before it")
 
 
-def test_prefill_empty_rows_are_zero():
+def test_prefill_empty_rows_are_zero(variant):
     # Non-causal window where the last rows see nothing (keys end at 10).
     w = workloads.Workload("empty rows", T=40, S=10, heads=4, kvHeads=4, headDim=128, causal=False,
                            window=3)
@@ -111,7 +119,7 @@ def test_prefill_is_deterministic():
 
 # ---- full-size workloads, sampled rows --------------------------------------
 
-def test_llama_prefill_full_size_sampled():
+def test_llama_prefill_full_size_sampled(variant):
     w = workloads.LLAMA_PREFILL
     _check(w, rows=sample_rows(w.T, seed=1, n_random=40, edges=(2048,)))
 
@@ -121,18 +129,18 @@ def test_llama_chunked_prefill_full_size():
     _check(w, rows=sample_rows(w.T, seed=2, n_random=64))
 
 
-def test_gemma2_swa_full_size_sampled():
+def test_gemma2_swa_full_size_sampled(variant):
     w = workloads.GEMMA2_SWA
     _check(w, rows=sample_rows(w.T, seed=3, n_random=24, edges=(4095, 4096, 4097, 6000)))
 
 
-def test_latent_noncausal_full_size():
+def test_latent_noncausal_full_size(variant):
     w = workloads.LATENT_NONCAUSAL
     _check(w, rows=sample_rows(w.T, seed=4, n_random=64))
 
 
 @pytest.mark.parametrize("splits", [2, 3, 7])
-def test_prefill_key_splits_match(splits):
+def test_prefill_key_splits_match(splits, variant):
     # Forced key-range splits (merged by the combine kernel) give the same result.
     w = workloads.Workload("split prefill", T=70, S=500, heads=8, kvHeads=2, headDim=128, posOffset=430,
                            alibi=True)
