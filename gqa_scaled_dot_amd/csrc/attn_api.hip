@@ -37,6 +37,7 @@ int ok() {
 
 // Process-wide tuning overrides (attn_set_option).
 int64_t g_opt_decode_splits = 0;
+int64_t g_opt_decode_depth = 0;
 int64_t g_opt_prefill_splits = 0;
 int64_t g_opt_prefill_variant = 0;
 int64_t g_opt_force_path = 0;
@@ -242,6 +243,7 @@ int make_plan(const Resolved& r, Plan* plan) {
     if (path == ATTN_PATH_DECODE) {
         attn::DecodePlan& d = plan->decode;
         d.nq = next_pow2_nq(nrows);
+        d.depth = g_opt_decode_depth ? (int32_t)g_opt_decode_depth : 2;
         d.range = kr;
         const int64_t n = kr.hi - kr.lo;
         int64_t splits = g_opt_decode_splits;
@@ -524,6 +526,12 @@ int attn_set_option(const char* name, int64_t value) {
         if (value < 0 || value > kDecodeMaxSplits)
             return fail(ATTN_ERR_INVALID, "decode_splits: must be in 0..%lld", (long long)kDecodeMaxSplits);
         g_opt_decode_splits = value;
+        return ok();
+    }
+    if (!strcmp(name, "decode_depth")) {
+        if (value != 0 && value != 2 && value != 3)
+            return fail(ATTN_ERR_INVALID, "decode_depth: must be 0, 2 or 3");
+        g_opt_decode_depth = value;
         return ok();
     }
     if (!strcmp(name, "prefill_splits")) {

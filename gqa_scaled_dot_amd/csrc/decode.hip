@@ -66,7 +66,9 @@ __device__ __forceinline__ bool chunk_all_visible(const Epilogue& e, int pos_fir
 
 // EPI: whether softcap, ALiBi or a bias can be on; without them the score
 // is the scaled dot product and the code for the rest is left out.
-template <int D, int DV, int NQ, bool EPI>
+// DEPTH: batches of U rows per row group held in registers as a ring; DEPTH-1
+// of them are in flight while one is used.
+template <int D, int DV, int NQ, bool EPI, int DEPTH>
 __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, DecodePlan plan,
                                                                    float* __restrict__ ws) {
     using Sh = DecodeShape<D, DV, NQ>;
@@ -200,15 +202,25 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
     };
 
     {
-        float4 ka[U][KJ], va[U][VJ], kb[U][KJ], vb[U][VJ];
-        int s = k0 + rg * U;
-        if (s < k1) load(ka, va, s);
-        for (; s < k1; s += 2 * kStep) {
-            if (s + kStep < k1) load(kb, vb, s + kStep);
-            process(ka, va, s);
-            if (s + kStep >= k1) break;
-            if (s + 2 * kStep < k1) load(ka, va, s + 2 * kStep);
-            process(kb, vb, s + kStep);
+        // Ring of DEPTH batches: batch i of a round is used while batches
+        // i+1 .. i+DEPTH-1 are in flight.
+        float4 kr[DEPTH][U][KJ], vr[DEPTH][U][VJ];
+        const int s0 = k0 + rg * U;
+#pragma unroll
+        for (int i = 0; i < DEPTH - 1; ++i)
+            if (s0 + i * kStep < k1) load(kr[i], vr[i], s0 + i * kStep);
+        bool done = false;
+        for (int s = s0; s < k1 && !done; s += DEPTH * kStep) {
+#pragma unroll
+            for (int i = 0; i < DEPTH; ++i) {
+                const int sn = s + (i + DEPTH - 1) * kStep;
+                if (sn < k1) load(kr[(i + DEPTH - 1) % DEPTH], vr[(i + DEPTH - 1) % DEPTH], sn);
+                if (s + i * kStep >= k1) {
+                    done = true;
+                    break;
+                }
+                process(kr[i], vr[i], s + i * kStep);
+            }
         }
     }
 
@@ -395,12 +407,27 @@ __global__ __launch_bounds__(kThreads) void combine_few_kernel(Problem p, int ns
     *orow = make_float4(a.x * inv, a.y * inv, a.z * inv, a.w * inv);
 }
 
-template <int D, int DV, int NQ>
-hipError_t launch_split_t(const Problem& p, const DecodePlan& plan, float* ws, const Launch& L) {
+template <int D, int DV, int NQ, int DEPTH>
+hipError_t launch_split_d(const Problem& p, const DecodePlan& plan, float* ws, const Launch& L) {
     const dim3 grid((unsigned)plan.splits, (unsigned)p.G);
     const bool epi = p.ep.softcap > 0.0f || p.ep.has_alibi || p.ep.bias_kind != ATTN_BIAS_NONE;
-    if (epi) return launch_kernel(decode_split_kernel<D, DV, NQ, true>, grid, dim3(kThreads), 0, L, p, plan, ws);
-    return launch_kernel(decode_split_kernel<D, DV, NQ, false>, grid, dim3(kThreads), 0, L, p, plan, ws);
+    if (epi) return launch_kernel(decode_split_kernel<D, DV, NQ, true, DEPTH>, grid, dim3(kThreads), 0, L, p, plan, ws);
+    return launch_kernel(decode_split_kernel<D, DV, NQ, false, DEPTH>, grid, dim3(kThreads), 0, L, p, plan, ws);
+}
+
+// A third ring batch only where it fits beside q and acc without spilling:
+// (KJ+VJ) * (24 + 4 NQ) registers for the ring, q and acc, under 200.
+template <int D, int DV, int NQ>
+constexpr bool depth3_fits() {
+    return (D / 64 + DV / 64) * (24 + 4 * NQ) < 200;
+}
+
+template <int D, int DV, int NQ>
+hipError_t launch_split_t(const Problem& p, const DecodePlan& plan, float* ws, const Launch& L) {
+    if constexpr (depth3_fits<D, DV, NQ>()) {
+        if (plan.depth >= 3) return launch_split_d<D, DV, NQ, 3>(p, plan, ws, L);
+    }
+    return launch_split_d<D, DV, NQ, 2>(p, plan, ws, L);
 }
 
 template <int D, int DV>

@@ -44,6 +44,7 @@ struct KeyRange {
 struct DecodePlan {
     int32_t nq;       // query rows per KV group this instance holds (template value)
     int32_t splits;   // key-range splits per KV group
+    int32_t depth;    // batches in the split kernel's register ring (2 or 3)
     int64_t chunk;    // keys per split (multiple of the row-group step)
     KeyRange range;
 };
