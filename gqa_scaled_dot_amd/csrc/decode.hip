@@ -45,8 +45,9 @@ struct DecodeShape {
     // Key rows per row group per batch. Two batches of two rows are in flight
     // per lane (16 (KJ+VJ) registers); measured on the Llama- and
     // latent-shaped decodes, four-row batches ran slower (more registers, no
-    // more bandwidth).
-    static constexpr int U = 2;
+    // more bandwidth). Where two-row batches and the query rows' q and acc
+    // (4 NQ (KJ+VJ) registers) would pass ~170 registers, batches are one row.
+    static constexpr int U = (KJ + VJ) * (16 + 4 * NQ) <= 170 ? 2 : 1;
 };
 
 __device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
@@ -123,19 +124,33 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
     const bool dense = chunk_all_visible(p.ep, p.ep.pos_offset, p.ep.pos_offset + (int)p.T - 1, k0, k1);
 
     // Rows past the chunk's end are clamped to its last row (in bounds) and
-    // their scores masked, so the loads need no branches.
-    auto load = [&](float4 (&kf)[U][KJ], float4 (&vf)[U][VJ], int s0) {
+    // their scores masked, so the loads need no branches. The bias entries of
+    // a batch travel with its K/V rows, so their latency is hidden too.
+    constexpr int BR = EPI ? NQ : 1;
+    auto load = [&](float4 (&kf)[U][KJ], float4 (&vf)[U][VJ], float (&bf)[BR][U], int s0) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const uint32_t row = (uint32_t)(min(s0 + u, k1 - 1) - k0);
+            const int sc = min(s0 + u, k1 - 1);
+            const uint32_t row = (uint32_t)(sc - k0);
 #pragma unroll
             for (int j = 0; j < KJ; ++j) kf[u][j] = load_stream4(kwg + row * kstride + 64 * j);
 #pragma unroll
             for (int j = 0; j < VJ; ++j) vf[u][j] = load_stream4(vwg + row * vstride + 64 * j);
+            if constexpr (EPI) {
+#pragma unroll
+                for (int r = 0; r < NQ; ++r) {
+                    float b = 0.0f;
+                    if (p.ep.bias_kind == ATTN_BIAS_TS) b = p.bias[(int64_t)tt[r] * p.S + sc];
+                    else if (p.ep.bias_kind == ATTN_BIAS_HTS)
+                        b = p.bias[((int64_t)hh[r] * p.T + tt[r]) * p.S + sc];
+                    bf[r][u] = b;
+                }
+            }
         }
     };
 
-    auto process = [&](const float4 (&kf)[U][KJ], const float4 (&vf)[U][VJ], int s0) {
+    auto process = [&](const float4 (&kf)[U][KJ], const float4 (&vf)[U][VJ], const float (&bf)[BR][U],
+                       int s0) {
         const bool check = !(dense && s0 + U <= k1);
         float x[NQ][U];
 #pragma unroll
@@ -149,12 +164,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
                 const int s = s0 + u;
                 float xs;
                 if constexpr (EPI) {
-                    const int sc = min(s, k1 - 1);  // in bounds for the bias read
-                    float b = 0.0f;
-                    if (p.ep.bias_kind == ATTN_BIAS_TS) b = p.bias[(int64_t)tt[r] * p.S + sc];
-                    else if (p.ep.bias_kind == ATTN_BIAS_HTS)
-                        b = p.bias[((int64_t)hh[r] * p.T + tt[r]) * p.S + sc];
-                    xs = score_epilogue(dot, p.ep, hh[r], pos[r], s, b) * kLog2e;
+                    xs = score_epilogue(dot, p.ep, hh[r], pos[r], s, bf[r][u]) * kLog2e;
                 } else {
                     xs = dot * (p.ep.scale * kLog2e);
                 }
@@ -205,21 +215,23 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
         // Ring of DEPTH batches: batch i of a round is used while batches
         // i+1 .. i+DEPTH-1 are in flight.
         float4 kr[DEPTH][U][KJ], vr[DEPTH][U][VJ];
+        float br[DEPTH][BR][U];
         const int s0 = k0 + rg * U;
 #pragma unroll
         for (int i = 0; i < DEPTH - 1; ++i)
-            if (s0 + i * kStep < k1) load(kr[i], vr[i], s0 + i * kStep);
+            if (s0 + i * kStep < k1) load(kr[i], vr[i], br[i], s0 + i * kStep);
         bool done = false;
         for (int s = s0; s < k1 && !done; s += DEPTH * kStep) {
 #pragma unroll
             for (int i = 0; i < DEPTH; ++i) {
                 const int sn = s + (i + DEPTH - 1) * kStep;
-                if (sn < k1) load(kr[(i + DEPTH - 1) % DEPTH], vr[(i + DEPTH - 1) % DEPTH], sn);
+                const int nx = (i + DEPTH - 1) % DEPTH;  // a constant once unrolled
+                if (sn < k1) load(kr[nx], vr[nx], br[nx], sn);
                 if (s + i * kStep >= k1) {
                     done = true;
                     break;
                 }
-                process(kr[i], vr[i], s + i * kStep);
+                process(kr[i], vr[i], br[i], s + i * kStep);
             }
         }
     }

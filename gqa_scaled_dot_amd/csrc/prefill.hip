@@ -180,6 +180,14 @@ __global__ __launch_bounds__(kThreads, prefill_min_waves(D, DV)) void prefill_ke
         const float* vt_ = vtile + buf * kBK * VLD;
         float x[16];
         if (any_vis) {
+            // Bias entries of the tile, requested before the matrix work so
+            // that it hides their latency.
+            float bpre[EPI ? 16 : 1];
+            if constexpr (EPI) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    bpre[r] = bias_at(p, h, t, s_first + 8 * (r >> 2) + 4 * half + (r & 3));
+            }
             // S^T = K Q^T for 32 keys x 32 queries.
             f32x16 sacc;
 #pragma unroll
@@ -201,7 +209,7 @@ __global__ __launch_bounds__(kThreads, prefill_min_waves(D, DV)) void prefill_ke
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int s = s_first + 8 * (r >> 2) + 4 * half + (r & 3);
-                float xs = score2<EPI>(p, sacc[r], qk_scale, h, t, pos, s);
+                float xs = score2<EPI>(p, sacc[r], qk_scale, h, pos, s, bpre[EPI ? r : 0]);
                 if (!all_vis) {
                     const bool vis = (s >= klo) & (s < khi) & key_visible(p.ep, pos, s);
                     xs = vis ? xs : -INFINITY;

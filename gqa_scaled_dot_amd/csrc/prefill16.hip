@@ -131,6 +131,16 @@ __global__ __launch_bounds__(kThreads16, 1) void prefill16_kernel(Problem p, Arg
         const float* vt_ = vtile + buf * kBK * VLD;
         float x[2][4];
         if (any_vis) {
+            // Bias entries of the tile, requested before the matrix work so
+            // that it hides their latency.
+            float bpre[2][EPI ? 4 : 1];
+            if constexpr (EPI) {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        bpre[kb][r] = bias_at(p, h, t, s_first + kb * 16 + 4 * quad + r);
+            }
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
                 f32x4v sacc = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
@@ -146,7 +156,7 @@ __global__ __launch_bounds__(kThreads16, 1) void prefill16_kernel(Problem p, Arg
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int s = s_first + kb * 16 + 4 * quad + r;
-                    float xs = score2<EPI>(p, sacc[r], qk_scale, h, t, pos, s);
+                    float xs = score2<EPI>(p, sacc[r], qk_scale, h, pos, s, bpre[kb][EPI ? r : 0]);
                     if (!all_vis) {
                         const bool vis = (s >= klo) & (s < khi) & key_visible(p.ep, pos, s);
                         xs = vis ? xs : -INFINITY;

@@ -117,20 +117,23 @@ __device__ __forceinline__ void stage_rows(const float4 (&st)[kBK * W / 4 / NT],
     }
 }
 
-// Score of register value `dot` for key s and query row t of head h, in the
-// base-2 domain: the full epilogue when EPI, else just the scale.
+// The bias entry of (head h, query row t, key s), clamped in bounds (masked
+// keys may lie outside the tensor); 0 without a bias.
+__device__ __forceinline__ float bias_at(const Problem& p, int h, int t, int s) {
+    const int sc = min(max(s, 0), (int)p.S - 1), tc = min(t, (int)p.T - 1);
+    if (p.ep.bias_kind == ATTN_BIAS_TS) return p.bias[(int64_t)tc * p.S + sc];
+    if (p.ep.bias_kind == ATTN_BIAS_HTS) return p.bias[((int64_t)h * p.T + tc) * p.S + sc];
+    return 0.0f;
+}
+
+// Score of register value `dot` for key s of the query at `pos` in head h, in
+// the base-2 domain: the full epilogue (with bias entry b) when EPI, else
+// just the scale.
 template <bool EPI>
-__device__ __forceinline__ float score2(const Problem& p, float dot, float qk_scale, int h, int t,
-                                        int pos, int s) {
-    if constexpr (EPI) {
-        float b = 0.0f;
-        const int sc = min(s, (int)p.S - 1), tc = min(t, (int)p.T - 1);
-        if (p.ep.bias_kind == ATTN_BIAS_TS) b = p.bias[(int64_t)tc * p.S + sc];
-        else if (p.ep.bias_kind == ATTN_BIAS_HTS) b = p.bias[((int64_t)h * p.T + tc) * p.S + sc];
-        return score_epilogue(dot, p.ep, h, pos, s, b) * kLog2e;
-    } else {
-        return dot * qk_scale;
-    }
+__device__ __forceinline__ float score2(const Problem& p, float dot, float qk_scale, int h, int pos,
+                                        int s, float b) {
+    if constexpr (EPI) return score_epilogue(dot, p.ep, h, pos, s, b) * kLog2e;
+    else return dot * qk_scale;
 }
 
 template <typename K>
