@@ -127,3 +127,24 @@ def test_decode_is_deterministic():
     a = run_library(q, k, v, None, w.params()).cpu().numpy()
     b = run_library(q, k, v, None, w.params()).cpu().numpy()
     np.testing.assert_array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_one_workspace_serves_every_shape_and_path():
+    # One workspace (left holding garbage between calls) reused by decode calls
+    # of several shapes and split counts and by a key-split prefill, in any
+    # order: every call must give the oracle's result.
+    t = torch()
+    ws = t.full((64 << 20,), 0x7F, dtype=t.uint8, device="cuda")
+    cases = [
+        _wl(S=5000, posOffset=4999, heads=32, kvHeads=8),
+        _wl(S=3000, posOffset=2999, heads=16, kvHeads=16, headDim=192, vHeadDim=128, bias="HTS",
+            bias_mask_prob=0.1),
+        workloads.Workload("split prefill", T=70, S=900, heads=8, kvHeads=2, headDim=128, posOffset=830),
+        _wl(S=9000, posOffset=8999, heads=8, kvHeads=1, headDim=64),
+    ]
+    for rep in range(2):
+        for w in cases:
+            q, k, v, bias = w.tensors()
+            got = ga.attn_forward(dev(q), dev(k), dev(v), dev(bias), workspace=ws, **w.params())
+            t.cuda.synchronize()
+            assert_close(got.cpu().numpy(), oracle.attention(q, k, v, bias, **w.params()), w.name)
