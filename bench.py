@@ -20,8 +20,15 @@ The same line carries `prefill`: the Llama-3-8B-shaped causal prefill
 (2 headDim + 2 vHeadDim)) over the call time give TFLOP/s, rated against the
 157.3 TFLOP/s fp32 matrix peak.
 
+`configs` lists the other workloads the same way (their own plan, kernel
+time, call rate, roofline and sampled-row parity): the Llama-shaped chunked
+prefill (T=512 at posOffset 3584), the Gemma-2-shaped sliding-window prefill
+(T=S=8192, headDim 256, softcap 50, window 4096), and the latent-shaped
+ALiBi + per-head bias decode (S=8192, headDim 192, vHeadDim 128) and
+non-causal prefill (T=S=1024).
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
-       [--prefill-steps K]
+       [--prefill-steps K] [--no-configs]
 """
 
 from __future__ import annotations
@@ -44,7 +51,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
     "decode_split": ["gqa_scaled_dot_amd/csrc/decode.hip", "gqa_scaled_dot_amd/csrc/device_common.h",
                      "gqa_scaled_dot_amd/csrc/kernels.h"],
-    "prefill": ["gqa_scaled_dot_amd/csrc/prefill.hip", "gqa_scaled_dot_amd/csrc/device_common.h",
+    "prefill": ["gqa_scaled_dot_amd/csrc/prefill.hip", "gqa_scaled_dot_amd/csrc/prefill16.hip",
+                "gqa_scaled_dot_amd/csrc/prefill_common.h", "gqa_scaled_dot_amd/csrc/device_common.h",
                 "gqa_scaled_dot_amd/csrc/kernels.h"],
 }
 
@@ -233,68 +241,97 @@ def run_decode(args):
     }
 
 
-def run_prefill(args):
+def sampled_rows(w, n_random=24):
+    """Rows whose outputs the oracle checks: both ends, the middle, seeded random ones."""
+    import numpy as np
+    fixed = [0, 1, 2, 31, 32, w.T // 2 - 1, w.T // 2, w.T - 2, w.T - 1]
+    rnd = np.random.default_rng(7).integers(0, w.T, n_random) if w.T > 1 else []
+    return sorted(set(r for r in fixed + [int(x) for x in rnd] if 0 <= r < w.T))
+
+
+def run_config(w, args, kv_buffers=1):
+    """Time attn_forward on one workload: kernel durations from dispatch-stamped
+    events, the call time from a plain loop; the result checked against the
+    oracle on sampled rows. Decode-shaped plans are rated in GB/s against HBM,
+    prefill-shaped ones in TFLOP/s against the fp32 matrix peak."""
     import numpy as np
     import torch
 
     import gqa_scaled_dot_amd as ga
     import oracle
-    import workloads
 
-    w = workloads.LLAMA_PREFILL
     params = w.params()
     dev = torch.device("cuda:0")
-    q, k, v, _ = w.tensors()
-    plan = ga.attn_plan(w.T, w.S, **params)
-    log(f"[bench] prefill workload: {w.name}; plan {plan}")
-    qd, kd, vd = (torch.from_numpy(x).to(dev) for x in (q, k, v))
+    q, k, v, bias = w.tensors()
+    kind = {None: 0, "TS": 1, "HTS": 2}[w.bias]
+    plan = ga.attn_plan(w.T, w.S, bias_kind=kind, **params)
+    log(f"[bench] workload: {w.name}; plan {plan}")
+    main_kernel = {"decode": "decode_split", "prefill": "prefill"}.get(plan["path"], "generic")
+    qd = torch.from_numpy(q).to(dev)
+    # Several copies of the K/V (and bias) so a timed call does not find them in the MALL.
+    kv = [tuple(torch.from_numpy(x).to(dev) if x is not None else None for x in (k, v, bias))
+          for _ in range(kv_buffers)]
     out = torch.empty((w.T, w.heads * w.Dv), dtype=torch.float32, device=dev)
-    call = ga.prepare_forward(qd, kd, vd, out=out, **params)
-    for _ in range(max(2, args.warmup // 5)):
-        call()
+    ws_bytes = ga.attn_workspace_size(w.T, w.S, bias_kind=kind, **params)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    calls = [ga.prepare_forward(qd, kb, vb, bb, out=out, workspace=ws, **params) for kb, vb, bb in kv]
+    n = args.prefill_steps if plan["path"] != "decode" else args.steps
+    for i in range(max(2, args.warmup // 5)):
+        calls[i % kv_buffers]()
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream(dev)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     # Kernel durations from dispatch-stamped events ...
     ga.attn_timing_enable(True)
-    for name in ("prefill", "combine"):
+    for name in (main_kernel, "combine"):
         ga.attn_timing_collect(name)
-    for _ in range(args.prefill_steps):
-        call()
+    for i in range(n):
+        calls[i % kv_buffers]()
     torch.cuda.synchronize()
-    k_ms, k_n = ga.attn_timing_collect("prefill")
-    ga.attn_timing_collect("combine")
+    k_ms, k_n = ga.attn_timing_collect(main_kernel)
+    c_ms, c_n = ga.attn_timing_collect("combine")
     ga.attn_timing_enable(False)
     # ... and the call time from a loop without them.
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
-    for _ in range(args.prefill_steps):
-        call()
+    for i in range(n):
+        calls[i % kv_buffers]()
     e1.record(stream)
     torch.cuda.synchronize()
-    ms_call = e0.elapsed_time(e1) / args.prefill_steps
-    flops = w.heads * visible_pairs(w) * (2 * w.headDim + 2 * w.Dv)
+    ms_call = e0.elapsed_time(e1) / n
     kern_s = k_ms / k_n * 1e-3
-    achieved = flops / kern_s / 1e12
-    log(f"[bench] prefill call {ms_call * 1e3:.1f} us, kernel {kern_s * 1e6:.1f} us x{k_n}, "
-        f"{achieved:.2f} TFLOP/s")
-    rows = sorted(set([0, 1, 2, 31, 32, 2047, 2048, 4094, 4095] +
-                      [int(x) for x in np.random.default_rng(7).integers(0, w.T, 24)]))
-    ref = oracle.attention(q, k, v, rows=rows, threads=cpu_threads(), **params)
+    if plan["path"] == "decode":
+        work = decode_algorithmic_bytes(w)
+        achieved, value, unit, peak, bound = work / kern_s / 1e9, work / (ms_call * 1e-3) / 1e9, \
+            "GB/s", HBM_PEAK_GBS, "hbm"
+    else:
+        work = w.heads * visible_pairs(w) * (2 * w.headDim + 2 * w.Dv)
+        achieved, value, unit, peak, bound = work / kern_s / 1e12, work / (ms_call * 1e-3) / 1e12, \
+            "TFLOP/s", FP32_PEAK_TFLOPS, "mfma"
+    log(f"[bench]   call {ms_call * 1e3:.1f} us, {main_kernel} {kern_s * 1e6:.1f} us x{k_n}"
+        + (f", combine {c_ms / c_n * 1e3:.2f} us" if c_n else "")
+        + f": {achieved:.2f} {unit} = {achieved / peak:.1%} of {peak}")
+    rows = sampled_rows(w)
+    ref = oracle.attention(q, k, v, bias, rows=rows, threads=cpu_threads(), **params)
     got = out.cpu().numpy()[rows].astype(np.float64)
     err = np.abs(got - ref)
     ok = bool(np.all(err <= 1e-4 + 1e-4 * np.abs(ref)))
-    log(f"[bench] prefill parity on {len(rows)} sampled rows: max |err| {err.max():.3e} ok={ok}")
-    return {
-        "workload": w.name, "value": round(flops / (ms_call * 1e-3) / 1e12, 3), "unit": "TFLOP/s",
-        "ms_per_call": round(ms_call, 6), "calls": args.prefill_steps,
-        "flops_per_call": flops,
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": FP32_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / FP32_PEAK_TFLOPS, 4),
-                     "traffic": measured_traffic("prefill", w.name),
-                     "kernel": "prefill", "flops_per_launch": flops,
-                     "avg_launch_us": round(kern_s * 1e6, 3)},
+    log(f"[bench]   parity on {len(rows)} sampled rows: max |err| {err.max():.3e} ok={ok}")
+    rec = {
+        "workload": w.name, "path": plan["path"], "splits": plan["splits"],
+        "value": round(value, 3), "unit": unit, "ms_per_call": round(ms_call, 6), "calls": n,
+        ("bytes_per_call" if bound == "hbm" else "flops_per_call"): work,
+        "roofline": {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
+                     "frac": round(achieved / peak, 4),
+                     "traffic": measured_traffic(main_kernel, w.name) if main_kernel in KERNEL_SOURCES else None,
+                     "kernel": main_kernel,
+                     ("bytes_per_launch" if bound == "hbm" else "flops_per_launch"): work,
+                     "avg_launch_us": round(kern_s * 1e6, 3),
+                     "combine_us": round(c_ms / c_n * 1e3, 3) if c_n else None},
         "parity": {"rows": len(rows), "max_abs_err": float(err.max()), "ok": ok},
     }
+    del kv, qd, out, ws
+    torch.cuda.empty_cache()
+    return rec
 
 
 def main():
@@ -304,6 +341,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--prefill-steps", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle timing")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="only the Llama-shaped decode and prefill, not the other workloads")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -311,8 +350,15 @@ def main():
         sys.exit(2)
     if args.steps < 1 or args.warmup < 0 or args.prefill_steps < 1:
         ap.error("--steps and --prefill-steps must be >= 1 and --warmup >= 0")
+    import workloads
     rec = run_decode(args)
-    rec["prefill"] = run_prefill(args)
+    rec["prefill"] = run_config(workloads.LLAMA_PREFILL, args)
+    if not args.no_configs:
+        # The other workloads, each on its own plan (decode-shaped ones over 4
+        # rotated K/V copies, as the Llama decode uses 2).
+        rec["configs"] = [run_config(w, args, kv_buffers=4 if w.T == 1 else 1)
+                          for w in (workloads.LLAMA_CHUNKED, workloads.GEMMA2_SWA,
+                                    workloads.LATENT_DECODE, workloads.LATENT_NONCAUSAL)]
     print(json.dumps(rec), flush=True)
 
 
