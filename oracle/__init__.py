@@ -199,3 +199,6 @@ def cache_write(cache: np.ndarray, values: np.ndarray, offset: int) -> np.ndarra
         raise ValueError("rows past the end of the cache")
     cache[offset:offset + rows] = values
     return cache
+
+
+from .rope import rope, table as rope_table  # noqa: E402  (op `rope`)

@@ -34,6 +34,27 @@ MUTANTS = {
     "max_not_subtracted": ("double p = exp(x[s] - M);", "double p = exp(x[s]);"),
 }
 
+# Slips in the rotary embedding (oracle/rope.py), caught by tests/test_oracle_rope.py.
+ROPE_MUTANTS = {
+    "rope_turn_sense": ("out[:, :, ia] = a * c - b * s", "out[:, :, ia] = a * c + b * s"),
+    "rope_half_partner": ("np.arange(half) + half", "np.arange(half) + half - 1"),
+    "rope_freq_exponent": ("return np.power(float(base), -2.0 * i / rd)",
+                           "return np.power(float(base), -1.0 * i / rd)"),
+    "rope_factor_dropped": ("c = (np.cos(ang) * af)[:, None, :]", "c = np.cos(ang)[:, None, :]"),
+    "rope_position_shift": ("pos = (p0 + np.arange(T, dtype=np.int64))",
+                            "pos = (p0 + 1 + np.arange(T, dtype=np.int64))"),
+    "rope_passthrough_scaled": ("out = y.copy()", "out = y.copy() * af"),
+    "rope_yarn_ramp_reversed": ("return theta * (1.0 - ramp) + (theta / factor) * ramp",
+                                "return theta * ramp + (theta / factor) * (1.0 - ramp)"),
+    "rope_llama3_blend_reversed": ("out[i] = (1.0 - smooth) * f / factor + smooth * f",
+                                   "out[i] = smooth * f / factor + (1.0 - smooth) * f"),
+    "rope_linear_multiplies": ("return theta / float(s[\"factor\"])", "return theta * float(s[\"factor\"])"),
+    "rope_dynamic_exponent": ("** (rd / (rd - 2.0))", "** (rd / (rd - 1.0))"),
+    "rope_longrope_sets_swapped": ('ext = s["long_factor"] if seq_len > orig else s["short_factor"]',
+                                   'ext = s["short_factor"] if seq_len > orig else s["long_factor"]'),
+    "rope_yarn_temperature": ("return 0.1 * k * math.log(scale) + 1.0", "return 0.1 * k * math.log(scale)"),
+}
+
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_pins_kill_mutant(name, tmp_path):
@@ -58,6 +79,28 @@ def test_pins_kill_mutant(name, tmp_path):
     (tree / "oracle" / "oracle.c").write_text(src)
     proc = subprocess.run(
         [sys.executable, "-m", "pytest", "tests/test_oracle.py", "-x", "-q",
+         "-p", "no:cacheprovider"],
+        cwd=tree, capture_output=True, text=True, timeout=600)
+    assert proc.returncode != 0, f"mutant {name} passed every pin:\n{proc.stdout[-2000:]}"
+    assert "failed" in proc.stdout, proc.stdout[-2000:] + proc.stderr[-2000:]
+
+
+@pytest.mark.parametrize("name", sorted(ROPE_MUTANTS))
+def test_rope_pins_kill_mutant(name, tmp_path):
+    old, new = ROPE_MUTANTS[name]
+    tree = tmp_path / "tree"
+    tree.mkdir()
+    shutil.copytree(os.path.join(ROOT, "oracle"), tree / "oracle",
+                    ignore=shutil.ignore_patterns("*.so", "__pycache__"))
+    shutil.copytree(os.path.join(ROOT, "tests"), tree / "tests",
+                    ignore=shutil.ignore_patterns("__pycache__", "test_oracle_mutants.py"))
+    shutil.copy(os.path.join(ROOT, "workloads.py"), tree / "workloads.py")
+    path = tree / "oracle" / "rope.py"
+    src = path.read_text()
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    path.write_text(src.replace(old, new))
+    proc = subprocess.run(
+        [sys.executable, "-m", "pytest", "tests/test_oracle_rope.py", "-x", "-q",
          "-p", "no:cacheprovider"],
         cwd=tree, capture_output=True, text=True, timeout=600)
     assert proc.returncode != 0, f"mutant {name} passed every pin:\n{proc.stdout[-2000:]}"
