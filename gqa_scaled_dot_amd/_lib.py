@@ -14,13 +14,38 @@ ATTN_ALIBI_MAX_HEADS = 256
 ATTN_BIAS_NONE, ATTN_BIAS_TS, ATTN_BIAS_HTS = 0, 1, 2
 ATTN_PATH_EMPTY, ATTN_PATH_ZERO, ATTN_PATH_GENERIC, ATTN_PATH_DECODE, ATTN_PATH_PREFILL = 0, 1, 2, 3, 4
 PATH_NAMES = {0: "empty", 1: "zero", 2: "generic", 3: "decode", 4: "prefill"}
+(ATTN_ROPE_DEFAULT, ATTN_ROPE_LINEAR, ATTN_ROPE_LLAMA3, ATTN_ROPE_YARN, ATTN_ROPE_LONGROPE,
+ ATTN_ROPE_DYNAMIC) = range(6)
+ATTN_ROPE_MAX_ROTARY_DIM = 256
+ROPE_SCALING = {"default": ATTN_ROPE_DEFAULT, "linear": ATTN_ROPE_LINEAR, "llama3": ATTN_ROPE_LLAMA3,
+                "yarn": ATTN_ROPE_YARN, "longrope": ATTN_ROPE_LONGROPE, "dynamic": ATTN_ROPE_DYNAMIC}
 
 # Every symbol include/attn.h declares.
 EXPORTS = (
     "attn_params_init", "attn_validate", "attn_workspace_size", "attn_forward",
     "attn_cache_write", "attn_last_error", "attn_plan", "attn_set_option",
     "attn_timing_enable", "attn_timing_collect",
+    "attn_rope_params_init", "attn_rope_table", "attn_rope", "attn_rope_cache_write",
 )
+
+
+class AttnRopeParams(ctypes.Structure):
+    _fields_ = [
+        ("head_dim", ctypes.c_int64), ("rotary_dim", ctypes.c_int64), ("offset", ctypes.c_int64),
+        ("interleaved", ctypes.c_int32), ("scaling", ctypes.c_int32),
+        ("base", ctypes.c_double),
+        ("inv_freq", ctypes.POINTER(ctypes.c_float)),
+        ("has_attention_factor", ctypes.c_int32), ("attention_factor", ctypes.c_float),
+        ("factor", ctypes.c_double),
+        ("low_freq_factor", ctypes.c_double), ("high_freq_factor", ctypes.c_double),
+        ("original_max_positions", ctypes.c_int64), ("max_positions", ctypes.c_int64),
+        ("beta_fast", ctypes.c_double), ("beta_slow", ctypes.c_double),
+        ("mscale", ctypes.c_double), ("mscale_all_dim", ctypes.c_double),
+        ("truncate", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("short_factor", ctypes.POINTER(ctypes.c_double)),
+        ("long_factor", ctypes.POINTER(ctypes.c_double)),
+        ("scaling_attention_factor", ctypes.c_double),
+    ]
 
 
 class AttnParams(ctypes.Structure):
@@ -34,6 +59,7 @@ class AttnParams(ctypes.Structure):
         ("alibi", ctypes.c_int32), ("alibi_max", ctypes.c_float),
         ("alibi_slopes", ctypes.POINTER(ctypes.c_float)),
         ("bias_kind", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("q_rope", ctypes.POINTER(AttnRopeParams)),
     ]
 
 
@@ -87,5 +113,16 @@ def lib():
     L.attn_timing_collect.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
                                       ctypes.POINTER(ctypes.c_int64)]
     L.attn_timing_collect.restype = ctypes.c_int
+    R = ctypes.POINTER(AttnRopeParams)
+    L.attn_rope_params_init.argtypes = [R]
+    L.attn_rope_params_init.restype = None
+    L.attn_rope_table.argtypes = [R, ctypes.c_int64, ctypes.POINTER(ctypes.c_float),
+                                  ctypes.POINTER(ctypes.c_float)]
+    L.attn_rope_table.restype = ctypes.c_int
+    L.attn_rope.argtypes = [R, ctypes.c_int64, ctypes.c_int64, vp, vp, vp]
+    L.attn_rope.restype = ctypes.c_int
+    L.attn_rope_cache_write.argtypes = [vp, ctypes.c_int64, ctypes.c_int64, vp, ctypes.c_int64,
+                                        ctypes.c_int64, R, vp]
+    L.attn_rope_cache_write.restype = ctypes.c_int
     _lib = L
     return L

@@ -4,7 +4,8 @@ Argument marshalling only: every step of the op runs in the library's HIP
 kernels. PyTorch supplies device memory (the output and workspace tensors)
 and the current stream. Parameters take the op catalogue's names for the
 `attention` op (heads, headDim, kvHeads, vHeadDim, causal, posOffset, scale,
-softcap, window, alibi, alibiMax, alibiSlopes).
+softcap, window, alibi, alibiMax, alibiSlopes) and the `rope` op (headDim,
+base, offset, rotaryDim, interleaved, scaling, invFreq, attentionFactor).
 """
 
 from __future__ import annotations
@@ -14,7 +15,7 @@ import math
 from typing import Optional, Sequence
 
 from . import _lib
-from ._lib import AttnParams, AttnPlanInfo
+from ._lib import AttnParams, AttnPlanInfo, AttnRopeParams
 
 
 class AttnError(RuntimeError):
@@ -35,14 +36,82 @@ def _check(rc: int) -> None:
         raise AttnError(rc, attn_last_error())
 
 
+def make_rope_params(headDim: Optional[int] = None, base: Optional[float] = None,
+                     offset: Optional[int] = None, rotaryDim: Optional[int] = None,
+                     interleaved: Optional[bool] = None, scaling: Optional[dict] = None,
+                     invFreq: Optional[Sequence[float]] = None,
+                     attentionFactor: Optional[float] = None):
+    """attn_rope_params for one call. `scaling` is a model config's rope_scaling
+    object as it stands (its rope_type or type, factor, low_freq_factor,
+    high_freq_factor, original_max_position_embeddings, max_position_embeddings,
+    beta_fast, beta_slow, mscale, mscale_all_dim, truncate, short_factor,
+    long_factor, attention_factor). Returns (params, keepalive)."""
+    L = _lib.lib()
+    r = AttnRopeParams()
+    L.attn_rope_params_init(ctypes.byref(r))
+    r.head_dim = int(headDim or 0)
+    r.rotary_dim = int(rotaryDim or 0)
+    r.offset = int(offset or 0)
+    r.interleaved = 1 if interleaved else 0
+    if base is not None:
+        r.base = float(base)
+    half = (r.rotary_dim or r.head_dim) // 2
+    keep = []
+
+    def doubles(name, values):
+        if len(values) != half:
+            raise AttnError(_lib.ATTN_ERR_INVALID, f"rope.scaling: {name} holds {len(values)} values, "
+                            f"rotaryDim/2 = {half} expected")
+        arr = (ctypes.c_double * half)(*[float(x) for x in values])
+        keep.append(arr)
+        return ctypes.cast(arr, ctypes.POINTER(ctypes.c_double))
+
+    if invFreq is not None:
+        if len(invFreq) != half:
+            raise AttnError(_lib.ATTN_ERR_INVALID, f"rope.invFreq: {len(invFreq)} values, "
+                            f"rotaryDim/2 = {half} expected")
+        import numpy as np
+        arr = (ctypes.c_float * half)(*np.asarray(invFreq, dtype=np.float64).astype(np.float32).tolist())
+        keep.append(arr)
+        r.inv_freq = ctypes.cast(arr, ctypes.POINTER(ctypes.c_float))
+    if attentionFactor is not None:
+        r.has_attention_factor, r.attention_factor = 1, float(attentionFactor)
+    if scaling:
+        kind = scaling.get("rope_type", scaling.get("type"))
+        if kind not in _lib.ROPE_SCALING:
+            raise AttnError(_lib.ATTN_ERR_UNSUPPORTED, f"rope.scaling: unknown type {kind!r}")
+        r.scaling = _lib.ROPE_SCALING[kind]
+        num = {"factor": "factor", "low_freq_factor": "low_freq_factor",
+               "high_freq_factor": "high_freq_factor", "beta_fast": "beta_fast",
+               "beta_slow": "beta_slow", "mscale": "mscale", "mscale_all_dim": "mscale_all_dim",
+               "attention_factor": "scaling_attention_factor"}
+        for key, field in num.items():
+            if scaling.get(key) is not None:
+                setattr(r, field, float(scaling[key]))
+        if scaling.get("original_max_position_embeddings") is not None:
+            r.original_max_positions = int(scaling["original_max_position_embeddings"])
+        if scaling.get("max_position_embeddings") is not None:
+            r.max_positions = int(scaling["max_position_embeddings"])
+        if scaling.get("truncate") is not None:
+            r.truncate = 1 if scaling["truncate"] else 0
+        if scaling.get("short_factor") is not None:
+            r.short_factor = doubles("short_factor", scaling["short_factor"])
+        if scaling.get("long_factor") is not None:
+            r.long_factor = doubles("long_factor", scaling["long_factor"])
+    return r, keep
+
+
 def make_params(T: int, S: int, *, heads: int, headDim: int, kvHeads: Optional[int] = None,
                 vHeadDim: Optional[int] = None, causal: Optional[bool] = None,
                 posOffset: Optional[int] = None, scale: Optional[float] = None,
                 softcap: Optional[float] = None, window: Optional[int] = None,
                 alibi: Optional[bool] = None, alibiMax: Optional[float] = None,
-                alibiSlopes: Optional[Sequence[float]] = None, bias_kind: int = 0):
+                alibiSlopes: Optional[Sequence[float]] = None, bias_kind: int = 0,
+                q_rope: Optional[dict] = None):
     """attn_params for one call. Returns (params, keepalive) - keep the second
-    alive until the call returns (it owns the explicit slope array)."""
+    alive until the call returns (it owns the explicit slope array and the
+    q_rope parameters). q_rope holds `rope` op params for q; its headDim
+    defaults to headDim and its offset to posOffset."""
     L = _lib.lib()
     p = AttnParams()
     L.attn_params_init(ctypes.byref(p))
@@ -74,6 +143,14 @@ def make_params(T: int, S: int, *, heads: int, headDim: int, kvHeads: Optional[i
     elif alibi:
         p.alibi = _lib.ATTN_ALIBI_BLOOM
     p.bias_kind = int(bias_kind)
+    if q_rope is not None:
+        rp = dict(q_rope)
+        rp.setdefault("headDim", headDim)
+        if rp.get("offset") is None:
+            rp["offset"] = posOffset or 0
+        r, rkeep = make_rope_params(**rp)
+        keep = (keep, r, rkeep)
+        p.q_rope = ctypes.pointer(r)
     return p, keep
 
 
@@ -279,3 +356,79 @@ def attn_cache_write(cache, values, offset: int, *, stream=None):
                                      _stream_ptr(stream, cache.device))
     _check(rc)
     return cache
+
+
+# -- op `rope` -------------------------------------------------------------------
+
+def attn_rope_table(rows: int = 1, **rope):
+    """(inverse frequencies as a float32 numpy array, attention factor) that the
+    library uses for `rows` rows starting at rope's offset."""
+    import numpy as np
+    r, keep = make_rope_params(**rope)
+    half = (r.rotary_dim or r.head_dim) // 2
+    buf = (ctypes.c_float * max(half, 1))()
+    af = ctypes.c_float()
+    _check(_lib.lib().attn_rope_table(ctypes.byref(r), int(rows), buf, ctypes.byref(af)))
+    del keep
+    return np.ctypeslib.as_array(buf)[:half].copy(), float(af.value)
+
+
+def attn_rope(x, *, out=None, stream=None, **rope):
+    """Op `rope` on x [T, heads*headDim]; out may be x itself (in place)."""
+    torch = _torch()
+    _dev_tensor(x, "x")
+    if x.dim() != 2:
+        raise ValueError("x: must be [T, heads*headDim]")
+    if out is None:
+        out = torch.empty_like(x)
+    _dev_tensor(out, "out")
+    if tuple(out.shape) != tuple(x.shape):
+        raise ValueError("out: must have the shape of x")
+    r, keep = make_rope_params(**rope)
+    rc = _lib.lib().attn_rope(ctypes.byref(r), x.shape[0], x.shape[1], x.data_ptr(), out.data_ptr(),
+                              _stream_ptr(stream, x.device))
+    del keep
+    _check(rc)
+    return out
+
+
+def _rope_cache_args(cache, values, offset, stream, rope):
+    _dev_tensor(cache, "cache")
+    _dev_tensor(values, "values")
+    if cache.dim() != 2 or values.dim() != 2 or cache.shape[1] != values.shape[1]:
+        raise ValueError("cache [maxRows, width] and values [rows, width] must share width")
+    rope = dict(rope)
+    if rope.get("offset") is None:
+        rope["offset"] = int(offset)
+    r, keep = make_rope_params(**rope)
+    args = (ctypes.c_void_p(cache.data_ptr()), ctypes.c_int64(cache.shape[0]),
+            ctypes.c_int64(cache.shape[1]), ctypes.c_void_p(values.data_ptr()),
+            ctypes.c_int64(values.shape[0]), ctypes.c_int64(int(offset)), ctypes.byref(r),
+            _stream_ptr(stream, cache.device))
+    return args, (r, keep, cache, values)
+
+
+def attn_rope_cache_write(cache, values, offset: int, rope: dict, *, stream=None):
+    """Ops `rope` then `cache_write`: rows [offset, offset+rows) of `cache` become
+    rope(values), in place. `rope` holds the rope op's params; the rows'
+    positions start at its offset, which defaults to the cache offset.
+    Returns the cache."""
+    args, held = _rope_cache_args(cache, values, offset, stream, rope)
+    rc = _lib.lib().attn_rope_cache_write(*args)
+    del held
+    _check(rc)
+    return cache
+
+
+def prepare_rope_cache_write(cache, values, offset: int, rope: dict, *, stream=None):
+    """Like prepare_forward, for attn_rope_cache_write."""
+    args, held = _rope_cache_args(cache, values, offset, stream, rope)
+    fn = _lib.lib().attn_rope_cache_write
+
+    def call():
+        rc = fn(*args)
+        if rc != _lib.ATTN_OK:
+            raise AttnError(rc, attn_last_error())
+
+    call.held = held
+    return call

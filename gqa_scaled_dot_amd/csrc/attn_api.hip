@@ -80,12 +80,174 @@ void slopes_mpt(int64_t H, double b, float* out) {
     for (int64_t i = 1; i <= n && k < H; i += 2) out[k++] = (float)exp2(-(double)i * b / (double)n);
 }
 
+// ---------------------------------------------------------------------------
+// Rotary embedding tables (op `rope`, params base, rotaryDim, scaling,
+// invFreq, attentionFactor). Every value is computed in double and rounded to
+// f32 once, with no fused multiply-adds (contraction is switched off in each
+// function), so the table is a fixed function of the parameters.
+// ---------------------------------------------------------------------------
+// RoFormer's frequencies base^(-2i/rd).
+double rope_theta(double base, int64_t i, int64_t rd) {
+#pragma clang fp contract(off)
+    return pow(base, -2.0 * (double)i / (double)rd);
+}
+
+// Llama 3.1: keep short wavelengths, divide long ones by factor, blend linearly
+// in original/wavelength between original/high_freq_factor and
+// original/low_freq_factor.
+double rope_llama3(double f, const attn_rope_params* r, double lo_f, double hi_f) {
+#pragma clang fp contract(off)
+    const double orig = (double)r->original_max_positions;
+    const double wl = 2.0 * M_PI / f;
+    if (wl < orig / hi_f) return f;
+    if (wl > orig / lo_f) return f / r->factor;
+    const double smooth = (orig / wl - lo_f) / (hi_f - lo_f);
+    return (1.0 - smooth) * f / r->factor + smooth * f;
+}
+
+double yarn_mscale(double scale, double k) {
+#pragma clang fp contract(off)
+    return scale > 1.0 ? 0.1 * k * log(scale) + 1.0 : 1.0;
+}
+
+// Checks *r and fills the device-side description for rows at positions
+// offset .. seq_len - 1.
+int rope_resolve(const attn_rope_params* r, int64_t seq_len, attn::RopeArgs* out) {
+#pragma clang fp contract(off)
+    if (!r) return fail(ATTN_ERR_INVALID, "rope: NULL params");
+    if (r->head_dim <= 0 || r->head_dim > kMaxDim)
+        return fail(ATTN_ERR_INVALID, "rope.headDim: must be in 1..%lld (got %lld)", (long long)kMaxDim,
+                    (long long)r->head_dim);
+    const int64_t rd = r->rotary_dim ? r->rotary_dim : r->head_dim;
+    if (rd < 0 || rd % 2 || rd > r->head_dim)
+        return fail(ATTN_ERR_INVALID, "rope.rotaryDim: must be even and in 2..headDim (got %lld)",
+                    (long long)rd);
+    if (rd > ATTN_ROPE_MAX_ROTARY_DIM)
+        return fail(ATTN_ERR_UNSUPPORTED, "rope.rotaryDim: at most %d rotated channels (got %lld)",
+                    ATTN_ROPE_MAX_ROTARY_DIM, (long long)rd);
+    if (r->interleaved != 0 && r->interleaved != 1)
+        return fail(ATTN_ERR_INVALID, "rope.interleaved: must be 0 or 1");
+    if (r->offset < 0) return fail(ATTN_ERR_INVALID, "rope.offset: must be >= 0 (got %lld)", (long long)r->offset);
+    if (seq_len > INT32_MAX) return fail(ATTN_ERR_UNSUPPORTED, "rope.offset: positions past 2^31-1");
+    const double base = r->base == 0.0 ? 10000.0 : r->base;
+    if (!(isfinite(base) && base > 0.0)) return fail(ATTN_ERR_INVALID, "rope.base: must be finite and > 0");
+    if (r->has_attention_factor && !isfinite(r->attention_factor))
+        return fail(ATTN_ERR_INVALID, "rope.attentionFactor: must be finite");
+    if (!isfinite(r->scaling_attention_factor))
+        return fail(ATTN_ERR_INVALID, "rope.scaling: attention_factor must be finite");
+    if (r->scaling < ATTN_ROPE_DEFAULT || r->scaling > ATTN_ROPE_DYNAMIC)
+        return fail(ATTN_ERR_UNSUPPORTED, "rope.scaling: unknown type %d", r->scaling);
+
+    attn::RopeArgs& a = *out;
+    memset(&a, 0, sizeof a);
+    a.on = 1;
+    a.rd = (int32_t)rd;
+    a.interleaved = r->interleaved;
+    a.pos0 = r->offset;
+    const int64_t half = rd / 2;
+    double af = 1.0;
+    const bool needs_factor = r->scaling == ATTN_ROPE_LINEAR || r->scaling == ATTN_ROPE_LLAMA3 ||
+                              r->scaling == ATTN_ROPE_YARN || r->scaling == ATTN_ROPE_DYNAMIC;
+    if (r->inv_freq) {
+        for (int64_t i = 0; i < half; ++i) {
+            if (!isfinite(r->inv_freq[i]))
+                return fail(ATTN_ERR_INVALID, "rope.invFreq: entry %lld is not finite", (long long)i);
+            a.inv_freq[i] = r->inv_freq[i];
+        }
+    } else {
+        if (needs_factor && !(isfinite(r->factor) && r->factor > 0.0))
+            return fail(ATTN_ERR_INVALID, "rope.scaling: factor must be finite and > 0");
+        if ((r->scaling == ATTN_ROPE_LLAMA3 || r->scaling == ATTN_ROPE_YARN ||
+             r->scaling == ATTN_ROPE_LONGROPE) && r->original_max_positions <= 0)
+            return fail(ATTN_ERR_INVALID, "rope.scaling: original_max_position_embeddings must be > 0");
+        double eff_base = base;
+        if (r->scaling == ATTN_ROPE_DYNAMIC) {
+            const int64_t orig = r->original_max_positions ? r->original_max_positions : r->max_positions;
+            if (orig <= 0)
+                return fail(ATTN_ERR_INVALID, "rope.scaling: dynamic needs original_max_position_embeddings");
+            if (rd <= 2) return fail(ATTN_ERR_INVALID, "rope.rotaryDim: dynamic scaling needs more than 2");
+            if (seq_len > orig)
+                eff_base = base * pow(r->factor * (double)seq_len / (double)orig - (r->factor - 1.0),
+                                      (double)rd / ((double)rd - 2.0));
+        }
+        double lo_f = 1.0, hi_f = 4.0;
+        if (r->scaling == ATTN_ROPE_LLAMA3) {
+            lo_f = r->low_freq_factor ? r->low_freq_factor : 1.0;
+            hi_f = r->high_freq_factor ? r->high_freq_factor : 4.0;
+            if (!(lo_f > 0.0 && hi_f > lo_f))
+                return fail(ATTN_ERR_INVALID, "rope.scaling: llama3 needs 0 < low_freq_factor < high_freq_factor");
+        }
+        const double* ext = nullptr;
+        if (r->scaling == ATTN_ROPE_LONGROPE) {
+            ext = seq_len > r->original_max_positions ? r->long_factor : r->short_factor;
+            if (!ext) return fail(ATTN_ERR_INVALID, "rope.scaling: longrope needs short_factor and long_factor");
+            for (int64_t i = 0; i < half; ++i)
+                if (!(isfinite(ext[i]) && ext[i] > 0.0))
+                    return fail(ATTN_ERR_INVALID, "rope.scaling: longrope factor %lld must be > 0", (long long)i);
+        }
+        // YaRN's ramp ends: the pair index at which the number of turns over
+        // the original context equals beta_fast (resp. beta_slow).
+        double ylo = 0.0, yhi = 0.0;
+        if (r->scaling == ATTN_ROPE_YARN) {
+            const double bf = r->beta_fast ? r->beta_fast : 32.0, bs = r->beta_slow ? r->beta_slow : 1.0;
+            if (!(bf > 0.0 && bs > 0.0)) return fail(ATTN_ERR_INVALID, "rope.scaling: yarn betas must be > 0");
+            const double orig = (double)r->original_max_positions;
+            ylo = (double)rd * log(orig / (bf * 2.0 * M_PI)) / (2.0 * log(base));
+            yhi = (double)rd * log(orig / (bs * 2.0 * M_PI)) / (2.0 * log(base));
+            if (r->truncate) {
+                ylo = floor(ylo);
+                yhi = ceil(yhi);
+            }
+            if (ylo < 0.0) ylo = 0.0;
+            if (yhi > (double)(rd - 1)) yhi = (double)(rd - 1);
+            if (ylo == yhi) yhi += 0.001;
+        }
+        for (int64_t i = 0; i < half; ++i) {
+            const double th = rope_theta(eff_base, i, rd);
+            double f = th;
+            switch (r->scaling) {
+                case ATTN_ROPE_LINEAR: f = th / r->factor; break;
+                case ATTN_ROPE_LLAMA3: f = rope_llama3(th, r, lo_f, hi_f); break;
+                case ATTN_ROPE_YARN: {
+                    double ramp = ((double)i - ylo) / (yhi - ylo);
+                    ramp = ramp < 0.0 ? 0.0 : (ramp > 1.0 ? 1.0 : ramp);
+                    f = th * (1.0 - ramp) + (th / r->factor) * ramp;
+                    break;
+                }
+                case ATTN_ROPE_LONGROPE: f = th / ext[i]; break;
+                default: break;
+            }
+            a.inv_freq[i] = (float)f;
+        }
+        if (r->scaling == ATTN_ROPE_YARN) {
+            af = (r->mscale != 0.0 && r->mscale_all_dim != 0.0)
+                     ? yarn_mscale(r->factor, r->mscale) / yarn_mscale(r->factor, r->mscale_all_dim)
+                     : yarn_mscale(r->factor, 1.0);
+        }
+        if (r->scaling == ATTN_ROPE_LONGROPE) {
+            double f = r->factor;
+            if (f == 0.0) {
+                if (r->max_positions <= 0 && !r->has_attention_factor && r->scaling_attention_factor == 0.0)
+                    return fail(ATTN_ERR_INVALID, "rope.scaling: longrope needs factor or max_position_embeddings");
+                f = (double)r->max_positions / (double)r->original_max_positions;
+            }
+            af = f > 1.0 ? sqrt(1.0 + log(f) / log((double)r->original_max_positions)) : 1.0;
+        }
+    }
+    if (r->scaling_attention_factor != 0.0) af = r->scaling_attention_factor;
+    if (r->has_attention_factor) af = (double)r->attention_factor;
+    a.af = (float)af;
+    return ok();
+}
+
+
 // Resolved view of attn_params.
 struct Resolved {
     int64_t T, S, H, G, D, Dv, P0, window;
     bool causal;
     int bias_kind;
     attn::Epilogue ep;
+    attn::RopeArgs rope;  // q_rope, resolved (rope.on = 0 without one)
 };
 
 int resolve(const attn_params* p, Resolved* r) {
@@ -173,6 +335,18 @@ int resolve(const attn_params* p, Resolved* r) {
                 return fail(ATTN_ERR_INVALID, "alibiSlopes: entry %lld is not finite", (long long)h);
             e.slopes[h] = p->alibi_slopes[h];
         }
+    }
+    memset(&o.rope, 0, sizeof o.rope);
+    if (p->q_rope) {
+        attn_rope_params qr = *p->q_rope;
+        if (qr.head_dim != 0 && qr.head_dim != o.D)
+            return fail(ATTN_ERR_INVALID, "q_rope.headDim: must be 0 or headDim (%lld), got %lld",
+                        (long long)o.D, (long long)qr.head_dim);
+        qr.head_dim = o.D;
+        if (qr.offset < 0 || qr.offset > INT32_MAX)
+            return fail(ATTN_ERR_INVALID, "rope.offset: must be in 0..2^31-1 (got %lld)", (long long)qr.offset);
+        const int rc = rope_resolve(&qr, qr.offset + o.T, &o.rope);
+        if (rc) return rc;
     }
     return ok();
 }
@@ -358,6 +532,23 @@ bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Shared checks of attn_rope and attn_rope_cache_write: the row layout and
+// the resolved table.
+int rope_rows(const attn_rope_params* r, int64_t rows, int64_t width, attn::RopeArgs* a, int64_t* heads) {
+    if (!r) return fail(ATTN_ERR_INVALID, "rope: NULL params");
+    if (rows < 0) return fail(ATTN_ERR_INVALID, "rows: must be >= 0");
+    if (width <= 0) return fail(ATTN_ERR_INVALID, "width: must be > 0");
+    if (r->head_dim <= 0 || width % r->head_dim)
+        return fail(ATTN_ERR_INVALID, "rope.headDim: the row width %lld is not a multiple of headDim %lld",
+                    (long long)width, (long long)r->head_dim);
+    if (width / r->head_dim > INT32_MAX) return fail(ATTN_ERR_UNSUPPORTED, "width: too many heads");
+    if ((double)rows * (double)width > 1e17) return fail(ATTN_ERR_INVALID, "sizes: tensors too large");
+    if (r->offset < 0 || r->offset > INT32_MAX)
+        return fail(ATTN_ERR_INVALID, "rope.offset: must be in 0..2^31-1 (got %lld)", (long long)r->offset);
+    *heads = width / r->head_dim;
+    return rope_resolve(r, r->offset + rows, a);
+}
+
 }  // namespace
 
 extern "C" {
@@ -454,6 +645,7 @@ int attn_forward(const attn_params* p, const float* q, const float* k, const flo
     prob.D = (int32_t)r.D;
     prob.Dv = (int32_t)r.Dv;
     prob.ep = r.ep;
+    prob.rope = r.rope;
     hipStream_t s = (hipStream_t)stream;
 
     hipError_t err = hipSuccess;
@@ -513,6 +705,66 @@ int attn_cache_write(float* cache, int64_t max_rows, int64_t width, const float*
     hipStream_t s = (hipStream_t)stream;
     const hipError_t err = timed("cache_write", s, [&](const attn::Launch& L) {
         return attn::launch_cache_write(dst, values, rows * width, L);
+    });
+    if (err != hipSuccess) return fail(ATTN_ERR_DEVICE, "launch: %s", hipGetErrorString(err));
+    return ok();
+}
+
+void attn_rope_params_init(attn_rope_params* r) {
+    if (!r) return;
+    memset(r, 0, sizeof *r);
+    r->truncate = 1;
+}
+
+int attn_rope_table(const attn_rope_params* r, int64_t rows, float* inv_freq, float* attention_factor) {
+    if (!inv_freq || !attention_factor) return fail(ATTN_ERR_INVALID, "rope: NULL output pointer");
+    if (rows < 0) return fail(ATTN_ERR_INVALID, "rows: must be >= 0");
+    if (r && (r->offset < 0 || r->offset > INT32_MAX))
+        return fail(ATTN_ERR_INVALID, "rope.offset: must be in 0..2^31-1");
+    attn::RopeArgs a;
+    const int rc = rope_resolve(r, r ? r->offset + rows : 0, &a);
+    if (rc) return rc;
+    memcpy(inv_freq, a.inv_freq, sizeof(float) * (size_t)(a.rd / 2));
+    *attention_factor = a.af;
+    return ok();
+}
+
+int attn_rope(const attn_rope_params* r, int64_t T, int64_t width, const float* x, float* out, void* stream) {
+    attn::RopeArgs a;
+    int64_t heads = 0;
+    int rc = rope_rows(r, T, width, &a, &heads);
+    if (rc) return rc;
+    if (T == 0) return ok();
+    if (!x || !out) return fail(ATTN_ERR_INVALID, "%s: NULL pointer", x ? "out" : "x");
+    const size_t n = sizeof(float) * (size_t)(T * width);
+    if (x != out && overlaps(x, n, out, n)) return fail(ATTN_ERR_INVALID, "out: overlaps x (only out == x is allowed)");
+    const hipError_t err = timed("rope", (hipStream_t)stream, [&](const attn::Launch& L) {
+        return attn::launch_rope(a, x, out, T, (int)heads, (int)r->head_dim, L);
+    });
+    if (err != hipSuccess) return fail(ATTN_ERR_DEVICE, "launch: %s", hipGetErrorString(err));
+    return ok();
+}
+
+int attn_rope_cache_write(float* cache, int64_t max_rows, int64_t width, const float* values, int64_t rows,
+                          int64_t offset, const attn_rope_params* r, void* stream) {
+    if (max_rows < 0) return fail(ATTN_ERR_INVALID, "maxRows: must be >= 0");
+    if (offset < 0) return fail(ATTN_ERR_INVALID, "offset: must be >= 0 (got %lld)", (long long)offset);
+    attn::RopeArgs a;
+    int64_t heads = 0;
+    int rc = rope_rows(r, rows, width, &a, &heads);
+    if (rc) return rc;
+    if (offset > max_rows || rows > max_rows - offset)
+        return fail(ATTN_ERR_INVALID, "offset: rows %lld..%lld run past the cache's %lld rows",
+                    (long long)offset, (long long)(offset + rows), (long long)max_rows);
+    if ((double)max_rows * (double)width > 1e17) return fail(ATTN_ERR_INVALID, "cache: too large");
+    if (rows == 0) return ok();
+    if (!cache) return fail(ATTN_ERR_INVALID, "cache: NULL pointer");
+    if (!values) return fail(ATTN_ERR_INVALID, "values: NULL pointer");
+    float* dst = cache + offset * width;
+    const size_t n = sizeof(float) * (size_t)(rows * width);
+    if (overlaps(dst, n, values, n)) return fail(ATTN_ERR_INVALID, "values: overlap the rows being written");
+    const hipError_t err = timed("rope", (hipStream_t)stream, [&](const attn::Launch& L) {
+        return attn::launch_rope(a, values, dst, rows, (int)heads, (int)r->head_dim, L);
     });
     if (err != hipSuccess) return fail(ATTN_ERR_DEVICE, "launch: %s", hipGetErrorString(err));
     return ok();

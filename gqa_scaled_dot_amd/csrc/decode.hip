@@ -26,6 +26,7 @@
 // combine_few: the same merge for up to 16 splits (prefill key-range parts),
 // one thread per 4 output floats.
 #include "device_common.h"
+#include "rope_device.h"
 
 namespace attn {
 
@@ -97,9 +98,33 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
         tt[r] = live[r] ? r / hpg : 0;
         hh[r] = g * hpg + (live[r] ? r % hpg : 0);
         pos[r] = p.ep.pos_offset + tt[r];
-        const float* qrow = p.q + (int64_t)tt[r] * p.H * D + (int64_t)hh[r] * D + 4 * ln;
+    }
+    if (p.rope.on) {
+        // q rows turned by the rotary embedding once per workgroup, through
+        // LDS (every row group needs the same values).
+        __shared__ __align__(16) float s_q[NQ * D];
+        for (int e = tid; e < NQ * D; e += kThreads) {
+            const int r = e / D, d = e % D;
+            float x = 0.0f;
+            if (r < nrows) {
+                const int t = r / hpg, h = g * hpg + r % hpg;
+                x = rope_channel(p.rope, p.q + (int64_t)t * p.H * D + (int64_t)h * D, d, p.rope.pos0 + t);
+            }
+            s_q[e] = x;
+        }
+        __syncthreads();
 #pragma unroll
-        for (int j = 0; j < KJ; ++j) qr[r][j] = live[r] ? ld4(qrow + 64 * j) : zero4();
+        for (int r = 0; r < NQ; ++r)
+#pragma unroll
+            for (int j = 0; j < KJ; ++j)
+                qr[r][j] = *reinterpret_cast<const float4*>(s_q + r * D + 64 * j + 4 * ln);
+    } else {
+#pragma unroll
+        for (int r = 0; r < NQ; ++r) {
+            const float* qrow = p.q + (int64_t)tt[r] * p.H * D + (int64_t)hh[r] * D + 4 * ln;
+#pragma unroll
+            for (int j = 0; j < KJ; ++j) qr[r][j] = live[r] ? ld4(qrow + 64 * j) : zero4();
+        }
     }
 
     float m[NQ], l[NQ];

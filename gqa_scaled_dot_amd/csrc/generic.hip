@@ -6,6 +6,7 @@
 // Slow but shape-agnostic; the tuned decode and prefill kernels cover the
 // common widths.
 #include "device_common.h"
+#include "rope_device.h"
 
 namespace attn {
 
@@ -51,7 +52,9 @@ __global__ __launch_bounds__(kThreads) void generic_kernel(Problem p) {
     const int pos = p.ep.pos_offset + (int)t;
     const int tid = threadIdx.x;
 
-    for (int d = tid; d < p.D; d += kThreads) qrow[d] = p.q[t * (int64_t)p.H * p.D + (int64_t)h * p.D + d];
+    const float* qhead = p.q + t * (int64_t)p.H * p.D + (int64_t)h * p.D;
+    for (int d = tid; d < p.D; d += kThreads)
+        qrow[d] = p.rope.on ? rope_channel(p.rope, qhead, d, p.rope.pos0 + t) : qhead[d];
     for (int e = tid; e < p.Dv; e += kThreads) acc[e] = 0.0f;
     __syncthreads();
 

@@ -24,6 +24,18 @@ struct Epilogue {
     float slopes[ATTN_ALIBI_MAX_HEADS];
 };
 
+// A resolved rotary embedding (op `rope`): the f32 inverse-frequency table
+// and attention factor computed on the host, the pairing and the position of
+// row 0.
+struct RopeArgs {
+    int32_t on;           // 0: no rotation (attention kernels' q path only)
+    int32_t rd;           // rotated channels per head (even, <= ATTN_ROPE_MAX_ROTARY_DIM)
+    int32_t interleaved;  // 1: pairs (2i, 2i+1); 0: pairs (i, i + rd/2)
+    float af;             // attention factor: multiplies cos and sin
+    int64_t pos0;         // position of row 0
+    float inv_freq[ATTN_ROPE_MAX_ROTARY_DIM / 2];
+};
+
 struct Problem {
     const float* q;
     const float* k;
@@ -33,6 +45,7 @@ struct Problem {
     int64_t T, S;
     int32_t H, G, D, Dv;
     Epilogue ep;
+    RopeArgs rope;  // applied to q as it is loaded when rope.on
 };
 
 // Key rows [lo, hi) that any query row of the call can see. Rows outside
@@ -75,6 +88,9 @@ inline hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block,
 
 // Launchers. Each returns hipSuccess or the launch error.
 hipError_t launch_cache_write(float* dst, const float* src, int64_t count, const Launch& L);
+// out rows = rope(x rows): rows x heads heads of D floats each; out may equal x.
+hipError_t launch_rope(const RopeArgs& ra, const float* x, float* out, int64_t rows, int heads, int D,
+                       const Launch& L);
 hipError_t launch_zero_fill(float* dst, int64_t count, const Launch& L);
 hipError_t launch_generic(const Problem& p, const Launch& L);
 bool decode_supported(int D, int Dv, int nq);

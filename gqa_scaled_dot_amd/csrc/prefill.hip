@@ -40,6 +40,7 @@
 // A 16x16x4 variant with 16 query rows per wave (prefill16.hip) serves wide
 // heads; the host picks one per shape.
 #include "prefill_common.h"
+#include "rope_device.h"
 
 namespace attn {
 
@@ -121,10 +122,14 @@ __global__ __launch_bounds__(kThreads, prefill_min_waves(D, DV)) void prefill_ke
     // This lane's half of its query row: q[t, h*D + half*D/2 + kk], kk < D/2.
     float qreg[D / 2];
     {
-        const float* qrow = p.q + (int64_t)min(t, T - 1) * p.H * D + (int64_t)h * D + half * (D / 2);
+        const int tc = min(t, T - 1);
+        const float* qhead = p.q + (int64_t)tc * p.H * D + (int64_t)h * D;
 #pragma unroll
         for (int kk = 0; kk < D / 2; kk += 4) {
-            const float4 v = *reinterpret_cast<const float4*>(qrow + kk);
+            // With a rotary embedding on q (rope.on is uniform), each channel is
+            // turned as it is loaded.
+            const float4 v = p.rope.on ? rope_channels4(p.rope, qhead, half * (D / 2) + kk, p.rope.pos0 + tc)
+                                       : *reinterpret_cast<const float4*>(qhead + half * (D / 2) + kk);
             qreg[kk] = trow ? v.x : 0.0f;
             qreg[kk + 1] = trow ? v.y : 0.0f;
             qreg[kk + 2] = trow ? v.z : 0.0f;

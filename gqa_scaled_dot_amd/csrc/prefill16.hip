@@ -21,6 +21,7 @@
 // bytes per LDS instruction (no bank conflicts), and each accumulator
 // register maps to float4 output stores.
 #include "prefill_common.h"
+#include "rope_device.h"
 
 namespace attn {
 
@@ -77,10 +78,12 @@ __global__ __launch_bounds__(kThreads16, 1) void prefill16_kernel(Problem p, Arg
     // This lane's quarter of its query row: q[t, h*D + quad*D/4 + kk], kk < D/4.
     float qreg[D / 4];
     {
-        const float* qrow = p.q + (int64_t)min(t, T - 1) * p.H * D + (int64_t)h * D + quad * (D / 4);
+        const int tc = min(t, T - 1);
+        const float* qhead = p.q + (int64_t)tc * p.H * D + (int64_t)h * D;
 #pragma unroll
         for (int kk = 0; kk < D / 4; kk += 4) {
-            const float4 v = *reinterpret_cast<const float4*>(qrow + kk);
+            const float4 v = p.rope.on ? rope_channels4(p.rope, qhead, quad * (D / 4) + kk, p.rope.pos0 + tc)
+                                       : *reinterpret_cast<const float4*>(qhead + quad * (D / 4) + kk);
             qreg[kk] = trow ? v.x : 0.0f;
             qreg[kk + 1] = trow ? v.y : 0.0f;
             qreg[kk + 2] = trow ? v.z : 0.0f;

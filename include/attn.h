@@ -1,7 +1,7 @@
 /*
  * attn.h - f32 grouped-query scaled dot-product attention on MI355X (gfx950).
  *
- * The C ABI of libattn.so. It implements two ops of the graph protocol's op
+ * The C ABI of libattn.so. It implements three ops of the graph protocol's op
  * catalogue (page "https://vtmu.mpakt.dev/api/ops"):
  *
  *   attention    "Scaled dot-product attention with grouped-query support";
@@ -11,6 +11,9 @@
  *   cache_write  writes rows into a preallocated cache in place (op
  *                `cache_write`: inputs cache [maxRows, width] and values
  *                [rows, width], param offset, mutatesInput 0).
+ *   rope         rotary position embedding (op `rope`), standalone, fused
+ *                into cache_write (rotate k, then write it) and fused into
+ *                attention's q loads (attn_params.q_rope).
  *
  * Conventions for every entry point:
  *   - Tensors are dense row-major f32 (catalogue convention: tensors are
@@ -88,6 +91,12 @@ extern "C" {
  *                not kept. At most ATTN_ALIBI_MAX_HEADS heads.
  *   bias_kind    ATTN_BIAS_*; the bias is added after softcap and ALiBi (a
  *                -1e9 entry masks its key, as the catalogue suggests).
+ *   q_rope       NULL, or a rotary embedding applied to q as the kernels load
+ *                it: the call computes attention(rope(q), k, v, bias) with
+ *                rope as attn_rope() defines it (its own offset gives row 0's
+ *                position; its head_dim must be 0 or head_dim). HOST pointer,
+ *                read during the call and not kept. It fuses the rope that
+ *                precedes attention in a decode graph into the attention call.
  *
  * A query row with no visible key outputs zeros.
  */
@@ -106,6 +115,7 @@ typedef struct attn_params {
     const float* alibi_slopes;
     int32_t bias_kind;
     int32_t reserved;
+    const struct attn_rope_params* q_rope;
 } attn_params;
 
 /* Fill *p with the catalogue's defaults: causal = 1, everything optional
@@ -150,6 +160,121 @@ int attn_forward(const attn_params* p, const float* q, const float* k, const flo
  */
 int attn_cache_write(float* cache, int64_t max_rows, int64_t width, const float* values,
                      int64_t rows, int64_t offset, void* stream);
+
+/*
+ * Op `rope` (graph protocol op catalogue: "Rotary position embedding over
+ * [tokens, heads*headDim]"; params headDim, base, offset, rotaryDim,
+ * interleaved, scaling, invFreq, attentionFactor; features rope.interleaved,
+ * rope.rotaryDim, rope.scaling).
+ *
+ * Row t of x sits at position offset + t. In each head the first rotary_dim
+ * channels form rotary_dim/2 pairs, (i, i + rotary_dim/2) by default or
+ * (2i, 2i+1) when interleaved, and pair i turns by the angle
+ * position * inv_freq[i]: (a, b) -> (a cos - b sin, a sin + b cos), with cos
+ * and sin both multiplied by the attention factor. Channels from rotary_dim
+ * on pass through unchanged.
+ *
+ * The inverse-frequency table is f32. It is an explicit inv_freq if given,
+ * else base^(-2i/rotary_dim), changed by `scaling` as a model config's
+ * rope_scaling asks:
+ *   LINEAR    every frequency divided by factor (position interpolation)
+ *   LLAMA3    Llama 3.1's rule: wavelengths below original/high_freq_factor
+ *             kept, above original/low_freq_factor divided by factor, blended
+ *             linearly in original/wavelength in between
+ *   YARN      YaRN's NTK-by-parts: pairs turning more than beta_fast times over
+ *             the original context kept, fewer than beta_slow times divided by
+ *             factor, a linear ramp over the pair index in between (its ends
+ *             rounded outwards unless truncate = 0); attention factor
+ *             0.1 ln(factor) + 1, or the ratio of that with mscale and with
+ *             mscale_all_dim when both are given
+ *   LONGROPE  frequencies divided by long_factor[i] once offset + T exceeds
+ *             original_max_positions, else by short_factor[i]; attention
+ *             factor sqrt(1 + ln(f) / ln(original)) with f = factor, or
+ *             max_positions / original when factor is 0
+ *   DYNAMIC   once offset + T exceeds original_max_positions (or
+ *             max_positions), base grows to base * (factor * (offset + T) /
+ *             original - (factor - 1))^(rotary_dim / (rotary_dim - 2))
+ * Each table entry and the attention factor are computed in double precision
+ * and rounded to f32 once. The attention factor is attention_factor when
+ * has_attention_factor, else scaling_attention_factor when non-zero (the
+ * scaling object's own attention_factor), else the scaling's derived one,
+ * else 1. The angle itself is evaluated to better than 1e-7 rad for every
+ * position below 2^31.
+ */
+#define ATTN_ROPE_DEFAULT 0
+#define ATTN_ROPE_LINEAR 1
+#define ATTN_ROPE_LLAMA3 2
+#define ATTN_ROPE_YARN 3
+#define ATTN_ROPE_LONGROPE 4
+#define ATTN_ROPE_DYNAMIC 5
+#define ATTN_ROPE_MAX_ROTARY_DIM 256
+
+/*
+ * One field per parameter of the catalogue's `rope` op; call
+ * attn_rope_params_init() first (0 means "absent" where noted).
+ *   head_dim      per-head width (> 0)
+ *   rotary_dim    rotated channels per head; 0 = head_dim. Even, <= head_dim,
+ *                 at most ATTN_ROPE_MAX_ROTARY_DIM.
+ *   offset        position of the first row (>= 0); positions stay below 2^31
+ *   interleaved   0: half-split pairs (Llama, NeoX); 1: interleaved (GPT-J)
+ *   base          rope_theta; 0 = 10000
+ *   inv_freq      HOST pointer to rotary_dim/2 floats, or NULL; replaces base
+ *                 and scaling
+ *   has_attention_factor, attention_factor
+ *                 the op's attentionFactor
+ *   scaling       ATTN_ROPE_*; the fields below hold the rope_scaling object's
+ *                 values: factor, low_freq_factor (0 = 1), high_freq_factor
+ *                 (0 = 4), original_max_positions, max_positions,
+ *                 beta_fast (0 = 32), beta_slow (0 = 1), mscale,
+ *                 mscale_all_dim, truncate (init: 1), short_factor and
+ *                 long_factor (HOST pointers to rotary_dim/2 doubles),
+ *                 scaling_attention_factor (0 = absent)
+ */
+typedef struct attn_rope_params {
+    int64_t head_dim;
+    int64_t rotary_dim;
+    int64_t offset;
+    int32_t interleaved;
+    int32_t scaling;
+    double base;
+    const float* inv_freq;
+    int32_t has_attention_factor;
+    float attention_factor;
+    double factor;
+    double low_freq_factor, high_freq_factor;
+    int64_t original_max_positions, max_positions;
+    double beta_fast, beta_slow;
+    double mscale, mscale_all_dim;
+    int32_t truncate;
+    int32_t reserved;
+    const double* short_factor;
+    const double* long_factor;
+    double scaling_attention_factor;
+} attn_rope_params;
+
+/* Fill *r with the defaults: everything absent, truncate = 1. */
+void attn_rope_params_init(attn_rope_params* r);
+
+/* The resolved table for `rows` rows starting at position r->offset (host
+ * only; dynamic and longrope depend on offset + rows): rotary_dim/2 floats
+ * into inv_freq (host memory) and the attention factor. */
+int attn_rope_table(const attn_rope_params* r, int64_t rows, float* inv_freq, float* attention_factor);
+
+/*
+ * out[T, width] = rope(x[T, width]), width = heads * head_dim (a multiple of
+ * head_dim). x and out are device pointers; out may equal x (in place) but
+ * must not otherwise overlap it. T = 0 is a no-op.
+ */
+int attn_rope(const attn_rope_params* r, int64_t T, int64_t width, const float* x, float* out,
+              void* stream);
+
+/*
+ * Rotate, then write (ops `rope` then `cache_write` fused): cache[offset + t, :]
+ * = rope(values)[t, :] for t < rows, the row positions taken from r->offset.
+ * width = kvHeads * head_dim. Same checks as attn_cache_write.
+ */
+int attn_rope_cache_write(float* cache, int64_t max_rows, int64_t width, const float* values,
+                          int64_t rows, int64_t offset, const attn_rope_params* r, void* stream);
 
 /* Text of the calling thread's last error ("" if the last call succeeded). */
 const char* attn_last_error(void);
@@ -197,7 +322,8 @@ int attn_set_option(const char* name, int64_t value);
  * path records nothing when off. Event pairs come from a fixed pool of 4096,
  * created on the first enable; launches beyond the pool are not timed.
  * Kernel names: "cache_write", "decode_split", "prefill", "combine" (merges
- * key-range splits after either), "generic", "zero_fill".
+ * key-range splits after either), "generic", "zero_fill", "rope" (attn_rope and
+ * attn_rope_cache_write).
  */
 int attn_timing_enable(int on);
 int attn_timing_collect(const char* kernel, double* total_ms, int64_t* launches);

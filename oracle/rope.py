@@ -44,9 +44,9 @@ def _f32(x) -> np.ndarray:
 
 
 def _theta(rd: int, base: float) -> np.ndarray:
-    """RoFormer's frequencies base^(-2i/rd), i < rd/2, in f64 (R4)."""
-    i = np.arange(rd // 2, dtype=np.float64)
-    return np.power(float(base), -2.0 * i / rd)
+    """RoFormer's frequencies base^(-2i/rd), i < rd/2, in f64 (R4). Python's
+    float power (the C library's pow), one entry at a time."""
+    return np.array([float(base) ** (-2.0 * i / rd) for i in range(rd // 2)], dtype=np.float64)
 
 
 def _linear(theta, s):
@@ -146,6 +146,8 @@ def _dynamic_base(base, s, rd, seq_len):
     base * (factor * seq_len / original - (factor - 1))^(rd / (rd - 2))."""
     orig = float(s.get("original_max_position_embeddings") or s["max_position_embeddings"])
     factor = float(s["factor"])
+    if rd <= 2:
+        raise ValueError("dynamic scaling needs rotaryDim > 2")
     if seq_len <= orig:
         return base
     return base * (factor * seq_len / orig - (factor - 1.0)) ** (rd / (rd - 2.0))

@@ -38,8 +38,7 @@ MUTANTS = {
 ROPE_MUTANTS = {
     "rope_turn_sense": ("out[:, :, ia] = a * c - b * s", "out[:, :, ia] = a * c + b * s"),
     "rope_half_partner": ("np.arange(half) + half", "np.arange(half) + half - 1"),
-    "rope_freq_exponent": ("return np.power(float(base), -2.0 * i / rd)",
-                           "return np.power(float(base), -1.0 * i / rd)"),
+    "rope_freq_exponent": ("float(base) ** (-2.0 * i / rd)", "float(base) ** (-1.0 * i / rd)"),
     "rope_factor_dropped": ("c = (np.cos(ang) * af)[:, None, :]", "c = np.cos(ang)[:, None, :]"),
     "rope_position_shift": ("pos = (p0 + np.arange(T, dtype=np.int64))",
                             "pos = (p0 + 1 + np.arange(T, dtype=np.int64))"),
