@@ -20,6 +20,10 @@ The same line carries `prefill`: the Llama-3-8B-shaped causal prefill
 (2 headDim + 2 vHeadDim)) over the call time give TFLOP/s, rated against the
 157.3 TFLOP/s fp32 matrix peak.
 
+`rope` holds the rotary embedding: the same decode step with rope fused in
+(K rotated as cache_write stores it, q as attention loads it) and the
+standalone rope kernel on a prefill-sized q, rated against HBM.
+
 `configs` lists the other workloads the same way (their own plan, kernel
 time, call rate, roofline and sampled-row parity): the Llama-shaped chunked
 prefill (T=512 at posOffset 3584), the Gemma-2-shaped sliding-window prefill
@@ -334,6 +338,117 @@ def run_config(w, args, kv_buffers=1):
     return rec
 
 
+LLAMA3_ROPE = dict(base=500000.0, scaling=dict(rope_type="llama3", factor=8.0, low_freq_factor=1.0,
+                                               high_freq_factor=4.0,
+                                               original_max_position_embeddings=8192))
+
+
+def run_rope(args):
+    """The Llama-shaped decode step with the rotary embedding fused in (K rotated
+    as it is written, q as attention loads it), and the standalone rope kernel
+    on a prefill-sized q [4096, 32*128], rated against HBM."""
+    import numpy as np
+    import torch
+
+    import gqa_scaled_dot_amd as ga
+    import oracle
+    import workloads
+
+    w = workloads.LLAMA_DECODE
+    params = w.params()
+    dev = torch.device("cuda:0")
+    q, k, v, _ = w.tensors()
+    rp = dict(headDim=w.headDim, **LLAMA3_ROPE)
+    n_buf = 2
+    qd, kd, vd = (torch.from_numpy(x).to(dev) for x in (q, k, v))
+    kc = [torch.empty_like(kd) for _ in range(n_buf)]
+    vc = [torch.empty_like(vd) for _ in range(n_buf)]
+    for b in range(n_buf):
+        ga.attn_rope_cache_write(kc[b], kd[:w.S - 1], 0, rp)
+        ga.attn_cache_write(vc[b], vd[:w.S - 1], 0)
+    new_k, new_v = kd[w.S - 1:], vd[w.S - 1:]
+    out = torch.empty((w.T, w.heads * w.Dv), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(ga.attn_workspace_size(w.T, w.S, **params), 256), dtype=torch.uint8, device=dev)
+    steps = [(ga.prepare_rope_cache_write(kc[b], new_k, w.S - 1, rp),
+              ga.prepare_cache_write(vc[b], new_v, w.S - 1),
+              ga.prepare_forward(qd, kc[b], vc[b], out=out, workspace=ws, q_rope=dict(LLAMA3_ROPE),
+                                 **params)) for b in range(n_buf)]
+
+    def step(i):
+        for c in steps[i % n_buf]:
+            c()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ga.attn_timing_enable(True)
+    for name in ("decode_split", "combine", "rope", "cache_write"):
+        ga.attn_timing_collect(name)
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    t = {name: ga.attn_timing_collect(name) for name in ("decode_split", "combine", "rope", "cache_write")}
+    ga.attn_timing_enable(False)
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / args.steps
+    us = {name: round(ms / max(n, 1) * 1e3, 3) for name, (ms, n) in t.items()}
+    log(f"[bench] decode step with fused rope: {ms_step * 1e3:.2f} us; kernels {us}")
+    # The oracle on the same step: K rotated at positions 0..S-1, q at S-1.
+    k_rot = oracle.rope(k, offset=0, **rp).astype(np.float32)
+    q_rot = oracle.rope(q, offset=w.posOffset, **rp).astype(np.float32)
+    ref = oracle.attention(q_rot, k_rot, v, threads=cpu_threads(), **params)
+    err = np.abs(out.cpu().numpy().astype(np.float64) - ref)
+    ok = bool(np.all(err <= 1e-4 + 1e-4 * np.abs(ref)))
+    log(f"[bench]   parity vs oracle: max |err| {err.max():.3e} ok={ok}")
+    alg = decode_algorithmic_bytes(w)
+    decode = {"workload": w.name + ", llama3 rope (theta 500000, factor 8) on q and the new K row",
+              "step": "attn_rope_cache_write (new K row) + cache_write (new V row) + attn_forward(q_rope)",
+              "ms_per_step": round(ms_step, 6), "value": round(alg / (ms_step * 1e-3) / 1e9, 1),
+              "unit": "GB/s", "kernel_us": us,
+              "parity": {"max_abs_err": float(err.max()), "ok": ok}}
+    del kc, vc, kd, vd, steps
+    torch.cuda.empty_cache()
+
+    # Standalone rope over a prefill's q: every element read and written once.
+    wp = workloads.LLAMA_PREFILL
+    x = workloads.normal((wp.T, wp.heads * wp.headDim), wp.seed, 0)
+    xd = torch.from_numpy(x).to(dev)
+    yd = torch.empty_like(xd)
+    rq = dict(headDim=wp.headDim, **LLAMA3_ROPE)
+    for _ in range(3):
+        ga.attn_rope(xd, out=yd, **rq)
+    torch.cuda.synchronize()
+    ga.attn_timing_enable(True)
+    ga.attn_timing_collect("rope")
+    for _ in range(args.prefill_steps):
+        ga.attn_rope(xd, out=yd, **rq)
+    torch.cuda.synchronize()
+    r_ms, r_n = ga.attn_timing_collect("rope")
+    ga.attn_timing_enable(False)
+    nbytes = 2 * x.size * 4
+    kern_s = r_ms / r_n * 1e-3
+    achieved = nbytes / kern_s / 1e9
+    rows = sampled_rows(wp)
+    refr = np.stack([oracle.rope(x[r:r + 1], offset=r, **rq)[0] for r in rows])
+    errr = np.abs(yd.cpu().numpy()[rows].astype(np.float64) - refr)
+    okr = bool(np.all(errr <= 4e-6 + 4e-6 * np.abs(refr)))
+    log(f"[bench] rope kernel on q [{wp.T}, {wp.heads * wp.headDim}]: {kern_s * 1e6:.1f} us, "
+        f"{achieved:.1f} GB/s = {achieved / HBM_PEAK_GBS:.1%} of 8 TB/s; parity max |err| {errr.max():.2e} ok={okr}")
+    kernel = {"workload": f"llama3 rope on a prefill's q [{wp.T}, {wp.heads * wp.headDim}]",
+              "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                           "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                           "kernel": "rope", "bytes_per_launch": nbytes,
+                           "avg_launch_us": round(kern_s * 1e6, 3)},
+              "parity": {"rows": len(rows), "max_abs_err": float(errr.max()), "ok": okr}}
+    return {"decode_step": decode, "kernel": kernel}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -353,6 +468,7 @@ def main():
     import workloads
     rec = run_decode(args)
     rec["prefill"] = run_config(workloads.LLAMA_PREFILL, args)
+    rec["rope"] = run_rope(args)
     if not args.no_configs:
         # The other workloads, each on its own plan (decode-shaped ones over 4
         # rotated K/V copies, as the Llama decode uses 2).

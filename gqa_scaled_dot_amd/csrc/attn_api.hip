@@ -110,9 +110,61 @@ double yarn_mscale(double scale, double k) {
     return scale > 1.0 ? 0.1 * k * log(scale) + 1.0 : 1.0;
 }
 
+int rope_compute(const attn_rope_params* r, int64_t seq_len, attn::RopeArgs* out);
+
+// The last table each thread resolved, keyed by the parameters (arrays by
+// content; the row offset only moves positions, and the sequence length
+// matters to dynamic and longrope alone), so a decode loop that passes the
+// same rope every step skips the table's pow and log calls.
+struct RopeCache {
+    bool valid = false;
+    attn_rope_params key;
+    int64_t seq_key = 0;
+    float inv[ATTN_ROPE_MAX_ROTARY_DIM / 2];
+    double sf[ATTN_ROPE_MAX_ROTARY_DIM / 2], lf[ATTN_ROPE_MAX_ROTARY_DIM / 2];
+    attn::RopeArgs val;
+};
+thread_local RopeCache g_rope_cache;
+
 // Checks *r and fills the device-side description for rows at positions
 // offset .. seq_len - 1.
 int rope_resolve(const attn_rope_params* r, int64_t seq_len, attn::RopeArgs* out) {
+    if (!r || r->head_dim <= 0 || r->head_dim > kMaxDim || r->offset < 0 || seq_len > INT32_MAX)
+        return rope_compute(r, seq_len, out);  // the error path names the field
+    const int64_t rd = r->rotary_dim ? r->rotary_dim : r->head_dim;
+    if (rd <= 0 || rd % 2 || rd > r->head_dim || rd > ATTN_ROPE_MAX_ROTARY_DIM)
+        return rope_compute(r, seq_len, out);
+    const int64_t half = rd / 2;
+    // The key keeps whether each array is given; their contents are compared below.
+    attn_rope_params key = *r;
+    key.offset = 0;
+    key.inv_freq = r->inv_freq ? reinterpret_cast<const float*>(1) : nullptr;
+    key.short_factor = r->short_factor ? reinterpret_cast<const double*>(1) : nullptr;
+    key.long_factor = r->long_factor ? reinterpret_cast<const double*>(1) : nullptr;
+    const bool seq_dep = !r->inv_freq && (r->scaling == ATTN_ROPE_DYNAMIC || r->scaling == ATTN_ROPE_LONGROPE);
+    const int64_t seq_key = seq_dep ? seq_len : -1;
+    RopeCache& c = g_rope_cache;
+    if (c.valid && c.seq_key == seq_key && !memcmp(&c.key, &key, sizeof key) &&
+        (!r->inv_freq || !memcmp(c.inv, r->inv_freq, sizeof(float) * half)) &&
+        (!r->short_factor || !memcmp(c.sf, r->short_factor, sizeof(double) * half)) &&
+        (!r->long_factor || !memcmp(c.lf, r->long_factor, sizeof(double) * half))) {
+        *out = c.val;
+        out->pos0 = r->offset;
+        return ok();
+    }
+    const int rc = rope_compute(r, seq_len, out);
+    if (rc) return rc;
+    c.valid = true;
+    c.key = key;
+    c.seq_key = seq_key;
+    if (r->inv_freq) memcpy(c.inv, r->inv_freq, sizeof(float) * half);
+    if (r->short_factor) memcpy(c.sf, r->short_factor, sizeof(double) * half);
+    if (r->long_factor) memcpy(c.lf, r->long_factor, sizeof(double) * half);
+    c.val = *out;
+    return ok();
+}
+
+int rope_compute(const attn_rope_params* r, int64_t seq_len, attn::RopeArgs* out) {
 #pragma clang fp contract(off)
     if (!r) return fail(ATTN_ERR_INVALID, "rope: NULL params");
     if (r->head_dim <= 0 || r->head_dim > kMaxDim)

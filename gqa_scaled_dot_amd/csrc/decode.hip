@@ -99,34 +99,31 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
         hh[r] = g * hpg + (live[r] ? r % hpg : 0);
         pos[r] = p.ep.pos_offset + tt[r];
     }
+    // With a rotary embedding, the raw q channels this thread turns, their pair
+    // partners and frequencies are fetched first, ahead of the K/V loads.
+    constexpr int QE = (NQ * D + kThreads - 1) / kThreads;
+    float qa[QE], qb[QE], qf[QE];
+#pragma unroll
+    for (int c = 0; c < QE; ++c) {
+        qa[c] = 0.0f;
+        qb[c] = 0.0f;
+        qf[c] = 0.0f;
+    }
     if (p.rope.on) {
-        // q rows turned by the rotary embedding once per workgroup, through
-        // LDS (every row group needs the same values).
-        __shared__ __align__(16) float s_q[NQ * D];
-        for (int e = tid; e < NQ * D; e += kThreads) {
+#pragma unroll
+        for (int c = 0; c < QE; ++c) {
+            const int e = tid + c * kThreads;
             const int r = e / D, d = e % D;
-            float x = 0.0f;
-            if (r < nrows) {
+            if (e < NQ * D && r < nrows) {
                 const int t = r / hpg, h = g * hpg + r % hpg;
-                x = rope_channel(p.rope, p.q + (int64_t)t * p.H * D + (int64_t)h * D, d, p.rope.pos0 + t);
+                const float* head = p.q + (int64_t)t * p.H * D + (int64_t)h * D;
+                const RopeTap tp = rope_tap(p.rope, d);
+                qa[c] = head[d];
+                qb[c] = head[tp.partner];
+                qf[c] = p.rope.inv_freq[tp.i];
             }
-            s_q[e] = x;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int r = 0; r < NQ; ++r)
-#pragma unroll
-            for (int j = 0; j < KJ; ++j)
-                qr[r][j] = *reinterpret_cast<const float4*>(s_q + r * D + 64 * j + 4 * ln);
-    } else {
-#pragma unroll
-        for (int r = 0; r < NQ; ++r) {
-            const float* qrow = p.q + (int64_t)tt[r] * p.H * D + (int64_t)hh[r] * D + 4 * ln;
-#pragma unroll
-            for (int j = 0; j < KJ; ++j) qr[r][j] = live[r] ? ld4(qrow + 64 * j) : zero4();
         }
     }
-
     float m[NQ], l[NQ];
     float4 acc[NQ][VJ];
 #pragma unroll
@@ -245,6 +242,37 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
 #pragma unroll
         for (int i = 0; i < DEPTH - 1; ++i)
             if (s0 + i * kStep < k1) load(kr[i], vr[i], br[i], s0 + i * kStep);
+        // q is loaded (and turned, with a rotary embedding) while the first
+        // K/V batches are in flight.
+        if (p.rope.on) {
+            // Every row group needs the same turned q, so each workgroup turns
+            // it once, through LDS: the raw channels were fetched before the
+            // K/V batches were issued, the turn happens while those load.
+            __shared__ __align__(16) float s_q[NQ * D];
+#pragma unroll
+            for (int c = 0; c < QE; ++c) {
+                const int e = tid + c * kThreads;
+                if (e < NQ * D) {
+                    const int r = e / D, d = e % D;
+                    const int t = r / hpg;
+                    s_q[e] = r < nrows ? rope_turn(p.rope, rope_tap(p.rope, d), qa[c], qb[c], qf[c], p.rope.pos0 + t)
+                                       : 0.0f;
+                }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int r = 0; r < NQ; ++r)
+#pragma unroll
+                for (int j = 0; j < KJ; ++j)
+                    qr[r][j] = *reinterpret_cast<const float4*>(s_q + r * D + 64 * j + 4 * ln);
+        } else {
+#pragma unroll
+            for (int r = 0; r < NQ; ++r) {
+                const float* qrow = p.q + (int64_t)tt[r] * p.H * D + (int64_t)hh[r] * D + 4 * ln;
+#pragma unroll
+                for (int j = 0; j < KJ; ++j) qr[r][j] = live[r] ? ld4(qrow + 64 * j) : zero4();
+            }
+        }
         bool done = false;
         for (int s = s0; s < k1 && !done; s += DEPTH * kStep) {
 #pragma unroll

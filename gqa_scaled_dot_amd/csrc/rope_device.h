@@ -56,27 +56,53 @@ __device__ __forceinline__ void rope_cos_sin(int64_t pos, float invf, float af, 
     s = sv * af;
 }
 
-// Channel d of one head (row `head`, head_dim channels) after the turn at
-// position pos. Channels from rd on pass through.
-__device__ __forceinline__ float rope_channel(const RopeArgs& ra, const float* head, int d, int64_t pos) {
-    if (d >= ra.rd) return head[d];
-    int i, partner;
+// Where channel d of a head gets its turn: the frequency index, the channel
+// it pairs with, and the sign of that channel's sine term. Channels from rd
+// on pass through (rot = false, partner = d).
+struct RopeTap {
+    int i;
+    int partner;
     float sgn;
-    if (ra.interleaved) {
-        i = d >> 1;
-        partner = d ^ 1;
-        sgn = (d & 1) ? 1.0f : -1.0f;
+    bool rot;
+};
+
+__device__ __forceinline__ RopeTap rope_tap(const RopeArgs& ra, int d) {
+    RopeTap tp;
+    tp.rot = d < ra.rd;
+    if (!tp.rot) {
+        tp.i = 0;
+        tp.partner = d;
+        tp.sgn = 0.0f;
+    } else if (ra.interleaved) {
+        tp.i = d >> 1;
+        tp.partner = d ^ 1;
+        tp.sgn = (d & 1) ? 1.0f : -1.0f;
     } else {
         const int half = ra.rd >> 1;
         const bool first = d < half;
-        i = first ? d : d - half;
-        partner = first ? d + half : d - half;
-        sgn = first ? -1.0f : 1.0f;
+        tp.i = first ? d : d - half;
+        tp.partner = first ? d + half : d - half;
+        tp.sgn = first ? -1.0f : 1.0f;
     }
+    return tp;
+}
+
+// The turned value of a channel x whose pair partner is xp, at position pos,
+// with invf = inv_freq[tp.i]: first of a pair a cos - b sin, second
+// b cos + a sin.
+__device__ __forceinline__ float rope_turn(const RopeArgs& ra, const RopeTap& tp, float x, float xp, float invf,
+                                           int64_t pos) {
+    if (!tp.rot) return x;
     float c, s;
-    rope_cos_sin(pos, ra.inv_freq[i], ra.af, c, s);
-    // first of a pair: a cos - b sin; second: b cos + a sin
-    return fmaf(sgn * head[partner], s, head[d] * c);
+    rope_cos_sin(pos, invf, ra.af, c, s);
+    return fmaf(tp.sgn * xp, s, x * c);
+}
+
+// Channel d of one head (row `head`, head_dim channels) after the turn at
+// position pos.
+__device__ __forceinline__ float rope_channel(const RopeArgs& ra, const float* head, int d, int64_t pos) {
+    const RopeTap tp = rope_tap(ra, d);
+    return rope_turn(ra, tp, head[d], head[tp.partner], ra.inv_freq[tp.i], pos);
 }
 
 // Channels d0..d0+3 of one head after the turn (d0 a multiple of 4).

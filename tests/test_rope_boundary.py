@@ -173,3 +173,30 @@ def test_q_rope_is_validated_with_the_attention_params():
     with pytest.raises(ga.AttnError) as e:
         ga.attn_validate(1, 64, heads=8, headDim=64, q_rope=dict(scaling=dict(rope_type="linear")))
     assert "factor" in e.value.message
+
+
+def test_table_cache_never_serves_a_stale_table():
+    # The library keeps the last resolved table per thread. Alternate every
+    # case, change an explicit table's contents in place at the same address,
+    # and move the sequence length across dynamic scaling's threshold.
+    order = list(range(len(TABLE_CASES))) * 2
+    np.random.default_rng(5).shuffle(order)
+    for i in order:
+        name, kw, rows = TABLE_CASES[i]
+        test_library_table_is_the_oracles_bit_for_bit(name, kw, rows)
+        test_library_table_is_the_oracles_bit_for_bit(name, kw, rows)   # a cache hit
+    L = _lib.lib()
+    r, keep = ga.make_rope_params(headDim=8, invFreq=[1.0, 0.5, 0.25, 0.125])
+    inv = (ctypes.c_float * 4)()
+    af = ctypes.c_float()
+    assert L.attn_rope_table(ctypes.byref(r), 1, inv, ctypes.byref(af)) == 0
+    assert list(inv) == [1.0, 0.5, 0.25, 0.125]
+    keep[0][2] = 3.0                                    # same pointer, new contents
+    assert L.attn_rope_table(ctypes.byref(r), 1, inv, ctypes.byref(af)) == 0
+    assert list(inv) == [1.0, 0.5, 3.0, 0.125]
+    dyn = dict(headDim=64, scaling=dict(rope_type="dynamic", factor=2.0,
+                                        original_max_position_embeddings=4096))
+    for rows in (10, 5000, 4096, 4097, 10):
+        got, _ = ga.attn_rope_table(rows=rows, **dyn)
+        want, _ = oracle.rope_table(64, scaling=dyn["scaling"], seq_len=rows)
+        np.testing.assert_array_equal(got, want)
