@@ -54,10 +54,12 @@ FP32_PEAK_TFLOPS = 157.3
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
     "decode_split": ["gqa_scaled_dot_amd/csrc/decode.hip", "gqa_scaled_dot_amd/csrc/device_common.h",
-                     "gqa_scaled_dot_amd/csrc/kernels.h"],
+                     "gqa_scaled_dot_amd/csrc/kernels.h", "gqa_scaled_dot_amd/csrc/rope_device.h"],
     "prefill": ["gqa_scaled_dot_amd/csrc/prefill.hip", "gqa_scaled_dot_amd/csrc/prefill16.hip",
                 "gqa_scaled_dot_amd/csrc/prefill_common.h", "gqa_scaled_dot_amd/csrc/device_common.h",
-                "gqa_scaled_dot_amd/csrc/kernels.h"],
+                "gqa_scaled_dot_amd/csrc/kernels.h", "gqa_scaled_dot_amd/csrc/rope_device.h"],
+    "rope": ["gqa_scaled_dot_amd/csrc/rope.hip", "gqa_scaled_dot_amd/csrc/rope_device.h",
+             "gqa_scaled_dot_amd/csrc/kernels.h"],
 }
 
 
@@ -338,6 +340,7 @@ def run_config(w, args, kv_buffers=1):
     return rec
 
 
+ROPE_Q_WORKLOAD = "llama3 rope on a prefill's q [4096, 4096]"
 LLAMA3_ROPE = dict(base=500000.0, scaling=dict(rope_type="llama3", factor=8.0, low_freq_factor=1.0,
                                                high_freq_factor=4.0,
                                                original_max_position_embeddings=8192))
@@ -440,9 +443,10 @@ def run_rope(args):
     okr = bool(np.all(errr <= 4e-6 + 4e-6 * np.abs(refr)))
     log(f"[bench] rope kernel on q [{wp.T}, {wp.heads * wp.headDim}]: {kern_s * 1e6:.1f} us, "
         f"{achieved:.1f} GB/s = {achieved / HBM_PEAK_GBS:.1%} of 8 TB/s; parity max |err| {errr.max():.2e} ok={okr}")
-    kernel = {"workload": f"llama3 rope on a prefill's q [{wp.T}, {wp.heads * wp.headDim}]",
+    kernel = {"workload": ROPE_Q_WORKLOAD,
               "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                           "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                           "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                           "traffic": measured_traffic("rope", ROPE_Q_WORKLOAD),
                            "kernel": "rope", "bytes_per_launch": nbytes,
                            "avg_launch_us": round(kern_s * 1e6, 3)},
               "parity": {"rows": len(rows), "max_abs_err": float(errr.max()), "ok": okr}}
