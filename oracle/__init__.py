@@ -17,6 +17,9 @@ protocol op catalogue, op `attention`, params):
   absolute position s.
 * scale defaults to 1/sqrt(headDim), which is what it "replaces".
 * softcap and window: absent or 0 means off; negative values are refused.
+* sinks (not a catalogue param: the IR schema's op_attention and slot_kv carry
+  it beside `window`): with a window, the first `sinks` keys stay visible, as
+  StreamingLLM keeps its initial tokens. 0 or absent means none.
 * ALiBi: alibiSlopes wins over alibiMax, which wins over alibi. The slopes
   enter as f32 values, as every tensor and number of the op is f32
   (catalogue convention: tensors are row-major f32); the same holds for
@@ -50,7 +53,7 @@ class _Args(ctypes.Structure):
         ("causal", ctypes.c_int32), ("pos_offset", ctypes.c_int64),
         ("scale", ctypes.c_double), ("softcap", ctypes.c_double),
         ("window", ctypes.c_int64), ("slopes", ctypes.POINTER(ctypes.c_double)),
-        ("bias_kind", ctypes.c_int32),
+        ("bias_kind", ctypes.c_int32), ("sinks", ctypes.c_int64),
     ]
 
 
@@ -97,7 +100,7 @@ def resolve(T: int, S: int, *, heads: int, headDim: int, kvHeads: Optional[int] 
             posOffset: Optional[int] = None, scale: Optional[float] = None,
             softcap: Optional[float] = None, window: Optional[int] = None,
             alibi: Optional[bool] = None, alibiMax: Optional[float] = None,
-            alibiSlopes: Optional[Sequence[float]] = None) -> dict:
+            alibiSlopes: Optional[Sequence[float]] = None, sinks: Optional[int] = None) -> dict:
     """Apply the catalogue's defaults; raise ValueError on what it cannot mean."""
     H = int(heads)
     G = int(kvHeads) if kvHeads else H
@@ -116,6 +119,9 @@ def resolve(T: int, S: int, *, heads: int, headDim: int, kvHeads: Optional[int] 
     w = int(window) if window else 0
     if w < 0:
         raise ValueError("window must be >= 0")
+    nsink = int(sinks) if sinks else 0
+    if nsink < 0:
+        raise ValueError("sinks must be >= 0")
     sigma = f32(scale) if scale is not None else f32(1.0 / math.sqrt(D))
     if alibiSlopes is not None:
         if len(alibiSlopes) != H:
@@ -129,7 +135,7 @@ def resolve(T: int, S: int, *, heads: int, headDim: int, kvHeads: Optional[int] 
         slopes = None
     return dict(T=int(T), S=int(S), H=H, G=G, D=D, Dv=Dv,
                 causal=True if causal is None else bool(causal), P0=P0,
-                scale=sigma, softcap=f32(c), window=w, slopes=slopes)
+                scale=sigma, softcap=f32(c), window=w, slopes=slopes, sinks=nsink)
 
 
 def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, bias: Optional[np.ndarray] = None,
@@ -173,7 +179,7 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, bias: Optional[np.nda
     slopes_arr = None
     args = _Args(T=T, S=S, H=H, G=G, D=D, Dv=Dv, causal=int(r["causal"]),
                  pos_offset=r["P0"], scale=r["scale"], softcap=r["softcap"],
-                 window=r["window"], slopes=None, bias_kind=bias_kind)
+                 window=r["window"], slopes=None, bias_kind=bias_kind, sinks=r["sinks"])
     if r["slopes"] is not None:
         slopes_arr = np.asarray(r["slopes"], dtype=np.float64)
         args.slopes = slopes_arr.ctypes.data_as(ctypes.POINTER(ctypes.c_double))

@@ -15,6 +15,11 @@
  *   g = floor(h * G / H) the key/value head h reads:
  *     visible(s)  causal:      pos - window < s <= pos   (window 0: s <= pos)
  *                 non-causal:  |pos - s| <= window        (window 0: every s)
+ *                 with a window and sinks > 0, the keys s < sinks are also
+ *                 visible (causal rows still need s <= pos): the attention
+ *                 sinks the IR schema pairs with `window` (op_attention and
+ *                 slot_kv, property `sinks`), read as StreamingLLM's kept
+ *                 initial tokens
  *     x_s = scale * sum_d q[t, h*D + d] * k[s, g*D + d]
  *     x_s = softcap * tanh(x_s / softcap)         if softcap > 0
  *     x_s = x_s - slope[h] * |pos - s|            if ALiBi slopes are given
@@ -43,6 +48,7 @@ typedef struct {
     int64_t window;        /* 0: off */
     const double* slopes;  /* NULL: no ALiBi; else H entries */
     int32_t bias_kind;     /* 0 none, 1 [T,S], 2 [H,T,S] */
+    int64_t sinks;         /* 0: none; with a window, keys s < sinks stay visible */
 } oracle_attention_args;
 
 typedef struct {
@@ -56,12 +62,15 @@ typedef struct {
 
 static int key_visible(const oracle_attention_args* a, int64_t pos, int64_t s)
 {
+    /* an attention sink: one of the first `sinks` keys, kept in view beside the window */
+    const int sink = a->window > 0 && s < a->sinks;
     if (a->causal) {
         if (s > pos) return 0;
+        if (sink) return 1;
         if (a->window > 0 && !(pos - a->window < s)) return 0;
         return 1;
     }
-    if (a->window > 0) {
+    if (a->window > 0 && !sink) {
         int64_t dist = pos > s ? pos - s : s - pos;
         if (dist > a->window) return 0;
     }

@@ -526,3 +526,115 @@ def test_cache_write_copies_rows_exactly():
     assert np.array_equal(cache[:4], before[:4]) and np.array_equal(cache[7:], before[7:])
     with pytest.raises(ValueError):
         oracle.cache_write(cache, vals, 8)
+
+
+# --------------------------------------------------------------------------
+# Attention sinks (the IR schema's `sinks` beside `window`; the reading is
+# StreamingLLM's kept initial tokens: keys s < sinks stay visible).
+# --------------------------------------------------------------------------
+
+def _uniform_weights_row_sinks(causal, S, pos, window, sinks):
+    q = np.zeros((1, 4), np.float32)
+    k = _rand((S, 4), 1)
+    v = np.eye(S, dtype=np.float32)
+    return oracle.attention(q, k, v, heads=1, headDim=4, vHeadDim=S, causal=bool(causal),
+                            posOffset=pos, window=window, sinks=sinks)[0]
+
+
+def test_golden_sink_visibility():
+    cases = 0
+    for line in _golden_lines("sink_visibility.txt"):
+        lhs, rhs = line.split(":")
+        causal, S, pos, window, sinks = (int(x) for x in lhs.split())
+        visible = [int(x) for x in rhs.split()]
+        row = _uniform_weights_row_sinks(causal, S, pos, window, sinks)
+        want = np.zeros(S)
+        want[visible] = 1.0 / len(visible)
+        np.testing.assert_allclose(row, want, rtol=0, atol=1e-15, err_msg=line)
+        cases += 1
+    assert cases >= 10
+
+
+def test_closed_form_one_sink_and_a_one_key_window():
+    # Causal row at position 5 with window 1 and one sink sees keys 0 and 5
+    # only; scores 0.5 * q.k are 0 and 1 (headDim 4, default scale 1/2).
+    q = np.ones((1, 4), np.float32)
+    k = np.full((6, 4), 9.0, np.float32)              # hidden keys would dominate if seen
+    k[0] = 0.0
+    k[5] = 0.5
+    v = np.arange(6, dtype=np.float32)[:, None] * 10.0
+    out = oracle.attention(q, k, v, heads=1, headDim=4, vHeadDim=1, posOffset=5, window=1, sinks=1)
+    w5 = _sigmoid(1.0)
+    assert out[0, 0] == pytest.approx(w5 * 50.0 + (1 - w5) * 0.0, abs=1e-12)
+
+
+def test_sinks_zero_or_without_window_change_nothing():
+    T, S, H, G, D = 6, 20, 4, 2, 8
+    q, k, v = _rand((T, H * D), 61), _rand((S, G * D), 62), _rand((S, G * D), 63)
+    for causal in (True, False):
+        kw = dict(heads=H, kvHeads=G, headDim=D, posOffset=12, causal=causal)
+        np.testing.assert_array_equal(oracle.attention(q, k, v, window=4, sinks=0, **kw),
+                                      oracle.attention(q, k, v, window=4, **kw))
+        np.testing.assert_array_equal(oracle.attention(q, k, v, sinks=5, **kw),
+                                      oracle.attention(q, k, v, **kw))
+
+
+def test_all_keys_sinks_is_plain_causal():
+    T, S, H, D = 5, 16, 2, 4
+    q, k, v = _rand((T, H * D), 64), _rand((S, D), 65), _rand((S, D), 66)
+    kw = dict(heads=H, kvHeads=1, headDim=D, posOffset=11)
+    np.testing.assert_array_equal(oracle.attention(q, k, v, window=2, sinks=S, **kw),
+                                  oracle.attention(q, k, v, **kw))
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_sinks_equal_a_bias_mask(causal):
+    # A -1e9 bias on every key outside (sinks U window) and no window gives the
+    # same result bit for bit (exp underflows to exactly 0).
+    T, S, H, G, D, P0, w, n = 6, 30, 4, 2, 8, 20, 5, 3
+    q, k, v = _rand((T, H * D), 67), _rand((S, G * D), 68), _rand((S, G * D), 69)
+    bias = np.zeros((T, S), np.float32)
+    for t in range(T):
+        pos = P0 + t
+        for s in range(S):
+            inwin = (pos - w < s <= pos) if causal else abs(pos - s) <= w
+            if not (inwin or s < n):
+                bias[t, s] = -1e9
+    kw = dict(heads=H, kvHeads=G, headDim=D, posOffset=P0, causal=causal)
+    np.testing.assert_array_equal(oracle.attention(q, k, v, bias, **kw),
+                                  oracle.attention(q, k, v, window=w, sinks=n, **kw))
+
+
+def _sdpa_with_sinks(q, k, v, H, G, D, causal, P0, sigma, window, sinks):
+    T, S = q.shape[0], k.shape[0]
+    qt = torch.from_numpy(q.astype(np.float64)).view(T, H, D).transpose(0, 1)
+    kt = torch.from_numpy(k.astype(np.float64)).view(S, G, D).transpose(0, 1).repeat_interleave(H // G, 0)
+    vt = torch.from_numpy(v.astype(np.float64)).view(S, G, D).transpose(0, 1).repeat_interleave(H // G, 0)
+    pos = P0 + torch.arange(T)[:, None]
+    s = torch.arange(S)[None, :]
+    win = ((s <= pos) & (s > pos - window)) if causal else ((pos - s).abs() <= window)
+    sink = (s < sinks) & ((s <= pos) if causal else torch.ones_like(win))
+    mask = torch.zeros(T, S, dtype=torch.float64).masked_fill(~(win | sink), float("-inf"))
+    out = torch.nn.functional.scaled_dot_product_attention(qt.contiguous()[None], kt.contiguous()[None],
+                                                           vt.contiguous()[None], attn_mask=mask,
+                                                           scale=sigma)
+    return out[0].transpose(0, 1).reshape(T, H * D).numpy()
+
+
+@pytest.mark.parametrize("causal, T, S, P0, window, sinks", [
+    (True, 7, 40, 33, 4, 4), (True, 16, 16, 0, 3, 2), (True, 1, 64, 63, 8, 1),
+    (False, 9, 30, 10, 2, 5), (False, 4, 12, 0, 1, 3)])
+def test_sinks_match_torch_sdpa_f64(causal, T, S, P0, window, sinks):
+    H, G, D = 4, 2, 8
+    q, k, v = _rand((T, H * D), 70 + T, 1.5), _rand((S, G * D), 71 + S, 1.5), _rand((S, G * D), 72)
+    got = oracle.attention(q, k, v, heads=H, kvHeads=G, headDim=D, posOffset=P0, causal=causal,
+                           window=window, sinks=sinks)
+    sigma = oracle.f32(1 / math.sqrt(D))   # the scale enters as an f32 number
+    want = _sdpa_with_sinks(q, k, v, H, G, D, causal, P0, sigma, window, sinks)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+def test_negative_sinks_refused():
+    with pytest.raises(ValueError):
+        oracle.attention(np.zeros((1, 4), np.float32), np.zeros((2, 4), np.float32),
+                         np.zeros((2, 4), np.float32), heads=1, headDim=4, window=1, sinks=-1)

@@ -32,6 +32,11 @@ MUTANTS = {
         "        if (a->slopes) {",
         "if (a->slopes) {"),
     "max_not_subtracted": ("double p = exp(x[s] - M);", "double p = exp(x[s]);"),
+    "sink_edge": ("const int sink = a->window > 0 && s < a->sinks;",
+                  "const int sink = a->window > 0 && s <= a->sinks;"),
+    "sink_ignores_causal": ("        if (s > pos) return 0;\n        if (sink) return 1;",
+                            "        if (sink) return 1;\n        if (s > pos) return 0;"),
+    "sink_noncausal_dropped": ("if (a->window > 0 && !sink) {", "if (a->window > 0) {"),
 }
 
 # Slips in the rotary embedding (oracle/rope.py), caught by tests/test_oracle_rope.py.
