@@ -29,7 +29,8 @@ time, call rate, roofline and sampled-row parity): the Llama-shaped chunked
 prefill (T=512 at posOffset 3584), the Gemma-2-shaped sliding-window prefill
 (T=S=8192, headDim 256, softcap 50, window 4096), and the latent-shaped
 ALiBi + per-head bias decode (S=8192, headDim 192, vHeadDim 128) and
-non-causal prefill (T=S=1024).
+non-causal prefill (T=S=1024), and the Llama-shaped streaming decode (window
+4096 plus 4 attention sinks over a 32768-row cache).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
        [--prefill-steps K] [--no-configs]
@@ -88,10 +89,13 @@ def measured_traffic(kernel: str, workload: str):
 
 
 def decode_algorithmic_bytes(w) -> int:
-    """Every visible K and V row once, plus q, out and the visible bias entries."""
+    """Every visible K and V row once (window rows and the sinks below them),
+    plus q, out and the visible bias entries."""
     lo = max(0, w.posOffset - (w.window or 0) + 1) if w.window else 0
     hi = min(w.S, w.posOffset + w.T)
     rows = hi - lo
+    if w.window and w.sinks:
+        rows += min(w.sinks, lo)
     b = rows * w.G * (w.headDim + w.Dv) * 4
     b += w.T * w.heads * w.headDim * 4 + w.T * w.heads * w.Dv * 4
     if w.bias == "HTS":
@@ -478,7 +482,8 @@ def main():
         # rotated K/V copies, as the Llama decode uses 2).
         rec["configs"] = [run_config(w, args, kv_buffers=4 if w.T == 1 else 1)
                           for w in (workloads.LLAMA_CHUNKED, workloads.GEMMA2_SWA,
-                                    workloads.LATENT_DECODE, workloads.LATENT_NONCAUSAL)]
+                                    workloads.LATENT_DECODE, workloads.LATENT_NONCAUSAL,
+                                    workloads.LLAMA_STREAMING)]
     print(json.dumps(rec), flush=True)
 
 

@@ -60,6 +60,7 @@ class AttnParams(ctypes.Structure):
         ("alibi_slopes", ctypes.POINTER(ctypes.c_float)),
         ("bias_kind", ctypes.c_int32), ("reserved", ctypes.c_int32),
         ("q_rope", ctypes.POINTER(AttnRopeParams)),
+        ("sinks", ctypes.c_int64),
     ]
 
 

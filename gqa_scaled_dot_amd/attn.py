@@ -107,11 +107,12 @@ def make_params(T: int, S: int, *, heads: int, headDim: int, kvHeads: Optional[i
                 softcap: Optional[float] = None, window: Optional[int] = None,
                 alibi: Optional[bool] = None, alibiMax: Optional[float] = None,
                 alibiSlopes: Optional[Sequence[float]] = None, bias_kind: int = 0,
-                q_rope: Optional[dict] = None):
+                q_rope: Optional[dict] = None, sinks: Optional[int] = None):
     """attn_params for one call. Returns (params, keepalive) - keep the second
     alive until the call returns (it owns the explicit slope array and the
     q_rope parameters). q_rope holds `rope` op params for q; its headDim
-    defaults to headDim and its offset to posOffset."""
+    defaults to headDim and its offset to posOffset. sinks: attention sinks
+    beside the window (keys s < sinks stay visible)."""
     L = _lib.lib()
     p = AttnParams()
     L.attn_params_init(ctypes.byref(p))
@@ -129,6 +130,8 @@ def make_params(T: int, S: int, *, heads: int, headDim: int, kvHeads: Optional[i
         p.softcap = float(softcap)
     if window is not None:
         p.window = int(window)
+    if sinks is not None:
+        p.sinks = int(sinks)
     keep = None
     if alibiSlopes is not None:
         # The C ABI takes `heads` floats; only the caller knows the list's length.

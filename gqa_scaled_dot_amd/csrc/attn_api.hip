@@ -334,6 +334,8 @@ int resolve(const attn_params* p, Resolved* r) {
         return fail(ATTN_ERR_INVALID, "softcap: must be finite and >= 0 (0 = off)");
     if (p->window < 0)
         return fail(ATTN_ERR_INVALID, "window: must be >= 0 (0 = off; got %lld)", (long long)p->window);
+    if (p->sinks < 0)
+        return fail(ATTN_ERR_INVALID, "sinks: must be >= 0 (0 = none; got %lld)", (long long)p->sinks);
     if (p->bias_kind < ATTN_BIAS_NONE || p->bias_kind > ATTN_BIAS_HTS)
         return fail(ATTN_ERR_INVALID, "bias: bias_kind must be 0, 1 ([T,S]) or 2 ([heads,T,S])");
     if (p->alibi < ATTN_ALIBI_NONE || p->alibi > ATTN_ALIBI_EXPLICIT)
@@ -378,6 +380,8 @@ int resolve(const attn_params* p, Resolved* r) {
     // Every position is below 2^31, so a wider window sees every key a window
     // of 2^31-1 sees.
     e.window = (int32_t)(o.window < INT32_MAX ? o.window : INT32_MAX);
+    // Sinks only matter beside a window; keys past S do not exist.
+    e.sinks = o.window > 0 ? (int32_t)(p->sinks < o.S ? p->sinks : o.S) : 0;
     e.has_alibi = p->alibi != ATTN_ALIBI_NONE;
     if (p->alibi == ATTN_ALIBI_BLOOM) slopes_bloom(o.H, e.slopes);
     if (p->alibi == ATTN_ALIBI_MPT) slopes_mpt(o.H, (double)p->alibi_max, e.slopes);
@@ -439,7 +443,9 @@ int make_plan(const Resolved& r, Plan* plan) {
         return ok();
     }
     const attn::KeyRange kr = key_range(r);
-    if (r.S == 0 || kr.hi <= kr.lo) {
+    // Attention sinks below the window range: keys every row sees.
+    const int64_t sink_hi = r.ep.sinks < kr.lo ? r.ep.sinks : kr.lo;
+    if (r.S == 0 || (kr.hi <= kr.lo && sink_hi == 0)) {
         plan->path = ATTN_PATH_ZERO;
         return ok();
     }
@@ -471,7 +477,7 @@ int make_plan(const Resolved& r, Plan* plan) {
         d.nq = next_pow2_nq(nrows);
         d.depth = g_opt_decode_depth ? (int32_t)g_opt_decode_depth : 2;
         d.range = kr;
-        const int64_t n = kr.hi - kr.lo;
+        const int64_t n = kr.hi > kr.lo ? kr.hi - kr.lo : 0;
         int64_t splits = g_opt_decode_splits;
         if (splits <= 0) {
             const int64_t target = ((int64_t)kCUs * kDecodeWgPerCU + r.G - 1) / r.G;
@@ -479,17 +485,20 @@ int make_plan(const Resolved& r, Plan* plan) {
             splits = target < most ? target : most;
         }
         if (splits < 1) splits = 1;
-        if (splits > kDecodeMaxSplits) splits = kDecodeMaxSplits;
-        int64_t chunk = (n + splits - 1) / splits;
+        if (splits > kDecodeMaxSplits - 1) splits = kDecodeMaxSplits - 1;
+        int64_t chunk = n > 0 ? (n + splits - 1) / splits : kDecodeChunkAlign;
         chunk = (chunk + kDecodeChunkAlign - 1) / kDecodeChunkAlign * kDecodeChunkAlign;
         // The kernel addresses a chunk with 32-bit offsets from its first row.
         const int64_t row_floats = r.G * (r.D > r.Dv ? r.D : r.Dv);
         const int64_t max_chunk = (INT32_MAX - row_floats) / row_floats / kDecodeChunkAlign * kDecodeChunkAlign;
-        if (max_chunk < kDecodeChunkAlign || (n + max_chunk - 1) / max_chunk > kDecodeMaxSplits)
+        if (max_chunk < kDecodeChunkAlign || (n + max_chunk - 1) / max_chunk > kDecodeMaxSplits - 1 ||
+            sink_hi > max_chunk)
             return fail(ATTN_ERR_UNSUPPORTED, "S: key range too long for the decode path at this width");
         if (chunk > max_chunk) chunk = max_chunk;
         d.chunk = chunk;
-        d.splits = (int32_t)((n + chunk - 1) / chunk);
+        // The sink keys below the window get a split of their own (the last).
+        d.sink_hi = (int32_t)sink_hi;
+        d.splits = (int32_t)((n + chunk - 1) / chunk) + (sink_hi > 0 ? 1 : 0);
         if (d.splits > 1)
             plan->workspace = sizeof(float) * (size_t)(r.T * r.H) * (size_t)d.splits * (size_t)(r.Dv + 2);
     }
@@ -512,7 +521,7 @@ int make_plan(const Resolved& r, Plan* plan) {
         pp.qblocks = (int32_t)qblocks;
         // Too few workgroups to fill the chip: split each one's key range.
         const int64_t slots = (int64_t)kCUs * attn::prefill_wgs_per_cu(pp.variant, (int)r.D, (int)r.Dv);
-        const int64_t tiles = (kr.hi - kr.lo + 31) / 32;
+        const int64_t tiles = (kr.hi > kr.lo ? (kr.hi - kr.lo + 31) / 32 : 0) + (sink_hi + 31) / 32;
         int64_t ks = g_opt_prefill_splits;
         if (ks <= 0) {
             ks = nwg >= slots ? 1 : (slots + nwg - 1) / nwg;

@@ -134,8 +134,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
         for (int j = 0; j < VJ; ++j) acc[r][j] = zero4();
     }
 
-    const int k0 = (int)(plan.range.lo + (int64_t)sp * plan.chunk);
-    const int k1 = (int)min(plan.range.hi, (int64_t)k0 + plan.chunk);
+    // This split's keys: a chunk of the window range, or (the last split, with
+    // attention sinks) the sink keys below it.
+    const bool sink_split = plan.sink_hi > 0 && sp == (int)gridDim.x - 1;
+    const int k0 = sink_split ? 0 : (int)(plan.range.lo + (int64_t)sp * plan.chunk);
+    const int k1 = sink_split ? plan.sink_hi : (int)min(plan.range.hi, (int64_t)k0 + plan.chunk);
     // Workgroup-uniform bases; per-lane offsets stay in 32 bits (the host
     // keeps chunk * row stride below 2^31 floats).
     const uint32_t kstride = (uint32_t)(p.G * D), vstride = (uint32_t)(p.G * DV);

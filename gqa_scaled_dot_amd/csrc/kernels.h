@@ -21,6 +21,7 @@ struct Epilogue {
     int32_t bias_kind;  // ATTN_BIAS_*
     int32_t pos_offset; // positions are below 2^31 (checked on the host)
     int32_t window;     // 0: off
+    int32_t sinks;      // attention sinks: keys s < sinks stay visible beside the window (0 without one)
     float slopes[ATTN_ALIBI_MAX_HEADS];
 };
 
@@ -56,9 +57,10 @@ struct KeyRange {
 
 struct DecodePlan {
     int32_t nq;       // query rows per KV group this instance holds (template value)
-    int32_t splits;   // key-range splits per KV group
+    int32_t splits;   // key-range splits per KV group (the sink split included)
     int32_t depth;    // batches in the split kernel's register ring (2 or 3)
-    int64_t chunk;    // keys per split (multiple of the row-group step)
+    int32_t sink_hi;  // > 0: the last split covers the sink keys [0, sink_hi) below `range`
+    int64_t chunk;    // keys per split of `range` (multiple of the row-group step)
     KeyRange range;
 };
 

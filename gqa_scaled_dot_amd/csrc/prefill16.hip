@@ -102,11 +102,12 @@ __global__ __launch_bounds__(kThreads16, 1) void prefill16_kernel(Problem p, Arg
     for (int b = 0; b < NB; ++b) o[b] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
     float m = -INFINITY, l = 0.0f;
 
-    const int kt_all0 = klo / kBK;
-    const int kt_all1 = khi > klo ? (khi + kBK - 1) / kBK : kt_all0;
-    const int per = (kt_all1 - kt_all0 + a.ksplit - 1) / a.ksplit;
-    const int kt0 = min(kt_all1, kt_all0 + c.ks * per);
-    const int kt1 = min(kt_all1, kt0 + per);
+    // This workgroup's part of its key tiles (sink tiles, then window tiles).
+    const KeyRows rows = key_rows(p.ep, klo, khi);
+    const TileSpan span = tile_span(rows);
+    const int per = (span.count + a.ksplit - 1) / a.ksplit;
+    const int v0 = min(span.count, c.ks * per);
+    const int v1 = min(span.count, v0 + per);
 
     const int64_t kstride = (int64_t)p.G * D, vstride = (int64_t)p.G * DV;
     const float* kg = p.k + (int64_t)c.g * D;
@@ -114,21 +115,25 @@ __global__ __launch_bounds__(kThreads16, 1) void prefill16_kernel(Problem p, Arg
     float4 kst[Sh::KF4], vst[Sh::VF4];
     const float qk_scale = p.ep.scale * kLog2e;
 
-    if (kt0 < kt1) {
-        fetch_rows<D, kThreads16>(kst, kg, kstride, kt0, klo, khi);
-        fetch_rows<DV, kThreads16>(vst, vg, vstride, kt0, klo, khi);
+    if (v0 < v1) {
+        fetch_rows<D, kThreads16>(kst, kg, kstride, span.tile(v0), rows);
+        fetch_rows<DV, kThreads16>(vst, vg, vstride, span.tile(v0), rows);
         stage_rows<D, kThreads16>(kst, ktile);
         stage_rows<DV, kThreads16>(vst, vtile);
     }
-    for (int kt = kt0; kt < kt1; ++kt) {
-        const int buf = (kt - kt0) & 1;
-        const bool more = kt + 1 < kt1;
+    for (int v = v0; v < v1; ++v) {
+        const int kt = span.tile(v);
+        const int buf = (v - v0) & 1;
+        const bool more = v + 1 < v1;
+        const int kt_next = span.tile(v + 1);
         __syncthreads();  // tile `kt` is in LDS; everyone is done with the other buffer
-        if (more) fetch_rows<D, kThreads16>(kst, kg, kstride, kt + 1, klo, khi);
+        if (more) fetch_rows<D, kThreads16>(kst, kg, kstride, kt_next, rows);
 
         const int s_first = kt * kBK;
         bool any_vis, all_vis;
-        tile_visibility(p.ep, s_first, s_first + kBK - 1, wpf, wpl, klo, khi, any_vis, all_vis);
+        tile_visibility(p.ep, s_first, s_first + kBK - 1, wpf, wpl, rows, any_vis, all_vis);
+        // Whether the tile holds attention sinks (their rule is checked only then).
+        const bool sink_tile = s_first < p.ep.sinks;
 
         const float* kt_ = ktile + buf * kBK * KLD;
         const float* vt_ = vtile + buf * kBK * VLD;
@@ -161,7 +166,8 @@ __global__ __launch_bounds__(kThreads16, 1) void prefill16_kernel(Problem p, Arg
                     const int s = s_first + kb * 16 + 4 * quad + r;
                     float xs = score2<EPI>(p, sacc[r], qk_scale, h, pos, s, bpre[kb][EPI ? r : 0]);
                     if (!all_vis) {
-                        const bool vis = (s >= klo) & (s < khi) & key_visible(p.ep, pos, s);
+                        bool vis = (s < rows.khi) & window_visible(p.ep, pos, s);
+                        if (sink_tile) vis = vis | ((s < rows.khi) & sink_visible(p.ep, pos, s));
                         xs = vis ? xs : -INFINITY;
                     }
                     x[kb][r] = xs;
@@ -195,7 +201,7 @@ __global__ __launch_bounds__(kThreads16, 1) void prefill16_kernel(Problem p, Arg
                     l += x[kb][r];
                 }
         }
-        if (more) fetch_rows<DV, kThreads16>(vst, vg, vstride, kt + 1, klo, khi);
+        if (more) fetch_rows<DV, kThreads16>(vst, vg, vstride, kt_next, rows);
 
         if (any_vis) {
 #pragma unroll

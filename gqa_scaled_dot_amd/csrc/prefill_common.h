@@ -66,10 +66,51 @@ __device__ __forceinline__ void visible_keys(const Epilogue& e, int S, int pf, i
     }
 }
 
+// The key rows a workgroup loads: the attention sinks below its window range,
+// [0, sink_hi), and the window range [klo, khi). Other rows are never read;
+// their LDS rows are zero. 1 <= khi <= S, so clamping a row number into
+// [klo, khi - 1] gives an in-bounds row whether or not the window is empty.
+// Every loaded row lies below khi, and every row below khi that is not loaded
+// is hidden from all the workgroup's queries (before every window, not a
+// sink), so inside a tile `s < khi` and the visibility rule mask exactly.
+struct KeyRows {
+    int sink_hi, klo, khi;
+    __device__ __forceinline__ bool loaded(int s) const {
+        return ((unsigned)s < (unsigned)sink_hi) | ((unsigned)(s - klo) < (unsigned)(khi - klo));
+    }
+};
+
+__device__ __forceinline__ KeyRows key_rows(const Epilogue& e, int klo, int khi) {
+    KeyRows r;
+    r.sink_hi = min(e.sinks, klo);  // e.sinks is 0 without a window
+    r.klo = klo;
+    r.khi = khi;
+    return r;
+}
+
+// The workgroup's key tiles in the order it visits them: the sink tiles
+// [0, nst), then the window tiles from kt_w0. Virtual tile v is tile
+// v < nst ? v : kt_w0 + v - nst.
+struct TileSpan {
+    int nst, kt_w0, count;
+    __device__ __forceinline__ int tile(int v) const { return v < nst ? v : kt_w0 + v - nst; }
+};
+
+__device__ __forceinline__ TileSpan tile_span(const KeyRows& r) {
+    TileSpan t;
+    t.kt_w0 = r.klo / kBK;
+    const int kt_w1 = r.khi > r.klo ? (r.khi + kBK - 1) / kBK : t.kt_w0;
+    // A sink tile that reaches the first window tile is that tile.
+    const int nst = (r.sink_hi + kBK - 1) / kBK;
+    t.nst = kt_w1 > t.kt_w0 ? min(nst, t.kt_w0) : nst;
+    t.count = t.nst + (kt_w1 - t.kt_w0);
+    return t;
+}
+
 // Whether any / every query at positions [wpf, wpl] sees any / every key of
-// [s_first, s_last] (every key also inside [klo, khi)).
+// [s_first, s_last] (every key also a loaded row).
 __device__ __forceinline__ void tile_visibility(const Epilogue& e, int s_first, int s_last, int wpf,
-                                                int wpl, int klo, int khi, bool& any_vis,
+                                                int wpl, const KeyRows& rows, bool& any_vis,
                                                 bool& all_vis) {
     if (e.causal) {
         any_vis = s_first <= wpl && (e.window == 0 || s_last > wpf - e.window);
@@ -82,24 +123,48 @@ __device__ __forceinline__ void tile_visibility(const Epilogue& e, int s_first, 
         any_vis = true;
         all_vis = true;
     }
-    all_vis = all_vis && s_first >= klo && s_last < khi;
+    all_vis = all_vis && s_first >= rows.klo && s_last < rows.khi;
+    if (s_first < e.sinks) {
+        // Sink keys: seen by every row (causal: at or before its position).
+        any_vis = any_vis || !e.causal || s_first <= wpl;
+        all_vis = all_vis || (s_last < rows.sink_hi && (!e.causal || s_last <= wpf));
+    }
 }
 
 // Global -> registers -> LDS staging of the rows [kt*kBK, kt*kBK + kBK) of a
 // K or V tile (width W floats, global row stride `stride`) by NT threads.
-// Rows outside [klo, khi) are loaded from a clamped, in-bounds row and
-// replaced by zeros, so the loads need no branches.
+// A tile whose rows are all loaded rows (all but the first and last tiles of
+// a range) is read straight: the tile's base is workgroup-uniform and each
+// lane adds a fixed 32-bit byte offset. Elsewhere rows that are not loaded
+// read a clamped, in-bounds row instead and are replaced by zeros, so the
+// loads need no branches. stride <= 65536 heads x 256 floats, so an offset
+// inside a tile (< kBK * stride * 4 bytes = 2^31) fits in 32 bits.
 template <int W, int NT>
 __device__ __forceinline__ void fetch_rows(float4 (&st)[kBK * W / 4 / NT], const float* base,
-                                           int64_t stride, int kt, int klo, int khi) {
+                                           int64_t stride, int kt, const KeyRows& rows) {
+    const int s0 = kt * kBK;
+    const bool whole = ((s0 >= rows.klo) & (s0 + kBK <= rows.khi)) | (s0 + kBK <= rows.sink_hi);
+    if (whole) {
+        const char* tb = reinterpret_cast<const char*>(base + (int64_t)s0 * stride);
+#pragma unroll
+        for (int j = 0; j < kBK * W / 4 / NT; ++j) {
+            const int f = (int)threadIdx.x + j * NT;
+            const uint32_t row = (uint32_t)(f / (W / 4)), c4 = (uint32_t)(f % (W / 4));
+            const uint32_t off = (row * (uint32_t)stride + 4u * c4) * 4u;
+            st[j] = *reinterpret_cast<const float4*>(tb + off);
+        }
+        return;
+    }
 #pragma unroll
     for (int j = 0; j < kBK * W / 4 / NT; ++j) {
         const int f = (int)threadIdx.x + j * NT;
         const int row = f / (W / 4), c4 = f % (W / 4);
-        const int s = kt * kBK + row;
-        const int sc = min(max(s, klo), khi - 1);
+        const int s = s0 + row;
+        const bool ok = rows.loaded(s);
+        // The nearest row of [klo, khi) (khi - 1 when that range is empty):
+        // usually a cache line the neighbouring loads touch anyway.
+        const int sc = ok ? s : min(max(s, rows.klo), rows.khi - 1);
         const float4 x = *reinterpret_cast<const float4*>(base + sc * stride + 4 * c4);
-        const bool ok = (s >= klo) & (s < khi);
         st[j].x = ok ? x.x : 0.0f;
         st[j].y = ok ? x.y : 0.0f;
         st[j].z = ok ? x.z : 0.0f;

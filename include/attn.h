@@ -97,6 +97,11 @@ extern "C" {
  *                position; its head_dim must be 0 or head_dim). HOST pointer,
  *                read during the call and not kept. It fuses the rope that
  *                precedes attention in a decode graph into the attention call.
+ *   sinks        attention sinks (0 = none; not a catalogue param: the graph
+ *                IR schema carries `sinks` beside `window` on op_attention and
+ *                slot_kv). With a window on, keys s < sinks stay visible beside
+ *                it, as StreamingLLM keeps its initial tokens; causal rows still
+ *                see only s <= pos. Without a window it changes nothing.
  *
  * A query row with no visible key outputs zeros.
  */
@@ -116,6 +121,7 @@ typedef struct attn_params {
     int32_t bias_kind;
     int32_t reserved;
     const struct attn_rope_params* q_rope;
+    int64_t sinks;
 } attn_params;
 
 /* Fill *p with the catalogue's defaults: causal = 1, everything optional

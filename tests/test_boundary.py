@@ -47,7 +47,7 @@ def test_params_init_defaults():
     assert p.causal == 1
     assert (p.T, p.S, p.heads, p.kv_heads, p.head_dim, p.v_head_dim) == (0, 0, 0, 0, 0, 0)
     assert (p.pos_offset, p.window, p.has_scale, p.softcap, p.alibi, p.bias_kind) == (0, 0, 0, 0, 0, 0)
-    assert not p.alibi_slopes
+    assert not p.alibi_slopes and not p.q_rope and p.sinks == 0
 
 
 BASE = dict(heads=8, kvHeads=2, headDim=64)
@@ -61,6 +61,7 @@ BASE = dict(heads=8, kvHeads=2, headDim=64)
     (dict(vHeadDim=-1), 1, "vHeadDim"),
     (dict(posOffset=-1), 1, "posOffset"),
     (dict(window=-1), 1, "window"),
+    (dict(window=4, sinks=-1), 1, "sinks"),
     (dict(softcap=-1.0), 1, "softcap"),
     (dict(softcap=float("inf")), 1, "softcap"),
     (dict(softcap=float("nan")), 1, "softcap"),
@@ -103,6 +104,10 @@ def test_plans():
     assert ga.attn_plan(4, 0, **BASE)["path"] == "zero"
     # Every row's window lies past the keys: nothing visible, zero fill.
     assert ga.attn_plan(2, 4, posOffset=10, window=2, **BASE)["path"] == "zero"
+    # Attention sinks keep keys in view when the window holds none.
+    assert ga.attn_plan(2, 4, posOffset=10, window=2, sinks=1, **BASE)["path"] == "decode"
+    # Sinks without a window change nothing.
+    assert ga.attn_plan(1, 4096, posOffset=4095, sinks=4, **BASE) == ga.attn_plan(1, 4096, posOffset=4095, **BASE)
     # Odd widths have no tuned kernel.
     assert ga.attn_plan(8, 8, heads=4, kvHeads=2, headDim=16)["path"] == "generic"
     assert ga.attn_plan(3, 9, heads=2, headDim=3, vHeadDim=5)["path"] == "generic"
@@ -113,6 +118,19 @@ def test_decode_workspace_matches_plan():
     plan = ga.attn_plan(1, 32768, **kw)
     assert ga.attn_workspace_size(1, 32768, **kw) == 4 * 32 * plan["splits"] * (128 + 2)
     assert ga.attn_workspace_size(8, 8, heads=4, kvHeads=2, headDim=16) == 0
+
+
+def test_decode_sink_split():
+    # Window 4096 of a 32768-row cache plus 4 sinks: the window splits, then
+    # one split of its own for the sink keys below the window.
+    kw = dict(heads=32, kvHeads=8, headDim=128, posOffset=32767, window=4096)
+    plain = ga.attn_plan(1, 32768, **kw)
+    sinks = ga.attn_plan(1, 32768, sinks=4, **kw)
+    assert sinks["splits"] == plain["splits"] + 1
+    assert ga.attn_workspace_size(1, 32768, sinks=4, **kw) == 4 * 32 * sinks["splits"] * (128 + 2)
+    # Sinks the window already covers need no split of their own.
+    near = dict(kw, posOffset=100)
+    assert ga.attn_plan(1, 32768, sinks=4, **near) == ga.attn_plan(1, 32768, **near)
 
 
 def test_options():

@@ -68,6 +68,7 @@ class Workload:
     scale: Optional[float] = None
     softcap: Optional[float] = None
     window: Optional[int] = None
+    sinks: Optional[int] = None
     alibi: Optional[bool] = None
     alibiMax: Optional[float] = None
     alibiSlopes: Optional[tuple] = None
@@ -89,7 +90,7 @@ class Workload:
         """The op parameters as keyword arguments (absent ones omitted)."""
         out = {"heads": self.heads, "headDim": self.headDim}
         for key in ("kvHeads", "vHeadDim", "posOffset", "scale", "softcap",
-                    "window", "alibi", "alibiMax", "alibiSlopes"):
+                    "window", "sinks", "alibi", "alibiMax", "alibiSlopes"):
             val = getattr(self, key)
             if val is not None:
                 out[key] = val
@@ -123,6 +124,10 @@ TINY = Workload("tiny causal prefill T=S=8 H=4 G=2 D=16",
 LLAMA_DECODE = Workload("llama3-8b-shaped GQA decode T=1 S=32768 H=32 G=8 D=128",
                         T=1, S=32768, heads=32, kvHeads=8, headDim=128,
                         posOffset=32767)
+
+LLAMA_STREAMING = Workload("llama3-8b-shaped streaming decode: window 4096 + 4 sinks over S=32768",
+                           T=1, S=32768, heads=32, kvHeads=8, headDim=128, posOffset=32767,
+                           window=4096, sinks=4)
 
 LLAMA_PREFILL = Workload("llama3-8b-shaped causal prefill T=S=4096 H=32 G=8 D=128",
                          T=4096, S=4096, heads=32, kvHeads=8, headDim=128)
