@@ -278,7 +278,10 @@ def run_config(w, args, kv_buffers=1):
     log(f"[bench] workload: {w.name}; plan {plan}")
     main_kernel = {"decode": "decode_split", "prefill": "prefill"}.get(plan["path"], "generic")
     qd = torch.from_numpy(q).to(dev)
-    # Several copies of the K/V (and bias) so a timed call does not find them in the MALL.
+    # Several copies of the K/V (and bias) so a timed call does not find them
+    # in the 256 MB MALL: decode plans rotate over at least 512 MiB of reads.
+    if plan["path"] == "decode":
+        kv_buffers = min(16, max(kv_buffers, -(-(512 << 20) // decode_algorithmic_bytes(w))))
     kv = [tuple(torch.from_numpy(x).to(dev) if x is not None else None for x in (k, v, bias))
           for _ in range(kv_buffers)]
     out = torch.empty((w.T, w.heads * w.Dv), dtype=torch.float32, device=dev)
@@ -327,7 +330,7 @@ def run_config(w, args, kv_buffers=1):
     ok = bool(np.all(err <= 1e-4 + 1e-4 * np.abs(ref)))
     log(f"[bench]   parity on {len(rows)} sampled rows: max |err| {err.max():.3e} ok={ok}")
     rec = {
-        "workload": w.name, "path": plan["path"], "splits": plan["splits"],
+        "workload": w.name, "path": plan["path"], "splits": plan["splits"], "kv_buffers": kv_buffers,
         "value": round(value, 3), "unit": unit, "ms_per_call": round(ms_call, 6), "calls": n,
         ("bytes_per_call" if bound == "hbm" else "flops_per_call"): work,
         "roofline": {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,

@@ -44,7 +44,11 @@ int64_t g_opt_force_path = 0;
 
 constexpr int kCUs = 256;                 // MI355X compute units
 constexpr int kDecodeWgPerCU = 2;         // decode_split occupancy target
-constexpr int64_t kDecodeMinKeys = 256;   // smallest key chunk worth a workgroup
+// Smallest key chunk worth a workgroup. A decode_split workgroup costs ~8 us
+// however few keys it reads (launch, q, two load round trips, merges), so
+// short caches want many small chunks: measured on Llama widths, 4096 keys
+// take 14 us in 32-64 chunks against 19 us in 16.
+constexpr int64_t kDecodeMinKeys = 64;
 constexpr int64_t kDecodeChunkAlign = 64; // key chunk granularity (a multiple of 16 row groups x 2 rows)
 constexpr int64_t kDecodeMaxSplits = 1024;
 constexpr int64_t kPrefillMaxSplits = 16;

@@ -23,8 +23,8 @@
 //
 // decode_combine: grid (T*heads), merges the splits' partial states:
 // M = max m_i, L = sum l_i 2^(m_i - M), out = sum acc_i 2^(m_i - M) / L.
-// combine_few: the same merge for up to 16 splits (prefill key-range parts),
-// one thread per 4 output floats.
+// combine_few: the same merge for up to 16 splits of many rows (prefill
+// key-range parts), one thread per 4 output floats.
 #include "device_common.h"
 #include "rope_device.h"
 
@@ -38,6 +38,7 @@ constexpr int kWaves = kThreads / 64;
 constexpr float kLazy = 8.0f;  // log2 of the largest weight before the reference moves
 constexpr int kMaxSplits = 1024;
 constexpr int kFewSplits = 16;  // up to this many splits, combine_few_kernel merges them
+constexpr int64_t kFewMinOutputs = 65536;  // ... when there are at least this many output float4s
 
 template <int D, int DV, int NQ>
 struct DecodeShape {
@@ -550,8 +551,12 @@ hipError_t launch_decode_split(const Problem& p, const DecodePlan& plan, float* 
 hipError_t launch_decode_combine(const Problem& p, const DecodePlan& plan, const float* ws,
                                  const Launch& L) {
     if (plan.splits < 1 || plan.splits > kMaxSplits) return hipErrorInvalidValue;
-    if (plan.splits <= kFewSplits) {
-        const int64_t n = p.T * p.H * (p.Dv / 4);
+    // combine_few runs one thread per output float4: only worth it with
+    // enough outputs to fill the chip (a prefill's rows). A decode's few
+    // rows take one workgroup per (row, head), which reads its splits in
+    // parallel (16 splits of a Llama-shaped decode: 4.0 us against 6.7 us).
+    const int64_t n = p.T * p.H * (p.Dv / 4);
+    if (plan.splits <= kFewSplits && n >= kFewMinOutputs) {
         const dim3 g((unsigned)((n + kThreads - 1) / kThreads)), b(kThreads);
         switch (p.Dv) {
             case 64: return launch_kernel(combine_few_kernel<64>, g, b, 0, L, p, plan.splits, ws);
