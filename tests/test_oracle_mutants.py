@@ -109,3 +109,43 @@ def test_rope_pins_kill_mutant(name, tmp_path):
         cwd=tree, capture_output=True, text=True, timeout=600)
     assert proc.returncode != 0, f"mutant {name} passed every pin:\n{proc.stdout[-2000:]}"
     assert "failed" in proc.stdout, proc.stdout[-2000:] + proc.stderr[-2000:]
+
+
+# Slips in the latent attention oracle (oracle/mla.py), caught by tests/test_oracle_mla.py.
+MLA_MUTANTS = {
+    # k_b read as if stored [kv_rank, qk_nope] per head
+    "mla_k_b_layout": ("keys[h, :, :N] = c @ k_b[h].astype(np.float64).T",
+                       "keys[h, :, :N] = c @ k_b[h].astype(np.float64).reshape(R, N)"),
+    "mla_rope_part_dropped": ("keys[h, :, N:] = kpe", "keys[h, :, N:] = 0.0"),
+    "mla_head_weights": ("vals[h] = c @ v_b[h].astype(np.float64).T",
+                         "vals[h] = c @ v_b[0].astype(np.float64).T"),
+    "mla_rope_from_latent": ("kpe = state[:, R:R + P].astype(np.float64)",
+                             "kpe = state[:, :P].astype(np.float64)"),
+    "mla_default_scale": ("np.float32(1.0 / math.sqrt(N + P))", "np.float32(1.0 / math.sqrt(N))"),
+    "mla_sink_edge": ("seen = in_window | (s < sinks)", "seen = in_window | (s <= sinks)"),
+    "mla_causal_diagonal": ("seen &= s <= pos", "seen &= s < pos"),
+    "mla_pos_offset_dropped": ('r["P0"] + t, S)', "t, S)"),
+    "mla_q_head_stride": ("qh = q[t, h * (N + P):(h + 1) * (N + P)]", "qh = q[t, h * N:h * N + N + P]"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MLA_MUTANTS))
+def test_mla_pins_kill_mutant(name, tmp_path):
+    old, new = MLA_MUTANTS[name]
+    tree = tmp_path / "tree"
+    tree.mkdir()
+    shutil.copytree(os.path.join(ROOT, "oracle"), tree / "oracle",
+                    ignore=shutil.ignore_patterns("*.so", "__pycache__"))
+    shutil.copytree(os.path.join(ROOT, "tests"), tree / "tests",
+                    ignore=shutil.ignore_patterns("__pycache__", "test_oracle_mutants.py"))
+    shutil.copy(os.path.join(ROOT, "workloads.py"), tree / "workloads.py")
+    path = tree / "oracle" / "mla.py"
+    src = path.read_text()
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    path.write_text(src.replace(old, new))
+    proc = subprocess.run(
+        [sys.executable, "-m", "pytest", "tests/test_oracle_mla.py", "-x", "-q",
+         "-p", "no:cacheprovider"],
+        cwd=tree, capture_output=True, text=True, timeout=600)
+    assert proc.returncode != 0, f"mutant {name} passed every pin:\n{proc.stdout[-2000:]}"
+    assert "failed" in proc.stdout, proc.stdout[-2000:] + proc.stderr[-2000:]

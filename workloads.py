@@ -23,6 +23,7 @@ from typing import Optional
 import numpy as np
 
 STREAM_Q, STREAM_K, STREAM_V, STREAM_BIAS, STREAM_BIAS_MASK = 0, 1, 2, 3, 4
+STREAM_K_B, STREAM_V_B = 5, 6  # latent attention's per-head up-projections
 MASK_VALUE = -1e9
 
 
@@ -117,6 +118,57 @@ class Workload:
         return dataclasses.replace(self, **kw)
 
 
+@dataclasses.dataclass(frozen=True)
+class MlaWorkload:
+    """One latent (MLA) attention call: the IR schema's op_mla_attention
+    properties (heads, kv_rank, qk_nope, qk_rope, v_head_dim, scale, causal,
+    window, sinks) plus posOffset and the tensor shapes.
+
+    Recipe: q [T, heads*(qk_nope+qk_rope)] (stream 0) and the latent state
+    [S, kv_rank+qk_rope] (stream 1) are N(0, 1); the up-projections k_b
+    [heads, qk_nope, kv_rank] (stream 5) and v_b [heads, v_head_dim, kv_rank]
+    (stream 6) are N(0, 1/kv_rank), a random initialisation that keeps the
+    materialized keys and values at unit scale.
+    """
+
+    name: str
+    T: int
+    S: int
+    heads: int
+    kv_rank: int
+    qk_nope: int
+    qk_rope: int
+    v_head_dim: int
+    causal: Optional[bool] = None
+    posOffset: Optional[int] = None
+    scale: Optional[float] = None
+    window: Optional[int] = None
+    sinks: Optional[int] = None
+    seed: int = 0
+
+    def params(self) -> dict:
+        out = {"heads": self.heads, "kv_rank": self.kv_rank, "qk_nope": self.qk_nope,
+               "qk_rope": self.qk_rope, "v_head_dim": self.v_head_dim}
+        for key in ("causal", "posOffset", "scale", "window", "sinks"):
+            val = getattr(self, key)
+            if val is not None:
+                out[key] = val
+        return out
+
+    def tensors(self):
+        """(q, state, k_b, v_b) as float32 host arrays."""
+        H, R, N, P, Dv = self.heads, self.kv_rank, self.qk_nope, self.qk_rope, self.v_head_dim
+        wstd = 1.0 / float(np.sqrt(R))
+        q = normal((self.T, H * (N + P)), self.seed, STREAM_Q)
+        state = normal((self.S, R + P), self.seed, STREAM_K)
+        k_b = normal((H, N, R), self.seed, STREAM_K_B, wstd)
+        v_b = normal((H, Dv, R), self.seed, STREAM_V_B, wstd)
+        return q, state, k_b, v_b
+
+    def replace(self, **kw) -> "MlaWorkload":
+        return dataclasses.replace(self, **kw)
+
+
 # The workloads the measurements and the full-size parity tests use.
 TINY = Workload("tiny causal prefill T=S=8 H=4 G=2 D=16",
                 T=8, S=8, heads=4, kvHeads=2, headDim=16)
@@ -152,3 +204,17 @@ LATENT_NONCAUSAL = Workload("latent-shaped ALiBi+bias non-causal T=S=1024 H=16 D
 
 ALL = (TINY, LLAMA_DECODE, LLAMA_PREFILL, LLAMA_CHUNKED, GEMMA2_SWA,
        LATENT_DECODE, LATENT_NONCAUSAL)
+
+# Latent attention in absorbed form over the same model shape as the
+# latent-shaped decode above (DeepSeek-V2-Lite: 16 heads, kv_rank 512,
+# qk_nope 128, qk_rope 64, v_head_dim 128): a 576-float latent row per key
+# instead of 16 heads x (192 + 128) floats.
+MLA_DECODE = MlaWorkload("deepseek-v2-lite-shaped absorbed MLA decode T=1 S=8192 H=16 kv_rank=512",
+                         T=1, S=8192, heads=16, kv_rank=512, qk_nope=128, qk_rope=64,
+                         v_head_dim=128, posOffset=8191)
+
+# The same at DeepSeek-V3's 128 heads over a 32768-row latent cache: eight
+# 16-head blocks share every latent row, so the matrix cores bound it.
+MLA_DECODE_V3 = MlaWorkload("deepseek-v3-shaped absorbed MLA decode T=1 S=32768 H=128 kv_rank=512",
+                            T=1, S=32768, heads=128, kv_rank=512, qk_nope=128, qk_rope=64,
+                            v_head_dim=128, posOffset=32767)
