@@ -2,7 +2,8 @@
 
 The graph protocol's `attention` op, its KV-cache companion `cache_write`
 and the `rope` op that precedes them (standalone, fused into cache_write and
-fused into attention's q loads), as hand-written HIP kernels behind the C ABI in
+fused into attention's q loads), and latent (MLA) attention in absorbed form,
+as hand-written HIP kernels behind the C ABI in
 include/attn.h (libattn.so). This package is the thin Python binding; it
 has no fallback implementation and raises if the library is not built.
 """
@@ -11,7 +12,9 @@ from .attn import (AttnError, attn_cache_write, attn_forward, attn_last_error, a
                    attn_rope, attn_rope_cache_write, attn_rope_table,
                    prepare_cache_write, prepare_forward, prepare_rope_cache_write,
                    attn_set_option, attn_timing_collect, attn_timing_enable, attn_validate,
-                   attn_workspace_size, make_params, make_rope_params)
+                   attn_workspace_size, make_params, make_rope_params,
+                   attn_mla_forward, attn_mla_plan, attn_mla_validate, attn_mla_workspace_size,
+                   make_mla_params, prepare_mla_forward)
 from ._lib import LIB_PATH, LibraryMissing
 
 __all__ = [
@@ -20,4 +23,6 @@ __all__ = [
     "attn_timing_enable", "attn_validate", "attn_workspace_size", "make_params",
     "prepare_cache_write", "prepare_forward", "attn_rope", "attn_rope_cache_write",
     "attn_rope_table", "make_rope_params", "prepare_rope_cache_write",
+    "attn_mla_forward", "attn_mla_plan", "attn_mla_validate", "attn_mla_workspace_size",
+    "make_mla_params", "prepare_mla_forward",
 ]

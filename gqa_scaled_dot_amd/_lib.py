@@ -13,7 +13,8 @@ ATTN_ALIBI_NONE, ATTN_ALIBI_BLOOM, ATTN_ALIBI_MPT, ATTN_ALIBI_EXPLICIT = 0, 1, 2
 ATTN_ALIBI_MAX_HEADS = 256
 ATTN_BIAS_NONE, ATTN_BIAS_TS, ATTN_BIAS_HTS = 0, 1, 2
 ATTN_PATH_EMPTY, ATTN_PATH_ZERO, ATTN_PATH_GENERIC, ATTN_PATH_DECODE, ATTN_PATH_PREFILL = 0, 1, 2, 3, 4
-PATH_NAMES = {0: "empty", 1: "zero", 2: "generic", 3: "decode", 4: "prefill"}
+ATTN_PATH_MLA = 5
+PATH_NAMES = {0: "empty", 1: "zero", 2: "generic", 3: "decode", 4: "prefill", 5: "mla"}
 (ATTN_ROPE_DEFAULT, ATTN_ROPE_LINEAR, ATTN_ROPE_LLAMA3, ATTN_ROPE_YARN, ATTN_ROPE_LONGROPE,
  ATTN_ROPE_DYNAMIC) = range(6)
 ATTN_ROPE_MAX_ROTARY_DIM = 256
@@ -26,6 +27,8 @@ EXPORTS = (
     "attn_cache_write", "attn_last_error", "attn_plan", "attn_set_option",
     "attn_timing_enable", "attn_timing_collect",
     "attn_rope_params_init", "attn_rope_table", "attn_rope", "attn_rope_cache_write",
+    "attn_mla_params_init", "attn_mla_validate", "attn_mla_workspace_size", "attn_mla_plan",
+    "attn_mla_forward",
 )
 
 
@@ -61,6 +64,17 @@ class AttnParams(ctypes.Structure):
         ("bias_kind", ctypes.c_int32), ("reserved", ctypes.c_int32),
         ("q_rope", ctypes.POINTER(AttnRopeParams)),
         ("sinks", ctypes.c_int64),
+    ]
+
+
+class AttnMlaParams(ctypes.Structure):
+    _fields_ = [
+        ("T", ctypes.c_int64), ("S", ctypes.c_int64),
+        ("heads", ctypes.c_int64), ("kv_rank", ctypes.c_int64), ("qk_nope", ctypes.c_int64),
+        ("qk_rope", ctypes.c_int64), ("v_head_dim", ctypes.c_int64),
+        ("causal", ctypes.c_int32), ("has_scale", ctypes.c_int32),
+        ("scale", ctypes.c_float), ("reserved", ctypes.c_int32),
+        ("pos_offset", ctypes.c_int64), ("window", ctypes.c_int64), ("sinks", ctypes.c_int64),
     ]
 
 
@@ -125,5 +139,16 @@ def lib():
     L.attn_rope_cache_write.argtypes = [vp, ctypes.c_int64, ctypes.c_int64, vp, ctypes.c_int64,
                                         ctypes.c_int64, R, vp]
     L.attn_rope_cache_write.restype = ctypes.c_int
+    M = ctypes.POINTER(AttnMlaParams)
+    L.attn_mla_params_init.argtypes = [M]
+    L.attn_mla_params_init.restype = None
+    L.attn_mla_validate.argtypes = [M]
+    L.attn_mla_validate.restype = ctypes.c_int
+    L.attn_mla_workspace_size.argtypes = [M]
+    L.attn_mla_workspace_size.restype = ctypes.c_size_t
+    L.attn_mla_plan.argtypes = [M, ctypes.POINTER(AttnPlanInfo)]
+    L.attn_mla_plan.restype = ctypes.c_int
+    L.attn_mla_forward.argtypes = [M, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    L.attn_mla_forward.restype = ctypes.c_int
     _lib = L
     return L

@@ -435,3 +435,112 @@ def prepare_rope_cache_write(cache, values, offset: int, rope: dict, *, stream=N
 
     call.held = held
     return call
+
+
+# -- latent (MLA) attention ----------------------------------------------------
+
+def make_mla_params(T: int, S: int, *, heads: int, kv_rank: int, qk_nope: int, qk_rope: int,
+                    v_head_dim: int, scale: Optional[float] = None, causal: Optional[bool] = None,
+                    posOffset: Optional[int] = None, window: Optional[int] = None,
+                    sinks: Optional[int] = None):
+    """attn_mla_params for one call (the IR schema's op_mla_attention names,
+    plus posOffset)."""
+    p = _lib.AttnMlaParams()
+    _lib.lib().attn_mla_params_init(ctypes.byref(p))
+    p.T, p.S = int(T), int(S)
+    p.heads, p.kv_rank, p.qk_nope = int(heads), int(kv_rank), int(qk_nope)
+    p.qk_rope, p.v_head_dim = int(qk_rope), int(v_head_dim)
+    if causal is not None:
+        p.causal = 1 if causal else 0
+    if posOffset is not None:
+        p.pos_offset = int(posOffset)
+    if scale is not None:
+        p.has_scale, p.scale = 1, float(scale)
+    if window is not None:
+        p.window = int(window)
+    if sinks is not None:
+        p.sinks = int(sinks)
+    return p
+
+
+def attn_mla_validate(T: int, S: int, **params) -> None:
+    p = make_mla_params(T, S, **params)
+    _check(_lib.lib().attn_mla_validate(ctypes.byref(p)))
+
+
+def attn_mla_workspace_size(T: int, S: int, **params) -> int:
+    p = make_mla_params(T, S, **params)
+    return int(_lib.lib().attn_mla_workspace_size(ctypes.byref(p)))
+
+
+def attn_mla_plan(T: int, S: int, **params) -> dict:
+    p = make_mla_params(T, S, **params)
+    info = AttnPlanInfo()
+    _check(_lib.lib().attn_mla_plan(ctypes.byref(p), ctypes.byref(info)))
+    return {"path": _lib.PATH_NAMES.get(info.path, str(info.path)), "splits": info.splits,
+            "tile_q": info.tile_q}
+
+
+def _check_mla(q, state, k_b, v_b, out, params):
+    for x, name in ((q, "q"), (state, "state"), (k_b, "k_b"), (v_b, "v_b")):
+        _dev_tensor(x, name)
+    H, R, N = int(params["heads"]), int(params["kv_rank"]), int(params["qk_nope"])
+    P, Dv = int(params["qk_rope"]), int(params["v_head_dim"])
+    if q.dim() != 2 or q.shape[1] != H * (N + P):
+        raise ValueError(f"q: {tuple(q.shape)} is not [T, heads*(qk_nope+qk_rope)] = [T, {H * (N + P)}]")
+    if state.dim() != 2 or state.shape[1] != R + P:
+        raise ValueError(f"state: {tuple(state.shape)} is not [S, kv_rank+qk_rope] = [S, {R + P}]")
+    if tuple(k_b.shape) != (H, N, R):
+        raise ValueError(f"k_b: {tuple(k_b.shape)} is not [heads, qk_nope, kv_rank] = {(H, N, R)}")
+    if tuple(v_b.shape) != (H, Dv, R):
+        raise ValueError(f"v_b: {tuple(v_b.shape)} is not [heads, v_head_dim, kv_rank] = {(H, Dv, R)}")
+    T = q.shape[0]
+    if out is not None:
+        _dev_tensor(out, "out")
+        if tuple(out.shape) != (T, H * Dv):
+            raise ValueError(f"out: {tuple(out.shape)} is not [T, heads*v_head_dim] = [{T}, {H * Dv}]")
+    return T, state.shape[0], H, Dv
+
+
+def _mla_args(q, state, k_b, v_b, out, workspace, stream, params):
+    T, S, H, Dv = _check_mla(q, state, k_b, v_b, out, params)
+    p = make_mla_params(T, S, **params)
+    L = _lib.lib()
+    if out is None:
+        out = _torch().empty((T, H * Dv), dtype=_torch().float32, device=q.device)
+    need = int(L.attn_mla_workspace_size(ctypes.byref(p)))
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = workspace_for(need, q.device)
+    args = (ctypes.byref(p), ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(state.data_ptr()),
+            ctypes.c_void_p(k_b.data_ptr()), ctypes.c_void_p(v_b.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+            ctypes.c_void_p(workspace.data_ptr() if workspace is not None else None),
+            ctypes.c_size_t(workspace.numel() * workspace.element_size() if workspace is not None else 0),
+            _stream_ptr(stream, q.device))
+    return args, (p, q, state, k_b, v_b, out, workspace), out
+
+
+def attn_mla_forward(q, state, k_b, v_b, *, out=None, workspace=None, stream=None, **params):
+    """Latent (MLA) attention: returns out [T, heads*v_head_dim] (float32).
+
+    q [T, heads*(qk_nope+qk_rope)], state [S, kv_rank+qk_rope], k_b [heads,
+    qk_nope, kv_rank] and v_b [heads, v_head_dim, kv_rank] are contiguous
+    float32 GPU tensors."""
+    args, held, out = _mla_args(q, state, k_b, v_b, out, workspace, stream, params)
+    rc = _lib.lib().attn_mla_forward(*args)
+    del held
+    _check(rc)
+    return out
+
+
+def prepare_mla_forward(q, state, k_b, v_b, *, out, workspace=None, stream=None, **params):
+    """Marshal one attn_mla_forward call once; returns a callable repeating it."""
+    args, held, _ = _mla_args(q, state, k_b, v_b, out, workspace, stream, params)
+    fn = _lib.lib().attn_mla_forward
+
+    def call():
+        rc = fn(*args)
+        if rc != _lib.ATTN_OK:
+            raise AttnError(rc, attn_last_error())
+
+    call.held = held
+    return call

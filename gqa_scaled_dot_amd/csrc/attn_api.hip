@@ -41,6 +41,8 @@ int64_t g_opt_decode_depth = 0;
 int64_t g_opt_prefill_splits = 0;
 int64_t g_opt_prefill_variant = 0;
 int64_t g_opt_force_path = 0;
+int64_t g_opt_mla_splits = 0;
+int64_t g_opt_mla_generic = 0;
 
 constexpr int kCUs = 256;                 // MI355X compute units
 constexpr int kDecodeWgPerCU = 2;         // decode_split occupancy target
@@ -54,6 +56,10 @@ constexpr int64_t kDecodeMaxSplits = 1024;
 constexpr int64_t kPrefillMaxSplits = 16;
 constexpr int64_t kPrefillMinTilesPerSplit = 4;
 constexpr int64_t kMaxDim = 1 << 16;
+constexpr int64_t kMlaMaxSplits = 1024;
+constexpr int64_t kMlaMinKeys = 32;       // smallest key chunk worth an MLA split workgroup (two tiles)
+constexpr int64_t kMlaChunkAlign = 16;    // the MLA split kernel's key tile
+constexpr int64_t kMlaGenericMaxFloats = 15000;  // generic MLA kernel: (R + P) + R + 260 floats of LDS
 
 // ---------------------------------------------------------------------------
 // ALiBi slope tables (op `attention`, params alibi / alibiMax / alibiSlopes).
@@ -614,6 +620,128 @@ int rope_rows(const attn_rope_params* r, int64_t rows, int64_t width, attn::Rope
     return rope_resolve(r, r->offset + rows, a);
 }
 
+// ---------------------------------------------------------------------------
+// Latent (MLA) attention (the IR schema's op_mla_attention; read as
+// DeepSeek-V2's multi-head latent attention, evaluated in absorbed form).
+// ---------------------------------------------------------------------------
+struct MlaResolved {
+    int64_t T, S, H, R, N, P, Dv, P0, window, sinks;
+    bool causal;
+    float scale;
+};
+
+int mla_resolve(const attn_mla_params* p, MlaResolved* r) {
+    if (!p) return fail(ATTN_ERR_INVALID, "params: NULL pointer");
+    if (p->T < 0) return fail(ATTN_ERR_INVALID, "T: must be >= 0 (got %lld)", (long long)p->T);
+    if (p->S < 0) return fail(ATTN_ERR_INVALID, "S: must be >= 0 (got %lld)", (long long)p->S);
+    if (p->heads <= 0 || p->heads > kMaxDim)
+        return fail(ATTN_ERR_INVALID, "heads: must be in 1..%lld (got %lld)", (long long)kMaxDim,
+                    (long long)p->heads);
+    if (p->kv_rank <= 0 || p->kv_rank > kMaxDim)
+        return fail(ATTN_ERR_INVALID, "kv_rank: must be in 1..%lld (got %lld)", (long long)kMaxDim,
+                    (long long)p->kv_rank);
+    if (p->qk_nope <= 0 || p->qk_nope > kMaxDim)
+        return fail(ATTN_ERR_INVALID, "qk_nope: must be in 1..%lld (got %lld)", (long long)kMaxDim,
+                    (long long)p->qk_nope);
+    if (p->qk_rope < 0 || p->qk_rope > kMaxDim)
+        return fail(ATTN_ERR_INVALID, "qk_rope: must be in 0..%lld (got %lld)", (long long)kMaxDim,
+                    (long long)p->qk_rope);
+    if (p->v_head_dim <= 0 || p->v_head_dim > kMaxDim)
+        return fail(ATTN_ERR_INVALID, "v_head_dim: must be in 1..%lld (got %lld)", (long long)kMaxDim,
+                    (long long)p->v_head_dim);
+    if (p->pos_offset < 0)
+        return fail(ATTN_ERR_INVALID, "posOffset: must be >= 0 (got %lld)", (long long)p->pos_offset);
+    if (p->window < 0) return fail(ATTN_ERR_INVALID, "window: must be >= 0 (0 = off; got %lld)", (long long)p->window);
+    if (p->sinks < 0) return fail(ATTN_ERR_INVALID, "sinks: must be >= 0 (0 = none; got %lld)", (long long)p->sinks);
+    if (p->has_scale && !isfinite(p->scale)) return fail(ATTN_ERR_INVALID, "scale: must be finite");
+    MlaResolved o;
+    o.T = p->T;
+    o.S = p->S;
+    o.H = p->heads;
+    o.R = p->kv_rank;
+    o.N = p->qk_nope;
+    o.P = p->qk_rope;
+    o.Dv = p->v_head_dim;
+    o.P0 = p->pos_offset;
+    o.causal = p->causal != 0;
+    o.window = p->window;
+    o.sinks = p->window > 0 ? (p->sinks < p->S ? p->sinks : p->S) : 0;
+    o.scale = p->has_scale ? p->scale : (float)(1.0 / sqrt((double)(o.N + o.P)));
+    if (o.S > INT32_MAX) return fail(ATTN_ERR_UNSUPPORTED, "S: more than 2^31-1 key rows");
+    if (o.P0 > INT32_MAX || o.T > INT32_MAX - o.P0)
+        return fail(ATTN_ERR_UNSUPPORTED, "posOffset: positions past 2^31-1");
+    if (o.T * o.H > INT32_MAX / 2) return fail(ATTN_ERR_UNSUPPORTED, "T: too many (row, head) pairs");
+    if (!attn::mla_fast_supported((int)o.R, (int)o.P) && 2 * o.R + o.P > kMlaGenericMaxFloats)
+        return fail(ATTN_ERR_UNSUPPORTED, "kv_rank/qk_rope: no kernel for kv_rank %lld with qk_rope %lld",
+                    (long long)o.R, (long long)o.P);
+    *r = o;
+    return ok();
+}
+
+struct MlaPlanFull {
+    int path;  // ATTN_PATH_EMPTY, _ZERO or _MLA
+    attn::MlaPlan plan;
+    size_t q_abs_bytes;  // workspace: q_abs first, the split partials after it
+    size_t workspace;
+};
+
+size_t align256(size_t n) { return (n + 255) / 256 * 256; }
+
+int mla_make_plan(const MlaResolved& r, MlaPlanFull* out) {
+    memset(out, 0, sizeof *out);
+    out->plan.splits = 1;
+    if (r.T == 0) {
+        out->path = ATTN_PATH_EMPTY;
+        return ok();
+    }
+    // Keys any query row can see: the attention op's rule over positions
+    // P0 .. P0+T-1, and the sink keys below that range.
+    Resolved kq{};
+    kq.T = r.T;
+    kq.S = r.S;
+    kq.P0 = r.P0;
+    kq.causal = r.causal;
+    kq.window = r.window;
+    const attn::KeyRange kr = key_range(kq);
+    const int64_t sink_hi = r.sinks < kr.lo ? r.sinks : kr.lo;
+    if (r.S == 0 || (kr.hi <= kr.lo && sink_hi == 0)) {
+        out->path = ATTN_PATH_ZERO;
+        return ok();
+    }
+    out->path = ATTN_PATH_MLA;
+    attn::MlaPlan& pl = out->plan;
+    pl.fast = attn::mla_fast_supported((int)r.R, (int)r.P) && !g_opt_mla_generic ? 1 : 0;
+    pl.range = kr;
+    const int64_t rows = r.T * r.H;
+    pl.row_blocks = (int32_t)((rows + 15) / 16);
+    const int64_t n = kr.hi > kr.lo ? kr.hi - kr.lo : 0;
+    if (pl.fast) {
+        if (pl.row_blocks > 65535) return fail(ATTN_ERR_UNSUPPORTED, "T: too many rows for the MLA grid");
+        int64_t splits = g_opt_mla_splits;
+        if (splits <= 0) {
+            // Two workgroups per CU over all row blocks, chunks of >= 2 tiles.
+            const int64_t target = ((int64_t)kCUs * 2 + pl.row_blocks - 1) / pl.row_blocks;
+            const int64_t most = (n + kMlaMinKeys - 1) / kMlaMinKeys;
+            splits = target < most ? target : most;
+        }
+        if (splits < 1) splits = 1;
+        if (splits > kMlaMaxSplits - 1) splits = kMlaMaxSplits - 1;
+        int64_t chunk = n > 0 ? (n + splits - 1) / splits : kMlaChunkAlign;
+        chunk = (chunk + kMlaChunkAlign - 1) / kMlaChunkAlign * kMlaChunkAlign;
+        pl.chunk = chunk;
+        pl.sink_hi = (int32_t)sink_hi;
+        pl.splits = (int32_t)((n + chunk - 1) / chunk) + (sink_hi > 0 ? 1 : 0);
+    } else {
+        // One workgroup per row scans every key itself.
+        pl.chunk = 0;
+        pl.sink_hi = 0;
+        pl.splits = 1;
+    }
+    out->q_abs_bytes = align256(sizeof(float) * (size_t)rows * (size_t)(r.R + r.P));
+    out->workspace = out->q_abs_bytes + sizeof(float) * (size_t)rows * (size_t)pl.splits * (size_t)(r.R + 2);
+    return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -837,6 +965,115 @@ int attn_rope_cache_write(float* cache, int64_t max_rows, int64_t width, const f
 
 const char* attn_last_error(void) { return g_last_error.c_str(); }
 
+void attn_mla_params_init(attn_mla_params* p) {
+    if (!p) return;
+    memset(p, 0, sizeof *p);
+    p->causal = 1;
+}
+
+int attn_mla_validate(const attn_mla_params* p) {
+    MlaResolved r;
+    int rc = mla_resolve(p, &r);
+    if (rc) return rc;
+    MlaPlanFull plan;
+    return mla_make_plan(r, &plan);
+}
+
+size_t attn_mla_workspace_size(const attn_mla_params* p) {
+    MlaResolved r;
+    if (mla_resolve(p, &r)) return 0;
+    MlaPlanFull plan;
+    if (mla_make_plan(r, &plan)) return 0;
+    return plan.workspace;
+}
+
+int attn_mla_plan(const attn_mla_params* p, attn_plan_info* info) {
+    if (!info) return fail(ATTN_ERR_INVALID, "info: NULL pointer");
+    MlaResolved r;
+    int rc = mla_resolve(p, &r);
+    if (rc) return rc;
+    MlaPlanFull plan;
+    rc = mla_make_plan(r, &plan);
+    if (rc) return rc;
+    info->path = plan.path;
+    info->splits = plan.path == ATTN_PATH_MLA ? plan.plan.splits : 1;
+    info->tile_q = plan.path == ATTN_PATH_MLA ? (plan.plan.fast ? 16 : 1) : 0;
+    info->reserved = 0;
+    return ok();
+}
+
+int attn_mla_forward(const attn_mla_params* p, const float* q, const float* state, const float* k_b,
+                     const float* v_b, float* out, void* workspace, size_t workspace_bytes, void* stream) {
+    MlaResolved r;
+    int rc = mla_resolve(p, &r);
+    if (rc) return rc;
+    MlaPlanFull plan;
+    rc = mla_make_plan(r, &plan);
+    if (rc) return rc;
+    if (plan.path == ATTN_PATH_EMPTY) return ok();
+
+    const size_t qn = sizeof(float) * (size_t)(r.T * r.H * (r.N + r.P));
+    const size_t sn = sizeof(float) * (size_t)(r.S * (r.R + r.P));
+    const size_t kbn = sizeof(float) * (size_t)(r.H * r.N * r.R);
+    const size_t vbn = sizeof(float) * (size_t)(r.H * r.Dv * r.R);
+    const size_t on = sizeof(float) * (size_t)(r.T * r.H * r.Dv);
+    if (!out) return fail(ATTN_ERR_INVALID, "out: NULL pointer");
+    if (!q || !k_b || !v_b)
+        return fail(ATTN_ERR_INVALID, "%s: NULL pointer", !q ? "q" : !k_b ? "k_b" : "v_b");
+    if (r.S > 0 && !state) return fail(ATTN_ERR_INVALID, "state: NULL pointer");
+    if (!aligned16(q) || !aligned16(state) || !aligned16(k_b) || !aligned16(v_b) || !aligned16(out))
+        return fail(ATTN_ERR_INVALID, "q/state/k_b/v_b/out: pointers must be 16-byte aligned");
+    if (overlaps(out, on, q, qn) || overlaps(out, on, state, sn) || overlaps(out, on, k_b, kbn) ||
+        overlaps(out, on, v_b, vbn))
+        return fail(ATTN_ERR_INVALID, "out: overlaps an input");
+    hipStream_t s = (hipStream_t)stream;
+    if (plan.path == ATTN_PATH_ZERO) {
+        const hipError_t err = timed("zero_fill", s, [&](const attn::Launch& L) {
+            return attn::launch_zero_fill(out, r.T * r.H * r.Dv, L);
+        });
+        if (err != hipSuccess) return fail(ATTN_ERR_DEVICE, "launch: %s", hipGetErrorString(err));
+        return ok();
+    }
+    if (!workspace || workspace_bytes < plan.workspace)
+        return fail(ATTN_ERR_INVALID, "workspace: %zu bytes needed, %zu given", plan.workspace,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (((uintptr_t)workspace & 255u) != 0) return fail(ATTN_ERR_INVALID, "workspace: must be 256-byte aligned");
+    if (overlaps(workspace, plan.workspace, out, on) || overlaps(workspace, plan.workspace, q, qn) ||
+        overlaps(workspace, plan.workspace, state, sn) || overlaps(workspace, plan.workspace, k_b, kbn) ||
+        overlaps(workspace, plan.workspace, v_b, vbn))
+        return fail(ATTN_ERR_INVALID, "workspace: overlaps a tensor");
+
+    attn::MlaProblem prob;
+    prob.q = q;
+    prob.state = state;
+    prob.k_b = k_b;
+    prob.v_b = v_b;
+    prob.out = out;
+    prob.q_abs = (float*)workspace;
+    prob.part = (float*)((char*)workspace + plan.q_abs_bytes);
+    prob.T = r.T;
+    prob.S = r.S;
+    prob.H = (int32_t)r.H;
+    prob.R = (int32_t)r.R;
+    prob.N = (int32_t)r.N;
+    prob.P = (int32_t)r.P;
+    prob.Dv = (int32_t)r.Dv;
+    prob.qk_scale = r.scale * 1.4426950408889634f;
+    prob.vis.causal = r.causal ? 1 : 0;
+    prob.vis.window = (int32_t)(r.window < INT32_MAX ? r.window : INT32_MAX);
+    prob.vis.sinks = (int32_t)r.sinks;
+    prob.vis.pos_offset = (int32_t)r.P0;
+
+    hipError_t err = timed("mla_absorb", s, [&](const attn::Launch& L) { return attn::launch_mla_absorb(prob, L); });
+    if (err == hipSuccess)
+        err = timed("mla_split", s, [&](const attn::Launch& L) { return attn::launch_mla_split(prob, plan.plan, L); });
+    if (err == hipSuccess)
+        err = timed("mla_combine", s,
+                    [&](const attn::Launch& L) { return attn::launch_mla_combine(prob, plan.plan, L); });
+    if (err != hipSuccess) return fail(ATTN_ERR_DEVICE, "launch: %s", hipGetErrorString(err));
+    return ok();
+}
+
 int attn_set_option(const char* name, int64_t value) {
     if (!name) return fail(ATTN_ERR_INVALID, "option: NULL name");
     if (!strcmp(name, "decode_splits")) {
@@ -868,6 +1105,17 @@ int attn_set_option(const char* name, int64_t value) {
             return fail(ATTN_ERR_INVALID, "force_path: must be 0, %d, %d or %d", ATTN_PATH_GENERIC,
                         ATTN_PATH_DECODE, ATTN_PATH_PREFILL);
         g_opt_force_path = value;
+        return ok();
+    }
+    if (!strcmp(name, "mla_splits")) {
+        if (value < 0 || value > kMlaMaxSplits - 1)
+            return fail(ATTN_ERR_INVALID, "mla_splits: must be in 0..%lld", (long long)(kMlaMaxSplits - 1));
+        g_opt_mla_splits = value;
+        return ok();
+    }
+    if (!strcmp(name, "mla_generic")) {
+        if (value != 0 && value != 1) return fail(ATTN_ERR_INVALID, "mla_generic: must be 0 or 1");
+        g_opt_mla_generic = value;
         return ok();
     }
     return fail(ATTN_ERR_INVALID, "option: unknown name '%s'", name);

@@ -15,7 +15,10 @@ constexpr float kLog2e = 1.4426950408889634f;
 // causal keys are visible when pos - window < s <= pos, non-causal keys when
 // |pos - s| <= window; window 0 means no window.
 // Positions are non-negative and below 2^31, so none of this overflows.
-__device__ __forceinline__ bool window_visible(const Epilogue& e, int pos, int s) {
+// E is any struct with the fields causal, window and sinks (Epilogue here,
+// the latent attention's own parameters elsewhere).
+template <typename E>
+__device__ __forceinline__ bool window_visible(const E& e, int pos, int s) {
     if (e.causal) return s <= pos && (e.window == 0 || s > pos - e.window);
     if (e.window == 0) return true;
     return abs(pos - s) <= e.window;
@@ -24,11 +27,13 @@ __device__ __forceinline__ bool window_visible(const Epilogue& e, int pos, int s
 // An attention sink (one of the first e.sinks keys; e.sinks is 0 without a
 // window) stays in view beside the window: non-causal rows always see it,
 // causal rows once it is at or before their position.
-__device__ __forceinline__ bool sink_visible(const Epilogue& e, int pos, int s) {
+template <typename E>
+__device__ __forceinline__ bool sink_visible(const E& e, int pos, int s) {
     return (s < e.sinks) & (!e.causal | (s <= pos));
 }
 
-__device__ __forceinline__ bool key_visible(const Epilogue& e, int pos, int s) {
+template <typename E>
+__device__ __forceinline__ bool key_visible(const E& e, int pos, int s) {
     return window_visible(e, pos, s) | sink_visible(e, pos, s);
 }
 

@@ -88,6 +88,38 @@ inline hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block,
     return hipGetLastError();
 }
 
+// Latent (MLA) attention in absorbed form. Rows are (query row t, head h)
+// pairs, row index t*H + h; the latent state row s is [c_s (R) | k_pe_s (P)].
+struct MlaVis {
+    int32_t causal;
+    int32_t window;      // 0: off
+    int32_t sinks;       // keys s < sinks stay visible beside the window (0 without one)
+    int32_t pos_offset;  // position of query row 0
+};
+
+struct MlaProblem {
+    const float* q;      // [T, H*(N+P)]: per head the no-rope part, then the rotary part
+    const float* state;  // [S, R+P]
+    const float* k_b;    // [H, N, R]
+    const float* v_b;    // [H, Dv, R]
+    float* out;          // [T, H*Dv]
+    float* q_abs;        // workspace [T*H, R+P]: k_b[h]^T q_nope, then q_pe
+    float* part;         // workspace: acc [T*H][splits][R], then (max, sum) [T*H][splits][2]
+    int64_t T, S;
+    int32_t H, R, N, P, Dv;
+    float qk_scale;      // scale * log2(e): scores live in the base-2 domain
+    MlaVis vis;
+};
+
+struct MlaPlan {
+    int32_t fast;        // 1: the MFMA split kernel has an instance for (R, P); 0: the generic one
+    int32_t splits;      // key-range splits (the sink split included)
+    int32_t sink_hi;     // > 0: the last split covers the sink keys [0, sink_hi) below `range`
+    int32_t row_blocks;  // workgroups along the T*H rows (16 rows each)
+    int64_t chunk;       // keys per split of `range` (a multiple of 16)
+    KeyRange range;
+};
+
 // Launchers. Each returns hipSuccess or the launch error.
 hipError_t launch_cache_write(float* dst, const float* src, int64_t count, const Launch& L);
 // out rows = rope(x rows): rows x heads heads of D floats each; out may equal x.
@@ -102,5 +134,9 @@ hipError_t launch_decode_combine(const Problem& p, const DecodePlan& plan, const
 bool prefill_supported(int D, int Dv);
 int prefill_wgs_per_cu(int variant, int D, int Dv);
 hipError_t launch_prefill(const Problem& p, const PrefillPlan& plan, float* ws, const Launch& L);
+bool mla_fast_supported(int R, int P);
+hipError_t launch_mla_absorb(const MlaProblem& p, const Launch& L);
+hipError_t launch_mla_split(const MlaProblem& p, const MlaPlan& plan, const Launch& L);
+hipError_t launch_mla_combine(const MlaProblem& p, const MlaPlan& plan, const Launch& L);
 
 }  // namespace attn

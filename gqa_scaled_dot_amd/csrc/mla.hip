@@ -1,0 +1,480 @@
+// Latent (MLA) attention in absorbed form (the IR schema's op_mla_attention,
+// read as DeepSeek-V2's multi-head latent attention).
+//
+// Head h attends with keys [k_b[h] c_s ; k_pe_s] and values v_b[h] c_s over
+// the latent state rows [c_s | k_pe_s]. Associativity moves the
+// up-projections off the key axis:
+//   q_abs[t,h] = [k_b[h]^T q_nope[t,h] ; q_pe[t,h]]          (mla_absorb)
+//   score(s)   = scale * q_abs[t,h] . state[s]                (mla_split)
+//   o_lat      = softmax-weighted sum of c_s                  (mla_split)
+//   out[t,h]   = v_b[h] o_lat                                 (mla_combine)
+// so each latent row (R + P floats) is read once for every head and query
+// row, instead of heads x (qk_nope + qk_rope + v_head_dim) floats of
+// materialized keys and values.
+//
+// mla_split is a flash-decoding kernel on the matrix cores: all T*H rows
+// share the single latent "KV head", so a workgroup takes 16 rows and a key
+// chunk, stages 16-key tiles of the state in LDS (double-buffered), and its
+// four waves split the channels: for scores wave w contracts R/4 latent
+// channels and P/4 rotary channels (partial scores summed through LDS); for
+// the weighted sum it owns the output channels [w R/4, (w+1) R/4). Scores
+// are formed transposed (S^T = C Q^T with v_mfma_f32_16x16x4f32, keys on the
+// A side), so register r of lane l holds the weight of key 4(l/16) + r for
+// row l%16: exactly the B operand of O^T = C^T P^T, as in the prefill
+// kernels. Partial (max, sum, acc) states of the key splits go to the
+// workspace; mla_combine merges them and applies v_b.
+//
+// Lane layouts of v_mfma_f32_16x16x4f32 (A 16x4, B 4x16, D 16x16, 64 lanes):
+// A[i][k] sits in lane i + 16k, B[k][j] in lane j + 16k, and D[i][j] in lane
+// j + 16*(i/4), register i%4.
+#include "device_common.h"
+
+namespace attn {
+
+namespace {
+
+constexpr int kMlaThreads = 256;
+constexpr int kMlaWaves = 4;
+constexpr int kMlaKT = 16;   // keys per tile
+constexpr int kMlaRB = 16;   // rows per workgroup
+constexpr int kMlaPad = 4;   // LDS row padding (floats): row stride = 4 mod 64 banks
+constexpr float kMlaLazy = 8.0f;
+constexpr int kMlaMaxSplits = 1024;
+
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4v mla_mfma(float a, float b, f32x4v c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+template <int R, int P>
+struct MlaShape {
+    static constexpr int DL = R + P;                            // latent row width
+    static constexpr int LD = DL + kMlaPad;                     // LDS row stride
+    static constexpr int NQ = R / kMlaWaves / 4;                // latent channels per quad of a wave
+    static constexpr int PQ = P / kMlaWaves / 4;                // rotary channels per quad of a wave
+    static constexpr int KQ = NQ + PQ;                          // score k-steps per wave and 16 keys
+    static constexpr int VW = R / kMlaWaves;                    // output channels per wave
+    static constexpr int VG = VW / 64;                          // 64-channel groups per wave
+    static constexpr int NB = VW / 16;                          // output blocks of 16 channels
+    static constexpr int F4 = kMlaKT * DL / 4 / kMlaThreads;    // staging float4s per thread
+    static constexpr size_t lds_bytes =
+        sizeof(float) * (2 * kMlaKT * LD) + sizeof(f32x4v) * kMlaWaves * 64;
+    static_assert(R % 256 == 0 && P % 64 == 0, "R must be a multiple of 256, P of 64");
+    static_assert((kMlaKT * DL / 4) % kMlaThreads == 0, "tile must split evenly over the threads");
+};
+
+// The latent/rotary channel that lane quad q of wave w contracts at score
+// k-step kk: its quarter of the wave's latent channels, then of its rotary ones.
+template <int R, int P>
+__device__ __forceinline__ int score_channel(int w, int q, int kk) {
+    using Sh = MlaShape<R, P>;
+    return kk < Sh::NQ ? w * (R / kMlaWaves) + q * Sh::NQ + kk
+                       : R + w * (P / kMlaWaves) + q * Sh::PQ + (kk - Sh::NQ);
+}
+
+// grid (splits, row_blocks), 256 threads.
+template <int R, int P>
+__global__ __launch_bounds__(kMlaThreads, 2) void mla_split_kernel(MlaProblem p, MlaPlan plan) {
+    using Sh = MlaShape<R, P>;
+    constexpr int DL = Sh::DL, LD = Sh::LD, KQ = Sh::KQ, NB = Sh::NB, VG = Sh::VG, F4 = Sh::F4;
+    extern __shared__ __align__(16) float lds[];
+    float* tiles = lds;                                                        // [2][kMlaKT][LD]
+    f32x4v* s_part = reinterpret_cast<f32x4v*>(lds + 2 * kMlaKT * LD);         // [kMlaWaves][64]
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int quad = lane >> 4;
+    const int col = lane & 15;
+    const int sp = blockIdx.x;
+    const int nrows = (int)p.T * p.H;
+    const int row = blockIdx.y * kMlaRB + col;  // this lane's (t, h) row
+    const bool live = row < nrows;
+    const int pos = p.vis.pos_offset + (live ? row / p.H : 0);
+
+    // This split's keys: a chunk of the window range, or (the last split,
+    // with attention sinks) the sink keys below it.
+    const bool sink_split = plan.sink_hi > 0 && sp == (int)gridDim.x - 1;
+    const int k0 = sink_split ? 0 : (int)(plan.range.lo + (int64_t)sp * plan.chunk);
+    const int k1 = sink_split ? plan.sink_hi : (int)min(plan.range.hi, (int64_t)k0 + plan.chunk);
+    const int ntiles = k1 > k0 ? (k1 - k0 + kMlaKT - 1) / kMlaKT : 0;
+
+    // q_abs of this lane's row, at the channels its quad contracts.
+    float qreg[KQ];
+    {
+        const float* qrow = p.q_abs + (int64_t)(live ? row : 0) * DL;
+#pragma unroll
+        for (int kk = 0; kk < KQ; kk += 4) {
+            const float4 v = *reinterpret_cast<const float4*>(qrow + score_channel<R, P>(wave, quad, kk));
+            qreg[kk] = live ? v.x : 0.0f;
+            qreg[kk + 1] = live ? v.y : 0.0f;
+            qreg[kk + 2] = live ? v.z : 0.0f;
+            qreg[kk + 3] = live ? v.w : 0.0f;
+        }
+    }
+
+    // Global -> registers: 16 state rows from key s0. Rows at or past k1 read
+    // row k1 - 1 (in bounds) and are zeroed; a tile inside [k0, k1) reads
+    // straight from a uniform base with fixed per-lane 32-bit offsets.
+    float4 st[F4];
+    auto fetch = [&](int s0) {
+        if (s0 + kMlaKT <= k1) {
+            const float* tb = p.state + (int64_t)s0 * DL;
+#pragma unroll
+            for (int j = 0; j < F4; ++j) {
+                const uint32_t f = (uint32_t)tid + (uint32_t)j * kMlaThreads;
+                const uint32_t r = f / (DL / 4), c4 = f % (DL / 4);
+                st[j] = *reinterpret_cast<const float4*>(tb + r * (uint32_t)DL + 4u * c4);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < F4; ++j) {
+                const int f = tid + j * kMlaThreads;
+                const int r = f / (DL / 4), c4 = f % (DL / 4);
+                const int s = s0 + r;
+                const bool ok = s < k1;
+                const float4 x =
+                    *reinterpret_cast<const float4*>(p.state + (int64_t)(ok ? s : k1 - 1) * DL + 4 * c4);
+                st[j] = ok ? x : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            }
+        }
+    };
+    auto stage = [&](int buf) {
+        float* t = tiles + buf * kMlaKT * LD;
+#pragma unroll
+        for (int j = 0; j < F4; ++j) {
+            const int f = tid + j * kMlaThreads;
+            const int r = f / (DL / 4), c4 = f % (DL / 4);
+            *reinterpret_cast<float4*>(t + r * LD + 4 * c4) = st[j];
+        }
+    };
+
+    f32x4v o[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) o[b] = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
+    float m = -INFINITY, l = 0.0f;
+
+    if (ntiles > 0) {
+        fetch(k0);
+        stage(0);
+    }
+    for (int n = 0; n < ntiles; ++n) {
+        const int buf = n & 1;
+        const int s0 = k0 + n * kMlaKT;
+        const bool more = n + 1 < ntiles;
+        __syncthreads();  // tile n is in LDS; every wave is done with the other buffer and s_part
+        if (more) fetch(s0 + kMlaKT);
+        const float* tile = tiles + buf * kMlaKT * LD;
+
+        // Partial S^T over this wave's channels: key col of the tile against
+        // this lane's row; three independent accumulator chains.
+        f32x4v sacc[3] = {f32x4v{0.0f, 0.0f, 0.0f, 0.0f}, f32x4v{0.0f, 0.0f, 0.0f, 0.0f},
+                          f32x4v{0.0f, 0.0f, 0.0f, 0.0f}};
+        const float* krow = tile + col * LD;
+#pragma unroll
+        for (int kk = 0; kk < KQ; kk += 4) {
+            const float4 kv = *reinterpret_cast<const float4*>(krow + score_channel<R, P>(wave, quad, kk));
+            f32x4v& acc = sacc[(kk / 4) % 3];
+            acc = mla_mfma(kv.x, qreg[kk], acc);
+            acc = mla_mfma(kv.y, qreg[kk + 1], acc);
+            acc = mla_mfma(kv.z, qreg[kk + 2], acc);
+            acc = mla_mfma(kv.w, qreg[kk + 3], acc);
+        }
+        s_part[wave * 64 + lane] = sacc[0] + sacc[1] + sacc[2];
+        __syncthreads();
+        f32x4v sc = s_part[lane];
+#pragma unroll
+        for (int w = 1; w < kMlaWaves; ++w) sc += s_part[w * 64 + lane];
+
+        // Register r: key s0 + 4*quad + r, row `row`. Mask, then online
+        // softmax in the base-2 domain with a lazily moved maximum.
+        float x[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int s = s0 + 4 * quad + r;
+            const bool vis = live & (s < k1) & key_visible(p.vis, pos, s);
+            x[r] = vis ? sc[r] * p.qk_scale : -INFINITY;
+        }
+        float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        if (mx > m + kMlaLazy) {
+            const float alpha = fast_exp2(m - mx);
+            l *= alpha;
+#pragma unroll
+            for (int b = 0; b < NB; ++b) o[b] *= alpha;
+            m = mx;
+        }
+        const float mu = m == -INFINITY ? 0.0f : m;
+        float pr[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            pr[r] = fast_exp2(x[r] - mu);
+            l += pr[r];
+        }
+
+        // O^T += C^T P^T over this wave's output channels: k-step r takes
+        // keys 4*quad + r; block 4g + u holds channel wave*VW + 64g + 4i + u
+        // for its row i, so the lane reads one float4 per 64-channel group.
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float* vrow = tile + (4 * quad + r) * LD + wave * Sh::VW + 4 * col;
+#pragma unroll
+            for (int g = 0; g < VG; ++g) {
+                const float4 v = *reinterpret_cast<const float4*>(vrow + 64 * g);
+                o[4 * g + 0] = mla_mfma(v.x, pr[r], o[4 * g + 0]);
+                o[4 * g + 1] = mla_mfma(v.y, pr[r], o[4 * g + 1]);
+                o[4 * g + 2] = mla_mfma(v.z, pr[r], o[4 * g + 2]);
+                o[4 * g + 3] = mla_mfma(v.w, pr[r], o[4 * g + 3]);
+            }
+        }
+        if (more) stage(buf ^ 1);
+    }
+
+    // The row's sum over the four quads' keys; every wave holds the same m, l.
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    if (!live) return;
+    const int nsplit = plan.splits;
+    const int64_t slot = (int64_t)row * nsplit + sp;
+    float* acc = p.part + slot * R + wave * Sh::VW;
+    // Lane (col, quad), register rr of block 4g + u: channel 64g + 16*quad + 4*rr + u.
+#pragma unroll
+    for (int g = 0; g < VG; ++g) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            const float4 v = make_float4(o[4 * g][rr], o[4 * g + 1][rr], o[4 * g + 2][rr], o[4 * g + 3][rr]);
+            *reinterpret_cast<float4*>(acc + 64 * g + 16 * quad + 4 * rr) = v;
+        }
+    }
+    if (wave == 0 && quad == 0) {
+        float* ml = p.part + (int64_t)nrows * nsplit * R + slot * 2;
+        ml[0] = m;
+        ml[1] = l;
+    }
+}
+
+// Any (R, P): one workgroup per row, every key checked; two passes (the
+// row's maximum, then weights and the weighted sum of the latent rows 256
+// keys at a time through LDS). Writes the single split's partial state.
+__global__ __launch_bounds__(kMlaThreads) void mla_generic_kernel(MlaProblem p) {
+    extern __shared__ __align__(16) float lds[];
+    const int DL = p.R + p.P;
+    float* qrow = lds;                 // DL
+    float* acc = qrow + DL;            // R
+    float* w = acc + p.R;              // kMlaThreads weights
+    float* red = w + kMlaThreads;      // kMlaWaves partials
+
+    const int tid = threadIdx.x;
+    const int row = blockIdx.x;
+    const int pos = p.vis.pos_offset + row / p.H;
+    for (int c = tid; c < DL; c += kMlaThreads) qrow[c] = p.q_abs[(int64_t)row * DL + c];
+    for (int c = tid; c < p.R; c += kMlaThreads) acc[c] = 0.0f;
+    __syncthreads();
+
+    auto score = [&](int s) {
+        const float* srow = p.state + (int64_t)s * DL;
+        float d = 0.0f;
+        for (int c = 0; c < DL; ++c) d = fmaf(qrow[c], srow[c], d);
+        return d * p.qk_scale;
+    };
+    auto block_reduce = [&](float x, bool is_max) {
+        for (int o = 32; o > 0; o >>= 1) {
+            const float y = __shfl_xor(x, o, 64);
+            x = is_max ? fmaxf(x, y) : x + y;
+        }
+        __syncthreads();
+        if ((tid & 63) == 0) red[tid >> 6] = x;
+        __syncthreads();
+        x = red[0];
+        for (int i = 1; i < kMlaWaves; ++i) x = is_max ? fmaxf(x, red[i]) : x + red[i];
+        return x;
+    };
+
+    float m = -INFINITY;
+    for (int s = tid; s < p.S; s += kMlaThreads)
+        if (key_visible(p.vis, pos, s)) m = fmaxf(m, score(s));
+    m = block_reduce(m, true);
+
+    float l = 0.0f;
+    if (m != -INFINITY) {
+        for (int s0 = 0; s0 < p.S; s0 += kMlaThreads) {
+            const int s = s0 + tid;
+            float wt = 0.0f;
+            if (s < p.S && key_visible(p.vis, pos, s)) wt = fast_exp2(score(s) - m);
+            l += wt;
+            __syncthreads();
+            w[tid] = wt;
+            __syncthreads();
+            const int n = p.S - s0 < kMlaThreads ? (int)(p.S - s0) : kMlaThreads;
+            for (int c = tid; c < p.R; c += kMlaThreads) {
+                float a = acc[c];
+                for (int j = 0; j < n; ++j)
+                    if (w[j] != 0.0f) a = fmaf(w[j], p.state[(int64_t)(s0 + j) * DL + c], a);
+                acc[c] = a;
+            }
+        }
+    }
+    l = block_reduce(l, false);
+    float* out_acc = p.part + (int64_t)row * p.R;
+    for (int c = tid; c < p.R; c += kMlaThreads) out_acc[c] = acc[c];
+    if (tid == 0) {
+        float* ml = p.part + (int64_t)p.T * p.H * p.R + (int64_t)row * 2;
+        ml[0] = m;
+        ml[1] = l;
+    }
+}
+
+// q_abs[t*H + h] = [k_b[h]^T q_nope[t,h] ; q_pe[t,h]].
+// grid (H, ceil(R/64), ceil(T/4)), 256 threads: 64 latent channels (one per
+// lane) of up to 4 query rows; the four waves split the qk_nope contraction
+// and add their partial sums through LDS. k_b rows are read coalesced.
+__global__ __launch_bounds__(kMlaThreads) void mla_absorb_kernel(MlaProblem p) {
+    extern __shared__ __align__(16) float lds[];
+    const int N = p.N, R = p.R, P = p.P, DL = R + P;
+    float* qn = lds;             // [4][N]: the block's q_nope rows
+    float* part = qn + 4 * N;    // [kMlaWaves][4][64]
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int h = blockIdx.x;
+    const int c = blockIdx.y * 64 + lane;
+    const int t0 = blockIdx.z * 4;
+    const int nt = min(4, (int)p.T - t0);
+    const int64_t qstride = (int64_t)p.H * (N + P);
+
+    for (int i = tid; i < 4 * N; i += kMlaThreads) {
+        const int tr = i / N, d = i % N;
+        qn[i] = tr < nt ? p.q[(int64_t)(t0 + tr) * qstride + (int64_t)h * (N + P) + d] : 0.0f;
+    }
+    __syncthreads();
+
+    float a[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (c < R) {
+        const float* kb = p.k_b + (int64_t)h * N * R + c;
+        for (int d = wave; d < N; d += kMlaWaves) {
+            const float x = kb[(int64_t)d * R];
+#pragma unroll
+            for (int tr = 0; tr < 4; ++tr) a[tr] = fmaf(qn[tr * N + d], x, a[tr]);
+        }
+    }
+#pragma unroll
+    for (int tr = 0; tr < 4; ++tr) part[(wave * 4 + tr) * 64 + lane] = a[tr];
+    __syncthreads();
+    // Wave tr writes row tr (fixed summation order over the waves).
+    if (wave < nt && c < R) {
+        float sum = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kMlaWaves; ++w) sum += part[(w * 4 + wave) * 64 + lane];
+        p.q_abs[((int64_t)(t0 + wave) * p.H + h) * DL + c] = sum;
+    }
+    if (blockIdx.y == 0 && wave < nt) {
+        const float* qpe = p.q + (int64_t)(t0 + wave) * qstride + (int64_t)h * (N + P) + N;
+        float* dst = p.q_abs + ((int64_t)(t0 + wave) * p.H + h) * DL + R;
+        for (int e = lane; e < P; e += 64) dst[e] = qpe[e];
+    }
+}
+
+// out[t, h*Dv + e] = v_b[h][e] . o_lat, o_lat the merge of the splits'
+// partial states: M = max m_i, L = sum l_i 2^(m_i - M),
+// o_lat = sum acc_i 2^(m_i - M) / L. A row with no visible key outputs 0.
+// grid (T*H, ceil(Dv/32)), 256 threads; each wave takes 8 output channels.
+__global__ __launch_bounds__(kMlaThreads) void mla_combine_kernel(MlaProblem p, int nsplit) {
+    extern __shared__ __align__(16) float lds[];
+    float* olat = lds;               // R
+    float* wts = olat + p.R;         // nsplit
+    float* red = wts + nsplit;       // kMlaWaves
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int row = blockIdx.x;
+    const int h = row % p.H;
+    const int e0 = blockIdx.y * 32;
+    const int R = p.R;
+    const float* ml = p.part + (int64_t)p.T * p.H * nsplit * R + (int64_t)row * nsplit * 2;
+    const float* acc = p.part + (int64_t)row * nsplit * R;
+    float* orow = p.out + (int64_t)row * p.Dv;
+
+    auto block_reduce = [&](float x, bool is_max) {
+        for (int o = 32; o > 0; o >>= 1) {
+            const float y = __shfl_xor(x, o, 64);
+            x = is_max ? fmaxf(x, y) : x + y;
+        }
+        __syncthreads();
+        if (lane == 0) red[wave] = x;
+        __syncthreads();
+        x = red[0];
+        for (int i = 1; i < kMlaWaves; ++i) x = is_max ? fmaxf(x, red[i]) : x + red[i];
+        return x;
+    };
+
+    float mx = -INFINITY;
+    for (int i = tid; i < nsplit; i += kMlaThreads) mx = fmaxf(mx, ml[2 * i]);
+    const float M = block_reduce(mx, true);
+    if (M == -INFINITY) {  // no visible key in any split
+        if (tid < 32 && e0 + tid < p.Dv) orow[e0 + tid] = 0.0f;
+        return;
+    }
+    float ls = 0.0f;
+    for (int i = tid; i < nsplit; i += kMlaThreads) {
+        const float wi = fast_exp2(ml[2 * i] - M);
+        wts[i] = wi;
+        ls += ml[2 * i + 1] * wi;
+    }
+    const float L = block_reduce(ls, false);  // its barriers also publish wts
+    const float inv = 1.0f / L;
+    for (int c = tid; c < R; c += kMlaThreads) {
+        float a = 0.0f;
+        for (int i = 0; i < nsplit; ++i) a = fmaf(acc[(int64_t)i * R + c], wts[i], a);
+        olat[c] = a * inv;
+    }
+    __syncthreads();
+
+    for (int k = 0; k < 8; ++k) {
+        const int e = e0 + wave * 8 + k;
+        if (e >= p.Dv) break;  // wave-uniform
+        const float* vb = p.v_b + ((int64_t)h * p.Dv + e) * R;
+        float d = 0.0f;
+        for (int c = lane; c < R; c += 64) d = fmaf(vb[c], olat[c], d);
+        for (int o = 32; o > 0; o >>= 1) d += __shfl_xor(d, o, 64);
+        if (lane == 0) orow[e] = d;
+    }
+}
+
+template <int R, int P>
+hipError_t launch_split_rp(const MlaProblem& p, const MlaPlan& plan, const Launch& L) {
+    const dim3 grid((unsigned)plan.splits, (unsigned)plan.row_blocks);
+    return launch_kernel(mla_split_kernel<R, P>, grid, dim3(kMlaThreads), (uint32_t)MlaShape<R, P>::lds_bytes,
+                         L, p, plan);
+}
+
+}  // namespace
+
+bool mla_fast_supported(int R, int P) { return (R == 512 || R == 256) && P == 64; }
+
+hipError_t launch_mla_absorb(const MlaProblem& p, const Launch& L) {
+    const dim3 grid((unsigned)p.H, (unsigned)((p.R + 63) / 64), (unsigned)((p.T + 3) / 4));
+    const size_t lds = sizeof(float) * (4 * (size_t)p.N + kMlaWaves * 4 * 64);
+    return launch_kernel(mla_absorb_kernel, grid, dim3(kMlaThreads), (uint32_t)lds, L, p);
+}
+
+hipError_t launch_mla_split(const MlaProblem& p, const MlaPlan& plan, const Launch& L) {
+    if (plan.splits < 1 || plan.splits > kMlaMaxSplits) return hipErrorInvalidValue;
+    if (plan.fast) {
+        if (p.R == 512 && p.P == 64) return launch_split_rp<512, 64>(p, plan, L);
+        if (p.R == 256 && p.P == 64) return launch_split_rp<256, 64>(p, plan, L);
+        return hipErrorInvalidValue;
+    }
+    if (plan.splits != 1) return hipErrorInvalidValue;
+    const size_t lds = sizeof(float) * ((size_t)p.R + p.P + p.R + kMlaThreads + kMlaWaves);
+    return launch_kernel(mla_generic_kernel, dim3((unsigned)(p.T * p.H)), dim3(kMlaThreads), (uint32_t)lds,
+                         L, p);
+}
+
+hipError_t launch_mla_combine(const MlaProblem& p, const MlaPlan& plan, const Launch& L) {
+    if (plan.splits < 1 || plan.splits > kMlaMaxSplits) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)(p.T * p.H), (unsigned)((p.Dv + 31) / 32));
+    const size_t lds = sizeof(float) * ((size_t)p.R + plan.splits + kMlaWaves);
+    return launch_kernel(mla_combine_kernel, grid, dim3(kMlaThreads), (uint32_t)lds, L, p, plan.splits);
+}
+
+}  // namespace attn

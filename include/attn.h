@@ -298,6 +298,7 @@ const char* attn_last_error(void);
 #define ATTN_PATH_GENERIC 2 /* any shape; correctness path */
 #define ATTN_PATH_DECODE 3  /* few query rows: split-S + combine */
 #define ATTN_PATH_PREFILL 4 /* fp32 MFMA flash kernel */
+#define ATTN_PATH_MLA 5     /* latent attention: absorb, split, combine (attn_mla_plan) */
 typedef struct attn_plan_info {
     int32_t path;
     int32_t splits;
@@ -305,6 +306,81 @@ typedef struct attn_plan_info {
     int32_t reserved;
 } attn_plan_info;
 int attn_plan(const attn_params* p, attn_plan_info* info);
+
+/*
+ * Latent (MLA) attention: the IR schema page's op_mla_attention (properties
+ * state, heads, kv_rank, qk_nope, qk_rope, v_head_dim, k_b, v_b, scale,
+ * causal, window, sinks; the op catalogue names DeepSeek MLA beside
+ * attention's vHeadDim). No page gives its rule; the reading implemented is
+ * DeepSeek-V2's multi-head latent attention: head h attends, exactly as op
+ * `attention` would, with keys [k_b[h] c_s ; k_pe_s] and values v_b[h] c_s,
+ * where state row s is [c_s (kv_rank floats) | k_pe_s (qk_rope floats)].
+ *
+ *   T, S         query rows and latent state rows
+ *   heads, kv_rank, qk_nope, qk_rope, v_head_dim
+ *                as the schema names them (qk_rope may be 0)
+ *   causal       default 1
+ *   has_scale, scale
+ *                scale multiplies q.key; default 1/sqrt(qk_nope + qk_rope)
+ *   pos_offset   position of query row 0 (>= 0); state row s sits at s
+ *   window, sinks
+ *                as attn_params (0 = off / none)
+ */
+typedef struct attn_mla_params {
+    int64_t T, S;
+    int64_t heads, kv_rank, qk_nope, qk_rope, v_head_dim;
+    int32_t causal;
+    int32_t has_scale;
+    float scale;
+    int32_t reserved;
+    int64_t pos_offset;
+    int64_t window;
+    int64_t sinks;
+} attn_mla_params;
+
+/* Defaults: causal = 1, everything else 0 / absent. */
+void attn_mla_params_init(attn_mla_params* p);
+
+/* Check *p without touching any device (ATTN_ERR_INVALID / _UNSUPPORTED name
+ * the field). */
+int attn_mla_validate(const attn_mla_params* p);
+
+/* Bytes of device workspace attn_mla_forward needs (0 for an invalid *p or
+ * when nothing is launched). It holds the absorbed queries and the key
+ * splits' partial softmax states. */
+size_t attn_mla_workspace_size(const attn_mla_params* p);
+
+/* Which kernels attn_mla_forward would launch: path ATTN_PATH_MLA (or EMPTY
+ * / ZERO), splits = key-range splits, tile_q = rows per workgroup (16 on
+ * the matrix-core kernel, 1 on the generic one). */
+int attn_mla_plan(const attn_mla_params* p, attn_plan_info* info);
+
+/*
+ * out[T, heads*v_head_dim] = latent attention, evaluated in absorbed form:
+ * q's no-rope part is multiplied into k_b first, the softmax runs over the
+ * latent rows themselves (each read once for every head), and v_b is
+ * applied to the weighted latent sum.
+ *   q      [T, heads*(qk_nope + qk_rope)]   device, read-only; per head the
+ *                                           no-rope part, then the rotary part
+ *   state  [S, kv_rank + qk_rope]           device, read-only (the latent KV
+ *                                           cache; rows past the visible
+ *                                           range are never read)
+ *   k_b    [heads, qk_nope, kv_rank]        device, read-only
+ *   v_b    [heads, v_head_dim, kv_rank]     device, read-only
+ *   out    [T, heads*v_head_dim]            device, written; must not
+ *                                           overlap any input
+ *   workspace, workspace_bytes
+ *          at least attn_mla_workspace_size(p) bytes, 256-byte aligned, not
+ *          overlapping any tensor; contents need no initialisation. Two
+ *          calls in flight at once must not share a workspace.
+ * All pointers 16-byte aligned. T = 0 is a no-op; rows that see no key
+ * (S = 0, or a window past the state) are 0. Rotary embeddings of q and
+ * k_pe are the caller's (they precede this op, as `rope` precedes
+ * `attention`).
+ */
+int attn_mla_forward(const attn_mla_params* p, const float* q, const float* state, const float* k_b,
+                     const float* v_b, float* out, void* workspace, size_t workspace_bytes,
+                     void* stream);
 
 /*
  * Tuning overrides for tests and sweeps (process-wide, not thread-safe):
@@ -315,6 +391,9 @@ int attn_plan(const attn_params* p, attn_plan_info* info);
  *                    16 (16x16x4 MFMA, 16-row waves); 0 = automatic
  *   "force_path"     force ATTN_PATH_GENERIC / _DECODE / _PREFILL (0 = automatic);
  *                    a forced path that cannot serve *p is refused
+ *   "mla_splits"     force the MLA key-range split count (0 = automatic)
+ *   "mla_generic"    1: run MLA on the generic kernel even where the
+ *                    matrix-core one has an instance (0 = automatic)
  * Returns ATTN_ERR_INVALID for an unknown name.
  */
 int attn_set_option(const char* name, int64_t value);
@@ -329,7 +408,7 @@ int attn_set_option(const char* name, int64_t value);
  * created on the first enable; launches beyond the pool are not timed.
  * Kernel names: "cache_write", "decode_split", "prefill", "combine" (merges
  * key-range splits after either), "generic", "zero_fill", "rope" (attn_rope and
- * attn_rope_cache_write).
+ * attn_rope_cache_write), "mla_absorb", "mla_split", "mla_combine".
  */
 int attn_timing_enable(int on);
 int attn_timing_collect(const char* kernel, double* total_ms, int64_t* launches);

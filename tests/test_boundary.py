@@ -199,3 +199,54 @@ def test_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 64)
     with pytest.raises(ValueError):
         ga.attn_forward(q, q, q, heads=1, headDim=64)
+
+
+MLA = dict(heads=16, kv_rank=512, qk_nope=128, qk_rope=64, v_head_dim=128)
+
+
+@pytest.mark.parametrize("bad, code, word", [
+    (dict(heads=0), 1, "heads"),
+    (dict(kv_rank=0), 1, "kv_rank"),
+    (dict(qk_nope=0), 1, "qk_nope"),
+    (dict(qk_rope=-1), 1, "qk_rope"),
+    (dict(v_head_dim=0), 1, "v_head_dim"),
+    (dict(posOffset=-1), 1, "posOffset"),
+    (dict(window=-2), 1, "window"),
+    (dict(window=4, sinks=-1), 1, "sinks"),
+    (dict(scale=float("inf")), 1, "scale"),
+    (dict(kv_rank=12000, qk_rope=8), 2, "kv_rank"),
+])
+def test_mla_invalid_params_are_named(bad, code, word):
+    kw = dict(MLA)
+    kw.update(bad)
+    with pytest.raises(ga.AttnError) as ei:
+        ga.attn_mla_validate(1, 64, **kw)
+    assert ei.value.code == code
+    assert word in ei.value.message
+
+
+def test_mla_plans_and_workspace():
+    dec = ga.attn_mla_plan(1, 8192, posOffset=8191, **MLA)
+    assert dec["path"] == "mla" and dec["tile_q"] == 16 and dec["splits"] > 1
+    # q_abs (16 rows x 576 floats, 256-byte aligned) then the splits' partial states.
+    want = 16 * 576 * 4 + 16 * dec["splits"] * (512 + 2) * 4
+    assert ga.attn_mla_workspace_size(1, 8192, posOffset=8191, **MLA) == want
+    assert ga.attn_mla_plan(0, 16, **MLA)["path"] == "empty"
+    assert ga.attn_mla_plan(1, 0, **MLA)["path"] == "zero"
+    assert ga.attn_mla_workspace_size(1, 0, **MLA) == 0
+    # Shapes without a matrix-core instance take the generic kernel, one split.
+    gen = ga.attn_mla_plan(2, 50, heads=3, kv_rank=48, qk_nope=8, qk_rope=16, v_head_dim=8)
+    assert gen["path"] == "mla" and gen["tile_q"] == 1 and gen["splits"] == 1
+    # The sink keys below a window take a split of their own.
+    kw = dict(MLA, posOffset=8191, window=1024)
+    assert ga.attn_mla_plan(1, 8192, sinks=4, **kw)["splits"] == ga.attn_mla_plan(1, 8192, **kw)["splits"] + 1
+    try:
+        ga.attn_set_option("mla_splits", 5)
+        assert ga.attn_mla_plan(1, 8192, posOffset=8191, **MLA)["splits"] == 5
+        ga.attn_set_option("mla_generic", 1)
+        assert ga.attn_mla_plan(1, 8192, posOffset=8191, **MLA)["tile_q"] == 1
+    finally:
+        ga.attn_set_option("mla_splits", 0)
+        ga.attn_set_option("mla_generic", 0)
+    with pytest.raises(ga.AttnError):
+        ga.attn_set_option("mla_generic", 2)
