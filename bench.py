@@ -32,6 +32,11 @@ ALiBi + per-head bias decode (S=8192, headDim 192, vHeadDim 128) and
 non-causal prefill (T=S=1024), and the Llama-shaped streaming decode (window
 4096 plus 4 attention sinks over a 32768-row cache).
 
+`mla` holds latent (MLA) attention in absorbed form: the DeepSeek-V2-Lite-
+shaped decode (16 heads, kv_rank 512, S=8192) and a DeepSeek-V3-shaped one
+(128 heads, S=32768): call time, the three kernels' durations, and the
+split kernel's roofline (HBM or fp32 matrix peak, whichever bounds it).
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
        [--prefill-steps K] [--no-configs]
 """
@@ -347,6 +352,125 @@ def run_config(w, args, kv_buffers=1):
     return rec
 
 
+def mla_work(w):
+    """Algorithmic bytes and flops of one latent-attention call and of its
+    split kernel alone. Visible latent rows are read once for all heads; the
+    split kernel reads them and q_abs and writes (m, l, acc) per split (left
+    out: workspace traffic is not algorithmic). Flops: absorbing q
+    (2 H N R per row), scores and weighted sum (2 (R+P) + 2 R per visible
+    (row, key, head)), and v_b (2 H Dv R per row)."""
+    import numpy as np
+    R, P, N, Dv, H, T = w.kv_rank, w.qk_rope, w.qk_nope, w.v_head_dim, w.heads, w.T
+    pos = (w.posOffset or 0) + np.arange(T, dtype=np.int64)
+    causal = True if w.causal is None else w.causal
+    s = np.arange(w.S, dtype=np.int64)
+    pairs = 0
+    rows_seen = np.zeros(w.S, dtype=bool)
+    for p in pos:
+        vis = np.ones(w.S, dtype=bool)
+        if w.window:
+            vis = ((s > p - w.window) if causal else (np.abs(p - s) <= w.window)) | (s < (w.sinks or 0))
+        if causal:
+            vis &= s <= p
+        pairs += int(vis.sum())
+        rows_seen |= vis
+    latent = int(rows_seen.sum()) * (R + P) * 4
+    weights = H * N * R * 4 + H * Dv * R * 4
+    io = T * H * (N + P) * 4 + T * H * Dv * 4
+    split_flops = H * pairs * (2 * (R + P) + 2 * R)
+    flops = split_flops + 2 * T * H * N * R + 2 * T * H * Dv * R
+    return {"bytes": latent + weights + io, "flops": flops,
+            "split_bytes": latent + T * H * (R + P) * 4, "split_flops": split_flops}
+
+
+def run_mla(w, args, n_buffers):
+    """Time attn_mla_forward on one latent workload: the three kernels' durations
+    from dispatch-stamped events, the call time from a plain loop over
+    rotated state copies; the split kernel rated against HBM or the fp32
+    matrix peak, whichever bounds it; sampled heads checked against the oracle."""
+    import numpy as np
+    import torch
+
+    import gqa_scaled_dot_amd as ga
+    from oracle import mla as oracle_mla
+
+    params = w.params()
+    dev = torch.device("cuda:0")
+    q, state, k_b, v_b = w.tensors()
+    plan = ga.attn_mla_plan(w.T, w.S, **params)
+    log(f"[bench] workload: {w.name}; plan {plan}")
+    qd = torch.from_numpy(q).to(dev)
+    sd = torch.from_numpy(state).to(dev)
+    bufs = [(sd if i == 0 else sd.clone(), torch.from_numpy(k_b).to(dev), torch.from_numpy(v_b).to(dev))
+            for i in range(n_buffers)]
+    out = torch.empty((w.T, w.heads * w.v_head_dim), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(ga.attn_mla_workspace_size(w.T, w.S, **params), 256), dtype=torch.uint8, device=dev)
+    calls = [ga.prepare_mla_forward(qd, sb, kb, vb, out=out, workspace=ws, **params) for sb, kb, vb in bufs]
+    n = args.steps
+    for i in range(max(2, args.warmup // 5)):
+        calls[i % n_buffers]()
+    torch.cuda.synchronize()
+    names = ("mla_absorb", "mla_split", "mla_combine")
+    ga.attn_timing_enable(True)
+    for name in names:
+        ga.attn_timing_collect(name)
+    for i in range(n):
+        calls[i % n_buffers]()
+    torch.cuda.synchronize()
+    kern_us = {}
+    for name in names:
+        ms, cnt = ga.attn_timing_collect(name)
+        kern_us[name] = round(ms / max(cnt, 1) * 1e3, 3)
+    ga.attn_timing_enable(False)
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(n):
+        calls[i % n_buffers]()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_call = e0.elapsed_time(e1) / n
+    work = mla_work(w)
+    split_s = kern_us["mla_split"] * 1e-6
+    # The split kernel's bound: its bytes at HBM peak against its flops at the matrix peak.
+    t_hbm = work["split_bytes"] / (HBM_PEAK_GBS * 1e9)
+    t_mfma = work["split_flops"] / (FP32_PEAK_TFLOPS * 1e12)
+    if t_hbm >= t_mfma:
+        roof = {"bound": "hbm", "achieved": round(work["split_bytes"] / split_s / 1e9, 3), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "bytes_per_launch": work["split_bytes"]}
+    else:
+        roof = {"bound": "mfma", "achieved": round(work["split_flops"] / split_s / 1e12, 3),
+                "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s", "flops_per_launch": work["split_flops"]}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = None
+    roof["kernel"] = "mla_split"
+    roof["avg_launch_us"] = kern_us["mla_split"]
+    call_gbs = work["bytes"] / (ms_call * 1e-3) / 1e9
+    call_tf = work["flops"] / (ms_call * 1e-3) / 1e12
+    log(f"[bench]   call {ms_call * 1e3:.1f} us ({call_gbs:.0f} GB/s, {call_tf:.1f} TFLOP/s); kernels {kern_us}; "
+        f"mla_split {roof['achieved']} {roof['unit']} = {roof['frac']:.1%} of {roof['peak']}")
+    got = out.cpu().numpy().astype(np.float64)
+    N, P, Dv = w.qk_nope, w.qk_rope, w.v_head_dim
+    heads = sorted(set([0, w.heads - 1] + [int(x) for x in np.random.default_rng(5).integers(0, w.heads, 4)]))
+    worst = 0.0
+    ok = True
+    for h in heads:
+        qh = np.ascontiguousarray(q[:, h * (N + P):(h + 1) * (N + P)])
+        ref = oracle_mla.mla_attention(qh, state, k_b[h:h + 1], v_b[h:h + 1], **w.replace(heads=1).params())
+        err = np.abs(got[:, h * Dv:(h + 1) * Dv] - ref)
+        worst = max(worst, float(err.max()))
+        ok = ok and bool(np.all(err <= 1e-4 + 1e-4 * np.abs(ref)))
+    log(f"[bench]   parity on heads {heads}: max |err| {worst:.3e} ok={ok}")
+    rec = {"workload": w.name, "path": plan["path"], "splits": plan["splits"], "state_buffers": n_buffers,
+           "value": round(call_gbs, 3), "unit": "GB/s", "ms_per_call": round(ms_call, 6), "calls": n,
+           "bytes_per_call": work["bytes"], "flops_per_call": work["flops"], "tflops": round(call_tf, 3),
+           "kernel_us": kern_us, "roofline": roof,
+           "parity": {"heads": heads, "max_abs_err": worst, "ok": ok}}
+    del bufs, qd, sd, out, ws
+    torch.cuda.empty_cache()
+    return rec
+
+
 ROPE_Q_WORKLOAD = "llama3 rope on a prefill's q [4096, 4096]"
 LLAMA3_ROPE = dict(base=500000.0, scaling=dict(rope_type="llama3", factor=8.0, low_freq_factor=1.0,
                                                high_freq_factor=4.0,
@@ -487,6 +611,9 @@ def main():
                           for w in (workloads.LLAMA_CHUNKED, workloads.GEMMA2_SWA,
                                     workloads.LATENT_DECODE, workloads.LATENT_NONCAUSAL,
                                     workloads.LLAMA_STREAMING)]
+        # Latent attention in absorbed form; state copies rotate over >= 512 MiB of reads.
+        rec["mla"] = [run_mla(w, args, n_buffers=min(16, max(2, -(-(512 << 20) // mla_work(w)["bytes"]))))
+                      for w in (workloads.MLA_DECODE, workloads.MLA_DECODE_V3)]
     print(json.dumps(rec), flush=True)
 
 

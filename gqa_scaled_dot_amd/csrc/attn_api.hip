@@ -57,7 +57,7 @@ constexpr int64_t kPrefillMaxSplits = 16;
 constexpr int64_t kPrefillMinTilesPerSplit = 4;
 constexpr int64_t kMaxDim = 1 << 16;
 constexpr int64_t kMlaMaxSplits = 1024;
-constexpr int64_t kMlaMinKeys = 32;       // smallest key chunk worth an MLA split workgroup (two tiles)
+constexpr int64_t kMlaMinKeys = 64;       // smallest key chunk worth an MLA split workgroup (four tiles)
 constexpr int64_t kMlaChunkAlign = 16;    // the MLA split kernel's key tile
 constexpr int64_t kMlaGenericMaxFloats = 15000;  // generic MLA kernel: (R + P) + R + 260 floats of LDS
 

@@ -326,6 +326,89 @@ __global__ __launch_bounds__(kMlaThreads) void mla_generic_kernel(MlaProblem p) 
     }
 }
 
+// q_abs[t*H + h] = [k_b[h]^T q_nope[t,h] ; q_pe[t,h]], R a multiple of 4.
+// grid (H, ceil(R/64), ceil(T/4)), 256 threads: 64 latent channels (16
+// float4 columns) of up to 4 query rows. Thread (dg, c4) sums the qk_nope
+// rows d = dg, dg + 16, ... of its column with independent 128-bit loads; the
+// 16 groups' partial sums are added through LDS in a fixed order.
+__global__ __launch_bounds__(kMlaThreads) void mla_absorb4_kernel(MlaProblem p) {
+    extern __shared__ __align__(16) float lds[];
+    const int N = p.N, R = p.R, P = p.P, DL = R + P;
+    float* qn = lds;                                            // [4][N]
+    float4* part = reinterpret_cast<float4*>(lds + ((4 * N + 3) & ~3));  // [16][4][16]
+    const int tid = threadIdx.x;
+    const int c4 = tid & 15, dg = tid >> 4;
+    const int h = blockIdx.x;
+    const int c = blockIdx.y * 64 + 4 * c4;
+    const int t0 = blockIdx.z * 4;
+    const int nt = min(4, (int)p.T - t0);
+    const int64_t qstride = (int64_t)p.H * (N + P);
+
+    for (int i = tid; i < 4 * N; i += kMlaThreads) {
+        const int tr = i / N, d = i % N;
+        qn[i] = tr < nt ? p.q[(int64_t)(t0 + tr) * qstride + (int64_t)h * (N + P) + d] : 0.0f;
+    }
+    __syncthreads();
+
+    float4 a[4];
+#pragma unroll
+    for (int tr = 0; tr < 4; ++tr) a[tr] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (c < R) {
+        const float* kb = p.k_b + (int64_t)h * N * R + c;
+        int d = dg;
+        for (; d + 48 < N; d += 64) {
+            float4 x[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) x[u] = *reinterpret_cast<const float4*>(kb + (int64_t)(d + 16 * u) * R);
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+#pragma unroll
+                for (int tr = 0; tr < 4; ++tr) {
+                    const float qv = qn[tr * N + d + 16 * u];
+                    a[tr].x = fmaf(qv, x[u].x, a[tr].x);
+                    a[tr].y = fmaf(qv, x[u].y, a[tr].y);
+                    a[tr].z = fmaf(qv, x[u].z, a[tr].z);
+                    a[tr].w = fmaf(qv, x[u].w, a[tr].w);
+                }
+        }
+        for (; d < N; d += 16) {
+            const float4 x = *reinterpret_cast<const float4*>(kb + (int64_t)d * R);
+#pragma unroll
+            for (int tr = 0; tr < 4; ++tr) {
+                const float qv = qn[tr * N + d];
+                a[tr].x = fmaf(qv, x.x, a[tr].x);
+                a[tr].y = fmaf(qv, x.y, a[tr].y);
+                a[tr].z = fmaf(qv, x.z, a[tr].z);
+                a[tr].w = fmaf(qv, x.w, a[tr].w);
+            }
+        }
+    }
+#pragma unroll
+    for (int tr = 0; tr < 4; ++tr) part[(dg * 4 + tr) * 16 + c4] = a[tr];
+    __syncthreads();
+    // Thread (tr, c4) of the first 64 adds the 16 groups for row tr.
+    if (tid < 64) {
+        const int tr = tid >> 4, cc = tid & 15;
+        const int cw = blockIdx.y * 64 + 4 * cc;
+        if (tr < nt && cw < R) {
+            float4 sum = part[tr * 16 + cc];
+            for (int g = 1; g < 16; ++g) {
+                const float4 v = part[(g * 4 + tr) * 16 + cc];
+                sum.x += v.x; sum.y += v.y; sum.z += v.z; sum.w += v.w;
+            }
+            *reinterpret_cast<float4*>(p.q_abs + ((int64_t)(t0 + tr) * p.H + h) * DL + cw) = sum;
+        }
+    }
+    if (blockIdx.y == 0) {
+        const int tr = tid >> 6, lane = tid & 63;
+        if (tr < nt) {
+            const float* qpe = p.q + (int64_t)(t0 + tr) * qstride + (int64_t)h * (N + P) + N;
+            float* dst = p.q_abs + ((int64_t)(t0 + tr) * p.H + h) * DL + R;
+            for (int e = lane; e < P; e += 64) dst[e] = qpe[e];
+        }
+    }
+}
+
 // q_abs[t*H + h] = [k_b[h]^T q_nope[t,h] ; q_pe[t,h]].
 // grid (H, ceil(R/64), ceil(T/4)), 256 threads: 64 latent channels (one per
 // lane) of up to 4 query rows; the four waves split the qk_nope contraction
@@ -440,6 +523,151 @@ __global__ __launch_bounds__(kMlaThreads) void mla_combine_kernel(MlaProblem p, 
     }
 }
 
+// The same merge and projection for R a multiple of 4 (R/4 <= 256 float4
+// columns), laid out for few rows: 1024 threads per workgroup, and every
+// thread first requests its splits' (max, sum) pairs, its first kBatch
+// accumulator float4s and the v_b rows it will project, so one memory round
+// trip covers nearly all of them. grid (T*H, ceil(Dv/32)). The splits'
+// accumulators are summed by G = 1024 / (R/4) thread groups (split i to
+// group i % G), then added through LDS in a fixed order; each of the 16
+// waves projects 2 output channels.
+constexpr int kCombThreads = 1024;
+constexpr int kCombWaves = kCombThreads / 64;
+constexpr int kCombOut = 32;     // output channels per workgroup
+constexpr int kCombBatch = 8;    // accumulator float4s requested up front per thread
+
+__global__ __launch_bounds__(kCombThreads) void mla_combine4_kernel(MlaProblem p, int nsplit) {
+    extern __shared__ __align__(16) float lds[];
+    const int R = p.R, C4 = R / 4;
+    float4* olat4 = reinterpret_cast<float4*>(lds);             // C4
+    float4* gpart = olat4 + C4;                                   // [G][C4]
+    float* wts = reinterpret_cast<float*>(gpart + kCombThreads);  // nsplit
+    float* red = wts + nsplit;                                    // kCombWaves
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int row = blockIdx.x;
+    const int h = row % p.H;
+    const int e0 = blockIdx.y * kCombOut;
+    const float* ml = p.part + (int64_t)p.T * p.H * nsplit * R + (int64_t)row * nsplit * 2;
+    const float4* acc4 = reinterpret_cast<const float4*>(p.part + (int64_t)row * nsplit * R);
+    float* orow = p.out + (int64_t)row * p.Dv;
+    const int G = kCombThreads / C4;
+    const int gi = tid / C4, c4 = tid % C4;
+    const bool summer = gi < G;
+
+    // Requests first: (max, sum) pairs, accumulators, v_b rows.
+    const float2 mlv = tid < nsplit ? *reinterpret_cast<const float2*>(ml + 2 * tid) : make_float2(-INFINITY, 0.0f);
+    float4 xa[kCombBatch];
+#pragma unroll
+    for (int u = 0; u < kCombBatch; ++u) {
+        const int i = gi + u * G;
+        xa[u] = summer && i < nsplit ? acc4[(int64_t)i * C4 + c4] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
+    constexpr int kVj = 256 / 64;  // float4s of a v_b row per lane (R/4 <= 256)
+    float4 vb[2][kVj];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int e = e0 + 2 * wave + k;
+#pragma unroll
+        for (int j = 0; j < kVj; ++j) {
+            const int c = lane + 64 * j;
+            vb[k][j] = e < p.Dv && c < C4
+                           ? *reinterpret_cast<const float4*>(p.v_b + ((int64_t)h * p.Dv + e) * R + 4 * c)
+                           : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        }
+    }
+
+    auto block_reduce = [&](float x, bool is_max) {
+        for (int o = 32; o > 0; o >>= 1) {
+            const float y = __shfl_xor(x, o, 64);
+            x = is_max ? fmaxf(x, y) : x + y;
+        }
+        __syncthreads();
+        if (lane == 0) red[wave] = x;
+        __syncthreads();
+        x = red[0];
+        for (int i = 1; i < kCombWaves; ++i) x = is_max ? fmaxf(x, red[i]) : x + red[i];
+        return x;
+    };
+
+    // nsplit <= 1024: one pair per thread.
+    const float M = block_reduce(mlv.x, true);
+    if (M == -INFINITY) {  // no visible key in any split
+        if (tid < kCombOut && e0 + tid < p.Dv) orow[e0 + tid] = 0.0f;
+        return;
+    }
+    float ls = 0.0f;
+    if (tid < nsplit) {
+        const float wi = fast_exp2(mlv.x - M);
+        wts[tid] = wi;
+        ls = mlv.y * wi;
+    }
+    const float L = block_reduce(ls, false);  // its barriers also publish wts
+    const float inv = 1.0f / L;
+
+    if (summer) {
+        float4 a = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+        for (int u = 0; u < kCombBatch; ++u) {
+            const int i = gi + u * G;
+            const float wv = i < nsplit ? wts[i] : 0.0f;
+            a.x = fmaf(xa[u].x, wv, a.x);
+            a.y = fmaf(xa[u].y, wv, a.y);
+            a.z = fmaf(xa[u].z, wv, a.z);
+            a.w = fmaf(xa[u].w, wv, a.w);
+        }
+        // Further splits, kCombBatch at a time.
+        for (int i0 = gi + kCombBatch * G; i0 < nsplit; i0 += kCombBatch * G) {
+#pragma unroll
+            for (int u = 0; u < kCombBatch; ++u) {
+                const int i = i0 + u * G;
+                xa[u] = i < nsplit ? acc4[(int64_t)i * C4 + c4] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            }
+#pragma unroll
+            for (int u = 0; u < kCombBatch; ++u) {
+                const int i = i0 + u * G;
+                const float wv = i < nsplit ? wts[i] : 0.0f;
+                a.x = fmaf(xa[u].x, wv, a.x);
+                a.y = fmaf(xa[u].y, wv, a.y);
+                a.z = fmaf(xa[u].z, wv, a.z);
+                a.w = fmaf(xa[u].w, wv, a.w);
+            }
+        }
+        gpart[gi * C4 + c4] = a;
+    }
+    __syncthreads();
+    for (int c = tid; c < C4; c += kCombThreads) {
+        float4 sum = gpart[c];
+        for (int g = 1; g < G; ++g) {
+            const float4 v = gpart[g * C4 + c];
+            sum.x += v.x; sum.y += v.y; sum.z += v.z; sum.w += v.w;
+        }
+        olat4[c] = make_float4(sum.x * inv, sum.y * inv, sum.z * inv, sum.w * inv);
+    }
+    __syncthreads();
+
+    // Wave w projects channels e0 + 2w and e0 + 2w + 1: lanes stride the
+    // latent channels in float4s, then the wave adds them up.
+    float d[2] = {0.0f, 0.0f};
+#pragma unroll
+    for (int j = 0; j < kVj; ++j) {
+        const int c = lane + 64 * j;
+        if (c < C4) {
+            const float4 o = olat4[c];
+#pragma unroll
+            for (int k = 0; k < 2; ++k)
+                d[k] = fmaf(vb[k][j].x, o.x, fmaf(vb[k][j].y, o.y, fmaf(vb[k][j].z, o.z, fmaf(vb[k][j].w, o.w, d[k]))));
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        float x = d[k];
+        for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+        const int e = e0 + 2 * wave + k;
+        if (lane == 0 && e < p.Dv) orow[e] = x;
+    }
+}
+
 template <int R, int P>
 hipError_t launch_split_rp(const MlaProblem& p, const MlaPlan& plan, const Launch& L) {
     const dim3 grid((unsigned)plan.splits, (unsigned)plan.row_blocks);
@@ -453,6 +681,10 @@ bool mla_fast_supported(int R, int P) { return (R == 512 || R == 256) && P == 64
 
 hipError_t launch_mla_absorb(const MlaProblem& p, const Launch& L) {
     const dim3 grid((unsigned)p.H, (unsigned)((p.R + 63) / 64), (unsigned)((p.T + 3) / 4));
+    if (p.R % 4 == 0) {
+        const size_t lds = sizeof(float) * (size_t)((4 * p.N + 3) & ~3) + sizeof(float4) * 16 * 4 * 16;
+        return launch_kernel(mla_absorb4_kernel, grid, dim3(kMlaThreads), (uint32_t)lds, L, p);
+    }
     const size_t lds = sizeof(float) * (4 * (size_t)p.N + kMlaWaves * 4 * 64);
     return launch_kernel(mla_absorb_kernel, grid, dim3(kMlaThreads), (uint32_t)lds, L, p);
 }
@@ -472,6 +704,11 @@ hipError_t launch_mla_split(const MlaProblem& p, const MlaPlan& plan, const Laun
 
 hipError_t launch_mla_combine(const MlaProblem& p, const MlaPlan& plan, const Launch& L) {
     if (plan.splits < 1 || plan.splits > kMlaMaxSplits) return hipErrorInvalidValue;
+    if (p.R % 4 == 0 && p.R / 4 <= 256) {
+        const dim3 grid((unsigned)(p.T * p.H), (unsigned)((p.Dv + kCombOut - 1) / kCombOut));
+        const size_t lds = sizeof(float4) * ((size_t)p.R / 4 + kCombThreads) + sizeof(float) * (plan.splits + kCombWaves);
+        return launch_kernel(mla_combine4_kernel, grid, dim3(kCombThreads), (uint32_t)lds, L, p, plan.splits);
+    }
     const dim3 grid((unsigned)(p.T * p.H), (unsigned)((p.Dv + 31) / 32));
     const size_t lds = sizeof(float) * ((size_t)p.R + plan.splits + kMlaWaves);
     return launch_kernel(mla_combine_kernel, grid, dim3(kMlaThreads), (uint32_t)lds, L, p, plan.splits);
