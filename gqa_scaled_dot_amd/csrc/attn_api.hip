@@ -43,6 +43,7 @@ int64_t g_opt_prefill_variant = 0;
 int64_t g_opt_force_path = 0;
 int64_t g_opt_mla_splits = 0;
 int64_t g_opt_mla_generic = 0;
+int64_t g_opt_mla_row_groups = 0;
 
 constexpr int kCUs = 256;                 // MI355X compute units
 constexpr int kDecodeWgPerCU = 2;         // decode_split occupancy target
@@ -714,13 +715,18 @@ int mla_make_plan(const MlaResolved& r, MlaPlanFull* out) {
     pl.range = kr;
     const int64_t rows = r.T * r.H;
     pl.row_blocks = (int32_t)((rows + 15) / 16);
+    // Two row blocks share each workgroup's key tiles when there are enough
+    // blocks to keep the chip busy (one such workgroup fills a CU's LDS).
+    pl.row_groups = g_opt_mla_row_groups ? (int32_t)g_opt_mla_row_groups : (pl.row_blocks >= 4 ? 2 : 1);
     const int64_t n = kr.hi > kr.lo ? kr.hi - kr.lo : 0;
     if (pl.fast) {
         if (pl.row_blocks > 65535) return fail(ATTN_ERR_UNSUPPORTED, "T: too many rows for the MLA grid");
         int64_t splits = g_opt_mla_splits;
         if (splits <= 0) {
-            // Two workgroups per CU over all row blocks, chunks of >= 2 tiles.
-            const int64_t target = ((int64_t)kCUs * 2 + pl.row_blocks - 1) / pl.row_blocks;
+            // Two workgroups per CU over all row blocks (one of two row
+            // groups), chunks of >= 64 keys.
+            const int64_t wg_rows = (pl.row_blocks + pl.row_groups - 1) / pl.row_groups;
+            const int64_t target = ((int64_t)kCUs * (3 - pl.row_groups) + wg_rows - 1) / wg_rows;
             const int64_t most = (n + kMlaMinKeys - 1) / kMlaMinKeys;
             splits = target < most ? target : most;
         }
@@ -1111,6 +1117,11 @@ int attn_set_option(const char* name, int64_t value) {
         if (value < 0 || value > kMlaMaxSplits - 1)
             return fail(ATTN_ERR_INVALID, "mla_splits: must be in 0..%lld", (long long)(kMlaMaxSplits - 1));
         g_opt_mla_splits = value;
+        return ok();
+    }
+    if (!strcmp(name, "mla_row_groups")) {
+        if (value < 0 || value > 2) return fail(ATTN_ERR_INVALID, "mla_row_groups: must be 0, 1 or 2");
+        g_opt_mla_row_groups = value;
         return ok();
     }
     if (!strcmp(name, "mla_generic")) {

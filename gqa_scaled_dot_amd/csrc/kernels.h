@@ -115,7 +115,8 @@ struct MlaPlan {
     int32_t fast;        // 1: the MFMA split kernel has an instance for (R, P); 0: the generic one
     int32_t splits;      // key-range splits (the sink split included)
     int32_t sink_hi;     // > 0: the last split covers the sink keys [0, sink_hi) below `range`
-    int32_t row_blocks;  // workgroups along the T*H rows (16 rows each)
+    int32_t row_blocks;  // 16-row blocks along the T*H rows
+    int32_t row_groups;  // 16-row blocks per workgroup of the split kernel (1 or 2)
     int64_t chunk;       // keys per split of `range` (a multiple of 16)
     KeyRange range;
 };

@@ -13,9 +13,9 @@
 // materialized keys and values.
 //
 // mla_split is a flash-decoding kernel on the matrix cores: all T*H rows
-// share the single latent "KV head", so a workgroup takes 16 rows and a key
-// chunk, stages 16-key tiles of the state in LDS (double-buffered), and its
-// four waves split the channels: for scores wave w contracts R/4 latent
+// share the single latent "KV head", so a workgroup takes one or two groups
+// of 16 rows and a key chunk, stages 16- or 32-key tiles of the state in LDS
+// (double-buffered), and the four waves of a row group split the channels: for scores wave w contracts R/4 latent
 // channels and P/4 rotary channels (partial scores summed through LDS); for
 // the weighted sum it owns the output channels [w R/4, (w+1) R/4). Scores
 // are formed transposed (S^T = C Q^T with v_mfma_f32_16x16x4f32, keys on the
@@ -37,7 +37,6 @@ constexpr int kMlaThreads = 256;
 constexpr int kMlaWaves = 4;
 constexpr int kMlaKT = 16;   // keys per tile
 constexpr int kMlaRB = 16;   // rows per workgroup
-constexpr int kMlaPad = 4;   // LDS row padding (floats): row stride = 4 mod 64 banks
 constexpr float kMlaLazy = 8.0f;
 constexpr int kMlaMaxSplits = 1024;
 
@@ -47,49 +46,68 @@ __device__ __forceinline__ f32x4v mla_mfma(float a, float b, f32x4v c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-template <int R, int P>
+// RG row groups of 16 rows share a workgroup (4 waves per group) and every
+// key tile, which holds 16 * RG keys: with many rows (the 128-head shape)
+// each staged tile then feeds twice the matrix work, and each barrier and
+// tile load is paid half as often per instruction.
+template <int R, int P, int RG>
 struct MlaShape {
     static constexpr int DL = R + P;                            // latent row width
-    static constexpr int LD = DL + kMlaPad;                     // LDS row stride
+    static constexpr int NT = kMlaThreads * RG;                 // threads
+    static constexpr int KT = kMlaKT * RG;                      // keys per tile
+    static constexpr int NKB = KT / 16;                         // 16-key blocks per tile
     static constexpr int NQ = R / kMlaWaves / 4;                // latent channels per quad of a wave
     static constexpr int PQ = P / kMlaWaves / 4;                // rotary channels per quad of a wave
     static constexpr int KQ = NQ + PQ;                          // score k-steps per wave and 16 keys
     static constexpr int VW = R / kMlaWaves;                    // output channels per wave
     static constexpr int VG = VW / 64;                          // 64-channel groups per wave
     static constexpr int NB = VW / 16;                          // output blocks of 16 channels
-    static constexpr int F4 = kMlaKT * DL / 4 / kMlaThreads;    // staging float4s per thread
+    static constexpr int F4 = KT * DL / 4 / NT;                 // staging float4s per thread
     static constexpr size_t lds_bytes =
-        sizeof(float) * (2 * kMlaKT * LD) + sizeof(f32x4v) * kMlaWaves * 64;
+        sizeof(float) * (2 * KT * DL) + sizeof(f32x4v) * kMlaWaves * RG * NKB * 64;
     static_assert(R % 256 == 0 && P % 64 == 0, "R must be a multiple of 256, P of 64");
-    static_assert((kMlaKT * DL / 4) % kMlaThreads == 0, "tile must split evenly over the threads");
+    static_assert(DL % 64 == 0, "rows must be whole 16-float4 bank groups for the swizzle");
+    static_assert((KT * DL / 4) % NT == 0, "tile must split evenly over the threads");
+    static_assert(lds_bytes <= 160 * 1024, "LDS");
 };
+
+// LDS tiles hold state rows unpadded (DL floats) with the float4 column c4 of
+// row r stored at c4 ^ (r & 15): the 16 rows a score read touches at one
+// column, and the 16 columns a weighted-sum read touches in one row, each
+// fall on 16 different float4 bank groups (64 banks x 4 bytes = 16 float4s).
+template <int DL>
+__device__ __forceinline__ const float* tile_at(const float* tile, int r, int c4) {
+    return tile + r * DL + 4 * (c4 ^ (r & 15));
+}
 
 // The latent/rotary channel that lane quad q of wave w contracts at score
 // k-step kk: its quarter of the wave's latent channels, then of its rotary ones.
 template <int R, int P>
 __device__ __forceinline__ int score_channel(int w, int q, int kk) {
-    using Sh = MlaShape<R, P>;
-    return kk < Sh::NQ ? w * (R / kMlaWaves) + q * Sh::NQ + kk
-                       : R + w * (P / kMlaWaves) + q * Sh::PQ + (kk - Sh::NQ);
+    constexpr int NQ = R / kMlaWaves / 4, PQ = P / kMlaWaves / 4;
+    return kk < NQ ? w * (R / kMlaWaves) + q * NQ + kk : R + w * (P / kMlaWaves) + q * PQ + (kk - NQ);
 }
 
-// grid (splits, row_blocks), 256 threads.
-template <int R, int P>
-__global__ __launch_bounds__(kMlaThreads, 2) void mla_split_kernel(MlaProblem p, MlaPlan plan) {
-    using Sh = MlaShape<R, P>;
-    constexpr int DL = Sh::DL, LD = Sh::LD, KQ = Sh::KQ, NB = Sh::NB, VG = Sh::VG, F4 = Sh::F4;
+// grid (splits, ceil(row_blocks / RG)), 256 * RG threads.
+template <int R, int P, int RG>
+__global__ __launch_bounds__(kMlaThreads * RG, 2 / RG) void mla_split_kernel(MlaProblem p, MlaPlan plan) {
+    using Sh = MlaShape<R, P, RG>;
+    constexpr int DL = Sh::DL, KQ = Sh::KQ, NB = Sh::NB, VG = Sh::VG, F4 = Sh::F4;
+    constexpr int NT = Sh::NT, KT = Sh::KT, NKB = Sh::NKB;
     extern __shared__ __align__(16) float lds[];
-    float* tiles = lds;                                                        // [2][kMlaKT][LD]
-    f32x4v* s_part = reinterpret_cast<f32x4v*>(lds + 2 * kMlaKT * LD);         // [kMlaWaves][64]
+    float* tiles = lds;                                                // [2][KT][DL], swizzled
+    f32x4v* s_part = reinterpret_cast<f32x4v*>(lds + 2 * KT * DL);     // [RG*4 waves][NKB][64]
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
+    const int grp = wave / kMlaWaves;   // row group
+    const int wv = wave % kMlaWaves;    // the wave's channel quarter
     const int lane = tid & 63;
     const int quad = lane >> 4;
     const int col = lane & 15;
     const int sp = blockIdx.x;
     const int nrows = (int)p.T * p.H;
-    const int row = blockIdx.y * kMlaRB + col;  // this lane's (t, h) row
+    const int row = (blockIdx.y * RG + grp) * kMlaRB + col;  // this lane's (t, h) row
     const bool live = row < nrows;
     const int pos = p.vis.pos_offset + (live ? row / p.H : 0);
 
@@ -98,7 +116,7 @@ __global__ __launch_bounds__(kMlaThreads, 2) void mla_split_kernel(MlaProblem p,
     const bool sink_split = plan.sink_hi > 0 && sp == (int)gridDim.x - 1;
     const int k0 = sink_split ? 0 : (int)(plan.range.lo + (int64_t)sp * plan.chunk);
     const int k1 = sink_split ? plan.sink_hi : (int)min(plan.range.hi, (int64_t)k0 + plan.chunk);
-    const int ntiles = k1 > k0 ? (k1 - k0 + kMlaKT - 1) / kMlaKT : 0;
+    const int ntiles = k1 > k0 ? (k1 - k0 + KT - 1) / KT : 0;
 
     // q_abs of this lane's row, at the channels its quad contracts.
     float qreg[KQ];
@@ -106,7 +124,7 @@ __global__ __launch_bounds__(kMlaThreads, 2) void mla_split_kernel(MlaProblem p,
         const float* qrow = p.q_abs + (int64_t)(live ? row : 0) * DL;
 #pragma unroll
         for (int kk = 0; kk < KQ; kk += 4) {
-            const float4 v = *reinterpret_cast<const float4*>(qrow + score_channel<R, P>(wave, quad, kk));
+            const float4 v = *reinterpret_cast<const float4*>(qrow + score_channel<R, P>(wv, quad, kk));
             qreg[kk] = live ? v.x : 0.0f;
             qreg[kk + 1] = live ? v.y : 0.0f;
             qreg[kk + 2] = live ? v.z : 0.0f;
@@ -114,23 +132,23 @@ __global__ __launch_bounds__(kMlaThreads, 2) void mla_split_kernel(MlaProblem p,
         }
     }
 
-    // Global -> registers: 16 state rows from key s0. Rows at or past k1 read
+    // Global -> registers: KT state rows from key s0. Rows at or past k1 read
     // row k1 - 1 (in bounds) and are zeroed; a tile inside [k0, k1) reads
     // straight from a uniform base with fixed per-lane 32-bit offsets.
     float4 st[F4];
     auto fetch = [&](int s0) {
-        if (s0 + kMlaKT <= k1) {
+        if (s0 + KT <= k1) {
             const float* tb = p.state + (int64_t)s0 * DL;
 #pragma unroll
             for (int j = 0; j < F4; ++j) {
-                const uint32_t f = (uint32_t)tid + (uint32_t)j * kMlaThreads;
+                const uint32_t f = (uint32_t)tid + (uint32_t)j * NT;
                 const uint32_t r = f / (DL / 4), c4 = f % (DL / 4);
                 st[j] = *reinterpret_cast<const float4*>(tb + r * (uint32_t)DL + 4u * c4);
             }
         } else {
 #pragma unroll
             for (int j = 0; j < F4; ++j) {
-                const int f = tid + j * kMlaThreads;
+                const int f = tid + j * NT;
                 const int r = f / (DL / 4), c4 = f % (DL / 4);
                 const int s = s0 + r;
                 const bool ok = s < k1;
@@ -141,12 +159,12 @@ __global__ __launch_bounds__(kMlaThreads, 2) void mla_split_kernel(MlaProblem p,
         }
     };
     auto stage = [&](int buf) {
-        float* t = tiles + buf * kMlaKT * LD;
+        float* t = tiles + buf * KT * DL;
 #pragma unroll
         for (int j = 0; j < F4; ++j) {
-            const int f = tid + j * kMlaThreads;
+            const int f = tid + j * NT;
             const int r = f / (DL / 4), c4 = f % (DL / 4);
-            *reinterpret_cast<float4*>(t + r * LD + 4 * c4) = st[j];
+            *reinterpret_cast<float4*>(t + r * DL + 4 * (c4 ^ (r & 15))) = st[j];
         }
     };
 
@@ -161,42 +179,54 @@ __global__ __launch_bounds__(kMlaThreads, 2) void mla_split_kernel(MlaProblem p,
     }
     for (int n = 0; n < ntiles; ++n) {
         const int buf = n & 1;
-        const int s0 = k0 + n * kMlaKT;
+        const int s0 = k0 + n * KT;
         const bool more = n + 1 < ntiles;
         __syncthreads();  // tile n is in LDS; every wave is done with the other buffer and s_part
-        if (more) fetch(s0 + kMlaKT);
-        const float* tile = tiles + buf * kMlaKT * LD;
+        if (more) fetch(s0 + KT);
+        const float* tile = tiles + buf * KT * DL;
 
-        // Partial S^T over this wave's channels: key col of the tile against
-        // this lane's row; three independent accumulator chains.
-        f32x4v sacc[3] = {f32x4v{0.0f, 0.0f, 0.0f, 0.0f}, f32x4v{0.0f, 0.0f, 0.0f, 0.0f},
-                          f32x4v{0.0f, 0.0f, 0.0f, 0.0f}};
-        const float* krow = tile + col * LD;
+        // Partial S^T over this wave's channels, per 16-key block kb: key
+        // 16kb + col of the tile against this lane's row.
 #pragma unroll
-        for (int kk = 0; kk < KQ; kk += 4) {
-            const float4 kv = *reinterpret_cast<const float4*>(krow + score_channel<R, P>(wave, quad, kk));
-            f32x4v& acc = sacc[(kk / 4) % 3];
-            acc = mla_mfma(kv.x, qreg[kk], acc);
-            acc = mla_mfma(kv.y, qreg[kk + 1], acc);
-            acc = mla_mfma(kv.z, qreg[kk + 2], acc);
-            acc = mla_mfma(kv.w, qreg[kk + 3], acc);
+        for (int kb = 0; kb < NKB; ++kb) {
+            f32x4v sacc[3] = {f32x4v{0.0f, 0.0f, 0.0f, 0.0f}, f32x4v{0.0f, 0.0f, 0.0f, 0.0f},
+                              f32x4v{0.0f, 0.0f, 0.0f, 0.0f}};
+            const int kr = 16 * kb + col;
+#pragma unroll
+            for (int kk = 0; kk < KQ; kk += 4) {
+                const float4 kv = *reinterpret_cast<const float4*>(
+                    tile_at<DL>(tile, kr, score_channel<R, P>(wv, quad, kk) / 4));
+                f32x4v& acc = sacc[(kk / 4) % 3];
+                acc = mla_mfma(kv.x, qreg[kk], acc);
+                acc = mla_mfma(kv.y, qreg[kk + 1], acc);
+                acc = mla_mfma(kv.z, qreg[kk + 2], acc);
+                acc = mla_mfma(kv.w, qreg[kk + 3], acc);
+            }
+            s_part[(wave * NKB + kb) * 64 + lane] = sacc[0] + sacc[1] + sacc[2];
         }
-        s_part[wave * 64 + lane] = sacc[0] + sacc[1] + sacc[2];
         __syncthreads();
-        f32x4v sc = s_part[lane];
-#pragma unroll
-        for (int w = 1; w < kMlaWaves; ++w) sc += s_part[w * 64 + lane];
 
-        // Register r: key s0 + 4*quad + r, row `row`. Mask, then online
-        // softmax in the base-2 domain with a lazily moved maximum.
-        float x[4];
+        // Register r of block kb: key s0 + 16kb + 4*quad + r, row `row`. The
+        // group's four partial sums, the mask, then the online softmax in
+        // the base-2 domain with a lazily moved maximum.
+        float x[NKB][4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int s = s0 + 4 * quad + r;
-            const bool vis = live & (s < k1) & key_visible(p.vis, pos, s);
-            x[r] = vis ? sc[r] * p.qk_scale : -INFINITY;
+        for (int kb = 0; kb < NKB; ++kb) {
+            f32x4v sc = s_part[((grp * kMlaWaves) * NKB + kb) * 64 + lane];
+#pragma unroll
+            for (int w = 1; w < kMlaWaves; ++w) sc += s_part[((grp * kMlaWaves + w) * NKB + kb) * 64 + lane];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int s = s0 + 16 * kb + 4 * quad + r;
+                const bool vis = live & (s < k1) & key_visible(p.vis, pos, s);
+                x[kb][r] = vis ? sc[r] * p.qk_scale : -INFINITY;
+            }
         }
-        float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+        float mx = x[0][0];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) mx = fmaxf(mx, x[kb][r]);
         mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
         if (mx > m + kMlaLazy) {
@@ -207,38 +237,45 @@ __global__ __launch_bounds__(kMlaThreads, 2) void mla_split_kernel(MlaProblem p,
             m = mx;
         }
         const float mu = m == -INFINITY ? 0.0f : m;
-        float pr[4];
+        float pr[NKB][4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            pr[r] = fast_exp2(x[r] - mu);
-            l += pr[r];
-        }
-
-        // O^T += C^T P^T over this wave's output channels: k-step r takes
-        // keys 4*quad + r; block 4g + u holds channel wave*VW + 64g + 4i + u
-        // for its row i, so the lane reads one float4 per 64-channel group.
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float* vrow = tile + (4 * quad + r) * LD + wave * Sh::VW + 4 * col;
-#pragma unroll
-            for (int g = 0; g < VG; ++g) {
-                const float4 v = *reinterpret_cast<const float4*>(vrow + 64 * g);
-                o[4 * g + 0] = mla_mfma(v.x, pr[r], o[4 * g + 0]);
-                o[4 * g + 1] = mla_mfma(v.y, pr[r], o[4 * g + 1]);
-                o[4 * g + 2] = mla_mfma(v.z, pr[r], o[4 * g + 2]);
-                o[4 * g + 3] = mla_mfma(v.w, pr[r], o[4 * g + 3]);
+            for (int r = 0; r < 4; ++r) {
+                pr[kb][r] = fast_exp2(x[kb][r] - mu);
+                l += pr[kb][r];
             }
-        }
+
+        // O^T += C^T P^T over this wave's output channels: k-step (kb, r)
+        // takes keys 16kb + 4*quad + r; block 4g + u holds channel
+        // wv*VW + 64g + 4i + u for its row i, so the lane reads one float4
+        // per 64-channel group.
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int vr = 16 * kb + 4 * quad + r;
+#pragma unroll
+                for (int g = 0; g < VG; ++g) {
+                    const float4 v = *reinterpret_cast<const float4*>(
+                        tile_at<DL>(tile, vr, wv * (Sh::VW / 4) + 16 * g + col));
+                    o[4 * g + 0] = mla_mfma(v.x, pr[kb][r], o[4 * g + 0]);
+                    o[4 * g + 1] = mla_mfma(v.y, pr[kb][r], o[4 * g + 1]);
+                    o[4 * g + 2] = mla_mfma(v.z, pr[kb][r], o[4 * g + 2]);
+                    o[4 * g + 3] = mla_mfma(v.w, pr[kb][r], o[4 * g + 3]);
+                }
+            }
         if (more) stage(buf ^ 1);
     }
 
-    // The row's sum over the four quads' keys; every wave holds the same m, l.
+    // The row's sum over the four quads' keys; every wave of the group holds
+    // the same m, l.
     l += __shfl_xor(l, 16, 64);
     l += __shfl_xor(l, 32, 64);
     if (!live) return;
     const int nsplit = plan.splits;
     const int64_t slot = (int64_t)row * nsplit + sp;
-    float* acc = p.part + slot * R + wave * Sh::VW;
+    float* acc = p.part + slot * R + wv * Sh::VW;
     // Lane (col, quad), register rr of block 4g + u: channel 64g + 16*quad + 4*rr + u.
 #pragma unroll
     for (int g = 0; g < VG; ++g) {
@@ -248,7 +285,7 @@ __global__ __launch_bounds__(kMlaThreads, 2) void mla_split_kernel(MlaProblem p,
             *reinterpret_cast<float4*>(acc + 64 * g + 16 * quad + 4 * rr) = v;
         }
     }
-    if (wave == 0 && quad == 0) {
+    if (wv == 0 && quad == 0) {
         float* ml = p.part + (int64_t)nrows * nsplit * R + slot * 2;
         ml[0] = m;
         ml[1] = l;
@@ -670,8 +707,14 @@ __global__ __launch_bounds__(kCombThreads) void mla_combine4_kernel(MlaProblem p
 
 template <int R, int P>
 hipError_t launch_split_rp(const MlaProblem& p, const MlaPlan& plan, const Launch& L) {
+    if (plan.row_groups == 2) {
+        const dim3 grid((unsigned)plan.splits, (unsigned)((plan.row_blocks + 1) / 2));
+        return launch_kernel(mla_split_kernel<R, P, 2>, grid, dim3(kMlaThreads * 2),
+                             (uint32_t)MlaShape<R, P, 2>::lds_bytes, L, p, plan);
+    }
+    if (plan.row_groups != 1) return hipErrorInvalidValue;
     const dim3 grid((unsigned)plan.splits, (unsigned)plan.row_blocks);
-    return launch_kernel(mla_split_kernel<R, P>, grid, dim3(kMlaThreads), (uint32_t)MlaShape<R, P>::lds_bytes,
+    return launch_kernel(mla_split_kernel<R, P, 1>, grid, dim3(kMlaThreads), (uint32_t)MlaShape<R, P, 1>::lds_bytes,
                          L, p, plan);
 }
 

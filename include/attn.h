@@ -392,6 +392,7 @@ int attn_mla_forward(const attn_mla_params* p, const float* q, const float* stat
  *   "force_path"     force ATTN_PATH_GENERIC / _DECODE / _PREFILL (0 = automatic);
  *                    a forced path that cannot serve *p is refused
  *   "mla_splits"     force the MLA key-range split count (0 = automatic)
+ *   "mla_row_groups" 16-row blocks per MLA split workgroup, 1 or 2 (0 = automatic)
  *   "mla_generic"    1: run MLA on the generic kernel even where the
  *                    matrix-core one has an instance (0 = automatic)
  * Returns ATTN_ERR_INVALID for an unknown name.
