@@ -20,6 +20,10 @@ protocol op catalogue, op `attention`, params):
 * sinks (not a catalogue param: the IR schema's op_attention and slot_kv carry
   it beside `window`): with a window, the first `sinks` keys stay visible, as
   StreamingLLM keeps its initial tokens. 0 or absent means none.
+* position_bias and relative_kv (not catalogue params: the IR schema's
+  attention op lists them without a rule) are read as T5's bucketed relative
+  position bias and Shaw et al.'s relative key/value embeddings; see the
+  core's header comment for the exact terms.
 * ALiBi: alibiSlopes wins over alibiMax, which wins over alibi. The slopes
   enter as f32 values, as every tensor and number of the op is f32
   (catalogue convention: tensors are row-major f32); the same holds for
@@ -54,6 +58,9 @@ class _Args(ctypes.Structure):
         ("scale", ctypes.c_double), ("softcap", ctypes.c_double),
         ("window", ctypes.c_int64), ("slopes", ctypes.POINTER(ctypes.c_double)),
         ("bias_kind", ctypes.c_int32), ("sinks", ctypes.c_int64),
+        ("pb_weight", ctypes.c_void_p), ("pb_bounds", ctypes.c_void_p), ("pb_n", ctypes.c_int64),
+        ("pb_bidirectional", ctypes.c_int32),
+        ("rel_k", ctypes.c_void_p), ("rel_v", ctypes.c_void_p), ("rel_max", ctypes.c_int64),
     ]
 
 
@@ -138,8 +145,40 @@ def resolve(T: int, S: int, *, heads: int, headDim: int, kvHeads: Optional[int] 
                 scale=sigma, softcap=f32(c), window=w, slopes=slopes, sinks=nsink)
 
 
+def _position_bias(pb: dict, H: int):
+    """(weight f32 [rows, H], thresholds int64, n, bidirectional) of a position_bias
+    {weight, buckets, bidirectional?}; buckets are ascending distance thresholds from 0."""
+    bounds = np.ascontiguousarray(pb["buckets"], dtype=np.int64)
+    n = bounds.size
+    if n < 1 or bounds[0] != 0 or np.any(np.diff(bounds) <= 0):
+        raise ValueError("position_bias.buckets must be ascending distance thresholds starting at 0")
+    bidir = bool(pb.get("bidirectional", False))
+    weight = np.ascontiguousarray(pb["weight"], dtype=np.float32)
+    if weight.shape != ((2 * n if bidir else n), H):
+        raise ValueError(f"position_bias.weight {weight.shape} is not [{2 * n if bidir else n}, heads]")
+    return weight, bounds, n, bidir
+
+
+def _relative_kv(rk: dict, D: int, Dv: int):
+    """(key f32 [2m+1, D], value f32 [2m+1, Dv] or None, m) of a relative_kv
+    {key, value?, max_distance}."""
+    m = int(rk["max_distance"])
+    if m < 0:
+        raise ValueError("relative_kv.max_distance must be >= 0")
+    key = np.ascontiguousarray(rk["key"], dtype=np.float32)
+    if key.shape != (2 * m + 1, D):
+        raise ValueError(f"relative_kv.key {key.shape} is not [2*max_distance+1, headDim]")
+    val = rk.get("value")
+    if val is not None:
+        val = np.ascontiguousarray(val, dtype=np.float32)
+        if val.shape != (2 * m + 1, Dv):
+            raise ValueError(f"relative_kv.value {val.shape} is not [2*max_distance+1, vHeadDim]")
+    return key, val, m
+
+
 def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, bias: Optional[np.ndarray] = None,
               *, rows: Optional[Sequence[int]] = None, threads: Optional[int] = None,
+              position_bias: Optional[dict] = None, relative_kv: Optional[dict] = None,
               **params) -> np.ndarray:
     """The op's output in f64: [T, heads*vHeadDim], or [len(rows), ...] for a row subset.
 
@@ -183,6 +222,17 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, bias: Optional[np.nda
     if r["slopes"] is not None:
         slopes_arr = np.asarray(r["slopes"], dtype=np.float64)
         args.slopes = slopes_arr.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+    keep = []
+    if position_bias is not None:
+        weight, bounds, n, bidir = _position_bias(position_bias, H)
+        keep += [weight, bounds]
+        args.pb_weight, args.pb_bounds, args.pb_n = weight.ctypes.data, bounds.ctypes.data, n
+        args.pb_bidirectional = int(bidir)
+    if relative_kv is not None:
+        key, val, m = _relative_kv(relative_kv, D, Dv)
+        keep += [key, val]
+        args.rel_k, args.rel_max = key.ctypes.data, m
+        args.rel_v = val.ctypes.data if val is not None else None
 
     lib = _load()
     rc = lib.oracle_attention(

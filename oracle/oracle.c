@@ -23,10 +23,24 @@
  *     x_s = scale * sum_d q[t, h*D + d] * k[s, g*D + d]
  *     x_s = softcap * tanh(x_s / softcap)         if softcap > 0
  *     x_s = x_s - slope[h] * |pos - s|            if ALiBi slopes are given
+ *     x_s = x_s + pb_weight[b(pos, s), h]         with a bucketed position bias
  *     x_s = x_s + bias[(h,) t, s]                 if a bias is given
  *     out[t, h*Dv + e] = sum_s exp(x_s - M) v[s, g*Dv + e] / sum_s exp(x_s - M)
  *       over the visible s, with M the largest visible x_s (the catalogue's
  *       max-subtracted softmax); a row with no visible key is 0.
+ *
+ * Two further score terms the IR schema lists on its attention op, with no
+ * rule on the pages (the readings are the published methods they are named
+ * after):
+ *   position_bias {weight, buckets}: T5's bucketed relative position bias.
+ *     buckets holds ascending distance thresholds starting at 0; the bucket
+ *     of a key is the last threshold <= |pos - s|, plus pb_n for a key after
+ *     the query when the table is bidirectional (T5's encoder layout); the
+ *     term is pb_weight[bucket, h], added where ALiBi is.
+ *   relative_kv {key, value, max_distance}: Shaw et al.'s relative position
+ *     representations. With r = clip(s - pos, -max, max) + max, the key
+ *     embedding rel_k[r] is added to k before the product with q (so it is
+ *     scaled with it) and rel_v[r] to v in the weighted sum.
  *
  * The resolution of absent parameters (defaults, slope tables) happens in the
  * Python wrapper beside this file; this core takes resolved numbers.
@@ -49,6 +63,13 @@ typedef struct {
     const double* slopes;  /* NULL: no ALiBi; else H entries */
     int32_t bias_kind;     /* 0 none, 1 [T,S], 2 [H,T,S] */
     int64_t sinks;         /* 0: none; with a window, keys s < sinks stay visible */
+    const float* pb_weight;      /* NULL: no position bias; else [pb_n or 2 pb_n, H] */
+    const int64_t* pb_bounds;    /* pb_n ascending distance thresholds, the first 0 */
+    int64_t pb_n;
+    int32_t pb_bidirectional;    /* keys after the query use the second pb_n rows */
+    const float* rel_k;          /* NULL: no relative keys; else [2 rel_max + 1, D] */
+    const float* rel_v;          /* NULL: no relative values; else [2 rel_max + 1, Dv] */
+    int64_t rel_max;
 } oracle_attention_args;
 
 typedef struct {
@@ -77,6 +98,27 @@ static int key_visible(const oracle_attention_args* a, int64_t pos, int64_t s)
     return 1;
 }
 
+/* The position-bias row of key s for a query at pos: the last threshold not
+ * above the distance, in the second half for later keys when bidirectional. */
+static int64_t pb_row(const oracle_attention_args* a, int64_t pos, int64_t s)
+{
+    const int64_t dist = pos > s ? pos - s : s - pos;
+    int64_t b = 0;
+    for (int64_t i = 0; i < a->pb_n; ++i)
+        if (a->pb_bounds[i] <= dist) b = i;
+    if (a->pb_bidirectional && s > pos) b += a->pb_n;
+    return b;
+}
+
+/* The relative-embedding row of key s for a query at pos. */
+static int64_t rel_row(const oracle_attention_args* a, int64_t pos, int64_t s)
+{
+    int64_t r = s - pos;
+    if (r < -a->rel_max) r = -a->rel_max;
+    if (r > a->rel_max) r = a->rel_max;
+    return r + a->rel_max;
+}
+
 /* One (query row, head): the definition above, written out. */
 static void attend_row(const worker_job* j, int64_t ri, int64_t h, double* x, unsigned char* vis)
 {
@@ -96,12 +138,17 @@ static void attend_row(const worker_job* j, int64_t ri, int64_t h, double* x, un
         const float* krow = j->k + s * (a->G * D) + g * D;
         double dot = 0.0;
         for (int64_t d = 0; d < D; ++d) dot += (double)qrow[d] * (double)krow[d];
+        if (a->rel_k) {
+            const float* rk = a->rel_k + rel_row(a, pos, s) * D;
+            for (int64_t d = 0; d < D; ++d) dot += (double)qrow[d] * (double)rk[d];
+        }
         double xs = a->scale * dot;
         if (a->softcap > 0.0) xs = a->softcap * tanh(xs / a->softcap);
         if (a->slopes) {
             double dist = (double)(pos > s ? pos - s : s - pos);
             xs -= a->slopes[h] * dist;
         }
+        if (a->pb_weight) xs += (double)a->pb_weight[pb_row(a, pos, s) * a->H + h];
         if (a->bias_kind == 1) xs += (double)j->bias[t * a->S + s];
         if (a->bias_kind == 2) xs += (double)j->bias[(h * a->T + t) * a->S + s];
         x[s] = xs;
@@ -118,6 +165,10 @@ static void attend_row(const worker_job* j, int64_t ri, int64_t h, double* x, un
         L += p;
         const float* vrow = j->v + s * (a->G * Dv) + g * Dv;
         for (int64_t e = 0; e < Dv; ++e) orow[e] += p * (double)vrow[e];
+        if (a->rel_v) {
+            const float* rv = a->rel_v + rel_row(a, pos, s) * Dv;
+            for (int64_t e = 0; e < Dv; ++e) orow[e] += p * (double)rv[e];
+        }
     }
     for (int64_t e = 0; e < Dv; ++e) orow[e] /= L;
 }

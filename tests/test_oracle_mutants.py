@@ -149,3 +149,40 @@ def test_mla_pins_kill_mutant(name, tmp_path):
         cwd=tree, capture_output=True, text=True, timeout=600)
     assert proc.returncode != 0, f"mutant {name} passed every pin:\n{proc.stdout[-2000:]}"
     assert "failed" in proc.stdout, proc.stdout[-2000:] + proc.stderr[-2000:]
+
+
+# Slips in the relative-position terms of the C core, caught by tests/test_oracle_relpos.py.
+RELPOS_MUTANTS = {
+    "pb_threshold_edge": ("if (a->pb_bounds[i] <= dist) b = i;", "if (a->pb_bounds[i] < dist) b = i;"),
+    "pb_bidirectional_side": ("if (a->pb_bidirectional && s > pos) b += a->pb_n;",
+                              "if (a->pb_bidirectional && s < pos) b += a->pb_n;"),
+    "pb_head_stride": ("a->pb_weight[pb_row(a, pos, s) * a->H + h]", "a->pb_weight[pb_row(a, pos, s) + h]"),
+    "rel_sign": ("int64_t r = s - pos;", "int64_t r = pos - s;"),
+    "rel_clip_edge": ("if (r < -a->rel_max) r = -a->rel_max;", "if (r < -a->rel_max) r = -a->rel_max + 1;"),
+    "rel_v_unweighted": ("for (int64_t e = 0; e < Dv; ++e) orow[e] += p * (double)rv[e];",
+                         "for (int64_t e = 0; e < Dv; ++e) orow[e] += (double)rv[e];"),
+    "rel_k_unscaled": ("        double xs = a->scale * dot;\n",
+                       "        double xs = a->scale * dot;\n        if (a->rel_k) xs += dot * (1.0 - a->scale);\n"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(RELPOS_MUTANTS))
+def test_relpos_pins_kill_mutant(name, tmp_path):
+    old, new = RELPOS_MUTANTS[name]
+    tree = tmp_path / "tree"
+    tree.mkdir()
+    shutil.copytree(os.path.join(ROOT, "oracle"), tree / "oracle",
+                    ignore=shutil.ignore_patterns("*.so", "__pycache__"))
+    shutil.copytree(os.path.join(ROOT, "tests"), tree / "tests",
+                    ignore=shutil.ignore_patterns("__pycache__", "test_oracle_mutants.py"))
+    shutil.copy(os.path.join(ROOT, "workloads.py"), tree / "workloads.py")
+    path = tree / "oracle" / "oracle.c"
+    src = path.read_text()
+    assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
+    path.write_text(src.replace(old, new))
+    proc = subprocess.run(
+        [sys.executable, "-m", "pytest", "tests/test_oracle_relpos.py", "-x", "-q",
+         "-p", "no:cacheprovider"],
+        cwd=tree, capture_output=True, text=True, timeout=600)
+    assert proc.returncode != 0, f"mutant {name} passed every pin:\n{proc.stdout[-2000:]}"
+    assert "failed" in proc.stdout, proc.stdout[-2000:] + proc.stderr[-2000:]
