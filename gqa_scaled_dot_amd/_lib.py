@@ -11,6 +11,7 @@ LIB_PATH = os.path.join(HERE, "libattn.so")
 ATTN_OK, ATTN_ERR_INVALID, ATTN_ERR_UNSUPPORTED, ATTN_ERR_DEVICE = 0, 1, 2, 3
 ATTN_ALIBI_NONE, ATTN_ALIBI_BLOOM, ATTN_ALIBI_MPT, ATTN_ALIBI_EXPLICIT = 0, 1, 2, 3
 ATTN_ALIBI_MAX_HEADS = 256
+ATTN_PB_MAX_BUCKETS, ATTN_PB_MAX_DIST = 128, 512
 ATTN_BIAS_NONE, ATTN_BIAS_TS, ATTN_BIAS_HTS = 0, 1, 2
 ATTN_PATH_EMPTY, ATTN_PATH_ZERO, ATTN_PATH_GENERIC, ATTN_PATH_DECODE, ATTN_PATH_PREFILL = 0, 1, 2, 3, 4
 ATTN_PATH_MLA = 5
@@ -64,6 +65,9 @@ class AttnParams(ctypes.Structure):
         ("bias_kind", ctypes.c_int32), ("reserved", ctypes.c_int32),
         ("q_rope", ctypes.POINTER(AttnRopeParams)),
         ("sinks", ctypes.c_int64),
+        ("pb_weight", ctypes.c_void_p), ("pb_buckets", ctypes.POINTER(ctypes.c_int64)),
+        ("pb_n", ctypes.c_int64), ("pb_bidirectional", ctypes.c_int32), ("reserved2", ctypes.c_int32),
+        ("rel_k", ctypes.c_void_p), ("rel_v", ctypes.c_void_p), ("rel_max", ctypes.c_int64),
     ]
 
 

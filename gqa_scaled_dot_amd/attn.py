@@ -107,12 +107,16 @@ def make_params(T: int, S: int, *, heads: int, headDim: int, kvHeads: Optional[i
                 softcap: Optional[float] = None, window: Optional[int] = None,
                 alibi: Optional[bool] = None, alibiMax: Optional[float] = None,
                 alibiSlopes: Optional[Sequence[float]] = None, bias_kind: int = 0,
-                q_rope: Optional[dict] = None, sinks: Optional[int] = None):
+                q_rope: Optional[dict] = None, sinks: Optional[int] = None,
+                position_bias: Optional[dict] = None, relative_kv: Optional[dict] = None):
     """attn_params for one call. Returns (params, keepalive) - keep the second
     alive until the call returns (it owns the explicit slope array and the
     q_rope parameters). q_rope holds `rope` op params for q; its headDim
     defaults to headDim and its offset to posOffset. sinks: attention sinks
-    beside the window (keys s < sinks stay visible)."""
+    beside the window (keys s < sinks stay visible). position_bias: {weight,
+    buckets, bidirectional} (weight a GPU tensor [n or 2n, heads], buckets
+    the n ascending distance thresholds). relative_kv: {key, value,
+    max_distance} (GPU tensors [2*max_distance+1, headDim / vHeadDim])."""
     L = _lib.lib()
     p = AttnParams()
     L.attn_params_init(ctypes.byref(p))
@@ -132,6 +136,19 @@ def make_params(T: int, S: int, *, heads: int, headDim: int, kvHeads: Optional[i
         p.window = int(window)
     if sinks is not None:
         p.sinks = int(sinks)
+    extra = []
+    if position_bias is not None:
+        buckets = [int(b) for b in position_bias["buckets"]]
+        arr = (ctypes.c_int64 * max(1, len(buckets)))(*buckets)
+        extra.append(arr)
+        p.pb_weight = _ptr(position_bias["weight"])
+        p.pb_buckets = ctypes.cast(arr, ctypes.POINTER(ctypes.c_int64))
+        p.pb_n = len(buckets)
+        p.pb_bidirectional = 1 if position_bias.get("bidirectional") else 0
+    if relative_kv is not None:
+        p.rel_k = _ptr(relative_kv["key"])
+        p.rel_v = _ptr(relative_kv.get("value"))
+        p.rel_max = int(relative_kv["max_distance"])
     keep = None
     if alibiSlopes is not None:
         # The C ABI takes `heads` floats; only the caller knows the list's length.
@@ -154,7 +171,18 @@ def make_params(T: int, S: int, *, heads: int, headDim: int, kvHeads: Optional[i
         r, rkeep = make_rope_params(**rp)
         keep = (keep, r, rkeep)
         p.q_rope = ctypes.pointer(r)
+    if extra:
+        keep = (keep, extra)
     return p, keep
+
+
+def _ptr(x):
+    """Device address of a tensor argument inside the params (None -> NULL)."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
 
 
 def attn_validate(T: int, S: int, bias_kind: int = 0, **params) -> None:
@@ -269,6 +297,22 @@ def _check_forward(q, k, v, bias, out, params):
         _dev_tensor(out, "out")
         if tuple(out.shape) != (T, H * Dv):
             raise ValueError(f"out: {tuple(out.shape)} is not [T, heads*vHeadDim] = [{T}, {H * Dv}]")
+    pb = params.get("position_bias")
+    if pb is not None:
+        _dev_tensor(pb["weight"], "position_bias.weight")
+        n = len(pb["buckets"]) * (2 if pb.get("bidirectional") else 1)
+        if tuple(pb["weight"].shape) != (n, H):
+            raise ValueError(f"position_bias.weight: {tuple(pb['weight'].shape)} is not [{n}, heads={H}]")
+    rk = params.get("relative_kv")
+    if rk is not None:
+        m = int(rk["max_distance"])
+        _dev_tensor(rk["key"], "relative_kv.key")
+        if tuple(rk["key"].shape) != (2 * m + 1, D):
+            raise ValueError(f"relative_kv.key: {tuple(rk['key'].shape)} is not [{2 * m + 1}, headDim={D}]")
+        if rk.get("value") is not None:
+            _dev_tensor(rk["value"], "relative_kv.value")
+            if tuple(rk["value"].shape) != (2 * m + 1, Dv):
+                raise ValueError(f"relative_kv.value: {tuple(rk['value'].shape)} is not [{2 * m + 1}, vHeadDim={Dv}]")
     return T, S, H, Dv, bias_kind
 
 

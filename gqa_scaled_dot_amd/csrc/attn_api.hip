@@ -403,6 +403,38 @@ int resolve(const attn_params* p, Resolved* r) {
             e.slopes[h] = p->alibi_slopes[h];
         }
     }
+    if (p->pb_weight) {
+        // Bucketed relative position bias: thresholds -> a bucket per distance.
+        if (!p->pb_buckets) return fail(ATTN_ERR_INVALID, "position_bias.buckets: NULL pointer");
+        if (p->pb_n < 1 || p->pb_n > ATTN_PB_MAX_BUCKETS)
+            return fail(p->pb_n < 1 ? ATTN_ERR_INVALID : ATTN_ERR_UNSUPPORTED,
+                        "position_bias.buckets: 1..%d thresholds supported (got %lld)", ATTN_PB_MAX_BUCKETS,
+                        (long long)p->pb_n);
+        if (p->pb_bidirectional != 0 && p->pb_bidirectional != 1)
+            return fail(ATTN_ERR_INVALID, "position_bias.bidirectional: must be 0 or 1");
+        if (p->pb_buckets[0] != 0)
+            return fail(ATTN_ERR_INVALID, "position_bias.buckets: the first threshold must be 0");
+        for (int64_t i = 1; i < p->pb_n; ++i)
+            if (p->pb_buckets[i] <= p->pb_buckets[i - 1])
+                return fail(ATTN_ERR_INVALID, "position_bias.buckets: thresholds must ascend (entry %lld)",
+                            (long long)i);
+        const int64_t dt = p->pb_buckets[p->pb_n - 1];
+        if (dt > ATTN_PB_MAX_DIST)
+            return fail(ATTN_ERR_UNSUPPORTED, "position_bias.buckets: thresholds past %d", ATTN_PB_MAX_DIST);
+        e.pb_weight = p->pb_weight;
+        e.pb_n = (int32_t)p->pb_n;
+        e.pb_bidir = p->pb_bidirectional;
+        e.pb_dt = (int32_t)dt;
+        e.pb_heads = (int32_t)o.H;
+        int64_t b = 0;
+        for (int64_t d = 0; d < dt; ++d) {
+            while (b + 1 < p->pb_n && p->pb_buckets[b + 1] <= d) ++b;
+            e.pb_bucket[d] = (uint8_t)b;
+        }
+    } else if (p->pb_buckets || p->pb_n) {
+        return fail(ATTN_ERR_INVALID, "position_bias.weight: NULL pointer with buckets given");
+    }
+    if (p->rel_k || p->rel_v) return fail(ATTN_ERR_UNSUPPORTED, "relative_kv: not supported yet");
     memset(&o.rope, 0, sizeof o.rope);
     if (p->q_rope) {
         attn_rope_params qr = *p->q_rope;
@@ -816,8 +848,9 @@ int attn_forward(const attn_params* p, const float* q, const float* k, const flo
     if (!r.bias_kind && bias) return fail(ATTN_ERR_INVALID, "bias: pointer given with bias_kind 0");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(bias) || !aligned16(out))
         return fail(ATTN_ERR_INVALID, "q/k/v/bias/out: pointers must be 16-byte aligned");
+    const size_t pbn = p->pb_weight ? sizeof(float) * (size_t)(p->pb_n * (p->pb_bidirectional ? 2 : 1) * r.H) : 0;
     if (overlaps(out, on, q, qn) || overlaps(out, on, k, kn) || overlaps(out, on, v, vn) ||
-        overlaps(out, on, bias, bn))
+        overlaps(out, on, bias, bn) || overlaps(out, on, p->pb_weight, pbn))
         return fail(ATTN_ERR_INVALID, "out: overlaps an input");
     if (plan.workspace) {
         if (!workspace || workspace_bytes < plan.workspace)

@@ -169,6 +169,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
                     if (p.ep.bias_kind == ATTN_BIAS_TS) b = p.bias[(int64_t)tt[r] * p.S + sc];
                     else if (p.ep.bias_kind == ATTN_BIAS_HTS)
                         b = p.bias[((int64_t)hh[r] * p.T + tt[r]) * p.S + sc];
+                    if (p.ep.pb_weight) b += position_bias(p.ep, hh[r], pos[r], sc);
                     bf[r][u] = b;
                 }
             }
@@ -488,7 +489,7 @@ __global__ __launch_bounds__(kThreads) void combine_few_kernel(Problem p, int ns
 template <int D, int DV, int NQ, int DEPTH>
 hipError_t launch_split_d(const Problem& p, const DecodePlan& plan, float* ws, const Launch& L) {
     const dim3 grid((unsigned)plan.splits, (unsigned)p.G);
-    const bool epi = p.ep.softcap > 0.0f || p.ep.has_alibi || p.ep.bias_kind != ATTN_BIAS_NONE;
+    const bool epi = p.ep.any();
     if (epi) return launch_kernel(decode_split_kernel<D, DV, NQ, true, DEPTH>, grid, dim3(kThreads), 0, L, p, plan, ws);
     return launch_kernel(decode_split_kernel<D, DV, NQ, false, DEPTH>, grid, dim3(kThreads), 0, L, p, plan, ws);
 }

@@ -37,9 +37,21 @@ __device__ __forceinline__ bool key_visible(const E& e, int pos, int s) {
     return window_visible(e, pos, s) | sink_visible(e, pos, s);
 }
 
+// The bucketed position bias of key s for a query at pos in head h: the
+// bucket of distance |pos - s| (the last threshold not above it), in the
+// second half of the table for a later key when the table is bidirectional.
+__device__ __forceinline__ float position_bias(const Epilogue& e, int h, int pos, int s) {
+    const int d = abs(pos - s);
+    int b = d < e.pb_dt ? (int)e.pb_bucket[d] : e.pb_n - 1;
+    if (e.pb_bidir && s > pos) b += e.pb_n;
+    return e.pb_weight[b * e.pb_heads + h];
+}
+
 // The score of one visible (query, key) pair, in the order the op fixes:
 // scale the dot product, softcap it (feature attention.softcap: before the
-// mask), then add the ALiBi penalty -slope*|pos - s| and the bias input.
+// mask), then add the ALiBi penalty -slope*|pos - s| and the bias entry
+// (the bias input plus the bucketed position bias, fetched ahead by the
+// caller).
 __device__ __forceinline__ float score_epilogue(float dot, const Epilogue& e, int h, int pos, int s,
                                                 float bias) {
     float x = dot * e.scale;

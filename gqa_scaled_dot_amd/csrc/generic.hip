@@ -36,6 +36,7 @@ __device__ __forceinline__ float score_at(const Problem& p, const float* qrow, i
     float b = 0.0f;
     if (p.ep.bias_kind == ATTN_BIAS_TS) b = p.bias[t * p.S + s];
     else if (p.ep.bias_kind == ATTN_BIAS_HTS) b = p.bias[((int64_t)h * p.T + t) * p.S + s];
+    if (p.ep.pb_weight) b += position_bias(p.ep, h, pos, s);
     return score_epilogue(dot, p.ep, h, pos, s, b);
 }
 

@@ -23,6 +23,19 @@ struct Epilogue {
     int32_t window;     // 0: off
     int32_t sinks;      // attention sinks: keys s < sinks stay visible beside the window (0 without one)
     float slopes[ATTN_ALIBI_MAX_HEADS];
+    // Bucketed relative position bias: pb_weight[bucket * pb_heads + h].
+    const float* pb_weight;  // NULL: off
+    int32_t pb_n;            // thresholds (buckets per direction)
+    int32_t pb_bidir;        // keys after the query take buckets pb_n .. 2 pb_n - 1
+    int32_t pb_dt;           // distances >= pb_dt take bucket pb_n - 1
+    int32_t pb_heads;        // row stride of pb_weight
+    uint8_t pb_bucket[ATTN_PB_MAX_DIST];  // bucket of each distance below pb_dt
+
+    // Whether any term beyond the scaled dot product is on (the kernels'
+    // epilogue-free instances serve the rest).
+    __host__ __device__ bool any() const {
+        return softcap > 0.0f || has_alibi || bias_kind != ATTN_BIAS_NONE || pb_weight != nullptr;
+    }
 };
 
 // A resolved rotary embedding (op `rope`): the f32 inverse-frequency table

@@ -317,7 +317,7 @@ hipError_t launch_t(const Problem& p, const Args& a, const Launch& L) {
 
 template <int D, int DV>
 hipError_t launch_dims(const Problem& p, const Args& a, const Launch& L) {
-    const bool epi = p.ep.softcap > 0.0f || p.ep.has_alibi || p.ep.bias_kind != ATTN_BIAS_NONE;
+    const bool epi = p.ep.any();
     return epi ? launch_t<D, DV, true>(p, a, L) : launch_t<D, DV, false>(p, a, L);
 }
 

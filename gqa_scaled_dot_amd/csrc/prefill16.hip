@@ -271,7 +271,7 @@ hipError_t launch16_t(const Problem& p, const Args& a, const Launch& L) {
 
 template <int D, int DV>
 hipError_t launch16_dims(const Problem& p, const Args& a, const Launch& L) {
-    const bool epi = p.ep.softcap > 0.0f || p.ep.has_alibi || p.ep.bias_kind != ATTN_BIAS_NONE;
+    const bool epi = p.ep.any();
     return epi ? launch16_t<D, DV, true>(p, a, L) : launch16_t<D, DV, false>(p, a, L);
 }
 

@@ -182,13 +182,16 @@ __device__ __forceinline__ void stage_rows(const float4 (&st)[kBK * W / 4 / NT],
     }
 }
 
-// The bias entry of (head h, query row t, key s), clamped in bounds (masked
-// keys may lie outside the tensor); 0 without a bias.
+// The bias entry of (head h, query row t, key s): the bias input's entry,
+// clamped in bounds (masked keys may lie outside the tensor), plus the
+// bucketed position bias; 0 without either.
 __device__ __forceinline__ float bias_at(const Problem& p, int h, int t, int s) {
     const int sc = min(max(s, 0), (int)p.S - 1), tc = min(t, (int)p.T - 1);
-    if (p.ep.bias_kind == ATTN_BIAS_TS) return p.bias[(int64_t)tc * p.S + sc];
-    if (p.ep.bias_kind == ATTN_BIAS_HTS) return p.bias[((int64_t)h * p.T + tc) * p.S + sc];
-    return 0.0f;
+    float b = 0.0f;
+    if (p.ep.bias_kind == ATTN_BIAS_TS) b = p.bias[(int64_t)tc * p.S + sc];
+    else if (p.ep.bias_kind == ATTN_BIAS_HTS) b = p.bias[((int64_t)h * p.T + tc) * p.S + sc];
+    if (p.ep.pb_weight) b += position_bias(p.ep, h, p.ep.pos_offset + t, s);
+    return b;
 }
 
 // Score of register value `dot` for key s of the query at `pos` in head h, in

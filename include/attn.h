@@ -55,6 +55,10 @@ extern "C" {
 #define ATTN_ALIBI_EXPLICIT 3 /* `alibiSlopes`: alibi_slopes[heads], host memory */
 #define ATTN_ALIBI_MAX_HEADS 256
 
+/* attn_params position bias limits (thresholds and the largest threshold). */
+#define ATTN_PB_MAX_BUCKETS 128
+#define ATTN_PB_MAX_DIST 512
+
 /* attn_params.bias_kind: the optional fourth input (feature attention.bias). */
 #define ATTN_BIAS_NONE 0
 #define ATTN_BIAS_TS 1  /* bias [T, S], shared by all heads */
@@ -97,6 +101,27 @@ extern "C" {
  *                position; its head_dim must be 0 or head_dim). HOST pointer,
  *                read during the call and not kept. It fuses the rope that
  *                precedes attention in a decode graph into the attention call.
+ *   pb_weight, pb_buckets, pb_n, pb_bidirectional
+ *                bucketed relative position bias (not a catalogue param: the
+ *                IR schema page lists position_bias {weight, buckets} on its
+ *                attention op; read as T5's relative attention bias).
+ *                pb_buckets: HOST pointer to pb_n ascending distance
+ *                thresholds, the first 0 and the last at most
+ *                ATTN_PB_MAX_DIST (read during the call, not kept); the
+ *                bucket of a key is the last threshold <= |pos - s|, plus
+ *                pb_n for a key after the query when pb_bidirectional.
+ *                pb_weight: DEVICE pointer to [pb_n (2 pb_n when
+ *                bidirectional), heads] f32; weight[bucket, h] is added to
+ *                the score where ALiBi is. pb_weight NULL = off. At most
+ *                ATTN_PB_MAX_BUCKETS thresholds.
+ *   rel_k, rel_v, rel_max
+ *                relative key/value embeddings (IR schema relative_kv {key,
+ *                value, max_distance}; read as Shaw et al.'s relative position
+ *                representations, shared by all heads). With
+ *                r = clip(s - pos, -rel_max, rel_max) + rel_max, rel_k[r]
+ *                (DEVICE, [2 rel_max + 1, head_dim]) is added to the key before
+ *                the product with q, rel_v[r] (DEVICE, [2 rel_max + 1,
+ *                v_head_dim], or NULL) to the value. rel_k NULL = off.
  *   sinks        attention sinks (0 = none; not a catalogue param: the graph
  *                IR schema carries `sinks` beside `window` on op_attention and
  *                slot_kv). With a window on, keys s < sinks stay visible beside
@@ -122,6 +147,14 @@ typedef struct attn_params {
     int32_t reserved;
     const struct attn_rope_params* q_rope;
     int64_t sinks;
+    const float* pb_weight;
+    const int64_t* pb_buckets;
+    int64_t pb_n;
+    int32_t pb_bidirectional;
+    int32_t reserved2;
+    const float* rel_k;
+    const float* rel_v;
+    int64_t rel_max;
 } attn_params;
 
 /* Fill *p with the catalogue's defaults: causal = 1, everything optional
