@@ -30,7 +30,9 @@ prefill (T=512 at posOffset 3584), the Gemma-2-shaped sliding-window prefill
 (T=S=8192, headDim 256, softcap 50, window 4096), and the latent-shaped
 ALiBi + per-head bias decode (S=8192, headDim 192, vHeadDim 128) and
 non-causal prefill (T=S=1024), and the Llama-shaped streaming decode (window
-4096 plus 4 attention sinks over a 32768-row cache).
+4096 plus 4 attention sinks over a 32768-row cache), and the Llama-shaped
+decode with a T5-style bucketed position bias or with relative key/value
+embeddings.
 
 `mla` holds latent (MLA) attention in absorbed form: the DeepSeek-V2-Lite-
 shaped decode (16 heads, kv_rank 512, S=8192) and a DeepSeek-V3-shaped one
@@ -264,7 +266,37 @@ def sampled_rows(w, n_random=24):
     return sorted(set(r for r in fixed + [int(x) for x in rnd] if 0 <= r < w.T))
 
 
-def run_config(w, args, kv_buffers=1):
+def relpos_terms(w, kind):
+    """Host tables of a relative-position term for workload w: a T5-style
+    bucketed bias (32 buckets, the log-spaced thresholds T5's bucket function
+    gives for max distance 128) or relative key/value embeddings (max
+    distance 128)."""
+    import math
+    import numpy as np
+    import workloads as wl
+    if kind == "position_bias":
+        th, prev = [], -1
+        for d in range(4096):  # first distance of each unidirectional T5 bucket
+            b = d if d < 16 else min(16 + int(math.log(d / 16) / math.log(128 / 16) * 16), 31)
+            if b != prev:
+                th.append(d)
+                prev = b
+        return {"position_bias": {"weight": wl.normal((len(th), w.heads), 31, 3), "buckets": th}}
+    m = 128
+    return {"relative_kv": {"key": wl.normal((2 * m + 1, w.headDim), 32, 1),
+                            "value": wl.normal((2 * m + 1, w.Dv), 32, 2), "max_distance": m}}
+
+
+def _device_terms(extra, dev):
+    """The same terms with their tables on the GPU (for the library)."""
+    import torch
+    out = {}
+    for key, term in extra.items():
+        out[key] = {k: (torch.from_numpy(v).to(dev) if hasattr(v, "dtype") else v) for k, v in term.items()}
+    return out
+
+
+def run_config(w, args, kv_buffers=1, extra=None, label=None):
     """Time attn_forward on one workload: kernel durations from dispatch-stamped
     events, the call time from a plain loop; the result checked against the
     oracle on sampled rows. Decode-shaped plans are rated in GB/s against HBM,
@@ -275,12 +307,14 @@ def run_config(w, args, kv_buffers=1):
     import gqa_scaled_dot_amd as ga
     import oracle
 
-    params = w.params()
     dev = torch.device("cuda:0")
+    extra = extra or {}
+    params = dict(w.params(), **_device_terms(extra, dev))
     q, k, v, bias = w.tensors()
     kind = {None: 0, "TS": 1, "HTS": 2}[w.bias]
     plan = ga.attn_plan(w.T, w.S, bias_kind=kind, **params)
-    log(f"[bench] workload: {w.name}; plan {plan}")
+    name = label or w.name
+    log(f"[bench] workload: {name}; plan {plan}")
     main_kernel = {"decode": "decode_split", "prefill": "prefill"}.get(plan["path"], "generic")
     qd = torch.from_numpy(q).to(dev)
     # Several copies of the K/V (and bias) so a timed call does not find them
@@ -329,18 +363,18 @@ def run_config(w, args, kv_buffers=1):
         + (f", combine {c_ms / c_n * 1e3:.2f} us" if c_n else "")
         + f": {achieved:.2f} {unit} = {achieved / peak:.1%} of {peak}")
     rows = sampled_rows(w)
-    ref = oracle.attention(q, k, v, bias, rows=rows, threads=cpu_threads(), **params)
+    ref = oracle.attention(q, k, v, bias, rows=rows, threads=cpu_threads(), **w.params(), **extra)
     got = out.cpu().numpy()[rows].astype(np.float64)
     err = np.abs(got - ref)
     ok = bool(np.all(err <= 1e-4 + 1e-4 * np.abs(ref)))
     log(f"[bench]   parity on {len(rows)} sampled rows: max |err| {err.max():.3e} ok={ok}")
     rec = {
-        "workload": w.name, "path": plan["path"], "splits": plan["splits"], "kv_buffers": kv_buffers,
+        "workload": name, "path": plan["path"], "splits": plan["splits"], "kv_buffers": kv_buffers,
         "value": round(value, 3), "unit": unit, "ms_per_call": round(ms_call, 6), "calls": n,
         ("bytes_per_call" if bound == "hbm" else "flops_per_call"): work,
         "roofline": {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 4),
-                     "traffic": measured_traffic(main_kernel, w.name) if main_kernel in KERNEL_SOURCES else None,
+                     "traffic": measured_traffic(main_kernel, name) if main_kernel in KERNEL_SOURCES else None,
                      "kernel": main_kernel,
                      ("bytes_per_launch" if bound == "hbm" else "flops_per_launch"): work,
                      "avg_launch_us": round(kern_s * 1e6, 3),
@@ -611,6 +645,13 @@ def main():
                           for w in (workloads.LLAMA_CHUNKED, workloads.GEMMA2_SWA,
                                     workloads.LATENT_DECODE, workloads.LATENT_NONCAUSAL,
                                     workloads.LLAMA_STREAMING)]
+        # Relative-position terms on the Llama-shaped decode.
+        for kind, label in (("position_bias", "llama3-8b-shaped decode with a T5-style bucketed position bias "
+                                              "(32 buckets, max distance 128)"),
+                            ("relative_kv", "llama3-8b-shaped decode with relative key/value embeddings "
+                                            "(max distance 128)")):
+            rec["configs"].append(run_config(workloads.LLAMA_DECODE, args, kv_buffers=2,
+                                             extra=relpos_terms(workloads.LLAMA_DECODE, kind), label=label))
         # Latent attention in absorbed form; state copies rotate over >= 512 MiB of reads.
         rec["mla"] = [run_mla(w, args, n_buffers=min(16, max(2, -(-(512 << 20) // mla_work(w)["bytes"]))))
                       for w in (workloads.MLA_DECODE, workloads.MLA_DECODE_V3)]

@@ -57,6 +57,7 @@ constexpr int64_t kDecodeMaxSplits = 1024;
 constexpr int64_t kPrefillMaxSplits = 16;
 constexpr int64_t kPrefillMinTilesPerSplit = 4;
 constexpr int64_t kMaxDim = 1 << 16;
+constexpr int64_t kRelMaxDistance = 512;  // relative_kv: per-row tables of 2 max + 1 entries in LDS
 constexpr int64_t kMlaMaxSplits = 1024;
 constexpr int64_t kMlaMinKeys = 64;       // smallest key chunk worth an MLA split workgroup (four tiles)
 constexpr int64_t kMlaChunkAlign = 16;    // the MLA split kernel's key tile
@@ -434,7 +435,17 @@ int resolve(const attn_params* p, Resolved* r) {
     } else if (p->pb_buckets || p->pb_n) {
         return fail(ATTN_ERR_INVALID, "position_bias.weight: NULL pointer with buckets given");
     }
-    if (p->rel_k || p->rel_v) return fail(ATTN_ERR_UNSUPPORTED, "relative_kv: not supported yet");
+    if (p->rel_k) {
+        if (p->rel_max < 0) return fail(ATTN_ERR_INVALID, "relative_kv.max_distance: must be >= 0");
+        if (p->rel_max > kRelMaxDistance)
+            return fail(ATTN_ERR_UNSUPPORTED, "relative_kv.max_distance: at most %lld (got %lld)",
+                        (long long)kRelMaxDistance, (long long)p->rel_max);
+        e.rel_k = p->rel_k;
+        e.rel_v = p->rel_v;
+        e.rel_max = (int32_t)p->rel_max;
+    } else if (p->rel_v) {
+        return fail(ATTN_ERR_INVALID, "relative_kv.key: NULL pointer with a value table given");
+    }
     memset(&o.rope, 0, sizeof o.rope);
     if (p->q_rope) {
         attn_rope_params qr = *p->q_rope;
@@ -495,7 +506,9 @@ int make_plan(const Resolved& r, Plan* plan) {
     const int64_t hpg = r.H / r.G;
     const int64_t nrows = r.T * hpg;
     const bool dec_ok = nrows <= 16 && attn::decode_supported((int)r.D, (int)r.Dv, next_pow2_nq(nrows));
-    const bool pre_ok = attn::prefill_supported((int)r.D, (int)r.Dv);
+    // Relative key/value embeddings have no prefill kernel: prefill-shaped
+    // calls take the generic one.
+    const bool pre_ok = attn::prefill_supported((int)r.D, (int)r.Dv) && !r.ep.rel_k;
     int path;
     if (g_opt_force_path) {
         path = (int)g_opt_force_path;
@@ -520,7 +533,24 @@ int make_plan(const Resolved& r, Plan* plan) {
         d.nq = next_pow2_nq(nrows);
         d.depth = g_opt_decode_depth ? (int32_t)g_opt_decode_depth : 2;
         d.range = kr;
-        const int64_t n = kr.hi > kr.lo ? kr.hi - kr.lo : 0;
+        // Relative-position terms: on a causal call, keys within the tables'
+        // reach of the first row (s > posOffset - reach) are looked up per
+        // key; they get a split of their own, so that this slower per-key
+        // work does not stretch a full-size chunk. The other splits see every
+        // key at the tables' far end: per-row constants.
+        if (r.causal && (r.ep.pb_weight || r.ep.rel_k) && kr.hi > kr.lo) {
+            const int64_t reach_pb = r.ep.pb_weight ? r.ep.pb_dt : 0, reach_rel = r.ep.rel_k ? r.ep.rel_max : 0;
+            const int64_t reach = reach_pb > reach_rel ? reach_pb : reach_rel;
+            int64_t near_lo = r.P0 - reach + 1;
+            if (near_lo < kr.lo) near_lo = kr.lo;
+            if (near_lo < kr.hi) {
+                d.near_lo = (int32_t)near_lo;
+                d.near_hi = (int32_t)kr.hi;
+                d.range.hi = near_lo;
+            }
+        }
+        const bool near = d.near_hi > d.near_lo;
+        const int64_t n = d.range.hi > d.range.lo ? d.range.hi - d.range.lo : 0;
         int64_t splits = g_opt_decode_splits;
         if (splits <= 0) {
             const int64_t target = ((int64_t)kCUs * kDecodeWgPerCU + r.G - 1) / r.G;
@@ -528,20 +558,21 @@ int make_plan(const Resolved& r, Plan* plan) {
             splits = target < most ? target : most;
         }
         if (splits < 1) splits = 1;
-        if (splits > kDecodeMaxSplits - 1) splits = kDecodeMaxSplits - 1;
+        if (splits > kDecodeMaxSplits - 2) splits = kDecodeMaxSplits - 2;
         int64_t chunk = n > 0 ? (n + splits - 1) / splits : kDecodeChunkAlign;
         chunk = (chunk + kDecodeChunkAlign - 1) / kDecodeChunkAlign * kDecodeChunkAlign;
         // The kernel addresses a chunk with 32-bit offsets from its first row.
         const int64_t row_floats = r.G * (r.D > r.Dv ? r.D : r.Dv);
         const int64_t max_chunk = (INT32_MAX - row_floats) / row_floats / kDecodeChunkAlign * kDecodeChunkAlign;
-        if (max_chunk < kDecodeChunkAlign || (n + max_chunk - 1) / max_chunk > kDecodeMaxSplits - 1 ||
-            sink_hi > max_chunk)
+        if (max_chunk < kDecodeChunkAlign || (n + max_chunk - 1) / max_chunk > kDecodeMaxSplits - 2 ||
+            sink_hi > max_chunk || (near && d.near_hi - d.near_lo > max_chunk))
             return fail(ATTN_ERR_UNSUPPORTED, "S: key range too long for the decode path at this width");
         if (chunk > max_chunk) chunk = max_chunk;
         d.chunk = chunk;
-        // The sink keys below the window get a split of their own (the last).
+        // The near keys, then the sink keys below the window, get a split of
+        // their own each (after the chunks of `range`).
         d.sink_hi = (int32_t)sink_hi;
-        d.splits = (int32_t)((n + chunk - 1) / chunk) + (sink_hi > 0 ? 1 : 0);
+        d.splits = (int32_t)((n + chunk - 1) / chunk) + (near ? 1 : 0) + (sink_hi > 0 ? 1 : 0);
         if (d.splits > 1)
             plan->workspace = sizeof(float) * (size_t)(r.T * r.H) * (size_t)d.splits * (size_t)(r.Dv + 2);
     }
@@ -850,7 +881,9 @@ int attn_forward(const attn_params* p, const float* q, const float* k, const flo
         return fail(ATTN_ERR_INVALID, "q/k/v/bias/out: pointers must be 16-byte aligned");
     const size_t pbn = p->pb_weight ? sizeof(float) * (size_t)(p->pb_n * (p->pb_bidirectional ? 2 : 1) * r.H) : 0;
     if (overlaps(out, on, q, qn) || overlaps(out, on, k, kn) || overlaps(out, on, v, vn) ||
-        overlaps(out, on, bias, bn) || overlaps(out, on, p->pb_weight, pbn))
+        overlaps(out, on, bias, bn) || overlaps(out, on, p->pb_weight, pbn) ||
+        overlaps(out, on, p->rel_k, p->rel_k ? sizeof(float) * (size_t)((2 * p->rel_max + 1) * r.D) : 0) ||
+        overlaps(out, on, p->rel_v, p->rel_v ? sizeof(float) * (size_t)((2 * p->rel_max + 1) * r.Dv) : 0))
         return fail(ATTN_ERR_INVALID, "out: overlaps an input");
     if (plan.workspace) {
         if (!workspace || workspace_bytes < plan.workspace)

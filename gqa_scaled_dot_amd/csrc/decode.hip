@@ -67,11 +67,16 @@ __device__ __forceinline__ bool chunk_all_visible(const Epilogue& e, int pos_fir
     return d <= e.window;
 }
 
+// RM: the relative-position terms (bucketed position bias, relative
+// key/value embeddings). 0: off. 1: on, for splits whose keys are all at the
+// tables' far end for every row (their terms are per-row constants). 2: on,
+// looked up per key (the split of keys near the query rows, the sink split,
+// and non-causal calls). RM > 0 implies EPI.
 // EPI: whether softcap, ALiBi or a bias can be on; without them the score
 // is the scaled dot product and the code for the rest is left out.
 // DEPTH: batches of U rows per row group held in registers as a ring; DEPTH-1
 // of them are in flight while one is used.
-template <int D, int DV, int NQ, bool EPI, int DEPTH>
+template <int D, int DV, int NQ, bool EPI, int RM, int DEPTH>
 __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, DecodePlan plan,
                                                                    float* __restrict__ ws) {
     using Sh = DecodeShape<D, DV, NQ>;
@@ -81,7 +86,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
     const int tid = threadIdx.x;
     const int ln = tid & 15;
     const int rg = tid >> 4;
-    const int sp = blockIdx.x;
+    constexpr bool REL = RM != 0;
+    constexpr bool FAR = RM == 1;
+    const int sp = plan.split_base + blockIdx.x;
     const int g = blockIdx.y;
     const int hpg = p.H / p.G;
     const int nrows = (int)p.T * hpg;
@@ -137,9 +144,14 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
 
     // This split's keys: a chunk of the window range, or (the last split, with
     // attention sinks) the sink keys below it.
-    const bool sink_split = plan.sink_hi > 0 && sp == (int)gridDim.x - 1;
-    const int k0 = sink_split ? 0 : (int)(plan.range.lo + (int64_t)sp * plan.chunk);
-    const int k1 = sink_split ? plan.sink_hi : (int)min(plan.range.hi, (int64_t)k0 + plan.chunk);
+    // (With relative-position terms, the split before it covers the keys
+    // near the query rows.)
+    const bool sink_split = plan.sink_hi > 0 && sp == plan.splits - 1;
+    const bool near_split = plan.near_hi > plan.near_lo && sp == plan.splits - 1 - (plan.sink_hi > 0 ? 1 : 0);
+    const int k0 = sink_split ? 0 : near_split ? plan.near_lo : (int)(plan.range.lo + (int64_t)sp * plan.chunk);
+    const int k1 = sink_split   ? plan.sink_hi
+                   : near_split ? plan.near_hi
+                                : (int)min(plan.range.hi, (int64_t)k0 + plan.chunk);
     // Workgroup-uniform bases; per-lane offsets stay in 32 bits (the host
     // keeps chunk * row stride below 2^31 floats).
     const uint32_t kstride = (uint32_t)(p.G * D), vstride = (uint32_t)(p.G * DV);
@@ -148,6 +160,42 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
     // With every key of the chunk visible to every row, only the chunk's end
     // needs checking.
     const bool dense = chunk_all_visible(p.ep, p.ep.pos_offset, p.ep.pos_offset + (int)p.T - 1, k0, k1);
+    // Relative key/value embeddings: every row's products with every key
+    // embedding go to LDS once q is in registers. A chunk whose keys all lie
+    // max_distance or more before the first row's position uses embedding 0
+    // alone: a per-row constant in the scores and l * rel_v[0] in the sums.
+    const bool rel = REL && p.ep.rel_k != nullptr;
+    const int nrel = rel ? 2 * p.ep.rel_max + 1 : 0;
+    const bool rel_far = rel && k1 - 1 <= p.ep.pos_offset - p.ep.rel_max;
+    // Likewise a chunk whose keys all lie at least the last threshold before
+    // the first row takes the last bucket's bias for every key: one number per row.
+    const bool pb = REL && p.ep.pb_weight != nullptr;
+    const bool pb_far = pb && k1 - 1 <= p.ep.pos_offset - p.ep.pb_dt;
+    // FAR instances run far splits through the batched ring with those
+    // constants, and a split of keys near the rows through a plain loop, one
+    // key per row group at a time, with every term looked up per key.
+    const bool split_far = (!pb || pb_far) && (!rel || rel_far);
+    const bool near_loop = FAR && !split_far;
+    float pbc[NQ];
+#pragma unroll
+    for (int r = 0; r < NQ; ++r) {
+        pbc[r] = 0.0f;
+        if (pb_far) pbc[r] = p.ep.pb_weight[(p.ep.pb_n - 1) * p.ep.pb_heads + hh[r]];
+    }
+    extern __shared__ float s_qrel[];  // [NQ][nrel], then the position-bias bucket of each distance
+    uint8_t* s_pbb = reinterpret_cast<uint8_t*>(s_qrel + NQ * nrel);
+    float qrel0[NQ];
+#pragma unroll
+    for (int r = 0; r < NQ; ++r) qrel0[r] = 0.0f;
+
+    if constexpr (REL) {
+        // The bucket of each distance, copied to LDS for per-key lookups
+        // (before any batch is fetched: the fetches look buckets up).
+        if (pb && !(FAR && split_far)) {
+            for (int d = tid; d < p.ep.pb_dt; d += kThreads) s_pbb[d] = p.ep.pb_bucket[d];
+            __syncthreads();
+        }
+    }
 
     // Rows past the chunk's end are clamped to its last row (in bounds) and
     // their scores masked, so the loads need no branches. The bias entries of
@@ -169,7 +217,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
                     if (p.ep.bias_kind == ATTN_BIAS_TS) b = p.bias[(int64_t)tt[r] * p.S + sc];
                     else if (p.ep.bias_kind == ATTN_BIAS_HTS)
                         b = p.bias[((int64_t)hh[r] * p.T + tt[r]) * p.S + sc];
-                    if (p.ep.pb_weight) b += position_bias(p.ep, hh[r], pos[r], sc);
+                    if constexpr (REL) {
+                        if constexpr (FAR) b += pbc[r];
+                        else if (pb_far) b += pbc[r];
+                        else if (pb) b += position_bias_tab(p.ep, s_pbb, hh[r], pos[r], sc);
+                    }
                     bf[r][u] = b;
                 }
             }
@@ -189,6 +241,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
                 for (int j = 0; j < KJ; ++j) dot = dot4(qr[r][j], kf[u][j], dot);
                 dot = row16_sum(dot);
                 const int s = s0 + u;
+                if constexpr (REL) {
+                    if constexpr (FAR) dot += qrel0[r];
+                    else if (rel_far) dot += qrel0[r];
+                    else if (rel) dot += s_qrel[r * nrel + rel_row(p.ep, pos[r], s)];
+                }
                 float xs;
                 if constexpr (EPI) {
                     xs = score_epilogue(dot, p.ep, hh[r], pos[r], s, bf[r][u]) * kLog2e;
@@ -235,6 +292,22 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
                 }
                 acc[r][j] = a;
             }
+            if constexpr (REL && !FAR) {
+                if (rel && !rel_far && p.ep.rel_v) {
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        const float* rv = p.ep.rel_v + (int64_t)rel_row(p.ep, pos[r], s0 + u) * DV + 4 * ln;
+#pragma unroll
+                        for (int j = 0; j < VJ; ++j) {
+                            const float4 x4 = ld4(rv + 64 * j);
+                            acc[r][j].x = fmaf(pu[u], x4.x, acc[r][j].x);
+                            acc[r][j].y = fmaf(pu[u], x4.y, acc[r][j].y);
+                            acc[r][j].z = fmaf(pu[u], x4.z, acc[r][j].z);
+                            acc[r][j].w = fmaf(pu[u], x4.w, acc[r][j].w);
+                        }
+                    }
+                }
+            }
         }
     };
 
@@ -255,7 +328,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
         constexpr bool kAlwaysPrefetch = EPI;
 #pragma unroll
         for (int i = 0; i < DEPTH - 1; ++i)
-            if (kAlwaysPrefetch || s0 + i * kStep < k1) load(kr[i], vr[i], br[i], s0 + i * kStep);
+            if (!near_loop && (kAlwaysPrefetch || s0 + i * kStep < k1)) load(kr[i], vr[i], br[i], s0 + i * kStep);
         // q is loaded (and turned, with a rotary embedding) while the first
         // K/V batches are in flight.
         if (p.rope.on) {
@@ -287,7 +360,105 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
                 for (int j = 0; j < KJ; ++j) qr[r][j] = live[r] ? ld4(qrow + 64 * j) : zero4();
             }
         }
-        bool done = false;
+        if constexpr (REL) {
+            if (rel && FAR && split_far) {
+                // Far keys all take embedding 0: one product per row, summed
+                // across the row group's 16 lanes (every lane gets it).
+                float4 kv[KJ];
+#pragma unroll
+                for (int jj = 0; jj < KJ; ++jj) kv[jj] = ld4(p.ep.rel_k + 4 * ln + 64 * jj);
+#pragma unroll
+                for (int r = 0; r < NQ; ++r) {
+                    float d = 0.0f;
+#pragma unroll
+                    for (int jj = 0; jj < KJ; ++jj) d = dot4(qr[r][jj], kv[jj], d);
+                    qrel0[r] = row16_sum(d);
+                }
+            } else if (rel) {
+                // q . rel_k[j] per row: row group rg takes j = rg, rg + 16, ...,
+                // four embeddings' loads in flight at a time.
+                for (int j0 = rg; j0 < nrel; j0 += 4 * kRowGroups) {
+                    float4 kv[4][KJ];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int j = min(j0 + i * kRowGroups, nrel - 1);
+#pragma unroll
+                        for (int jj = 0; jj < KJ; ++jj) kv[i][jj] = ld4(p.ep.rel_k + (int64_t)j * D + 4 * ln + 64 * jj);
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int j = j0 + i * kRowGroups;
+#pragma unroll
+                        for (int r = 0; r < NQ; ++r) {
+                            float d = 0.0f;
+#pragma unroll
+                            for (int jj = 0; jj < KJ; ++jj) d = dot4(qr[r][jj], kv[i][jj], d);
+                            d = row16_sum(d);
+                            if (ln == 0 && j < nrel) s_qrel[r * nrel + j] = d;
+                        }
+                    }
+                }
+            }
+            if (!(FAR && split_far) && rel) {
+                __syncthreads();
+#pragma unroll
+                for (int r = 0; r < NQ; ++r) qrel0[r] = rel ? s_qrel[r * nrel] : 0.0f;
+            }
+        }
+        if constexpr (FAR) {
+            if (near_loop) {
+                // Keys near the rows: one key per row group at a time, every
+                // relative-position term looked up (LDS tables), v + rel_v[j].
+                for (int s = k0 + rg; s < k1; s += kRowGroups) {
+                    const uint32_t row = (uint32_t)(s - k0);
+                    float4 kf[KJ], vf[VJ];
+#pragma unroll
+                    for (int j = 0; j < KJ; ++j) kf[j] = ld4(kwg + row * kstride + 64 * j);
+#pragma unroll
+                    for (int j = 0; j < VJ; ++j) vf[j] = ld4(vwg + row * vstride + 64 * j);
+#pragma unroll
+                    for (int r = 0; r < NQ; ++r) {
+                        float dot = 0.0f;
+#pragma unroll
+                        for (int j = 0; j < KJ; ++j) dot = dot4(qr[r][j], kf[j], dot);
+                        dot = row16_sum(dot);
+                        const int jr = rel ? rel_row(p.ep, pos[r], s) : 0;
+                        if (rel) dot += s_qrel[r * nrel + jr];
+                        float b = 0.0f;
+                        if (p.ep.bias_kind == ATTN_BIAS_TS) b = p.bias[(int64_t)tt[r] * p.S + s];
+                        else if (p.ep.bias_kind == ATTN_BIAS_HTS) b = p.bias[((int64_t)hh[r] * p.T + tt[r]) * p.S + s];
+                        if (pb) b += position_bias_tab(p.ep, s_pbb, hh[r], pos[r], s);
+                        float xs = score_epilogue(dot, p.ep, hh[r], pos[r], s, b) * kLog2e;
+                        xs = (live[r] & key_visible(p.ep, pos[r], s)) ? xs : -INFINITY;
+                        if (xs > m[r] + kLazy) {
+                            const float alpha = fast_exp2(m[r] - xs);
+                            l[r] *= alpha;
+#pragma unroll
+                            for (int j = 0; j < VJ; ++j) {
+                                acc[r][j].x *= alpha; acc[r][j].y *= alpha;
+                                acc[r][j].z *= alpha; acc[r][j].w *= alpha;
+                            }
+                            m[r] = xs;
+                        }
+                        const float pw = fast_exp2(xs - (m[r] == -INFINITY ? 0.0f : m[r]));
+                        l[r] += pw;
+#pragma unroll
+                        for (int j = 0; j < VJ; ++j) {
+                            float4 vv = vf[j];
+                            if (rel && p.ep.rel_v) {
+                                const float4 rv = ld4(p.ep.rel_v + (int64_t)jr * DV + 4 * ln + 64 * j);
+                                vv.x += rv.x; vv.y += rv.y; vv.z += rv.z; vv.w += rv.w;
+                            }
+                            acc[r][j].x = fmaf(pw, vv.x, acc[r][j].x);
+                            acc[r][j].y = fmaf(pw, vv.y, acc[r][j].y);
+                            acc[r][j].z = fmaf(pw, vv.z, acc[r][j].z);
+                            acc[r][j].w = fmaf(pw, vv.w, acc[r][j].w);
+                        }
+                    }
+                }
+            }
+        }
+        bool done = near_loop;
         for (int s = s0; s < k1 && !done; s += DEPTH * kStep) {
 #pragma unroll
             for (int i = 0; i < DEPTH; ++i) {
@@ -300,6 +471,22 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
                 }
                 process(kr[i], vr[i], br[i], s + i * kStep);
             }
+        }
+    }
+
+    if constexpr (REL) {
+        // A far chunk's keys all take rel_v[0]: add it once, weighted by l.
+        if (rel_far && p.ep.rel_v) {
+#pragma unroll
+            for (int r = 0; r < NQ; ++r)
+#pragma unroll
+                for (int j = 0; j < VJ; ++j) {
+                    const float4 x4 = ld4(p.ep.rel_v + 4 * ln + 64 * j);
+                    acc[r][j].x = fmaf(l[r], x4.x, acc[r][j].x);
+                    acc[r][j].y = fmaf(l[r], x4.y, acc[r][j].y);
+                    acc[r][j].z = fmaf(l[r], x4.z, acc[r][j].z);
+                    acc[r][j].w = fmaf(l[r], x4.w, acc[r][j].w);
+                }
         }
     }
 
@@ -490,8 +677,21 @@ template <int D, int DV, int NQ, int DEPTH>
 hipError_t launch_split_d(const Problem& p, const DecodePlan& plan, float* ws, const Launch& L) {
     const dim3 grid((unsigned)plan.splits, (unsigned)p.G);
     const bool epi = p.ep.any();
-    if (epi) return launch_kernel(decode_split_kernel<D, DV, NQ, true, DEPTH>, grid, dim3(kThreads), 0, L, p, plan, ws);
-    return launch_kernel(decode_split_kernel<D, DV, NQ, false, DEPTH>, grid, dim3(kThreads), 0, L, p, plan, ws);
+    // With relative embeddings, every row's products with them sit in LDS.
+    const uint32_t lds = p.ep.rel_k ? (uint32_t)(sizeof(float) * NQ * (2 * p.ep.rel_max + 1)) : 0u;
+    if (p.ep.pb_weight || p.ep.rel_k) {
+        // Causal calls with a split of near keys: the far instance (batched
+        // ring for far splits, plain loop for the near one); otherwise every
+        // split looks its terms up per key.
+        const uint32_t lds_all = lds + (p.ep.pb_weight ? (uint32_t)((p.ep.pb_dt + 3) & ~3) : 0u);
+        if (plan.near_hi > plan.near_lo)
+            return launch_kernel(decode_split_kernel<D, DV, NQ, true, 1, DEPTH>, grid, dim3(kThreads), lds_all, L,
+                                 p, plan, ws);
+        return launch_kernel(decode_split_kernel<D, DV, NQ, true, 2, DEPTH>, grid, dim3(kThreads), lds_all, L, p,
+                             plan, ws);
+    }
+    if (epi) return launch_kernel(decode_split_kernel<D, DV, NQ, true, 0, DEPTH>, grid, dim3(kThreads), 0, L, p, plan, ws);
+    return launch_kernel(decode_split_kernel<D, DV, NQ, false, 0, DEPTH>, grid, dim3(kThreads), 0, L, p, plan, ws);
 }
 
 // A third ring batch only where it fits beside q and acc without spilling:

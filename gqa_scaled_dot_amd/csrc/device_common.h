@@ -47,6 +47,20 @@ __device__ __forceinline__ float position_bias(const Epilogue& e, int h, int pos
     return e.pb_weight[b * e.pb_heads + h];
 }
 
+// The relative-embedding row of key s for a query at pos:
+// clip(s - pos, -rel_max, rel_max) + rel_max.
+__device__ __forceinline__ int rel_row(const Epilogue& e, int pos, int s) {
+    return min(max(s - pos, -e.rel_max), e.rel_max) + e.rel_max;
+}
+
+// The same with the distance -> bucket table in LDS (tab, pb_dt entries).
+__device__ __forceinline__ float position_bias_tab(const Epilogue& e, const uint8_t* tab, int h, int pos, int s) {
+    const int d = abs(pos - s);
+    int b = d < e.pb_dt ? (int)tab[d] : e.pb_n - 1;
+    if (e.pb_bidir && s > pos) b += e.pb_n;
+    return e.pb_weight[b * e.pb_heads + h];
+}
+
 // The score of one visible (query, key) pair, in the order the op fixes:
 // scale the dot product, softcap it (feature attention.softcap: before the
 // mask), then add the ALiBi penalty -slope*|pos - s| and the bias entry

@@ -28,11 +28,14 @@ __device__ float block_reduce(float x, float* red, bool is_max) {
     return x;
 }
 
-__device__ __forceinline__ float score_at(const Problem& p, const float* qrow, int h, int g,
-                                          int64_t t, int pos, int s) {
+// qrel: the row's products with the relative key embeddings (q . rel_k[j]),
+// or NULL without them.
+__device__ __forceinline__ float score_at(const Problem& p, const float* qrow, const float* qrel, int h,
+                                          int g, int64_t t, int pos, int s) {
     const float* krow = p.k + s * (int64_t)p.G * p.D + (int64_t)g * p.D;
     float dot = 0.0f;
     for (int d = 0; d < p.D; ++d) dot = fmaf(qrow[d], krow[d], dot);
+    if (qrel) dot += qrel[rel_row(p.ep, pos, s)];
     float b = 0.0f;
     if (p.ep.bias_kind == ATTN_BIAS_TS) b = p.bias[t * p.S + s];
     else if (p.ep.bias_kind == ATTN_BIAS_HTS) b = p.bias[((int64_t)h * p.T + t) * p.S + s];
@@ -46,6 +49,7 @@ __global__ __launch_bounds__(kThreads) void generic_kernel(Problem p) {
     float* acc = qrow + p.D;       // Dv
     float* w = acc + p.Dv;         // kThreads weights of the current key chunk
     float* red = w + kThreads;     // kThreads / 64 partials
+    float* qrel = red + kThreads / 64;  // 2 rel_max + 1 products q . rel_k[j] (with relative keys)
 
     const int64_t t = blockIdx.x;
     const int h = blockIdx.y;
@@ -58,10 +62,19 @@ __global__ __launch_bounds__(kThreads) void generic_kernel(Problem p) {
         qrow[d] = p.rope.on ? rope_channel(p.rope, qhead, d, p.rope.pos0 + t) : qhead[d];
     for (int e = tid; e < p.Dv; e += kThreads) acc[e] = 0.0f;
     __syncthreads();
+    const int nrel = p.ep.rel_k ? 2 * p.ep.rel_max + 1 : 0;
+    for (int j = tid; j < nrel; j += kThreads) {
+        const float* rk = p.ep.rel_k + (int64_t)j * p.D;
+        float d = 0.0f;
+        for (int c = 0; c < p.D; ++c) d = fmaf(qrow[c], rk[c], d);
+        qrel[j] = d;
+    }
+    if (nrel) __syncthreads();
+    const float* qr = nrel ? qrel : nullptr;
 
     float m = -INFINITY;
     for (int s = tid; s < p.S; s += kThreads)
-        if (key_visible(p.ep, pos, s)) m = fmaxf(m, score_at(p, qrow, h, g, t, pos, s));
+        if (key_visible(p.ep, pos, s)) m = fmaxf(m, score_at(p, qrow, qr, h, g, t, pos, s));
     m = block_reduce(m, red, true);
 
     float* orow = p.out + t * (int64_t)p.H * p.Dv + (int64_t)h * p.Dv;
@@ -75,7 +88,7 @@ __global__ __launch_bounds__(kThreads) void generic_kernel(Problem p) {
         const int s = s0 + tid;
         float wt = 0.0f;
         if (s < p.S && key_visible(p.ep, pos, s))
-            wt = exp2f((score_at(p, qrow, h, g, t, pos, s) - m) * kLog2e);
+            wt = exp2f((score_at(p, qrow, qr, h, g, t, pos, s) - m) * kLog2e);
         l += wt;
         __syncthreads();
         w[tid] = wt;
@@ -84,7 +97,11 @@ __global__ __launch_bounds__(kThreads) void generic_kernel(Problem p) {
         for (int e = tid; e < p.Dv; e += kThreads) {
             float a = acc[e];
             for (int j = 0; j < n; ++j)
-                if (w[j] != 0.0f) a = fmaf(w[j], p.v[(int64_t)(s0 + j) * p.G * p.Dv + (int64_t)g * p.Dv + e], a);
+                if (w[j] != 0.0f) {
+                    float val = p.v[(int64_t)(s0 + j) * p.G * p.Dv + (int64_t)g * p.Dv + e];
+                    if (p.ep.rel_v) val += p.ep.rel_v[(int64_t)rel_row(p.ep, pos, s0 + j) * p.Dv + e];
+                    a = fmaf(w[j], val, a);
+                }
             acc[e] = a;
         }
     }
@@ -96,7 +113,8 @@ __global__ __launch_bounds__(kThreads) void generic_kernel(Problem p) {
 }  // namespace
 
 hipError_t launch_generic(const Problem& p, const Launch& L) {
-    const size_t lds = sizeof(float) * ((size_t)p.D + p.Dv + kThreads + kThreads / 64);
+    const size_t nrel = p.ep.rel_k ? 2 * (size_t)p.ep.rel_max + 1 : 0;
+    const size_t lds = sizeof(float) * ((size_t)p.D + p.Dv + kThreads + kThreads / 64 + nrel);
     return launch_kernel(generic_kernel, dim3((unsigned)p.T, (unsigned)p.H), dim3(kThreads),
                          (uint32_t)lds, L, p);
 }

@@ -30,11 +30,16 @@ struct Epilogue {
     int32_t pb_dt;           // distances >= pb_dt take bucket pb_n - 1
     int32_t pb_heads;        // row stride of pb_weight
     uint8_t pb_bucket[ATTN_PB_MAX_DIST];  // bucket of each distance below pb_dt
+    // Relative key/value embeddings, row clip(s - pos, -rel_max, rel_max) + rel_max.
+    const float* rel_k;      // NULL: off; else [2 rel_max + 1, D], joins k before the q product
+    const float* rel_v;      // NULL or [2 rel_max + 1, Dv], joins v
+    int32_t rel_max;
 
     // Whether any term beyond the scaled dot product is on (the kernels'
     // epilogue-free instances serve the rest).
     __host__ __device__ bool any() const {
-        return softcap > 0.0f || has_alibi || bias_kind != ATTN_BIAS_NONE || pb_weight != nullptr;
+        return softcap > 0.0f || has_alibi || bias_kind != ATTN_BIAS_NONE || pb_weight != nullptr ||
+               rel_k != nullptr;
     }
 };
 
@@ -73,6 +78,9 @@ struct DecodePlan {
     int32_t splits;   // key-range splits per KV group (the sink split included)
     int32_t depth;    // batches in the split kernel's register ring (2 or 3)
     int32_t sink_hi;  // > 0: the last split covers the sink keys [0, sink_hi) below `range`
+    int32_t split_base;        // first split this launch covers (grid x = its splits)
+    int32_t near_lo, near_hi;  // near_hi > near_lo: a split (before the sink split) covers
+                               // [near_lo, near_hi), the keys the relative-position tables reach
     int64_t chunk;    // keys per split of `range` (multiple of the row-group step)
     KeyRange range;
 };

@@ -97,3 +97,64 @@ def test_position_bias_refusals():
         with pytest.raises(ga.AttnError) as ei:
             ga.attn_forward(dev(q), dev(k), dev(v), **w.params(), position_bias=dict(weight=wt, buckets=buckets))
         assert "position_bias" in ei.value.message and word in ei.value.message
+
+
+# --------------------------------------------------------------------------
+# relative_kv
+# --------------------------------------------------------------------------
+
+def _check_rkv(w, m, with_v, paths, seed=21, rows=None):
+    q, k, v, bias = w.tensors()
+    rk = workloads.normal((2 * m + 1, w.headDim), seed, 1)
+    rv = workloads.normal((2 * m + 1, w.Dv), seed, 2) if with_v else None
+    params = dict(w.params(), relative_kv=dict(key=dev(rk), value=dev(rv) if with_v else None, max_distance=m))
+    ref = oracle.attention(q, k, v, bias, rows=rows, **w.params(),
+                           relative_kv=dict(key=rk, value=rv, max_distance=m))
+    for path in paths:
+        got = _run(w, q, k, v, bias, params, path)
+        sel = got if rows is None else got[np.asarray(rows)]
+        assert_close(sel, ref, f"{w.name} m={m} {path}")
+
+
+@pytest.mark.parametrize("D, H, G", [(128, 32, 8), (64, 8, 8), (192, 16, 16), (256, 8, 4)])
+@pytest.mark.parametrize("m", [0, 1, 16, 200])
+def test_relative_kv_decode(D, H, G, m):
+    w = workloads.Workload("rkv decode", T=1, S=3000, heads=H, kvHeads=G, headDim=D,
+                           vHeadDim=128 if D == 192 else None, posOffset=2999, seed=D + m)
+    _check_rkv(w, m, True, ("decode", "generic"))
+
+
+@pytest.mark.parametrize("kw", [dict(T=2, heads=8, kvHeads=4), dict(T=1, causal=False, posOffset=900),
+                                dict(T=1, softcap=20.0, alibi=True), dict(T=1, window=300, sinks=2),
+                                dict(T=4, heads=4, kvHeads=4, posOffset=500)])
+def test_relative_kv_decode_features(kw):
+    base = dict(T=1, S=1200, heads=8, kvHeads=2, headDim=128, posOffset=1200 - kw.get("T", 1))
+    base.update(kw)
+    w = workloads.Workload("rkv mix", **base)
+    _check_rkv(w, 24, True, ("decode", "generic"))
+    _check_rkv(w, 24, False, ("decode",))
+
+
+def test_relative_kv_forced_splits():
+    w = workloads.Workload("rkv splits", T=1, S=5000, heads=8, kvHeads=2, headDim=128, posOffset=4999)
+    try:
+        for splits in (1, 3, 40):
+            ga.attn_set_option("decode_splits", splits)
+            _check_rkv(w, 100, True, (None,))
+    finally:
+        ga.attn_set_option("decode_splits", 0)
+
+
+def test_relative_kv_prefill_shape_takes_generic():
+    w = workloads.Workload("rkv prefill", T=70, S=90, heads=4, kvHeads=2, headDim=64, posOffset=20)
+    assert ga.attn_plan(w.T, w.S, **w.params(), relative_kv=dict(key=1, value=None, max_distance=4))["path"] == "generic"
+    _check_rkv(w, 4, True, (None,))
+
+
+def test_relative_kv_refusals():
+    w = workloads.Workload("rkv bad", T=1, S=10, heads=2, headDim=64, posOffset=9)
+    q, k, v, _ = w.tensors()
+    with pytest.raises(ga.AttnError) as ei:
+        ga.attn_forward(dev(q), dev(k), dev(v), **w.params(),
+                        relative_kv=dict(key=dev(np.zeros((1025 * 2 + 1, 64), np.float32)), max_distance=1025))
+    assert "relative_kv" in ei.value.message
