@@ -38,6 +38,7 @@ int ok() {
 // Process-wide tuning overrides (attn_set_option).
 int64_t g_opt_decode_splits = 0;
 int64_t g_opt_decode_depth = 0;
+int64_t g_opt_decode_rotate = 0;
 int64_t g_opt_prefill_splits = 0;
 int64_t g_opt_prefill_variant = 0;
 int64_t g_opt_force_path = 0;
@@ -532,6 +533,7 @@ int make_plan(const Resolved& r, Plan* plan) {
         attn::DecodePlan& d = plan->decode;
         d.nq = next_pow2_nq(nrows);
         d.depth = g_opt_decode_depth ? (int32_t)g_opt_decode_depth : 2;
+
         d.range = kr;
         // Relative-position terms: on a causal call, keys within the tables'
         // reach of the first row (s > posOffset - reach) are looked up per
@@ -569,6 +571,11 @@ int make_plan(const Resolved& r, Plan* plan) {
             return fail(ATTN_ERR_UNSUPPORTED, "S: key range too long for the decode path at this width");
         if (chunk > max_chunk) chunk = max_chunk;
         d.chunk = chunk;
+        // Splits start their chunk at one of 8 phases (split i at (5 i mod 8)
+        // eighths): chunks start at aligned addresses, and walking them in
+        // lockstep from the same phase loads the same memory channels at once.
+        // Measured on the latent-shaped decode: 30.5 -> 28.9 us.
+        d.rotate = (int32_t)(g_opt_decode_rotate ? g_opt_decode_rotate : chunk * 5 / 8);
         // The near keys, then the sink keys below the window, get a split of
         // their own each (after the chunks of `range`).
         d.sink_hi = (int32_t)sink_hi;
@@ -1152,6 +1159,11 @@ int attn_set_option(const char* name, int64_t value) {
         if (value < 0 || value > kDecodeMaxSplits)
             return fail(ATTN_ERR_INVALID, "decode_splits: must be in 0..%lld", (long long)kDecodeMaxSplits);
         g_opt_decode_splits = value;
+        return ok();
+    }
+    if (!strcmp(name, "decode_rotate")) {
+        if (value < 0 || value > (1 << 20)) return fail(ATTN_ERR_INVALID, "decode_rotate: must be in 0..2^20");
+        g_opt_decode_rotate = value;
         return ok();
     }
     if (!strcmp(name, "decode_depth")) {

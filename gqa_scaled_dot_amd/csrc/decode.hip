@@ -157,6 +157,15 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
     const uint32_t kstride = (uint32_t)(p.G * D), vstride = (uint32_t)(p.G * DV);
     const float* kwg = p.k + (int64_t)k0 * kstride + (int64_t)g * D + 4 * ln;
     const float* vwg = p.v + (int64_t)k0 * vstride + (int64_t)g * DV + 4 * ln;
+    // Splits may walk their chunk from a rotated start (a whole number of
+    // batch steps), so that splits whose chunks start at aligned addresses
+    // do not all hit the same memory channels at once.
+    const int nk = k1 - k0;
+    int rot = 0;
+    if (plan.rotate > 0 && nk > 0 && nk % kStep == 0) {
+        rot = (int)(((int64_t)sp * plan.rotate) % nk);
+        rot -= rot % kStep;
+    }
     // With every key of the chunk visible to every row, only the chunk's end
     // needs checking.
     const bool dense = chunk_all_visible(p.ep, p.ep.pos_offset, p.ep.pos_offset + (int)p.T - 1, k0, k1);
@@ -204,7 +213,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
     auto load = [&](float4 (&kf)[U][KJ], float4 (&vf)[U][VJ], float (&bf)[BR][U], int s0) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int sc = min(s0 + u, k1 - 1);
+            int sc = min(s0 + u, k1 - 1) + rot;
+            if (sc >= k1) sc -= nk;
             const uint32_t row = (uint32_t)(sc - k0);
 #pragma unroll
             for (int j = 0; j < KJ; ++j) kf[u][j] = load_stream4(kwg + row * kstride + 64 * j);
@@ -240,7 +250,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
 #pragma unroll
                 for (int j = 0; j < KJ; ++j) dot = dot4(qr[r][j], kf[u][j], dot);
                 dot = row16_sum(dot);
-                const int s = s0 + u;
+                int s = s0 + u + rot;
+                if (s >= k1 + rot) s -= rot;  // a row past the chunk's end: masked below
+                else if (s >= k1) s -= nk;
                 if constexpr (REL) {
                     if constexpr (FAR) dot += qrel0[r];
                     else if (rel_far) dot += qrel0[r];
@@ -296,7 +308,10 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
                 if (rel && !rel_far && p.ep.rel_v) {
 #pragma unroll
                     for (int u = 0; u < U; ++u) {
-                        const float* rv = p.ep.rel_v + (int64_t)rel_row(p.ep, pos[r], s0 + u) * DV + 4 * ln;
+                        int ps = s0 + u + rot;  // the key's row (chunk walks may be rotated)
+                        if (ps >= k1 + rot) ps -= rot;
+                        else if (ps >= k1) ps -= nk;
+                        const float* rv = p.ep.rel_v + (int64_t)rel_row(p.ep, pos[r], ps) * DV + 4 * ln;
 #pragma unroll
                         for (int j = 0; j < VJ; ++j) {
                             const float4 x4 = ld4(rv + 64 * j);

@@ -79,6 +79,7 @@ struct DecodePlan {
     int32_t depth;    // batches in the split kernel's register ring (2 or 3)
     int32_t sink_hi;  // > 0: the last split covers the sink keys [0, sink_hi) below `range`
     int32_t split_base;        // first split this launch covers (grid x = its splits)
+    int32_t rotate;            // split sp starts (sp * rotate mod chunk) rows into its chunk (0: in order)
     int32_t near_lo, near_hi;  // near_hi > near_lo: a split (before the sink split) covers
                                // [near_lo, near_hi), the keys the relative-position tables reach
     int64_t chunk;    // keys per split of `range` (multiple of the row-group step)

@@ -419,6 +419,8 @@ int attn_mla_forward(const attn_mla_params* p, const float* q, const float* stat
  * Tuning overrides for tests and sweeps (process-wide, not thread-safe):
  *   "decode_splits"  force the decode split count (0 = automatic)
  *   "decode_depth"   batches in flight per lane in the decode kernel, 2 or 3 (0 = automatic)
+ *   "decode_rotate"  split i starts its chunk (i * value mod chunk) rows in
+ *                    (rounded to a batch step); 0 = automatic (5/8 of a chunk)
  *   "prefill_splits" force the prefill key-range split count (0 = automatic, max 16)
  *   "prefill_variant" force the prefill kernel: 32 (32x32x2 MFMA, 32-row waves) or
  *                    16 (16x16x4 MFMA, 16-row waves); 0 = automatic
