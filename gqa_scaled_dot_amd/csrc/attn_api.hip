@@ -39,6 +39,7 @@ int ok() {
 int64_t g_opt_decode_splits = 0;
 int64_t g_opt_decode_depth = 0;
 int64_t g_opt_decode_rotate = 0;
+int64_t g_opt_decode_block = 0;
 int64_t g_opt_prefill_splits = 0;
 int64_t g_opt_prefill_variant = 0;
 int64_t g_opt_force_path = 0;
@@ -54,6 +55,7 @@ constexpr int kDecodeWgPerCU = 2;         // decode_split occupancy target
 // take 14 us in 32-64 chunks against 19 us in 16.
 constexpr int64_t kDecodeMinKeys = 64;
 constexpr int64_t kDecodeChunkAlign = 64; // key chunk granularity (a multiple of 16 row groups x 2 rows)
+constexpr int64_t kDecodeBlock = 256;     // rows per interleaved block, automatic choice (power of two)
 constexpr int64_t kDecodeMaxSplits = 1024;
 constexpr int64_t kPrefillMaxSplits = 16;
 constexpr int64_t kPrefillMinTilesPerSplit = 4;
@@ -477,6 +479,15 @@ attn::KeyRange key_range(const Resolved& r) {
     return kr;
 }
 
+// Whether every query row sees every key of kr (same rules as key_range).
+bool range_all_visible(const Resolved& r, const attn::KeyRange& kr) {
+    if (kr.hi <= kr.lo) return true;
+    const int64_t first = r.P0, last = r.P0 + r.T - 1;
+    if (r.causal) return kr.hi - 1 <= first && (r.window == 0 || kr.lo > last - r.window);
+    if (r.window == 0) return true;
+    return last - kr.lo <= r.window && kr.hi - 1 - first <= r.window;
+}
+
 int next_pow2_nq(int64_t n) {
     int q = 1;
     while (q < n) q *= 2;
@@ -555,14 +566,27 @@ int make_plan(const Resolved& r, Plan* plan) {
         const int64_t n = d.range.hi > d.range.lo ? d.range.hi - d.range.lo : 0;
         int64_t splits = g_opt_decode_splits;
         if (splits <= 0) {
-            const int64_t target = ((int64_t)kCUs * kDecodeWgPerCU + r.G - 1) / r.G;
+            // As many workgroups as the chip holds at once, near and sink
+            // splits included, and no more: a few workgroups past that
+            // would run as a second wave and nearly double the time.
+            const int64_t extra = (near ? 1 : 0) + (sink_hi > 0 ? 1 : 0);
+            const int64_t target = (int64_t)kCUs * kDecodeWgPerCU / r.G - extra;
             const int64_t most = (n + kDecodeMinKeys - 1) / kDecodeMinKeys;
             splits = target < most ? target : most;
         }
         if (splits < 1) splits = 1;
         if (splits > kDecodeMaxSplits - 2) splits = kDecodeMaxSplits - 2;
-        int64_t chunk = n > 0 ? (n + splits - 1) / splits : kDecodeChunkAlign;
-        chunk = (chunk + kDecodeChunkAlign - 1) / kDecodeChunkAlign * kDecodeChunkAlign;
+        // Chunks of a whole number of 64-key steps where that keeps 15/16 of
+        // the splits, else of finer steps (down to a 2-row batch): over a
+        // short range, rounding up to 64 keys could halve the split count.
+        int64_t chunk = kDecodeChunkAlign;
+        if (n > 0) {
+            const int64_t per = (n + splits - 1) / splits;
+            for (const int64_t a : {kDecodeChunkAlign, (int64_t)32, (int64_t)16, (int64_t)2}) {
+                chunk = (per + a - 1) / a * a;
+                if ((n + chunk - 1) / chunk * 16 >= splits * 15) break;
+            }
+        }
         // The kernel addresses a chunk with 32-bit offsets from its first row.
         const int64_t row_floats = r.G * (r.D > r.Dv ? r.D : r.Dv);
         const int64_t max_chunk = (INT32_MAX - row_floats) / row_floats / kDecodeChunkAlign * kDecodeChunkAlign;
@@ -576,10 +600,35 @@ int make_plan(const Resolved& r, Plan* plan) {
         // lockstep from the same phase loads the same memory channels at once.
         // Measured on the latent-shaped decode: 30.5 -> 28.9 us.
         d.rotate = (int32_t)(g_opt_decode_rotate ? g_opt_decode_rotate : chunk * 5 / 8);
+        d.main_splits = (int32_t)((n + chunk - 1) / chunk);
+        // Where every row sees every key of the range, the splits can take
+        // interleaved blocks of it instead of a chunk each (same keys per
+        // split, fixed at planning, so results do not depend on timing):
+        // all splits then stream through the same stretch of memory together.
+        // Measured on decode shapes from 8k to 128k keys: blocks of 256 rows
+        // beat chunks where a chunk is 1024 keys or more (Llama-shaped
+        // 128k-key decode 175-195 -> 166-176 us), and are no better below.
+        // Automatic blocks never lengthen the longest split.
+        int64_t block = g_opt_decode_block;
+        if (block == 0) {
+            block = -1;
+            for (int64_t b = kDecodeBlock; b >= 64 && chunk >= 4 * kDecodeBlock; b /= 2) {
+                if ((n + b - 1) / b <= d.main_splits * (chunk / b)) {
+                    block = b;
+                    break;
+                }
+            }
+        }
+        if (block > 0 && n > 0 && range_all_visible(r, d.range) && n <= (INT32_MAX - row_floats) / row_floats) {
+            const int64_t nblocks = (n + block - 1) / block;
+            d.block = (int32_t)block;
+            if (d.main_splits > nblocks) d.main_splits = (int32_t)nblocks;
+            d.rotate = 0;
+        }
         // The near keys, then the sink keys below the window, get a split of
-        // their own each (after the chunks of `range`).
+        // their own each (after the splits of `range`).
         d.sink_hi = (int32_t)sink_hi;
-        d.splits = (int32_t)((n + chunk - 1) / chunk) + (near ? 1 : 0) + (sink_hi > 0 ? 1 : 0);
+        d.splits = d.main_splits + (near ? 1 : 0) + (sink_hi > 0 ? 1 : 0);
         if (d.splits > 1)
             plan->workspace = sizeof(float) * (size_t)(r.T * r.H) * (size_t)d.splits * (size_t)(r.Dv + 2);
     }
@@ -795,8 +844,10 @@ int mla_make_plan(const MlaResolved& r, MlaPlanFull* out) {
         if (splits <= 0) {
             // Two workgroups per CU over all row blocks (one of two row
             // groups), chunks of >= 64 keys.
+            // (Rounded down, the sink split included: workgroups past one
+            // wave would run as a second.)
             const int64_t wg_rows = (pl.row_blocks + pl.row_groups - 1) / pl.row_groups;
-            const int64_t target = ((int64_t)kCUs * (3 - pl.row_groups) + wg_rows - 1) / wg_rows;
+            const int64_t target = (int64_t)kCUs * (3 - pl.row_groups) / wg_rows - (sink_hi > 0 ? 1 : 0);
             const int64_t most = (n + kMlaMinKeys - 1) / kMlaMinKeys;
             splits = target < most ? target : most;
         }
@@ -1164,6 +1215,12 @@ int attn_set_option(const char* name, int64_t value) {
     if (!strcmp(name, "decode_rotate")) {
         if (value < 0 || value > (1 << 20)) return fail(ATTN_ERR_INVALID, "decode_rotate: must be in 0..2^20");
         g_opt_decode_rotate = value;
+        return ok();
+    }
+    if (!strcmp(name, "decode_block")) {
+        if (value != 0 && value != -1 && (value < 32 || value > 4096 || (value & (value - 1))))
+            return fail(ATTN_ERR_INVALID, "decode_block: must be 0, -1 or a power of two in 32..4096");
+        g_opt_decode_block = value;
         return ok();
     }
     if (!strcmp(name, "decode_depth")) {

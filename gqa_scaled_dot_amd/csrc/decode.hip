@@ -142,32 +142,56 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
         for (int j = 0; j < VJ; ++j) acc[r][j] = zero4();
     }
 
-    // This split's keys: a chunk of the window range, or (the last split, with
-    // attention sinks) the sink keys below it.
+    // This split's keys: its share of the window range, or (the last split,
+    // with attention sinks) the sink keys below it.
     // (With relative-position terms, the split before it covers the keys
     // near the query rows.)
     const bool sink_split = plan.sink_hi > 0 && sp == plan.splits - 1;
     const bool near_split = plan.near_hi > plan.near_lo && sp == plan.splits - 1 - (plan.sink_hi > 0 ? 1 : 0);
-    const int k0 = sink_split ? 0 : near_split ? plan.near_lo : (int)(plan.range.lo + (int64_t)sp * plan.chunk);
-    const int k1 = sink_split   ? plan.sink_hi
-                   : near_split ? plan.near_hi
-                                : (int)min(plan.range.hi, (int64_t)k0 + plan.chunk);
+    const bool spread = plan.block > 0 && !sink_split && !near_split;
+    // [k0, k1): the rows the split's keys lie in. A split walks nw rows in
+    // blocks of 2^bsh; its j-th block is block (j * bstride + boff) of
+    // [k0, k1), less bwrap when that passes bwrap.
+    int k0, k1, nw, bsh, bstride = 1, boff = 0, bwrap = INT_MAX;
+    if (spread) {
+        // Splits of the range interleave blocks: at any moment every split
+        // reads near every other, so all of them see the same mix of memory
+        // channels instead of each camping on its own stretch.
+        k0 = (int)plan.range.lo;
+        k1 = (int)plan.range.hi;
+        bsh = 31 - __builtin_clz((unsigned)plan.block);
+        const int nblocks = (k1 - k0 + plan.block - 1) >> bsh;
+        nw = ((nblocks - 1 - sp) / plan.main_splits + 1) << bsh;
+        bstride = plan.main_splits;
+        boff = sp;
+    } else {
+        k0 = sink_split ? 0 : near_split ? plan.near_lo : (int)(plan.range.lo + (int64_t)sp * plan.chunk);
+        k1 = sink_split   ? plan.sink_hi
+             : near_split ? plan.near_hi
+                          : (int)min(plan.range.hi, (int64_t)k0 + plan.chunk);
+        nw = k1 - k0;
+        bsh = 31 - __builtin_clz((unsigned)kStep);
+        // A chunk may be walked from a rotated start (a whole number of
+        // batch steps), so that splits whose chunks start at aligned
+        // addresses do not all hit the same memory channels at once.
+        if (plan.rotate > 0 && nw > 0 && nw % kStep == 0) {
+            boff = (int)((((int64_t)sp * plan.rotate) % nw) >> bsh);
+            bwrap = nw >> bsh;
+        }
+    }
+    // First row of the walk's batch starting at w (batches never straddle a block).
+    auto walk_row = [&](int w) {
+        int b = (w >> bsh) * bstride + boff;
+        if (b >= bwrap) b -= bwrap;
+        return k0 + (b << bsh) + (w & ((1 << bsh) - 1));
+    };
     // Workgroup-uniform bases; per-lane offsets stay in 32 bits (the host
-    // keeps chunk * row stride below 2^31 floats).
+    // keeps (k1 - k0) * row stride below 2^31 floats).
     const uint32_t kstride = (uint32_t)(p.G * D), vstride = (uint32_t)(p.G * DV);
     const float* kwg = p.k + (int64_t)k0 * kstride + (int64_t)g * D + 4 * ln;
     const float* vwg = p.v + (int64_t)k0 * vstride + (int64_t)g * DV + 4 * ln;
-    // Splits may walk their chunk from a rotated start (a whole number of
-    // batch steps), so that splits whose chunks start at aligned addresses
-    // do not all hit the same memory channels at once.
-    const int nk = k1 - k0;
-    int rot = 0;
-    if (plan.rotate > 0 && nk > 0 && nk % kStep == 0) {
-        rot = (int)(((int64_t)sp * plan.rotate) % nk);
-        rot -= rot % kStep;
-    }
-    // With every key of the chunk visible to every row, only the chunk's end
-    // needs checking.
+    // With every key of [k0, k1) visible to every row, only rows past the
+    // walk's or the range's end need checking.
     const bool dense = chunk_all_visible(p.ep, p.ep.pos_offset, p.ep.pos_offset + (int)p.T - 1, k0, k1);
     // Relative key/value embeddings: every row's products with every key
     // embedding go to LDS once q is in registers. A chunk whose keys all lie
@@ -206,15 +230,15 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
         }
     }
 
-    // Rows past the chunk's end are clamped to its last row (in bounds) and
-    // their scores masked, so the loads need no branches. The bias entries of
+    // Rows past the walk's or the range's end are clamped to row k1 - 1 (in
+    // bounds) and their scores masked, so the loads need no branches. The bias entries of
     // a batch travel with its K/V rows, so their latency is hidden too.
     constexpr int BR = EPI ? NQ : 1;
-    auto load = [&](float4 (&kf)[U][KJ], float4 (&vf)[U][VJ], float (&bf)[BR][U], int s0) {
+    auto load = [&](float4 (&kf)[U][KJ], float4 (&vf)[U][VJ], float (&bf)[BR][U], int w0) {
+        const int r0 = walk_row(w0);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            int sc = min(s0 + u, k1 - 1) + rot;
-            if (sc >= k1) sc -= nk;
+            const int sc = min(r0 + u, k1 - 1);
             const uint32_t row = (uint32_t)(sc - k0);
 #pragma unroll
             for (int j = 0; j < KJ; ++j) kf[u][j] = load_stream4(kwg + row * kstride + 64 * j);
@@ -239,8 +263,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
     };
 
     auto process = [&](const float4 (&kf)[U][KJ], const float4 (&vf)[U][VJ], const float (&bf)[BR][U],
-                       int s0) {
-        const bool check = !(dense && s0 + U <= k1);
+                       int w0) {
+        const int r0 = walk_row(w0);
+        const bool check = !(dense && w0 + U <= nw && r0 + U <= k1);
         float x[NQ][U];
 #pragma unroll
         for (int r = 0; r < NQ; ++r) {
@@ -250,9 +275,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
 #pragma unroll
                 for (int j = 0; j < KJ; ++j) dot = dot4(qr[r][j], kf[u][j], dot);
                 dot = row16_sum(dot);
-                int s = s0 + u + rot;
-                if (s >= k1 + rot) s -= rot;  // a row past the chunk's end: masked below
-                else if (s >= k1) s -= nk;
+                const int s = r0 + u;
                 if constexpr (REL) {
                     if constexpr (FAR) dot += qrel0[r];
                     else if (rel_far) dot += qrel0[r];
@@ -264,7 +287,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
                 } else {
                     xs = dot * (p.ep.scale * kLog2e);
                 }
-                const bool vis = !check | (live[r] & (s < k1) & key_visible(p.ep, pos[r], s));
+                const bool vis = !check | (live[r] & (w0 + u < nw) & (s < k1) & key_visible(p.ep, pos[r], s));
                 x[r][u] = vis ? xs : -INFINITY;
             }
         }
@@ -308,10 +331,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
                 if (rel && !rel_far && p.ep.rel_v) {
 #pragma unroll
                     for (int u = 0; u < U; ++u) {
-                        int ps = s0 + u + rot;  // the key's row (chunk walks may be rotated)
-                        if (ps >= k1 + rot) ps -= rot;
-                        else if (ps >= k1) ps -= nk;
-                        const float* rv = p.ep.rel_v + (int64_t)rel_row(p.ep, pos[r], ps) * DV + 4 * ln;
+                        const float* rv = p.ep.rel_v + (int64_t)rel_row(p.ep, pos[r], r0 + u) * DV + 4 * ln;
 #pragma unroll
                         for (int j = 0; j < VJ; ++j) {
                             const float4 x4 = ld4(rv + 64 * j);
@@ -331,7 +351,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
         // i+1 .. i+DEPTH-1 are in flight.
         float4 kr[DEPTH][U][KJ], vr[DEPTH][U][VJ];
         float br[DEPTH][BR][U];
-        const int s0 = k0 + rg * U;
+        const int w_rg = rg * U;  // this row group's first batch in the walk
         // With the epilogue on, batches are prefetched unconditionally (load()
         // clamps rows past the chunk's end, so one spare batch is read at the
         // end): a conditional load makes the compiler's wait counts assume it
@@ -343,7 +363,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
         constexpr bool kAlwaysPrefetch = EPI;
 #pragma unroll
         for (int i = 0; i < DEPTH - 1; ++i)
-            if (!near_loop && (kAlwaysPrefetch || s0 + i * kStep < k1)) load(kr[i], vr[i], br[i], s0 + i * kStep);
+            if (!near_loop && (kAlwaysPrefetch || w_rg + i * kStep < nw)) load(kr[i], vr[i], br[i], w_rg + i * kStep);
         // q is loaded (and turned, with a rotary embedding) while the first
         // K/V batches are in flight.
         if (p.rope.on) {
@@ -474,17 +494,17 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
             }
         }
         bool done = near_loop;
-        for (int s = s0; s < k1 && !done; s += DEPTH * kStep) {
+        for (int w = w_rg; w < nw && !done; w += DEPTH * kStep) {
 #pragma unroll
             for (int i = 0; i < DEPTH; ++i) {
-                const int sn = s + (i + DEPTH - 1) * kStep;
+                const int wn = w + (i + DEPTH - 1) * kStep;
                 const int nx = (i + DEPTH - 1) % DEPTH;  // a constant once unrolled
-                if (kAlwaysPrefetch || sn < k1) load(kr[nx], vr[nx], br[nx], sn);
-                if (s + i * kStep >= k1) {
+                if (kAlwaysPrefetch || wn < nw) load(kr[nx], vr[nx], br[nx], wn);
+                if (w + i * kStep >= nw) {
                     done = true;
                     break;
                 }
-                process(kr[i], vr[i], br[i], s + i * kStep);
+                process(kr[i], vr[i], br[i], w + i * kStep);
             }
         }
     }

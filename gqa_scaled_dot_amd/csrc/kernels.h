@@ -82,6 +82,10 @@ struct DecodePlan {
     int32_t rotate;            // split sp starts (sp * rotate mod chunk) rows into its chunk (0: in order)
     int32_t near_lo, near_hi;  // near_hi > near_lo: a split (before the sink split) covers
                                // [near_lo, near_hi), the keys the relative-position tables reach
+    int32_t block;    // > 0: the splits of `range` interleave blocks of this many rows (a power
+                      // of two, multiple of the row-group step): split i takes blocks i,
+                      // i + main_splits, ...; 0: split i takes the i-th chunk of `chunk` rows
+    int32_t main_splits;  // splits over `range` (the near and sink splits follow them)
     int64_t chunk;    // keys per split of `range` (multiple of the row-group step)
     KeyRange range;
 };

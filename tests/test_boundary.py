@@ -120,14 +120,35 @@ def test_decode_workspace_matches_plan():
     assert ga.attn_workspace_size(8, 8, heads=4, kvHeads=2, headDim=16) == 0
 
 
+@pytest.mark.parametrize("G", [1, 2, 6, 8, 12, 16, 24])
+def test_decode_splits_fit_one_wave(G):
+    # Two workgroups per CU on 256 CUs: splits x KV groups never passes 512,
+    # near and sink splits included.
+    kw = dict(heads=G * 2, kvHeads=G, headDim=128, posOffset=65535)
+    # (Planning reads no device memory: a stand-in weight address will do.)
+    for extra in ({}, dict(window=4096, sinks=4), dict(position_bias=dict(weight=4096, buckets=list(range(32)))),
+                  dict(window=4096, sinks=4, position_bias=dict(weight=4096, buckets=list(range(0, 320, 10))))):
+        plan = ga.attn_plan(1, 65536, **kw, **extra)
+        assert plan["path"] == "decode" and plan["splits"] * G <= 512, (G, extra, plan)
+        if "window" not in extra:  # enough keys for most slots (chunks are whole multiples of 64 keys)
+            assert plan["splits"] * G > 256, (G, extra, plan)
+
+
 def test_decode_sink_split():
     # Window 4096 of a 32768-row cache plus 4 sinks: the window splits, then
     # one split of its own for the sink keys below the window.
+    # The window takes one split fewer, so the 8 groups' workgroups still fit
+    # one wave of 2 per CU.
     kw = dict(heads=32, kvHeads=8, headDim=128, posOffset=32767, window=4096)
     plain = ga.attn_plan(1, 32768, **kw)
     sinks = ga.attn_plan(1, 32768, sinks=4, **kw)
-    assert sinks["splits"] == plain["splits"] + 1
+    assert plain["splits"] == 64 and sinks["splits"] == 64
     assert ga.attn_workspace_size(1, 32768, sinks=4, **kw) == 4 * 32 * sinks["splits"] * (128 + 2)
+    try:
+        ga.attn_set_option("decode_splits", 7)
+        assert ga.attn_plan(1, 32768, sinks=4, **kw)["splits"] == ga.attn_plan(1, 32768, **kw)["splits"] + 1
+    finally:
+        ga.attn_set_option("decode_splits", 0)
     # Sinks the window already covers need no split of their own.
     near = dict(kw, posOffset=100)
     assert ga.attn_plan(1, 32768, sinks=4, **near) == ga.attn_plan(1, 32768, **near)

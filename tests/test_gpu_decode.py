@@ -148,3 +148,46 @@ def test_one_workspace_serves_every_shape_and_path():
             got = ga.attn_forward(dev(q), dev(k), dev(v), dev(bias), workspace=ws, **w.params())
             t.cuda.synchronize()
             assert_close(got.cpu().numpy(), oracle.attention(q, k, v, bias, **w.params()), w.name)
+
+
+WALK_CASES = [
+    dict(S=4000, posOffset=3999, heads=32, kvHeads=8),
+    dict(S=1001, posOffset=1000, heads=8, kvHeads=2),                       # ragged last block
+    dict(S=3000, posOffset=2999, heads=8, kvHeads=2, window=1234),          # window start mid-block
+    dict(S=3000, posOffset=1500, heads=8, kvHeads=2, causal=False, window=700),
+    dict(S=5000, posOffset=4999, heads=8, kvHeads=2, window=2100, sinks=5),  # sink split after the blocks
+    dict(S=2000, posOffset=1999, heads=16, kvHeads=16, headDim=192, vHeadDim=128, alibi=True,
+         bias="HTS", bias_mask_prob=0.2),
+    dict(S=2500, posOffset=2497, T=3, heads=8, kvHeads=8),                  # rows see different keys: chunks
+    dict(S=100, posOffset=99, heads=4, kvHeads=1, headDim=64),              # fewer blocks than splits
+]
+
+
+@pytest.mark.parametrize("block", [-1, 32, 64, 1024])
+@pytest.mark.parametrize("case", range(len(WALK_CASES)))
+def test_decode_split_walks_agree(block, case):
+    # Chunks per split (block -1) or interleaved blocks of `block` rows: both
+    # cover every visible key once; each against the oracle, and each
+    # deterministic.
+    w = _wl(**WALK_CASES[case], seed=case)
+    q, k, v, bias = w.tensors()
+    try:
+        ga.attn_set_option("decode_block", block)
+        got1 = compare(q, k, v, bias, w.params(), what=f"block={block} {WALK_CASES[case]}")
+        got2 = run_library(q, k, v, bias, w.params()).cpu().numpy()
+    finally:
+        ga.attn_set_option("decode_block", 0)
+    np.testing.assert_array_equal(got1.view(np.uint32), got2.view(np.uint32))
+
+
+@pytest.mark.parametrize("splits", [3, 7, 64])
+def test_decode_interleaved_blocks_with_forced_splits(splits):
+    # 4000 keys in blocks of 32 (125 blocks): split counts that do not
+    # divide them leave splits with one block more than others.
+    w = _wl(S=4000, posOffset=3999, heads=32, kvHeads=8, seed=splits)
+    q, k, v, _ = w.tensors()
+    try:
+        ga.attn_set_option("decode_splits", splits)
+        compare(q, k, v, None, w.params(), what=f"interleaved, splits={splits}")
+    finally:
+        ga.attn_set_option("decode_splits", 0)

@@ -64,9 +64,10 @@ def test_decode_sink_split_and_forced_split_counts():
     try:
         for splits in (1, 2, 7, 16):
             ga.attn_set_option("decode_splits", splits)
-            # window splits: 1000 keys in chunks rounded up to 64 keys; plus the sink split
-            chunk = -(-(-(-1000 // splits)) // 64) * 64
-            assert ga.attn_plan(w.T, w.S, **w.params())["splits"] == -(-1000 // chunk) + 1
+            # The window's 1000 keys keep the forced count (chunks of whole
+            # 64-key steps, finer where those would drop a split), plus the
+            # sink split.
+            assert ga.attn_plan(w.T, w.S, **w.params())["splits"] == splits + 1
             compare(q, k, v, None, w.params(), what=f"window splits {splits}")
     finally:
         ga.attn_set_option("decode_splits", 0)
