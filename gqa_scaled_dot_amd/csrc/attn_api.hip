@@ -38,6 +38,7 @@ int ok() {
 // Process-wide tuning overrides (attn_set_option).
 int64_t g_opt_decode_splits = 0;
 int64_t g_opt_decode_depth = 0;
+int64_t g_opt_decode_wgs = 0;
 int64_t g_opt_decode_rotate = 0;
 int64_t g_opt_decode_block = 0;
 int64_t g_opt_prefill_splits = 0;
@@ -49,6 +50,7 @@ int64_t g_opt_mla_row_groups = 0;
 
 constexpr int kCUs = 256;                 // MI355X compute units
 constexpr int kDecodeWgPerCU = 2;         // decode_split occupancy target
+constexpr int kDecodeDepth = 1;           // decode_split batches per lane at a time (no prefetch ring)
 // Smallest key chunk worth a workgroup. A decode_split workgroup costs ~8 us
 // however few keys it reads (launch, q, two load round trips, merges), so
 // short caches want many small chunks: measured on Llama widths, 4096 keys
@@ -543,7 +545,7 @@ int make_plan(const Resolved& r, Plan* plan) {
     if (path == ATTN_PATH_DECODE) {
         attn::DecodePlan& d = plan->decode;
         d.nq = next_pow2_nq(nrows);
-        d.depth = g_opt_decode_depth ? (int32_t)g_opt_decode_depth : 2;
+        d.depth = g_opt_decode_depth ? (int32_t)g_opt_decode_depth : kDecodeDepth;
 
         d.range = kr;
         // Relative-position terms: on a causal call, keys within the tables'
@@ -570,7 +572,8 @@ int make_plan(const Resolved& r, Plan* plan) {
             // splits included, and no more: a few workgroups past that
             // would run as a second wave and nearly double the time.
             const int64_t extra = (near ? 1 : 0) + (sink_hi > 0 ? 1 : 0);
-            const int64_t target = (int64_t)kCUs * kDecodeWgPerCU / r.G - extra;
+            const int64_t per_cu = g_opt_decode_wgs ? g_opt_decode_wgs : kDecodeWgPerCU;
+            const int64_t target = (int64_t)kCUs * per_cu / r.G - extra;
             const int64_t most = (n + kDecodeMinKeys - 1) / kDecodeMinKeys;
             splits = target < most ? target : most;
         }
@@ -1217,6 +1220,11 @@ int attn_set_option(const char* name, int64_t value) {
         g_opt_decode_rotate = value;
         return ok();
     }
+    if (!strcmp(name, "decode_wgs_per_cu")) {
+        if (value < 0 || value > 8) return fail(ATTN_ERR_INVALID, "decode_wgs_per_cu: must be in 0..8");
+        g_opt_decode_wgs = value;
+        return ok();
+    }
     if (!strcmp(name, "decode_block")) {
         if (value != 0 && value != -1 && (value < 32 || value > 4096 || (value & (value - 1))))
             return fail(ATTN_ERR_INVALID, "decode_block: must be 0, -1 or a power of two in 32..4096");
@@ -1224,8 +1232,7 @@ int attn_set_option(const char* name, int64_t value) {
         return ok();
     }
     if (!strcmp(name, "decode_depth")) {
-        if (value != 0 && value != 2 && value != 3)
-            return fail(ATTN_ERR_INVALID, "decode_depth: must be 0, 2 or 3");
+        if (value < 0 || value > 3) return fail(ATTN_ERR_INVALID, "decode_depth: must be 0, 1, 2 or 3");
         g_opt_decode_depth = value;
         return ok();
     }

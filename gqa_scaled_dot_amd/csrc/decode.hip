@@ -44,12 +44,14 @@ template <int D, int DV, int NQ>
 struct DecodeShape {
     static constexpr int KJ = D / 64;   // float4 per lane per K row
     static constexpr int VJ = DV / 64;  // float4 per lane per V row
-    // Key rows per row group per batch. Two batches of two rows are in flight
-    // per lane (16 (KJ+VJ) registers); measured on the Llama- and
-    // latent-shaped decodes, four-row batches ran slower (more registers, no
-    // more bandwidth). Where two-row batches and the query rows' q and acc
-    // (4 NQ (KJ+VJ) registers) would pass ~170 registers, batches are one row.
-    static constexpr int U = (KJ + VJ) * (16 + 4 * NQ) <= 170 ? 2 : 1;
+    // Key rows per row group per batch: two where that is at most 8 float4
+    // loads per lane, else one. Fewer loads in flight ran faster: measured
+    // with one batch per lane at a time, the Llama-shaped decode took 44.3 us
+    // with two-row batches (8 loads) and 49.3 us with four; the latent-shaped
+    // one (5 loads per row) 27.7 us with one-row batches and 29.2 us with two.
+    // (Two-row batches also need q and acc, 4 NQ (KJ+VJ) registers, to stay
+    // under ~170 registers with the ring.)
+    static constexpr int U = ((KJ + VJ) * 2 <= 8 && (KJ + VJ) * (16 + 4 * NQ) <= 170) ? 2 : 1;
 };
 
 __device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
@@ -352,17 +354,22 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
         float4 kr[DEPTH][U][KJ], vr[DEPTH][U][VJ];
         float br[DEPTH][BR][U];
         const int w_rg = rg * U;  // this row group's first batch in the walk
-        // With the epilogue on, batches are prefetched unconditionally (load()
-        // clamps rows past the chunk's end, so one spare batch is read at the
-        // end): a conditional load makes the compiler's wait counts assume it
-        // was skipped, so processing a batch would also wait for most of the
-        // next one. Measured on the latent-shaped ALiBi+bias decode: 31.6 ->
-        // 30.6 us. Without the epilogue the spare batch's latency at the end
-        // costs more than the overlap gains (46.4 -> 47.0 us on the
-        // Llama-shaped decode), so those instances keep the condition.
+        // In a ring (DEPTH >= 2) with the epilogue on, batches are prefetched
+        // unconditionally (load() clamps rows past the chunk's end, so one
+        // spare batch is read at the end): a conditional load makes the
+        // compiler's wait counts assume it was skipped, so processing a batch
+        // would also wait for most of the next one. Measured on the
+        // latent-shaped ALiBi+bias decode: 31.6 -> 30.6 us. Without the
+        // epilogue the spare batch's latency at the end costs more than the
+        // overlap gains (46.4 -> 47.0 us on the Llama-shaped decode), so
+        // those instances keep the condition. (With one batch at a time, the
+        // default, there is no overlap to lose.)
         constexpr bool kAlwaysPrefetch = EPI;
+        // The first batch (the first DEPTH-1 of a ring) is on its way before
+        // q is fetched and set up, so its latency overlaps that work.
+        constexpr int kLead = DEPTH > 1 ? DEPTH - 1 : 1;
 #pragma unroll
-        for (int i = 0; i < DEPTH - 1; ++i)
+        for (int i = 0; i < kLead; ++i)
             if (!near_loop && (kAlwaysPrefetch || w_rg + i * kStep < nw)) load(kr[i], vr[i], br[i], w_rg + i * kStep);
         // q is loaded (and turned, with a rotary embedding) while the first
         // K/V batches are in flight.
@@ -494,6 +501,15 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
             }
         }
         bool done = near_loop;
+        if constexpr (DEPTH == 1) {
+            // One batch per lane at a time: use it, then fetch the next into
+            // the same registers.
+            for (int w = w_rg; w < nw && !done; w += kStep) {
+                process(kr[0], vr[0], br[0], w);
+                if (w + kStep < nw) load(kr[0], vr[0], br[0], w + kStep);
+            }
+            done = true;
+        }
         for (int w = w_rg; w < nw && !done; w += DEPTH * kStep) {
 #pragma unroll
             for (int i = 0; i < DEPTH; ++i) {
@@ -741,6 +757,7 @@ hipError_t launch_split_t(const Problem& p, const DecodePlan& plan, float* ws, c
     if constexpr (depth3_fits<D, DV, NQ>()) {
         if (plan.depth >= 3) return launch_split_d<D, DV, NQ, 3>(p, plan, ws, L);
     }
+    if (plan.depth == 1) return launch_split_d<D, DV, NQ, 1>(p, plan, ws, L);
     return launch_split_d<D, DV, NQ, 2>(p, plan, ws, L);
 }
 

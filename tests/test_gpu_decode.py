@@ -191,3 +191,29 @@ def test_decode_interleaved_blocks_with_forced_splits(splits):
         compare(q, k, v, None, w.params(), what=f"interleaved, splits={splits}")
     finally:
         ga.attn_set_option("decode_splits", 0)
+
+
+DEPTH_CASES = [
+    dict(S=3001, posOffset=3000, heads=32, kvHeads=8),
+    dict(S=2000, posOffset=1999, heads=16, kvHeads=16, headDim=192, vHeadDim=128, alibi=True, bias="HTS",
+         bias_mask_prob=0.2),
+    dict(S=1500, posOffset=1499, heads=16, kvHeads=2, headDim=64),
+    dict(S=1500, posOffset=1499, heads=4, kvHeads=2, headDim=256, window=700, sinks=3),
+    dict(S=900, posOffset=898, T=2, heads=8, kvHeads=4, softcap=20.0),
+]
+
+
+@pytest.mark.parametrize("depth", [1, 2, 3])
+@pytest.mark.parametrize("case", range(len(DEPTH_CASES)))
+def test_decode_ring_depths(depth, case):
+    # One batch per lane at a time (depth 1, the default) or a ring of 2 or 3
+    # (where it fits; else 2): every depth against the oracle.
+    w = _wl(**DEPTH_CASES[case], seed=40 + case)
+    q, k, v, bias = w.tensors()
+    got = {}
+    try:
+        for d in (1, depth):
+            ga.attn_set_option("decode_depth", d)
+            got[d] = compare(q, k, v, bias, w.params(), what=f"depth={d} {DEPTH_CASES[case]}")
+    finally:
+        ga.attn_set_option("decode_depth", 0)
