@@ -181,12 +181,17 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
             bwrap = nw >> bsh;
         }
     }
-    // First row of the walk's batch starting at w (batches never straddle a block).
-    auto walk_row = [&](int w) {
+    // The walk goes in steps of kStep rows, one batch of U rows per row
+    // group; a step never straddles a block. First row of step st (the same
+    // for the whole workgroup, so it stays in scalar registers):
+    auto step_row = [&](int st) {
+        const int w = st * kStep;
         int b = (w >> bsh) * bstride + boff;
         if (b >= bwrap) b -= bwrap;
         return k0 + (b << bsh) + (w & ((1 << bsh) - 1));
     };
+    const int w_rg = rg * U;  // this row group's batch within a step
+    const int nsteps = (nw + kStep - 1) / kStep;
     // Workgroup-uniform bases; per-lane offsets stay in 32 bits (the host
     // keeps (k1 - k0) * row stride below 2^31 floats).
     const uint32_t kstride = (uint32_t)(p.G * D), vstride = (uint32_t)(p.G * DV);
@@ -236,8 +241,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
     // bounds) and their scores masked, so the loads need no branches. The bias entries of
     // a batch travel with its K/V rows, so their latency is hidden too.
     constexpr int BR = EPI ? NQ : 1;
-    auto load = [&](float4 (&kf)[U][KJ], float4 (&vf)[U][VJ], float (&bf)[BR][U], int w0) {
-        const int r0 = walk_row(w0);
+    auto load = [&](float4 (&kf)[U][KJ], float4 (&vf)[U][VJ], float (&bf)[BR][U], int st) {
+        const int r0 = step_row(st) + w_rg;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int sc = min(r0 + u, k1 - 1);
@@ -265,8 +270,12 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
     };
 
     auto process = [&](const float4 (&kf)[U][KJ], const float4 (&vf)[U][VJ], const float (&bf)[BR][U],
-                       int w0) {
-        const int r0 = walk_row(w0);
+                       int st) {
+        const int w0 = st * kStep + w_rg;
+        const int r0 = step_row(st) + w_rg;
+        // Rows to mask only past the walk's or the range's end, or where not
+        // every row sees every key; the masks are worked out only when some
+        // lane of the wave has such rows.
         const bool check = !(dense && w0 + U <= nw && r0 + U <= k1);
         float x[NQ][U];
 #pragma unroll
@@ -283,14 +292,22 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
                     else if (rel_far) dot += qrel0[r];
                     else if (rel) dot += s_qrel[r * nrel + rel_row(p.ep, pos[r], s)];
                 }
-                float xs;
                 if constexpr (EPI) {
-                    xs = score_epilogue(dot, p.ep, hh[r], pos[r], s, bf[r][u]) * kLog2e;
+                    x[r][u] = score_epilogue(dot, p.ep, hh[r], pos[r], s, bf[r][u]) * kLog2e;
                 } else {
-                    xs = dot * (p.ep.scale * kLog2e);
+                    x[r][u] = dot;  // q carries scale * log2(e)
                 }
-                const bool vis = !check | (live[r] & (w0 + u < nw) & (s < k1) & key_visible(p.ep, pos[r], s));
-                x[r][u] = vis ? xs : -INFINITY;
+            }
+        }
+        if (__ballot(check)) {
+#pragma unroll
+            for (int r = 0; r < NQ; ++r) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int s = r0 + u;
+                    const bool vis = !check | (live[r] & (w0 + u < nw) & (s < k1) & key_visible(p.ep, pos[r], s));
+                    if (!vis) x[r][u] = -INFINITY;
+                }
             }
         }
 #pragma unroll
@@ -353,7 +370,6 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
         // i+1 .. i+DEPTH-1 are in flight.
         float4 kr[DEPTH][U][KJ], vr[DEPTH][U][VJ];
         float br[DEPTH][BR][U];
-        const int w_rg = rg * U;  // this row group's first batch in the walk
         // In a ring (DEPTH >= 2) with the epilogue on, batches are prefetched
         // unconditionally (load() clamps rows past the chunk's end, so one
         // spare batch is read at the end): a conditional load makes the
@@ -370,7 +386,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
         constexpr int kLead = DEPTH > 1 ? DEPTH - 1 : 1;
 #pragma unroll
         for (int i = 0; i < kLead; ++i)
-            if (!near_loop && (kAlwaysPrefetch || w_rg + i * kStep < nw)) load(kr[i], vr[i], br[i], w_rg + i * kStep);
+            if (!near_loop && (kAlwaysPrefetch || i < nsteps)) load(kr[i], vr[i], br[i], i);
         // q is loaded (and turned, with a rotary embedding) while the first
         // K/V batches are in flight.
         if (p.rope.on) {
@@ -401,6 +417,17 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
 #pragma unroll
                 for (int j = 0; j < KJ; ++j) qr[r][j] = live[r] ? ld4(qrow + 64 * j) : zero4();
             }
+        }
+        if constexpr (!EPI) {
+            // Without an epilogue the score is the scaled product: q takes
+            // the scale (and the base change of exp2) once.
+            const float c = p.ep.scale * kLog2e;
+#pragma unroll
+            for (int r = 0; r < NQ; ++r)
+#pragma unroll
+                for (int j = 0; j < KJ; ++j) {
+                    qr[r][j].x *= c; qr[r][j].y *= c; qr[r][j].z *= c; qr[r][j].w *= c;
+                }
         }
         if constexpr (REL) {
             if (rel && FAR && split_far) {
@@ -504,23 +531,23 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
         if constexpr (DEPTH == 1) {
             // One batch per lane at a time: use it, then fetch the next into
             // the same registers.
-            for (int w = w_rg; w < nw && !done; w += kStep) {
-                process(kr[0], vr[0], br[0], w);
-                if (w + kStep < nw) load(kr[0], vr[0], br[0], w + kStep);
+            for (int st = 0; st < nsteps && !done; ++st) {
+                process(kr[0], vr[0], br[0], st);
+                if (st + 1 < nsteps) load(kr[0], vr[0], br[0], st + 1);
             }
             done = true;
         }
-        for (int w = w_rg; w < nw && !done; w += DEPTH * kStep) {
+        for (int st = 0; st < nsteps && !done; st += DEPTH) {
 #pragma unroll
             for (int i = 0; i < DEPTH; ++i) {
-                const int wn = w + (i + DEPTH - 1) * kStep;
+                const int sn = st + i + DEPTH - 1;
                 const int nx = (i + DEPTH - 1) % DEPTH;  // a constant once unrolled
-                if (kAlwaysPrefetch || wn < nw) load(kr[nx], vr[nx], br[nx], wn);
-                if (w + i * kStep >= nw) {
+                if (kAlwaysPrefetch || sn < nsteps) load(kr[nx], vr[nx], br[nx], sn);
+                if (st + i >= nsteps) {
                     done = true;
                     break;
                 }
-                process(kr[i], vr[i], br[i], w + i * kStep);
+                process(kr[i], vr[i], br[i], st + i);
             }
         }
     }
