@@ -333,8 +333,8 @@ def run_config(w, args, kv_buffers=1, extra=None, label=None):
     torch.cuda.synchronize()
     # Kernel durations from dispatch-stamped events ...
     ga.attn_timing_enable(True)
-    for name in (main_kernel, "combine"):
-        ga.attn_timing_collect(name)
+    for kname in (main_kernel, "combine"):
+        ga.attn_timing_collect(kname)
     for i in range(n):
         calls[i % kv_buffers]()
     torch.cuda.synchronize()
