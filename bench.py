@@ -125,6 +125,39 @@ def visible_pairs(w) -> int:
     return int(np.maximum(hi - lo + 1, 0).sum())
 
 
+def host_cpu() -> str:
+    """The host CPU's model name (the oracle's hardware), from /proc/cpuinfo."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def device_clocks():
+    """Current shader and memory clock of the GPU, read from the amdgpu driver's
+    sysfs files (the ones rocm-smi reads: the level marked '*'), or None where
+    they are absent or more than one card shows them."""
+    import glob
+    cards = sorted(glob.glob("/sys/class/drm/card[0-9]*/device/pp_dpm_sclk"))
+    if len(cards) != 1:
+        return None
+    dev = os.path.dirname(cards[0])
+    out = {}
+    for name in ("sclk", "mclk", "fclk"):
+        try:
+            with open(os.path.join(dev, "pp_dpm_" + name)) as f:
+                for line in f:
+                    if line.rstrip().endswith("*"):
+                        out[name] = line.split(":", 1)[1].replace("*", "").strip()
+        except OSError:
+            pass
+    return out or None
+
+
 def cpu_threads() -> int:
     try:
         n = len(os.sched_getaffinity(0))
@@ -190,6 +223,7 @@ def run_decode(args):
         step(i)
     e1.record(stream)
     torch.cuda.synchronize()
+    clocks = device_clocks()  # right after the timed steps, while the clocks are still up
     ms_timed = e0.elapsed_time(e1) / args.steps
     split_ms, split_n = ga.attn_timing_collect("decode_split")
     comb_ms, comb_n = ga.attn_timing_collect("combine")
@@ -239,7 +273,7 @@ def run_decode(args):
             total += time.perf_counter() - t0
             reps += 1
         cpu_baseline = {"value": round(alg_bytes * reps / total / 1e9, 4), "unit": "GB/s",
-                        "cores": threads, "kind": "oracle",
+                        "cores": threads, "kind": "oracle", "cpu": host_cpu(),
                         "sample": f"the full decode step (1 query row, 32 heads, 32768 keys), "
                                   f"{reps} runs in {total:.1f} s, f64"}
 
@@ -255,6 +289,7 @@ def run_decode(args):
         "roofline": roofline,
         "cpu_baseline": cpu_baseline,
         "parity": {"max_abs_err": float(err.max()), "ok": parity_ok},
+        "device": {"clocks_after_timed_steps": clocks, "host_cpu": host_cpu(), "host_threads": threads},
     }
 
 
@@ -363,11 +398,14 @@ def run_config(w, args, kv_buffers=1, extra=None, label=None):
         + (f", combine {c_ms / c_n * 1e3:.2f} us" if c_n else "")
         + f": {achieved:.2f} {unit} = {achieved / peak:.1%} of {peak}")
     rows = sampled_rows(w)
+    t_oracle = time.perf_counter()
     ref = oracle.attention(q, k, v, bias, rows=rows, threads=cpu_threads(), **w.params(), **extra)
+    t_oracle = time.perf_counter() - t_oracle
     got = out.cpu().numpy()[rows].astype(np.float64)
     err = np.abs(got - ref)
     ok = bool(np.all(err <= 1e-4 + 1e-4 * np.abs(ref)))
-    log(f"[bench]   parity on {len(rows)} sampled rows: max |err| {err.max():.3e} ok={ok}")
+    log(f"[bench]   parity on {len(rows)} sampled rows: max |err| {err.max():.3e} ok={ok} "
+        f"(oracle {t_oracle:.2f} s on {cpu_threads()} threads)")
     rec = {
         "workload": name, "path": plan["path"], "splits": plan["splits"], "kv_buffers": kv_buffers,
         "value": round(value, 3), "unit": unit, "ms_per_call": round(ms_call, 6), "calls": n,
@@ -379,7 +417,8 @@ def run_config(w, args, kv_buffers=1, extra=None, label=None):
                      ("bytes_per_launch" if bound == "hbm" else "flops_per_launch"): work,
                      "avg_launch_us": round(kern_s * 1e6, 3),
                      "combine_us": round(c_ms / c_n * 1e3, 3) if c_n else None},
-        "parity": {"rows": len(rows), "max_abs_err": float(err.max()), "ok": ok},
+        "parity": {"rows": len(rows), "max_abs_err": float(err.max()), "ok": ok,
+                   "oracle_s": round(t_oracle, 3), "oracle_threads": cpu_threads()},
     }
     del kv, qd, out, ws
     torch.cuda.empty_cache()
