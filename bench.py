@@ -8,6 +8,10 @@ attn_forward attends over the whole cache (decode_split + combine). K/V
 caches rotate over two copies (512 MiB together) so no step finds its
 working set in the 256 MB Infinity Cache.
 
+The prefill is measured first, so the decode's warm-up steps start on a GPU
+whose clocks are already up (timed right after start-up, the decode kernel
+measured about 1 us slower over its first few hundred launches).
+
 `value` is the decode's algorithmic KV bandwidth: the bytes attention must
 move (every visible K and V row once, plus q and out) per step time, in
 GB/s. `roofline` rates the dominant kernel, decode_split, on its own: the
@@ -660,8 +664,8 @@ def run_rope(args):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--prefill-steps", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle timing")
     ap.add_argument("--no-configs", action="store_true",
@@ -674,8 +678,9 @@ def main():
     if args.steps < 1 or args.warmup < 0 or args.prefill_steps < 1:
         ap.error("--steps and --prefill-steps must be >= 1 and --warmup >= 0")
     import workloads
+    prefill = run_config(workloads.LLAMA_PREFILL, args)
     rec = run_decode(args)
-    rec["prefill"] = run_config(workloads.LLAMA_PREFILL, args)
+    rec["prefill"] = prefill
     rec["rope"] = run_rope(args)
     if not args.no_configs:
         # The other workloads, each on its own plan (decode-shaped ones over 4
