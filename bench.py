@@ -2,9 +2,10 @@
 """Benchmark of the attention op's hot path on one MI355X.
 
 One step is one decode step of the Llama-3-8B-shaped GQA workload (T=1,
-S=32768, heads 32, kvHeads 8, headDim 128, causal, posOffset 32767): two
-cache_write calls append the new K and V rows at row 32767, then
-attn_forward attends over the whole cache (decode_split + combine). K/V
+S=32768, heads 32, kvHeads 8, headDim 128, causal, posOffset 32767): the
+new K and V rows are appended at row 32767 (two cache_write ops in one
+launch, attn_cache_write2), then attn_forward attends over the whole cache
+(decode_split + combine). K/V
 caches rotate over two copies (512 MiB together) so no step finds its
 working set in the 256 MB Infinity Cache.
 
@@ -201,15 +202,13 @@ def run_decode(args):
 
     steps = []
     for b in range(n_buf):
-        steps.append((ga.prepare_cache_write(kc[b], new_k, w.S - 1),
-                      ga.prepare_cache_write(vc[b], new_v, w.S - 1),
+        steps.append((ga.prepare_cache_write2(kc[b], new_k, vc[b], new_v, w.S - 1),
                       ga.prepare_forward(qd, kc[b], vc[b], out=out, workspace=ws, **params)))
 
     def step(i):
-        a, b, c = steps[i % n_buf]
-        a()
-        b()
-        c()
+        append, attend = steps[i % n_buf]
+        append()
+        attend()
 
     for i in range(args.warmup):
         step(i)
@@ -289,7 +288,7 @@ def run_decode(args):
         "config": {"workload": w.name, "T": w.T, "S": w.S, "heads": w.heads, "kvHeads": w.G,
                    "headDim": w.headDim, "vHeadDim": w.Dv, "posOffset": w.posOffset,
                    "causal": True, "kv_buffers": n_buf, "splits": plan["splits"],
-                   "step": "2x cache_write (new K/V row) + attn_forward"},
+                   "step": "cache_write of the new K and V rows (attn_cache_write2, one launch) + attn_forward"},
         "roofline": roofline,
         "cpu_baseline": cpu_baseline,
         "parity": {"max_abs_err": float(err.max()), "ok": parity_ok},

@@ -25,7 +25,7 @@ ROPE_SCALING = {"default": ATTN_ROPE_DEFAULT, "linear": ATTN_ROPE_LINEAR, "llama
 # Every symbol include/attn.h declares.
 EXPORTS = (
     "attn_params_init", "attn_validate", "attn_workspace_size", "attn_forward",
-    "attn_cache_write", "attn_last_error", "attn_plan", "attn_set_option",
+    "attn_cache_write", "attn_cache_write2", "attn_last_error", "attn_plan", "attn_set_option",
     "attn_timing_enable", "attn_timing_collect",
     "attn_rope_params_init", "attn_rope_table", "attn_rope", "attn_rope_cache_write",
     "attn_mla_params_init", "attn_mla_validate", "attn_mla_workspace_size", "attn_mla_plan",
@@ -121,6 +121,9 @@ def lib():
     L.attn_cache_write.argtypes = [vp, ctypes.c_int64, ctypes.c_int64, vp, ctypes.c_int64,
                                    ctypes.c_int64, vp]
     L.attn_cache_write.restype = ctypes.c_int
+    L.attn_cache_write2.argtypes = [vp, ctypes.c_int64, ctypes.c_int64, vp, vp, ctypes.c_int64, ctypes.c_int64,
+                                    vp, ctypes.c_int64, ctypes.c_int64, vp]
+    L.attn_cache_write2.restype = ctypes.c_int
     L.attn_last_error.argtypes = []
     L.attn_last_error.restype = ctypes.c_char_p
     L.attn_plan.argtypes = [P, ctypes.POINTER(AttnPlanInfo)]

@@ -405,6 +405,43 @@ def attn_cache_write(cache, values, offset: int, *, stream=None):
     return cache
 
 
+def _cache_write2_args(cache_a, values_a, cache_b, values_b, offset, stream):
+    for t, n in ((cache_a, "cache_a"), (values_a, "values_a"), (cache_b, "cache_b"), (values_b, "values_b")):
+        _dev_tensor(t, n)
+    for c, v in ((cache_a, values_a), (cache_b, values_b)):
+        if c.dim() != 2 or v.dim() != 2 or c.shape[1] != v.shape[1]:
+            raise ValueError("each cache [maxRows, width] and its values [rows, width] must share width")
+    if values_a.shape[0] != values_b.shape[0]:
+        raise ValueError("values_a and values_b must hold the same number of rows")
+    return (ctypes.c_void_p(cache_a.data_ptr()), ctypes.c_int64(cache_a.shape[0]), ctypes.c_int64(cache_a.shape[1]),
+            ctypes.c_void_p(values_a.data_ptr()),
+            ctypes.c_void_p(cache_b.data_ptr()), ctypes.c_int64(cache_b.shape[0]), ctypes.c_int64(cache_b.shape[1]),
+            ctypes.c_void_p(values_b.data_ptr()),
+            ctypes.c_int64(values_a.shape[0]), ctypes.c_int64(int(offset)), _stream_ptr(stream, cache_a.device))
+
+
+def attn_cache_write2(cache_a, values_a, cache_b, values_b, offset: int, *, stream=None):
+    """Two `cache_write` ops at the same rows in one launch (a decode step's new
+    K and V rows). Returns (cache_a, cache_b)."""
+    _check(_lib.lib().attn_cache_write2(*_cache_write2_args(cache_a, values_a, cache_b, values_b, offset, stream)))
+    return cache_a, cache_b
+
+
+def prepare_cache_write2(cache_a, values_a, cache_b, values_b, offset: int, *, stream=None):
+    """Like prepare_forward, for attn_cache_write2."""
+    args = _cache_write2_args(cache_a, values_a, cache_b, values_b, offset, stream)
+    fn = _lib.lib().attn_cache_write2
+    held = (cache_a, values_a, cache_b, values_b)
+
+    def call():
+        rc = fn(*args)
+        if rc != _lib.ATTN_OK:
+            raise AttnError(rc, attn_last_error())
+
+    call.held = held
+    return call
+
+
 # -- op `rope` -------------------------------------------------------------------
 
 def attn_rope_table(rows: int = 1, **rope):

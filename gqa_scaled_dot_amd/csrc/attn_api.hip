@@ -872,6 +872,28 @@ int mla_make_plan(const MlaResolved& r, MlaPlanFull* out) {
     return ok();
 }
 
+// The checks of op `cache_write` on one cache; *dst = the first row written
+// (left NULL when rows == 0). `which` prefixes the messages ("" or "a: ").
+int check_cache_write(const char* which, float* cache, int64_t max_rows, int64_t width, const float* values,
+                      int64_t rows, int64_t offset, float** dst) {
+    *dst = nullptr;
+    if (max_rows < 0) return fail(ATTN_ERR_INVALID, "%smaxRows: must be >= 0", which);
+    if (width <= 0) return fail(ATTN_ERR_INVALID, "%swidth: must be > 0", which);
+    if (rows < 0) return fail(ATTN_ERR_INVALID, "rows: must be >= 0");
+    if (offset < 0) return fail(ATTN_ERR_INVALID, "offset: must be >= 0 (got %lld)", (long long)offset);
+    if (offset > max_rows || rows > max_rows - offset)
+        return fail(ATTN_ERR_INVALID, "%soffset: rows %lld..%lld run past the cache's %lld rows", which,
+                    (long long)offset, (long long)(offset + rows), (long long)max_rows);
+    if ((double)max_rows * (double)width > 1e17) return fail(ATTN_ERR_INVALID, "%scache: too large", which);
+    if (rows == 0) return ok();
+    if (!cache) return fail(ATTN_ERR_INVALID, "%scache: NULL pointer", which);
+    if (!values) return fail(ATTN_ERR_INVALID, "%svalues: NULL pointer", which);
+    *dst = cache + offset * width;
+    const size_t n = sizeof(float) * (size_t)(rows * width);
+    if (overlaps(*dst, n, values, n)) return fail(ATTN_ERR_INVALID, "%svalues: overlap the rows being written", which);
+    return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -1014,23 +1036,33 @@ int attn_forward(const attn_params* p, const float* q, const float* k, const flo
 
 int attn_cache_write(float* cache, int64_t max_rows, int64_t width, const float* values,
                      int64_t rows, int64_t offset, void* stream) {
-    if (max_rows < 0) return fail(ATTN_ERR_INVALID, "maxRows: must be >= 0");
-    if (width <= 0) return fail(ATTN_ERR_INVALID, "width: must be > 0");
-    if (rows < 0) return fail(ATTN_ERR_INVALID, "rows: must be >= 0");
-    if (offset < 0) return fail(ATTN_ERR_INVALID, "offset: must be >= 0 (got %lld)", (long long)offset);
-    if (offset > max_rows || rows > max_rows - offset)
-        return fail(ATTN_ERR_INVALID, "offset: rows %lld..%lld run past the cache's %lld rows",
-                    (long long)offset, (long long)(offset + rows), (long long)max_rows);
-    if ((double)max_rows * (double)width > 1e17) return fail(ATTN_ERR_INVALID, "cache: too large");
-    if (rows == 0) return ok();
-    if (!cache) return fail(ATTN_ERR_INVALID, "cache: NULL pointer");
-    if (!values) return fail(ATTN_ERR_INVALID, "values: NULL pointer");
-    float* dst = cache + offset * width;
-    const size_t n = sizeof(float) * (size_t)(rows * width);
-    if (overlaps(dst, n, values, n)) return fail(ATTN_ERR_INVALID, "values: overlap the rows being written");
+    float* dst = nullptr;
+    const int rc = check_cache_write("", cache, max_rows, width, values, rows, offset, &dst);
+    if (rc || rows == 0) return rc;
     hipStream_t s = (hipStream_t)stream;
     const hipError_t err = timed("cache_write", s, [&](const attn::Launch& L) {
         return attn::launch_cache_write(dst, values, rows * width, L);
+    });
+    if (err != hipSuccess) return fail(ATTN_ERR_DEVICE, "launch: %s", hipGetErrorString(err));
+    return ok();
+}
+
+int attn_cache_write2(float* cache_a, int64_t max_rows_a, int64_t width_a, const float* values_a,
+                      float* cache_b, int64_t max_rows_b, int64_t width_b, const float* values_b,
+                      int64_t rows, int64_t offset, void* stream) {
+    float *dst_a = nullptr, *dst_b = nullptr;
+    int rc = check_cache_write("a: ", cache_a, max_rows_a, width_a, values_a, rows, offset, &dst_a);
+    if (rc) return rc;
+    rc = check_cache_write("b: ", cache_b, max_rows_b, width_b, values_b, rows, offset, &dst_b);
+    if (rc || rows == 0) return rc;
+    // The two copies run side by side: neither may write what the other
+    // reads or writes.
+    const size_t na = sizeof(float) * (size_t)(rows * width_a), nb = sizeof(float) * (size_t)(rows * width_b);
+    if (overlaps(dst_a, na, dst_b, nb)) return fail(ATTN_ERR_INVALID, "b: rows overlap the rows a writes");
+    if (overlaps(dst_a, na, values_b, nb)) return fail(ATTN_ERR_INVALID, "b: values overlap the rows a writes");
+    if (overlaps(dst_b, nb, values_a, na)) return fail(ATTN_ERR_INVALID, "a: values overlap the rows b writes");
+    const hipError_t err = timed("cache_write", (hipStream_t)stream, [&](const attn::Launch& L) {
+        return attn::launch_cache_write_pair(dst_a, values_a, rows * width_a, dst_b, values_b, rows * width_b, L);
     });
     if (err != hipSuccess) return fail(ATTN_ERR_DEVICE, "launch: %s", hipGetErrorString(err));
     return ok();

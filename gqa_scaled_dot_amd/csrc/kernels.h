@@ -149,6 +149,9 @@ struct MlaPlan {
 
 // Launchers. Each returns hipSuccess or the launch error.
 hipError_t launch_cache_write(float* dst, const float* src, int64_t count, const Launch& L);
+// Two flat copies (count_a and count_b floats, both > 0) in one launch.
+hipError_t launch_cache_write_pair(float* dst_a, const float* src_a, int64_t count_a, float* dst_b,
+                                   const float* src_b, int64_t count_b, const Launch& L);
 // out rows = rope(x rows): rows x heads heads of D floats each; out may equal x.
 hipError_t launch_rope(const RopeArgs& ra, const float* x, float* out, int64_t rows, int heads, int D,
                        const Launch& L);

@@ -201,6 +201,18 @@ int attn_cache_write(float* cache, int64_t max_rows, int64_t width, const float*
                      int64_t rows, int64_t offset, void* stream);
 
 /*
+ * Two `cache_write` ops at the same rows in one launch, as a decode step
+ * appends its new K and V rows: cache_a[offset + r, :] = values_a[r, :] and
+ * cache_b[offset + r, :] = values_b[r, :] for r < rows. Each cache takes
+ * attn_cache_write's checks (messages prefixed "a: " / "b: "); in addition
+ * neither copy may write rows the other one reads or writes. Same result,
+ * bit for bit, as the two attn_cache_write calls. rows = 0 is a no-op.
+ */
+int attn_cache_write2(float* cache_a, int64_t max_rows_a, int64_t width_a, const float* values_a,
+                      float* cache_b, int64_t max_rows_b, int64_t width_b, const float* values_b,
+                      int64_t rows, int64_t offset, void* stream);
+
+/*
  * Op `rope` (graph protocol op catalogue: "Rotary position embedding over
  * [tokens, heads*headDim]"; params headDim, base, offset, rotaryDim,
  * interleaved, scaling, invFreq, attentionFactor; features rope.interleaved,

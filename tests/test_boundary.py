@@ -22,7 +22,7 @@ HEADER = os.path.join(ROOT, "include", "attn.h")
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    names = set(re.findall(r"\b(attn_[a-z_]+)\s*\(", text))
+    names = set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text))
     return sorted(names)
 
 
@@ -213,6 +213,34 @@ def test_cache_write_refuses_before_launch():
     assert L.attn_cache_write(A, 10, 4, A + 16, 2, 1, None) == 1
     assert "overlap" in ga.attn_last_error()
     assert L.attn_cache_write(A, 10, 4, 2 * A, 0, 10, None) == 0  # rows = 0: no-op
+
+
+def test_cache_write2_refuses_before_launch():
+    # Each cache's own checks (named "a: " / "b: "), then the cross checks:
+    # neither copy may write rows the other reads or writes. Fake addresses:
+    # nothing runs before the checks pass.
+    L = _lib.lib()
+    A, B = 1 << 20, 1 << 24
+    ok = (A, 10, 4, 2 * A, B, 10, 6, 2 * B)
+    assert L.attn_cache_write2(*ok, 0, 3, None) == 0  # rows = 0: no-op
+    assert L.attn_cache_write2(A, 10, 4, 2 * A, B, 10, 6, 2 * B, 3, 8, None) == 1
+    assert ga.attn_last_error().startswith("a: offset")
+    assert L.attn_cache_write2(A, 10, 4, 2 * A, B, 4, 6, 2 * B, 2, 3, None) == 1
+    assert ga.attn_last_error().startswith("b: offset")
+    assert L.attn_cache_write2(A, 10, 4, 2 * A, B, 10, 0, 2 * B, 1, 0, None) == 1
+    assert ga.attn_last_error().startswith("b: width")
+    assert L.attn_cache_write2(A, 10, 4, 2 * A, None, 10, 6, 2 * B, 1, 0, None) == 1
+    assert ga.attn_last_error().startswith("b: cache")
+    assert L.attn_cache_write2(A, 10, 4, A + 16, B, 10, 6, 2 * B, 2, 1, None) == 1
+    assert ga.attn_last_error().startswith("a: values")
+    # b writes rows 1..2 of a cache that starts 16 bytes into a's row 1.
+    assert L.attn_cache_write2(A, 10, 4, 2 * A, A + 16, 10, 4, 2 * B, 2, 1, None) == 1
+    assert "overlap the rows a writes" in ga.attn_last_error()
+    # b reads values that a is writing.
+    assert L.attn_cache_write2(A, 10, 4, 2 * A, B, 10, 6, A + 16, 2, 1, None) == 1
+    assert "b: values overlap the rows a writes" in ga.attn_last_error()
+    assert L.attn_cache_write2(A, 10, 4, B + 48, B, 10, 6, 2 * B, 2, 1, None) == 1
+    assert "a: values overlap the rows b writes" in ga.attn_last_error()
 
 
 def test_binding_refuses_cpu_tensors():

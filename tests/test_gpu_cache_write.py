@@ -81,3 +81,66 @@ def test_cache_write_refuses_out_of_range():
         ga.attn_cache_write(cache, vals, 3)
     torch().cuda.synchronize()
     assert np.all(cache.cpu().numpy() == 1.0)
+
+
+@pytest.mark.parametrize("wa, wb", [(1024, 1024), (3072, 2048), (1023, 5), (12, 4096), (1, 3)])
+@pytest.mark.parametrize("rows, offset", [(1, 0), (1, 99), (7, 40), (64, 36)])
+def test_cache_write2_equals_two_cache_writes(wa, wb, rows, offset):
+    # K and V rows in one launch: each cache ends up bit for bit as one
+    # attn_cache_write leaves it, every other row untouched.
+    import gqa_scaled_dot_amd as ga
+    max_rows = 100
+    ca = dev(workloads.normal((max_rows, wa), 11, 1))
+    cb = dev(workloads.normal((max_rows, wb), 11, 2))
+    before_a, before_b = _bits(ca), _bits(cb)
+    va_np = workloads.normal((rows, wa), 11, 3)
+    vb_np = workloads.normal((rows, wb), 11, 4)
+    va_np[0, 0] = np.float32(np.nan)
+    vb_np[-1, -1] = np.float32(-0.0)
+    ra, rb = ga.attn_cache_write2(ca, dev(va_np), cb, dev(vb_np), offset)
+    torch().cuda.synchronize()
+    assert ra is ca and rb is cb
+    for after, before, v in ((_bits(ca), before_a, va_np), (_bits(cb), before_b, vb_np)):
+        np.testing.assert_array_equal(after[offset:offset + rows], v.view(np.uint32))
+        np.testing.assert_array_equal(after[:offset], before[:offset])
+        np.testing.assert_array_equal(after[offset + rows:], before[offset + rows:])
+
+
+@pytest.mark.parametrize("shift_a, shift_b", [(0, 1), (3, 0), (2, 2), (1, 3)])
+def test_cache_write2_misaligned_sources(shift_a, shift_b):
+    # Sources off the destinations' 16-byte phase take the 32-bit copy; each
+    # copy picks its own.
+    import gqa_scaled_dot_amd as ga
+    rows, offset, wa, wb = 5, 13, 257, 130
+    ca = dev(np.zeros((30, wa), np.float32))
+    cb = dev(np.zeros((30, wb), np.float32))
+    pa_np = workloads.normal((rows * wa + 8,), 5, 1)
+    pb_np = workloads.normal((rows * wb + 8,), 5, 2)
+    pa, pb = dev(pa_np), dev(pb_np)
+    va = pa[shift_a:shift_a + rows * wa].view(rows, wa)
+    vb = pb[shift_b:shift_b + rows * wb].view(rows, wb)
+    ga.attn_cache_write2(ca, va, cb, vb, offset)
+    torch().cuda.synchronize()
+    for got, p_np, w, sh in ((_bits(ca), pa_np, wa, shift_a), (_bits(cb), pb_np, wb, shift_b)):
+        want = p_np[sh:sh + rows * w].reshape(rows, w).view(np.uint32)
+        np.testing.assert_array_equal(got[offset:offset + rows], want)
+        assert not got[:offset].any() and not got[offset + rows:].any()
+
+
+def test_cache_write2_decode_append_then_attend():
+    # The decode step's append: the new K and V rows at 32767 of the
+    # Llama-shaped caches, then attention over them, against the oracle.
+    import gqa_scaled_dot_amd as ga
+    import oracle
+    from tests.parity import assert_close
+    t = torch()
+    w = workloads.LLAMA_DECODE
+    q, k, v, _ = w.tensors()
+    kc = t.full(k.shape, float("nan"), dtype=t.float32, device="cuda")
+    vc = t.full(v.shape, float("nan"), dtype=t.float32, device="cuda")
+    kd, vd = dev(k), dev(v)
+    ga.attn_cache_write2(kc, kd[:-1], vc, vd[:-1], 0)
+    ga.attn_cache_write2(kc, kd[-1:], vc, vd[-1:], w.S - 1)
+    got = ga.attn_forward(dev(q), kc, vc, **w.params())
+    t.cuda.synchronize()
+    assert_close(got.cpu().numpy(), oracle.attention(q, k, v, **w.params()), "cache_write2 then decode")
