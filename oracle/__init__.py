@@ -30,7 +30,9 @@ protocol op catalogue, op `attention`, params):
   scale and softcap.
 
 Readings where the pages are silent are listed in the module docstrings of
-`oracle.alibi` and in the core's header comment.
+`oracle.alibi` and in the core's header comment. Parity unpinned: a row with
+no visible key gives 0, and non-causal ALiBi uses -slope * |pos - s|; both
+are readings that no page fact can confirm.
 """
 
 from __future__ import annotations

@@ -42,6 +42,13 @@
  *     embedding rel_k[r] is added to k before the product with q (so it is
  *     scaled with it) and rel_v[r] to v in the weighted sum.
  *
+ * Parity unpinned (readings, not facts the pages fix, so nothing outside
+ * this definition can confirm them): the zero output of a row with no
+ * visible key, and the ALiBi term's symmetric form -slope * |pos - s| on
+ * non-causal rows (on causal rows it differs from BLOOM's slope * s and
+ * MPT's slope * (s - (S - 1)) only by a per-row constant, which the softmax
+ * removes; the pins check that).
+ *
  * The resolution of absent parameters (defaults, slope tables) happens in the
  * Python wrapper beside this file; this core takes resolved numbers.
  * Every input is an f32 array and is widened to f64 (exact); all arithmetic
