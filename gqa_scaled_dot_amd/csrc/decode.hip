@@ -76,8 +76,9 @@ __device__ __forceinline__ bool chunk_all_visible(const Epilogue& e, int pos_fir
 // and non-causal calls). RM > 0 implies EPI.
 // EPI: whether softcap, ALiBi or a bias can be on; without them the score
 // is the scaled dot product and the code for the rest is left out.
-// DEPTH: batches of U rows per row group held in registers as a ring; DEPTH-1
-// of them are in flight while one is used.
+// DEPTH: batches of U rows per row group held in registers. 1 (the default):
+// one batch at a time, the next fetched once the current one is used; 2 or
+// 3: a ring, DEPTH-1 batches in flight while one is used.
 template <int D, int DV, int NQ, bool EPI, int RM, int DEPTH>
 __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, DecodePlan plan,
                                                                    float* __restrict__ ws) {
@@ -201,17 +202,17 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
     // walk's or the range's end need checking.
     const bool dense = chunk_all_visible(p.ep, p.ep.pos_offset, p.ep.pos_offset + (int)p.T - 1, k0, k1);
     // Relative key/value embeddings: every row's products with every key
-    // embedding go to LDS once q is in registers. A chunk whose keys all lie
+    // embedding go to LDS once q is in registers. A split whose keys all lie
     // max_distance or more before the first row's position uses embedding 0
     // alone: a per-row constant in the scores and l * rel_v[0] in the sums.
     const bool rel = REL && p.ep.rel_k != nullptr;
     const int nrel = rel ? 2 * p.ep.rel_max + 1 : 0;
     const bool rel_far = rel && k1 - 1 <= p.ep.pos_offset - p.ep.rel_max;
-    // Likewise a chunk whose keys all lie at least the last threshold before
+    // Likewise a split whose keys all lie at least the last threshold before
     // the first row takes the last bucket's bias for every key: one number per row.
     const bool pb = REL && p.ep.pb_weight != nullptr;
     const bool pb_far = pb && k1 - 1 <= p.ep.pos_offset - p.ep.pb_dt;
-    // FAR instances run far splits through the batched ring with those
+    // FAR instances run far splits through the batched walk with those
     // constants, and a split of keys near the rows through a plain loop, one
     // key per row group at a time, with every term looked up per key.
     const bool split_far = (!pb || pb_far) && (!rel || rel_far);
@@ -366,8 +367,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
     };
 
     {
-        // Ring of DEPTH batches: batch i of a round is used while batches
-        // i+1 .. i+DEPTH-1 are in flight.
+        // DEPTH batch slots: one (a batch at a time) or a ring in which
+        // batch i of a round is used while batches i+1 .. i+DEPTH-1 are in
+        // flight.
         float4 kr[DEPTH][U][KJ], vr[DEPTH][U][VJ];
         float br[DEPTH][BR][U];
         // In a ring (DEPTH >= 2) with the epilogue on, batches are prefetched
@@ -553,7 +555,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
     }
 
     if constexpr (REL) {
-        // A far chunk's keys all take rel_v[0]: add it once, weighted by l.
+        // A far split's keys all take rel_v[0]: add it once, weighted by l.
         if (rel_far && p.ep.rel_v) {
 #pragma unroll
             for (int r = 0; r < NQ; ++r)
@@ -759,7 +761,7 @@ hipError_t launch_split_d(const Problem& p, const DecodePlan& plan, float* ws, c
     const uint32_t lds = p.ep.rel_k ? (uint32_t)(sizeof(float) * NQ * (2 * p.ep.rel_max + 1)) : 0u;
     if (p.ep.pb_weight || p.ep.rel_k) {
         // Causal calls with a split of near keys: the far instance (batched
-        // ring for far splits, plain loop for the near one); otherwise every
+        // walk for far splits, plain loop for the near one); otherwise every
         // split looks its terms up per key.
         const uint32_t lds_all = lds + (p.ep.pb_weight ? (uint32_t)((p.ep.pb_dt + 3) & ~3) : 0u);
         if (plan.near_hi > plan.near_lo)
