@@ -683,24 +683,52 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(Problem p, int
     const float* ml = ws + (int64_t)p.T * p.H * nsplit * DV + th * nsplit * 2;
     float4* orow = reinterpret_cast<float4*>(p.out + th * DV);
 
+    // Every load is requested before any reduction: this thread's first
+    // kPre accumulator float4s and its splits' (max, sum) pairs.
+    const int e4 = tid % E4, grp = tid / E4;
+    constexpr int kPre = 64 / kGroups > 0 ? 64 / kGroups : 1;  // covers 64 splits
+    float4 pre[kPre];
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) {
+        const int i = grp + u * kGroups;
+        pre[u] = i < nsplit ? acc4[(int64_t)i * E4 + e4] : zero4();
+    }
+    float2 mlv[kMaxSplits / kThreads];
+#pragma unroll
+    for (int u = 0; u < kMaxSplits / kThreads; ++u) {
+        const int i = tid + u * kThreads;
+        mlv[u] = i < nsplit ? *reinterpret_cast<const float2*>(ml + 2 * i) : make_float2(-INFINITY, 0.0f);
+    }
+
     float m = -INFINITY;
-    for (int i = tid; i < nsplit; i += kThreads) m = fmaxf(m, ml[2 * i]);
+#pragma unroll
+    for (int u = 0; u < kMaxSplits / kThreads; ++u) m = fmaxf(m, mlv[u].x);
     const float M = block_max(m, s_red);
     if (M == -INFINITY) {  // no visible key in any split
         for (int e = tid; e < E4; e += kThreads) orow[e] = zero4();
         return;
     }
     float lsum = 0.0f;
-    for (int i = tid; i < nsplit; i += kThreads) {
-        const float w = fast_exp2(ml[2 * i] - M);
-        s_w[i] = w;
-        lsum += ml[2 * i + 1] * w;
+#pragma unroll
+    for (int u = 0; u < kMaxSplits / kThreads; ++u) {
+        const int i = tid + u * kThreads;
+        if (i < nsplit) {
+            const float w = fast_exp2(mlv[u].x - M);
+            s_w[i] = w;
+            lsum += mlv[u].y * w;
+        }
     }
     const float L = block_sum(lsum, s_red);  // ends with a barrier, so s_w is complete
 
-    const int e4 = tid % E4, grp = tid / E4;
     float4 a = zero4();
-    for (int i = grp; i < nsplit; i += kGroups) {
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) {
+        const int i = grp + u * kGroups;
+        const float w = i < nsplit ? s_w[i] : 0.0f;
+        a.x = fmaf(pre[u].x, w, a.x); a.y = fmaf(pre[u].y, w, a.y);
+        a.z = fmaf(pre[u].z, w, a.z); a.w = fmaf(pre[u].w, w, a.w);
+    }
+    for (int i = grp + kPre * kGroups; i < nsplit; i += kGroups) {
         const float w = s_w[i];
         const float4 c = acc4[(int64_t)i * E4 + e4];
         a.x = fmaf(c.x, w, a.x); a.y = fmaf(c.y, w, a.y);
