@@ -3,9 +3,11 @@
 
 One step is one decode step of the Llama-3-8B-shaped GQA workload (T=1,
 S=32768, heads 32, kvHeads 8, headDim 128, causal, posOffset 32767): the
-new K and V rows are appended at row 32767 (two cache_write ops in one
-launch, attn_cache_write2), then attn_forward attends over the whole cache
-(decode_split + combine). K/V
+new K and V rows are appended at row 32767 and attention runs over the
+whole cache, in one call (attn_forward_append: decode_split reads the new
+rows from their buffers, stores them into the caches and attends over them
+with the rest; then combine). The same step made of separate calls
+(attn_cache_write2, then attn_forward) is timed too. K/V
 caches rotate over two copies (512 MiB together) so no step finds its
 working set in the 256 MB Infinity Cache.
 
@@ -200,13 +202,16 @@ def run_decode(args):
     out = torch.empty((w.T, w.heads * w.Dv), dtype=torch.float32, device=dev)
     ws = torch.empty(max(ga.attn_workspace_size(w.T, w.S, **params), 256), dtype=torch.uint8, device=dev)
 
-    steps = []
-    for b in range(n_buf):
-        steps.append((ga.prepare_cache_write2(kc[b], new_k, vc[b], new_v, w.S - 1),
-                      ga.prepare_forward(qd, kc[b], vc[b], out=out, workspace=ws, **params)))
+    steps = [ga.prepare_forward_append(qd, kc[b], vc[b], new_k, new_v, w.S - 1, out=out, workspace=ws, **params)
+             for b in range(n_buf)]
+    separate = [(ga.prepare_cache_write2(kc[b], new_k, vc[b], new_v, w.S - 1),
+                 ga.prepare_forward(qd, kc[b], vc[b], out=out, workspace=ws, **params)) for b in range(n_buf)]
 
     def step(i):
-        append, attend = steps[i % n_buf]
+        steps[i % n_buf]()
+
+    def step_separate(i):
+        append, attend = separate[i % n_buf]
         append()
         attend()
 
@@ -241,7 +246,21 @@ def run_decode(args):
     e1.record(stream)
     torch.cuda.synchronize()
     ms_per_step = e0.elapsed_time(e1) / args.steps
-    log(f"[bench] step {ms_per_step * 1e3:.2f} us (with kernel events {ms_timed * 1e3:.2f} us); "
+    # The same step as separate calls, for comparison (after its own warm-up).
+    for i in range(args.warmup):
+        step_separate(i)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
+        step_separate(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_separate = e0.elapsed_time(e1) / args.steps
+    for i in range(2):  # leave `out` as the fused step computes it
+        step(i)
+    torch.cuda.synchronize()
+    log(f"[bench] step {ms_per_step * 1e3:.2f} us (with kernel events {ms_timed * 1e3:.2f} us; "
+        f"as separate calls {ms_separate * 1e3:.2f} us); "
         f"decode_split {split_ms / max(split_n, 1) * 1e3:.2f} us x{split_n}, "
         f"combine {comb_ms / max(comb_n, 1) * 1e3:.2f} us x{comb_n}, "
         f"cache_write {cw_ms / max(cw_n, 1) * 1e3:.2f} us x{cw_n}")
@@ -288,7 +307,9 @@ def run_decode(args):
         "config": {"workload": w.name, "T": w.T, "S": w.S, "heads": w.heads, "kvHeads": w.G,
                    "headDim": w.headDim, "vHeadDim": w.Dv, "posOffset": w.posOffset,
                    "causal": True, "kv_buffers": n_buf, "splits": plan["splits"],
-                   "step": "cache_write of the new K and V rows (attn_cache_write2, one launch) + attn_forward"},
+                   "step": "attn_forward_append: the new K and V rows written and attended in decode_split "
+                           "(one more split per KV head), then combine"},
+        "ms_per_step_separate_calls": round(ms_separate, 6),
         "roofline": roofline,
         "cpu_baseline": cpu_baseline,
         "parity": {"max_abs_err": float(err.max()), "ok": parity_ok},

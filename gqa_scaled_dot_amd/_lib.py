@@ -25,8 +25,8 @@ ROPE_SCALING = {"default": ATTN_ROPE_DEFAULT, "linear": ATTN_ROPE_LINEAR, "llama
 # Every symbol include/attn.h declares.
 EXPORTS = (
     "attn_params_init", "attn_validate", "attn_workspace_size", "attn_forward",
-    "attn_cache_write", "attn_cache_write2", "attn_last_error", "attn_plan", "attn_set_option",
-    "attn_timing_enable", "attn_timing_collect",
+    "attn_forward_append", "attn_cache_write", "attn_cache_write2", "attn_last_error", "attn_plan",
+    "attn_set_option", "attn_timing_enable", "attn_timing_collect",
     "attn_rope_params_init", "attn_rope_table", "attn_rope", "attn_rope_cache_write",
     "attn_mla_params_init", "attn_mla_validate", "attn_mla_workspace_size", "attn_mla_plan",
     "attn_mla_forward",
@@ -118,6 +118,9 @@ def lib():
     L.attn_workspace_size.restype = ctypes.c_size_t
     L.attn_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     L.attn_forward.restype = ctypes.c_int
+    L.attn_forward_append.argtypes = [P, vp, vp, vp, vp, vp, ctypes.c_int64, ctypes.c_int64, vp, vp, vp,
+                                      ctypes.c_size_t, vp]
+    L.attn_forward_append.restype = ctypes.c_int
     L.attn_cache_write.argtypes = [vp, ctypes.c_int64, ctypes.c_int64, vp, ctypes.c_int64,
                                    ctypes.c_int64, vp]
     L.attn_cache_write.restype = ctypes.c_int

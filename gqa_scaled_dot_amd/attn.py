@@ -371,6 +371,60 @@ def prepare_forward(q, k, v, bias=None, *, out, workspace=None, stream=None, **p
     return call
 
 
+def _forward_append_args(q, k, v, k_new, v_new, offset, bias, out, workspace, stream, params):
+    torch = _torch()
+    T, S, H, Dv, bias_kind = _check_forward(q, k, v, bias, out, params)
+    _dev_tensor(k_new, "k_new")
+    _dev_tensor(v_new, "v_new")
+    if k_new.dim() != 2 or k_new.shape[1] != k.shape[1]:
+        raise ValueError(f"k_new: {tuple(k_new.shape)} is not [rows, kvHeads*headDim = {k.shape[1]}]")
+    if tuple(v_new.shape) != (k_new.shape[0], v.shape[1]):
+        raise ValueError(f"v_new: {tuple(v_new.shape)} is not [rows = {k_new.shape[0]}, {v.shape[1]}]")
+    p, keep = make_params(T, S, bias_kind=bias_kind, **params)
+    L = _lib.lib()
+    if out is None:
+        out = torch.empty((T, H * Dv), dtype=torch.float32, device=q.device)
+    need = int(L.attn_workspace_size(ctypes.byref(p)))
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = workspace_for(need, q.device)
+    args = (ctypes.byref(p), ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
+            ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(k_new.data_ptr()),
+            ctypes.c_void_p(v_new.data_ptr()), ctypes.c_int64(k_new.shape[0]), ctypes.c_int64(int(offset)),
+            ctypes.c_void_p(bias.data_ptr() if bias is not None else None),
+            ctypes.c_void_p(out.data_ptr()),
+            ctypes.c_void_p(workspace.data_ptr() if workspace is not None else None),
+            ctypes.c_size_t(workspace.numel() * workspace.element_size() if workspace is not None else 0),
+            _stream_ptr(stream, q.device))
+    return args, (p, keep, q, k, v, k_new, v_new, bias, out, workspace), out
+
+
+def attn_forward_append(q, k, v, k_new, v_new, offset: int, bias=None, *, out=None, workspace=None,
+                        stream=None, **params):
+    """A decode step in one call: rows [offset, offset + rows) of the caches k
+    and v become k_new and v_new [rows, ...] (op `cache_write`), then op
+    `attention` of q over the caches. Returns out [T, heads*vHeadDim]."""
+    args, held, out = _forward_append_args(q, k, v, k_new, v_new, offset, bias, out, workspace, stream, params)
+    rc = _lib.lib().attn_forward_append(*args)
+    del held
+    _check(rc)
+    return out
+
+
+def prepare_forward_append(q, k, v, k_new, v_new, offset: int, bias=None, *, out, workspace=None, stream=None,
+                           **params):
+    """Like prepare_forward, for attn_forward_append."""
+    args, held, _ = _forward_append_args(q, k, v, k_new, v_new, offset, bias, out, workspace, stream, params)
+    fn = _lib.lib().attn_forward_append
+
+    def call():
+        rc = fn(*args)
+        if rc != _lib.ATTN_OK:
+            raise AttnError(rc, attn_last_error())
+
+    call.held = held
+    return call
+
+
 def prepare_cache_write(cache, values, offset: int, *, stream=None):
     """Like prepare_forward, for attn_cache_write."""
     _dev_tensor(cache, "cache")

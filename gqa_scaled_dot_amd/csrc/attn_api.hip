@@ -59,6 +59,7 @@ constexpr int64_t kDecodeMinKeys = 64;
 constexpr int64_t kDecodeChunkAlign = 64; // key chunk granularity (a multiple of 16 row groups x 2 rows)
 constexpr int64_t kDecodeBlock = 256;     // rows per interleaved block, automatic choice (power of two)
 constexpr int64_t kDecodeMaxSplits = 1024;
+constexpr int64_t kDecodeMaxAppend = 64;  // appended rows one decode split takes (two batch steps)
 constexpr int64_t kPrefillMaxSplits = 16;
 constexpr int64_t kPrefillMinTilesPerSplit = 4;
 constexpr int64_t kMaxDim = 1 << 16;
@@ -500,10 +501,20 @@ struct Plan {
     int path;
     attn::DecodePlan decode;
     attn::PrefillPlan prefill;
-    size_t workspace;
+    size_t workspace;  // bytes this plan's launches need
+    size_t reserve;    // bytes attn_workspace_size reports: enough for this call made
+                       // through attn_forward or attn_forward_append
+    bool fused;        // the decode launch also appends the call's new rows
 };
 
-int make_plan(const Resolved& r, Plan* plan) {
+// Cache rows [lo, hi) that an attn_forward_append call writes.
+struct AppendRows {
+    int64_t lo, hi;
+};
+
+// With `app`, the plan takes the appended rows into the decode launch where
+// it can (plan->fused); otherwise they are left to a separate copy.
+int make_plan(const Resolved& r, Plan* plan, const AppendRows* app = nullptr) {
     memset(plan, 0, sizeof *plan);
     plan->decode.splits = 1;
     if (r.T == 0) {
@@ -548,6 +559,17 @@ int make_plan(const Resolved& r, Plan* plan) {
         d.depth = g_opt_decode_depth ? (int32_t)g_opt_decode_depth : kDecodeDepth;
 
         d.range = kr;
+        // An appending call whose new rows end the key range, without
+        // relative-position terms: the near split takes those rows, reading
+        // them from the new-row buffers and storing them into the caches, and
+        // `range` stops below them. The rows then need no copy beforehand.
+        if (app && app->hi > app->lo && app->lo >= kr.lo && app->hi == kr.hi && !r.ep.pb_weight &&
+            !r.ep.rel_k && app->hi - app->lo <= kDecodeMaxAppend) {
+            d.near_lo = (int32_t)app->lo;
+            d.near_hi = (int32_t)app->hi;
+            d.range.hi = app->lo;
+            plan->fused = true;
+        }
         // Relative-position terms: on a causal call, keys within the tables'
         // reach of the first row (s > posOffset - reach) are looked up per
         // key; they get a split of their own, so that this slower per-key
@@ -571,7 +593,11 @@ int make_plan(const Resolved& r, Plan* plan) {
             // As many workgroups as the chip holds at once, near and sink
             // splits included, and no more: a few workgroups past that
             // would run as a second wave and nearly double the time.
-            const int64_t extra = (near ? 1 : 0) + (sink_hi > 0 ? 1 : 0);
+            // (The split of appended rows is short, and at one batch per
+            // lane every instance it runs in holds at least 3 workgroups per
+            // CU, one more than planned: it goes beside the full set.)
+            const bool light = plan->fused && d.depth == 1;
+            const int64_t extra = (near && !light ? 1 : 0) + (sink_hi > 0 ? 1 : 0);
             const int64_t per_cu = g_opt_decode_wgs ? g_opt_decode_wgs : kDecodeWgPerCU;
             const int64_t target = (int64_t)kCUs * per_cu / r.G - extra;
             const int64_t most = (n + kDecodeMinKeys - 1) / kDecodeMinKeys;
@@ -632,8 +658,14 @@ int make_plan(const Resolved& r, Plan* plan) {
         // their own each (after the splits of `range`).
         d.sink_hi = (int32_t)sink_hi;
         d.splits = d.main_splits + (near ? 1 : 0) + (sink_hi > 0 ? 1 : 0);
-        if (d.splits > 1)
-            plan->workspace = sizeof(float) * (size_t)(r.T * r.H) * (size_t)d.splits * (size_t)(r.Dv + 2);
+        const size_t per_split = sizeof(float) * (size_t)(r.T * r.H) * (size_t)(r.Dv + 2);
+        if (d.splits > 1) plan->workspace = per_split * (size_t)d.splits;
+        // The same call made through attn_forward_append may add the split of
+        // appended rows (its range loses those rows, so it has no more of
+        // the others).
+        const int32_t most_splits = d.splits + (!near && !r.ep.pb_weight && !r.ep.rel_k ? 1 : 0);
+        plan->reserve = most_splits > 1 ? per_split * (size_t)most_splits : 0;
+        if (plan->workspace > plan->reserve) plan->reserve = plan->workspace;
     }
     if (path == ATTN_PATH_PREFILL) {
         // Four waves of 32 query rows; heads of a KV group side by side
@@ -665,6 +697,7 @@ int make_plan(const Resolved& r, Plan* plan) {
         if (ks > kPrefillMaxSplits) ks = kPrefillMaxSplits;
         pp.ksplit = (int32_t)ks;
         if (ks > 1) plan->workspace = sizeof(float) * (size_t)(r.T * r.H) * (size_t)ks * (size_t)(r.Dv + 2);
+        plan->reserve = plan->workspace;
     }
     return ok();
 }
@@ -894,60 +927,12 @@ int check_cache_write(const char* which, float* cache, int64_t max_rows, int64_t
     return ok();
 }
 
-}  // namespace
 
-extern "C" {
-
-void attn_params_init(attn_params* p) {
-    if (!p) return;
-    memset(p, 0, sizeof *p);
-    p->causal = 1;
-}
-
-int attn_validate(const attn_params* p) {
-    Resolved r;
-    int rc = resolve(p, &r);
-    if (rc) return rc;
-    Plan plan;
-    return make_plan(r, &plan);
-}
-
-size_t attn_workspace_size(const attn_params* p) {
-    Resolved r;
-    if (resolve(p, &r)) return 0;
-    Plan plan;
-    if (make_plan(r, &plan)) return 0;
-    return plan.workspace;
-}
-
-int attn_plan(const attn_params* p, attn_plan_info* info) {
-    if (!info) return fail(ATTN_ERR_INVALID, "info: NULL pointer");
-    Resolved r;
-    int rc = resolve(p, &r);
-    if (rc) return rc;
-    Plan plan;
-    rc = make_plan(r, &plan);
-    if (rc) return rc;
-    info->path = plan.path;
-    info->splits = plan.path == ATTN_PATH_DECODE    ? plan.decode.splits
-                   : plan.path == ATTN_PATH_PREFILL ? plan.prefill.ksplit
-                                                    : 1;
-    info->tile_q = plan.path == ATTN_PATH_PREFILL ? plan.prefill.tile_q : 0;
-    info->reserved = 0;
-    return ok();
-}
-
-int attn_forward(const attn_params* p, const float* q, const float* k, const float* v,
-                 const float* bias, float* out, void* workspace, size_t workspace_bytes,
-                 void* stream) {
-    Resolved r;
-    int rc = resolve(p, &r);
-    if (rc) return rc;
-    Plan plan;
-    rc = make_plan(r, &plan);
-    if (rc) return rc;
-    if (plan.path == ATTN_PATH_EMPTY) return ok();
-
+// attn_forward's checks of the tensors and the workspace (`need` bytes) for
+// a valid plan.
+int check_forward_args(const attn_params* p, const Resolved& r, size_t need, const float* q, const float* k,
+                       const float* v, const float* bias, const float* out, const void* workspace,
+                       size_t workspace_bytes) {
     const size_t qn = sizeof(float) * (size_t)(r.T * r.H * r.D);
     const size_t kn = sizeof(float) * (size_t)(r.S * r.G * r.D);
     const size_t vn = sizeof(float) * (size_t)(r.S * r.G * r.Dv);
@@ -968,18 +953,22 @@ int attn_forward(const attn_params* p, const float* q, const float* k, const flo
         overlaps(out, on, p->rel_k, p->rel_k ? sizeof(float) * (size_t)((2 * p->rel_max + 1) * r.D) : 0) ||
         overlaps(out, on, p->rel_v, p->rel_v ? sizeof(float) * (size_t)((2 * p->rel_max + 1) * r.Dv) : 0))
         return fail(ATTN_ERR_INVALID, "out: overlaps an input");
-    if (plan.workspace) {
-        if (!workspace || workspace_bytes < plan.workspace)
-            return fail(ATTN_ERR_INVALID, "workspace: %zu bytes needed, %zu given", plan.workspace,
+    if (need) {
+        if (!workspace || workspace_bytes < need)
+            return fail(ATTN_ERR_INVALID, "workspace: %zu bytes needed, %zu given", need,
                         workspace ? workspace_bytes : (size_t)0);
         if (((uintptr_t)workspace & 255u) != 0)
             return fail(ATTN_ERR_INVALID, "workspace: must be 256-byte aligned");
-        if (overlaps(workspace, plan.workspace, out, on) || overlaps(workspace, plan.workspace, q, qn) ||
-            overlaps(workspace, plan.workspace, k, kn) || overlaps(workspace, plan.workspace, v, vn) ||
-            overlaps(workspace, plan.workspace, bias, bn))
+        if (overlaps(workspace, need, out, on) || overlaps(workspace, need, q, qn) ||
+            overlaps(workspace, need, k, kn) || overlaps(workspace, need, v, vn) ||
+            overlaps(workspace, need, bias, bn))
             return fail(ATTN_ERR_INVALID, "workspace: overlaps a tensor");
     }
+    return ok();
+}
 
+attn::Problem make_problem(const Resolved& r, const float* q, const float* k, const float* v, const float* bias,
+                           float* out) {
     attn::Problem prob;
     prob.q = q;
     prob.k = k;
@@ -994,13 +983,18 @@ int attn_forward(const attn_params* p, const float* q, const float* k, const flo
     prob.Dv = (int32_t)r.Dv;
     prob.ep = r.ep;
     prob.rope = r.rope;
-    hipStream_t s = (hipStream_t)stream;
+    return prob;
+}
 
+// Launches a checked plan's kernels on stream s.
+int run_plan(const Resolved& r, const Plan& plan, const attn::Problem& prob, void* workspace, hipStream_t s) {
     hipError_t err = hipSuccess;
     switch (plan.path) {
+        case ATTN_PATH_EMPTY:
+            return ok();
         case ATTN_PATH_ZERO:
             err = timed("zero_fill", s, [&](const attn::Launch& L) {
-                return attn::launch_zero_fill(out, r.T * r.H * r.Dv, L);
+                return attn::launch_zero_fill(prob.out, r.T * r.H * r.Dv, L);
             });
             break;
         case ATTN_PATH_GENERIC:
@@ -1032,6 +1026,122 @@ int attn_forward(const attn_params* p, const float* q, const float* k, const flo
     }
     if (err != hipSuccess) return fail(ATTN_ERR_DEVICE, "launch: %s", hipGetErrorString(err));
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+void attn_params_init(attn_params* p) {
+    if (!p) return;
+    memset(p, 0, sizeof *p);
+    p->causal = 1;
+}
+
+int attn_validate(const attn_params* p) {
+    Resolved r;
+    int rc = resolve(p, &r);
+    if (rc) return rc;
+    Plan plan;
+    return make_plan(r, &plan);
+}
+
+size_t attn_workspace_size(const attn_params* p) {
+    Resolved r;
+    if (resolve(p, &r)) return 0;
+    Plan plan;
+    if (make_plan(r, &plan)) return 0;
+    return plan.reserve;
+}
+
+int attn_plan(const attn_params* p, attn_plan_info* info) {
+    if (!info) return fail(ATTN_ERR_INVALID, "info: NULL pointer");
+    Resolved r;
+    int rc = resolve(p, &r);
+    if (rc) return rc;
+    Plan plan;
+    rc = make_plan(r, &plan);
+    if (rc) return rc;
+    info->path = plan.path;
+    info->splits = plan.path == ATTN_PATH_DECODE    ? plan.decode.splits
+                   : plan.path == ATTN_PATH_PREFILL ? plan.prefill.ksplit
+                                                    : 1;
+    info->tile_q = plan.path == ATTN_PATH_PREFILL ? plan.prefill.tile_q : 0;
+    info->reserved = 0;
+    return ok();
+}
+
+int attn_forward(const attn_params* p, const float* q, const float* k, const float* v,
+                 const float* bias, float* out, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+    Resolved r;
+    int rc = resolve(p, &r);
+    if (rc) return rc;
+    Plan plan;
+    rc = make_plan(r, &plan);
+    if (rc) return rc;
+    if (plan.path == ATTN_PATH_EMPTY) return ok();
+    rc = check_forward_args(p, r, plan.workspace, q, k, v, bias, out, workspace, workspace_bytes);
+    if (rc) return rc;
+    return run_plan(r, plan, make_problem(r, q, k, v, bias, out), workspace, (hipStream_t)stream);
+}
+
+int attn_forward_append(const attn_params* p, const float* q, float* k, float* v, const float* k_new,
+                        const float* v_new, int64_t rows, int64_t offset, const float* bias, float* out,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+    Resolved r;
+    int rc = resolve(p, &r);
+    if (rc) return rc;
+    // The two cache_write ops: rows [offset, offset + rows) of the caches.
+    float *dk = nullptr, *dv = nullptr;
+    rc = check_cache_write("k: ", k, r.S, r.G * r.D, k_new, rows, offset, &dk);
+    if (rc) return rc;
+    rc = check_cache_write("v: ", v, r.S, r.G * r.Dv, v_new, rows, offset, &dv);
+    if (rc) return rc;
+    const size_t kw = sizeof(float) * (size_t)(rows * r.G * r.D), vw = sizeof(float) * (size_t)(rows * r.G * r.Dv);
+    if (overlaps(dk, kw, dv, vw)) return fail(ATTN_ERR_INVALID, "v: rows written overlap the k rows written");
+    if (overlaps(dk, kw, v_new, vw)) return fail(ATTN_ERR_INVALID, "v: values overlap the k rows written");
+    if (overlaps(dv, vw, k_new, kw)) return fail(ATTN_ERR_INVALID, "k: values overlap the v rows written");
+    Plan plan;
+    // The fused decode reads the new rows as 16-byte vectors.
+    const AppendRows app{offset, offset + rows};
+    rc = make_plan(r, &plan, aligned16(k_new) && aligned16(v_new) ? &app : nullptr);
+    if (rc) return rc;
+    hipStream_t s = (hipStream_t)stream;
+    if (plan.path != ATTN_PATH_EMPTY) {
+        rc = check_forward_args(p, r, plan.workspace, q, k, v, bias, out, workspace, workspace_bytes);
+        if (rc) return rc;
+        // Nothing else the call reads or writes may lie in the rows written
+        // (the attention may run while they are being written), and out and
+        // the workspace may not hold the new rows.
+        const size_t qn = sizeof(float) * (size_t)(r.T * r.H * r.D);
+        const size_t on = sizeof(float) * (size_t)(r.T * r.H * r.Dv);
+        const size_t bn = r.bias_kind == ATTN_BIAS_TS    ? sizeof(float) * (size_t)(r.T * r.S)
+                          : r.bias_kind == ATTN_BIAS_HTS ? sizeof(float) * (size_t)(r.H * r.T * r.S)
+                                                         : 0;
+        if (overlaps(dk, kw, q, qn) || overlaps(dv, vw, q, qn))
+            return fail(ATTN_ERR_INVALID, "q: overlaps the cache rows written");
+        if (overlaps(dk, kw, bias, bn) || overlaps(dv, vw, bias, bn))
+            return fail(ATTN_ERR_INVALID, "bias: overlaps the cache rows written");
+        if (overlaps(out, on, k_new, kw) || overlaps(out, on, v_new, vw))
+            return fail(ATTN_ERR_INVALID, "out: overlaps k_new or v_new");
+        if (plan.workspace && (overlaps(workspace, plan.workspace, k_new, kw) ||
+                               overlaps(workspace, plan.workspace, v_new, vw)))
+            return fail(ATTN_ERR_INVALID, "workspace: overlaps k_new or v_new");
+    }
+    if (plan.fused) {
+        plan.decode.k_new = k_new;
+        plan.decode.v_new = v_new;
+        plan.decode.k_cache = k;
+        plan.decode.v_cache = v;
+    } else if (rows > 0) {
+        const hipError_t err = timed("cache_write", s, [&](const attn::Launch& L) {
+            return attn::launch_cache_write_pair(dk, k_new, rows * r.G * r.D, dv, v_new, rows * r.G * r.Dv, L);
+        });
+        if (err != hipSuccess) return fail(ATTN_ERR_DEVICE, "launch: %s", hipGetErrorString(err));
+    }
+    if (plan.path == ATTN_PATH_EMPTY) return ok();
+    return run_plan(r, plan, make_problem(r, q, k, v, bias, out), workspace, s);
 }
 
 int attn_cache_write(float* cache, int64_t max_rows, int64_t width, const float* values,

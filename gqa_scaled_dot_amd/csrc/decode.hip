@@ -2,7 +2,7 @@
 // range (a KV cache). HBM-bound: every visible K and V row of a KV head is
 // read exactly once, for all the query rows of that head's group.
 //
-// decode_split: grid (splits, kv_heads), 256 threads. The workgroup of KV
+// decode_split: grid (splits, kv_heads), 256 threads (1-D on appending calls). The workgroup of KV
 // head g walks its share of the key range. Its 256 lanes form 16 row groups
 // of 16 lanes (one DPP row each); a row group takes U consecutive key rows
 // at a time, and each lane of it loads a 4-float slice of every 64-float
@@ -14,6 +14,9 @@
 // follow, and the lane accumulates its V slice for all query rows of the
 // group. At the end the 16 row groups' partial states are merged (lane
 // shuffles, then LDS) into one (max, sum, acc) per query row and split.
+// On an appending call one more split per KV head takes the call's new key
+// and value rows straight from the caller's buffers and stores them into
+// the caches as it reads them: a decode step needs no copy launch first.
 //
 // The running maximum is moved lazily: weights are taken against a
 // reference that may trail the true maximum by up to 2^8 (so a weight is at
@@ -91,8 +94,26 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
     const int rg = tid >> 4;
     constexpr bool REL = RM != 0;
     constexpr bool FAR = RM == 1;
-    const int sp = plan.split_base + blockIdx.x;
-    const int g = blockIdx.y;
+    // Split sp of KV group g. On an appending call the splits of appended
+    // rows (short ones) are dispatched after every other workgroup: placed
+    // first, they would push a third full-length split onto some CUs.
+    int sp, g;
+    if (plan.k_new) {
+        const int per = plan.splits - 1;  // the other splits of a group
+        const int near_sp = plan.splits - 1 - (plan.sink_hi > 0 ? 1 : 0);
+        const int id = blockIdx.x;
+        if (id < per * p.G) {
+            g = id / per;
+            const int x = id - g * per;
+            sp = x < near_sp ? x : x + 1;
+        } else {
+            g = id - per * p.G;
+            sp = near_sp;
+        }
+    } else {
+        sp = blockIdx.x;
+        g = blockIdx.y;
+    }
     const int hpg = p.H / p.G;
     const int nrows = (int)p.T * hpg;
 
@@ -148,9 +169,12 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
     // This split's keys: its share of the window range, or (the last split,
     // with attention sinks) the sink keys below it.
     // (With relative-position terms, the split before it covers the keys
-    // near the query rows.)
+    // near the query rows; on an appending call, the rows appended.)
     const bool sink_split = plan.sink_hi > 0 && sp == plan.splits - 1;
     const bool near_split = plan.near_hi > plan.near_lo && sp == plan.splits - 1 - (plan.sink_hi > 0 ? 1 : 0);
+    // The appended rows come from the caller's new-row buffers, and this
+    // split also stores them into the caches (no other split reads them).
+    const bool append = !REL && near_split && plan.k_new != nullptr;
     const bool spread = plan.block > 0 && !sink_split && !near_split;
     // [k0, k1): the rows the split's keys lie in. A split walks nw rows in
     // blocks of 2^bsh; its j-th block is block (j * bstride + boff) of
@@ -196,8 +220,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
     // Workgroup-uniform bases; per-lane offsets stay in 32 bits (the host
     // keeps (k1 - k0) * row stride below 2^31 floats).
     const uint32_t kstride = (uint32_t)(p.G * D), vstride = (uint32_t)(p.G * DV);
-    const float* kwg = p.k + (int64_t)k0 * kstride + (int64_t)g * D + 4 * ln;
-    const float* vwg = p.v + (int64_t)k0 * vstride + (int64_t)g * DV + 4 * ln;
+    const float* kwg = (append ? plan.k_new : p.k + (int64_t)k0 * kstride) + (int64_t)g * D + 4 * ln;
+    const float* vwg = (append ? plan.v_new : p.v + (int64_t)k0 * vstride) + (int64_t)g * DV + 4 * ln;
     // With every key of [k0, k1) visible to every row, only rows past the
     // walk's or the range's end need checking.
     const bool dense = chunk_all_visible(p.ep, p.ep.pos_offset, p.ep.pos_offset + (int)p.T - 1, k0, k1);
@@ -360,6 +384,28 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
                             acc[r][j].z = fmaf(pu[u], x4.z, acc[r][j].z);
                             acc[r][j].w = fmaf(pu[u], x4.w, acc[r][j].w);
                         }
+                    }
+                }
+            }
+        }
+        if constexpr (!REL) {
+            // Rows read from the new-row buffers go on into the caches: each
+            // lane stores the slices it loaded.
+            // (Uniform bases and 32-bit lane offsets, so that no per-lane
+            // address stays live through the walk.)
+            if (append) {
+                float* kd = plan.k_cache + (int64_t)k0 * kstride + (int64_t)g * D;
+                float* vd = plan.v_cache + (int64_t)k0 * vstride + (int64_t)g * DV;
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    if (w0 + u < nw && r0 + u < k1) {
+                        const uint32_t row = (uint32_t)(r0 + u - k0);
+#pragma unroll
+                        for (int j = 0; j < KJ; ++j)
+                            *reinterpret_cast<float4*>(kd + (row * kstride + 4 * ln + 64 * j)) = kf[u][j];
+#pragma unroll
+                        for (int j = 0; j < VJ; ++j)
+                            *reinterpret_cast<float4*>(vd + (row * vstride + 4 * ln + 64 * j)) = vf[u][j];
                     }
                 }
             }
@@ -783,7 +829,7 @@ __global__ __launch_bounds__(kThreads) void combine_few_kernel(Problem p, int ns
 
 template <int D, int DV, int NQ, int DEPTH>
 hipError_t launch_split_d(const Problem& p, const DecodePlan& plan, float* ws, const Launch& L) {
-    const dim3 grid((unsigned)plan.splits, (unsigned)p.G);
+    const dim3 grid = plan.k_new ? dim3((unsigned)(plan.splits * p.G)) : dim3((unsigned)plan.splits, (unsigned)p.G);
     const bool epi = p.ep.any();
     // With relative embeddings, every row's products with them sit in LDS.
     const uint32_t lds = p.ep.rel_k ? (uint32_t)(sizeof(float) * NQ * (2 * p.ep.rel_max + 1)) : 0u;

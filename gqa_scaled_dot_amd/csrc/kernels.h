@@ -78,16 +78,25 @@ struct DecodePlan {
     int32_t splits;   // key-range splits per KV group (the sink split included)
     int32_t depth;    // batches in the split kernel's register ring (2 or 3)
     int32_t sink_hi;  // > 0: the last split covers the sink keys [0, sink_hi) below `range`
-    int32_t split_base;        // first split this launch covers (grid x = its splits)
     int32_t rotate;            // split sp starts (sp * rotate mod chunk) rows into its chunk (0: in order)
     int32_t near_lo, near_hi;  // near_hi > near_lo: a split (before the sink split) covers
-                               // [near_lo, near_hi), the keys the relative-position tables reach
+                               // [near_lo, near_hi), the keys nearest the query rows: those the
+                               // relative-position tables reach, or the rows the call appends
     int32_t block;    // > 0: the splits of `range` interleave blocks of this many rows (a power
                       // of two, multiple of the row-group step): split i takes blocks i,
                       // i + main_splits, ...; 0: split i takes the i-th chunk of `chunk` rows
     int32_t main_splits;  // splits over `range` (the near and sink splits follow them)
     int64_t chunk;    // keys per split of `range` (multiple of the row-group step)
     KeyRange range;
+    // Appending calls: the near split reads its rows from k_new / v_new (row
+    // i there is row near_lo + i; same row widths as the caches) and stores
+    // them into k_cache / v_cache as it goes. Null otherwise. With them the
+    // grid is 1-D: the other splits of every KV group in the usual order,
+    // then the near split of each group.
+    const float* k_new;
+    const float* v_new;
+    float* k_cache;
+    float* v_cache;
 };
 
 struct PrefillPlan {

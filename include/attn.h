@@ -165,8 +165,9 @@ void attn_params_init(attn_params* p);
  * ATTN_ERR_UNSUPPORTED, with attn_last_error() naming the field. */
 int attn_validate(const attn_params* p);
 
-/* Bytes of device workspace attn_forward needs for *p (0 if none; also 0
- * for an invalid *p). The workspace holds per-split partial softmax state. */
+/* Bytes of device workspace attn_forward or attn_forward_append needs for
+ * *p (0 if none; also 0 for an invalid *p). The workspace holds per-split
+ * partial softmax state. */
 size_t attn_workspace_size(const attn_params* p);
 
 /*
@@ -211,6 +212,39 @@ int attn_cache_write(float* cache, int64_t max_rows, int64_t width, const float*
 int attn_cache_write2(float* cache_a, int64_t max_rows_a, int64_t width_a, const float* values_a,
                       float* cache_b, int64_t max_rows_b, int64_t width_b, const float* values_b,
                       int64_t rows, int64_t offset, void* stream);
+
+/*
+ * A decode step in one call: the two `cache_write` ops that append the
+ * step's new K and V rows to the caches, then op `attention` over the
+ * caches (the op catalogue's cache_write feeding attention through a
+ * preallocated KV cache at posOffset). Same result as
+ *   attn_cache_write2(k, S, kv_heads*head_dim, k_new,
+ *                     v, S, kv_heads*v_head_dim, v_new, rows, offset, stream);
+ *   attn_forward(p, q, k, v, bias, out, workspace, workspace_bytes, stream);
+ * with the caches bit for bit that copy's and out within rounding of that
+ * attn_forward (its splits of the key range may differ).
+ *   k      [S, kv_heads*head_dim]     device, the K cache; rows
+ *                                     [offset, offset + rows) are written
+ *   v      [S, kv_heads*v_head_dim]   device, the V cache; likewise
+ *   k_new  [rows, kv_heads*head_dim]    device, read-only
+ *   v_new  [rows, kv_heads*v_head_dim]  device, read-only
+ *   q, bias, out, workspace, stream as for attn_forward (p->S is the
+ *   caches' row count); workspace_bytes >= attn_workspace_size(p).
+ * Requires 0 <= offset and offset + rows <= S; rows = 0 is attn_forward.
+ * Each cache takes attn_cache_write's checks (messages prefixed "k: " and
+ * "v: "). The K rows written and the V rows written must not overlap, nor
+ * either of them a new-row buffer, q or bias; out and the workspace must
+ * not overlap k_new or v_new. Where the new rows are the last keys the
+ * call sees (offset + rows is the end of its key range, as in a causal decode
+ * step appending at posOffset), there are at most 64 of them, k_new and v_new
+ * are 16-byte aligned and the call takes the decode path without
+ * relative-position terms, one kernel reads them from k_new and v_new while
+ * it writes them to the caches; otherwise the copy runs first, in a launch
+ * of its own. T = 0 only writes the rows.
+ */
+int attn_forward_append(const attn_params* p, const float* q, float* k, float* v, const float* k_new,
+                        const float* v_new, int64_t rows, int64_t offset, const float* bias, float* out,
+                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Op `rope` (graph protocol op catalogue: "Rotary position embedding over

@@ -114,10 +114,19 @@ def test_plans():
 
 
 def test_decode_workspace_matches_plan():
+    # Room for every split's partial state, plus one more split: the same
+    # call made through attn_forward_append may add the split of appended rows.
     kw = dict(heads=32, kvHeads=8, headDim=128, posOffset=32767)
     plan = ga.attn_plan(1, 32768, **kw)
-    assert ga.attn_workspace_size(1, 32768, **kw) == 4 * 32 * plan["splits"] * (128 + 2)
+    assert ga.attn_workspace_size(1, 32768, **kw) == 4 * 32 * (plan["splits"] + 1) * (128 + 2)
     assert ga.attn_workspace_size(8, 8, heads=4, kvHeads=2, headDim=16) == 0
+    # One split: attn_forward needs none, attn_forward_append may need two.
+    short = dict(heads=4, kvHeads=1, headDim=64, posOffset=40)
+    assert ga.attn_plan(1, 41, **short)["splits"] == 1
+    assert ga.attn_workspace_size(1, 41, **short) == 4 * 4 * 2 * (64 + 2)
+    # Relative-position terms: no fused append, no extra split.
+    rel = dict(kw, position_bias=dict(weight=4096, buckets=list(range(32))))
+    assert ga.attn_workspace_size(1, 32768, **rel) == 4 * 32 * ga.attn_plan(1, 32768, **rel)["splits"] * (128 + 2)
 
 
 @pytest.mark.parametrize("G", [1, 2, 6, 8, 12, 16, 24])
@@ -143,7 +152,7 @@ def test_decode_sink_split():
     plain = ga.attn_plan(1, 32768, **kw)
     sinks = ga.attn_plan(1, 32768, sinks=4, **kw)
     assert plain["splits"] == 64 and sinks["splits"] == 64
-    assert ga.attn_workspace_size(1, 32768, sinks=4, **kw) == 4 * 32 * sinks["splits"] * (128 + 2)
+    assert ga.attn_workspace_size(1, 32768, sinks=4, **kw) == 4 * 32 * (sinks["splits"] + 1) * (128 + 2)
     try:
         ga.attn_set_option("decode_splits", 7)
         assert ga.attn_plan(1, 32768, sinks=4, **kw)["splits"] == ga.attn_plan(1, 32768, **kw)["splits"] + 1
@@ -243,11 +252,56 @@ def test_cache_write2_refuses_before_launch():
     assert "a: values overlap the rows b writes" in ga.attn_last_error()
 
 
+def _append_raw(p, q, k, v, k_new, v_new, rows, offset, bias, out, ws=None, ws_bytes=0):
+    return _lib.lib().attn_forward_append(ctypes.byref(p), q, k, v, k_new, v_new, rows, offset, bias, out,
+                                          ws, ws_bytes, None)
+
+
+def test_forward_append_refuses_before_launch():
+    # Fake, never-dereferenced addresses (caches of 16 rows, 2 KV heads of 64
+    # floats: rows of 512 bytes). Every case is refused on the host.
+    p, _ = ga.make_params(1, 16, posOffset=15, **BASE)
+    A = 1 << 32
+    q, k, v, kn, vn, out = A, 2 * A, 3 * A, 4 * A, 5 * A, 6 * A
+    assert _append_raw(p, q, k, v, kn, vn, 2, 15, None, out) == 1
+    assert ga.attn_last_error().startswith("k: offset")
+    assert _append_raw(p, q, k, v, kn, vn, -1, 15, None, out) == 1 and "rows" in ga.attn_last_error()
+    assert _append_raw(p, q, k, v, kn, None, 1, 15, None, out) == 1
+    assert ga.attn_last_error().startswith("v: values")
+    assert _append_raw(p, q, k, v, k + 15 * 512, vn, 1, 15, None, out) == 1
+    assert ga.attn_last_error().startswith("k: values")
+    # The V rows written start inside the K rows written.
+    assert _append_raw(p, q, k, k + 64, kn, vn, 1, 15, None, out) == 1
+    assert "overlap the k rows written" in ga.attn_last_error()
+    assert _append_raw(p, q, k, v, kn, k + 15 * 512 + 16, 1, 15, None, out) == 1
+    assert ga.attn_last_error().startswith("v: values overlap the k rows")
+    # q, out, the workspace and the new rows (this call has two splits: it
+    # needs a workspace).
+    ws = (7 * A, 1 << 20)
+    assert _append_raw(p, q, k, v, kn, vn, 1, 15, None, out) == 1 and "workspace" in ga.attn_last_error()
+    assert _append_raw(p, k + 15 * 512, k, v, kn, vn, 1, 15, None, out, *ws) == 1
+    assert ga.attn_last_error().startswith("q: overlaps the cache rows")
+    assert _append_raw(p, q, k, v, kn, vn, 1, 15, None, kn + 64, *ws) == 1
+    assert ga.attn_last_error().startswith("out: overlaps k_new")
+    assert _append_raw(p, q, k, v, kn, vn, 1, 15, None, out, vn - 256, 1 << 20) == 1
+    assert ga.attn_last_error().startswith("workspace: overlaps k_new")
+    # attn_forward's own checks still apply.
+    assert _append_raw(p, None, k, v, kn, vn, 1, 15, None, out) == 1 and "q" in ga.attn_last_error()
+    assert _append_raw(p, q, k, v, kn, vn, 1, 15, None, out + 4) == 1 and "aligned" in ga.attn_last_error()
+    pd, _ = ga.make_params(1, 32768, heads=32, kvHeads=8, headDim=128, posOffset=32767)
+    assert _append_raw(pd, q, k, v, kn, vn, 1, 32767, None, out) == 1 and "workspace" in ga.attn_last_error()
+    # T = 0 and no rows: nothing to do.
+    p0, _ = ga.make_params(0, 16, **BASE)
+    assert _append_raw(p0, None, None, None, None, None, 0, 0, None, None) == 0
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     q = torch.zeros(1, 64)
     with pytest.raises(ValueError):
         ga.attn_forward(q, q, q, heads=1, headDim=64)
+    with pytest.raises(ValueError):
+        ga.attn_forward_append(q, q, q, q, q, 0, heads=1, headDim=64)
 
 
 MLA = dict(heads=16, kv_rank=512, qk_nope=128, qk_rope=64, v_head_dim=128)
