@@ -730,9 +730,12 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(Problem p, int
     float4* orow = reinterpret_cast<float4*>(p.out + th * DV);
 
     // Every load is requested before any reduction: this thread's first
-    // kPre accumulator float4s and its splits' (max, sum) pairs.
+    // kPre accumulator float4s and its splits' (max, sum) pairs. They cover
+    // 64 splits of the key range plus the near and sink splits (a split
+    // past them would cost one more round trip after the reductions).
     const int e4 = tid % E4, grp = tid / E4;
-    constexpr int kPre = 64 / kGroups > 0 ? 64 / kGroups : 1;  // covers 64 splits
+    constexpr int kPreSplits = 66;
+    constexpr int kPre = (kPreSplits + kGroups - 1) / kGroups;
     float4 pre[kPre];
 #pragma unroll
     for (int u = 0; u < kPre; ++u) {
@@ -774,6 +777,7 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(Problem p, int
         a.x = fmaf(pre[u].x, w, a.x); a.y = fmaf(pre[u].y, w, a.y);
         a.z = fmaf(pre[u].z, w, a.z); a.w = fmaf(pre[u].w, w, a.w);
     }
+#pragma unroll 4
     for (int i = grp + kPre * kGroups; i < nsplit; i += kGroups) {
         const float w = s_w[i];
         const float4 c = acc4[(int64_t)i * E4 + e4];
