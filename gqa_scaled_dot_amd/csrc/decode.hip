@@ -691,106 +691,81 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
     }
 }
 
-__device__ __forceinline__ float block_max(float x, float* red) {
-    for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
-    __syncthreads();
-    x = red[0];
-    for (int w = 1; w < kWaves; ++w) x = fmaxf(x, red[w]);
-    return x;
-}
-
-__device__ __forceinline__ float block_sum(float x, float* red) {
-    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
-    __syncthreads();
-    x = red[0];
-    for (int w = 1; w < kWaves; ++w) x += red[w];
-    return x;
-}
-
-// One workgroup per (query row, head). Every split's (max, sum) is read at
-// once, one per thread; the accumulators are read as float4 with the splits
-// spread over thread groups and summed through LDS.
+// One workgroup per (query row, head). Thread group grp (E4 threads, one
+// float4 column each) takes splits grp, grp + kGroups, ...: it merges their
+// (max, sum, acc) on its own, from loads all requested up front, and one
+// barrier later the first group merges the groups' results.
 template <int DV>
 __global__ __launch_bounds__(kThreads) void decode_combine_kernel(Problem p, int nsplit,
                                                                   const float* __restrict__ ws) {
     constexpr int E4 = DV / 4;
     constexpr int kGroups = kThreads / E4;
-    __shared__ float s_w[kMaxSplits];
-    __shared__ float s_red[kWaves];
+    // Up-front loads cover 64 splits of the key range plus the near and sink
+    // splits; further splits (plans with few KV heads) are read afterwards.
+    constexpr int kPreSplits = 66;
+    constexpr int kPre = (kPreSplits + kGroups - 1) / kGroups;
+    __shared__ float2 s_ml[kGroups];
     __shared__ float4 s_part[kGroups][E4];
 
     const int tid = threadIdx.x;
+    const int e4 = tid % E4, grp = tid / E4;
     const int64_t th = blockIdx.x;  // t * H + h
     const float4* acc4 = reinterpret_cast<const float4*>(ws + th * nsplit * DV);
-    const float* ml = ws + (int64_t)p.T * p.H * nsplit * DV + th * nsplit * 2;
+    const float2* ml2 = reinterpret_cast<const float2*>(ws + (int64_t)p.T * p.H * nsplit * DV + th * nsplit * 2);
     float4* orow = reinterpret_cast<float4*>(p.out + th * DV);
 
-    // Every load is requested before any reduction: this thread's first
-    // kPre accumulator float4s and its splits' (max, sum) pairs. They cover
-    // 64 splits of the key range plus the near and sink splits (a split
-    // past them would cost one more round trip after the reductions).
-    const int e4 = tid % E4, grp = tid / E4;
-    constexpr int kPreSplits = 66;
-    constexpr int kPre = (kPreSplits + kGroups - 1) / kGroups;
     float4 pre[kPre];
+    float2 mlp[kPre];
 #pragma unroll
     for (int u = 0; u < kPre; ++u) {
         const int i = grp + u * kGroups;
         pre[u] = i < nsplit ? acc4[(int64_t)i * E4 + e4] : zero4();
+        mlp[u] = i < nsplit ? ml2[i] : make_float2(-INFINITY, 0.0f);
     }
-    float2 mlv[kMaxSplits / kThreads];
+    // The group's maximum, then its sum and accumulator against it.
+    float mg = -INFINITY;
 #pragma unroll
-    for (int u = 0; u < kMaxSplits / kThreads; ++u) {
-        const int i = tid + u * kThreads;
-        mlv[u] = i < nsplit ? *reinterpret_cast<const float2*>(ml + 2 * i) : make_float2(-INFINITY, 0.0f);
-    }
-
-    float m = -INFINITY;
-#pragma unroll
-    for (int u = 0; u < kMaxSplits / kThreads; ++u) m = fmaxf(m, mlv[u].x);
-    const float M = block_max(m, s_red);
-    if (M == -INFINITY) {  // no visible key in any split
-        for (int e = tid; e < E4; e += kThreads) orow[e] = zero4();
-        return;
-    }
-    float lsum = 0.0f;
-#pragma unroll
-    for (int u = 0; u < kMaxSplits / kThreads; ++u) {
-        const int i = tid + u * kThreads;
-        if (i < nsplit) {
-            const float w = fast_exp2(mlv[u].x - M);
-            s_w[i] = w;
-            lsum += mlv[u].y * w;
-        }
-    }
-    const float L = block_sum(lsum, s_red);  // ends with a barrier, so s_w is complete
-
+    for (int u = 0; u < kPre; ++u) mg = fmaxf(mg, mlp[u].x);
+    for (int i = grp + kPre * kGroups; i < nsplit; i += kGroups) mg = fmaxf(mg, ml2[i].x);
+    const float mu = mg == -INFINITY ? 0.0f : mg;
+    float lg = 0.0f;
     float4 a = zero4();
 #pragma unroll
     for (int u = 0; u < kPre; ++u) {
-        const int i = grp + u * kGroups;
-        const float w = i < nsplit ? s_w[i] : 0.0f;
+        const float w = fast_exp2(mlp[u].x - mu);
+        lg = fmaf(mlp[u].y, w, lg);
         a.x = fmaf(pre[u].x, w, a.x); a.y = fmaf(pre[u].y, w, a.y);
         a.z = fmaf(pre[u].z, w, a.z); a.w = fmaf(pre[u].w, w, a.w);
     }
 #pragma unroll 4
     for (int i = grp + kPre * kGroups; i < nsplit; i += kGroups) {
-        const float w = s_w[i];
+        const float2 mi = ml2[i];
         const float4 c = acc4[(int64_t)i * E4 + e4];
+        const float w = fast_exp2(mi.x - mu);
+        lg = fmaf(mi.y, w, lg);
         a.x = fmaf(c.x, w, a.x); a.y = fmaf(c.y, w, a.y);
         a.z = fmaf(c.z, w, a.z); a.w = fmaf(c.w, w, a.w);
     }
     s_part[grp][e4] = a;
+    if (e4 == 0) s_ml[grp] = make_float2(mg, lg);
     __syncthreads();
     if (grp == 0) {
-        float4 t = s_part[0][e4];
-        for (int q = 1; q < kGroups; ++q) {
+        float M = s_ml[0].x;
+#pragma unroll
+        for (int q = 1; q < kGroups; ++q) M = fmaxf(M, s_ml[q].x);
+        if (M == -INFINITY) {  // no visible key in any split
+            orow[e4] = zero4();
+            return;
+        }
+        float L = 0.0f;
+        float4 t = zero4();
+#pragma unroll
+        for (int q = 0; q < kGroups; ++q) {
+            const float w = fast_exp2(s_ml[q].x - M);
+            L = fmaf(s_ml[q].y, w, L);
             const float4 c = s_part[q][e4];
-            t.x += c.x; t.y += c.y; t.z += c.z; t.w += c.w;
+            t.x = fmaf(c.x, w, t.x); t.y = fmaf(c.y, w, t.y);
+            t.z = fmaf(c.z, w, t.z); t.w = fmaf(c.w, w, t.w);
         }
         const float inv = 1.0f / L;
         orow[e4] = make_float4(t.x * inv, t.y * inv, t.z * inv, t.w * inv);

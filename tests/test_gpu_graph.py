@@ -1,8 +1,8 @@
 """A decode step captured in a HIP graph (torch.cuda.graph) and replayed.
 
 The library allocates nothing, never synchronises and launches only kernels
-on the caller's stream, so a step (the K/V append, then attention) can be
-captured once and replayed. Every replay is checked against the same step run
+on the caller's stream, so a step (the K/V append, then attention, as two
+calls or as one attn_forward_append) can be captured once and replayed. Every replay is checked against the same step run
 eagerly, with eager work and synchronisations between replays, and after the
 captured inputs are rewritten in place.
 """
@@ -18,7 +18,8 @@ from tests.parity import assert_close, dev, torch
 pytestmark = pytest.mark.gpu
 
 
-def test_decode_step_replays_from_a_graph():
+@pytest.mark.parametrize("fused", [False, True], ids=["cache_write2 + attn_forward", "attn_forward_append"])
+def test_decode_step_replays_from_a_graph(fused):
     t = torch()
     w = workloads.LLAMA_DECODE.replace(name="graph decode", S=4096, posOffset=4095)
     q, k, v, _ = w.tensors()
@@ -31,8 +32,11 @@ def test_decode_step_replays_from_a_graph():
     ws = t.empty(ga.attn_workspace_size(w.T, w.S, **w.params()), dtype=t.uint8, device="cuda")
 
     def step():
-        ga.attn_cache_write2(kc, new_k, vc, new_v, pos)
-        ga.attn_forward(qd, kc, vc, out=out, workspace=ws, **w.params())
+        if fused:
+            ga.attn_forward_append(qd, kc, vc, new_k, new_v, pos, out=out, workspace=ws, **w.params())
+        else:
+            ga.attn_cache_write2(kc, new_k, vc, new_v, pos)
+            ga.attn_forward(qd, kc, vc, out=out, workspace=ws, **w.params())
 
     step()
     t.cuda.synchronize()
@@ -51,11 +55,15 @@ def test_decode_step_replays_from_a_graph():
 
     for rep in range(4):
         out.fill_(float("nan"))
+        kc[pos:].fill_(float("nan"))  # the replay writes the new row again
+        vc[pos:].fill_(float("nan"))
         scratch = t.randn(1024, device="cuda") * 2.0  # eager work between replays
         t.cuda.synchronize()
         graph.replay()
         t.cuda.synchronize()
         np.testing.assert_array_equal(out.cpu().numpy().view(np.uint32), eager.cpu().numpy().view(np.uint32))
+        np.testing.assert_array_equal(kc[pos:].cpu().numpy().view(np.uint32), k[pos:].view(np.uint32))
+        np.testing.assert_array_equal(vc[pos:].cpu().numpy().view(np.uint32), v[pos:].view(np.uint32))
         del scratch
 
     # New inputs written in place into the captured buffers.
