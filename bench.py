@@ -28,7 +28,8 @@ The same line carries `prefill`: the Llama-3-8B-shaped causal prefill
 157.3 TFLOP/s fp32 matrix peak.
 
 `rope` holds the rotary embedding: the same decode step with rope fused in
-(K rotated as cache_write stores it, q as attention loads it) and the
+(the new K row rotated into a staging row, then attn_forward_append with q
+rotated as attention loads it; also timed as three separate calls) and the
 standalone rope kernel on a prefill-sized q, rated against HBM.
 
 `configs` lists the other workloads the same way (their own plan, kernel
@@ -600,13 +601,21 @@ def run_rope(args):
     new_k, new_v = kd[w.S - 1:], vd[w.S - 1:]
     out = torch.empty((w.T, w.heads * w.Dv), dtype=torch.float32, device=dev)
     ws = torch.empty(max(ga.attn_workspace_size(w.T, w.S, **params), 256), dtype=torch.uint8, device=dev)
-    steps = [(ga.prepare_rope_cache_write(kc[b], new_k, w.S - 1, rp),
-              ga.prepare_cache_write(vc[b], new_v, w.S - 1),
-              ga.prepare_forward(qd, kc[b], vc[b], out=out, workspace=ws, q_rope=dict(LLAMA3_ROPE),
-                                 **params)) for b in range(n_buf)]
+    # The step: the new K row turned at position S-1 into a one-row staging
+    # buffer, then attn_forward_append (both rows written by the decode
+    # kernel, q turned as it is loaded). Also timed: the same step as
+    # attn_rope_cache_write (K) + cache_write (V) + attn_forward.
+    k_rot = torch.empty_like(new_k)
+    steps = [(ga.prepare_rope_cache_write(k_rot, new_k, 0, dict(rp, offset=w.S - 1)),
+              ga.prepare_forward_append(qd, kc[b], vc[b], k_rot, new_v, w.S - 1, out=out, workspace=ws,
+                                        q_rope=dict(LLAMA3_ROPE), **params)) for b in range(n_buf)]
+    separate = [(ga.prepare_rope_cache_write(kc[b], new_k, w.S - 1, rp),
+                 ga.prepare_cache_write(vc[b], new_v, w.S - 1),
+                 ga.prepare_forward(qd, kc[b], vc[b], out=out, workspace=ws, q_rope=dict(LLAMA3_ROPE),
+                                    **params)) for b in range(n_buf)]
 
-    def step(i):
-        for c in steps[i % n_buf]:
+    def step(i, calls=steps):
+        for c in calls[i % n_buf]:
             c()
 
     for i in range(args.warmup):
@@ -628,8 +637,21 @@ def run_rope(args):
     e1.record(stream)
     torch.cuda.synchronize()
     ms_step = e0.elapsed_time(e1) / args.steps
+    for i in range(args.warmup):
+        step(i, separate)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
+        step(i, separate)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_separate = e0.elapsed_time(e1) / args.steps
+    for i in range(2):  # leave `out` as the step computes it
+        step(i)
+    torch.cuda.synchronize()
     us = {name: round(ms / max(n, 1) * 1e3, 3) for name, (ms, n) in t.items()}
-    log(f"[bench] decode step with fused rope: {ms_step * 1e3:.2f} us; kernels {us}")
+    log(f"[bench] decode step with fused rope: {ms_step * 1e3:.2f} us (as three calls {ms_separate * 1e3:.2f} us); "
+        f"kernels {us}")
     # The oracle on the same step: K rotated at positions 0..S-1, q at S-1.
     k_rot = oracle.rope(k, offset=0, **rp).astype(np.float32)
     q_rot = oracle.rope(q, offset=w.posOffset, **rp).astype(np.float32)
@@ -639,11 +661,13 @@ def run_rope(args):
     log(f"[bench]   parity vs oracle: max |err| {err.max():.3e} ok={ok}")
     alg = decode_algorithmic_bytes(w)
     decode = {"workload": w.name + ", llama3 rope (theta 500000, factor 8) on q and the new K row",
-              "step": "attn_rope_cache_write (new K row) + cache_write (new V row) + attn_forward(q_rope)",
+              "step": "attn_rope_cache_write (new K row, into a staging row) + attn_forward_append(q_rope)",
               "ms_per_step": round(ms_step, 6), "value": round(alg / (ms_step * 1e-3) / 1e9, 1),
+              "ms_per_step_separate_calls": round(ms_separate, 6),
+              "separate_calls": "attn_rope_cache_write (new K row) + cache_write (new V row) + attn_forward(q_rope)",
               "unit": "GB/s", "kernel_us": us,
               "parity": {"max_abs_err": float(err.max()), "ok": ok}}
-    del kc, vc, kd, vd, steps
+    del kc, vc, kd, vd, steps, separate, k_rot
     torch.cuda.empty_cache()
 
     # Standalone rope over a prefill's q: every element read and written once.
