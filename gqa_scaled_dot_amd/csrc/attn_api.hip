@@ -588,6 +588,11 @@ int make_plan(const Resolved& r, Plan* plan, const AppendRows* app = nullptr) {
         }
         const bool near = d.near_hi > d.near_lo;
         const int64_t n = d.range.hi > d.range.lo ? d.range.hi - d.range.lo : 0;
+        // Chunks are sized for the range with any appended rows still in it,
+        // so an appending call never has more range splits than the same
+        // call without the append (the workspace attn_workspace_size reports
+        // holds one split more, for the append split).
+        const int64_t np = plan->fused ? kr.hi - d.range.lo : n;
         int64_t splits = g_opt_decode_splits;
         if (splits <= 0) {
             // As many workgroups as the chip holds at once, near and sink
@@ -600,7 +605,7 @@ int make_plan(const Resolved& r, Plan* plan, const AppendRows* app = nullptr) {
             const int64_t extra = (near && !light ? 1 : 0) + (sink_hi > 0 ? 1 : 0);
             const int64_t per_cu = g_opt_decode_wgs ? g_opt_decode_wgs : kDecodeWgPerCU;
             const int64_t target = (int64_t)kCUs * per_cu / r.G - extra;
-            const int64_t most = (n + kDecodeMinKeys - 1) / kDecodeMinKeys;
+            const int64_t most = (np + kDecodeMinKeys - 1) / kDecodeMinKeys;
             splits = target < most ? target : most;
         }
         if (splits < 1) splits = 1;
@@ -609,11 +614,11 @@ int make_plan(const Resolved& r, Plan* plan, const AppendRows* app = nullptr) {
         // the splits, else of finer steps (down to a 2-row batch): over a
         // short range, rounding up to 64 keys could halve the split count.
         int64_t chunk = kDecodeChunkAlign;
-        if (n > 0) {
-            const int64_t per = (n + splits - 1) / splits;
+        if (np > 0) {
+            const int64_t per = (np + splits - 1) / splits;
             for (const int64_t a : {kDecodeChunkAlign, (int64_t)32, (int64_t)16, (int64_t)2}) {
                 chunk = (per + a - 1) / a * a;
-                if ((n + chunk - 1) / chunk * 16 >= splits * 15) break;
+                if ((np + chunk - 1) / chunk * 16 >= splits * 15) break;
             }
         }
         // The kernel addresses a chunk with 32-bit offsets from its first row.
@@ -1107,6 +1112,14 @@ int attn_forward_append(const attn_params* p, const float* q, float* k, float* v
     const AppendRows app{offset, offset + rows};
     rc = make_plan(r, &plan, aligned16(k_new) && aligned16(v_new) ? &app : nullptr);
     if (rc) return rc;
+    if (plan.fused) {
+        // A fused plan never asks for more workspace than attn_workspace_size
+        // reports; if one would, the call copies first instead.
+        Plan plain;
+        rc = make_plan(r, &plain);
+        if (rc) return rc;
+        if (plan.workspace > plain.reserve) plan = plain;
+    }
     hipStream_t s = (hipStream_t)stream;
     if (plan.path != ATTN_PATH_EMPTY) {
         rc = check_forward_args(p, r, plan.workspace, q, k, v, bias, out, workspace, workspace_bytes);

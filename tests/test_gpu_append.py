@@ -220,3 +220,30 @@ def test_decode_loop_matches_separate_calls():
         assert_close(fused.cpu().numpy(), ref, f"step {i}")
         assert_close(sep.cpu().numpy(), ref, f"step {i} separate")
 
+
+
+@pytest.mark.parametrize("S, G, D", [(4097, 8, 128), (4721, 8, 128), (8193, 4, 128), (16385, 2, 128),
+                                     (2321, 16, 64), (32769, 1, 64)])
+def test_fused_within_the_reported_workspace(S, G, D):
+    # Shapes where a range one row shorter rounds to more chunks: the call
+    # still fits the workspace attn_workspace_size reports, and still fuses
+    # (chunks are sized for the range with the appended row in it).
+    t = torch()
+    w = _wl(S=S, heads=2 * G, kvHeads=G, headDim=D)
+    q, k, v, _ = w.tensors()
+    ws = t.empty(ga.attn_workspace_size(w.T, w.S, **w.params()), dtype=t.uint8, device="cuda")
+    kc, vc = dev(k), dev(v)
+    kc[-1] = float("nan")
+    vc[-1] = float("nan")
+    ga.attn_timing_enable(True)
+    try:
+        ga.attn_timing_collect("cache_write")
+        out = ga.attn_forward_append(dev(q), kc, vc, dev(k[-1:]), dev(v[-1:]), S - 1, workspace=ws, **w.params())
+        t.cuda.synchronize()
+        _, copies = ga.attn_timing_collect("cache_write")
+    finally:
+        ga.attn_timing_enable(False)
+    assert copies == 0
+    np.testing.assert_array_equal(_bits(kc), k.view(np.uint32))
+    np.testing.assert_array_equal(_bits(vc), v.view(np.uint32))
+    assert_close(out.cpu().numpy(), oracle.attention(q, k, v, **w.params()), f"S={S} G={G}")
