@@ -2,21 +2,23 @@
 // range (a KV cache). HBM-bound: every visible K and V row of a KV head is
 // read exactly once, for all the query rows of that head's group.
 //
-// decode_split: grid (splits, kv_heads), 256 threads (1-D on appending calls). The workgroup of KV
-// head g walks its share of the key range. Its 256 lanes form 16 row groups
-// of 16 lanes (one DPP row each); a row group takes U consecutive key rows
-// at a time, and each lane of it loads a 4-float slice of every 64-float
-// stretch of the K and V rows (128-bit loads, a whole row per 16 lanes).
-// The loads of the next U rows are issued before the current ones are
-// used, so two batches are in flight per lane. Dot products are partial per
-// lane and summed across the row with DPP rotations, so every lane of the
-// row group holds every score. The score epilogue and an online softmax
-// follow, and the lane accumulates its V slice for all query rows of the
-// group. At the end the 16 row groups' partial states are merged (lane
-// shuffles, then LDS) into one (max, sum, acc) per query row and split.
-// On an appending call one more split per KV head takes the call's new key
-// and value rows straight from the caller's buffers and stores them into
-// the caches as it reads them: a decode step needs no copy launch first.
+// decode_split: grid (splits, kv_heads), 256 threads (1-D on appending
+// calls). The workgroup of KV head g walks its share of the key range. Its
+// 256 lanes form 16 row groups of 16 lanes (one DPP row each); a row group
+// takes U consecutive key rows at a time, and each lane of it loads a
+// 4-float slice of every 64-float stretch of the K and V rows (128-bit
+// loads, a whole row per 16 lanes). By default a lane holds one batch at a
+// time: it uses the batch, then fetches the next (with more loads in flight
+// per lane this memory system ran slower); a ring of 2 or 3 batches is an
+// option. Dot products are partial per lane and summed across the row
+// with DPP rotations, so every lane of the row group holds every score.
+// The score epilogue and an online softmax follow, and the lane accumulates
+// its V slice for all query rows of the group. At the end the 16 row
+// groups' partial states are merged (lane shuffles, then LDS) into one
+// (max, sum, acc) per query row and split. On an appending call one more
+// split per KV head takes the call's new key and value rows straight from
+// the caller's buffers and stores them into the caches as it reads them: a
+// decode step needs no copy launch first.
 //
 // The running maximum is moved lazily: weights are taken against a
 // reference that may trail the true maximum by up to 2^8 (so a weight is at

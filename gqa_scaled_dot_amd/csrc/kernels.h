@@ -76,7 +76,7 @@ struct KeyRange {
 struct DecodePlan {
     int32_t nq;       // query rows per KV group this instance holds (template value)
     int32_t splits;   // key-range splits per KV group (the sink split included)
-    int32_t depth;    // batches in the split kernel's register ring (2 or 3)
+    int32_t depth;    // batches of key rows per lane in registers: 1 (one at a time) or a ring of 2 or 3
     int32_t sink_hi;  // > 0: the last split covers the sink keys [0, sink_hi) below `range`
     int32_t rotate;            // split sp starts (sp * rotate mod chunk) rows into its chunk (0: in order)
     int32_t near_lo, near_hi;  // near_hi > near_lo: a split (before the sink split) covers
