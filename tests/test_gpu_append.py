@@ -247,3 +247,55 @@ def test_fused_within_the_reported_workspace(S, G, D):
     np.testing.assert_array_equal(_bits(kc), k.view(np.uint32))
     np.testing.assert_array_equal(_bits(vc), v.view(np.uint32))
     assert_close(out.cpu().numpy(), oracle.attention(q, k, v, **w.params()), f"S={S} G={G}")
+
+
+def _random_case(seed):
+    rng = np.random.default_rng(1000 + seed)
+    D, Dv, most = [(64, 64, 8), (128, 128, 4), (192, 128, 4), (256, 256, 2)][rng.integers(4)]
+    G = int(rng.choice([1, 2, 4, 8]))
+    T = int(rng.integers(1, 3))
+    hpg = int(rng.choice([h for h in (1, 2, 4, 8) if h * T <= most] or [1]))
+    T = 1 if hpg * T > most else T
+    S = int(rng.integers(T, 6000))
+    kw = dict(name=f"random append {seed}", T=T, S=S, heads=G * hpg, kvHeads=G, headDim=D, seed=seed)
+    if Dv != D:
+        kw["vHeadDim"] = Dv
+    feats = rng.random(5)
+    if feats[0] < 0.3:
+        kw["alibi"] = True
+    if feats[1] < 0.3:
+        kw["softcap"] = 20.0
+    if feats[2] < 0.3:
+        kw["bias"] = "TS" if rng.random() < 0.5 else "HTS"
+    if feats[3] < 0.3 and S > 100:
+        kw["window"] = int(rng.integers(16, S))
+        if feats[4] < 0.5:
+            kw["sinks"] = int(rng.integers(1, 8))
+    w = _wl(**kw)
+    if rng.random() < 0.75:  # the step's own rows, at the end of the range
+        rows = int(rng.integers(w.T, min(64, S) + 1)) if rng.random() < 0.3 else w.T
+        rows = min(rows, w.posOffset + w.T)
+        offset = w.posOffset + w.T - rows
+    else:  # rows anywhere in the cache
+        rows = int(rng.integers(1, min(80, S) + 1))
+        offset = int(rng.integers(0, S - rows + 1))
+    opts = {}
+    if rng.random() < 0.25:
+        opts[str(rng.choice(["decode_splits", "decode_block", "decode_depth"]))] = None
+    for k in opts:
+        opts[k] = {"decode_splits": int(rng.integers(1, 40)), "decode_block": 64, "decode_depth": 2}[k]
+    return w, rows, offset, opts
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_random_appends(seed):
+    w, rows, offset, opts = _random_case(seed)
+    bias_kind = {None: 0, "TS": 1, "HTS": 2}[w.bias]
+    assert ga.attn_plan(w.T, w.S, bias_kind=bias_kind, **w.params())["path"] == "decode", w
+    try:
+        for k, val in opts.items():
+            ga.attn_set_option(k, val)
+        _append(w, rows, offset, what=f"seed {seed}: rows {rows} at {offset} {opts} {w}")
+    finally:
+        for k in opts:
+            ga.attn_set_option(k, 0)
