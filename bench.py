@@ -38,9 +38,10 @@ prefill (T=512 at posOffset 3584), the Gemma-2-shaped sliding-window prefill
 (T=S=8192, headDim 256, softcap 50, window 4096), and the latent-shaped
 ALiBi + per-head bias decode (S=8192, headDim 192, vHeadDim 128) and
 non-causal prefill (T=S=1024), and the Llama-shaped streaming decode (window
-4096 plus 4 attention sinks over a 32768-row cache), and the Llama-shaped
-decode with a T5-style bucketed position bias or with relative key/value
-embeddings.
+4096 plus 4 attention sinks over a 32768-row cache), the wide-group decodes
+(Llama-3-70B-shaped 64 heads over 8 KV heads, Qwen2-7B-shaped 28 over 4),
+and the Llama-shaped decode with a T5-style bucketed position bias or with
+relative key/value embeddings.
 
 `mla` holds latent (MLA) attention in absorbed form: the DeepSeek-V2-Lite-
 shaped decode (16 heads, kv_rank 512, S=8192) and a DeepSeek-V3-shaped one
@@ -732,7 +733,8 @@ def main():
         rec["configs"] = [run_config(w, args, kv_buffers=4 if w.T == 1 else 1)
                           for w in (workloads.LLAMA_CHUNKED, workloads.GEMMA2_SWA,
                                     workloads.LATENT_DECODE, workloads.LATENT_NONCAUSAL,
-                                    workloads.LLAMA_STREAMING)]
+                                    workloads.LLAMA_STREAMING, workloads.LLAMA70_DECODE,
+                                    workloads.QWEN2_DECODE)]
         # Relative-position terms on the Llama-shaped decode.
         for kind, label in (("position_bias", "llama3-8b-shaped decode with a T5-style bucketed position bias "
                                               "(32 buckets, max distance 128)"),

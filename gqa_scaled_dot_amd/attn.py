@@ -253,15 +253,22 @@ def _stream_ptr(stream, device):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def workspace_for(nbytes: int, device):
-    """A cached device buffer of at least nbytes (None for 0)."""
+def workspace_for(nbytes: int, device, stream=None):
+    """A cached device buffer of at least nbytes (None for 0), one per
+    (device, stream): calls in flight at the same time must not share a
+    workspace, and calls on one stream run in order. The buffer is allocated
+    with its stream current, so when a larger one replaces it the caching
+    allocator hands the old memory out again only in that stream's order."""
     if nbytes <= 0:
         return None
     torch = _torch()
-    key = (device.type, device.index)
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    key = (device.type, device.index, stream.cuda_stream)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        with torch.cuda.stream(stream):
+            ws = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws
 
@@ -330,7 +337,7 @@ def attn_forward(q, k, v, bias=None, *, out=None, workspace=None, stream=None, *
         out = torch.empty((T, H * Dv), dtype=torch.float32, device=q.device)
     need = int(L.attn_workspace_size(ctypes.byref(p)))
     if workspace is None:
-        workspace = workspace_for(need, q.device)
+        workspace = workspace_for(need, q.device, stream)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     rc = L.attn_forward(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(),
@@ -351,7 +358,7 @@ def prepare_forward(q, k, v, bias=None, *, out, workspace=None, stream=None, **p
     L = _lib.lib()
     need = int(L.attn_workspace_size(ctypes.byref(p)))
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = workspace_for(need, q.device)
+        workspace = workspace_for(need, q.device, stream)
     args = (ctypes.byref(p), ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
             ctypes.c_void_p(v.data_ptr()),
             ctypes.c_void_p(bias.data_ptr() if bias is not None else None),
@@ -386,7 +393,7 @@ def _forward_append_args(q, k, v, k_new, v_new, offset, bias, out, workspace, st
         out = torch.empty((T, H * Dv), dtype=torch.float32, device=q.device)
     need = int(L.attn_workspace_size(ctypes.byref(p)))
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = workspace_for(need, q.device)
+        workspace = workspace_for(need, q.device, stream)
     args = (ctypes.byref(p), ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()),
             ctypes.c_void_p(v.data_ptr()), ctypes.c_void_p(k_new.data_ptr()),
             ctypes.c_void_p(v_new.data_ptr()), ctypes.c_int64(k_new.shape[0]), ctypes.c_int64(int(offset)),
@@ -645,7 +652,7 @@ def _mla_args(q, state, k_b, v_b, out, workspace, stream, params):
         out = _torch().empty((T, H * Dv), dtype=_torch().float32, device=q.device)
     need = int(L.attn_mla_workspace_size(ctypes.byref(p)))
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = workspace_for(need, q.device)
+        workspace = workspace_for(need, q.device, stream)
     args = (ctypes.byref(p), ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(state.data_ptr()),
             ctypes.c_void_p(k_b.data_ptr()), ctypes.c_void_p(v_b.data_ptr()), ctypes.c_void_p(out.data_ptr()),
             ctypes.c_void_p(workspace.data_ptr() if workspace is not None else None),

@@ -376,6 +376,16 @@ int resolve(const attn_params* p, Resolved* r) {
     o.P0 = p->pos_offset;
     o.window = p->window;
     o.causal = p->causal != 0;
+    // A window that cannot hide any key of this call is switched off: causal
+    // rows see s > pos - window, which excludes nothing once window > the
+    // last position; non-causal rows see |pos - s| <= window, which excludes
+    // nothing once window >= the largest distance to a key. (This also keeps
+    // every sum of a position and the window that the kernels form below 2^31.)
+    if (o.window > 0) {
+        const int64_t last = o.P0 + (o.T > 0 ? o.T - 1 : 0);
+        const int64_t reach = o.causal ? last + 1 : (last > o.S - 1 - o.P0 ? last : o.S - 1 - o.P0);
+        if (o.window >= reach) o.window = 0;
+    }
     o.bias_kind = p->bias_kind;
     // Sizes of every tensor must stay far below 2^62 bytes.
     const double elems = (double)o.T * o.H * (double)(o.D > o.Dv ? o.D : o.Dv) +
@@ -395,9 +405,9 @@ int resolve(const attn_params* p, Resolved* r) {
     e.causal = o.causal;
     e.bias_kind = o.bias_kind;
     e.pos_offset = (int32_t)o.P0;
-    // Every position is below 2^31, so a wider window sees every key a window
-    // of 2^31-1 sees.
-    e.window = (int32_t)(o.window < INT32_MAX ? o.window : INT32_MAX);
+    // A window that is still on is below the largest position or distance,
+    // so it is below 2^31.
+    e.window = (int32_t)o.window;
     // Sinks only matter beside a window; keys past S do not exist.
     e.sinks = o.window > 0 ? (int32_t)(p->sinks < o.S ? p->sinks : o.S) : 0;
     e.has_alibi = p->alibi != ATTN_ALIBI_NONE;

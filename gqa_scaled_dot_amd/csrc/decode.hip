@@ -855,7 +855,10 @@ hipError_t launch_split_nq(const Problem& p, const DecodePlan& plan, float* ws, 
             if constexpr (KV <= 5) return launch_split_t<D, DV, 4>(p, plan, ws, L);
             break;
         case 8:
-            if constexpr (KV <= 2) return launch_split_t<D, DV, 8>(p, plan, ws, L);
+            // Eight rows (a group of 8 query heads, or 7 padded to 8) at
+            // D = Dv = 128 fit in 189-218 registers at one batch per lane; the
+            // far instance for relative-position terms spills (rare shapes).
+            if constexpr (KV <= 4) return launch_split_t<D, DV, 8>(p, plan, ws, L);
             break;
         default: break;
     }
@@ -868,7 +871,7 @@ hipError_t launch_split_nq(const Problem& p, const DecodePlan& plan, float* ws, 
 // each holds in registers without spilling.
 static int decode_max_nq(int D, int Dv) {
     if (D == 64 && Dv == 64) return 8;
-    if (D == 128 && Dv == 128) return 4;
+    if (D == 128 && Dv == 128) return 8;
     if (D == 192 && Dv == 128) return 4;
     if (D == 256 && Dv == 256) return 2;
     return 0;

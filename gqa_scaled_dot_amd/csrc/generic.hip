@@ -1,8 +1,9 @@
 // Correctness path of op `attention` for any head widths: one workgroup per
 // (query row, head). It makes two passes over the visible keys: the first
 // finds the row's largest score, the second forms the max-subtracted
-// weights (catalogue op `softmax`: "max-subtracted so large logits do not
-// overflow") 256 keys at a time and accumulates weight * v into LDS.
+// weights (catalogue op `softmax` subtracts the row maximum first, which
+// keeps exp from overflowing) 256 keys at a time and accumulates weight * v
+// into LDS.
 // Slow but shape-agnostic; the tuned decode and prefill kernels cover the
 // common widths.
 #include "device_common.h"

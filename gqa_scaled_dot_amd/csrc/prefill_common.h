@@ -62,7 +62,7 @@ __device__ __forceinline__ void visible_keys(const Epilogue& e, int S, int pf, i
         if (e.window > 0) klo = max(0, pf - e.window + 1);
     } else if (e.window > 0) {
         klo = max(0, pf - e.window);
-        khi = min(S, pl + e.window + 1);
+        khi = (int)min((int64_t)S, (int64_t)pl + e.window + 1);
     }
 }
 
@@ -116,7 +116,7 @@ __device__ __forceinline__ void tile_visibility(const Epilogue& e, int s_first, 
         any_vis = s_first <= wpl && (e.window == 0 || s_last > wpf - e.window);
         all_vis = s_last <= wpf && (e.window == 0 || s_first > wpl - e.window);
     } else if (e.window > 0) {
-        any_vis = s_first <= wpl + e.window && s_last >= wpf - e.window;
+        any_vis = (int64_t)s_first <= (int64_t)wpl + e.window && s_last >= wpf - e.window;
         all_vis = max(max(abs(wpf - s_first), abs(wpf - s_last)),
                       max(abs(wpl - s_first), abs(wpl - s_last))) <= e.window;
     } else {

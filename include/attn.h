@@ -4,8 +4,9 @@
  * The C ABI of libattn.so. It implements three ops of the graph protocol's op
  * catalogue (page "https://vtmu.mpakt.dev/api/ops"):
  *
- *   attention    "Scaled dot-product attention with grouped-query support";
- *                q, k and v are flat row-major f32, the score matrix is never
+ *   attention    scaled dot-product attention in which several query heads
+ *                may share one key/value head; q, k and v are flat
+ *                row-major f32, the score matrix is never
  *                written to memory (op `attention`: summary, inputs, params,
  *                features attention.alibi/.bias/.scale/.softcap/.window).
  *   cache_write  writes rows into a preallocated cache in place (op
@@ -25,8 +26,9 @@
  *     synchronisation, not in the return code.
  *   - Every argument is checked before anything is launched, so a call that
  *     returns an error has written nothing. Errors name the parameter or the
- *     feature, following the catalogue's rule that a graph needing a missing
- *     feature is refused with the feature named; attn_last_error() returns
+ *     feature, following the catalogue's rule that a graph which needs an
+ *     unsupported feature is rejected and the error names that feature;
+ *     attn_last_error() returns
  *     that text for the calling thread.
  *   - Calls that write overlapping memory on one stream are ordered by the
  *     stream; on different streams they race.
@@ -77,7 +79,7 @@ extern "C" {
  *   v_head_dim   value width per head; 0 = absent = head_dim.
  *   causal       default 1. Causal: key s is visible to query row t when
  *                s <= pos with pos = pos_offset + t.
- *   pos_offset   absolute position of the first query row (>= 0, default 0);
+ *   pos_offset   the position query row 0 sits at (>= 0, default 0);
  *                key row s sits at position s. With a KV cache, k and v are
  *                the whole caches (S = maxRows) and causal masking hides the
  *                rows past the current position, which are never read.
@@ -86,7 +88,7 @@ extern "C" {
  *                q.k only, never the ALiBi or bias terms.
  *   softcap      0 = off, > 0: x = softcap * tanh(x / softcap), applied to the
  *                scaled score before ALiBi, bias and the mask (feature
- *                attention.softcap: "before the mask").
+ *                attention.softcap places the cap ahead of masking).
  *   window       0 = off, > 0: sliding window. Causal: pos - window < s <= pos.
  *                Non-causal: |pos - s| <= window.
  *   alibi, alibi_max, alibi_slopes
@@ -247,8 +249,8 @@ int attn_forward_append(const attn_params* p, const float* q, float* k, float* v
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Op `rope` (graph protocol op catalogue: "Rotary position embedding over
- * [tokens, heads*headDim]"; params headDim, base, offset, rotaryDim,
+ * Op `rope` (graph protocol op catalogue: rotary position embedding of a
+ * [tokens, heads*headDim] tensor; params headDim, base, offset, rotaryDim,
  * interleaved, scaling, invFreq, attentionFactor; features rope.interleaved,
  * rope.rotaryDim, rope.scaling).
  *

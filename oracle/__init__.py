@@ -11,7 +11,7 @@ protocol op catalogue, op `attention`, params):
 
 * kvHeads defaults to heads; query head h reads key/value head
   floor(h * kvHeads / heads) (contiguous groups, the usual grouped-query
-  layout; the page only says "grouped-query support").
+  layout; the page names grouped-query support and gives no mapping).
 * vHeadDim defaults to headDim.
 * causal defaults to true; posOffset defaults to 0 and key row s sits at
   absolute position s.

@@ -1,9 +1,9 @@
 """ALiBi slope tables for the oracle (test infrastructure only).
 
-The op catalogue's `attention` entry names three ways to ask for ALiBi
-("true for BLOOM ALiBi slopes", "MPT ALiBi with alibi_bias_max (usually 8)",
-"explicit per-head ALiBi slopes") but defines none of them. The published
-definitions are used:
+The op catalogue's `attention` entry offers three ways to ask for ALiBi
+(param `alibi`: BLOOM's slopes; param `alibiMax`: MPT's slopes from an
+alibi_bias_max, typically 8; param `alibiSlopes`: one slope per head given
+outright) but defines none of them. The published definitions are used:
 
 * BLOOM / the ALiBi paper (Press, Smith and Lewis, "Train Short, Test Long"):
   with p the largest power of two not above H, head i (1-based) of the first

@@ -1,8 +1,8 @@
 """The op catalogue's own primitive ops, in numpy f64, for the composition pin.
 
 Each function follows its catalogue entry (graph protocol op catalogue):
-`slice` ("a window along the leading axis or the last one"), `matmul`
-(with `transB`: read b as [out, in]), `scale` ("multiply by a constant"),
+`slice` (a contiguous run of the first axis or of the last one), `matmul`
+(with `transB`: read b as [out, in]), `scale` (times a constant factor),
 `softcap` (cap * tanh(x / cap)), `add` (elementwise; b may be a row vector
 or a single value), `causal_mask` (strict upper triangle of each square
 block of the last two dims set to -inf) and `softmax` (over the last

@@ -2,7 +2,8 @@
 
 The library must load, export every entry point include/attn.h declares,
 resolve the op's defaults, and refuse bad arguments by name before any
-launch (the catalogue refuses a graph "with the feature named").
+launch (the catalogue rejects a graph that needs an unsupported feature and
+names that feature).
 """
 
 import ctypes
@@ -108,6 +109,20 @@ def test_plans():
     assert ga.attn_plan(2, 4, posOffset=10, window=2, sinks=1, **BASE)["path"] == "decode"
     # Sinks without a window change nothing.
     assert ga.attn_plan(1, 4096, posOffset=4095, sinks=4, **BASE) == ga.attn_plan(1, 4096, posOffset=4095, **BASE)
+    # A window that cannot hide any key (causal: wider than the last
+    # position; non-causal: at least the largest distance) plans as no window,
+    # with or without sinks, however far past 2^31 it reaches.
+    dec_kw = dict(heads=32, kvHeads=8, headDim=128, posOffset=32767)
+    for w in (32768, 2 ** 31 - 1, 2 ** 40):
+        assert ga.attn_plan(1, 32768, window=w, sinks=4, **dec_kw) == ga.attn_plan(1, 32768, **dec_kw)
+        assert ga.attn_plan(1024, 1024, causal=False, window=w + 1023 - 32768 if w == 32768 else w,
+                            **BASE) == ga.attn_plan(1024, 1024, causal=False, **BASE)
+    # One key short of that still takes the windowed plan's sink split.
+    assert ga.attn_plan(1, 32768, window=32767, sinks=4, **dec_kw) != ga.attn_plan(1, 32768, **dec_kw)
+    # Eight query heads per KV head (64/8, and 28/4 padded to 8) take the
+    # decode path at headDim 128: each KV row is read once for the group.
+    for H, G in ((64, 8), (28, 4), (8, 1)):
+        assert ga.attn_plan(1, 32768, heads=H, kvHeads=G, headDim=128, posOffset=32767)["path"] == "decode"
     # Odd widths have no tuned kernel.
     assert ga.attn_plan(8, 8, heads=4, kvHeads=2, headDim=16)["path"] == "generic"
     assert ga.attn_plan(3, 9, heads=2, headDim=3, vHeadDim=5)["path"] == "generic"

@@ -1,7 +1,8 @@
 """Seeded random combinations of the op's features on every path, against the oracle.
 
 Each case draws a shape (head widths with and without matrix-core
-instances, grouped-query ratios, one to a few dozen query rows) and a mix of
+instances, grouped-query ratios of 1 to 8 query heads per KV head, one to a
+few dozen query rows) and a mix of
 the op's parameters (causal or not, posOffset, window with or without sinks,
 softcap, the three ALiBi forms, either bias layout, a scale override), then
 runs it on the path the library picks and again on every other path the
@@ -21,6 +22,7 @@ from tests.parity import compare
 pytestmark = pytest.mark.gpu
 
 N_CASES = 150
+N_WIDE_CASES = 50  # further cases with 5 to 8 query heads per KV head
 PATHS = {"generic": _lib.ATTN_PATH_GENERIC, "decode": _lib.ATTN_PATH_DECODE, "prefill": _lib.ATTN_PATH_PREFILL}
 WIDTHS = [(64, 64), (128, 128), (192, 128), (256, 256), (32, 32), (80, 48)]
 
@@ -29,7 +31,8 @@ def _draw(i: int) -> workloads.Workload:
     r = np.random.default_rng(np.random.SeedSequence([2024, i]))
     D, Dv = WIDTHS[r.integers(len(WIDTHS))]
     G = int(r.choice([1, 2, 4, 8]))
-    hpg = int(r.choice([1, 2, 4]))
+    wide = N_CASES <= i < N_CASES + N_WIDE_CASES
+    hpg = int(r.choice([5, 6, 7, 8])) if wide else int(r.choice([1, 2, 4]))
     H = G * hpg
     T = int(r.choice([1, 1, 2, 3, int(r.integers(5, 70))]))
     S = int(r.integers(max(T, 1), 700))
@@ -64,7 +67,7 @@ def _draw(i: int) -> workloads.Workload:
     return workloads.Workload(**kw)
 
 
-@pytest.mark.parametrize("i", range(N_CASES))
+@pytest.mark.parametrize("i", range(N_CASES + N_WIDE_CASES))
 def test_random_combination(i):
     w = _draw(i)
     q, k, v, bias = w.tensors()

@@ -26,10 +26,11 @@ def _check(w, what=None, expect_path="decode"):
 
 
 @pytest.mark.parametrize("D, Dv", [(64, 64), (128, 128), (192, 128), (256, 256)])
-@pytest.mark.parametrize("H, G, T", [(8, 2, 1), (16, 16, 1), (8, 4, 1), (4, 1, 1), (8, 8, 2), (6, 3, 1), (8, 8, 3), (16, 2, 1)])
+@pytest.mark.parametrize("H, G, T", [(8, 2, 1), (16, 16, 1), (8, 4, 1), (4, 1, 1), (8, 8, 2), (6, 3, 1), (8, 8, 3),
+                                     (16, 2, 1), (64, 8, 1), (28, 4, 1), (7, 1, 1), (12, 4, 2)])
 def test_decode_shapes(D, Dv, H, G, T):
     nq = T * H // G
-    if nq > {64: 8, 128: 4, 192: 4, 256: 2}[D]:
+    if nq > {64: 8, 128: 8, 192: 4, 256: 2}[D]:
         pytest.skip("more query rows per group than this width's decode instance holds")
     S = 777
     w = _wl(T=T, S=S, heads=H, kvHeads=G, headDim=D, vHeadDim=Dv, posOffset=S - T, seed=D + H + T)
@@ -114,6 +115,15 @@ def test_llama_decode_full_size():
     t.cuda.synchronize()
     ref = oracle.attention(q, k, v, **w.params())
     assert_close(got.cpu().numpy(), ref, w.name)
+
+
+@pytest.mark.parametrize("w", [workloads.LLAMA70_DECODE, workloads.QWEN2_DECODE], ids=["64-8", "28-4"])
+def test_wide_group_decode_full_size(w):
+    # 8 (or 7) query heads per KV head take the decode path, all rows of a
+    # group in one workgroup; every output element against the oracle.
+    plan = ga.attn_plan(w.T, w.S, **w.params())
+    assert plan["path"] == "decode", plan
+    _check(w)
 
 
 def test_latent_alibi_bias_decode_full_size():

@@ -151,3 +151,14 @@ def test_prefill_key_splits_match(splits, variant):
         compare(q, k, v, None, w.params(), what=f"prefill splits={splits}")
     finally:
         ga.attn_set_option("prefill_splits", 0)
+
+
+@pytest.mark.parametrize("window", [1000, 2 ** 31 - 1, 2 ** 40])
+@pytest.mark.parametrize("causal", [False, True])
+def test_prefill_windows_wider_than_any_distance(window, causal, variant):
+    # Windows at and past 2^31 - 1: a window that cannot hide a key must give
+    # the result without one (no position + window sum may wrap), and one that
+    # still hides keys (1000 of 1023 distances) must keep hiding them.
+    w = workloads.Workload("wide window", T=1024, S=1024, heads=8, kvHeads=2, headDim=128,
+                           causal=causal, window=window, seed=window % 997)
+    _check(w, rows=sample_rows(w.T, seed=3, edges=(1000, 23)), what=f"window={window} causal={causal}")

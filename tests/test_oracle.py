@@ -148,7 +148,7 @@ def test_closed_form_softcap_saturates_and_bias_masks_after_it():
     out = oracle.attention(q, k, v, heads=1, headDim=1, causal=False, scale=1.0)
     assert out[0, 0] == pytest.approx(4.0, abs=1e-12)
     # A -1e9 bias still masks when softcap is on: it is added after the cap
-    # (the catalogue applies softcap "before the mask"; the bias is how a
+    # (the catalogue puts softcap ahead of masking; the bias is how a
     # caller masks). Were it capped, the key would keep weight e^-20.
     bias = np.array([[0.0, -1e9]], np.float32)
     out = oracle.attention(q, k, v, bias, heads=1, headDim=1, causal=False, scale=1.0, softcap=10.0)

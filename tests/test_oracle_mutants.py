@@ -57,6 +57,14 @@ ROPE_MUTANTS = {
     "rope_longrope_sets_swapped": ('ext = s["long_factor"] if seq_len > orig else s["short_factor"]',
                                    'ext = s["short_factor"] if seq_len > orig else s["long_factor"]'),
     "rope_yarn_temperature": ("return 0.1 * k * math.log(scale) + 1.0", "return 0.1 * k * math.log(scale)"),
+    # One table entry one f32 ulp off, and the frequencies computed in f32:
+    # both within the transformers pin's 5e-7, caught by the exact-table pin.
+    "rope_table_one_ulp": ("    return _f32(inv), float(np.float32(af))",
+                           "    inv = _f32(inv)\n"
+                           "    inv[len(inv) // 3] = np.nextafter(inv[len(inv) // 3], np.float32(1))\n"
+                           "    return inv, float(np.float32(af))"),
+    "rope_table_f32_power": ("[float(base) ** (-2.0 * i / rd) for i in range(rd // 2)]",
+                             "[float(np.float32(base) ** np.float32(-2.0 * i / rd)) for i in range(rd // 2)]"),
 }
 
 

@@ -239,3 +239,144 @@ def test_interleaved_rotation_matches_gptj():
     want = torch.cat([rot, xt[..., rd:]], dim=-1).reshape(T, H * D).numpy()
     got = oracle.rope(x, headDim=D, rotaryDim=rd, offset=p0, interleaved=True, invFreq=inv)
     np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+
+
+# ---- every table entry against a 50-digit evaluation ------------------------------
+#
+# The oracle computes each table entry in f64 (the C library's pow, log and
+# exp) and rounds it to f32 once. Here the same definitions are evaluated in
+# 50-digit decimal arithmetic, with pi from Machin's formula and powers as
+# exp(e ln b), and every f32 entry must be exactly the f32 nearest to that
+# value: the last bit of the oracle's table is then fixed by the mathematics,
+# not by the library's pow.
+
+from decimal import Decimal as Dec, localcontext
+
+DIGITS = 50
+
+
+def _dpi() -> Dec:
+    """pi = 16 atan(1/5) - 4 atan(1/239) (Machin), atan by its Taylor series."""
+    def atan_inv(n):
+        x = Dec(1) / n
+        x2, term, total, k = x * x, x, x, 1
+        while True:
+            term *= -x2
+            k += 2
+            nxt = total + term / k
+            if nxt == total:
+                return total
+            total = nxt
+    return 16 * atan_inv(5) - 4 * atan_inv(239)
+
+
+def _dpow(b: Dec, e: Dec) -> Dec:
+    return (e * b.ln()).exp()
+
+
+def exact_table(rd, base, scaling=None, seq_len=1):
+    """(invFreq entries, attention factor) as 50-digit decimals, following the
+    definitions the oracle's docstrings state (RoFormer's base^(-2i/rd); the
+    linear, llama3, yarn, dynamic and longrope scalings)."""
+    with localcontext() as ctx:
+        ctx.prec = DIGITS
+        pi = _dpi()
+        b = Dec(base)
+        s = dict(scaling or {})
+        kind = s.get("rope_type", "default")
+        if kind == "dynamic":
+            orig = Dec(s.get("original_max_position_embeddings") or s["max_position_embeddings"])
+            f = Dec(s["factor"])
+            if seq_len > orig:
+                b = b * _dpow(f * seq_len / orig - (f - 1), Dec(rd) / (rd - 2))
+        theta = [_dpow(b, Dec(-2 * i) / rd) for i in range(rd // 2)]
+        af = Dec(1)
+        if kind == "linear":
+            inv = [t / Dec(s["factor"]) for t in theta]
+        elif kind == "llama3":
+            f, lo_f, hi_f = Dec(s["factor"]), Dec(s["low_freq_factor"]), Dec(s["high_freq_factor"])
+            orig = Dec(s["original_max_position_embeddings"])
+            inv = []
+            for t in theta:
+                wl = 2 * pi / t
+                if wl < orig / hi_f:
+                    inv.append(t)
+                elif wl > orig / lo_f:
+                    inv.append(t / f)
+                else:
+                    sm = (orig / wl - lo_f) / (hi_f - lo_f)
+                    inv.append((1 - sm) * t / f + sm * t)
+        elif kind == "yarn":
+            f, orig = Dec(s["factor"]), Dec(s["original_max_position_embeddings"])
+            b_fast, b_slow = Dec(s.get("beta_fast") or 32), Dec(s.get("beta_slow") or 1)
+
+            def index_for(turns):
+                return rd * (orig / (turns * 2 * pi)).ln() / (2 * b.ln())
+
+            lo, hi = index_for(b_fast), index_for(b_slow)
+            if s.get("truncate", True):
+                lo, hi = Dec(math.floor(lo)), Dec(math.ceil(hi))
+            lo, hi = max(lo, Dec(0)), min(hi, Dec(rd - 1))
+            if lo == hi:
+                hi += Dec("0.001")
+            inv = []
+            for i, t in enumerate(theta):
+                ramp = min(max((i - lo) / (hi - lo), Dec(0)), Dec(1))
+                inv.append(t * (1 - ramp) + t / f * ramp)
+
+            def mscale(k):
+                return Dec("0.1") * k * f.ln() + 1 if f > 1 else Dec(1)
+            m, m_all = s.get("mscale"), s.get("mscale_all_dim")
+            af = mscale(Dec(m)) / mscale(Dec(m_all)) if m and m_all else mscale(Dec(1))
+        elif kind == "longrope":
+            orig = Dec(s["original_max_position_embeddings"])
+            ext = s["long_factor"] if seq_len > orig else s["short_factor"]
+            inv = [t / Dec(float(e)) for t, e in zip(theta, ext)]
+            f = Dec(s["factor"]) if s.get("factor") is not None else Dec(s["max_position_embeddings"]) / orig
+            af = (1 + f.ln() / orig.ln()).sqrt() if f > 1 else Dec(1)
+        else:
+            inv = theta
+        return inv, af
+
+
+def nearest_f32(x: Dec) -> np.float32:
+    """The f32 nearest to x, checked against both neighbours in decimal."""
+    f = np.float32(float(x))
+    with localcontext() as ctx:
+        ctx.prec = DIGITS
+        d = abs(x - Dec(float(f)))
+        for nb in (np.nextafter(f, np.float32(np.inf)), np.nextafter(f, np.float32(-np.inf))):
+            assert d <= abs(x - Dec(float(nb))), f"{x} rounds nearer to {nb!r} than {f!r}"
+    return f
+
+
+EXACT_CASES = [
+    ("default-128", 128, 10000.0, None, 1),
+    ("default-64-500k", 64, 500000.0, None, 1),
+    ("default-96-1e6", 96, 1e6, None, 1),
+    ("linear", 128, 10000.0, dict(rope_type="linear", factor=4.0), 1),
+    ("llama3.1", 128, 500000.0, dict(rope_type="llama3", factor=8.0, low_freq_factor=1.0, high_freq_factor=4.0,
+                                      original_max_position_embeddings=8192), 1),
+    ("yarn", 64, 10000.0, dict(rope_type="yarn", factor=4.0, original_max_position_embeddings=4096), 1),
+    ("yarn-mscale", 64, 10000.0, dict(rope_type="yarn", factor=4.0, original_max_position_embeddings=4096,
+                                      beta_fast=16, beta_slow=2, mscale=0.707, mscale_all_dim=1.0), 1),
+    ("yarn-untruncated", 128, 1e6, dict(rope_type="yarn", factor=4.0, original_max_position_embeddings=4096,
+                                        truncate=False), 1),
+    ("dynamic-long", 64, 10000.0, dict(rope_type="dynamic", factor=2.0, max_position_embeddings=16384), 32768),
+    ("dynamic-short", 64, 10000.0, dict(rope_type="dynamic", factor=2.0, max_position_embeddings=16384), 8000),
+    ("longrope-short", 64, 10000.0, dict(rope_type="longrope", short_factor=SHORT, long_factor=LONG,
+                                         original_max_position_embeddings=4096, max_position_embeddings=131072),
+     4096),
+    ("longrope-long", 64, 10000.0, dict(rope_type="longrope", short_factor=SHORT, long_factor=LONG,
+                                        original_max_position_embeddings=4096, max_position_embeddings=131072),
+     9000),
+]
+
+
+@pytest.mark.parametrize("name, rd, base, scaling, seq_len", EXACT_CASES, ids=[c[0] for c in EXACT_CASES])
+def test_table_entries_are_the_nearest_f32(name, rd, base, scaling, seq_len):
+    want, af_want = exact_table(rd, base, scaling, seq_len)
+    got, af = oracle.rope_table(rd, base=base, scaling=scaling, seq_len=seq_len)
+    want32 = np.array([nearest_f32(x) for x in want], dtype=np.float32)
+    np.testing.assert_array_equal(got.view(np.uint32), want32.view(np.uint32), err_msg=name)
+    assert np.float32(af) == nearest_f32(af_want), name

@@ -181,6 +181,14 @@ LLAMA_STREAMING = Workload("llama3-8b-shaped streaming decode: window 4096 + 4 s
                            T=1, S=32768, heads=32, kvHeads=8, headDim=128, posOffset=32767,
                            window=4096, sinks=4)
 
+# Wide grouped-query groups: 8 query heads per KV head (Llama-3-70B's 64/8)
+# and 7 (Qwen2-7B's 28/4), each KV row read once for the whole group.
+LLAMA70_DECODE = Workload("llama3-70b-shaped GQA decode T=1 S=32768 H=64 G=8 D=128",
+                          T=1, S=32768, heads=64, kvHeads=8, headDim=128, posOffset=32767)
+
+QWEN2_DECODE = Workload("qwen2-7b-shaped GQA decode T=1 S=32768 H=28 G=4 D=128",
+                        T=1, S=32768, heads=28, kvHeads=4, headDim=128, posOffset=32767)
+
 LLAMA_PREFILL = Workload("llama3-8b-shaped causal prefill T=S=4096 H=32 G=8 D=128",
                          T=4096, S=4096, heads=32, kvHeads=8, headDim=128)
 
