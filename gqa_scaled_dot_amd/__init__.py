@@ -9,6 +9,7 @@ has no fallback implementation and raises if the library is not built.
 """
 
 from .attn import (AttnError, attn_cache_write, attn_cache_write2, attn_forward, attn_forward_append,
+                   attn_forward_noalloc,
                    attn_last_error, attn_plan,
                    attn_rope, attn_rope_cache_write, attn_rope_table,
                    prepare_cache_write, prepare_cache_write2, prepare_forward, prepare_forward_append,
@@ -26,5 +27,5 @@ __all__ = [
     "prepare_cache_write", "prepare_cache_write2", "prepare_forward", "prepare_forward_append",
     "attn_rope", "attn_rope_cache_write", "attn_rope_table", "make_rope_params", "prepare_rope_cache_write",
     "attn_mla_forward", "attn_mla_plan", "attn_mla_validate", "attn_mla_workspace_size",
-    "make_mla_params", "prepare_mla_forward",
+    "make_mla_params", "prepare_mla_forward", "attn_forward_noalloc",
 ]

@@ -19,6 +19,7 @@ PATH_NAMES = {0: "empty", 1: "zero", 2: "generic", 3: "decode", 4: "prefill", 5:
 (ATTN_ROPE_DEFAULT, ATTN_ROPE_LINEAR, ATTN_ROPE_LLAMA3, ATTN_ROPE_YARN, ATTN_ROPE_LONGROPE,
  ATTN_ROPE_DYNAMIC) = range(6)
 ATTN_ROPE_MAX_ROTARY_DIM = 256
+ATTN_NOALLOC_SCRATCH_BYTES = 16 << 20
 ROPE_SCALING = {"default": ATTN_ROPE_DEFAULT, "linear": ATTN_ROPE_LINEAR, "llama3": ATTN_ROPE_LLAMA3,
                 "yarn": ATTN_ROPE_YARN, "longrope": ATTN_ROPE_LONGROPE, "dynamic": ATTN_ROPE_DYNAMIC}
 
@@ -29,7 +30,7 @@ EXPORTS = (
     "attn_set_option", "attn_timing_enable", "attn_timing_collect",
     "attn_rope_params_init", "attn_rope_table", "attn_rope", "attn_rope_cache_write",
     "attn_mla_params_init", "attn_mla_validate", "attn_mla_workspace_size", "attn_mla_plan",
-    "attn_mla_forward",
+    "attn_mla_forward", "attn_forward_noalloc",
 )
 
 
@@ -118,6 +119,8 @@ def lib():
     L.attn_workspace_size.restype = ctypes.c_size_t
     L.attn_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     L.attn_forward.restype = ctypes.c_int
+    L.attn_forward_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp]
+    L.attn_forward_noalloc.restype = ctypes.c_int
     L.attn_forward_append.argtypes = [P, vp, vp, vp, vp, vp, ctypes.c_int64, ctypes.c_int64, vp, vp, vp,
                                       ctypes.c_size_t, vp]
     L.attn_forward_append.restype = ctypes.c_int

@@ -348,6 +348,20 @@ def attn_forward(q, k, v, bias=None, *, out=None, workspace=None, stream=None, *
     return out
 
 
+def attn_forward_noalloc(q, k, v, bias=None, *, out, stream=None, **params):
+    """attn_forward with the split state in the library's own per-GPU scratch
+    array: the call allocates nothing, so `out` [T, heads*vHeadDim] must be
+    given. Calls that overlap in time on one GPU race on that array. Returns out."""
+    T, S, H, Dv, bias_kind = _check_forward(q, k, v, bias, out, params)
+    p, keep = make_params(T, S, bias_kind=bias_kind, **params)
+    rc = _lib.lib().attn_forward_noalloc(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                         bias.data_ptr() if bias is not None else None, out.data_ptr(),
+                                         _stream_ptr(stream, q.device))
+    del keep
+    _check(rc)
+    return out
+
+
 def prepare_forward(q, k, v, bias=None, *, out, workspace=None, stream=None, **params):
     """Marshal one attn_forward call once and return a zero-argument callable
     that repeats it (same tensors, same stream). For timing loops, where

@@ -16,6 +16,14 @@
 #include "attn.h"
 #include "kernels.h"
 
+// Workspace of attn_forward_noalloc: the key-range splits' partial softmax
+// states live in this array instead of a caller's buffer, for callers that
+// cannot allocate. Every GPU the library runs on holds its own copy until the
+// process ends. Host code never uses this name as an address (on the host it
+// is only a stand-in): it takes each device's address once, through
+// hipGetSymbolAddress, and passes that to the kernels.
+static __device__ __align__(256) unsigned char scratch[ATTN_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -943,6 +951,39 @@ int check_cache_write(const char* which, float* cache, int64_t max_rows, int64_t
 }
 
 
+// The device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+int scratch_address(hipStream_t stream, void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(ATTN_ERR_DEVICE, "scratch: hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(ATTN_ERR_UNSUPPORTED, "scratch: device %d past the %d this library tracks", dev, kMaxDevices);
+    if (stream) {
+        // The stream must run on the current device: the address is that device's.
+        hipDevice_t sdev = -1;
+        e = hipStreamGetDevice(stream, &sdev);
+        if (e != hipSuccess)
+            return fail(ATTN_ERR_DEVICE, "scratch: hipStreamGetDevice: %s", hipGetErrorString(e));
+        if ((int)sdev != dev)
+            return fail(ATTN_ERR_INVALID, "stream: belongs to device %d, but device %d is current", (int)sdev, dev);
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(ATTN_ERR_DEVICE, "scratch: hipGetSymbolAddress: %s", hipGetErrorString(e));
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return ok();
+}
+
 // attn_forward's checks of the tensors and the workspace (`need` bytes) for
 // a valid plan.
 int check_forward_args(const attn_params* p, const Resolved& r, size_t need, const float* q, const float* k,
@@ -1099,6 +1140,30 @@ int attn_forward(const attn_params* p, const float* q, const float* k, const flo
     rc = check_forward_args(p, r, plan.workspace, q, k, v, bias, out, workspace, workspace_bytes);
     if (rc) return rc;
     return run_plan(r, plan, make_problem(r, q, k, v, bias, out), workspace, (hipStream_t)stream);
+}
+
+int attn_forward_noalloc(const attn_params* p, const float* q, const float* k, const float* v,
+                         const float* bias, float* out, void* stream) {
+    Resolved r;
+    int rc = resolve(p, &r);
+    if (rc) return rc;
+    Plan plan;
+    rc = make_plan(r, &plan);
+    if (rc) return rc;
+    if (plan.path == ATTN_PATH_EMPTY) return ok();
+    if (plan.workspace > (size_t)ATTN_NOALLOC_SCRATCH_BYTES)
+        return fail(ATTN_ERR_UNSUPPORTED,
+                    "workspace: this call needs %zu bytes of split state, past the %zu-byte built-in scratch "
+                    "(use attn_forward with a workspace)",
+                    plan.workspace, (size_t)ATTN_NOALLOC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    if (plan.workspace) {
+        rc = scratch_address((hipStream_t)stream, &ws);
+        if (rc) return rc;
+    }
+    rc = check_forward_args(p, r, plan.workspace, q, k, v, bias, out, ws, ws ? (size_t)ATTN_NOALLOC_SCRATCH_BYTES : 0);
+    if (rc) return rc;
+    return run_plan(r, plan, make_problem(r, q, k, v, bias, out), ws, (hipStream_t)stream);
 }
 
 int attn_forward_append(const attn_params* p, const float* q, float* k, float* v, const float* k_new,

@@ -192,6 +192,35 @@ int attn_forward(const attn_params* p, const float* q, const float* k, const flo
                  const float* bias, float* out, void* workspace, size_t workspace_bytes,
                  void* stream);
 
+/* Size of the device array attn_forward_noalloc keeps its split state in. */
+#define ATTN_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/*
+ * attn_forward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same plan, kernels and result as attn_forward, with the key-range
+ * splits' partial softmax states in a library-owned array of
+ * ATTN_NOALLOC_SCRATCH_BYTES (16 MiB) per GPU instead of a caller's workspace.
+ *   q, k, v, bias, out, stream  as for attn_forward; the caller still
+ *                               provides every input and the output.
+ * The array is a file-scope device variable: each GPU the library runs on
+ * holds its own copy from its first use until the process ends. The call
+ * allocates nothing and calls no allocating routine; its first call on a
+ * device looks the array's address up (hipGetSymbolAddress) with that
+ * device current, and later calls reuse it. `stream` must belong to the
+ * current device (else ATTN_ERR_INVALID).
+ * A call whose plan needs more split state than the array holds (the
+ * figure attn_workspace_size reports for attn_forward's own plan) is
+ * refused with ATTN_ERR_UNSUPPORTED before anything runs; decode calls
+ * need at most a few MiB (heads x splits x (v_head_dim + 2) floats).
+ * Every call on one GPU shares that GPU's array, and nothing in it needs
+ * clearing (each split writes its whole state before the merge reads it):
+ * two calls that overlap in time on one GPU, on different streams or from
+ * different threads, race on it.
+ */
+int attn_forward_noalloc(const attn_params* p, const float* q, const float* k, const float* v,
+                         const float* bias, float* out, void* stream);
+
 /*
  * Op `cache_write`: cache[offset + r, :] = values[r, :] for r < rows, in
  * place; the rest of the cache is untouched. An exact bit copy.
