@@ -31,8 +31,9 @@ protocol op catalogue, op `attention`, params):
 
 Readings where the pages are silent are listed in the module docstrings of
 `oracle.alibi` and in the core's header comment. Parity unpinned: a row with
-no visible key gives 0, and non-causal ALiBi uses -slope * |pos - s|; both
-are readings that no page fact can confirm.
+no visible key gives 0, a reading that no page fact and no published method
+can confirm. (Non-causal ALiBi uses -slope * |pos - s|, MPT's bidirectional
+form; the tests pin it against MPT's own construction of that bias.)
 """
 
 from __future__ import annotations

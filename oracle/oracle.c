@@ -42,12 +42,13 @@
  *     embedding rel_k[r] is added to k before the product with q (so it is
  *     scaled with it) and rel_v[r] to v in the weighted sum.
  *
- * Parity unpinned (readings, not facts the pages fix, so nothing outside
- * this definition can confirm them): the zero output of a row with no
- * visible key, and the ALiBi term's symmetric form -slope * |pos - s| on
- * non-causal rows (on causal rows it differs from BLOOM's slope * s and
- * MPT's slope * (s - (S - 1)) only by a per-row constant, which the softmax
- * removes; the pins check that).
+ * Parity unpinned (a reading, not a fact the pages fix, so nothing outside
+ * this definition can confirm it): the zero output of a row with no visible
+ * key. The ALiBi term -slope * |pos - s| is, on non-causal rows, MPT's
+ * bidirectional bias (its "full" form: minus the absolute key - query
+ * distance), and on causal rows it differs from BLOOM's slope * s and MPT's
+ * slope * (s - (S - 1)) only by a per-row constant, which the softmax
+ * removes; the tests pin both against those models' own constructions.
  *
  * The resolution of absent parameters (defaults, slope tables) happens in the
  * Python wrapper beside this file; this core takes resolved numbers.

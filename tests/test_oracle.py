@@ -341,6 +341,61 @@ def test_alibi_equals_bias_with_same_penalty():
                                       oracle.attention(q, k, v, bias, **kw))
 
 
+def mpt_full_alibi(H: int, S: int, alibi_bias_max: float = 8.0) -> np.ndarray:
+    """MPT's bidirectional ("full") ALiBi bias for an S x S block, built the
+    way that model builds it: a row vector of key positions 1-S .. 0, minus
+    the same positions as a column (the query positions), made non-positive
+    by taking minus its absolute value, then scaled per head by MPT's slopes
+    (2^(-i b / n) over the next power of two n >= H, even-numbered first).
+    Returns [H, S, S] f32."""
+    pos = np.arange(1 - S, 1, dtype=np.float64)
+    diff = pos[None, :] - pos[:, None]                       # key minus query
+    dist = -np.abs(diff)
+    n = 1 << (H - 1).bit_length()
+    m = np.array([2.0 ** (-(i + 1) * alibi_bias_max / n) for i in range(n)])
+    if n != H:
+        m = np.concatenate([m[1::2], m[0::2]])[:H]
+    return (dist[None, :, :] * m[:, None, None]).astype(np.float32)
+
+
+@pytest.mark.parametrize("H, S", [(8, 12), (6, 9), (16, 5)])
+def test_noncausal_alibi_is_mpt_full_bias(H, S):
+    # The non-causal ALiBi reading (-slope * |pos - s|) is MPT's bidirectional
+    # bias: the oracle's alibiMax path must equal the same call with MPT's own
+    # construction passed as the bias input. With 8 or 6 heads the slopes are
+    # powers of two, so slope times distance is exact in f32 and the two agree
+    # bit for bit; 16 heads have slopes 2^(-i/2), where the bias input holds
+    # the f32 rounding of each product (the oracle rounds the slope once),
+    # a difference far below the bar. Also with a window.
+    D = 4
+    q, k, v = _rand((S, H * D), 40 + H), _rand((S, 2 * D), 41), _rand((S, 2 * D), 42)
+    bias = mpt_full_alibi(H, S, 8.0)
+    for extra in ({}, dict(window=3)):
+        kw = dict(heads=H, kvHeads=2 if H % 2 == 0 else 1, headDim=D, causal=False, **extra)
+        if kw["kvHeads"] == 1:
+            kv = (k[:, :D].copy(), v[:, :D].copy())
+        else:
+            kv = (k, v)
+        got = oracle.attention(q, *kv, alibiMax=8.0, **kw)
+        want = oracle.attention(q, *kv, bias, **kw)
+        if H == 16:
+            np.testing.assert_allclose(got, want, rtol=1e-6, atol=1e-7)
+        else:
+            np.testing.assert_array_equal(got, want)
+
+
+def test_noncausal_alibi_mpt_bias_on_a_shifted_block():
+    # Rows at positions P0..P0+T-1 of a longer key range: the rows of MPT's
+    # S x S construction at those positions (its positions are shifted by a
+    # constant, which the differences do not see).
+    H, S, T, P0, D = 8, 14, 5, 6, 4
+    q, k, v = _rand((T, H * D), 45), _rand((S, D), 46), _rand((S, D), 47)
+    bias = np.ascontiguousarray(mpt_full_alibi(H, S)[:, P0:P0 + T, :])
+    kw = dict(heads=H, kvHeads=1, headDim=D, causal=False, posOffset=P0)
+    np.testing.assert_array_equal(oracle.attention(q, k, v, alibi=True, **kw),
+                                  oracle.attention(q, k, v, bias, **kw))
+
+
 def test_alibi_relative_equals_bloom_absolute_when_causal():
     # BLOOM adds +m*s; on causal rows -m*|pos - s| differs by the row constant -m*pos.
     T, S, H, D = 4, 11, 8, 4

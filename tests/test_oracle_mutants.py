@@ -37,6 +37,13 @@ MUTANTS = {
     "sink_ignores_causal": ("        if (s > pos) return 0;\n        if (sink) return 1;",
                             "        if (sink) return 1;\n        if (s > pos) return 0;"),
     "sink_noncausal_dropped": ("if (a->window > 0 && !sink) {", "if (a->window > 0) {"),
+    # ALiBi distance signed (BLOOM's one-sided form carried over to
+    # non-causal rows), and a penalty of |pos - s| + 1: equal to the reading
+    # on causal rows up to a row constant, so only the non-causal pins see them.
+    "alibi_signed_distance": ("double dist = (double)(pos > s ? pos - s : s - pos);",
+                              "double dist = (double)(pos - s);"),
+    "alibi_distance_plus_one": ("double dist = (double)(pos > s ? pos - s : s - pos);",
+                                "double dist = (double)(pos > s ? pos - s : s - pos) + 1.0;"),
 }
 
 # Slips in the rotary embedding (oracle/rope.py), caught by tests/test_oracle_rope.py.
