@@ -68,11 +68,13 @@ class _Args(ctypes.Structure):
 
 
 def build() -> str:
-    """Compile the oracle core with gcc (plain -O2, no fast-math)."""
-    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-o", _LIB + ".tmp", _SRC,
-           "-lpthread", "-lm"]
+    """Compile the oracle core with gcc (plain -O2, no fast-math). Each process
+    writes its own temporary file and renames it into place, so test workers
+    that rebuild at the same time never load a half-written library."""
+    tmp = f"{_LIB}.tmp{os.getpid()}"
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-o", tmp, _SRC, "-lpthread", "-lm"]
     subprocess.run(cmd, check=True)
-    os.replace(_LIB + ".tmp", _LIB)
+    os.replace(tmp, _LIB)
     return _LIB
 
 
