@@ -48,8 +48,12 @@ shaped decode (16 heads, kv_rank 512, S=8192) and a DeepSeek-V3-shaped one
 (128 heads, S=32768): call time, the three kernels' durations, and the
 split kernel's roofline (HBM or fp32 matrix peak, whichever bounds it).
 
+Every benchmarked output is checked against the CPU oracle on the same
+inputs, every row of it (the prefill-shaped ones too, which takes the oracle
+tens of seconds for the largest; --sampled-parity checks ~30 rows instead).
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
-       [--prefill-steps K] [--no-configs]
+       [--prefill-steps K] [--no-configs] [--sampled-parity]
 """
 
 from __future__ import annotations
@@ -77,6 +81,8 @@ KERNEL_SOURCES = {
                 "gqa_scaled_dot_amd/csrc/kernels.h", "gqa_scaled_dot_amd/csrc/rope_device.h"],
     "rope": ["gqa_scaled_dot_amd/csrc/rope.hip", "gqa_scaled_dot_amd/csrc/rope_device.h",
              "gqa_scaled_dot_amd/csrc/kernels.h"],
+    "decode_mfma": ["gqa_scaled_dot_amd/csrc/decode_mfma.hip", "gqa_scaled_dot_amd/csrc/device_common.h",
+                    "gqa_scaled_dot_amd/csrc/kernels.h", "gqa_scaled_dot_amd/csrc/rope_device.h"],
 }
 
 
@@ -167,12 +173,21 @@ def device_clocks():
     return out or None
 
 
-def cpu_threads() -> int:
+def affinity_cpus() -> int:
+    """CPUs this process may run on (len(os.sched_getaffinity(0)))."""
     try:
-        n = len(os.sched_getaffinity(0))
+        return len(os.sched_getaffinity(0))
     except AttributeError:
-        n = os.cpu_count() or 1
-    return max(1, min(n, 16))
+        return os.cpu_count() or 1
+
+
+# A one-GPU box grants its jobs 16 host CPUs, whatever the affinity mask
+# shows, so the oracle runs at most 16 threads; the records state both counts.
+CPU_SHARE = 16
+
+
+def cpu_threads() -> int:
+    return max(1, min(affinity_cpus(), CPU_SHARE))
 
 
 def run_decode(args):
@@ -297,7 +312,7 @@ def run_decode(args):
             total += time.perf_counter() - t0
             reps += 1
         cpu_baseline = {"value": round(alg_bytes * reps / total / 1e9, 4), "unit": "GB/s",
-                        "cores": threads, "kind": "oracle", "cpu": host_cpu(),
+                        "cores": threads, "affinity_cpus": affinity_cpus(), "kind": "oracle", "cpu": host_cpu(),
                         "sample": f"the full decode step (1 query row, 32 heads, 32768 keys), "
                                   f"{reps} runs in {total:.1f} s, f64"}
 
@@ -315,7 +330,10 @@ def run_decode(args):
         "roofline": roofline,
         "cpu_baseline": cpu_baseline,
         "parity": {"max_abs_err": float(err.max()), "ok": parity_ok},
-        "device": {"clocks_after_timed_steps": clocks, "host_cpu": host_cpu(), "host_threads": threads},
+        "device": {"clocks_after_timed_steps": clocks, "host_cpu": host_cpu(), "host_threads": threads,
+                   "host_affinity_cpus": affinity_cpus(),
+                   "host_threads_note": f"the oracle runs min(affinity CPUs, {CPU_SHARE}) threads: "
+                                        f"a one-GPU box grants {CPU_SHARE} host CPUs"},
     }
 
 
@@ -376,7 +394,8 @@ def run_config(w, args, kv_buffers=1, extra=None, label=None):
     plan = ga.attn_plan(w.T, w.S, bias_kind=kind, **params)
     name = label or w.name
     log(f"[bench] workload: {name}; plan {plan}")
-    main_kernel = {"decode": "decode_split", "prefill": "prefill"}.get(plan["path"], "generic")
+    main_kernel = {"decode": "decode_mfma" if plan["variant"] == 1 else "decode_split",
+                   "prefill": "prefill"}.get(plan["path"], "generic")
     qd = torch.from_numpy(q).to(dev)
     # Several copies of the K/V (and bias) so a timed call does not find them
     # in the 256 MB MALL: decode plans rotate over at least 512 MiB of reads.
@@ -423,14 +442,19 @@ def run_config(w, args, kv_buffers=1, extra=None, label=None):
     log(f"[bench]   call {ms_call * 1e3:.1f} us, {main_kernel} {kern_s * 1e6:.1f} us x{k_n}"
         + (f", combine {c_ms / c_n * 1e3:.2f} us" if c_n else "")
         + f": {achieved:.2f} {unit} = {achieved / peak:.1%} of {peak}")
-    rows = sampled_rows(w)
+    # The oracle checks every output row (prefill-shaped calls too, unless
+    # --sampled-parity asks for a row sample).
+    rows = sampled_rows(w) if (args.sampled_parity and w.T > 1) else None
     t_oracle = time.perf_counter()
     ref = oracle.attention(q, k, v, bias, rows=rows, threads=cpu_threads(), **w.params(), **extra)
     t_oracle = time.perf_counter() - t_oracle
-    got = out.cpu().numpy()[rows].astype(np.float64)
+    got = out.cpu().numpy().astype(np.float64)
+    if rows is not None:
+        got = got[rows]
     err = np.abs(got - ref)
     ok = bool(np.all(err <= 1e-4 + 1e-4 * np.abs(ref)))
-    log(f"[bench]   parity on {len(rows)} sampled rows: max |err| {err.max():.3e} ok={ok} "
+    n_rows = w.T if rows is None else len(rows)
+    log(f"[bench]   parity on {'all ' if rows is None else ''}{n_rows} rows: max |err| {err.max():.3e} ok={ok} "
         f"(oracle {t_oracle:.2f} s on {cpu_threads()} threads)")
     rec = {
         "workload": name, "path": plan["path"], "splits": plan["splits"], "kv_buffers": kv_buffers,
@@ -443,7 +467,7 @@ def run_config(w, args, kv_buffers=1, extra=None, label=None):
                      ("bytes_per_launch" if bound == "hbm" else "flops_per_launch"): work,
                      "avg_launch_us": round(kern_s * 1e6, 3),
                      "combine_us": round(c_ms / c_n * 1e3, 3) if c_n else None},
-        "parity": {"rows": len(rows), "max_abs_err": float(err.max()), "ok": ok,
+        "parity": {"rows": n_rows, "all_rows": rows is None, "max_abs_err": float(err.max()), "ok": ok,
                    "oracle_s": round(t_oracle, 3), "oracle_threads": cpu_threads()},
     }
     del kv, qd, out, ws
@@ -690,8 +714,9 @@ def run_rope(args):
     nbytes = 2 * x.size * 4
     kern_s = r_ms / r_n * 1e-3
     achieved = nbytes / kern_s / 1e9
-    rows = sampled_rows(wp)
-    refr = np.stack([oracle.rope(x[r:r + 1], offset=r, **rq)[0] for r in rows])
+    # Every row against the oracle (row t sits at position t).
+    rows = sampled_rows(wp) if args.sampled_parity else list(range(wp.T))
+    refr = oracle.rope(x, offset=0, **rq)[rows]
     errr = np.abs(yd.cpu().numpy()[rows].astype(np.float64) - refr)
     okr = bool(np.all(errr <= 4e-6 + 4e-6 * np.abs(refr)))
     log(f"[bench] rope kernel on q [{wp.T}, {wp.heads * wp.headDim}]: {kern_s * 1e6:.1f} us, "
@@ -715,6 +740,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle timing")
     ap.add_argument("--no-configs", action="store_true",
                     help="only the Llama-shaped decode and prefill, not the other workloads")
+    ap.add_argument("--sampled-parity", action="store_true",
+                    help="check ~30 sampled rows of prefill-shaped outputs instead of every row")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "

@@ -85,7 +85,7 @@ class AttnMlaParams(ctypes.Structure):
 
 class AttnPlanInfo(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("splits", ctypes.c_int32),
-                ("tile_q", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("tile_q", ctypes.c_int32), ("variant", ctypes.c_int32)]
 
 
 class LibraryMissing(ImportError):

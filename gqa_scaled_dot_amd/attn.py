@@ -204,7 +204,7 @@ def attn_plan(T: int, S: int, bias_kind: int = 0, **params) -> dict:
     _check(_lib.lib().attn_plan(ctypes.byref(p), ctypes.byref(info)))
     del keep
     return {"path": _lib.PATH_NAMES.get(info.path, str(info.path)), "splits": info.splits,
-            "tile_q": info.tile_q}
+            "tile_q": info.tile_q, "variant": info.variant}
 
 
 def attn_set_option(name: str, value: int) -> None:

@@ -16,8 +16,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libattn.so")
-SOURCES = ["attn_api.hip", "cache_write.hip", "generic.hip", "decode.hip", "prefill.hip", "prefill16.hip",
-           "rope.hip", "mla.hip"]
+SOURCES = ["attn_api.hip", "cache_write.hip", "generic.hip", "decode.hip", "decode_mfma.hip", "prefill.hip",
+           "prefill16.hip", "rope.hip", "mla.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

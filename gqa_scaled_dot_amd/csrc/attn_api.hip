@@ -52,6 +52,7 @@ int64_t g_opt_decode_block = 0;
 int64_t g_opt_prefill_splits = 0;
 int64_t g_opt_prefill_variant = 0;
 int64_t g_opt_force_path = 0;
+int64_t g_opt_decode_mfma = 0;  // 0: automatic; 1: the matrix-core decode wherever it can serve; -1: never
 int64_t g_opt_mla_splits = 0;
 int64_t g_opt_mla_generic = 0;
 int64_t g_opt_mla_row_groups = 0;
@@ -67,7 +68,8 @@ constexpr int64_t kDecodeMinKeys = 64;
 constexpr int64_t kDecodeChunkAlign = 64; // key chunk granularity (a multiple of 16 row groups x 2 rows)
 constexpr int64_t kDecodeBlock = 256;     // rows per interleaved block, automatic choice (power of two)
 constexpr int64_t kDecodeMaxSplits = 1024;
-constexpr int64_t kDecodeMaxAppend = 64;  // appended rows one decode split takes (two batch steps)
+constexpr int64_t kDecodeMaxAppend = 64;
+constexpr int64_t kDecodeMfmaFrom = 5;    // groups of this many query rows or more take decode_mfma  // appended rows one decode split takes (two batch steps)
 constexpr int64_t kPrefillMaxSplits = 16;
 constexpr int64_t kPrefillMinTilesPerSplit = 4;
 constexpr int64_t kMaxDim = 1 << 16;
@@ -548,7 +550,16 @@ int make_plan(const Resolved& r, Plan* plan, const AppendRows* app = nullptr) {
     }
     const int64_t hpg = r.H / r.G;
     const int64_t nrows = r.T * hpg;
-    const bool dec_ok = nrows <= 16 && attn::decode_supported((int)r.D, (int)r.Dv, next_pow2_nq(nrows));
+    // Two decode kernels: decode_split (rows in registers, VALU arithmetic)
+    // and decode_mfma (matrix cores, up to 16 or 32 rows, no
+    // relative-position terms). The automatic choice takes decode_mfma for
+    // groups wider than kDecodeMfmaFrom rows, where decode_split's work per key
+    // (which grows with the rows) would set the pace.
+    const bool valu_ok = nrows <= 16 && attn::decode_supported((int)r.D, (int)r.Dv, next_pow2_nq(nrows));
+    const bool mfma_ok = g_opt_decode_mfma >= 0 && !r.ep.pb_weight && !r.ep.rel_k &&
+                         nrows <= attn::decode_mfma_max_rows((int)r.D, (int)r.Dv);
+    const bool use_mfma = mfma_ok && (g_opt_decode_mfma > 0 || !valu_ok || nrows >= kDecodeMfmaFrom);
+    const bool dec_ok = valu_ok || mfma_ok;
     // Relative key/value embeddings have no prefill kernel: prefill-shaped
     // calls take the generic one.
     const bool pre_ok = attn::prefill_supported((int)r.D, (int)r.Dv) && !r.ep.rel_k;
@@ -574,6 +585,7 @@ int make_plan(const Resolved& r, Plan* plan, const AppendRows* app = nullptr) {
     if (path == ATTN_PATH_DECODE) {
         attn::DecodePlan& d = plan->decode;
         d.nq = next_pow2_nq(nrows);
+        d.mfma = use_mfma ? 1 : 0;
         d.depth = g_opt_decode_depth ? (int32_t)g_opt_decode_depth : kDecodeDepth;
 
         d.range = kr;
@@ -619,7 +631,9 @@ int make_plan(const Resolved& r, Plan* plan, const AppendRows* app = nullptr) {
             // (The split of appended rows is short, and at one batch per
             // lane every instance it runs in holds at least 3 workgroups per
             // CU, one more than planned: it goes beside the full set.)
-            const bool light = plan->fused && d.depth == 1;
+            // (decode_mfma holds only 2 workgroups per CU in most instances:
+            // there the append split counts like any other.)
+            const bool light = plan->fused && !d.mfma && d.depth == 1;
             const int64_t extra = (near && !light ? 1 : 0) + (sink_hi > 0 ? 1 : 0);
             const int64_t per_cu = g_opt_decode_wgs ? g_opt_decode_wgs : kDecodeWgPerCU;
             const int64_t target = (int64_t)kCUs * per_cu / r.G - extra;
@@ -1057,9 +1071,14 @@ int run_plan(const Resolved& r, const Plan& plan, const attn::Problem& prob, voi
             err = timed("generic", s, [&](const attn::Launch& L) { return attn::launch_generic(prob, L); });
             break;
         case ATTN_PATH_DECODE:
-            err = timed("decode_split", s, [&](const attn::Launch& L) {
-                return attn::launch_decode_split(prob, plan.decode, (float*)workspace, L);
-            });
+            if (plan.decode.mfma)
+                err = timed("decode_mfma", s, [&](const attn::Launch& L) {
+                    return attn::launch_decode_mfma(prob, plan.decode, (float*)workspace, L);
+                });
+            else
+                err = timed("decode_split", s, [&](const attn::Launch& L) {
+                    return attn::launch_decode_split(prob, plan.decode, (float*)workspace, L);
+                });
             if (err == hipSuccess && plan.decode.splits > 1)
                 err = timed("combine", s, [&](const attn::Launch& L) {
                     return attn::launch_decode_combine(prob, plan.decode, (const float*)workspace, L);
@@ -1123,7 +1142,9 @@ int attn_plan(const attn_params* p, attn_plan_info* info) {
                    : plan.path == ATTN_PATH_PREFILL ? plan.prefill.ksplit
                                                     : 1;
     info->tile_q = plan.path == ATTN_PATH_PREFILL ? plan.prefill.tile_q : 0;
-    info->reserved = 0;
+    info->variant = plan.path == ATTN_PATH_DECODE    ? plan.decode.mfma
+                    : plan.path == ATTN_PATH_PREFILL ? plan.prefill.variant
+                                                     : 0;
     return ok();
 }
 
@@ -1361,7 +1382,7 @@ int attn_mla_plan(const attn_mla_params* p, attn_plan_info* info) {
     info->path = plan.path;
     info->splits = plan.path == ATTN_PATH_MLA ? plan.plan.splits : 1;
     info->tile_q = plan.path == ATTN_PATH_MLA ? (plan.plan.fast ? 16 : 1) : 0;
-    info->reserved = 0;
+    info->variant = 0;
     return ok();
 }
 
@@ -1459,6 +1480,11 @@ int attn_set_option(const char* name, int64_t value) {
         if (value != 0 && value != -1 && (value < 32 || value > 4096 || (value & (value - 1))))
             return fail(ATTN_ERR_INVALID, "decode_block: must be 0, -1 or a power of two in 32..4096");
         g_opt_decode_block = value;
+        return ok();
+    }
+    if (!strcmp(name, "decode_mfma")) {
+        if (value < -1 || value > 1) return fail(ATTN_ERR_INVALID, "decode_mfma: must be -1, 0 or 1");
+        g_opt_decode_mfma = value;
         return ok();
     }
     if (!strcmp(name, "decode_depth")) {

@@ -62,18 +62,6 @@ struct DecodeShape {
 __device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
 __device__ __forceinline__ float4 zero4() { return make_float4(0.f, 0.f, 0.f, 0.f); }
 
-// Whether every query row of positions [pos_first, pos_last] sees every key
-// of [k0, k1) (graph protocol op catalogue, op `attention`, window rule).
-__device__ __forceinline__ bool chunk_all_visible(const Epilogue& e, int pos_first, int pos_last,
-                                                  int k0, int k1) {
-    if (k1 <= k0) return true;
-    if (e.causal) return k1 - 1 <= pos_first && (e.window == 0 || k0 > pos_last - e.window);
-    if (e.window == 0) return true;
-    const int d = max(max(abs(pos_first - k0), abs(pos_first - (k1 - 1))),
-                      max(abs(pos_last - k0), abs(pos_last - (k1 - 1))));
-    return d <= e.window;
-}
-
 // RM: the relative-position terms (bucketed position bias, relative
 // key/value embeddings). 0: off. 1: on, for splits whose keys are all at the
 // tables' far end for every row (their terms are per-row constants). 2: on,

@@ -37,6 +37,18 @@ __device__ __forceinline__ bool key_visible(const E& e, int pos, int s) {
     return window_visible(e, pos, s) | sink_visible(e, pos, s);
 }
 
+// Whether every query row of positions [pos_first, pos_last] sees every key
+// of [k0, k1) (graph protocol op catalogue, op `attention`, window rule).
+__device__ __forceinline__ bool chunk_all_visible(const Epilogue& e, int pos_first, int pos_last,
+                                                  int k0, int k1) {
+    if (k1 <= k0) return true;
+    if (e.causal) return k1 - 1 <= pos_first && (e.window == 0 || k0 > pos_last - e.window);
+    if (e.window == 0) return true;
+    const int d = max(max(abs(pos_first - k0), abs(pos_first - (k1 - 1))),
+                      max(abs(pos_last - k0), abs(pos_last - (k1 - 1))));
+    return d <= e.window;
+}
+
 // The bucketed position bias of key s for a query at pos in head h: the
 // bucket of distance |pos - s| (the last threshold not above it), in the
 // second half of the table for a later key when the table is bidirectional.
@@ -62,8 +74,8 @@ __device__ __forceinline__ float position_bias_tab(const Epilogue& e, const uint
 }
 
 // The score of one visible (query, key) pair, in the order the op fixes:
-// scale the dot product, softcap it (feature attention.softcap: before the
-// mask), then add the ALiBi penalty -slope*|pos - s| and the bias entry
+// scale the dot product, softcap it (feature attention.softcap puts the cap
+// ahead of masking), then add the ALiBi penalty -slope*|pos - s| and the bias entry
 // (the bias input plus the bucketed position bias, fetched ahead by the
 // caller).
 __device__ __forceinline__ float score_epilogue(float dot, const Epilogue& e, int h, int pos, int s,

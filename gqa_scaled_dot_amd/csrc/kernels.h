@@ -75,6 +75,7 @@ struct KeyRange {
 
 struct DecodePlan {
     int32_t nq;       // query rows per KV group this instance holds (template value)
+    int32_t mfma;     // 1: decode_mfma (matrix cores, rows in blocks of 16); 0: decode_split
     int32_t splits;   // key-range splits per KV group (the sink split included)
     int32_t depth;    // batches of key rows per lane in registers: 1 (one at a time) or a ring of 2 or 3
     int32_t sink_hi;  // > 0: the last split covers the sink keys [0, sink_hi) below `range`
@@ -170,6 +171,8 @@ bool decode_supported(int D, int Dv, int nq);
 hipError_t launch_decode_split(const Problem& p, const DecodePlan& plan, float* ws, const Launch& L);
 hipError_t launch_decode_combine(const Problem& p, const DecodePlan& plan, const float* ws,
                                  const Launch& L);
+int decode_mfma_max_rows(int D, int Dv);
+hipError_t launch_decode_mfma(const Problem& p, const DecodePlan& plan, float* ws, const Launch& L);
 bool prefill_supported(int D, int Dv);
 int prefill_wgs_per_cu(int variant, int D, int Dv);
 hipError_t launch_prefill(const Problem& p, const PrefillPlan& plan, float* ws, const Launch& L);

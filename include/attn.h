@@ -413,7 +413,8 @@ typedef struct attn_plan_info {
     int32_t path;
     int32_t splits;
     int32_t tile_q;
-    int32_t reserved;
+    int32_t variant;  /* decode: 1 = the matrix-core kernel, 0 = the vector one;
+                         prefill: the MFMA tile (32 = 32x32x2, 16 = 16x16x4) */
 } attn_plan_info;
 int attn_plan(const attn_params* p, attn_plan_info* info);
 
