@@ -52,8 +52,12 @@ Every benchmarked output is checked against the CPU oracle on the same
 inputs, every row of it (the prefill-shaped ones too, which takes the oracle
 tens of seconds for the largest; --sampled-parity checks ~30 rows instead).
 
+`--only NAME,...` times just the named workloads of workloads.py (one
+record each, no headline line): the profiles under profiles/ run the
+profiler over one workload at a time this way.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
-       [--prefill-steps K] [--no-configs] [--sampled-parity]
+       [--prefill-steps K] [--no-configs] [--sampled-parity] [--only NAME,...]
 """
 
 from __future__ import annotations
@@ -742,6 +746,9 @@ def main():
                     help="only the Llama-shaped decode and prefill, not the other workloads")
     ap.add_argument("--sampled-parity", action="store_true",
                     help="check ~30 sampled rows of prefill-shaped outputs instead of every row")
+    ap.add_argument("--only", default=None,
+                    help="comma-separated workload names from workloads.py (e.g. LLAMA_CHUNKED,MLA_DECODE): "
+                         "time just those, one record each, for profiling one kernel and shape at a time")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -750,6 +757,18 @@ def main():
     if args.steps < 1 or args.warmup < 0 or args.prefill_steps < 1:
         ap.error("--steps and --prefill-steps must be >= 1 and --warmup >= 0")
     import workloads
+    if args.only:
+        recs = []
+        for name in args.only.split(","):
+            w = getattr(workloads, name.strip(), None)
+            if w is None:
+                ap.error(f"--only: no workload named {name!r} in workloads.py")
+            if isinstance(w, workloads.MlaWorkload):
+                recs.append(run_mla(w, args, n_buffers=min(16, max(2, -(-(512 << 20) // mla_work(w)["bytes"])))))
+            else:
+                recs.append(run_config(w, args, kv_buffers=4 if w.T == 1 else 1))
+        print(json.dumps({"metric": METRIC, "only": args.only, "configs": recs}), flush=True)
+        return
     prefill = run_config(workloads.LLAMA_PREFILL, args)
     rec = run_decode(args)
     rec["prefill"] = prefill

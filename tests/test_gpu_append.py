@@ -299,3 +299,51 @@ def test_random_appends(seed):
     finally:
         for k in opts:
             ga.attn_set_option(k, 0)
+
+
+def _random_noncausal_case(seed):
+    """A non-causal appending call whose new rows end its key range: the
+    cache's end without a window, else the last row's position + window + 1
+    (rows past that hold NaN). Groups up to 16 rows (decode_mfma) where the
+    width allows."""
+    rng = np.random.default_rng(5000 + seed)
+    D, Dv, most = [(64, 64, 16), (128, 128, 16), (192, 128, 16), (256, 256, 2)][rng.integers(4)]
+    G = int(rng.choice([1, 2, 4, 8]))
+    T = int(rng.integers(1, 3))
+    hpg = int(rng.choice([h for h in (1, 2, 4, 7, 8) if h * T <= most] or [1]))
+    S = int(rng.integers(T + 80, 6000))
+    P0 = int(rng.integers(0, S - T + 1))
+    kw = dict(name=f"random non-causal append {seed}", T=T, S=S, heads=G * hpg, kvHeads=G, headDim=D,
+              causal=False, posOffset=P0, seed=seed)
+    if Dv != D:
+        kw["vHeadDim"] = Dv
+    lo, end = 0, S
+    if rng.random() < 0.6:
+        window = int(rng.integers(1, S))
+        kw["window"] = window
+        lo, end = max(0, P0 - window), min(S, P0 + T + window)
+        if rng.random() < 0.3:
+            kw["sinks"] = int(rng.integers(1, 8))
+    feats = rng.random(3)
+    if feats[0] < 0.3:
+        kw["alibi"] = True
+    if feats[1] < 0.3:
+        kw["softcap"] = 20.0
+    if feats[2] < 0.3:
+        kw["bias"] = "TS" if rng.random() < 0.5 else "HTS"
+    w = _wl(**kw)
+    rows = int(rng.integers(1, min(64, end - lo) + 1))
+    return w, rows, end - rows, (end if end < S else None)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_noncausal_appends(seed):
+    # Non-causal calls whose appended rows end the key range take them into
+    # the decode launch too (no separate copy); caches bit for bit, output
+    # against the oracle.
+    w, rows, offset, poison_past = _random_noncausal_case(seed)
+    bias_kind = {None: 0, "TS": 1, "HTS": 2}[w.bias]
+    assert ga.attn_plan(w.T, w.S, bias_kind=bias_kind, **w.params())["path"] == "decode", w
+    copies = _append(w, rows, offset, poison_past=poison_past,
+                     what=f"seed {seed}: rows {rows} at {offset}, rows from {poison_past} NaN; {w}")
+    assert copies == 0
