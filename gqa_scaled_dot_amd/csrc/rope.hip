@@ -22,28 +22,34 @@ __device__ __forceinline__ void st4(float* p, float4 v) { *reinterpret_cast<floa
 //   interleaved (rd % 4 == 0): unit u < rd/4 owns channels 4u..4u+3, i.e.
 //     pairs 2u and 2u+1;
 //   then one unit per pass-through float4 (channels rd..D-1).
-__global__ __launch_bounds__(kThreads) void rope_vec_kernel(RopeArgs ra, const float* x, float* out,
-                                                            int64_t rows, int heads, int D, int units) {
+// grid (rows, ceil(heads * units / kThreads)): every head of a row turns by
+// the same angles, so the workgroup computes the row's rd/2 (cos, sin)
+// pairs once, into LDS, and its threads read them there (the same f32
+// values each thread would compute itself).
+__global__ __launch_bounds__(kThreads) void rope_vec_kernel(RopeArgs ra, const float* x, float* out, int heads,
+                                                            int D, int units) {
+    __shared__ float s_cos[ATTN_ROPE_MAX_ROTARY_DIM / 2], s_sin[ATTN_ROPE_MAX_ROTARY_DIM / 2];
     const int rot_units = ra.interleaved ? ra.rd / 4 : ra.rd / 8;
-    const int64_t total = rows * heads * units;
+    const int64_t row = blockIdx.x;
+    const int64_t pos = ra.pos0 + row;
+    for (int i = threadIdx.x; i < ra.rd / 2; i += kThreads) rope_cos_sin(pos, ra.inv_freq[i], ra.af, s_cos[i], s_sin[i]);
+    __syncthreads();
+    const int idx = (int)blockIdx.y * kThreads + (int)threadIdx.x;
+    if (idx >= heads * units) return;
     const bool in_place = x == out;
-    for (int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x; idx < total;
-         idx += (int64_t)gridDim.x * kThreads) {
-        const int u = (int)(idx % units);
-        const int64_t rh = idx / units;  // row * heads + head
-        const int64_t pos = ra.pos0 + rh / heads;
-        const float* xh = x + rh * D;
-        float* oh = out + rh * D;
-        if (u >= rot_units) {
-            const int d = ra.rd + 4 * (u - rot_units);
-            if (!in_place) st4(oh + d, ld4(xh + d));
-            continue;
-        }
+    const int h = idx / units, u = idx - h * units;
+    const int64_t rh = row * heads + h;
+    const float* xh = x + rh * D;
+    float* oh = out + rh * D;
+    if (u >= rot_units) {
+        const int d = ra.rd + 4 * (u - rot_units);
+        if (!in_place) st4(oh + d, ld4(xh + d));
+        return;
+    }
+    {
         if (ra.interleaved) {
             const float4 v = ld4(xh + 4 * u);
-            float c0, s0, c1, s1;
-            rope_cos_sin(pos, ra.inv_freq[2 * u], ra.af, c0, s0);
-            rope_cos_sin(pos, ra.inv_freq[2 * u + 1], ra.af, c1, s1);
+            const float c0 = s_cos[2 * u], s0 = s_sin[2 * u], c1 = s_cos[2 * u + 1], s1 = s_sin[2 * u + 1];
             float4 o;
             o.x = fmaf(-v.y, s0, v.x * c0);
             o.y = fmaf(v.x, s0, v.y * c0);
@@ -55,7 +61,10 @@ __global__ __launch_bounds__(kThreads) void rope_vec_kernel(RopeArgs ra, const f
             const float4 a = ld4(xh + 4 * u), b = ld4(xh + half + 4 * u);
             float c[4], s[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) rope_cos_sin(pos, ra.inv_freq[4 * u + j], ra.af, c[j], s[j]);
+            for (int j = 0; j < 4; ++j) {
+                c[j] = s_cos[4 * u + j];
+                s[j] = s_sin[4 * u + j];
+            }
             float4 oa, ob;
             oa.x = fmaf(-b.x, s[0], a.x * c[0]);
             oa.y = fmaf(-b.y, s[1], a.y * c[1]);
@@ -110,11 +119,10 @@ hipError_t launch_rope(const RopeArgs& ra, const float* x, float* out, int64_t r
                        const Launch& L) {
     const bool aligned = (((uintptr_t)x | (uintptr_t)out) & 15u) == 0;
     const bool vec = aligned && D % 4 == 0 && (ra.interleaved ? ra.rd % 4 == 0 : ra.rd % 8 == 0);
-    if (vec) {
-        const int units = (ra.interleaved ? ra.rd / 4 : ra.rd / 8) + (D - ra.rd) / 4;
-        const int64_t total = rows * heads * units;
-        return launch_kernel(rope_vec_kernel, dim3((unsigned)grid_for(total)), dim3(kThreads), 0, L, ra, x,
-                             out, rows, heads, D, units);
+    const int units = (ra.interleaved ? ra.rd / 4 : ra.rd / 8) + (D - ra.rd) / 4;
+    if (vec && rows > 0 && rows <= INT32_MAX && (int64_t)heads * units <= 65535LL * kThreads) {
+        const dim3 grid((unsigned)rows, (unsigned)((heads * units + kThreads - 1) / kThreads));
+        return launch_kernel(rope_vec_kernel, grid, dim3(kThreads), 0, L, ra, x, out, heads, D, units);
     }
     const int64_t total = rows * heads * (ra.rd / 2 + (D - ra.rd));
     return launch_kernel(rope_scalar_kernel, dim3((unsigned)grid_for(total)), dim3(kThreads), 0, L, ra, x,
