@@ -52,9 +52,10 @@ Every benchmarked output is checked against the CPU oracle on the same
 inputs, every row of it (the prefill-shaped ones too, which takes the oracle
 tens of seconds for the largest; --sampled-parity checks ~30 rows instead).
 
-`--only NAME,...` times just the named workloads of workloads.py (one
-record each, no headline line): the profiles under profiles/ run the
-profiler over one workload at a time this way.
+`--only NAME,...` times just the named workloads of workloads.py (or ROPE,
+the rope section; one record each, no headline line), after one plain
+134,213,632-byte copy that calibrates the profiler's traffic counters: the
+profiles under profiles/ run the profiler over one workload at a time this way.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
        [--prefill-steps K] [--no-configs] [--sampled-parity] [--only NAME,...]
@@ -87,6 +88,8 @@ KERNEL_SOURCES = {
              "gqa_scaled_dot_amd/csrc/kernels.h"],
     "decode_mfma": ["gqa_scaled_dot_amd/csrc/decode_mfma.hip", "gqa_scaled_dot_amd/csrc/device_common.h",
                     "gqa_scaled_dot_amd/csrc/kernels.h", "gqa_scaled_dot_amd/csrc/rope_device.h"],
+    "mla_split": ["gqa_scaled_dot_amd/csrc/mla.hip", "gqa_scaled_dot_amd/csrc/device_common.h",
+                  "gqa_scaled_dot_amd/csrc/kernels.h"],
 }
 
 
@@ -103,15 +106,17 @@ def source_hash(kernel: str) -> str:
 
 
 def measured_traffic(kernel: str, workload: str):
-    """HBM bytes per launch from rocprofv3 counters, if taken on this very kernel source."""
+    """HBM bytes per launch of `kernel` on `workload` from rocprofv3 counters
+    (profiles/traffic.json), if they were taken on this very kernel source."""
     try:
         with open(TRAFFIC_FILE) as f:
-            rec = json.load(f).get(kernel)
+            entries = json.load(f).get("entries", [])
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("source_sha256") != source_hash(kernel) or rec.get("workload") != workload:
-        return None
-    return rec.get("bytes_per_launch")
+    for rec in entries:
+        if rec.get("kernel") == kernel and rec.get("workload") == workload:
+            return rec.get("bytes_per_launch") if rec.get("source_sha256") == source_hash(kernel) else None
+    return None
 
 
 def decode_algorithmic_bytes(w) -> int:
@@ -192,6 +197,24 @@ CPU_SHARE = 16
 
 def cpu_threads() -> int:
     return max(1, min(affinity_cpus(), CPU_SHARE))
+
+
+CALIBRATION_COPY_BYTES = 32767 * 4096 * 4  # the Llama-shaped decode's cache fill: 134,213,632 bytes
+
+
+def calibration_copy():
+    """One plain copy of known size (attn_cache_write of 32767 rows x 4 KiB,
+    the Llama-shaped decode's cache fill): the reference that scales the
+    profiler's FETCH_SIZE / WRITE_SIZE readings to bytes in every counter pass."""
+    import torch
+
+    import gqa_scaled_dot_amd as ga
+    src = torch.zeros((32767, 1024), dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    ga.attn_cache_write(dst, src, 0)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
 
 
 def run_decode(args):
@@ -569,7 +592,7 @@ def run_mla(w, args, n_buffers):
         roof = {"bound": "mfma", "achieved": round(work["split_flops"] / split_s / 1e12, 3),
                 "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s", "flops_per_launch": work["split_flops"]}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic("mla_split", w.name)
     roof["kernel"] = "mla_split"
     roof["avg_launch_us"] = kern_us["mla_split"]
     call_gbs = work["bytes"] / (ms_call * 1e-3) / 1e9
@@ -758,11 +781,17 @@ def main():
         ap.error("--steps and --prefill-steps must be >= 1 and --warmup >= 0")
     import workloads
     if args.only:
+        names = [n.strip() for n in args.only.split(",")]
+        for name in names:
+            if name != "ROPE" and getattr(workloads, name, None) is None:
+                ap.error(f"--only: no workload named {name!r} in workloads.py (or ROPE)")
+        calibration_copy()
         recs = []
-        for name in args.only.split(","):
-            w = getattr(workloads, name.strip(), None)
-            if w is None:
-                ap.error(f"--only: no workload named {name!r} in workloads.py")
+        for name in names:
+            if name == "ROPE":
+                recs.append(run_rope(args))
+                continue
+            w = getattr(workloads, name)
             if isinstance(w, workloads.MlaWorkload):
                 recs.append(run_mla(w, args, n_buffers=min(16, max(2, -(-(512 << 20) // mla_work(w)["bytes"])))))
             else:
@@ -788,6 +817,12 @@ def main():
                                             "(max distance 128)")):
             rec["configs"].append(run_config(workloads.LLAMA_DECODE, args, kv_buffers=2,
                                              extra=relpos_terms(workloads.LLAMA_DECODE, kind), label=label))
+        # Relative key/value embeddings on a prefill-shaped call (the 32x32x2
+        # prefill kernel's band and far-key handling).
+        rec["configs"].append(run_config(workloads.LLAMA_CHUNKED, args,
+                                         extra=relpos_terms(workloads.LLAMA_CHUNKED, "relative_kv"),
+                                         label="llama3-8b-shaped chunked prefill T=512 at 3584, S=4096, with "
+                                               "relative key/value embeddings (max distance 128)"))
         # Latent attention in absorbed form; state copies rotate over >= 512 MiB of reads.
         rec["mla"] = [run_mla(w, args, n_buffers=min(16, max(2, -(-(512 << 20) // mla_work(w)["bytes"]))))
                       for w in (workloads.MLA_DECODE, workloads.MLA_DECODE_V3)]

@@ -560,9 +560,10 @@ int make_plan(const Resolved& r, Plan* plan, const AppendRows* app = nullptr) {
                          nrows <= attn::decode_mfma_max_rows((int)r.D, (int)r.Dv);
     const bool use_mfma = mfma_ok && (g_opt_decode_mfma > 0 || !valu_ok || nrows >= kDecodeMfmaFrom);
     const bool dec_ok = valu_ok || mfma_ok;
-    // Relative key/value embeddings have no prefill kernel: prefill-shaped
-    // calls take the generic one.
-    const bool pre_ok = attn::prefill_supported((int)r.D, (int)r.Dv) && !r.ep.rel_k;
+    // Relative key/value embeddings: the 32x32x2 prefill kernel holds them up
+    // to headDim + vHeadDim = 256; wider heads take the generic kernel.
+    const bool pre_ok = attn::prefill_supported((int)r.D, (int)r.Dv) &&
+                        (!r.ep.rel_k || attn::prefill_rel_supported((int)r.D, (int)r.Dv));
     int path;
     if (g_opt_force_path) {
         path = (int)g_opt_force_path;
@@ -710,7 +711,7 @@ int make_plan(const Resolved& r, Plan* plan, const AppendRows* app = nullptr) {
         attn::PrefillPlan& pp = plan->prefill;
         // Heads of one KV group side by side in a workgroup; its other waves
         // on further query blocks. Wide heads take the 16-row-wave variant.
-        pp.variant = g_opt_prefill_variant ? (int32_t)g_opt_prefill_variant : (r.D + r.Dv > 256 ? 16 : 32);
+        pp.variant = r.ep.rel_k ? 32 : g_opt_prefill_variant ? (int32_t)g_opt_prefill_variant : (r.D + r.Dv > 256 ? 16 : 32);
         const int64_t waves = pp.variant == 16 ? 8 : 4, rows_per_wave = pp.variant == 16 ? 16 : 32;
         int64_t nh = 1;
         while (nh * 2 <= waves && hpg % (nh * 2) == 0) nh *= 2;
@@ -722,7 +723,7 @@ int make_plan(const Resolved& r, Plan* plan, const AppendRows* app = nullptr) {
             return fail(ATTN_ERR_UNSUPPORTED, "T: too many query rows for the prefill grid");
         pp.qblocks = (int32_t)qblocks;
         // Too few workgroups to fill the chip: split each one's key range.
-        const int64_t slots = (int64_t)kCUs * attn::prefill_wgs_per_cu(pp.variant, (int)r.D, (int)r.Dv);
+        const int64_t slots = (int64_t)kCUs * attn::prefill_wgs_per_cu(pp.variant, (int)r.D, (int)r.Dv, r.ep.rel_k != nullptr);
         const int64_t tiles = (kr.hi > kr.lo ? (kr.hi - kr.lo + 31) / 32 : 0) + (sink_hi + 31) / 32;
         int64_t ks = g_opt_prefill_splits;
         if (ks <= 0) {

@@ -174,7 +174,8 @@ hipError_t launch_decode_combine(const Problem& p, const DecodePlan& plan, const
 int decode_mfma_max_rows(int D, int Dv);
 hipError_t launch_decode_mfma(const Problem& p, const DecodePlan& plan, float* ws, const Launch& L);
 bool prefill_supported(int D, int Dv);
-int prefill_wgs_per_cu(int variant, int D, int Dv);
+int prefill_wgs_per_cu(int variant, int D, int Dv, bool rel);
+bool prefill_rel_supported(int D, int Dv);
 hipError_t launch_prefill(const Problem& p, const PrefillPlan& plan, float* ws, const Launch& L);
 bool mla_fast_supported(int R, int P);
 hipError_t launch_mla_absorb(const MlaProblem& p, const Launch& L);

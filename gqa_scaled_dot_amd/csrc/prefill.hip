@@ -39,6 +39,25 @@
 //
 // A 16x16x4 variant with 16 query rows per wave (prefill16.hip) serves wide
 // heads; the host picks one per shape.
+//
+// Relative key/value embeddings (REL instances; the IR schema page's
+// attention property relative_kv, read as Shaw et al.'s relative position
+// representations): key s of query row t uses embedding row
+// r = clip(s - pos, -M, M) + M, rel_k[r] joining k before the product with q
+// and rel_v[r] joining v in the weighted sum. Per wave and key tile, with
+// d = s - pos spanning [d_lo, d_lo + 62] over the wave's 32 queries:
+//   - a tile whose d are all <= -M (or all >= M) uses row 0 (or 2M) for
+//     every key: q . rel_k[0] is a per-query constant added to the scores,
+//     and the tile's weight sum joins a per-query sum wL (or wR) that
+//     multiplies rel_v[0] (or rel_v[2M]) once at the end (rescaled with the
+//     running maximum like the softmax sum);
+//   - any other tile (the band within M of the diagonal) forms q . rel_k for
+//     the 64 relative rows d_lo .. d_lo + 63 on the matrix cores into the
+//     wave's own LDS rows, adds entry d - d_lo to each score, and after the
+//     softmax scatters the weights by d into the same rows for a second
+//     contraction with the rel_v rows (O^T += rel_v^T P_rel^T).
+// A wave's LDS rows are its own, and a wave's LDS accesses complete in
+// order, so no barrier is needed around them.
 #include "prefill_common.h"
 #include "rope_device.h"
 
@@ -82,6 +101,8 @@ __device__ __forceinline__ void lds_read(const float* src, float (&dst)[NB]) {
 // in 256 registers per lane).
 constexpr int prefill_min_waves(int D, int DV) { return D + DV <= 256 ? 2 : 1; }
 
+constexpr int kRelRows = 64;  // relative rows per band tile: d_lo .. d_lo + 63
+
 template <int D, int DV>
 struct PrefillShape {
     static constexpr int KLD = D + kPad;    // LDS row stride of a K tile
@@ -90,10 +111,12 @@ struct PrefillShape {
     static constexpr int VF4 = kBK * DV / 4 / kThreads;  // float4 per thread per V tile
     static constexpr int NB = DV / 32;      // output blocks (and V floats per lane per k-step)
     static constexpr size_t lds_bytes = sizeof(float) * 2 * kBK * (size_t)(KLD + VLD);
+    // REL instances: each wave's [32 queries][kRelRows] rows after the tiles.
+    static constexpr size_t rel_lds_bytes = sizeof(float) * kWaves * kBQ * kRelRows;
 };
 
-template <int D, int DV, bool EPI>
-__global__ __launch_bounds__(kThreads, prefill_min_waves(D, DV)) void prefill_kernel(
+template <int D, int DV, bool EPI, bool REL>
+__global__ __launch_bounds__(kThreads, REL ? 1 : prefill_min_waves(D, DV)) void prefill_kernel(
     Problem p, Args a) {
     using Sh = PrefillShape<D, DV>;
     constexpr int KLD = Sh::KLD, VLD = Sh::VLD, NB = Sh::NB;
@@ -152,6 +175,26 @@ __global__ __launch_bounds__(kThreads, prefill_min_waves(D, DV)) void prefill_ke
         for (int r = 0; r < 16; ++r) o[b][r] = 0.0f;
     float m = -INFINITY, l = 0.0f;
 
+    // Relative embeddings: this wave's LDS rows, the per-query products with
+    // rows 0 and 2M, and the weight sums of the keys beyond reach.
+    const int M = REL ? p.ep.rel_max : 0;
+    float* wrel = lds + 2 * kBK * (KLD + VLD) + wave * (kBQ * kRelRows) + col * kRelRows;
+    float qrel0 = 0.0f, qrelN = 0.0f, wL = 0.0f, wR = 0.0f;
+    if constexpr (REL) {
+        const float* r0 = p.ep.rel_k + half * (D / 2);
+        const float* rN = p.ep.rel_k + (int64_t)(2 * M) * D + half * (D / 2);
+        float a0 = 0.0f, aN = 0.0f;
+#pragma unroll
+        for (int kk = 0; kk < D / 2; kk += 4) {
+            const float4 x0 = *reinterpret_cast<const float4*>(r0 + kk);
+            const float4 xN = *reinterpret_cast<const float4*>(rN + kk);
+            a0 = fmaf(qreg[kk], x0.x, fmaf(qreg[kk + 1], x0.y, fmaf(qreg[kk + 2], x0.z, fmaf(qreg[kk + 3], x0.w, a0))));
+            aN = fmaf(qreg[kk], xN.x, fmaf(qreg[kk + 1], xN.y, fmaf(qreg[kk + 2], xN.z, fmaf(qreg[kk + 3], xN.w, aN))));
+        }
+        qrel0 = a0 + __shfl_xor(a0, 32, 64);
+        qrelN = aN + __shfl_xor(aN, 32, 64);
+    }
+
     // This workgroup's part of its key tiles (sink tiles, then window tiles).
     const KeyRows rows = key_rows(p.ep, klo, khi);
     const TileSpan span = tile_span(rows);
@@ -188,6 +231,7 @@ __global__ __launch_bounds__(kThreads, prefill_min_waves(D, DV)) void prefill_ke
         const float* kt_ = ktile + buf * kBK * KLD;
         const float* vt_ = vtile + buf * kBK * VLD;
         float x[16];
+        int rel_cls = 0, d_lo = 0, delta = 0;  // REL: 0 band tile, 1 every key at row 0, 2 every key at row 2M
         if (any_vis) {
             // Bias entries of the tile, requested before the matrix work so
             // that it hides their latency.
@@ -212,6 +256,44 @@ __global__ __launch_bounds__(kThreads, prefill_min_waves(D, DV)) void prefill_ke
                 // Keep the scheduler from hoisting every LDS read of the tile
                 // at once (it would need D/2 registers for them).
                 if (kk % 16 == 12) __builtin_amdgcn_sched_barrier(0);
+            }
+            if constexpr (REL) {
+                // The relative-key term joins the product before the scale.
+                d_lo = s_first - wpl;
+                const int d_hi = s_first + kBK - 1 - wpf;
+                rel_cls = d_hi <= -M ? 1 : (d_lo >= M ? 2 : 0);
+                if (rel_cls == 1) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) sacc[r] += qrel0;
+                } else if (rel_cls == 2) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) sacc[r] += qrelN;
+                } else {
+                    // q . rel_k[clip(d) + M] for d = d_lo + i, i < 64 (rows
+                    // i = 32 ps + col on the A side), into the wave's LDS rows.
+#pragma unroll
+                    for (int ps = 0; ps < kRelRows / 32; ++ps) {
+                        const int rr = min(max(d_lo + 32 * ps + col, -M), M) + M;
+                        const float* rk = p.ep.rel_k + (int64_t)rr * D + half * (D / 2);
+                        f32x16 racc;
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) racc[r] = 0.0f;
+#pragma unroll
+                        for (int kk = 0; kk < D / 2; kk += 4) {
+                            const float4 kv = *reinterpret_cast<const float4*>(rk + kk);
+                            racc = mfma32(kv.x, qreg[kk], racc);
+                            racc = mfma32(kv.y, qreg[kk + 1], racc);
+                            racc = mfma32(kv.z, qreg[kk + 2], racc);
+                            racc = mfma32(kv.w, qreg[kk + 3], racc);
+                        }
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) wrel[32 * ps + 8 * (r >> 2) + 4 * half + (r & 3)] = racc[r];
+                    }
+                    // Key f(r, half) of query pos sits at d - d_lo = f + (wpl - pos).
+                    delta = min(max(wpl - pos, 0), kBK - 1);
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) sacc[r] += wrel[8 * (r >> 2) + 4 * half + (r & 3) + delta];
+                }
             }
 
             // Score epilogue and mask; keys of register r: f(r, half).
@@ -238,6 +320,10 @@ __global__ __launch_bounds__(kThreads, prefill_min_waves(D, DV)) void prefill_ke
             if (mx > m + kLazy) {
                 const float alpha = fast_exp2(m - mx);
                 l *= alpha;
+                if constexpr (REL) {
+                    wL *= alpha;
+                    wR *= alpha;
+                }
 #pragma unroll
                 for (int b = 0; b < NB; ++b)
 #pragma unroll
@@ -245,10 +331,42 @@ __global__ __launch_bounds__(kThreads, prefill_min_waves(D, DV)) void prefill_ke
                 m = mx;
             }
             const float mu = m == -INFINITY ? 0.0f : m;
+            float ps = 0.0f;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 x[r] = fast_exp2(x[r] - mu);
-                l += x[r];
+                ps += x[r];
+            }
+            l += ps;
+            if constexpr (REL) {
+                if (rel_cls == 1) {
+                    wL += ps;
+                } else if (rel_cls == 2) {
+                    wR += ps;
+                } else if (p.ep.rel_v) {
+                    // The weights by relative offset (zero where no key of
+                    // this query falls), then O^T += rel_v^T P_rel^T.
+#pragma unroll
+                    for (int e = 0; e < 32; e += 4)
+                        *reinterpret_cast<float4*>(wrel + 32 * half + e) = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) wrel[8 * (r >> 2) + 4 * half + (r & 3) + delta] = x[r];
+#pragma unroll
+                    for (int ps2 = 0; ps2 < kRelRows / 32; ++ps2) {
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int i = 32 * ps2 + 8 * (r >> 2) + 4 * half + (r & 3);
+                            const int rr = min(max(d_lo + i, -M), M) + M;
+                            float vv[NB];
+                            const float* rv = p.ep.rel_v + (int64_t)rr * DV + NB * col;
+#pragma unroll
+                            for (int b = 0; b < NB; ++b) vv[b] = rv[b];
+                            const float pw = wrel[i];
+#pragma unroll
+                            for (int b = 0; b < NB; ++b) o[b] = mfma32(vv[b], pw, o[b]);
+                        }
+                    }
+                }
             }
         }
         if (more) fetch_rows<DV, kThreads>(vst, vg, vstride, kt_next, rows);
@@ -270,6 +388,20 @@ __global__ __launch_bounds__(kThreads, prefill_min_waves(D, DV)) void prefill_ke
 
     // Register r of block b is dv = NB*(8(r/4) + 4 half + r%4) + b.
     const float lt = l + __shfl_xor(l, 32, 64);
+    if constexpr (REL) {
+        // Keys beyond reach: their weight sums times rel_v[0] and rel_v[2M].
+        const float wLt = wL + __shfl_xor(wL, 32, 64), wRt = wR + __shfl_xor(wR, 32, 64);
+        if (p.ep.rel_v) {
+            const float* v0 = p.ep.rel_v;
+            const float* vN = p.ep.rel_v + (int64_t)(2 * M) * DV;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int i = 8 * (r >> 2) + 4 * half + (r & 3);
+#pragma unroll
+                for (int b = 0; b < NB; ++b) o[b][r] = fmaf(wLt, v0[NB * i + b], fmaf(wRt, vN[NB * i + b], o[b][r]));
+            }
+        }
+    }
     if (!trow) return;
     const int64_t th = (int64_t)t * p.H + h;
     float* dst;
@@ -301,10 +433,10 @@ __global__ __launch_bounds__(kThreads, prefill_min_waves(D, DV)) void prefill_ke
     }
 }
 
-template <int D, int DV, bool EPI>
+template <int D, int DV, bool EPI, bool REL = false>
 hipError_t launch_t(const Problem& p, const Args& a, const Launch& L) {
-    auto kern = prefill_kernel<D, DV, EPI>;
-    constexpr size_t lds = PrefillShape<D, DV>::lds_bytes;
+    auto kern = prefill_kernel<D, DV, EPI, REL>;
+    constexpr size_t lds = PrefillShape<D, DV>::lds_bytes + (REL ? PrefillShape<D, DV>::rel_lds_bytes : 0);
     static bool configured = false;
     if (!configured) {
         const hipError_t e = set_lds_limit(kern, lds);
@@ -317,6 +449,10 @@ hipError_t launch_t(const Problem& p, const Args& a, const Launch& L) {
 
 template <int D, int DV>
 hipError_t launch_dims(const Problem& p, const Args& a, const Launch& L) {
+    if (p.ep.rel_k) {
+        if constexpr (D + DV <= 256) return launch_t<D, DV, true, true>(p, a, L);
+        return hipErrorInvalidValue;
+    }
     const bool epi = p.ep.any();
     return epi ? launch_t<D, DV, true>(p, a, L) : launch_t<D, DV, false>(p, a, L);
 }
@@ -331,10 +467,13 @@ bool prefill_supported(int D, int Dv) {
 }
 
 // Workgroups per CU the prefill kernels reach (registers and LDS).
-int prefill_wgs_per_cu(int variant, int D, int Dv) {
+int prefill_wgs_per_cu(int variant, int D, int Dv, bool rel) {
     if (variant == 16) return D + Dv <= 256 ? 2 : 1;
-    return prefill_min_waves(D, Dv);
+    return rel ? 1 : prefill_min_waves(D, Dv);
 }
+
+// Relative key/value embeddings have 32x32x2 instances up to D + Dv = 256.
+bool prefill_rel_supported(int D, int Dv) { return prefill_supported(D, Dv) && D + Dv <= 256; }
 
 hipError_t launch_prefill(const Problem& p, const PrefillPlan& plan, float* ws, const Launch& L) {
     Args a;

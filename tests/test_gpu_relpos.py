@@ -145,10 +145,67 @@ def test_relative_kv_forced_splits():
         ga.attn_set_option("decode_splits", 0)
 
 
-def test_relative_kv_prefill_shape_takes_generic():
-    w = workloads.Workload("rkv prefill", T=70, S=90, heads=4, kvHeads=2, headDim=64, posOffset=20)
-    assert ga.attn_plan(w.T, w.S, **w.params(), relative_kv=dict(key=1, value=None, max_distance=4))["path"] == "generic"
+def _rkv_plan(w, m):
+    return ga.attn_plan(w.T, w.S, bias_kind={None: 0, "TS": 1, "HTS": 2}[w.bias], **w.params(),
+                        relative_kv=dict(key=1, value=None, max_distance=m))
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("m", [0, 1, 16, 40, 200])
+def test_relative_kv_prefill(D, causal, m):
+    # The 32x32x2 prefill kernel with relative embeddings: keys far on either
+    # side of each query (one embedding row each) and the band within m of it
+    # (per-key rows), on ragged tiles; also without value embeddings; and the
+    # generic kernel on the same call.
+    w = workloads.Workload("rkv prefill", T=150, S=230 if causal else 200, heads=8, kvHeads=2, headDim=D,
+                           posOffset=80 if causal else 30, causal=causal, seed=D + m)
+    assert _rkv_plan(w, m)["path"] == "prefill"
+    _check_rkv(w, m, True, (None, "generic"), seed=m)
+    _check_rkv(w, m, False, (None,), seed=m + 1)
+
+
+@pytest.mark.parametrize("kw", [dict(window=50, sinks=3), dict(causal=False, window=40, posOffset=60),
+                                dict(softcap=20.0, alibi=True, bias="HTS", bias_mask_prob=0.1, std=2.0),
+                                dict(T=300, S=300, posOffset=0, heads=4, kvHeads=4),
+                                dict(T=70, S=900, posOffset=830)])
+def test_relative_kv_prefill_features(kw):
+    base = dict(T=160, S=400, heads=8, kvHeads=2, headDim=128, posOffset=240)
+    base.update(kw)
+    w = workloads.Workload("rkv prefill mix", **base)
+    q, k, v, bias = w.tensors()
+    assert _rkv_plan(w, 32)["path"] == "prefill"
+    _check_rkv(w, 32, True, (None,), seed=5)
+
+
+@pytest.mark.parametrize("splits", [2, 5])
+def test_relative_kv_prefill_key_splits(splits):
+    # Key-range parts merged by the combine kernel: the embedding terms and
+    # the far-key weight sums travel in the partial states.
+    w = workloads.Workload("rkv prefill splits", T=100, S=2000, heads=8, kvHeads=2, headDim=128, posOffset=1900)
+    try:
+        ga.attn_set_option("prefill_splits", splits)
+        assert _rkv_plan(w, 64)["splits"] == splits
+        _check_rkv(w, 64, True, (None,), seed=splits)
+    finally:
+        ga.attn_set_option("prefill_splits", 0)
+
+
+def test_relative_kv_wide_heads_take_generic():
+    # 192/128 and 256 widths have no prefill instance with the embeddings.
+    for D, Dv in ((192, 128), (256, 256)):
+        w = workloads.Workload("rkv wide", T=70, S=90, heads=4, kvHeads=2, headDim=D, vHeadDim=Dv, posOffset=20)
+        assert _rkv_plan(w, 4)["path"] == "generic"
     _check_rkv(w, 4, True, (None,))
+
+
+def test_relative_kv_chunked_prefill_full_size_sampled():
+    # The Llama-shaped chunked prefill (T=512 at 3584 over 4096 keys) with
+    # relative embeddings of max distance 128, sampled rows.
+    from tests.parity import sample_rows
+    w = workloads.LLAMA_CHUNKED
+    assert _rkv_plan(w, 128)["path"] == "prefill"
+    _check_rkv(w, 128, True, (None,), rows=sample_rows(w.T, seed=4, n_random=24, edges=(128, 256)))
 
 
 def test_relative_kv_refusals():
