@@ -199,7 +199,7 @@ def cpu_threads() -> int:
     return max(1, min(affinity_cpus(), CPU_SHARE))
 
 
-CALIBRATION_COPY_BYTES = 32767 * 4096 * 4  # the Llama-shaped decode's cache fill: 134,213,632 bytes
+CALIBRATION_COPY_BYTES = 32767 * 4096  # the Llama-shaped decode's cache fill: 32767 rows of 4 KiB, 134,213,632 bytes
 
 
 def calibration_copy():

@@ -153,6 +153,7 @@ struct MlaPlan {
     int32_t sink_hi;     // > 0: the last split covers the sink keys [0, sink_hi) below `range`
     int32_t row_blocks;  // 16-row blocks along the T*H rows
     int32_t row_groups;  // 16-row blocks per workgroup of the split kernel (1 or 2)
+    int32_t combine_out; // output channels per combine workgroup (32 or 16)
     int64_t chunk;       // keys per split of `range` (a multiple of 16)
     KeyRange range;
 };

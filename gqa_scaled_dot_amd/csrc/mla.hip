@@ -570,10 +570,12 @@ __global__ __launch_bounds__(kMlaThreads) void mla_combine_kernel(MlaProblem p, 
 // waves projects 2 output channels.
 constexpr int kCombThreads = 1024;
 constexpr int kCombWaves = kCombThreads / 64;
-constexpr int kCombOut = 32;     // output channels per workgroup
 constexpr int kCombBatch = 8;    // accumulator float4s requested up front per thread
 
+// OUT: output channels per workgroup (32: 2 per wave; 16: 1 per wave).
+template <int OUT>
 __global__ __launch_bounds__(kCombThreads) void mla_combine4_kernel(MlaProblem p, int nsplit) {
+    constexpr int EPW = OUT / kCombWaves;
     extern __shared__ __align__(16) float lds[];
     const int R = p.R, C4 = R / 4;
     float4* olat4 = reinterpret_cast<float4*>(lds);             // C4
@@ -584,7 +586,7 @@ __global__ __launch_bounds__(kCombThreads) void mla_combine4_kernel(MlaProblem p
     const int wave = tid >> 6, lane = tid & 63;
     const int row = blockIdx.x;
     const int h = row % p.H;
-    const int e0 = blockIdx.y * kCombOut;
+    const int e0 = blockIdx.y * OUT;
     const float* ml = p.part + (int64_t)p.T * p.H * nsplit * R + (int64_t)row * nsplit * 2;
     const float4* acc4 = reinterpret_cast<const float4*>(p.part + (int64_t)row * nsplit * R);
     float* orow = p.out + (int64_t)row * p.Dv;
@@ -601,10 +603,10 @@ __global__ __launch_bounds__(kCombThreads) void mla_combine4_kernel(MlaProblem p
         xa[u] = summer && i < nsplit ? acc4[(int64_t)i * C4 + c4] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     }
     constexpr int kVj = 256 / 64;  // float4s of a v_b row per lane (R/4 <= 256)
-    float4 vb[2][kVj];
+    float4 vb[EPW][kVj];
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        const int e = e0 + 2 * wave + k;
+    for (int k = 0; k < EPW; ++k) {
+        const int e = e0 + EPW * wave + k;
 #pragma unroll
         for (int j = 0; j < kVj; ++j) {
             const int c = lane + 64 * j;
@@ -630,7 +632,7 @@ __global__ __launch_bounds__(kCombThreads) void mla_combine4_kernel(MlaProblem p
     // nsplit <= 1024: one pair per thread.
     const float M = block_reduce(mlv.x, true);
     if (M == -INFINITY) {  // no visible key in any split
-        if (tid < kCombOut && e0 + tid < p.Dv) orow[e0 + tid] = 0.0f;
+        if (tid < OUT && e0 + tid < p.Dv) orow[e0 + tid] = 0.0f;
         return;
     }
     float ls = 0.0f;
@@ -685,22 +687,24 @@ __global__ __launch_bounds__(kCombThreads) void mla_combine4_kernel(MlaProblem p
 
     // Wave w projects channels e0 + 2w and e0 + 2w + 1: lanes stride the
     // latent channels in float4s, then the wave adds them up.
-    float d[2] = {0.0f, 0.0f};
+    float d[EPW];
+#pragma unroll
+    for (int k = 0; k < EPW; ++k) d[k] = 0.0f;
 #pragma unroll
     for (int j = 0; j < kVj; ++j) {
         const int c = lane + 64 * j;
         if (c < C4) {
             const float4 o = olat4[c];
 #pragma unroll
-            for (int k = 0; k < 2; ++k)
+            for (int k = 0; k < EPW; ++k)
                 d[k] = fmaf(vb[k][j].x, o.x, fmaf(vb[k][j].y, o.y, fmaf(vb[k][j].z, o.z, fmaf(vb[k][j].w, o.w, d[k]))));
         }
     }
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
+    for (int k = 0; k < EPW; ++k) {
         float x = d[k];
         for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
-        const int e = e0 + 2 * wave + k;
+        const int e = e0 + EPW * wave + k;
         if (lane == 0 && e < p.Dv) orow[e] = x;
     }
 }
@@ -748,9 +752,13 @@ hipError_t launch_mla_split(const MlaProblem& p, const MlaPlan& plan, const Laun
 hipError_t launch_mla_combine(const MlaProblem& p, const MlaPlan& plan, const Launch& L) {
     if (plan.splits < 1 || plan.splits > kMlaMaxSplits) return hipErrorInvalidValue;
     if (p.R % 4 == 0 && p.R / 4 <= 256) {
-        const dim3 grid((unsigned)(p.T * p.H), (unsigned)((p.Dv + kCombOut - 1) / kCombOut));
         const size_t lds = sizeof(float4) * ((size_t)p.R / 4 + kCombThreads) + sizeof(float) * (plan.splits + kCombWaves);
-        return launch_kernel(mla_combine4_kernel, grid, dim3(kCombThreads), (uint32_t)lds, L, p, plan.splits);
+        if (plan.combine_out == 16) {
+            const dim3 grid((unsigned)(p.T * p.H), (unsigned)((p.Dv + 15) / 16));
+            return launch_kernel(mla_combine4_kernel<16>, grid, dim3(kCombThreads), (uint32_t)lds, L, p, plan.splits);
+        }
+        const dim3 grid((unsigned)(p.T * p.H), (unsigned)((p.Dv + 31) / 32));
+        return launch_kernel(mla_combine4_kernel<32>, grid, dim3(kCombThreads), (uint32_t)lds, L, p, plan.splits);
     }
     const dim3 grid((unsigned)(p.T * p.H), (unsigned)((p.Dv + 31) / 32));
     const size_t lds = sizeof(float) * ((size_t)p.R + plan.splits + kMlaWaves);

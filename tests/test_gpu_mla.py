@@ -93,6 +93,20 @@ def test_mla_forced_splits(splits):
         ga.attn_set_option("mla_splits", 0)
 
 
+@pytest.mark.parametrize("out", [16, 32])
+@pytest.mark.parametrize("kw", [dict(S=2000, T=2, heads=16, window=900, sinks=8), dict(S=700, T=1, heads=40),
+                                dict(S=1500, T=1, heads=16, kv_rank=256, v_head_dim=96)])
+def test_mla_combine_widths(out, kw):
+    # Combine workgroups of 16 or 32 output channels (v_head_dim 96 leaves a
+    # partial last slice at 32).
+    w = _wl(**kw)
+    try:
+        ga.attn_set_option("mla_combine_out", out)
+        _check(w, what=f"combine_out={out} {kw}")
+    finally:
+        ga.attn_set_option("mla_combine_out", 0)
+
+
 def test_mla_never_reads_past_the_position_or_the_gap():
     # Causal decode over a cache of 4096 rows at position 2999: rows past it
     # and rows between the sinks and the window hold NaN.
