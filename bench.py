@@ -758,6 +758,26 @@ def run_rope(args):
     return {"decode_step": decode, "kernel": kernel}
 
 
+# The relative-position bench lines: (workload, term kind, K/V copies, label).
+RELPOS_LINES = {
+    "LLAMA_DECODE_T5BIAS": ("LLAMA_DECODE", "position_bias", 2,
+                            "llama3-8b-shaped decode with a T5-style bucketed position bias "
+                            "(32 buckets, max distance 128)"),
+    "LLAMA_DECODE_RELKV": ("LLAMA_DECODE", "relative_kv", 2,
+                           "llama3-8b-shaped decode with relative key/value embeddings (max distance 128)"),
+    "LLAMA_CHUNKED_RELKV": ("LLAMA_CHUNKED", "relative_kv", 1,
+                            "llama3-8b-shaped chunked prefill T=512 at 3584, S=4096, with relative key/value "
+                            "embeddings (max distance 128)"),
+}
+
+
+def run_relpos(name, args):
+    import workloads
+    wname, kind, kv_buffers, label = RELPOS_LINES[name]
+    w = getattr(workloads, wname)
+    return run_config(w, args, kv_buffers=kv_buffers, extra=relpos_terms(w, kind), label=label)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -770,8 +790,10 @@ def main():
     ap.add_argument("--sampled-parity", action="store_true",
                     help="check ~30 sampled rows of prefill-shaped outputs instead of every row")
     ap.add_argument("--only", default=None,
-                    help="comma-separated workload names from workloads.py (e.g. LLAMA_CHUNKED,MLA_DECODE): "
-                         "time just those, one record each, for profiling one kernel and shape at a time")
+                    help="comma-separated workload names from workloads.py (e.g. LLAMA_CHUNKED,MLA_DECODE), "
+                         "ROPE, or a relative-position line (LLAMA_DECODE_T5BIAS, LLAMA_DECODE_RELKV, "
+                         "LLAMA_CHUNKED_RELKV): time just those, one record each, for profiling one kernel "
+                         "and shape at a time")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -783,13 +805,17 @@ def main():
     if args.only:
         names = [n.strip() for n in args.only.split(",")]
         for name in names:
-            if name != "ROPE" and getattr(workloads, name, None) is None:
-                ap.error(f"--only: no workload named {name!r} in workloads.py (or ROPE)")
+            if name != "ROPE" and name not in RELPOS_LINES and getattr(workloads, name, None) is None:
+                ap.error(f"--only: no workload named {name!r} in workloads.py (or ROPE, "
+                         f"or one of {', '.join(RELPOS_LINES)})")
         calibration_copy()
         recs = []
         for name in names:
             if name == "ROPE":
                 recs.append(run_rope(args))
+                continue
+            if name in RELPOS_LINES:
+                recs.append(run_relpos(name, args))
                 continue
             w = getattr(workloads, name)
             if isinstance(w, workloads.MlaWorkload):
@@ -810,19 +836,8 @@ def main():
                                     workloads.LATENT_DECODE, workloads.LATENT_NONCAUSAL,
                                     workloads.LLAMA_STREAMING, workloads.LLAMA70_DECODE,
                                     workloads.QWEN2_DECODE)]
-        # Relative-position terms on the Llama-shaped decode.
-        for kind, label in (("position_bias", "llama3-8b-shaped decode with a T5-style bucketed position bias "
-                                              "(32 buckets, max distance 128)"),
-                            ("relative_kv", "llama3-8b-shaped decode with relative key/value embeddings "
-                                            "(max distance 128)")):
-            rec["configs"].append(run_config(workloads.LLAMA_DECODE, args, kv_buffers=2,
-                                             extra=relpos_terms(workloads.LLAMA_DECODE, kind), label=label))
-        # Relative key/value embeddings on a prefill-shaped call (the 32x32x2
-        # prefill kernel's band and far-key handling).
-        rec["configs"].append(run_config(workloads.LLAMA_CHUNKED, args,
-                                         extra=relpos_terms(workloads.LLAMA_CHUNKED, "relative_kv"),
-                                         label="llama3-8b-shaped chunked prefill T=512 at 3584, S=4096, with "
-                                               "relative key/value embeddings (max distance 128)"))
+        # Relative-position terms on the Llama-shaped decode and chunked prefill.
+        rec["configs"] += [run_relpos(name, args) for name in RELPOS_LINES]
         # Latent attention in absorbed form; state copies rotate over >= 512 MiB of reads.
         rec["mla"] = [run_mla(w, args, n_buffers=min(16, max(2, -(-(512 << 20) // mla_work(w)["bytes"]))))
                       for w in (workloads.MLA_DECODE, workloads.MLA_DECODE_V3)]
