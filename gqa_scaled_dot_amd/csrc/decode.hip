@@ -45,18 +45,22 @@ constexpr int kMaxSplits = 1024;
 constexpr int kFewSplits = 16;  // up to this many splits, combine_few_kernel merges them
 constexpr int64_t kFewMinOutputs = 65536;  // ... when there are at least this many output float4s
 
-template <int D, int DV, int NQ>
+template <int D, int DV, int NQ, bool EPI>
 struct DecodeShape {
     static constexpr int KJ = D / 64;   // float4 per lane per K row
     static constexpr int VJ = DV / 64;  // float4 per lane per V row
-    // Key rows per row group per batch: two where that is at most 8 float4
-    // loads per lane, else one. Fewer loads in flight ran faster: measured
-    // with one batch per lane at a time, the Llama-shaped decode took 44.3 us
-    // with two-row batches (8 loads) and 49.3 us with four; the latent-shaped
-    // one (5 loads per row) 27.7 us with one-row batches and 29.2 us with two.
-    // (Two-row batches also need q and acc, 4 NQ (KJ+VJ) registers, to stay
-    // under ~170 registers with the ring.)
-    static constexpr int U = ((KJ + VJ) * 2 <= 8 && (KJ + VJ) * (16 + 4 * NQ) <= 170) ? 2 : 1;
+    // Key rows per row group per batch (one batch per lane at a time). Fewer
+    // loads in flight ran faster, down to about four float4s per lane: with
+    // 128-wide heads the epilogue-free instance takes one-row batches (4
+    // loads; Llama-shaped decode 43.3 us against 45.5 us with two-row ones,
+    // the 4096-window streaming decode 13.1 against 14.3), but the instances
+    // with softcap, ALiBi, bias or relative-position terms are faster with
+    // two-row batches (softcap 48.2 against 53.5 us; bucketed bias 48.5
+    // against 58.7), and 64-wide heads (1 + 1 loads per row) need two rows
+    // (49.2 against 64.8 us). Rows of 5 or more loads (192/128, 256) take
+    // one. (Two-row batches also need q and acc, 4 NQ (KJ+VJ) registers, to
+    // stay under ~170 registers with the ring.)
+    static constexpr int U = (KJ + VJ) * 2 <= 8 && (KJ + VJ) * (16 + 4 * NQ) <= 170 && (EPI || KJ + VJ < 4) ? 2 : 1;
 };
 
 __device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
@@ -75,7 +79,7 @@ __device__ __forceinline__ float4 zero4() { return make_float4(0.f, 0.f, 0.f, 0.
 template <int D, int DV, int NQ, bool EPI, int RM, int DEPTH>
 __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, DecodePlan plan,
                                                                    float* __restrict__ ws) {
-    using Sh = DecodeShape<D, DV, NQ>;
+    using Sh = DecodeShape<D, DV, NQ, EPI>;
     constexpr int KJ = Sh::KJ, VJ = Sh::VJ, U = Sh::U;
     constexpr int kStep = kRowGroups * U;
 
