@@ -59,7 +59,7 @@ int64_t g_opt_mla_row_groups = 0;
 int64_t g_opt_mla_combine_out = 0;  // 0: automatic; 16 or 32 output channels per combine workgroup
 
 constexpr int kCUs = 256;                 // MI355X compute units
-constexpr int kDecodeWgPerCU = 2;         // decode_split occupancy target
+constexpr int kDecodeWgPerCU = 2;         // decode_split occupancy target (decode_mfma: see make_plan)
 constexpr int kDecodeDepth = 1;           // decode_split batches per lane at a time (no prefetch ring)
 // Smallest key chunk worth a workgroup. A decode_split workgroup costs ~8 us
 // however few keys it reads (launch, q, two load round trips, merges), so
@@ -637,7 +637,16 @@ int make_plan(const Resolved& r, Plan* plan, const AppendRows* app = nullptr) {
             // there the append split counts like any other.)
             const bool light = plan->fused && !d.mfma && d.depth == 1;
             const int64_t extra = (near && !light ? 1 : 0) + (sink_hi > 0 ? 1 : 0);
-            const int64_t per_cu = g_opt_decode_wgs ? g_opt_decode_wgs : kDecodeWgPerCU;
+            // decode_mfma with rows of 256 or more K and V floats (16 or more
+            // float4 loads per lane per tile) plans one workgroup per CU:
+            // the kernel is as fast with half the loads in flight, and the
+            // combine merges half the splits (64 heads over 8 KV heads and
+            // 32768 keys: call 50.4 against 51.1 us; 28 over 4: 30.0 against
+            // 31.9; 32 over 1: 27.2 against 42.2). With 64-wide heads two per
+            // CU stay faster (55.2 against 59.2 us).
+            const int64_t per_cu = g_opt_decode_wgs ? g_opt_decode_wgs
+                                   : d.mfma && r.D + r.Dv >= 256 ? 1
+                                                                 : kDecodeWgPerCU;
             const int64_t target = (int64_t)kCUs * per_cu / r.G - extra;
             const int64_t most = (np + kDecodeMinKeys - 1) / kDecodeMinKeys;
             splits = target < most ? target : most;
