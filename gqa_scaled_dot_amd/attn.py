@@ -634,7 +634,7 @@ def attn_mla_plan(T: int, S: int, **params) -> dict:
     info = AttnPlanInfo()
     _check(_lib.lib().attn_mla_plan(ctypes.byref(p), ctypes.byref(info)))
     return {"path": _lib.PATH_NAMES.get(info.path, str(info.path)), "splits": info.splits,
-            "tile_q": info.tile_q}
+            "tile_q": info.tile_q, "slices": info.variant}
 
 
 def _check_mla(q, state, k_b, v_b, out, params):

@@ -57,6 +57,7 @@ int64_t g_opt_mla_splits = 0;
 int64_t g_opt_mla_generic = 0;
 int64_t g_opt_mla_row_groups = 0;
 int64_t g_opt_mla_combine_out = 0;  // 0: automatic; 16 or 32 output channels per combine workgroup
+int64_t g_opt_mla_slices = 0;       // 0: automatic; 1: merge by latent slices where possible; -1: never
 
 constexpr int kCUs = 256;                 // MI355X compute units
 constexpr int kDecodeWgPerCU = 2;         // decode_split occupancy target (decode_mfma: see make_plan)
@@ -886,6 +887,7 @@ struct MlaPlanFull {
     int path;  // ATTN_PATH_EMPTY, _ZERO or _MLA
     attn::MlaPlan plan;
     size_t q_abs_bytes;  // workspace: q_abs first, the split partials after it
+    size_t part_bytes;   // then the split partials; then (slices > 0) the slice shares and counters
     size_t workspace;
 };
 
@@ -954,8 +956,17 @@ int mla_make_plan(const MlaResolved& r, MlaPlanFull* out) {
         pl.sink_hi = 0;
         pl.splits = 1;
     }
+    // The merge by latent slices reads each split's accumulator once (the
+    // per-output merge reads a row's partials once per group of outputs):
+    // V3-shaped combine 16.1 against 17.4 us, V2-Lite-shaped the same 7.9.
+    pl.slices = pl.fast && attn::mla_slices_supported((int)r.R, (int)r.Dv) && g_opt_mla_slices >= 0
+                    ? (int32_t)(r.R / 64) : 0;
     out->q_abs_bytes = align256(sizeof(float) * (size_t)rows * (size_t)(r.R + r.P));
-    out->workspace = out->q_abs_bytes + sizeof(float) * (size_t)rows * (size_t)pl.splits * (size_t)(r.R + 2);
+    out->part_bytes = align256(sizeof(float) * (size_t)rows * (size_t)pl.splits * (size_t)(r.R + 2));
+    out->workspace = out->q_abs_bytes + out->part_bytes;
+    if (pl.slices > 0)
+        out->workspace += align256(sizeof(float) * (size_t)rows * (size_t)pl.slices * (size_t)r.Dv) +
+                          sizeof(uint32_t) * (size_t)rows;
     return ok();
 }
 
@@ -1399,7 +1410,7 @@ int attn_mla_plan(const attn_mla_params* p, attn_plan_info* info) {
     info->path = plan.path;
     info->splits = plan.path == ATTN_PATH_MLA ? plan.plan.splits : 1;
     info->tile_q = plan.path == ATTN_PATH_MLA ? (plan.plan.fast ? 16 : 1) : 0;
-    info->variant = 0;
+    info->variant = plan.path == ATTN_PATH_MLA ? plan.plan.slices : 0;
     return ok();
 }
 
@@ -1452,6 +1463,14 @@ int attn_mla_forward(const attn_mla_params* p, const float* q, const float* stat
     prob.out = out;
     prob.q_abs = (float*)workspace;
     prob.part = (float*)((char*)workspace + plan.q_abs_bytes);
+    prob.yslice = nullptr;
+    prob.tickets = nullptr;
+    if (plan.plan.slices > 0) {
+        prob.yslice = (float*)((char*)workspace + plan.q_abs_bytes + plan.part_bytes);
+        prob.tickets = (uint32_t*)((char*)prob.yslice +
+                                   align256(sizeof(float) * (size_t)(r.T * r.H) * (size_t)plan.plan.slices *
+                                            (size_t)r.Dv));
+    }
     prob.T = r.T;
     prob.S = r.S;
     prob.H = (int32_t)r.H;
@@ -1497,6 +1516,11 @@ int attn_set_option(const char* name, int64_t value) {
         if (value != 0 && value != -1 && (value < 32 || value > 4096 || (value & (value - 1))))
             return fail(ATTN_ERR_INVALID, "decode_block: must be 0, -1 or a power of two in 32..4096");
         g_opt_decode_block = value;
+        return ok();
+    }
+    if (!strcmp(name, "mla_slices")) {
+        if (value < -1 || value > 1) return fail(ATTN_ERR_INVALID, "mla_slices: must be -1, 0 or 1");
+        g_opt_mla_slices = value;
         return ok();
     }
     if (!strcmp(name, "mla_combine_out")) {

@@ -141,6 +141,8 @@ struct MlaProblem {
     float* out;          // [T, H*Dv]
     float* q_abs;        // workspace [T*H, R+P]: k_b[h]^T q_nope, then q_pe
     float* part;         // workspace: acc [T*H][splits][R], then (max, sum) [T*H][splits][2]
+    float* yslice;       // workspace [T*H][slices][Dv]: each latent slice's share of out (slices > 0)
+    uint32_t* tickets;   // workspace [T*H]: slices of the row finished (zeroed by mla_absorb)
     int64_t T, S;
     int32_t H, R, N, P, Dv;
     float qk_scale;      // scale * log2(e): scores live in the base-2 domain
@@ -154,6 +156,7 @@ struct MlaPlan {
     int32_t row_blocks;  // 16-row blocks along the T*H rows
     int32_t row_groups;  // 16-row blocks per workgroup of the split kernel (1 or 2)
     int32_t combine_out; // output channels per combine workgroup (32 or 16)
+    int32_t slices;      // > 0: mla_combine_slice, R / 64 latent slices per row; 0: mla_combine4
     int64_t chunk;       // keys per split of `range` (a multiple of 16)
     KeyRange range;
 };
@@ -179,6 +182,8 @@ int prefill_wgs_per_cu(int variant, int D, int Dv, bool rel);
 bool prefill_rel_supported(int D, int Dv);
 hipError_t launch_prefill(const Problem& p, const PrefillPlan& plan, float* ws, const Launch& L);
 bool mla_fast_supported(int R, int P);
+// Whether mla_combine_slice serves (R, Dv): R a multiple of 64 up to 512, Dv <= 256.
+bool mla_slices_supported(int R, int Dv);
 hipError_t launch_mla_absorb(const MlaProblem& p, const Launch& L);
 hipError_t launch_mla_split(const MlaProblem& p, const MlaPlan& plan, const Launch& L);
 hipError_t launch_mla_combine(const MlaProblem& p, const MlaPlan& plan, const Launch& L);

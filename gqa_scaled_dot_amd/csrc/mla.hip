@@ -442,6 +442,8 @@ __global__ __launch_bounds__(kMlaThreads) void mla_absorb4_kernel(MlaProblem p) 
             const float* qpe = p.q + (int64_t)(t0 + tr) * qstride + (int64_t)h * (N + P) + N;
             float* dst = p.q_abs + ((int64_t)(t0 + tr) * p.H + h) * DL + R;
             for (int e = lane; e < P; e += 64) dst[e] = qpe[e];
+            // The row's slice counter for mla_combine_slice starts at zero.
+            if (lane == 0 && p.tickets) p.tickets[(int64_t)(t0 + tr) * p.H + h] = 0u;
         }
     }
 }
@@ -492,6 +494,7 @@ __global__ __launch_bounds__(kMlaThreads) void mla_absorb_kernel(MlaProblem p) {
         const float* qpe = p.q + (int64_t)(t0 + wave) * qstride + (int64_t)h * (N + P) + N;
         float* dst = p.q_abs + ((int64_t)(t0 + wave) * p.H + h) * DL + R;
         for (int e = lane; e < P; e += 64) dst[e] = qpe[e];
+        if (lane == 0 && p.tickets) p.tickets[(int64_t)(t0 + wave) * p.H + h] = 0u;
     }
 }
 
@@ -709,6 +712,174 @@ __global__ __launch_bounds__(kCombThreads) void mla_combine4_kernel(MlaProblem p
     }
 }
 
+// The merge split by latent channels instead of outputs: grid (T*H, R/64),
+// 256 threads. Workgroup (row, slice) merges the row's splits over its 64
+// latent channels only (so every partial accumulator is read once per call)
+// and multiplies them by the matching 64 columns of v_b[h], which gives the
+// slice's share of all Dv outputs:
+//   y[slice][e] = sum over c in the slice of v_b[h][e][c] o_lat[c].
+// out[e] is the sum of the slices' shares, added in slice order by whichever
+// workgroup of the row finishes last (a counter per row, zeroed by
+// mla_absorb earlier in the call). The shares are agent-scope atomic stores,
+// which reach the memory every XCD sees before the store completes; each
+// wave waits for its stores to complete before the workgroup takes its
+// ticket, and the last workgroup reads the shares with agent-scope atomic
+// loads, which do not hit a stale cached copy. (An agent-scope release fence
+// would write back the whole L2 of the XCD for each workgroup, which costs far
+// more than these few hundred bytes.)
+constexpr int kSliceW = 64;                   // latent channels per slice
+constexpr int kSliceC4 = kSliceW / 4;         // their float4 columns
+constexpr int kSliceGroups = kMlaThreads / kSliceC4;  // split groups (16)
+constexpr int kSliceBatch = 8;                // accumulator float4s requested up front per thread
+constexpr int kSliceMaxDv = 256;
+constexpr int kSliceMax = 8;                 // slices per row (R <= 512)
+
+__global__ __launch_bounds__(kMlaThreads) void mla_combine_slice_kernel(MlaProblem p, int nsplit) {
+    __shared__ float4 s_part[kSliceGroups][kSliceC4];
+    __shared__ float4 s_olat[kSliceC4];
+    __shared__ float s_w[kMlaMaxSplits];
+    __shared__ float s_red[kMlaWaves];
+    __shared__ uint32_t s_ticket;
+    const int R = p.R, C4 = R / 4;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int row = blockIdx.x;
+    const int slice = blockIdx.y, nslices = gridDim.y;
+    const int h = row % p.H;
+    const int sg = tid / kSliceC4, c4 = tid % kSliceC4;
+    const float* ml = p.part + (int64_t)p.T * p.H * nsplit * R + (int64_t)row * nsplit * 2;
+    const float4* acc4 = reinterpret_cast<const float4*>(p.part + (int64_t)row * nsplit * R) + slice * kSliceC4 + c4;
+
+    // Requests first: (max, sum) pairs, accumulator columns, v_b columns.
+    constexpr int kPairs = kMlaMaxSplits / kMlaThreads;
+    float2 mlv[kPairs];
+#pragma unroll
+    for (int j = 0; j < kPairs; ++j) {
+        const int i = tid + j * kMlaThreads;
+        mlv[j] = i < nsplit ? *reinterpret_cast<const float2*>(ml + 2 * i) : make_float2(-INFINITY, 0.0f);
+    }
+    float4 xa[kSliceBatch];
+#pragma unroll
+    for (int u = 0; u < kSliceBatch; ++u) {
+        const int i = sg + u * kSliceGroups;
+        xa[u] = i < nsplit ? acc4[(int64_t)i * C4] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
+    // Output e = 64 k + tid / 4 takes slice channels 16 q .. 16 q + 15 (q = tid % 4).
+    constexpr int kPass = kSliceMaxDv / 64;
+    const int eq = tid >> 2, q = tid & 3;
+    float4 vb[kPass][4];
+#pragma unroll
+    for (int k = 0; k < kPass; ++k) {
+        const int e = 64 * k + eq;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            vb[k][j] = e < p.Dv ? *reinterpret_cast<const float4*>(p.v_b + ((int64_t)h * p.Dv + e) * R +
+                                                                    slice * kSliceW + 16 * q + 4 * j)
+                                : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
+
+    auto block_reduce = [&](float x, bool is_max) {
+        for (int o = 32; o > 0; o >>= 1) {
+            const float y = __shfl_xor(x, o, 64);
+            x = is_max ? fmaxf(x, y) : x + y;
+        }
+        __syncthreads();
+        if (lane == 0) s_red[wave] = x;
+        __syncthreads();
+        x = s_red[0];
+        for (int i = 1; i < kMlaWaves; ++i) x = is_max ? fmaxf(x, s_red[i]) : x + s_red[i];
+        return x;
+    };
+
+    float mx = mlv[0].x;
+#pragma unroll
+    for (int j = 1; j < kPairs; ++j) mx = fmaxf(mx, mlv[j].x);
+    const float M = block_reduce(mx, true);
+    // No visible key in any split: every weight is zero and so is the row.
+    float ls = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kPairs; ++j) {
+        const int i = tid + j * kMlaThreads;
+        if (i < nsplit) {
+            const float wi = M == -INFINITY ? 0.0f : fast_exp2(mlv[j].x - M);
+            s_w[i] = wi;
+            ls = fmaf(mlv[j].y, wi, ls);
+        }
+    }
+    const float L = block_reduce(ls, false);  // its barriers also publish s_w
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+
+    float4 a = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    for (int i0 = sg;; i0 += kSliceBatch * kSliceGroups) {
+#pragma unroll
+        for (int u = 0; u < kSliceBatch; ++u) {
+            const int i = i0 + u * kSliceGroups;
+            const float wv = i < nsplit ? s_w[i] : 0.0f;
+            a.x = fmaf(xa[u].x, wv, a.x);
+            a.y = fmaf(xa[u].y, wv, a.y);
+            a.z = fmaf(xa[u].z, wv, a.z);
+            a.w = fmaf(xa[u].w, wv, a.w);
+        }
+        const int next = i0 + kSliceBatch * kSliceGroups;
+        if (next >= nsplit) break;
+#pragma unroll
+        for (int u = 0; u < kSliceBatch; ++u) {
+            const int i = next + u * kSliceGroups;
+            xa[u] = i < nsplit ? acc4[(int64_t)i * C4] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        }
+    }
+    s_part[sg][c4] = a;
+    __syncthreads();
+    if (tid < kSliceC4) {
+        float4 sum = s_part[0][tid];
+        for (int g = 1; g < kSliceGroups; ++g) {
+            const float4 v = s_part[g][tid];
+            sum.x += v.x; sum.y += v.y; sum.z += v.z; sum.w += v.w;
+        }
+        s_olat[tid] = make_float4(sum.x * inv, sum.y * inv, sum.z * inv, sum.w * inv);
+    }
+    __syncthreads();
+
+    // This slice's share of every output: four lanes per output, then their sum.
+    float* ys = p.yslice + ((int64_t)row * nslices + slice) * p.Dv;
+#pragma unroll
+    for (int k = 0; k < kPass; ++k) {
+        const int e = 64 * k + eq;
+        float d = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float4 o = s_olat[4 * q + j];
+            d = fmaf(vb[k][j].x, o.x, fmaf(vb[k][j].y, o.y, fmaf(vb[k][j].z, o.z, fmaf(vb[k][j].w, o.w, d))));
+        }
+        d += __shfl_xor(d, 1, 64);
+        d += __shfl_xor(d, 2, 64);
+        if (q == 0 && e < p.Dv) __hip_atomic_store(ys + e, d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    // Every wave's shares have completed before the ticket is taken.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0)
+        s_ticket = __hip_atomic_fetch_add(p.tickets + row, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (s_ticket != (uint32_t)(nslices - 1)) return;
+    const float* yr = p.yslice + (int64_t)row * nslices * p.Dv;
+    float* orow = p.out + (int64_t)row * p.Dv;
+    for (int e = tid; e < p.Dv; e += kMlaThreads) {
+        // All the row's shares requested before any is added.
+        float y[kSliceMax];
+#pragma unroll
+        for (int sl = 0; sl < kSliceMax; ++sl)
+            y[sl] = sl < nslices ? __hip_atomic_load(yr + (int64_t)sl * p.Dv + e, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT)
+                                 : 0.0f;
+        float sum = y[0];
+#pragma unroll
+        for (int sl = 1; sl < kSliceMax; ++sl)
+            if (sl < nslices) sum += y[sl];
+        orow[e] = sum;
+    }
+}
+
 template <int R, int P>
 hipError_t launch_split_rp(const MlaProblem& p, const MlaPlan& plan, const Launch& L) {
     if (plan.row_groups == 2) {
@@ -725,6 +896,9 @@ hipError_t launch_split_rp(const MlaProblem& p, const MlaPlan& plan, const Launc
 }  // namespace
 
 bool mla_fast_supported(int R, int P) { return (R == 512 || R == 256) && P == 64; }
+bool mla_slices_supported(int R, int Dv) {
+    return R % kSliceW == 0 && R / kSliceW <= kSliceMax && Dv >= 1 && Dv <= kSliceMaxDv;
+}
 
 hipError_t launch_mla_absorb(const MlaProblem& p, const Launch& L) {
     const dim3 grid((unsigned)p.H, (unsigned)((p.R + 63) / 64), (unsigned)((p.T + 3) / 4));
@@ -751,6 +925,12 @@ hipError_t launch_mla_split(const MlaProblem& p, const MlaPlan& plan, const Laun
 
 hipError_t launch_mla_combine(const MlaProblem& p, const MlaPlan& plan, const Launch& L) {
     if (plan.splits < 1 || plan.splits > kMlaMaxSplits) return hipErrorInvalidValue;
+    if (plan.slices > 0) {
+        if (!mla_slices_supported(p.R, p.Dv) || plan.slices != p.R / kSliceW || !p.yslice || !p.tickets)
+            return hipErrorInvalidValue;
+        const dim3 grid((unsigned)(p.T * p.H), (unsigned)plan.slices);
+        return launch_kernel(mla_combine_slice_kernel, grid, dim3(kMlaThreads), 0, L, p, plan.splits);
+    }
     if (p.R % 4 == 0 && p.R / 4 <= 256) {
         const size_t lds = sizeof(float4) * ((size_t)p.R / 4 + kCombThreads) + sizeof(float) * (plan.splits + kCombWaves);
         if (plan.combine_out == 16) {

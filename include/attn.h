@@ -414,7 +414,9 @@ typedef struct attn_plan_info {
     int32_t splits;
     int32_t tile_q;
     int32_t variant;  /* decode: 1 = the matrix-core kernel, 0 = the vector one;
-                         prefill: the MFMA tile (32 = 32x32x2, 16 = 16x16x4) */
+                         prefill: the MFMA tile (32 = 32x32x2, 16 = 16x16x4);
+                         MLA (attn_mla_plan): the latent slices the merge uses
+                         (0 = one merge per group of output channels) */
 } attn_plan_info;
 int attn_plan(const attn_params* p, attn_plan_info* info);
 
@@ -497,6 +499,11 @@ int attn_mla_forward(const attn_mla_params* p, const float* q, const float* stat
  * Tuning overrides for tests and sweeps (process-wide, not thread-safe):
  *   "decode_splits"  force the decode split count (0 = automatic)
  *   "decode_depth"   batches in flight per lane in the decode kernel, 2 or 3 (0 = automatic)
+ *   "decode_wgs_per_cu" workgroups per CU the decode split count aims for, 1..8
+ *                    (0 = automatic: 2 for the vector kernel; 1 for the
+ *                    matrix-core one where headDim + vHeadDim >= 256, else 2)
+ *   "decode_mfma"    1: the matrix-core decode wherever it can serve; -1: never;
+ *                    0 = automatic (groups of 5 or more query rows)
  *   "decode_rotate"  split i starts its chunk (i * value mod chunk) rows in
  *                    (rounded to a batch step); 0 = automatic (5/8 of a chunk)
  *   "decode_block"   where every query row sees every key of the range, the
@@ -512,6 +519,11 @@ int attn_mla_forward(const attn_mla_params* p, const float* q, const float* stat
  *                    a forced path that cannot serve *p is refused
  *   "mla_splits"     force the MLA key-range split count (0 = automatic)
  *   "mla_row_groups" 16-row blocks per MLA split workgroup, 1 or 2 (0 = automatic)
+ *   "mla_combine_out" output channels per MLA merge workgroup, 16 or 32 (0 = automatic)
+ *   "mla_slices"     1: merge the MLA splits by 64-channel latent slices (each
+ *                    slice's share of the outputs, added by the row's last
+ *                    slice workgroup) where kv_rank is a multiple of 64 up to 512
+ *                    and v_head_dim <= 256; -1: never; 0 = automatic
  *   "mla_generic"    1: run MLA on the generic kernel even where the
  *                    matrix-core one has an instance (0 = automatic)
  * Returns ATTN_ERR_INVALID for an unknown name.

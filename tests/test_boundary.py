@@ -345,16 +345,30 @@ def test_mla_invalid_params_are_named(bad, code, word):
 
 def test_mla_plans_and_workspace():
     dec = ga.attn_mla_plan(1, 8192, posOffset=8191, **MLA)
-    assert dec["path"] == "mla" and dec["tile_q"] == 16 and dec["splits"] > 1
-    # q_abs (16 rows x 576 floats, 256-byte aligned) then the splits' partial states.
-    want = 16 * 576 * 4 + 16 * dec["splits"] * (512 + 2) * 4
+    assert dec["path"] == "mla" and dec["tile_q"] == 16 and dec["splits"] > 1 and dec["slices"] == 8
+    # q_abs (16 rows x 576 floats, 256-byte aligned), the splits' partial
+    # states (256-byte aligned), then each row's 8 slice shares of the 128
+    # outputs (256-byte aligned) and one counter per row.
+    a256 = lambda n: -(-n // 256) * 256
+    part = a256(16 * dec["splits"] * (512 + 2) * 4)
+    want = 16 * 576 * 4 + part + a256(16 * 8 * 128 * 4) + 16 * 4
     assert ga.attn_mla_workspace_size(1, 8192, posOffset=8191, **MLA) == want
+    try:
+        ga.attn_set_option("mla_slices", -1)
+        assert ga.attn_mla_plan(1, 8192, posOffset=8191, **MLA)["slices"] == 0
+        assert ga.attn_mla_workspace_size(1, 8192, posOffset=8191, **MLA) == 16 * 576 * 4 + part
+    finally:
+        ga.attn_set_option("mla_slices", 0)
+    # v_head_dim past 256 keeps the per-output merge.
+    assert ga.attn_mla_plan(1, 8192, posOffset=8191, **dict(MLA, v_head_dim=320))["slices"] == 0
+    with pytest.raises(ga.AttnError):
+        ga.attn_set_option("mla_slices", 2)
     assert ga.attn_mla_plan(0, 16, **MLA)["path"] == "empty"
     assert ga.attn_mla_plan(1, 0, **MLA)["path"] == "zero"
     assert ga.attn_mla_workspace_size(1, 0, **MLA) == 0
     # Shapes without a matrix-core instance take the generic kernel, one split.
     gen = ga.attn_mla_plan(2, 50, heads=3, kv_rank=48, qk_nope=8, qk_rope=16, v_head_dim=8)
-    assert gen["path"] == "mla" and gen["tile_q"] == 1 and gen["splits"] == 1
+    assert gen["path"] == "mla" and gen["tile_q"] == 1 and gen["splits"] == 1 and gen["slices"] == 0
     # The sink keys below a window take a split of their own.
     kw = dict(MLA, posOffset=8191, window=1024)
     assert ga.attn_mla_plan(1, 8192, sinks=4, **kw)["splits"] == ga.attn_mla_plan(1, 8192, **kw)["splits"] + 1

@@ -97,14 +97,17 @@ def test_mla_forced_splits(splits):
 @pytest.mark.parametrize("kw", [dict(S=2000, T=2, heads=16, window=900, sinks=8), dict(S=700, T=1, heads=40),
                                 dict(S=1500, T=1, heads=16, kv_rank=256, v_head_dim=96)])
 def test_mla_combine_widths(out, kw):
-    # Combine workgroups of 16 or 32 output channels (v_head_dim 96 leaves a
-    # partial last slice at 32).
+    # The per-output merge: workgroups of 16 or 32 output channels (v_head_dim
+    # 96 leaves a partial last group at 32).
     w = _wl(**kw)
     try:
+        ga.attn_set_option("mla_slices", -1)
         ga.attn_set_option("mla_combine_out", out)
+        assert ga.attn_mla_plan(w.T, w.S, **w.params())["slices"] == 0
         _check(w, what=f"combine_out={out} {kw}")
     finally:
         ga.attn_set_option("mla_combine_out", 0)
+        ga.attn_set_option("mla_slices", 0)
 
 
 def test_mla_never_reads_past_the_position_or_the_gap():
@@ -155,3 +158,80 @@ def test_mla_v3_decode_full_size_sampled_heads():
         qh = np.ascontiguousarray(q[:, h * (N + P):(h + 1) * (N + P)])
         ref = mla.mla_attention(qh, state, k_b[h:h + 1], v_b[h:h + 1], **one.params())
         assert_close(got[:, h * Dv:(h + 1) * Dv], ref, f"v3 head {h}")
+
+
+@pytest.fixture
+def slice_merge():
+    ga.attn_set_option("mla_slices", 1)  # also the automatic choice for these shapes
+    yield
+    ga.attn_set_option("mla_slices", 0)
+
+
+@pytest.mark.parametrize("kw", [dict(T=1, S=300, heads=16), dict(T=2, S=1000, heads=16), dict(T=5, S=129, heads=7),
+                                dict(T=33, S=64, heads=4), dict(T=1, S=513, heads=128),
+                                dict(T=1, S=300, heads=3, kv_rank=256), dict(T=3, S=700, heads=5, v_head_dim=100),
+                                dict(T=2, S=90, heads=4, v_head_dim=7, qk_nope=16),
+                                dict(T=1, S=200, heads=4, v_head_dim=256, qk_nope=192),
+                                dict(S=2000, T=2, heads=16, window=900, sinks=8), dict(S=900, causal=False, window=40),
+                                dict(S=900, T=4, causal=False, window=5, sinks=2, posOffset=50),
+                                dict(S=17, T=1, heads=5), dict(S=1, T=1, heads=2)])
+def test_mla_slice_merge(kw, slice_merge):
+    # The merge by latent slices: each slice workgroup projects its share,
+    # the row's last one adds the shares.
+    w = _wl(**kw)
+    plan = ga.attn_mla_plan(w.T, w.S, **w.params())
+    assert plan["slices"] == w.kv_rank // 64, plan
+    _check(w, what=f"slices {kw}")
+
+
+def test_mla_slice_merge_empty_rows(slice_merge):
+    # Window 1 at positions S-1 and S: the second row sees only key S, past
+    # the state, so its output is exactly zero while the first row's is not.
+    w = _wl(S=50, T=2, heads=4, window=1, posOffset=49)
+    got = _check(w, what="slices, one empty row")
+    assert np.all(got[1] == 0.0) and np.any(got[0] != 0.0)
+
+
+@pytest.mark.parametrize("splits", [1, 3, 250, 1000])
+def test_mla_slice_merge_split_counts(splits, slice_merge):
+    # Split counts past one batch of accumulator loads per thread (8 x 16).
+    w = _wl(S=16000, T=1, heads=4)
+    try:
+        ga.attn_set_option("mla_splits", splits)
+        assert ga.attn_mla_plan(w.T, w.S, **w.params())["splits"] == splits
+        _check(w, what=f"slices, splits={splits}")
+    finally:
+        ga.attn_set_option("mla_splits", 0)
+
+
+def test_mla_slice_merge_repeated_calls(slice_merge):
+    # Each call's counters start from zero: back-to-back calls with one
+    # workspace, a larger then a smaller problem, give the same bits as fresh ones.
+    big, small = _wl(S=3000, T=2, heads=16), _wl(S=500, T=1, heads=4)
+    tb, ts = big.tensors(), small.tensors()
+    ws = torch().empty(max(ga.attn_mla_workspace_size(big.T, big.S, **big.params()),
+                           ga.attn_mla_workspace_size(small.T, small.S, **small.params())),
+                       dtype=torch().uint8, device="cuda")
+    def run(w, t):
+        o = ga.attn_mla_forward(dev(t[0]), dev(t[1]), dev(t[2]), dev(t[3]), workspace=ws, **w.params())
+        torch().cuda.synchronize()
+        return o.cpu().numpy()
+    first = [run(big, tb), run(small, ts)]
+    for _ in range(3):
+        assert np.array_equal(run(big, tb), first[0])
+        assert np.array_equal(run(small, ts), first[1])
+    assert_close(first[0], mla.mla_attention(*tb, **big.params()), "slices, repeated big")
+    assert_close(first[1], mla.mla_attention(*ts, **small.params()), "slices, repeated small")
+
+
+def test_mla_slice_merge_full_size(slice_merge):
+    _check(workloads.MLA_DECODE, what="slices, V2-Lite-shaped")
+    w = workloads.MLA_DECODE_V3
+    q, state, k_b, v_b = w.tensors()
+    got = _run(w, (q, state, k_b, v_b))
+    N, P, Dv = w.qk_nope, w.qk_rope, w.v_head_dim
+    for h in (0, 5, 63, 127):
+        one = w.replace(heads=1)
+        qh = np.ascontiguousarray(q[:, h * (N + P):(h + 1) * (N + P)])
+        ref = mla.mla_attention(qh, state, k_b[h:h + 1], v_b[h:h + 1], **one.params())
+        assert_close(got[:, h * Dv:(h + 1) * Dv], ref, f"slices, v3 head {h}")
