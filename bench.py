@@ -78,6 +78,8 @@ METRIC = "decode KV GB/s + prefill TFLOP/s (f32), % of MI355X roofline, 1 GPU"
 HBM_PEAK_GBS = 8000.0
 FP32_PEAK_TFLOPS = 157.3
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+# The sources a kernel's counters depend on: its own files, and the planner
+# (attn_api.hip), which sets its grid, split counts and workspace layout.
 KERNEL_SOURCES = {
     "decode_split": ["gqa_scaled_dot_amd/csrc/decode.hip", "gqa_scaled_dot_amd/csrc/device_common.h",
                      "gqa_scaled_dot_amd/csrc/kernels.h", "gqa_scaled_dot_amd/csrc/rope_device.h"],
@@ -91,6 +93,8 @@ KERNEL_SOURCES = {
     "mla_split": ["gqa_scaled_dot_amd/csrc/mla.hip", "gqa_scaled_dot_amd/csrc/device_common.h",
                   "gqa_scaled_dot_amd/csrc/kernels.h"],
 }
+for _srcs in KERNEL_SOURCES.values():
+    _srcs.append("gqa_scaled_dot_amd/csrc/attn_api.hip")
 
 
 def log(*a):
