@@ -459,13 +459,15 @@ void attn_mla_params_init(attn_mla_params* p);
 int attn_mla_validate(const attn_mla_params* p);
 
 /* Bytes of device workspace attn_mla_forward needs (0 for an invalid *p or
- * when nothing is launched). It holds the absorbed queries and the key
- * splits' partial softmax states. */
+ * when nothing is launched). It holds the absorbed queries, the key
+ * splits' partial softmax states and, for the merge by latent slices, each
+ * slice's share of the outputs and a counter per row. */
 size_t attn_mla_workspace_size(const attn_mla_params* p);
 
 /* Which kernels attn_mla_forward would launch: path ATTN_PATH_MLA (or EMPTY
  * / ZERO), splits = key-range splits, tile_q = rows per workgroup (16 on
- * the matrix-core kernel, 1 on the generic one). */
+ * the matrix-core kernel, 1 on the generic one), variant = latent slices of
+ * the merge (0: per-output merge). */
 int attn_mla_plan(const attn_mla_params* p, attn_plan_info* info);
 
 /*
