@@ -444,13 +444,16 @@ def run_config(w, args, kv_buffers=1, extra=None, label=None):
     torch.cuda.synchronize()
     # Kernel durations from dispatch-stamped events ...
     ga.attn_timing_enable(True)
-    for kname in (main_kernel, "combine"):
+    for kname in (main_kernel, "combine", "prefill_band"):
         ga.attn_timing_collect(kname)
     for i in range(n):
         calls[i % kv_buffers]()
     torch.cuda.synchronize()
     k_ms, k_n = ga.attn_timing_collect(main_kernel)
     c_ms, c_n = ga.attn_timing_collect("combine")
+    # Relative embeddings at 128-wide heads: the band tiles' launch counts
+    # with the prefill kernel's.
+    b_ms, b_n = ga.attn_timing_collect("prefill_band")
     ga.attn_timing_enable(False)
     # ... and the call time from a loop without them.
     stream = torch.cuda.current_stream(dev)
@@ -461,7 +464,7 @@ def run_config(w, args, kv_buffers=1, extra=None, label=None):
     e1.record(stream)
     torch.cuda.synchronize()
     ms_call = e0.elapsed_time(e1) / n
-    kern_s = k_ms / k_n * 1e-3
+    kern_s = k_ms / k_n * 1e-3 + (b_ms / b_n * 1e-3 if b_n else 0.0)
     if plan["path"] == "decode":
         work = decode_algorithmic_bytes(w)
         achieved, value, unit, peak, bound = work / kern_s / 1e9, work / (ms_call * 1e-3) / 1e9, \
@@ -471,6 +474,7 @@ def run_config(w, args, kv_buffers=1, extra=None, label=None):
         achieved, value, unit, peak, bound = work / kern_s / 1e12, work / (ms_call * 1e-3) / 1e12, \
             "TFLOP/s", FP32_PEAK_TFLOPS, "mfma"
     log(f"[bench]   call {ms_call * 1e3:.1f} us, {main_kernel} {kern_s * 1e6:.1f} us x{k_n}"
+        + (f" (band launch {b_ms / b_n * 1e3:.1f} us of it)" if b_n else "")
         + (f", combine {c_ms / c_n * 1e3:.2f} us" if c_n else "")
         + f": {achieved:.2f} {unit} = {achieved / peak:.1%} of {peak}")
     # The oracle checks every output row (prefill-shaped calls too, unless
@@ -497,6 +501,7 @@ def run_config(w, args, kv_buffers=1, extra=None, label=None):
                      "kernel": main_kernel,
                      ("bytes_per_launch" if bound == "hbm" else "flops_per_launch"): work,
                      "avg_launch_us": round(kern_s * 1e6, 3),
+                     "band_launch_us": round(b_ms / b_n * 1e3, 3) if b_n else None,
                      "combine_us": round(c_ms / c_n * 1e3, 3) if c_n else None},
         "parity": {"rows": n_rows, "all_rows": rows is None, "max_abs_err": float(err.max()), "ok": ok,
                    "oracle_s": round(t_oracle, 3), "oracle_threads": cpu_threads()},

@@ -734,7 +734,26 @@ int make_plan(const Resolved& r, Plan* plan, const AppendRows* app = nullptr) {
             return fail(ATTN_ERR_UNSUPPORTED, "T: too many query rows for the prefill grid");
         pp.qblocks = (int32_t)qblocks;
         // Too few workgroups to fill the chip: split each one's key range.
-        const int64_t slots = (int64_t)kCUs * attn::prefill_wgs_per_cu(pp.variant, (int)r.D, (int)r.Dv, r.ep.rel_k != nullptr);
+        // Relative embeddings at widths past 64/64: the tiles beyond the
+        // tables' reach go to a launch of their own, on an instance without
+        // the band code (as many workgroups per CU as the epilogue instance),
+        // and the band tiles to a second launch (one part per workgroup).
+        pp.rel_band = r.ep.rel_k && r.D + r.Dv > 128 ? 1 : 0;
+        const bool rel_occupancy = r.ep.rel_k != nullptr && !pp.rel_band;
+        if (pp.rel_band) {
+            // The band launch runs one workgroup per CU: split its tiles
+            // into parts where the grid alone would leave CUs idle, keeping
+            // two or more band tiles per part (a causal row block has about
+            // (max_distance + rows) / 32 of them).
+            const int64_t band_slots = (int64_t)kCUs * attn::prefill_wgs_per_cu(pp.variant, (int)r.D, (int)r.Dv, true);
+            int64_t kb = nwg >= band_slots ? 1 : (band_slots + nwg - 1) / nwg;
+            const int64_t band_tiles = (r.ep.rel_max + pp.tile_q) / 32;
+            if (kb > band_tiles / 2) kb = band_tiles / 2;
+            if (kb < 1) kb = 1;
+            if (kb > kPrefillMaxSplits) kb = kPrefillMaxSplits;
+            pp.rel_band = (int32_t)kb;
+        }
+        const int64_t slots = (int64_t)kCUs * attn::prefill_wgs_per_cu(pp.variant, (int)r.D, (int)r.Dv, rel_occupancy);
         const int64_t tiles = (kr.hi > kr.lo ? (kr.hi - kr.lo + 31) / 32 : 0) + (sink_hi + 31) / 32;
         int64_t ks = g_opt_prefill_splits;
         if (ks <= 0) {
@@ -745,7 +764,8 @@ int make_plan(const Resolved& r, Plan* plan, const AppendRows* app = nullptr) {
         if (ks < 1) ks = 1;
         if (ks > kPrefillMaxSplits) ks = kPrefillMaxSplits;
         pp.ksplit = (int32_t)ks;
-        if (ks > 1) plan->workspace = sizeof(float) * (size_t)(r.T * r.H) * (size_t)ks * (size_t)(r.Dv + 2);
+        const int64_t kslots = ks + pp.rel_band;
+        if (kslots > 1) plan->workspace = sizeof(float) * (size_t)(r.T * r.H) * (size_t)kslots * (size_t)(r.Dv + 2);
         plan->reserve = plan->workspace;
     }
     return ok();
@@ -1114,11 +1134,15 @@ int run_plan(const Resolved& r, const Plan& plan, const attn::Problem& prob, voi
             break;
         case ATTN_PATH_PREFILL:
             err = timed("prefill", s, [&](const attn::Launch& L) {
-                return attn::launch_prefill(prob, plan.prefill, (float*)workspace, L);
+                return attn::launch_prefill(prob, plan.prefill, (float*)workspace, plan.prefill.rel_band ? 1 : 0, L);
             });
-            if (err == hipSuccess && plan.prefill.ksplit > 1) {
+            if (err == hipSuccess && plan.prefill.rel_band)
+                err = timed("prefill_band", s, [&](const attn::Launch& L) {
+                    return attn::launch_prefill(prob, plan.prefill, (float*)workspace, 2, L);
+                });
+            if (err == hipSuccess && plan.prefill.ksplit + plan.prefill.rel_band > 1) {
                 attn::DecodePlan merge{};
-                merge.splits = plan.prefill.ksplit;
+                merge.splits = plan.prefill.ksplit + plan.prefill.rel_band;
                 err = timed("combine", s, [&](const attn::Launch& L) {
                     return attn::launch_decode_combine(prob, merge, (const float*)workspace, L);
                 });
@@ -1167,7 +1191,7 @@ int attn_plan(const attn_params* p, attn_plan_info* info) {
     if (rc) return rc;
     info->path = plan.path;
     info->splits = plan.path == ATTN_PATH_DECODE    ? plan.decode.splits
-                   : plan.path == ATTN_PATH_PREFILL ? plan.prefill.ksplit
+                   : plan.path == ATTN_PATH_PREFILL ? plan.prefill.ksplit + plan.prefill.rel_band
                                                     : 1;
     info->tile_q = plan.path == ATTN_PATH_PREFILL ? plan.prefill.tile_q : 0;
     info->variant = plan.path == ATTN_PATH_DECODE    ? plan.decode.mfma

@@ -106,6 +106,9 @@ struct PrefillPlan {
     int32_t nh;       // heads of one KV group per workgroup
     int32_t qblocks;  // workgroups along the query rows
     int32_t ksplit;   // key-range parts per workgroup (partials merged by the combine kernel)
+    int32_t rel_band; // > 0: relative embeddings in two launches, the tiles beyond the tables'
+                      // reach (ksplit parts) then the band tiles (rel_band parts): ksplit +
+                      // rel_band partials; 0: one launch
 };
 
 // Where and how one kernel launch goes: the caller's stream, and optionally
@@ -180,7 +183,9 @@ hipError_t launch_decode_mfma(const Problem& p, const DecodePlan& plan, float* w
 bool prefill_supported(int D, int Dv);
 int prefill_wgs_per_cu(int variant, int D, int Dv, bool rel);
 bool prefill_rel_supported(int D, int Dv);
-hipError_t launch_prefill(const Problem& p, const PrefillPlan& plan, float* ws, const Launch& L);
+// part: 0 every key tile; with plan.rel_band, 1 the tiles beyond the relative
+// tables' reach, 2 the band tiles.
+hipError_t launch_prefill(const Problem& p, const PrefillPlan& plan, float* ws, int part, const Launch& L);
 bool mla_fast_supported(int R, int P);
 // Whether mla_combine_slice serves (R, Dv): R a multiple of 64 up to 512, Dv <= 256.
 bool mla_slices_supported(int R, int Dv);

@@ -100,6 +100,9 @@ __device__ __forceinline__ void lds_read(const float* src, float (&dst)[NB]) {
 // Waves per SIMD the register budget allows (two while q, o and staging fit
 // in 256 registers per lane).
 constexpr int prefill_min_waves(int D, int DV) { return D + DV <= 256 ? 2 : 1; }
+// The same for the instances with relative key/value embeddings (their band
+// tiles hold the relative rows' scores and weights as well): two only at 64/64.
+constexpr int prefill_rel_waves(int D, int DV) { return D + DV <= 128 ? 2 : 1; }
 
 constexpr int kRelRows = 64;  // relative rows per band tile: d_lo .. d_lo + 63
 
@@ -115,9 +118,15 @@ struct PrefillShape {
     static constexpr size_t rel_lds_bytes = sizeof(float) * kWaves * kBQ * kRelRows;
 };
 
-template <int D, int DV, bool EPI, bool REL>
-__global__ __launch_bounds__(kThreads, REL ? 1 : prefill_min_waves(D, DV)) void prefill_kernel(
+// RM: relative key/value embeddings. 0: off. 2: on, every tile (band tiles
+// with their per-key rows). 1: on, for a launch of the tiles beyond the
+// tables' reach for every row of the workgroup (Args::part 1): the band code
+// is left out, so the instance needs no more registers than the epilogue one.
+template <int D, int DV, bool EPI, int RM>
+__global__ __launch_bounds__(kThreads, RM == 2 ? prefill_rel_waves(D, DV) : prefill_min_waves(D, DV)) void prefill_kernel(
     Problem p, Args a) {
+    constexpr bool REL = RM != 0;
+    constexpr bool BAND = RM == 2;
     using Sh = PrefillShape<D, DV>;
     constexpr int KLD = Sh::KLD, VLD = Sh::VLD, NB = Sh::NB;
     extern __shared__ float lds[];
@@ -195,12 +204,24 @@ __global__ __launch_bounds__(kThreads, REL ? 1 : prefill_min_waves(D, DV)) void 
         qrelN = aN + __shfl_xor(aN, 32, 64);
     }
 
-    // This workgroup's part of its key tiles (sink tiles, then window tiles).
+    // This workgroup's part of its key tiles (sink tiles, then window tiles):
+    // with relative embeddings split over two launches, the tiles beyond
+    // their reach (part 1, index j skipping the band run [vb0, vb1)) or the
+    // band run alone (part 2).
     const KeyRows rows = key_rows(p.ep, klo, khi);
     const TileSpan span = tile_span(rows);
-    const int per = (span.count + a.ksplit - 1) / a.ksplit;
-    const int v0 = min(span.count, ks * per);
-    const int v1 = min(span.count, v0 + per);
+    int vb0 = 0, vb1 = 0;
+    if (a.part != 0) band_tiles(span, p.ep.pos_offset + qwg0, p.ep.pos_offset + wg_last, M, vb0, vb1);
+    const int nsel = a.part == 0 ? span.count : a.part == 1 ? span.count - (vb1 - vb0) : vb1 - vb0;
+    const int skip = a.part == 1 ? vb1 - vb0 : 0;
+    const int first = a.part == 2 ? vb0 : 0;
+    auto tile_of = [&](int jj) {
+        const int v = first + (jj < vb0 || a.part != 1 ? jj : jj + skip);
+        return span.tile(v);
+    };
+    const int per = (nsel + a.ksplit - 1) / a.ksplit;
+    const int v0 = min(nsel, ks * per);
+    const int v1 = min(nsel, v0 + per);
 
     const int64_t kstride = (int64_t)p.G * D, vstride = (int64_t)p.G * DV;
     const float* kg = p.k + (int64_t)g * D;
@@ -209,16 +230,16 @@ __global__ __launch_bounds__(kThreads, REL ? 1 : prefill_min_waves(D, DV)) void 
 
     const float qk_scale = p.ep.scale * kLog2e;
     if (v0 < v1) {
-        fetch_rows<D, kThreads>(kst, kg, kstride, span.tile(v0), rows);
-        fetch_rows<DV, kThreads>(vst, vg, vstride, span.tile(v0), rows);
+        fetch_rows<D, kThreads>(kst, kg, kstride, tile_of(v0), rows);
+        fetch_rows<DV, kThreads>(vst, vg, vstride, tile_of(v0), rows);
         stage_rows<D, kThreads>(kst, ktile);
         stage_rows<DV, kThreads>(vst, vtile);
     }
     for (int v = v0; v < v1; ++v) {
-        const int kt = span.tile(v);
+        const int kt = tile_of(v);
         const int buf = (v - v0) & 1;
         const bool more = v + 1 < v1;
-        const int kt_next = span.tile(v + 1);
+        const int kt_next = tile_of(v + 1);
         __syncthreads();  // tile `kt` is in LDS; everyone is done with the other buffer
         if (more) fetch_rows<D, kThreads>(kst, kg, kstride, kt_next, rows);
 
@@ -261,14 +282,14 @@ __global__ __launch_bounds__(kThreads, REL ? 1 : prefill_min_waves(D, DV)) void 
                 // The relative-key term joins the product before the scale.
                 d_lo = s_first - wpl;
                 const int d_hi = s_first + kBK - 1 - wpf;
-                rel_cls = d_hi <= -M ? 1 : (d_lo >= M ? 2 : 0);
+                rel_cls = d_hi <= -M ? 1 : (d_lo >= M || !BAND ? 2 : 0);
                 if (rel_cls == 1) {
 #pragma unroll
                     for (int r = 0; r < 16; ++r) sacc[r] += qrel0;
                 } else if (rel_cls == 2) {
 #pragma unroll
                     for (int r = 0; r < 16; ++r) sacc[r] += qrelN;
-                } else {
+                } else if constexpr (BAND) {
                     // q . rel_k[clip(d) + M] for d = d_lo + i, i < 64 (rows
                     // i = 32 ps + col on the A side), into the wave's LDS rows.
 #pragma unroll
@@ -343,7 +364,7 @@ __global__ __launch_bounds__(kThreads, REL ? 1 : prefill_min_waves(D, DV)) void 
                     wL += ps;
                 } else if (rel_cls == 2) {
                     wR += ps;
-                } else if (p.ep.rel_v) {
+                } else if (BAND && p.ep.rel_v) {
                     // The weights by relative offset (zero where no key of
                     // this query falls), then O^T += rel_v^T P_rel^T.
 #pragma unroll
@@ -406,15 +427,16 @@ __global__ __launch_bounds__(kThreads, REL ? 1 : prefill_min_waves(D, DV)) void 
     const int64_t th = (int64_t)t * p.H + h;
     float* dst;
     float sc;
-    if (a.ksplit == 1) {
+    if (a.kslots == 1) {
         dst = p.out + th * DV;
         sc = lt > 0.0f ? 1.0f / lt : 0.0f;
     } else {
         // Unnormalised partial state (max in the base-2 domain, sum, acc).
-        dst = a.ws + (th * a.ksplit + ks) * DV;
+        const int slot = a.kslot0 + ks;
+        dst = a.ws + (th * a.kslots + slot) * DV;
         sc = 1.0f;
         if (half == 0) {
-            float* ml = a.ws + (int64_t)T * p.H * a.ksplit * DV + (th * a.ksplit + ks) * 2;
+            float* ml = a.ws + (int64_t)T * p.H * a.kslots * DV + (th * a.kslots + slot) * 2;
             ml[0] = m;
             ml[1] = lt;
         }
@@ -433,10 +455,10 @@ __global__ __launch_bounds__(kThreads, REL ? 1 : prefill_min_waves(D, DV)) void 
     }
 }
 
-template <int D, int DV, bool EPI, bool REL = false>
+template <int D, int DV, bool EPI, int RM = 0>
 hipError_t launch_t(const Problem& p, const Args& a, const Launch& L) {
-    auto kern = prefill_kernel<D, DV, EPI, REL>;
-    constexpr size_t lds = PrefillShape<D, DV>::lds_bytes + (REL ? PrefillShape<D, DV>::rel_lds_bytes : 0);
+    auto kern = prefill_kernel<D, DV, EPI, RM>;
+    constexpr size_t lds = PrefillShape<D, DV>::lds_bytes + (RM == 2 ? PrefillShape<D, DV>::rel_lds_bytes : 0);
     static bool configured = false;
     if (!configured) {
         const hipError_t e = set_lds_limit(kern, lds);
@@ -450,9 +472,20 @@ hipError_t launch_t(const Problem& p, const Args& a, const Launch& L) {
 template <int D, int DV>
 hipError_t launch_dims(const Problem& p, const Args& a, const Launch& L) {
     if (p.ep.rel_k) {
-        if constexpr (D + DV <= 256) return launch_t<D, DV, true, true>(p, a, L);
+        if constexpr (D + DV <= 256) {
+            if constexpr (D + DV > 128) {
+                // The far tiles need the epilogue instance only for terms
+                // besides the embeddings (their per-row constant joins the
+                // product before the scale either way).
+                const bool other = p.ep.softcap > 0.0f || p.ep.has_alibi || p.ep.bias_kind != ATTN_BIAS_NONE ||
+                                   p.ep.pb_weight != nullptr;
+                if (a.part == 1) return other ? launch_t<D, DV, true, 1>(p, a, L) : launch_t<D, DV, false, 1>(p, a, L);
+            }
+            return a.part == 1 ? hipErrorInvalidValue : launch_t<D, DV, true, 2>(p, a, L);
+        }
         return hipErrorInvalidValue;
     }
+    if (a.part != 0) return hipErrorInvalidValue;
     const bool epi = p.ep.any();
     return epi ? launch_t<D, DV, true>(p, a, L) : launch_t<D, DV, false>(p, a, L);
 }
@@ -469,24 +502,29 @@ bool prefill_supported(int D, int Dv) {
 // Workgroups per CU the prefill kernels reach (registers and LDS).
 int prefill_wgs_per_cu(int variant, int D, int Dv, bool rel) {
     if (variant == 16) return D + Dv <= 256 ? 2 : 1;
-    return rel ? 1 : prefill_min_waves(D, Dv);
+    return rel ? prefill_rel_waves(D, Dv) : prefill_min_waves(D, Dv);
 }
 
 // Relative key/value embeddings have 32x32x2 instances up to D + Dv = 256.
 bool prefill_rel_supported(int D, int Dv) { return prefill_supported(D, Dv) && D + Dv <= 256; }
 
-hipError_t launch_prefill(const Problem& p, const PrefillPlan& plan, float* ws, const Launch& L) {
+hipError_t launch_prefill(const Problem& p, const PrefillPlan& plan, float* ws, int part, const Launch& L) {
     Args a;
     a.nh = plan.nh;
     a.hgroups = (p.H / p.G) / plan.nh;
     a.qblocks = plan.qblocks;
-    a.ksplit = plan.ksplit;
     a.causal_order = p.ep.causal ? 1 : 0;
     a.ws = ws;
+    a.part = part;
+    a.kslots = plan.ksplit + plan.rel_band;
+    a.ksplit = part == 2 ? plan.rel_band : plan.ksplit;
+    a.kslot0 = part == 2 ? plan.ksplit : 0;
+    if (part < 0 || part > 2 || (part != 0) != (plan.rel_band != 0) || (part != 0 && !p.ep.rel_k))
+        return hipErrorInvalidValue;
     if (a.nh < 1 || a.hgroups < 1 || a.qblocks < 1 || a.ksplit < 1) return hipErrorInvalidValue;
-    if (a.ksplit > 1 && !ws) return hipErrorInvalidValue;
+    if (a.kslots > 1 && !ws) return hipErrorInvalidValue;
     if ((int64_t)a.qblocks * p.G * a.hgroups * a.ksplit > INT32_MAX) return hipErrorInvalidValue;
-    if (plan.variant == 16) return launch_prefill16(p, a, L);
+    if (plan.variant == 16) return part == 0 ? launch_prefill16(p, a, L) : hipErrorInvalidValue;
     if (plan.variant != 32) return hipErrorInvalidValue;
     if (p.D == 64 && p.Dv == 64) return launch_dims<64, 64>(p, a, L);
     if (p.D == 128 && p.Dv == 128) return launch_dims<128, 128>(p, a, L);

@@ -231,14 +231,15 @@ __global__ __launch_bounds__(kThreads16, 1) void prefill16_kernel(Problem p, Arg
     const int64_t th = (int64_t)t * p.H + h;
     float* dst;
     float sc;
-    if (a.ksplit == 1) {
+    if (a.kslots == 1) {
         dst = p.out + th * DV;
         sc = lt > 0.0f ? 1.0f / lt : 0.0f;
     } else {
-        dst = a.ws + (th * a.ksplit + c.ks) * DV;
+        const int slot = a.kslot0 + c.ks;
+        dst = a.ws + (th * a.kslots + slot) * DV;
         sc = 1.0f;
         if (quad == 0) {
-            float* ml = a.ws + (int64_t)T * p.H * a.ksplit * DV + (th * a.ksplit + c.ks) * 2;
+            float* ml = a.ws + (int64_t)T * p.H * a.kslots * DV + (th * a.kslots + slot) * 2;
             ml[0] = m;
             ml[1] = lt;
         }

@@ -21,10 +21,15 @@ struct Args {
     int nh;            // heads per workgroup
     int hgroups;       // head groups per KV head = (heads/kvHeads) / nh
     int qblocks;       // workgroups along the query rows
-    int ksplit;        // parts of each workgroup's key range (1: write out directly)
+    int ksplit;        // parts of this launch's key tiles per workgroup
     int causal_order;  // 1: heaviest query blocks first
-    float* ws;         // partial states when ksplit > 1
+    float* ws;         // partial states when kslots > 1
+    int part;          // key tiles of a workgroup this launch takes: 0 all; with relative
+                       // embeddings 1 those beyond their reach for every row, 2 the rest
+    int kslot0;        // partial-state slot of this launch's part 0
+    int kslots;        // partial-state slots per row over all launches (1: write out directly)
 };
+
 
 struct Coords {
     int ks;   // key-range part
@@ -105,6 +110,27 @@ __device__ __forceinline__ TileSpan tile_span(const KeyRows& r) {
     t.nst = kt_w1 > t.kt_w0 ? min(nst, t.kt_w0) : nst;
     t.count = t.nst + (kt_w1 - t.kt_w0);
     return t;
+}
+
+// The key-tile indices (in tile_span order) of the tiles that some query at
+// positions [pf, pl] sees within M of its position: a contiguous run
+// [vb0, vb1), since tile_span's tiles rise with the index. Tiles before it lie
+// M or more before every query, tiles after it M or more after.
+__device__ __forceinline__ void band_tiles(const TileSpan& t, int pf, int pl, int M, int& vb0, int& vb1) {
+    // Tiles below key tile x, in tile_span order.
+    auto below = [&](int x) {
+        const int sinks = min(t.nst, max(x, 0));
+        const int win = min(max(x - t.kt_w0, 0), t.count - t.nst);
+        return sinks + win;
+    };
+    // Far before every query: the tile's last key s with s - pf <= -M.
+    const int kl = pf - M - (kBK - 1);  // key tile kt is far iff kt * kBK <= kl
+    const int first_band = kl < 0 ? 0 : kl / kBK + 1;
+    // Far after every query: the tile's first key s with s - pl >= M.
+    const int kr = pl + M;              // key tile kt is far iff kt * kBK >= kr
+    const int first_after = kr <= 0 ? 0 : (kr + kBK - 1) / kBK;
+    vb0 = below(first_band);
+    vb1 = max(vb0, below(first_after));
 }
 
 // Whether any / every query at positions [wpf, wpl] sees any / every key of

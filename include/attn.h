@@ -540,9 +540,11 @@ int attn_set_option(const char* name, int64_t value);
  * count since the last collect (then clears them). Off by default; the hot
  * path records nothing when off. Event pairs come from a fixed pool of 4096,
  * created on the first enable; launches beyond the pool are not timed.
- * Kernel names: "cache_write", "decode_split", "prefill", "combine" (merges
- * key-range splits after either), "generic", "zero_fill", "rope" (attn_rope and
- * attn_rope_cache_write), "mla_absorb", "mla_split", "mla_combine".
+ * Kernel names: "cache_write", "decode_split", "decode_mfma", "prefill",
+ * "prefill_band" (the band tiles' launch of a prefill with relative key/value
+ * embeddings at widths past 64/64), "combine" (merges key-range splits after
+ * the decode and prefill kernels), "generic", "zero_fill", "rope" (attn_rope
+ * and attn_rope_cache_write), "mla_absorb", "mla_split", "mla_combine".
  */
 int attn_timing_enable(int on);
 int attn_timing_collect(const char* kernel, double* total_ms, int64_t* launches);

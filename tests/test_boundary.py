@@ -144,6 +144,28 @@ def test_decode_workspace_matches_plan():
     assert ga.attn_workspace_size(1, 32768, **rel) == 4 * 32 * ga.attn_plan(1, 32768, **rel)["splits"] * (128 + 2)
 
 
+def test_relative_kv_prefill_plans():
+    # Relative key/value embeddings on the 32x32x2 prefill kernel: at 128-wide
+    # heads the tiles beyond the tables' reach and the band tiles run as two
+    # launches, the band one in parts of its own (here 2: 128 workgroups for
+    # 256 CUs, (128 + 32) / 32 = 5 band tiles per row block), each leaving a
+    # partial state per row; at 64-wide heads one launch covers every tile.
+    for D, band in ((128, 2), (64, 0)):
+        kw = dict(heads=32, kvHeads=8, headDim=D, posOffset=3584,
+                  relative_kv=dict(key=4096, value=8192, max_distance=128))
+        plan = ga.attn_plan(512, 4096, **kw)
+        assert plan["path"] == "prefill" and plan["variant"] == 32
+        try:
+            ga.attn_set_option("prefill_splits", 3)
+            assert ga.attn_plan(512, 4096, **kw)["splits"] == 3 + band
+            assert ga.attn_workspace_size(512, 4096, **kw) == 4 * 512 * 32 * (3 + band) * (D + 2)
+            ga.attn_set_option("prefill_splits", 1)
+            assert ga.attn_plan(512, 4096, **kw)["splits"] == 1 + band
+            assert ga.attn_workspace_size(512, 4096, **kw) == (4 * 512 * 32 * (1 + band) * (D + 2) if band else 0)
+        finally:
+            ga.attn_set_option("prefill_splits", 0)
+
+
 @pytest.mark.parametrize("G", [1, 2, 6, 8, 12, 16, 24])
 def test_decode_splits_fit_one_wave(G):
     # Two workgroups per CU on 256 CUs: splits x KV groups never passes 512,
