@@ -47,8 +47,12 @@ constexpr int64_t kFewMinOutputs = 65536;  // ... when there are at least this m
 
 template <int D, int DV, int NQ, bool EPI>
 struct DecodeShape {
-    static constexpr int KJ = D / 64;   // float4 per lane per K row
-    static constexpr int VJ = DV / 64;  // float4 per lane per V row
+    // float4 per lane per K / V row: lane ln of a row group takes channels
+    // 64 j + 4 ln .. + 3; past the width (80- or 96-wide rows: the second
+    // group is partly empty) a lane loads the row's last float4 again, zeroes
+    // it where it enters a product, and stores nothing.
+    static constexpr int KJ = (D + 63) / 64;
+    static constexpr int VJ = (DV + 63) / 64;
     // Key rows per row group per batch (one batch per lane at a time). Fewer
     // loads in flight ran faster, down to about four float4s per lane: with
     // 128-wide heads the epilogue-free instance takes one-row batches (4
@@ -86,6 +90,12 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
     const int tid = threadIdx.x;
     const int ln = tid & 15;
     const int rg = tid >> 4;
+    // Whether this lane's float4 j of a K / V row lies within the row, and the
+    // in-row offset it loads from (the row's last float4 when it does not).
+    auto kin = [&](int j) { return 64 * j + 64 <= D || 64 * j + 4 * ln < D; };
+    auto vin = [&](int j) { return 64 * j + 64 <= DV || 64 * j + 4 * ln < DV; };
+    auto koff = [&](int j) { return kin(j) ? 64 * j : D - 4 - 4 * ln; };
+    auto voff = [&](int j) { return vin(j) ? 64 * j : DV - 4 - 4 * ln; };
     constexpr bool REL = RM != 0;
     constexpr bool FAR = RM == 1;
     // Split sp of KV group g. On an appending call the splits of appended
@@ -267,9 +277,12 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
             const int sc = min(r0 + u, k1 - 1);
             const uint32_t row = (uint32_t)(sc - k0);
 #pragma unroll
-            for (int j = 0; j < KJ; ++j) kf[u][j] = load_stream4(kwg + row * kstride + 64 * j);
+            for (int j = 0; j < KJ; ++j) {
+                const float4 x = load_stream4(kwg + row * kstride + koff(j));
+                kf[u][j] = kin(j) ? x : zero4();
+            }
 #pragma unroll
-            for (int j = 0; j < VJ; ++j) vf[u][j] = load_stream4(vwg + row * vstride + 64 * j);
+            for (int j = 0; j < VJ; ++j) vf[u][j] = load_stream4(vwg + row * vstride + voff(j));
             if constexpr (EPI) {
 #pragma unroll
                 for (int r = 0; r < NQ; ++r) {
@@ -372,7 +385,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
                         const float* rv = p.ep.rel_v + (int64_t)rel_row(p.ep, pos[r], r0 + u) * DV + 4 * ln;
 #pragma unroll
                         for (int j = 0; j < VJ; ++j) {
-                            const float4 x4 = ld4(rv + 64 * j);
+                            const float4 x4 = ld4(rv + voff(j));
                             acc[r][j].x = fmaf(pu[u], x4.x, acc[r][j].x);
                             acc[r][j].y = fmaf(pu[u], x4.y, acc[r][j].y);
                             acc[r][j].z = fmaf(pu[u], x4.z, acc[r][j].z);
@@ -396,10 +409,10 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
                         const uint32_t row = (uint32_t)(r0 + u - k0);
 #pragma unroll
                         for (int j = 0; j < KJ; ++j)
-                            *reinterpret_cast<float4*>(kd + (row * kstride + 4 * ln + 64 * j)) = kf[u][j];
+                            if (kin(j)) *reinterpret_cast<float4*>(kd + (row * kstride + 4 * ln + 64 * j)) = kf[u][j];
 #pragma unroll
                         for (int j = 0; j < VJ; ++j)
-                            *reinterpret_cast<float4*>(vd + (row * vstride + 4 * ln + 64 * j)) = vf[u][j];
+                            if (vin(j)) *reinterpret_cast<float4*>(vd + (row * vstride + 4 * ln + 64 * j)) = vf[u][j];
                     }
                 }
             }
@@ -451,13 +464,13 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
             for (int r = 0; r < NQ; ++r)
 #pragma unroll
                 for (int j = 0; j < KJ; ++j)
-                    qr[r][j] = *reinterpret_cast<const float4*>(s_q + r * D + 64 * j + 4 * ln);
+                    qr[r][j] = kin(j) ? *reinterpret_cast<const float4*>(s_q + r * D + 64 * j + 4 * ln) : zero4();
         } else {
 #pragma unroll
             for (int r = 0; r < NQ; ++r) {
                 const float* qrow = p.q + (int64_t)tt[r] * p.H * D + (int64_t)hh[r] * D + 4 * ln;
 #pragma unroll
-                for (int j = 0; j < KJ; ++j) qr[r][j] = live[r] ? ld4(qrow + 64 * j) : zero4();
+                for (int j = 0; j < KJ; ++j) qr[r][j] = live[r] && kin(j) ? ld4(qrow + 64 * j) : zero4();
             }
         }
         if constexpr (!EPI) {
@@ -477,7 +490,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
                 // across the row group's 16 lanes (every lane gets it).
                 float4 kv[KJ];
 #pragma unroll
-                for (int jj = 0; jj < KJ; ++jj) kv[jj] = ld4(p.ep.rel_k + 4 * ln + 64 * jj);
+                for (int jj = 0; jj < KJ; ++jj) kv[jj] = ld4(p.ep.rel_k + 4 * ln + koff(jj));
 #pragma unroll
                 for (int r = 0; r < NQ; ++r) {
                     float d = 0.0f;
@@ -494,7 +507,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
                     for (int i = 0; i < 4; ++i) {
                         const int j = min(j0 + i * kRowGroups, nrel - 1);
 #pragma unroll
-                        for (int jj = 0; jj < KJ; ++jj) kv[i][jj] = ld4(p.ep.rel_k + (int64_t)j * D + 4 * ln + 64 * jj);
+                        for (int jj = 0; jj < KJ; ++jj) kv[i][jj] = ld4(p.ep.rel_k + (int64_t)j * D + 4 * ln + koff(jj));
                     }
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
@@ -524,9 +537,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
                     const uint32_t row = (uint32_t)(s - k0);
                     float4 kf[KJ], vf[VJ];
 #pragma unroll
-                    for (int j = 0; j < KJ; ++j) kf[j] = ld4(kwg + row * kstride + 64 * j);
+                    for (int j = 0; j < KJ; ++j) kf[j] = kin(j) ? ld4(kwg + row * kstride + koff(j)) : zero4();
 #pragma unroll
-                    for (int j = 0; j < VJ; ++j) vf[j] = ld4(vwg + row * vstride + 64 * j);
+                    for (int j = 0; j < VJ; ++j) vf[j] = ld4(vwg + row * vstride + voff(j));
 #pragma unroll
                     for (int r = 0; r < NQ; ++r) {
                         float dot = 0.0f;
@@ -557,7 +570,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
                         for (int j = 0; j < VJ; ++j) {
                             float4 vv = vf[j];
                             if (rel && p.ep.rel_v) {
-                                const float4 rv = ld4(p.ep.rel_v + (int64_t)jr * DV + 4 * ln + 64 * j);
+                                const float4 rv = ld4(p.ep.rel_v + (int64_t)jr * DV + 4 * ln + voff(j));
                                 vv.x += rv.x; vv.y += rv.y; vv.z += rv.z; vv.w += rv.w;
                             }
                             acc[r][j].x = fmaf(pw, vv.x, acc[r][j].x);
@@ -601,7 +614,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
             for (int r = 0; r < NQ; ++r)
 #pragma unroll
                 for (int j = 0; j < VJ; ++j) {
-                    const float4 x4 = ld4(p.ep.rel_v + 4 * ln + 64 * j);
+                    const float4 x4 = ld4(p.ep.rel_v + 4 * ln + voff(j));
                     acc[r][j].x = fmaf(l[r], x4.x, acc[r][j].x);
                     acc[r][j].y = fmaf(l[r], x4.y, acc[r][j].y);
                     acc[r][j].z = fmaf(l[r], x4.z, acc[r][j].z);
@@ -646,7 +659,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
                 s_l[wave][r] = l[r];
             }
 #pragma unroll
-            for (int j = 0; j < VJ; ++j) s_acc[wave][r][j * 16 + ln] = acc[r][j];
+            for (int j = 0; j < VJ; ++j)
+                if (vin(j)) s_acc[wave][r][j * 16 + ln] = acc[r][j];
         }
     }
     __syncthreads();
@@ -703,6 +717,9 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(Problem p, int
 
     const int tid = threadIdx.x;
     const int e4 = tid % E4, grp = tid / E4;
+    // With E4 not dividing the workgroup (80- and 96-wide rows) the last
+    // threads form no whole group: they only keep the barrier.
+    const bool active = grp < kGroups;
     const int64_t th = blockIdx.x;  // t * H + h
     const float4* acc4 = reinterpret_cast<const float4*>(ws + th * nsplit * DV);
     const float2* ml2 = reinterpret_cast<const float2*>(ws + (int64_t)p.T * p.H * nsplit * DV + th * nsplit * 2);
@@ -712,7 +729,7 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(Problem p, int
     float2 mlp[kPre];
 #pragma unroll
     for (int u = 0; u < kPre; ++u) {
-        const int i = grp + u * kGroups;
+        const int i = active ? grp + u * kGroups : nsplit;
         pre[u] = i < nsplit ? acc4[(int64_t)i * E4 + e4] : zero4();
         mlp[u] = i < nsplit ? ml2[i] : make_float2(-INFINITY, 0.0f);
     }
@@ -720,7 +737,8 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(Problem p, int
     float mg = -INFINITY;
 #pragma unroll
     for (int u = 0; u < kPre; ++u) mg = fmaxf(mg, mlp[u].x);
-    for (int i = grp + kPre * kGroups; i < nsplit; i += kGroups) mg = fmaxf(mg, ml2[i].x);
+    const int i_rest = active ? grp + kPre * kGroups : nsplit;  // splits past the up-front loads
+    for (int i = i_rest; i < nsplit; i += kGroups) mg = fmaxf(mg, ml2[i].x);
     const float mu = mg == -INFINITY ? 0.0f : mg;
     float lg = 0.0f;
     float4 a = zero4();
@@ -732,7 +750,7 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(Problem p, int
         a.z = fmaf(pre[u].z, w, a.z); a.w = fmaf(pre[u].w, w, a.w);
     }
 #pragma unroll 4
-    for (int i = grp + kPre * kGroups; i < nsplit; i += kGroups) {
+    for (int i = i_rest; i < nsplit; i += kGroups) {
         const float2 mi = ml2[i];
         const float4 c = acc4[(int64_t)i * E4 + e4];
         const float w = fast_exp2(mi.x - mu);
@@ -740,8 +758,10 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(Problem p, int
         a.x = fmaf(c.x, w, a.x); a.y = fmaf(c.y, w, a.y);
         a.z = fmaf(c.z, w, a.z); a.w = fmaf(c.w, w, a.w);
     }
-    s_part[grp][e4] = a;
-    if (e4 == 0) s_ml[grp] = make_float2(mg, lg);
+    if (active) {
+        s_part[grp][e4] = a;
+        if (e4 == 0) s_ml[grp] = make_float2(mg, lg);
+    }
     __syncthreads();
     if (grp == 0) {
         float M = s_ml[0].x;
@@ -825,7 +845,7 @@ hipError_t launch_split_d(const Problem& p, const DecodePlan& plan, float* ws, c
 // (KJ+VJ) * (24 + 4 NQ) registers for the ring, q and acc, under 200.
 template <int D, int DV, int NQ>
 constexpr bool depth3_fits() {
-    return (D / 64 + DV / 64) * (24 + 4 * NQ) < 200;
+    return ((D + 63) / 64 + (DV + 63) / 64) * (24 + 4 * NQ) < 200;
 }
 
 template <int D, int DV, int NQ>
@@ -839,7 +859,7 @@ hipError_t launch_split_t(const Problem& p, const DecodePlan& plan, float* ws, c
 
 template <int D, int DV>
 hipError_t launch_split_nq(const Problem& p, const DecodePlan& plan, float* ws, const Launch& L) {
-    constexpr int KV = D / 64 + DV / 64;
+    constexpr int KV = (D + 63) / 64 + (DV + 63) / 64;
     switch (plan.nq) {
         case 1: return launch_split_t<D, DV, 1>(p, plan, ws, L);
         case 2: return launch_split_t<D, DV, 2>(p, plan, ws, L);
@@ -863,6 +883,7 @@ hipError_t launch_split_nq(const Problem& p, const DecodePlan& plan, float* ws, 
 // each holds in registers without spilling.
 static int decode_max_nq(int D, int Dv) {
     if (D == 64 && Dv == 64) return 8;
+    if ((D == 80 && Dv == 80) || (D == 96 && Dv == 96)) return 8;  // the 128-wide layout, partly empty
     if (D == 128 && Dv == 128) return 8;
     if (D == 192 && Dv == 128) return 4;
     if (D == 256 && Dv == 256) return 2;
@@ -874,6 +895,8 @@ bool decode_supported(int D, int Dv, int nq) { return nq >= 1 && nq <= decode_ma
 hipError_t launch_decode_split(const Problem& p, const DecodePlan& plan, float* ws, const Launch& L) {
     if (plan.splits < 1 || plan.splits > kMaxSplits) return hipErrorInvalidValue;
     if (p.D == 64 && p.Dv == 64) return launch_split_nq<64, 64>(p, plan, ws, L);
+    if (p.D == 80 && p.Dv == 80) return launch_split_nq<80, 80>(p, plan, ws, L);
+    if (p.D == 96 && p.Dv == 96) return launch_split_nq<96, 96>(p, plan, ws, L);
     if (p.D == 128 && p.Dv == 128) return launch_split_nq<128, 128>(p, plan, ws, L);
     if (p.D == 192 && p.Dv == 128) return launch_split_nq<192, 128>(p, plan, ws, L);
     if (p.D == 256 && p.Dv == 256) return launch_split_nq<256, 256>(p, plan, ws, L);
@@ -892,6 +915,8 @@ hipError_t launch_decode_combine(const Problem& p, const DecodePlan& plan, const
         const dim3 g((unsigned)((n + kThreads - 1) / kThreads)), b(kThreads);
         switch (p.Dv) {
             case 64: return launch_kernel(combine_few_kernel<64>, g, b, 0, L, p, plan.splits, ws);
+            case 80: return launch_kernel(combine_few_kernel<80>, g, b, 0, L, p, plan.splits, ws);
+            case 96: return launch_kernel(combine_few_kernel<96>, g, b, 0, L, p, plan.splits, ws);
             case 128: return launch_kernel(combine_few_kernel<128>, g, b, 0, L, p, plan.splits, ws);
             case 256: return launch_kernel(combine_few_kernel<256>, g, b, 0, L, p, plan.splits, ws);
             default: return hipErrorInvalidValue;
@@ -900,6 +925,8 @@ hipError_t launch_decode_combine(const Problem& p, const DecodePlan& plan, const
     const dim3 grid((unsigned)(p.T * p.H)), block(kThreads);
     switch (p.Dv) {
         case 64: return launch_kernel(decode_combine_kernel<64>, grid, block, 0, L, p, plan.splits, ws);
+        case 80: return launch_kernel(decode_combine_kernel<80>, grid, block, 0, L, p, plan.splits, ws);
+        case 96: return launch_kernel(decode_combine_kernel<96>, grid, block, 0, L, p, plan.splits, ws);
         case 128: return launch_kernel(decode_combine_kernel<128>, grid, block, 0, L, p, plan.splits, ws);
         case 256: return launch_kernel(decode_combine_kernel<256>, grid, block, 0, L, p, plan.splits, ws);
         default: return hipErrorInvalidValue;

@@ -1,0 +1,112 @@
+"""80- and 96-wide heads (Phi-2, StableLM-3B; Phi-3-mini, GPT-NeoX-20B) on the
+decode kernel, whose 16-lane row layout leaves part of the second float4 group
+of each row empty, against the oracle on the GPU."""
+
+import numpy as np
+import pytest
+
+import gqa_scaled_dot_amd as ga
+import workloads
+from tests.parity import compare, dev, run_library, torch
+from tests.test_gpu_append import _append
+from tests.test_gpu_relpos import _check_pb, _check_rkv, _pb
+
+pytestmark = pytest.mark.gpu
+
+WIDTHS = [80, 96]
+
+
+def _wl(D, **kw):
+    base = dict(name=f"D={D} decode", T=1, S=1000, heads=8, kvHeads=2, headDim=D, posOffset=999, seed=D)
+    base.update(kw)
+    return workloads.Workload(**base)
+
+
+def _check(w, what=None, expect_path="decode", out=None):
+    q, k, v, bias = w.tensors()
+    plan = ga.attn_plan(w.T, w.S, bias_kind={None: 0, "TS": 1, "HTS": 2}[w.bias], **w.params())
+    assert plan["path"] == expect_path, plan
+    return compare(q, k, v, bias, w.params(), what=what or w.name, out=out)
+
+
+@pytest.mark.parametrize("D", WIDTHS)
+@pytest.mark.parametrize("H, G, T", [(8, 2, 1), (16, 16, 1), (8, 4, 1), (4, 1, 1), (8, 8, 2), (6, 3, 1), (8, 8, 3),
+                                     (16, 2, 1), (32, 32, 1), (12, 4, 2)])
+def test_width_decode_shapes(D, H, G, T):
+    S = 777
+    _check(_wl(D, T=T, S=S, heads=H, kvHeads=G, posOffset=S - T, seed=D + H + T), what=f"D={D} H={H} G={G} T={T}")
+
+
+@pytest.mark.parametrize("D", WIDTHS)
+@pytest.mark.parametrize("feature", [
+    dict(window=100), dict(window=64, sinks=4), dict(softcap=5.0, std=3.0), dict(alibi=True),
+    dict(bias="TS", bias_mask_prob=0.1), dict(bias="HTS", bias_mask_prob=0.3), dict(causal=False),
+    dict(causal=False, window=50, posOffset=500),
+    dict(softcap=20.0, window=300, alibi=True, bias="HTS", bias_mask_prob=0.1, std=2.0),
+])
+def test_width_decode_features(D, feature):
+    _check(_wl(D, **feature), what=f"D={D} {feature}")
+
+
+@pytest.mark.parametrize("opt, val", [("decode_splits", 1), ("decode_splits", 5), ("decode_splits", 64),
+                                      ("decode_block", 64), ("decode_depth", 2), ("decode_depth", 3)])
+def test_width_decode_plan_options(opt, val):
+    w = _wl(80, S=6000, posOffset=5999, heads=16, kvHeads=4)
+    try:
+        ga.attn_set_option(opt, val)
+        _check(w, what=f"D=80 {opt}={val}")
+    finally:
+        ga.attn_set_option(opt, 0)
+
+
+@pytest.mark.parametrize("D", WIDTHS)
+def test_width_decode_never_reads_past_the_position(D):
+    # Rows past the query's position hold NaN: they must not reach the output.
+    w = _wl(D, S=2048, posOffset=1499)
+    q, k, v, _ = w.tensors()
+    kp, vp = k.copy(), v.copy()
+    kp[1500:] = np.nan
+    vp[1500:] = np.nan
+    got = run_library(q, kp, vp, None, w.params()).cpu().numpy()
+    want = run_library(q, k, v, None, w.params()).cpu().numpy()
+    np.testing.assert_array_equal(got, want)
+    assert np.isfinite(got).all()
+
+
+@pytest.mark.parametrize("D", WIDTHS)
+def test_width_decode_output_guard_bands_untouched(D):
+    # Each lane stores only the channels inside its row: the neighbours of
+    # the output stay as they were.
+    t = torch()
+    w = _wl(D, heads=16, kvHeads=4)
+    n, pad = w.T * 16 * D, 64
+    big = t.full((n + 2 * pad,), float("nan"), dtype=t.float32, device="cuda")
+    out = big[pad:pad + n].view(w.T, 16 * D)
+    _check(w, what=f"D={D} guarded out", out=out)
+    b = big.cpu().numpy()
+    assert np.isnan(b[:pad]).all() and np.isnan(b[-pad:]).all()
+
+
+@pytest.mark.parametrize("D", WIDTHS)
+@pytest.mark.parametrize("kw", [dict(T=1, S=3000, heads=32, kvHeads=8), dict(T=3, S=900, heads=4, kvHeads=2),
+                                dict(T=1, S=2049, heads=8, kvHeads=8, alibi=True, bias="TS", bias_mask_prob=0.1)])
+def test_width_fused_append(D, kw):
+    # The appended rows are read from their buffers and stored into the
+    # caches by the decode kernel itself: every cache bit is checked, and no
+    # lane may write past its row.
+    w = workloads.Workload(name=f"D={D} append", headDim=D, posOffset=kw["S"] - kw["T"], seed=D + kw["S"], **kw)
+    assert _append(w, w.T, w.posOffset, poison_past=w.posOffset + w.T) == 0
+
+
+@pytest.mark.parametrize("D", WIDTHS)
+@pytest.mark.parametrize("m", [0, 16, 200])
+def test_width_relative_kv_decode(D, m):
+    w = workloads.Workload("rkv decode", T=1, S=3000, heads=8, kvHeads=2, headDim=D, posOffset=2999, seed=D + m)
+    _check_rkv(w, m, True, ("decode", "generic"))
+
+
+@pytest.mark.parametrize("D", WIDTHS)
+def test_width_position_bias_decode(D):
+    w = workloads.Workload("pb decode", T=1, S=3000, heads=8, kvHeads=4, headDim=D, posOffset=2999, seed=D)
+    th, weight = _pb(8)
+    _check_pb(w, th, weight, False, ("decode", "generic"))
