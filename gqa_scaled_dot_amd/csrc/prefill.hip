@@ -77,10 +77,15 @@ __device__ __forceinline__ f32x16 mfma32(float a, float b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
-// NB consecutive floats from LDS (NB = 2 or a multiple of 4).
+// NB consecutive floats from LDS (NB = 2, 3 or a multiple of 4).
 template <int NB>
 __device__ __forceinline__ void lds_read(const float* src, float (&dst)[NB]) {
-    if constexpr (NB % 4 == 0) {
+    if constexpr (NB == 3) {
+        // 96-wide rows: three floats at a 12-byte stride, read one by one.
+        dst[0] = src[0];
+        dst[1] = src[1];
+        dst[2] = src[2];
+    } else if constexpr (NB % 4 == 0) {
 #pragma unroll
         for (int b = 0; b < NB; b += 4) {
             const float4 w = *reinterpret_cast<const float4*>(src + b);
@@ -90,7 +95,7 @@ __device__ __forceinline__ void lds_read(const float* src, float (&dst)[NB]) {
             dst[b + 3] = w.w;
         }
     } else {
-        static_assert(NB == 2, "vHeadDim must be 64 or a multiple of 128");
+        static_assert(NB == 2, "vHeadDim must be 64, 96 or a multiple of 128");
         const float2 w = *reinterpret_cast<const float2*>(src);
         dst[0] = w.x;
         dst[1] = w.y;
@@ -449,6 +454,9 @@ __global__ __launch_bounds__(kThreads, RM == 2 ? prefill_rel_waves(D, DV) : pref
             for (int b = 0; b < NB; b += 4)
                 *reinterpret_cast<float4*>(dst + NB * i + b) =
                     make_float4(o[b][r] * sc, o[b + 1][r] * sc, o[b + 2][r] * sc, o[b + 3][r] * sc);
+        } else if constexpr (NB == 3) {
+#pragma unroll
+            for (int b = 0; b < 3; ++b) dst[3 * i + b] = o[b][r] * sc;
         } else {
             *reinterpret_cast<float2*>(dst + NB * i) = make_float2(o[0][r] * sc, o[1][r] * sc);
         }
@@ -495,8 +503,8 @@ hipError_t launch_dims(const Problem& p, const Args& a, const Launch& L) {
 hipError_t launch_prefill16(const Problem& p, const pf::Args& a, const Launch& L);
 
 bool prefill_supported(int D, int Dv) {
-    return (D == 64 && Dv == 64) || (D == 128 && Dv == 128) || (D == 192 && Dv == 128) ||
-           (D == 256 && Dv == 256);
+    return (D == 64 && Dv == 64) || (D == 96 && Dv == 96) || (D == 128 && Dv == 128) ||
+           (D == 192 && Dv == 128) || (D == 256 && Dv == 256);
 }
 
 // Workgroups per CU the prefill kernels reach (registers and LDS).
@@ -527,6 +535,7 @@ hipError_t launch_prefill(const Problem& p, const PrefillPlan& plan, float* ws, 
     if (plan.variant == 16) return part == 0 ? launch_prefill16(p, a, L) : hipErrorInvalidValue;
     if (plan.variant != 32) return hipErrorInvalidValue;
     if (p.D == 64 && p.Dv == 64) return launch_dims<64, 64>(p, a, L);
+    if (p.D == 96 && p.Dv == 96) return launch_dims<96, 96>(p, a, L);
     if (p.D == 128 && p.Dv == 128) return launch_dims<128, 128>(p, a, L);
     if (p.D == 192 && p.Dv == 128) return launch_dims<192, 128>(p, a, L);
     if (p.D == 256 && p.Dv == 256) return launch_dims<256, 256>(p, a, L);

@@ -110,3 +110,62 @@ def test_width_position_bias_decode(D):
     w = workloads.Workload("pb decode", T=1, S=3000, heads=8, kvHeads=4, headDim=D, posOffset=2999, seed=D)
     th, weight = _pb(8)
     _check_pb(w, th, weight, False, ("decode", "generic"))
+
+
+# --------------------------------------------------------------------------
+# 96-wide heads on the 32x32x2 prefill kernel (three output floats per lane
+# and k-step); 80-wide heads take the generic kernel there.
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kw", [dict(T=300, S=300, heads=8, kvHeads=2, posOffset=0),
+                                dict(T=77, S=1077, heads=4, kvHeads=4, posOffset=1000),
+                                dict(T=130, S=130, heads=32, kvHeads=32, posOffset=0),
+                                dict(T=64, S=200, heads=16, kvHeads=1, posOffset=136),
+                                dict(T=1, S=700, heads=64, kvHeads=2, posOffset=699)])
+def test_width_96_prefill_shapes(kw):
+    w = _wl(96, name="D=96 prefill", **kw)
+    assert ga.attn_plan(w.T, w.S, **w.params())["variant"] == 32
+    _check(w, what=f"D=96 {kw}", expect_path="prefill")
+
+
+@pytest.mark.parametrize("feature", [
+    dict(window=100), dict(window=64, sinks=4), dict(softcap=5.0, std=3.0), dict(alibi=True),
+    dict(bias="TS", bias_mask_prob=0.1), dict(bias="HTS", bias_mask_prob=0.3), dict(causal=False),
+    dict(causal=False, window=50),
+])
+def test_width_96_prefill_features(feature):
+    w = _wl(96, name="D=96 prefill feature", T=200, S=260, heads=8, kvHeads=2, posOffset=60, **feature)
+    _check(w, what=f"D=96 {feature}", expect_path="prefill")
+
+
+@pytest.mark.parametrize("splits", [2, 5])
+def test_width_96_prefill_key_splits(splits):
+    w = _wl(96, name="D=96 chunked", T=100, S=2100, heads=8, kvHeads=2, posOffset=2000)
+    try:
+        ga.attn_set_option("prefill_splits", splits)
+        assert ga.attn_plan(w.T, w.S, **w.params())["splits"] == splits
+        _check(w, what=f"D=96 splits={splits}", expect_path="prefill")
+    finally:
+        ga.attn_set_option("prefill_splits", 0)
+
+
+@pytest.mark.parametrize("m", [0, 16, 200])
+@pytest.mark.parametrize("causal", [True, False])
+def test_width_96_relative_kv_prefill(m, causal):
+    w = workloads.Workload("D=96 rkv prefill", T=150, S=230 if causal else 200, heads=8, kvHeads=2, headDim=96,
+                           posOffset=80 if causal else 30, causal=causal, seed=96 + m)
+    _check_rkv(w, m, True, (None, "generic"), seed=m)
+
+
+def test_width_96_prefill_full_size_sampled():
+    # A Phi-3-mini-shaped causal prefill: 32 heads of 96 over 2048 rows.
+    from tests.parity import sample_rows
+    w = _wl(96, name="D=96 2048", T=2048, S=2048, heads=32, kvHeads=32, posOffset=0)
+    q, k, v, _ = w.tensors()
+    assert ga.attn_plan(w.T, w.S, **w.params())["path"] == "prefill"
+    compare(q, k, v, None, w.params(), rows=sample_rows(w.T, seed=96), what="D=96 2048 sampled")
+
+
+def test_width_80_prefill_takes_generic():
+    w = _wl(80, name="D=80 prefill", T=40, S=90, heads=4, kvHeads=2, posOffset=50)
+    _check(w, what="D=80 prefill on generic", expect_path="generic")
