@@ -111,13 +111,18 @@ constexpr int prefill_rel_waves(int D, int DV) { return D + DV <= 128 ? 2 : 1; }
 
 constexpr int kRelRows = 64;  // relative rows per band tile: d_lo .. d_lo + 63
 
+// Tile widths: the row widths rounded up to 32 floats (80-wide rows sit in
+// 96-wide tiles whose last 16 columns are zeros, and q's are zeros there too).
+constexpr int tile_width(int w) { return (w + 31) / 32 * 32; }
+
 template <int D, int DV>
 struct PrefillShape {
-    static constexpr int KLD = D + kPad;    // LDS row stride of a K tile
-    static constexpr int VLD = DV + kPad;   // LDS row stride of a V tile
-    static constexpr int KF4 = kBK * D / 4 / kThreads;   // float4 per thread per K tile
-    static constexpr int VF4 = kBK * DV / 4 / kThreads;  // float4 per thread per V tile
-    static constexpr int NB = DV / 32;      // output blocks (and V floats per lane per k-step)
+    static constexpr int DP = tile_width(D), DVP = tile_width(DV);
+    static constexpr int KLD = DP + kPad;   // LDS row stride of a K tile
+    static constexpr int VLD = DVP + kPad;  // LDS row stride of a V tile
+    static constexpr int KF4 = kBK * DP / 4 / kThreads;   // float4 per thread per K tile
+    static constexpr int VF4 = kBK * DVP / 4 / kThreads;  // float4 per thread per V tile
+    static constexpr int NB = DVP / 32;     // output blocks (and V floats per lane per k-step)
     static constexpr size_t lds_bytes = sizeof(float) * 2 * kBK * (size_t)(KLD + VLD);
     // REL instances: each wave's [32 queries][kRelRows] rows after the tiles.
     static constexpr size_t rel_lds_bytes = sizeof(float) * kWaves * kBQ * kRelRows;
@@ -133,7 +138,7 @@ __global__ __launch_bounds__(kThreads, RM == 2 ? prefill_rel_waves(D, DV) : pref
     constexpr bool REL = RM != 0;
     constexpr bool BAND = RM == 2;
     using Sh = PrefillShape<D, DV>;
-    constexpr int KLD = Sh::KLD, VLD = Sh::VLD, NB = Sh::NB;
+    constexpr int KLD = Sh::KLD, VLD = Sh::VLD, NB = Sh::NB, DP = Sh::DP, DVP = Sh::DVP;
     extern __shared__ float lds[];
     float* ktile = lds;                       // [2][kBK][KLD]
     float* vtile = lds + 2 * kBK * KLD;       // [2][kBK][VLD]
@@ -156,17 +161,22 @@ __global__ __launch_bounds__(kThreads, RM == 2 ? prefill_rel_waves(D, DV) : pref
     const bool trow = t < T;
     const int pos = p.ep.pos_offset + t;
 
-    // This lane's half of its query row: q[t, h*D + half*D/2 + kk], kk < D/2.
-    float qreg[D / 2];
+    // This lane's half of its query row: q[t, h*D + half*DP/2 + kk], kk < DP/2
+    // (zeros past D).
+    float qreg[DP / 2];
     {
         const int tc = min(t, T - 1);
         const float* qhead = p.q + (int64_t)tc * p.H * D + (int64_t)h * D;
 #pragma unroll
-        for (int kk = 0; kk < D / 2; kk += 4) {
+        for (int kk = 0; kk < DP / 2; kk += 4) {
+            const int c = half * (DP / 2) + kk;
+            const bool in = DP == D || c < D;
             // With a rotary embedding on q (rope.on is uniform), each channel is
             // turned as it is loaded.
-            const float4 v = p.rope.on ? rope_channels4(p.rope, qhead, half * (D / 2) + kk, p.rope.pos0 + tc)
-                                       : *reinterpret_cast<const float4*>(qhead + half * (D / 2) + kk);
+            float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            if (in)
+                v = p.rope.on ? rope_channels4(p.rope, qhead, c, p.rope.pos0 + tc)
+                              : *reinterpret_cast<const float4*>(qhead + c);
             qreg[kk] = trow ? v.x : 0.0f;
             qreg[kk + 1] = trow ? v.y : 0.0f;
             qreg[kk + 2] = trow ? v.z : 0.0f;
@@ -195,11 +205,12 @@ __global__ __launch_bounds__(kThreads, RM == 2 ? prefill_rel_waves(D, DV) : pref
     float* wrel = lds + 2 * kBK * (KLD + VLD) + wave * (kBQ * kRelRows) + col * kRelRows;
     float qrel0 = 0.0f, qrelN = 0.0f, wL = 0.0f, wR = 0.0f;
     if constexpr (REL) {
-        const float* r0 = p.ep.rel_k + half * (D / 2);
-        const float* rN = p.ep.rel_k + (int64_t)(2 * M) * D + half * (D / 2);
+        const float* r0 = p.ep.rel_k + half * (DP / 2);
+        const float* rN = p.ep.rel_k + (int64_t)(2 * M) * D + half * (DP / 2);
         float a0 = 0.0f, aN = 0.0f;
 #pragma unroll
-        for (int kk = 0; kk < D / 2; kk += 4) {
+        for (int kk = 0; kk < DP / 2; kk += 4) {
+            if (DP != D && half * (DP / 2) + kk >= D) continue;  // q is zero there
             const float4 x0 = *reinterpret_cast<const float4*>(r0 + kk);
             const float4 xN = *reinterpret_cast<const float4*>(rN + kk);
             a0 = fmaf(qreg[kk], x0.x, fmaf(qreg[kk + 1], x0.y, fmaf(qreg[kk + 2], x0.z, fmaf(qreg[kk + 3], x0.w, a0))));
@@ -235,10 +246,10 @@ __global__ __launch_bounds__(kThreads, RM == 2 ? prefill_rel_waves(D, DV) : pref
 
     const float qk_scale = p.ep.scale * kLog2e;
     if (v0 < v1) {
-        fetch_rows<D, kThreads>(kst, kg, kstride, tile_of(v0), rows);
-        fetch_rows<DV, kThreads>(vst, vg, vstride, tile_of(v0), rows);
-        stage_rows<D, kThreads>(kst, ktile);
-        stage_rows<DV, kThreads>(vst, vtile);
+        fetch_rows<D, kThreads, DP>(kst, kg, kstride, tile_of(v0), rows);
+        fetch_rows<DV, kThreads, DVP>(vst, vg, vstride, tile_of(v0), rows);
+        stage_rows<DP, kThreads>(kst, ktile);
+        stage_rows<DVP, kThreads>(vst, vtile);
     }
     for (int v = v0; v < v1; ++v) {
         const int kt = tile_of(v);
@@ -246,7 +257,7 @@ __global__ __launch_bounds__(kThreads, RM == 2 ? prefill_rel_waves(D, DV) : pref
         const bool more = v + 1 < v1;
         const int kt_next = tile_of(v + 1);
         __syncthreads();  // tile `kt` is in LDS; everyone is done with the other buffer
-        if (more) fetch_rows<D, kThreads>(kst, kg, kstride, kt_next, rows);
+        if (more) fetch_rows<D, kThreads, DP>(kst, kg, kstride, kt_next, rows);
 
         const int s_first = kt * kBK;
         bool any_vis, all_vis;
@@ -271,16 +282,16 @@ __global__ __launch_bounds__(kThreads, RM == 2 ? prefill_rel_waves(D, DV) : pref
             f32x16 sacc;
 #pragma unroll
             for (int r = 0; r < 16; ++r) sacc[r] = 0.0f;
-            const float* krow = kt_ + col * KLD + half * (D / 2);
+            const float* krow = kt_ + col * KLD + half * (DP / 2);
 #pragma unroll
-            for (int kk = 0; kk < D / 2; kk += 4) {
+            for (int kk = 0; kk < DP / 2; kk += 4) {
                 const float4 kv = *reinterpret_cast<const float4*>(krow + kk);
                 sacc = mfma32(kv.x, qreg[kk], sacc);
                 sacc = mfma32(kv.y, qreg[kk + 1], sacc);
                 sacc = mfma32(kv.z, qreg[kk + 2], sacc);
                 sacc = mfma32(kv.w, qreg[kk + 3], sacc);
                 // Keep the scheduler from hoisting every LDS read of the tile
-                // at once (it would need D/2 registers for them).
+                // at once (it would need DP/2 registers for them).
                 if (kk % 16 == 12) __builtin_amdgcn_sched_barrier(0);
             }
             if constexpr (REL) {
@@ -300,13 +311,15 @@ __global__ __launch_bounds__(kThreads, RM == 2 ? prefill_rel_waves(D, DV) : pref
 #pragma unroll
                     for (int ps = 0; ps < kRelRows / 32; ++ps) {
                         const int rr = min(max(d_lo + 32 * ps + col, -M), M) + M;
-                        const float* rk = p.ep.rel_k + (int64_t)rr * D + half * (D / 2);
+                        const float* rk = p.ep.rel_k + (int64_t)rr * D + half * (DP / 2);
                         f32x16 racc;
 #pragma unroll
                         for (int r = 0; r < 16; ++r) racc[r] = 0.0f;
 #pragma unroll
-                        for (int kk = 0; kk < D / 2; kk += 4) {
-                            const float4 kv = *reinterpret_cast<const float4*>(rk + kk);
+                        for (int kk = 0; kk < DP / 2; kk += 4) {
+                            const bool in = DP == D || half * (DP / 2) + kk < D;  // q is zero past D
+                            const float4 kv = in ? *reinterpret_cast<const float4*>(rk + kk)
+                                                 : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
                             racc = mfma32(kv.x, qreg[kk], racc);
                             racc = mfma32(kv.y, qreg[kk + 1], racc);
                             racc = mfma32(kv.z, qreg[kk + 2], racc);
@@ -335,7 +348,7 @@ __global__ __launch_bounds__(kThreads, RM == 2 ? prefill_rel_waves(D, DV) : pref
                 x[r] = xs;
             }
         }
-        if (more) stage_rows<D, kThreads>(kst, ktile + (buf ^ 1) * kBK * KLD);
+        if (more) stage_rows<DP, kThreads>(kst, ktile + (buf ^ 1) * kBK * KLD);
 
         if (any_vis) {
             // Online softmax for this lane's query (both halves share the max).
@@ -386,7 +399,7 @@ __global__ __launch_bounds__(kThreads, RM == 2 ? prefill_rel_waves(D, DV) : pref
                             float vv[NB];
                             const float* rv = p.ep.rel_v + (int64_t)rr * DV + NB * col;
 #pragma unroll
-                            for (int b = 0; b < NB; ++b) vv[b] = rv[b];
+                            for (int b = 0; b < NB; ++b) vv[b] = DVP == DV || NB * col + b < DV ? rv[b] : 0.0f;
                             const float pw = wrel[i];
 #pragma unroll
                             for (int b = 0; b < NB; ++b) o[b] = mfma32(vv[b], pw, o[b]);
@@ -395,7 +408,7 @@ __global__ __launch_bounds__(kThreads, RM == 2 ? prefill_rel_waves(D, DV) : pref
                 }
             }
         }
-        if (more) fetch_rows<DV, kThreads>(vst, vg, vstride, kt_next, rows);
+        if (more) fetch_rows<DV, kThreads, DVP>(vst, vg, vstride, kt_next, rows);
 
         if (any_vis) {
             // O^T += V^T P^T: k-step r uses keys f(r, half) and P from register r.
@@ -409,7 +422,7 @@ __global__ __launch_bounds__(kThreads, RM == 2 ? prefill_rel_waves(D, DV) : pref
                 if (NB * (r + 1) % 16 == 0) __builtin_amdgcn_sched_barrier(0);
             }
         }
-        if (more) stage_rows<DV, kThreads>(vst, vtile + (buf ^ 1) * kBK * VLD);
+        if (more) stage_rows<DVP, kThreads>(vst, vtile + (buf ^ 1) * kBK * VLD);
     }
 
     // Register r of block b is dv = NB*(8(r/4) + 4 half + r%4) + b.
@@ -424,7 +437,9 @@ __global__ __launch_bounds__(kThreads, RM == 2 ? prefill_rel_waves(D, DV) : pref
             for (int r = 0; r < 16; ++r) {
                 const int i = 8 * (r >> 2) + 4 * half + (r & 3);
 #pragma unroll
-                for (int b = 0; b < NB; ++b) o[b][r] = fmaf(wLt, v0[NB * i + b], fmaf(wRt, vN[NB * i + b], o[b][r]));
+                for (int b = 0; b < NB; ++b)
+                    if (DVP == DV || NB * i + b < DV)
+                        o[b][r] = fmaf(wLt, v0[NB * i + b], fmaf(wRt, vN[NB * i + b], o[b][r]));
             }
         }
     }
@@ -456,7 +471,8 @@ __global__ __launch_bounds__(kThreads, RM == 2 ? prefill_rel_waves(D, DV) : pref
                     make_float4(o[b][r] * sc, o[b + 1][r] * sc, o[b + 2][r] * sc, o[b + 3][r] * sc);
         } else if constexpr (NB == 3) {
 #pragma unroll
-            for (int b = 0; b < 3; ++b) dst[3 * i + b] = o[b][r] * sc;
+            for (int b = 0; b < 3; ++b)
+                if (DVP == DV || 3 * i + b < DV) dst[3 * i + b] = o[b][r] * sc;
         } else {
             *reinterpret_cast<float2*>(dst + NB * i) = make_float2(o[0][r] * sc, o[1][r] * sc);
         }
@@ -503,7 +519,7 @@ hipError_t launch_dims(const Problem& p, const Args& a, const Launch& L) {
 hipError_t launch_prefill16(const Problem& p, const pf::Args& a, const Launch& L);
 
 bool prefill_supported(int D, int Dv) {
-    return (D == 64 && Dv == 64) || (D == 96 && Dv == 96) || (D == 128 && Dv == 128) ||
+    return (D == 64 && Dv == 64) || (D == 80 && Dv == 80) || (D == 96 && Dv == 96) || (D == 128 && Dv == 128) ||
            (D == 192 && Dv == 128) || (D == 256 && Dv == 256);
 }
 
@@ -535,6 +551,7 @@ hipError_t launch_prefill(const Problem& p, const PrefillPlan& plan, float* ws, 
     if (plan.variant == 16) return part == 0 ? launch_prefill16(p, a, L) : hipErrorInvalidValue;
     if (plan.variant != 32) return hipErrorInvalidValue;
     if (p.D == 64 && p.Dv == 64) return launch_dims<64, 64>(p, a, L);
+    if (p.D == 80 && p.Dv == 80) return launch_dims<80, 80>(p, a, L);
     if (p.D == 96 && p.Dv == 96) return launch_dims<96, 96>(p, a, L);
     if (p.D == 128 && p.Dv == 128) return launch_dims<128, 128>(p, a, L);
     if (p.D == 192 && p.Dv == 128) return launch_dims<192, 128>(p, a, L);

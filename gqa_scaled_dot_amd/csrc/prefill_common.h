@@ -165,32 +165,36 @@ __device__ __forceinline__ void tile_visibility(const Epilogue& e, int s_first, 
 // read a clamped, in-bounds row instead and are replaced by zeros, so the
 // loads need no branches. stride <= 65536 heads x 256 floats, so an offset
 // inside a tile (< kBK * stride * 4 bytes = 2^31) fits in 32 bits.
-template <int W, int NT>
-__device__ __forceinline__ void fetch_rows(float4 (&st)[kBK * W / 4 / NT], const float* base,
+// The tile may be wider than the rows (WP >= W floats per LDS row, 80-wide
+// rows in a 96-wide tile): columns past W are zeros and never read from
+// memory.
+template <int W, int NT, int WP = W>
+__device__ __forceinline__ void fetch_rows(float4 (&st)[kBK * WP / 4 / NT], const float* base,
                                            int64_t stride, int kt, const KeyRows& rows) {
     const int s0 = kt * kBK;
     const bool whole = ((s0 >= rows.klo) & (s0 + kBK <= rows.khi)) | (s0 + kBK <= rows.sink_hi);
     if (whole) {
         const char* tb = reinterpret_cast<const char*>(base + (int64_t)s0 * stride);
 #pragma unroll
-        for (int j = 0; j < kBK * W / 4 / NT; ++j) {
+        for (int j = 0; j < kBK * WP / 4 / NT; ++j) {
             const int f = (int)threadIdx.x + j * NT;
-            const uint32_t row = (uint32_t)(f / (W / 4)), c4 = (uint32_t)(f % (W / 4));
+            const uint32_t row = (uint32_t)(f / (WP / 4)), c4 = (uint32_t)(f % (WP / 4));
             const uint32_t off = (row * (uint32_t)stride + 4u * c4) * 4u;
-            st[j] = *reinterpret_cast<const float4*>(tb + off);
+            if (WP == W || c4 < (uint32_t)(W / 4)) st[j] = *reinterpret_cast<const float4*>(tb + off);
+            else st[j] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         }
         return;
     }
 #pragma unroll
-    for (int j = 0; j < kBK * W / 4 / NT; ++j) {
+    for (int j = 0; j < kBK * WP / 4 / NT; ++j) {
         const int f = (int)threadIdx.x + j * NT;
-        const int row = f / (W / 4), c4 = f % (W / 4);
+        const int row = f / (WP / 4), c4 = f % (WP / 4);
         const int s = s0 + row;
-        const bool ok = rows.loaded(s);
+        const bool ok = rows.loaded(s) && (WP == W || c4 < W / 4);
         // The nearest row of [klo, khi) (khi - 1 when that range is empty):
         // usually a cache line the neighbouring loads touch anyway.
-        const int sc = ok ? s : min(max(s, rows.klo), rows.khi - 1);
-        const float4 x = *reinterpret_cast<const float4*>(base + sc * stride + 4 * c4);
+        const int sc = rows.loaded(s) ? s : min(max(s, rows.klo), rows.khi - 1);
+        const float4 x = *reinterpret_cast<const float4*>(base + sc * stride + 4 * min(c4, W / 4 - 1));
         st[j].x = ok ? x.x : 0.0f;
         st[j].y = ok ? x.y : 0.0f;
         st[j].z = ok ? x.z : 0.0f;

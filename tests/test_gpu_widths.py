@@ -113,59 +113,88 @@ def test_width_position_bias_decode(D):
 
 
 # --------------------------------------------------------------------------
-# 96-wide heads on the 32x32x2 prefill kernel (three output floats per lane
-# and k-step); 80-wide heads take the generic kernel there.
+# 80- and 96-wide heads on the 32x32x2 prefill kernel: 96-wide tiles (80-wide
+# rows padded with zero columns), three output floats per lane and k-step.
 # --------------------------------------------------------------------------
 
+@pytest.mark.parametrize("D", WIDTHS)
 @pytest.mark.parametrize("kw", [dict(T=300, S=300, heads=8, kvHeads=2, posOffset=0),
                                 dict(T=77, S=1077, heads=4, kvHeads=4, posOffset=1000),
                                 dict(T=130, S=130, heads=32, kvHeads=32, posOffset=0),
                                 dict(T=64, S=200, heads=16, kvHeads=1, posOffset=136),
                                 dict(T=1, S=700, heads=64, kvHeads=2, posOffset=699)])
-def test_width_96_prefill_shapes(kw):
-    w = _wl(96, name="D=96 prefill", **kw)
+def test_width_prefill_shapes(D, kw):
+    w = _wl(D, name=f"D={D} prefill", **kw)
     assert ga.attn_plan(w.T, w.S, **w.params())["variant"] == 32
-    _check(w, what=f"D=96 {kw}", expect_path="prefill")
+    _check(w, what=f"D={D} {kw}", expect_path="prefill")
 
 
+@pytest.mark.parametrize("D", WIDTHS)
 @pytest.mark.parametrize("feature", [
     dict(window=100), dict(window=64, sinks=4), dict(softcap=5.0, std=3.0), dict(alibi=True),
     dict(bias="TS", bias_mask_prob=0.1), dict(bias="HTS", bias_mask_prob=0.3), dict(causal=False),
     dict(causal=False, window=50),
 ])
-def test_width_96_prefill_features(feature):
-    w = _wl(96, name="D=96 prefill feature", T=200, S=260, heads=8, kvHeads=2, posOffset=60, **feature)
-    _check(w, what=f"D=96 {feature}", expect_path="prefill")
+def test_width_prefill_features(D, feature):
+    w = _wl(D, name=f"D={D} prefill feature", T=200, S=260, heads=8, kvHeads=2, posOffset=60, **feature)
+    _check(w, what=f"D={D} {feature}", expect_path="prefill")
 
 
+@pytest.mark.parametrize("D", WIDTHS)
 @pytest.mark.parametrize("splits", [2, 5])
-def test_width_96_prefill_key_splits(splits):
-    w = _wl(96, name="D=96 chunked", T=100, S=2100, heads=8, kvHeads=2, posOffset=2000)
+def test_width_prefill_key_splits(D, splits):
+    w = _wl(D, name=f"D={D} chunked", T=100, S=2100, heads=8, kvHeads=2, posOffset=2000)
     try:
         ga.attn_set_option("prefill_splits", splits)
         assert ga.attn_plan(w.T, w.S, **w.params())["splits"] == splits
-        _check(w, what=f"D=96 splits={splits}", expect_path="prefill")
+        _check(w, what=f"D={D} splits={splits}", expect_path="prefill")
     finally:
         ga.attn_set_option("prefill_splits", 0)
 
 
+@pytest.mark.parametrize("D", WIDTHS)
+def test_width_prefill_output_guard_bands_untouched(D):
+    # Lanes whose columns lie past the row (the padding of 80-wide rows) store
+    # nothing: the neighbours of the output stay as they were.
+    t = torch()
+    w = _wl(D, name=f"D={D} prefill guarded", T=96, S=96, heads=4, kvHeads=2, posOffset=0)
+    n, pad = w.T * 4 * D, 64
+    big = t.full((n + 2 * pad,), float("nan"), dtype=t.float32, device="cuda")
+    out = big[pad:pad + n].view(w.T, 4 * D)
+    _check(w, what=f"D={D} prefill guarded out", expect_path="prefill", out=out)
+    b = big.cpu().numpy()
+    assert np.isnan(b[:pad]).all() and np.isnan(b[-pad:]).all()
+
+
+@pytest.mark.parametrize("D", WIDTHS)
+def test_width_prefill_with_rotary_q(D):
+    # q turned as it is loaded (half-split pairs over the whole width).
+    import oracle
+    from tests.parity import assert_close
+    w = _wl(D, name=f"D={D} rope prefill", T=150, S=150, heads=8, kvHeads=2, posOffset=0)
+    q, k, v, _ = w.tensors()
+    qr = dict(base=10000.0)
+    roped = oracle.rope(q, headDim=D, offset=0, **qr).astype(np.float32)
+    ref = oracle.attention(roped, k, v, None, **w.params())
+    out = ga.attn_forward(dev(q), dev(k), dev(v), **w.params(), q_rope=dict(qr))
+    torch().cuda.synchronize()
+    assert_close(out.cpu().numpy(), ref, f"D={D} rope prefill")
+
+
+@pytest.mark.parametrize("D", WIDTHS)
 @pytest.mark.parametrize("m", [0, 16, 200])
 @pytest.mark.parametrize("causal", [True, False])
-def test_width_96_relative_kv_prefill(m, causal):
-    w = workloads.Workload("D=96 rkv prefill", T=150, S=230 if causal else 200, heads=8, kvHeads=2, headDim=96,
-                           posOffset=80 if causal else 30, causal=causal, seed=96 + m)
+def test_width_relative_kv_prefill(D, m, causal):
+    w = workloads.Workload(f"D={D} rkv prefill", T=150, S=230 if causal else 200, heads=8, kvHeads=2, headDim=D,
+                           posOffset=80 if causal else 30, causal=causal, seed=D + m)
     _check_rkv(w, m, True, (None, "generic"), seed=m)
 
 
-def test_width_96_prefill_full_size_sampled():
-    # A Phi-3-mini-shaped causal prefill: 32 heads of 96 over 2048 rows.
+@pytest.mark.parametrize("D", WIDTHS)
+def test_width_prefill_full_size_sampled(D):
+    # A Phi-shaped causal prefill: 32 heads over 2048 rows.
     from tests.parity import sample_rows
-    w = _wl(96, name="D=96 2048", T=2048, S=2048, heads=32, kvHeads=32, posOffset=0)
+    w = _wl(D, name=f"D={D} 2048", T=2048, S=2048, heads=32, kvHeads=32, posOffset=0)
     q, k, v, _ = w.tensors()
     assert ga.attn_plan(w.T, w.S, **w.params())["path"] == "prefill"
-    compare(q, k, v, None, w.params(), rows=sample_rows(w.T, seed=96), what="D=96 2048 sampled")
-
-
-def test_width_80_prefill_takes_generic():
-    w = _wl(80, name="D=80 prefill", T=40, S=90, heads=4, kvHeads=2, posOffset=50)
-    _check(w, what="D=80 prefill on generic", expect_path="generic")
+    compare(q, k, v, None, w.params(), rows=sample_rows(w.T, seed=D), what=f"D={D} 2048 sampled")
