@@ -198,3 +198,37 @@ def test_width_prefill_full_size_sampled(D):
     q, k, v, _ = w.tensors()
     assert ga.attn_plan(w.T, w.S, **w.params())["path"] == "prefill"
     compare(q, k, v, None, w.params(), rows=sample_rows(w.T, seed=D), what=f"D={D} 2048 sampled")
+
+
+@pytest.mark.parametrize("D", WIDTHS)
+def test_width_prefill_key_splits_many_rows(D):
+    # Many output rows and few key-range parts: the merge takes one thread per
+    # output float4 (combine_few) at these widths.
+    from tests.parity import sample_rows
+    w = _wl(D, name=f"D={D} split many rows", T=1024, S=3072, heads=32, kvHeads=8, posOffset=2048)
+    q, k, v, _ = w.tensors()
+    try:
+        ga.attn_set_option("prefill_splits", 3)
+        assert ga.attn_plan(w.T, w.S, **w.params())["splits"] == 3
+        compare(q, k, v, None, w.params(), rows=sample_rows(w.T, seed=D + 1), what=f"D={D} combine_few")
+    finally:
+        ga.attn_set_option("prefill_splits", 0)
+
+
+@pytest.mark.parametrize("D", WIDTHS)
+def test_width_fused_append_with_rotary_q(D):
+    # The decode kernel turns q through LDS: lanes past the row's width take zeros.
+    import oracle
+    from tests.parity import assert_close
+    w = _wl(D, name=f"D={D} rope decode", S=640, posOffset=639, heads=8, kvHeads=2)
+    qr = dict(base=10000.0)
+    q, k, v, _ = w.tensors()
+    roped = oracle.rope(q, headDim=D, offset=w.posOffset, **qr).astype(np.float32)
+    ref = oracle.attention(roped, k, v, None, **w.params())
+    kc, vc = dev(k), dev(v)
+    kc[-1] = float("nan")
+    vc[-1] = float("nan")
+    out = ga.attn_forward_append(dev(q), kc, vc, dev(k[-1:]), dev(v[-1:]), w.S - 1, q_rope=dict(qr), **w.params())
+    torch().cuda.synchronize()
+    assert_close(out.cpu().numpy(), ref, f"D={D} rotary q decode")
+    np.testing.assert_array_equal(kc.cpu().numpy().view(np.uint32), k.view(np.uint32))
