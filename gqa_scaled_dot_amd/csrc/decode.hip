@@ -733,30 +733,50 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(Problem p, int
         pre[u] = i < nsplit ? acc4[(int64_t)i * E4 + e4] : zero4();
         mlp[u] = i < nsplit ? ml2[i] : make_float2(-INFINITY, 0.0f);
     }
-    // The group's maximum, then its sum and accumulator against it.
+    // The group's maximum, then its sum and accumulator against it; splits
+    // past the up-front loads come in chunks of kChunk per group (all their
+    // loads in flight at once), merged into the running state as they arrive.
     float mg = -INFINITY;
 #pragma unroll
     for (int u = 0; u < kPre; ++u) mg = fmaxf(mg, mlp[u].x);
-    const int i_rest = active ? grp + kPre * kGroups : nsplit;  // splits past the up-front loads
-    for (int i = i_rest; i < nsplit; i += kGroups) mg = fmaxf(mg, ml2[i].x);
-    const float mu = mg == -INFINITY ? 0.0f : mg;
     float lg = 0.0f;
     float4 a = zero4();
+    {
+        const float mu = mg == -INFINITY ? 0.0f : mg;
 #pragma unroll
-    for (int u = 0; u < kPre; ++u) {
-        const float w = fast_exp2(mlp[u].x - mu);
-        lg = fmaf(mlp[u].y, w, lg);
-        a.x = fmaf(pre[u].x, w, a.x); a.y = fmaf(pre[u].y, w, a.y);
-        a.z = fmaf(pre[u].z, w, a.z); a.w = fmaf(pre[u].w, w, a.w);
+        for (int u = 0; u < kPre; ++u) {
+            const float w = fast_exp2(mlp[u].x - mu);
+            lg = fmaf(mlp[u].y, w, lg);
+            a.x = fmaf(pre[u].x, w, a.x); a.y = fmaf(pre[u].y, w, a.y);
+            a.z = fmaf(pre[u].z, w, a.z); a.w = fmaf(pre[u].w, w, a.w);
+        }
     }
-#pragma unroll 4
-    for (int i = i_rest; i < nsplit; i += kGroups) {
-        const float2 mi = ml2[i];
-        const float4 c = acc4[(int64_t)i * E4 + e4];
-        const float w = fast_exp2(mi.x - mu);
-        lg = fmaf(mi.y, w, lg);
-        a.x = fmaf(c.x, w, a.x); a.y = fmaf(c.y, w, a.y);
-        a.z = fmaf(c.z, w, a.z); a.w = fmaf(c.w, w, a.w);
+    constexpr int kChunk = 16;
+    const int i_rest = active ? grp + kPre * kGroups : nsplit;  // splits past the up-front loads
+    for (int i0 = i_rest; i0 < nsplit; i0 += kChunk * kGroups) {
+        float2 mc[kChunk];
+        float4 cc[kChunk];
+#pragma unroll
+        for (int u = 0; u < kChunk; ++u) {
+            const int i = i0 + u * kGroups;
+            mc[u] = i < nsplit ? ml2[i] : make_float2(-INFINITY, 0.0f);
+            cc[u] = i < nsplit ? acc4[(int64_t)i * E4 + e4] : zero4();
+        }
+        float mx = mg;
+#pragma unroll
+        for (int u = 0; u < kChunk; ++u) mx = fmaxf(mx, mc[u].x);
+        const float mu = mx == -INFINITY ? 0.0f : mx;
+        const float r = fast_exp2(mg - mu);  // 0 while nothing is merged yet
+        lg *= r;
+        a.x *= r; a.y *= r; a.z *= r; a.w *= r;
+#pragma unroll
+        for (int u = 0; u < kChunk; ++u) {
+            const float w = fast_exp2(mc[u].x - mu);
+            lg = fmaf(mc[u].y, w, lg);
+            a.x = fmaf(cc[u].x, w, a.x); a.y = fmaf(cc[u].y, w, a.y);
+            a.z = fmaf(cc[u].z, w, a.z); a.w = fmaf(cc[u].w, w, a.w);
+        }
+        mg = mx;
     }
     if (active) {
         s_part[grp][e4] = a;
