@@ -135,6 +135,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
         hh[r] = g * hpg + (live[r] ? r % hpg : 0);
         pos[r] = p.ep.pos_offset + tt[r];
     }
+    float slope[NQ];
+#pragma unroll
+    for (int r = 0; r < NQ; ++r) slope[r] = alibi_slope(p.ep, hh[r]);
     // With a rotary embedding, the raw q channels this thread turns, their pair
     // partners and frequencies are fetched first, ahead of the K/V loads.
     constexpr int QE = (NQ * D + kThreads - 1) / kThreads;
@@ -325,7 +328,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
                     else if (rel) dot += s_qrel[r * nrel + rel_row(p.ep, pos[r], s)];
                 }
                 if constexpr (EPI) {
-                    x[r][u] = score_epilogue(dot, p.ep, hh[r], pos[r], s, bf[r][u]) * kLog2e;
+                    x[r][u] = score_epilogue(dot, p.ep, slope[r], pos[r], s, bf[r][u]) * kLog2e;
                 } else {
                     x[r][u] = dot;  // q carries scale * log2(e)
                 }
@@ -552,7 +555,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
                         if (p.ep.bias_kind == ATTN_BIAS_TS) b = p.bias[(int64_t)tt[r] * p.S + s];
                         else if (p.ep.bias_kind == ATTN_BIAS_HTS) b = p.bias[((int64_t)hh[r] * p.T + tt[r]) * p.S + s];
                         if (pb) b += position_bias_tab(p.ep, s_pbb, hh[r], pos[r], s);
-                        float xs = score_epilogue(dot, p.ep, hh[r], pos[r], s, b) * kLog2e;
+                        float xs = score_epilogue(dot, p.ep, slope[r], pos[r], s, b) * kLog2e;
                         xs = (live[r] & key_visible(p.ep, pos[r], s)) ? xs : -INFINITY;
                         if (xs > m[r] + kLazy) {
                             const float alpha = fast_exp2(m[r] - xs);

@@ -104,6 +104,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(Problem p, Dec
         hh[b] = g * hpg + (live[b] ? r % hpg : 0);
         pos[b] = p.ep.pos_offset + tt[b];
     }
+    float slope[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) slope[b] = alibi_slope(p.ep, hh[b]);
 
     // The split's keys, walked in tiles of 16 rows (decode_split's walk, in
     // tile units): a chunk (possibly from a rotated start), interleaved
@@ -263,7 +266,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(Problem p, Dec
             for (int i = 0; i < 4; ++i) {
                 const int s = s0 + 4 * kg + i;
                 float v = sc[b][i];
-                if constexpr (EPI) v = score_epilogue(v, p.ep, hh[b], pos[b], s, bf[b][i]) * kLog2e;
+                if constexpr (EPI) v = score_epilogue(v, p.ep, slope[b], pos[b], s, bf[b][i]) * kLog2e;
                 if (check) {
                     const bool vis = live[b] & (s < k1) & key_visible(p.ep, pos[b], s);
                     if (!vis) v = -INFINITY;

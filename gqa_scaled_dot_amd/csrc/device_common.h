@@ -73,17 +73,62 @@ __device__ __forceinline__ float position_bias_tab(const Epilogue& e, const uint
     return e.pb_weight[b * e.pb_heads + h];
 }
 
+// tanh without branches or library calls. Below |x| = 1/4 its Taylor
+// series through x^9 (truncation error under 1e-8 relative there); above,
+// the identity tanh|x| = (1 - e^(-2|x|)) / (1 + e^(-2|x|)) with the hardware
+// exp2 and reciprocal, where 1 - e^(-2|x|) > 0.39 loses no accuracy to
+// cancellation; then the sign of x. A few ulp from the true value
+// everywhere, saturating to +-1 for large |x|; NaN stays NaN.
+__device__ __forceinline__ float fast_tanh(float x) {
+    const float a = fabsf(x);
+    const float z = x * x;
+    const float series =
+        fmaf(x * z, fmaf(z, fmaf(z, fmaf(z, 62.0f / 2835.0f, -17.0f / 315.0f), 2.0f / 15.0f), -1.0f / 3.0f), x);
+    const float t = __builtin_amdgcn_exp2f(-2.0f * kLog2e * a);
+    const float big = copysignf((1.0f - t) * __builtin_amdgcn_rcpf(1.0f + t), x);
+    return a < 0.25f ? series : big;
+}
+
+// The ALiBi slope of head h (0 without ALiBi). Kernels read it once per query
+// row, ahead of their key loops: the slope table sits in the kernel's argument
+// block, and an index that the compiler cannot prove uniform turns each read
+// into a vector memory load, which inside a key loop also makes the wave wait
+// for every load issued before it.
+__device__ __forceinline__ float alibi_slope(const Epilogue& e, int h) { return e.has_alibi ? e.slopes[h] : 0.0f; }
+
 // The score of one visible (query, key) pair, in the order the op fixes:
 // scale the dot product, softcap it (feature attention.softcap puts the cap
-// ahead of masking), then add the ALiBi penalty -slope*|pos - s| and the bias entry
-// (the bias input plus the bucketed position bias, fetched ahead by the
-// caller).
-__device__ __forceinline__ float score_epilogue(float dot, const Epilogue& e, int h, int pos, int s,
+// ahead of masking), then add the ALiBi penalty -slope*|pos - s| (slope:
+// alibi_slope of the row's head) and the bias entry (the bias input plus the
+// bucketed position bias, fetched ahead by the caller).
+__device__ __forceinline__ float score_epilogue(float dot, const Epilogue& e, float slope, int pos, int s,
                                                 float bias) {
     float x = dot * e.scale;
-    if (e.softcap > 0.0f) x = e.softcap * tanhf(x * e.inv_softcap);
-    if (e.has_alibi) x -= e.slopes[h] * (float)abs(pos - s);
+    if (e.softcap > 0.0f) x = e.softcap * fast_tanh(x * e.inv_softcap);
+    if (e.has_alibi) x -= slope * (float)abs(pos - s);
     return x + bias;
+}
+
+// score_epilogue for N scores of one query row at once (key of score i:
+// s[i]), times log2(e) (the base-2 domain): the same operations per score in
+// the same order, with each term's test (the same for the whole wave) taken
+// once for all N, so that their independent computations interleave instead
+// of running one score at a time between branches.
+template <int N>
+__device__ __forceinline__ void score_epilogue_n(float (&x)[N], const Epilogue& e, float slope, int pos,
+                                                 const int (&s)[N], const float (&bias)[N]) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] *= e.scale;
+    if (e.softcap > 0.0f) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) x[i] = e.softcap * fast_tanh(x[i] * e.inv_softcap);
+    }
+    if (e.has_alibi) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) x[i] -= slope * (float)abs(pos - s[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] = (x[i] + bias[i]) * kLog2e;
 }
 
 // 2^x with the hardware exponential (v_exp_f32; about 1 ulp). Inputs here are

@@ -32,7 +32,7 @@ __device__ float block_reduce(float x, float* red, bool is_max) {
 // qrel: the row's products with the relative key embeddings (q . rel_k[j]),
 // or NULL without them.
 __device__ __forceinline__ float score_at(const Problem& p, const float* qrow, const float* qrel, int h,
-                                          int g, int64_t t, int pos, int s) {
+                                          float slope, int g, int64_t t, int pos, int s) {
     const float* krow = p.k + s * (int64_t)p.G * p.D + (int64_t)g * p.D;
     float dot = 0.0f;
     for (int d = 0; d < p.D; ++d) dot = fmaf(qrow[d], krow[d], dot);
@@ -41,7 +41,7 @@ __device__ __forceinline__ float score_at(const Problem& p, const float* qrow, c
     if (p.ep.bias_kind == ATTN_BIAS_TS) b = p.bias[t * p.S + s];
     else if (p.ep.bias_kind == ATTN_BIAS_HTS) b = p.bias[((int64_t)h * p.T + t) * p.S + s];
     if (p.ep.pb_weight) b += position_bias(p.ep, h, pos, s);
-    return score_epilogue(dot, p.ep, h, pos, s, b);
+    return score_epilogue(dot, p.ep, slope, pos, s, b);
 }
 
 __global__ __launch_bounds__(kThreads) void generic_kernel(Problem p) {
@@ -56,6 +56,7 @@ __global__ __launch_bounds__(kThreads) void generic_kernel(Problem p) {
     const int h = blockIdx.y;
     const int g = (int)(((int64_t)h * p.G) / p.H);
     const int pos = p.ep.pos_offset + (int)t;
+    const float slope = alibi_slope(p.ep, h);
     const int tid = threadIdx.x;
 
     const float* qhead = p.q + t * (int64_t)p.H * p.D + (int64_t)h * p.D;
@@ -75,7 +76,7 @@ __global__ __launch_bounds__(kThreads) void generic_kernel(Problem p) {
 
     float m = -INFINITY;
     for (int s = tid; s < p.S; s += kThreads)
-        if (key_visible(p.ep, pos, s)) m = fmaxf(m, score_at(p, qrow, qr, h, g, t, pos, s));
+        if (key_visible(p.ep, pos, s)) m = fmaxf(m, score_at(p, qrow, qr, h, slope, g, t, pos, s));
     m = block_reduce(m, red, true);
 
     float* orow = p.out + t * (int64_t)p.H * p.Dv + (int64_t)h * p.Dv;
@@ -89,7 +90,7 @@ __global__ __launch_bounds__(kThreads) void generic_kernel(Problem p) {
         const int s = s0 + tid;
         float wt = 0.0f;
         if (s < p.S && key_visible(p.ep, pos, s))
-            wt = exp2f((score_at(p, qrow, qr, h, g, t, pos, s) - m) * kLog2e);
+            wt = exp2f((score_at(p, qrow, qr, h, slope, g, t, pos, s) - m) * kLog2e);
         l += wt;
         __syncthreads();
         w[tid] = wt;

@@ -245,6 +245,8 @@ __global__ __launch_bounds__(kThreads, RM == 2 ? prefill_rel_waves(D, DV) : pref
     float4 kst[Sh::KF4], vst[Sh::VF4];
 
     const float qk_scale = p.ep.scale * kLog2e;
+    const float slope = alibi_slope(p.ep, h);
+    const bool vec_bias = bias_vec4(p);
     if (v0 < v1) {
         fetch_rows<D, kThreads, DP>(kst, kg, kstride, tile_of(v0), rows);
         fetch_rows<DV, kThreads, DVP>(vst, vg, vstride, tile_of(v0), rows);
@@ -272,12 +274,8 @@ __global__ __launch_bounds__(kThreads, RM == 2 ? prefill_rel_waves(D, DV) : pref
         if (any_vis) {
             // Bias entries of the tile, requested before the matrix work so
             // that it hides their latency.
-            float bpre[EPI ? 16 : 1];
-            if constexpr (EPI) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    bpre[r] = bias_at(p, h, t, s_first + 8 * (r >> 2) + 4 * half + (r & 3));
-            }
+            float bpre[EPI ? 4 : 1][4];
+            if constexpr (EPI) bias_quads<4>(p, vec_bias, h, t, s_first + 4 * half, 8, bpre);
             // S^T = K Q^T for 32 keys x 32 queries.
             f32x16 sacc;
 #pragma unroll
@@ -335,17 +333,30 @@ __global__ __launch_bounds__(kThreads, RM == 2 ? prefill_rel_waves(D, DV) : pref
                 }
             }
 
-            // Score epilogue and mask; keys of register r: f(r, half).
+            // Score epilogue, then the mask; keys of register r: f(r, half).
+            int sk[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int s = s_first + 8 * (r >> 2) + 4 * half + (r & 3);
-                float xs = score2<EPI>(p, sacc[r], qk_scale, h, pos, s, bpre[EPI ? r : 0]);
-                if (!all_vis) {
+                sk[r] = s_first + 8 * (r >> 2) + 4 * half + (r & 3);
+                x[r] = sacc[r];
+            }
+            if constexpr (EPI) {
+                float bb[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) bb[r] = bpre[r >> 2][r & 3];
+                score_epilogue_n<16>(x, p.ep, slope, pos, sk, bb);
+            } else {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) x[r] *= qk_scale;
+            }
+            if (!all_vis) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int s = sk[r];
                     bool vis = (s < rows.khi) & window_visible(p.ep, pos, s);
                     if (sink_tile) vis = vis | ((s < rows.khi) & sink_visible(p.ep, pos, s));
-                    xs = vis ? xs : -INFINITY;
+                    x[r] = vis ? x[r] : -INFINITY;
                 }
-                x[r] = xs;
             }
         }
         if (more) stage_rows<DP, kThreads>(kst, ktile + (buf ^ 1) * kBK * KLD);

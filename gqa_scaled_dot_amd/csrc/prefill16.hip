@@ -114,6 +114,8 @@ __global__ __launch_bounds__(kThreads16, 1) void prefill16_kernel(Problem p, Arg
     const float* vg = p.v + (int64_t)c.g * DV;
     float4 kst[Sh::KF4], vst[Sh::VF4];
     const float qk_scale = p.ep.scale * kLog2e;
+    const float slope = alibi_slope(p.ep, h);
+    const bool vec_bias = bias_vec4(p);
 
     if (v0 < v1) {
         fetch_rows<D, kThreads16>(kst, kg, kstride, span.tile(v0), rows);
@@ -142,13 +144,12 @@ __global__ __launch_bounds__(kThreads16, 1) void prefill16_kernel(Problem p, Arg
             // Bias entries of the tile, requested before the matrix work so
             // that it hides their latency.
             float bpre[2][EPI ? 4 : 1];
-            if constexpr (EPI) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        bpre[kb][r] = bias_at(p, h, t, s_first + kb * 16 + 4 * quad + r);
-            }
+            if constexpr (EPI) bias_quads<2>(p, vec_bias, h, t, s_first + 4 * quad, 16, bpre);
+            // Scores of both 16-key blocks, then the epilogue over the 8 scores
+            // of the lane, then the mask. Score 4 kb + r: key s_first + 16 kb +
+            // 4 quad + r.
+            float xe[8];
+            int sk[8];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
                 f32x4v sacc = f32x4v{0.0f, 0.0f, 0.0f, 0.0f};
@@ -163,16 +164,30 @@ __global__ __launch_bounds__(kThreads16, 1) void prefill16_kernel(Problem p, Arg
                 }
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int s = s_first + kb * 16 + 4 * quad + r;
-                    float xs = score2<EPI>(p, sacc[r], qk_scale, h, pos, s, bpre[kb][EPI ? r : 0]);
-                    if (!all_vis) {
-                        bool vis = (s < rows.khi) & window_visible(p.ep, pos, s);
-                        if (sink_tile) vis = vis | ((s < rows.khi) & sink_visible(p.ep, pos, s));
-                        xs = vis ? xs : -INFINITY;
-                    }
-                    x[kb][r] = xs;
+                    xe[4 * kb + r] = sacc[r];
+                    sk[4 * kb + r] = s_first + kb * 16 + 4 * quad + r;
                 }
             }
+            if constexpr (EPI) {
+                float bb[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) bb[i] = bpre[i >> 2][i & 3];
+                score_epilogue_n<8>(xe, p.ep, slope, pos, sk, bb);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) xe[i] *= qk_scale;
+            }
+            if (!all_vis) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int s = sk[i];
+                    bool vis = (s < rows.khi) & window_visible(p.ep, pos, s);
+                    if (sink_tile) vis = vis | ((s < rows.khi) & sink_visible(p.ep, pos, s));
+                    xe[i] = vis ? xe[i] : -INFINITY;
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[i >> 2][i & 3] = xe[i];
         }
         if (more) stage_rows<D, kThreads16>(kst, ktile + (buf ^ 1) * kBK * KLD);
 

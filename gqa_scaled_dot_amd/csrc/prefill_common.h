@@ -224,14 +224,45 @@ __device__ __forceinline__ float bias_at(const Problem& p, int h, int t, int s) 
     return b;
 }
 
-// Score of register value `dot` for key s of the query at `pos` in head h, in
-// the base-2 domain: the full epilogue (with bias entry b) when EPI, else
-// just the scale.
-template <bool EPI>
-__device__ __forceinline__ float score2(const Problem& p, float dot, float qk_scale, int h, int pos,
-                                        int s, float b) {
-    if constexpr (EPI) return score_epilogue(dot, p.ep, h, pos, s, b) * kLog2e;
-    else return dot * qk_scale;
+// Whether a tile's bias entries can come four at a time: a bias input and no
+// bucketed position bias, whose rows start 16-byte aligned when S is a
+// multiple of 4 (the base pointer always is: the host refuses others).
+__device__ __forceinline__ bool bias_vec4(const Problem& p) {
+    return p.ep.bias_kind != ATTN_BIAS_NONE && !p.ep.pb_weight && (p.S & 3) == 0;
+}
+
+// bias_at for NQ groups of four keys, group j at s0 + j * step .. + 3 (s0 and
+// step multiples of 4), one 128-bit load per group when `vec` (bias_vec4).
+// All groups are requested under one branch, so their loads are in flight
+// together. Past the last key (only in a tile's masked tail) the entries are
+// those of the last four keys. (With the bucketed position bias on, the
+// per-entry path serves: its table lookups beside these loads made the
+// compiler wait for every load of the tile before the matrix work.)
+template <int NQ>
+__device__ __forceinline__ void bias_quads(const Problem& p, bool vec, int h, int t, int s0, int step,
+                                           float (&b)[NQ][4]) {
+    if (vec) {
+        const int tc = min(t, (int)p.T - 1);
+        const float* row = p.bias + (p.ep.bias_kind == ATTN_BIAS_HTS ? (int64_t)h * p.T + tc : (int64_t)tc) * p.S;
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) {
+            const float4 v = *reinterpret_cast<const float4*>(row + min(s0 + j * step, (int)p.S - 4));
+            b[j][0] = v.x;
+            b[j][1] = v.y;
+            b[j][2] = v.z;
+            b[j][3] = v.w;
+        }
+    } else if (p.ep.bias_kind != ATTN_BIAS_NONE || p.ep.pb_weight) {
+#pragma unroll
+        for (int j = 0; j < NQ; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) b[j][i] = bias_at(p, h, t, s0 + j * step + i);
+    } else {
+#pragma unroll
+        for (int j = 0; j < NQ; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) b[j][i] = 0.0f;
+    }
 }
 
 template <typename K>

@@ -162,3 +162,17 @@ def test_prefill_windows_wider_than_any_distance(window, causal, variant):
     w = workloads.Workload("wide window", T=1024, S=1024, heads=8, kvHeads=2, headDim=128,
                            causal=causal, window=window, seed=window % 997)
     _check(w, rows=sample_rows(w.T, seed=3, edges=(1000, 23)), what=f"window={window} causal={causal}")
+
+
+@pytest.mark.parametrize("S", [260, 258], ids=["rows16B", "ragged"])
+@pytest.mark.parametrize("kind, causal", [("TS", True), ("HTS", False)])
+@pytest.mark.parametrize("D, Dv", [(128, 128), (192, 128)])
+def test_prefill_bias_entries_four_at_a_time(S, kind, causal, D, Dv, variant):
+    # Bias rows of a multiple of 4 entries are read four entries per load;
+    # ragged rows (S not a multiple of 4) one entry per load. Both against the
+    # oracle, with ALiBi beside the bias and a last key tile past S.
+    w = workloads.Workload("bias four at a time", T=96, S=S, heads=8, kvHeads=2, headDim=D, vHeadDim=Dv,
+                           causal=causal, posOffset=S - 96 if causal else 0, alibi=True, bias=kind,
+                           bias_mask_prob=0.1, seed=S + D)
+    q, k, v, bias = w.tensors()
+    compare(q, k, v, bias, w.params(), what=f"{kind} S={S} D={D}")
