@@ -247,6 +247,17 @@ __global__ __launch_bounds__(kThreads, RM == 2 ? prefill_rel_waves(D, DV) : pref
     const float qk_scale = p.ep.scale * kLog2e;
     const float slope = alibi_slope(p.ep, h);
     const bool vec_bias = bias_vec4(p);
+    // Bucketed position bias: its tables in LDS past the tiles (and the
+    // relative rows), filled here and published by the loop's first barrier.
+    const uint8_t* pb_b = nullptr;
+    const float* pb_w = nullptr;
+    if (EPI && p.ep.pb_weight) {
+        uint8_t* b = reinterpret_cast<uint8_t*>(lds + 2 * kBK * (KLD + VLD) + (RM == 2 ? kWaves * kBQ * kRelRows : 0));
+        float* w = reinterpret_cast<float*>(b + ATTN_PB_MAX_DIST);
+        pb_fill(p.ep, b, w, g * hpg + hgi * a.nh, a.nh);
+        pb_b = b;
+        pb_w = w + (wave % a.nh) * pb_nbk(p.ep);
+    }
     if (v0 < v1) {
         fetch_rows<D, kThreads, DP>(kst, kg, kstride, tile_of(v0), rows);
         fetch_rows<DV, kThreads, DVP>(vst, vg, vstride, tile_of(v0), rows);
@@ -285,7 +296,7 @@ __global__ __launch_bounds__(kThreads, RM == 2 ? prefill_rel_waves(D, DV) : pref
             // Bias entries of the tile, requested before the matrix work so
             // that it hides their latency.
             float bpre[EPI ? 4 : 1][4];
-            if constexpr (EPI) bias_quads<4>(p, vec_bias, h, t, s_first + 4 * half, 8, bpre);
+            if constexpr (EPI) bias_quads<4>(p, vec_bias, h, t, pos, s_first + 4 * half, 8, pb_b, pb_w, bpre);
             // S^T = K Q^T for 32 keys x 32 queries.
             f32x16 sacc;
 #pragma unroll
@@ -504,14 +515,16 @@ template <int D, int DV, bool EPI, int RM = 0>
 hipError_t launch_t(const Problem& p, const Args& a, const Launch& L) {
     auto kern = prefill_kernel<D, DV, EPI, RM>;
     constexpr size_t lds = PrefillShape<D, DV>::lds_bytes + (RM == 2 ? PrefillShape<D, DV>::rel_lds_bytes : 0);
+    constexpr size_t lds_pb = EPI ? pb_lds_bytes(kWaves) : 0;  // with the bucketed position bias
     static bool configured = false;
     if (!configured) {
-        const hipError_t e = set_lds_limit(kern, lds);
+        const hipError_t e = set_lds_limit(kern, lds + lds_pb);
         if (e != hipSuccess) return e;
         configured = true;
     }
     const int64_t nwg = (int64_t)a.qblocks * p.G * a.hgroups * a.ksplit;
-    return launch_kernel(kern, dim3((unsigned)nwg), dim3(kThreads), (uint32_t)lds, L, p, a);
+    const size_t bytes = lds + (p.ep.pb_weight ? lds_pb : 0);
+    return launch_kernel(kern, dim3((unsigned)nwg), dim3(kThreads), (uint32_t)bytes, L, p, a);
 }
 
 template <int D, int DV>

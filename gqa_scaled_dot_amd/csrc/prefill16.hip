@@ -116,6 +116,17 @@ __global__ __launch_bounds__(kThreads16, 1) void prefill16_kernel(Problem p, Arg
     const float qk_scale = p.ep.scale * kLog2e;
     const float slope = alibi_slope(p.ep, h);
     const bool vec_bias = bias_vec4(p);
+    // Bucketed position bias: its tables in LDS past the tiles, filled here
+    // and published by the loop's first barrier.
+    const uint8_t* pb_b = nullptr;
+    const float* pb_w = nullptr;
+    if (EPI && p.ep.pb_weight) {
+        uint8_t* b = reinterpret_cast<uint8_t*>(lds + 2 * kBK * (KLD + VLD));
+        float* w = reinterpret_cast<float*>(b + ATTN_PB_MAX_DIST);
+        pb_fill(p.ep, b, w, c.g * hpg + c.hgi * a.nh, a.nh);
+        pb_b = b;
+        pb_w = w + (wave % a.nh) * pb_nbk(p.ep);
+    }
 
     if (v0 < v1) {
         fetch_rows<D, kThreads16>(kst, kg, kstride, span.tile(v0), rows);
@@ -144,7 +155,7 @@ __global__ __launch_bounds__(kThreads16, 1) void prefill16_kernel(Problem p, Arg
             // Bias entries of the tile, requested before the matrix work so
             // that it hides their latency.
             float bpre[2][EPI ? 4 : 1];
-            if constexpr (EPI) bias_quads<2>(p, vec_bias, h, t, s_first + 4 * quad, 16, bpre);
+            if constexpr (EPI) bias_quads<2>(p, vec_bias, h, t, pos, s_first + 4 * quad, 16, pb_b, pb_w, bpre);
             // Scores of both 16-key blocks, then the epilogue over the 8 scores
             // of the lane, then the mask. Score 4 kb + r: key s_first + 16 kb +
             // 4 quad + r.
@@ -275,14 +286,16 @@ template <int D, int DV, bool EPI>
 hipError_t launch16_t(const Problem& p, const Args& a, const Launch& L) {
     auto kern = prefill16_kernel<D, DV, EPI>;
     constexpr size_t lds = Shape16<D, DV>::lds_bytes;
+    constexpr size_t lds_pb = EPI ? pb_lds_bytes(kWaves16) : 0;  // with the bucketed position bias
     static bool configured = false;
     if (!configured) {
-        const hipError_t e = set_lds_limit(kern, lds);
+        const hipError_t e = set_lds_limit(kern, lds + lds_pb);
         if (e != hipSuccess) return e;
         configured = true;
     }
     const int64_t nwg = (int64_t)a.qblocks * p.G * a.hgroups * a.ksplit;
-    return launch_kernel(kern, dim3((unsigned)nwg), dim3(kThreads16), (uint32_t)lds, L, p, a);
+    const size_t bytes = lds + (p.ep.pb_weight ? lds_pb : 0);
+    return launch_kernel(kern, dim3((unsigned)nwg), dim3(kThreads16), (uint32_t)bytes, L, p, a);
 }
 
 template <int D, int DV>

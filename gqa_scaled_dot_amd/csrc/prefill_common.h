@@ -212,38 +212,60 @@ __device__ __forceinline__ void stage_rows(const float4 (&st)[kBK * W / 4 / NT],
     }
 }
 
-// The bias entry of (head h, query row t, key s): the bias input's entry,
-// clamped in bounds (masked keys may lie outside the tensor), plus the
-// bucketed position bias; 0 without either.
-__device__ __forceinline__ float bias_at(const Problem& p, int h, int t, int s) {
-    const int sc = min(max(s, 0), (int)p.S - 1), tc = min(t, (int)p.T - 1);
-    float b = 0.0f;
-    if (p.ep.bias_kind == ATTN_BIAS_TS) b = p.bias[(int64_t)tc * p.S + sc];
-    else if (p.ep.bias_kind == ATTN_BIAS_HTS) b = p.bias[((int64_t)h * p.T + tc) * p.S + sc];
-    if (p.ep.pb_weight) b += position_bias(p.ep, h, p.ep.pos_offset + t, s);
-    return b;
+// The bucketed position bias through LDS: the distance -> bucket table
+// (pb_dt bytes) and the weights of the workgroup's heads ([head][bucket]),
+// filled once per workgroup, so that a score's term costs two LDS reads
+// rather than two dependent memory loads (which inside the key loop also
+// made the wave wait for every load issued before them, the next tile's K
+// rows included). Bytes a kernel of up to nh_max heads per workgroup adds
+// to its LDS when the term is on:
+__host__ __device__ constexpr size_t pb_lds_bytes(int nh_max) {
+    return ATTN_PB_MAX_DIST + sizeof(float) * (size_t)nh_max * 2 * ATTN_PB_MAX_BUCKETS;
 }
 
-// Whether a tile's bias entries can come four at a time: a bias input and no
-// bucketed position bias, whose rows start 16-byte aligned when S is a
-// multiple of 4 (the base pointer always is: the host refuses others).
+// Fill the tables for heads h0 .. h0 + nh - 1 (all threads of the block take
+// part; the caller's next barrier publishes them). Weights of local head hl
+// start at w + hl * pb_nbk(e).
+__device__ __forceinline__ int pb_nbk(const Epilogue& e) { return e.pb_bidir ? 2 * e.pb_n : e.pb_n; }
+__device__ __forceinline__ void pb_fill(const Epilogue& e, uint8_t* bkt, float* w, int h0, int nh) {
+    const int nt = (int)blockDim.x;
+    for (int d = (int)threadIdx.x; d < e.pb_dt; d += nt) bkt[d] = e.pb_bucket[d];
+    const int nbk = pb_nbk(e);
+    for (int i = (int)threadIdx.x; i < nh * nbk; i += nt) {
+        const int hl = i / nbk, b = i - hl * nbk;
+        w[i] = e.pb_weight[b * e.pb_heads + h0 + hl];
+    }
+}
+
+// position_bias with the tables in LDS (whead: the row's head's weights).
+__device__ __forceinline__ float pb_lds(const Epilogue& e, const uint8_t* bkt, const float* whead, int pos, int s) {
+    const int d = abs(pos - s);
+    int b = d < e.pb_dt ? (int)bkt[d] : e.pb_n - 1;
+    if (e.pb_bidir && s > pos) b += e.pb_n;
+    return whead[b];
+}
+
+// Whether a tile's bias entries can come four at a time: the bias rows start
+// 16-byte aligned when S is a multiple of 4 (the base pointer always is: the
+// host refuses others).
 __device__ __forceinline__ bool bias_vec4(const Problem& p) {
-    return p.ep.bias_kind != ATTN_BIAS_NONE && !p.ep.pb_weight && (p.S & 3) == 0;
+    return p.ep.bias_kind != ATTN_BIAS_NONE && (p.S & 3) == 0;
 }
 
-// bias_at for NQ groups of four keys, group j at s0 + j * step .. + 3 (s0 and
-// step multiples of 4), one 128-bit load per group when `vec` (bias_vec4).
-// All groups are requested under one branch, so their loads are in flight
+// The bias entries of (head h, query row t at position pos) for NQ groups of
+// four keys, group j at s0 + j * step .. + 3 (s0 and step multiples of 4):
+// the bias input's entry (one 128-bit load per group when `vec`, bias_vec4;
+// else one per entry, clamped in bounds) plus, with pb_w the head's weights
+// in LDS (NULL: off), the bucketed position bias; 0 without either. All
+// groups' loads are requested under one branch, so they are in flight
 // together. Past the last key (only in a tile's masked tail) the entries are
-// those of the last four keys. (With the bucketed position bias on, the
-// per-entry path serves: its table lookups beside these loads made the
-// compiler wait for every load of the tile before the matrix work.)
+// those of the last keys.
 template <int NQ>
-__device__ __forceinline__ void bias_quads(const Problem& p, bool vec, int h, int t, int s0, int step,
-                                           float (&b)[NQ][4]) {
+__device__ __forceinline__ void bias_quads(const Problem& p, bool vec, int h, int t, int pos, int s0, int step,
+                                           const uint8_t* pb_b, const float* pb_w, float (&b)[NQ][4]) {
+    const int tc = min(t, (int)p.T - 1);
+    const float* row = p.bias + (p.ep.bias_kind == ATTN_BIAS_HTS ? (int64_t)h * p.T + tc : (int64_t)tc) * p.S;
     if (vec) {
-        const int tc = min(t, (int)p.T - 1);
-        const float* row = p.bias + (p.ep.bias_kind == ATTN_BIAS_HTS ? (int64_t)h * p.T + tc : (int64_t)tc) * p.S;
 #pragma unroll
         for (int j = 0; j < NQ; ++j) {
             const float4 v = *reinterpret_cast<const float4*>(row + min(s0 + j * step, (int)p.S - 4));
@@ -252,16 +274,22 @@ __device__ __forceinline__ void bias_quads(const Problem& p, bool vec, int h, in
             b[j][2] = v.z;
             b[j][3] = v.w;
         }
-    } else if (p.ep.bias_kind != ATTN_BIAS_NONE || p.ep.pb_weight) {
+    } else if (p.ep.bias_kind != ATTN_BIAS_NONE) {
 #pragma unroll
         for (int j = 0; j < NQ; ++j)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) b[j][i] = bias_at(p, h, t, s0 + j * step + i);
+            for (int i = 0; i < 4; ++i) b[j][i] = row[min(max(s0 + j * step + i, 0), (int)p.S - 1)];
     } else {
 #pragma unroll
         for (int j = 0; j < NQ; ++j)
 #pragma unroll
             for (int i = 0; i < 4; ++i) b[j][i] = 0.0f;
+    }
+    if (pb_w) {
+#pragma unroll
+        for (int j = 0; j < NQ; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) b[j][i] += pb_lds(p.ep, pb_b, pb_w, pos, s0 + j * step + i);
     }
 }
 
