@@ -12,14 +12,14 @@
 // as decode_split). The workgroup's four waves take the split's key rows in
 // tiles of 16 (wave w: tiles w, w + 4, ...), each with its own online
 // softmax over the group's rows (up to 16 per row block, NB blocks), and
-// merge through LDS at the end. Operands come straight from HBM into
-// registers, laid out as the MFMA wants them (lane l, column n = l % 16,
-// lane group kg = l / 16):
+// merge through LDS at the end. A tile's K and V rows are loaded row by row
+// (each load instruction of a wave reads whole row slices), pass through the
+// wave's own LDS area and come out laid out as the MFMA wants them (lane l,
+// column n = l % 16, lane group kg = l / 16):
 //   scores S^T = K Q^T, one MFMA per 4 channels: A[key i][k] in lane i + 16k
 //     holds K[key][d], B[k][query j] in lane j + 16k holds q[query][d], for
-//     the channel d = 16 m + 4 kg + c of step (m, c). So lane l loads 16
-//     consecutive bytes of K row n at 64-byte steps: the four lanes of a row
-//     read 64 contiguous bytes per load. The result D[key i][query j] sits
+//     the channel d = 16 m + 4 kg + c of step (m, c): lane l takes 16 bytes
+//     of K row n at 64-byte steps. The result D[key i][query j] sits
 //     in lane j + 16 (i / 4), element i % 4: lane l holds the scores of
 //     keys 4 kg .. 4 kg + 3 for query n.
 //   weighted sum O^T += V^T P^T, step r contracting keys 4k + r: A[e][k] =
@@ -57,18 +57,40 @@ __device__ __forceinline__ float comp(const float4& v, int c) {
 
 __device__ __forceinline__ float4 zero4() { return make_float4(0.f, 0.f, 0.f, 0.f); }
 
+// Orders one wave's LDS writes and its lanes' later reads of them (and
+// reads before later writes): a wave's LDS instructions complete in order,
+// so only the compiler must not move accesses across this point.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // D: key/query width, DV: value width, NB: blocks of 16 query rows per KV
 // group, EPI: softcap / ALiBi / bias possible (else the score is the scaled
 // product and q carries the scale).
+// Built for one workgroup per CU where headDim + vHeadDim >= 256 (the
+// planner's choice there; the raw rows, the matrix-layout copies and the
+// accumulators then have a SIMD's 512 registers), else two.
 template <int D, int DV, int NB, bool EPI>
-__global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(Problem p, DecodePlan plan,
-                                                                  float* __restrict__ ws) {
+__global__ __launch_bounds__(kThreads, (D + DV >= 256 ? 1 : 2)) void decode_mfma_kernel(Problem p, DecodePlan plan,
+                                                                                       float* __restrict__ ws) {
     constexpr int KM = D / 16;   // float4 of a K row per lane (4 channels each of KM 16-channel steps)
     constexpr int VH = DV / 64;  // float4 of each of 4 V rows per lane
     constexpr int NO = 4 * VH;   // output blocks of 16 values per row block
+    constexpr int KT4 = D / 4, VT4 = DV / 4;  // float4s per K / V row
+    constexpr int KR = kTile * KT4 / 64, VR = kTile * VT4 / 64;  // raw float4 loads per lane per tile
+    static_assert(kTile * KT4 % 64 == 0 && kTile * VT4 % 64 == 0, "a tile's rows must split evenly over a wave");
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int n = lane & 15, kg = lane >> 4;
+    // LDS: each wave's K area [kTile][KT4] and V area [kTile][VT4] float4s
+    // (float4 c of row r at c ^ (r & 15): both the row-wise writes and the
+    // matrix-layout reads hit distinct bank groups), then the merge's
+    // (max, sum) pairs.
+    extern __shared__ float4 lds4[];
+    float4* wk = lds4 + wave * kTile * KT4;
+    float4* wv = lds4 + kWaves * kTile * KT4 + wave * kTile * VT4;
 
     // Split sp of KV group g (appending calls: the append splits last).
     int sp, g;
@@ -148,30 +170,42 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(Problem p, Dec
     // Workgroup-uniform bases, 32-bit per-lane offsets (the host keeps a
     // split's rows times the row stride below 2^31 floats).
     const uint32_t kstride = (uint32_t)(p.G * D), vstride = (uint32_t)(p.G * DV);
-    const float* kwg = (append ? plan.k_new : p.k + (int64_t)k0 * kstride) + (int64_t)g * D + 4 * kg;
-    const float* vwg = (append ? plan.v_new : p.v + (int64_t)k0 * vstride) + (int64_t)g * DV + 4 * n;
+    const float* kwg = (append ? plan.k_new : p.k + (int64_t)k0 * kstride) + (int64_t)g * D;
+    const float* vwg = (append ? plan.v_new : p.v + (int64_t)k0 * vstride) + (int64_t)g * DV;
 
-    // A tile's K goes out once the previous tile's scores are formed, its V
-    // (and bias entries) once the previous weighted sum is done, so each
-    // load lands in registers just freed. The first tile's loads go out
-    // before q is fetched. Rows past the split's end read its last row and
-    // are masked.
-    float4 kf[KM], vf[4][VH];
+    // A tile's K and V rows come from memory row by row (each load
+    // instruction of a wave reads whole row slices: 2 rows of 512 bytes at
+    // headDim 128), into the wave's own LDS area, and from there into the
+    // matrix layouts above. (Loaded straight in the matrix layout, each K
+    // instruction touched 64 bytes of 16 different rows: a load-only kernel
+    // with that pattern streamed 64/8-head-shaped K/V at 6.0 TB/s, with
+    // whole-row loads and the trip through LDS at 6.5 TB/s.) A tile's K goes
+    // out once the previous tile's K has moved to LDS, its V once the
+    // previous V has, and its bias entries once the previous weighted sum is
+    // done. The first tile's loads go out before q is fetched. Rows past the
+    // split's end read its last row and are masked.
+    float4 kr[KR], vr[VR];
     float bf[NB][4];
     auto load_k = [&](int j) {
         const int s0 = tile_row(j);
-        const uint32_t rk = (uint32_t)(min(s0 + n, k1 - 1) - k0);
 #pragma unroll
-        for (int m = 0; m < KM; ++m) kf[m] = load_stream4(kwg + rk * kstride + 16 * m);
+        for (int i = 0; i < KR; ++i) {
+            const int f = 64 * i + lane, row = f / KT4, c4 = f - row * KT4;
+            const uint32_t rk = (uint32_t)(min(s0 + row, k1 - 1) - k0);
+            kr[i] = load_stream4(kwg + rk * kstride + 4 * c4);
+        }
     };
     auto load_v = [&](int j) {
         const int s0 = tile_row(j);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const uint32_t rv = (uint32_t)(min(s0 + 4 * kg + r, k1 - 1) - k0);
-#pragma unroll
-            for (int h = 0; h < VH; ++h) vf[r][h] = load_stream4(vwg + rv * vstride + 64 * h);
+        for (int i = 0; i < VR; ++i) {
+            const int f = 64 * i + lane, row = f / VT4, c4 = f - row * VT4;
+            const uint32_t rv = (uint32_t)(min(s0 + row, k1 - 1) - k0);
+            vr[i] = load_stream4(vwg + rv * vstride + 4 * c4);
         }
+    };
+    auto load_bias = [&](int j) {
+        const int s0 = tile_row(j);
         if constexpr (EPI) {
 #pragma unroll
             for (int b = 0; b < NB; ++b)
@@ -188,6 +222,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(Problem p, Dec
     if (wave < ntiles) {
         load_k(wave);
         load_v(wave);
+        load_bias(wave);
     }
 
     // q, in the B layout: lane l holds channels 16 m + 4 kg .. + 3 of its
@@ -223,6 +258,30 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(Problem p, Dec
 
     for (int j = wave; j < ntiles; j += kWaves) {
         const int s0 = tile_row(j);
+        const bool more = j + kWaves < ntiles;
+        // K: raw rows into LDS, back out in the A layout (row n, channels
+        // 16 m + 4 kg .. + 3); then the next tile's K goes out.
+#pragma unroll
+        for (int i = 0; i < KR; ++i) {
+            const int f = 64 * i + lane, row = f / KT4, c4 = f - row * KT4;
+            wk[row * KT4 + (c4 ^ (row & 15))] = kr[i];
+        }
+        wave_lds_sync();
+        float4 kf[KM];
+#pragma unroll
+        for (int m = 0; m < KM; ++m) kf[m] = wk[n * KT4 + ((4 * m + kg) ^ n)];
+        // Appended rows go on into the caches: each lane stores the row
+        // slices it loaded (every element of the tile exactly once).
+        if (append) {
+            float* kd = plan.k_cache + (int64_t)k0 * kstride + (int64_t)g * D;
+#pragma unroll
+            for (int i = 0; i < KR; ++i) {
+                const int f = 64 * i + lane, row = f / KT4, c4 = f - row * KT4;
+                if (s0 + row < k1)
+                    *reinterpret_cast<float4*>(kd + ((uint32_t)(s0 + row - k0) * kstride + 4 * c4)) = kr[i];
+            }
+        }
+        if (more) load_k(j + kWaves);
         // Scores of keys s0 + 4 kg + i for this lane's query of each block.
         f32x4v sc[NB];
 #pragma unroll
@@ -234,29 +293,30 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(Problem p, Dec
                 for (int c = 0; c < 4; ++c) s = mfma16(comp(kf[m], c), comp(qf[b][m], c), s);
             sc[b] = s;
         }
-        // Appended rows go on into the caches: each lane stores what it
-        // loaded (every element of the tile exactly once).
+        __builtin_amdgcn_sched_barrier(0);  // V's trip through LDS after the score work
+        // V: raw rows into LDS, back out in the A layout of the weighted sum
+        // (rows 4 kg + r, channels 64 h + 4 n .. + 3); then the next V.
+#pragma unroll
+        for (int i = 0; i < VR; ++i) {
+            const int f = 64 * i + lane, row = f / VT4, c4 = f - row * VT4;
+            wv[row * VT4 + (c4 ^ (row & 15))] = vr[i];
+        }
+        wave_lds_sync();
+        float4 vf[4][VH];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int h = 0; h < VH; ++h) vf[r][h] = wv[(4 * kg + r) * VT4 + ((16 * h + n) ^ ((4 * kg + r) & 15))];
         if (append) {
-            float* kd = plan.k_cache + (int64_t)k0 * kstride + (int64_t)g * D + 4 * kg;
-            float* vd = plan.v_cache + (int64_t)k0 * vstride + (int64_t)g * DV + 4 * n;
-            if (s0 + n < k1) {
-                const uint32_t rk = (uint32_t)(s0 + n - k0);
+            float* vd = plan.v_cache + (int64_t)k0 * vstride + (int64_t)g * DV;
 #pragma unroll
-                for (int m = 0; m < KM; ++m) *reinterpret_cast<float4*>(kd + (rk * kstride + 16 * m)) = kf[m];
-            }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                if (s0 + 4 * kg + r < k1) {
-                    const uint32_t rv = (uint32_t)(s0 + 4 * kg + r - k0);
-#pragma unroll
-                    for (int h = 0; h < VH; ++h)
-                        *reinterpret_cast<float4*>(vd + (rv * vstride + 64 * h)) = vf[r][h];
-                }
+            for (int i = 0; i < VR; ++i) {
+                const int f = 64 * i + lane, row = f / VT4, c4 = f - row * VT4;
+                if (s0 + row < k1)
+                    *reinterpret_cast<float4*>(vd + ((uint32_t)(s0 + row - k0) * vstride + 4 * c4)) = vr[i];
             }
         }
-        // The next tile's K goes out while this one's weights are formed.
-        const bool more = j + kWaves < ntiles;
-        if (more) load_k(j + kWaves);
+        if (more) load_v(j + kWaves);
 
         const bool check = !(dense && s0 + kTile <= k1);
 #pragma unroll
@@ -298,13 +358,16 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(Problem p, Dec
                     for (int c = 0; c < 4; ++c)
                         acc[b][4 * h + c] = mfma16(comp(vf[r][h], c), pw[r], acc[b][4 * h + c]);
         }
-        if (more) load_v(j + kWaves);
+        if (more) load_bias(j + kWaves);
+        wave_lds_sync();  // this tile's LDS reads come before the next tile's writes
     }
 
     // Each query's sum over its four lane groups, then the four waves merge
-    // through LDS, one row block at a time.
-    __shared__ float s_m[kWaves][16], s_l[kWaves][16];
-    __shared__ float4 s_acc[kWaves][16][DV / 4];
+    // through LDS, one row block at a time; a wave's share of the merge goes
+    // into its own V area ([16][DV / 4] float4s).
+    float* s_m = reinterpret_cast<float*>(lds4 + kWaves * kTile * (KT4 + VT4));  // [kWaves][16]
+    float* s_l = s_m + kWaves * 16;                                               // [kWaves][16]
+    auto s_acc = [&](int w, int rn, int e4) -> float4& { return lds4[kWaves * kTile * KT4 + w * kTile * VT4 + rn * VT4 + e4]; };
     const int nsplit = plan.splits;
     float* ws_acc = ws;
     float* ws_ml = ws + (int64_t)p.T * p.H * nsplit * DV;
@@ -315,31 +378,31 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(Problem p, Dec
         l += __shfl_xor(l, 32, 64);
         if (b > 0) __syncthreads();  // the previous block's merge has read s_*
         if (kg == 0) {
-            s_m[wave][n] = mrow[b];
-            s_l[wave][n] = l;
+            s_m[wave * 16 + n] = mrow[b];
+            s_l[wave * 16 + n] = l;
         }
 #pragma unroll
         for (int h = 0; h < VH; ++h)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                s_acc[wave][n][16 * h + 4 * kg + i] =
+                s_acc(wave, n, 16 * h + 4 * kg + i) =
                     make_float4(acc[b][4 * h][i], acc[b][4 * h + 1][i], acc[b][4 * h + 2][i], acc[b][4 * h + 3][i]);
         __syncthreads();
         for (int idx = tid; idx < 16 * (DV / 4); idx += kThreads) {
             const int rn = idx / (DV / 4), e4 = idx % (DV / 4);
             const int r = 16 * b + rn;
             if (r >= nrows) continue;
-            float M = s_m[0][rn];
+            float M = s_m[rn];
 #pragma unroll
-            for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w][rn]);
+            for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w * 16 + rn]);
             const float Mu = M == -INFINITY ? 0.0f : M;
             float L = 0.0f;
             float4 A = zero4();
 #pragma unroll
             for (int w = 0; w < kWaves; ++w) {
-                const float f = fast_exp2(s_m[w][rn] - Mu);
-                L += s_l[w][rn] * f;
-                const float4 c = s_acc[w][rn][e4];
+                const float f = fast_exp2(s_m[w * 16 + rn] - Mu);
+                L += s_l[w * 16 + rn] * f;
+                const float4 c = s_acc(w, rn, e4);
                 A.x += c.x * f; A.y += c.y * f; A.z += c.z * f; A.w += c.w * f;
             }
             const int64_t th = (int64_t)(r / hpg) * p.H + (g * hpg + r % hpg);
@@ -358,11 +421,25 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(Problem p, Dec
     }
 }
 
+template <int D, int DV, int NB, bool EPI>
+hipError_t launch_t(const Problem& p, const DecodePlan& plan, float* ws, const Launch& L) {
+    auto kern = decode_mfma_kernel<D, DV, NB, EPI>;
+    constexpr size_t lds = sizeof(float4) * kWaves * kTile * (D / 4 + DV / 4) + sizeof(float) * 2 * kWaves * 16;
+    static bool configured = false;
+    if (!configured) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        configured = true;
+    }
+    const dim3 grid = plan.k_new ? dim3((unsigned)(plan.splits * p.G)) : dim3((unsigned)plan.splits, (unsigned)p.G);
+    return launch_kernel(kern, grid, dim3(kThreads), (uint32_t)lds, L, p, plan, ws);
+}
+
 template <int D, int DV, int NB>
 hipError_t launch_nb(const Problem& p, const DecodePlan& plan, float* ws, const Launch& L) {
-    const dim3 grid = plan.k_new ? dim3((unsigned)(plan.splits * p.G)) : dim3((unsigned)plan.splits, (unsigned)p.G);
-    if (p.ep.any()) return launch_kernel(decode_mfma_kernel<D, DV, NB, true>, grid, dim3(kThreads), 0, L, p, plan, ws);
-    return launch_kernel(decode_mfma_kernel<D, DV, NB, false>, grid, dim3(kThreads), 0, L, p, plan, ws);
+    if (p.ep.any()) return launch_t<D, DV, NB, true>(p, plan, ws, L);
+    return launch_t<D, DV, NB, false>(p, plan, ws, L);
 }
 
 template <int D, int DV>
