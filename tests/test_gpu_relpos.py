@@ -75,6 +75,20 @@ def test_position_bias_with_other_terms(features):
     _check_pb(w, th, weight, False, ("decode", "prefill", "generic"))
 
 
+@pytest.mark.parametrize("variant", [32, 16])
+@pytest.mark.parametrize("S, causal, bidirectional", [(300, True, False), (298, True, False), (260, False, True)])
+def test_position_bias_prefill_with_bias_and_alibi(variant, S, causal, bidirectional):
+    # The prefill kernels' table lookups beside the bias input's entries,
+    # read four per load (S a multiple of 4) or one per load, and ALiBi;
+    # 8 heads over 2 KV heads: four heads per workgroup, each its own
+    # weights.
+    w = workloads.Workload("pb+bias prefill", T=120, S=S, heads=8, kvHeads=2, headDim=128,
+                           posOffset=S - 120 if causal else 10, causal=causal, alibi=True, bias="HTS",
+                           bias_mask_prob=0.1, seed=S + variant)
+    th, weight = _pb(8, bidirectional)
+    _check_pb(w, th, weight, bidirectional, ("prefill",), variant)
+
+
 def test_position_bias_small_tables():
     # One bucket, then thresholds [0, 1, 2, 4, 8, 16] bidirectional on a non-causal decode.
     w = workloads.Workload("pb small", T=2, S=50, heads=4, kvHeads=2, headDim=64, posOffset=20, causal=False)
