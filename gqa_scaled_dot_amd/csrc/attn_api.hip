@@ -60,6 +60,7 @@ int64_t g_opt_mla_combine_out = 0;  // 0: automatic; 16 or 32 output channels pe
 int64_t g_opt_mla_slices = 0;       // 0: automatic; 1: merge by latent slices where possible; -1: never
 
 constexpr int kCUs = 256;                 // MI355X compute units
+constexpr int kXcdCount = 8;              // XCDs (each with its own L2) the CUs sit in
 constexpr int kDecodeWgPerCU = 2;         // decode_split occupancy target (decode_mfma: see make_plan)
 constexpr int kDecodeDepth = 1;           // decode_split batches per lane at a time (no prefetch ring)
 // Smallest key chunk worth a workgroup. A decode_split workgroup costs ~8 us
@@ -779,6 +780,19 @@ int make_plan(const Resolved& r, Plan* plan, const AppendRows* app = nullptr) {
         int64_t ks = g_opt_prefill_splits;
         if (ks <= 0) {
             ks = nwg >= want ? 1 : (want + nwg - 1) / nwg;
+            if (uneven) {
+                // Causal grids with fewer workgroups per KV head than an XCD
+                // runs at once (MHA: one head per workgroup): split them to
+                // that many, up to 4 parts. Measured (32 heads of 128, one
+                // box): 2048 x 2048 442 -> 372 us (4 parts), 4096 x 4096
+                // 1603 -> 1175 us (2 parts) per call, although the parts
+                // fetch more from HBM (a 4096-row call 0.24 -> 0.76 GB);
+                // 8192 rows (64 blocks per head) stay whole at 81%.
+                const int64_t per_head = qblocks * (hpg / nh), xcd_slots = slots / kXcdCount;
+                int64_t kh = (xcd_slots + per_head - 1) / per_head;
+                if (kh > 4) kh = 4;
+                if (kh > ks) ks = kh;
+            }
             const int64_t most = tiles / kPrefillMinTilesPerSplit;
             if (ks > most) ks = most;
         }
