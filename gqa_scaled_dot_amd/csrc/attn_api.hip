@@ -781,15 +781,22 @@ int make_plan(const Resolved& r, Plan* plan, const AppendRows* app = nullptr) {
         if (ks <= 0) {
             ks = nwg >= want ? 1 : (want + nwg - 1) / nwg;
             if (uneven) {
-                // Causal grids with fewer workgroups per KV head than an XCD
-                // runs at once (MHA: one head per workgroup): split them to
-                // that many, up to 4 parts. Measured (32 heads of 128, one
-                // box): 2048 x 2048 442 -> 372 us (4 parts), 4096 x 4096
-                // 1603 -> 1175 us (2 parts) per call, although the parts
-                // fetch more from HBM (a 4096-row call 0.24 -> 0.76 GB);
-                // 8192 rows (64 blocks per head) stay whole at 81%.
-                const int64_t per_head = qblocks * (hpg / nh), xcd_slots = slots / kXcdCount;
-                int64_t kh = (xcd_slots + per_head - 1) / per_head;
+                // Causal grids with fewer query blocks per head than an XCD
+                // runs workgroups at once (workgroups of 128 rows of one
+                // head: MHA, or 5 or 7 heads per KV head): split them to
+                // that many, one part more where each workgroup holds one of
+                // several heads of a KV head (5 or 7 per KV head), up to 4
+                // parts. Measured (one box,
+                // per call): 32 heads of 128, 2048 x 2048 442 -> 372 us (4
+                // parts), 4096 x 4096 1603 -> 1175 us (2 parts), although the
+                // parts fetch more from HBM (a 4096-row call 0.24 -> 0.76 GB);
+                // 8192 rows (64 blocks per head) stay whole at 81%. 40 heads
+                // over 8, 4096 rows: 1861 us whole, 1630 in 2 parts, 1506 in
+                // 3; 28 over 4: 1590 whole, 1157 in 2, 1124 in 4, and at 8192
+                // rows 4287 whole, 4168 in 2; 64 over 8 (4 heads per
+                // workgroup) stays whole (2 parts: 2048 rows 580 -> 624 us).
+                const int64_t xcd_slots = slots / kXcdCount;
+                int64_t kh = (xcd_slots + qblocks - 1) / qblocks + (nh == 1 && hpg > 1 ? 1 : 0);
                 if (kh > 4) kh = 4;
                 if (kh > ks) ks = kh;
             }
