@@ -166,6 +166,29 @@ def test_relative_kv_prefill_plans():
             ga.attn_set_option("prefill_splits", 0)
 
 
+@pytest.mark.parametrize("T, H, G, splits", [
+    (4096, 32, 8, 1),    # Llama-shaped: 4 heads per workgroup, 128 query blocks per head, 1024 workgroups
+    (2048, 32, 8, 2),    # one wave of 512 workgroups for 256 CUs: 1.5 waves (uneven causal blocks)
+    (1024, 32, 8, 3),
+    (4096, 64, 8, 1),    # 8 heads per KV head in two workgroups of 4
+    (4096, 32, 32, 2),   # MHA: 32 query blocks of 128 rows per head, 64 workgroups per XCD
+    (2048, 32, 32, 4),
+    (8192, 32, 32, 1),
+    (4096, 40, 8, 3),    # 5 heads per KV head, one per workgroup: one part more
+    (4096, 28, 4, 3),
+])
+def test_causal_prefill_key_splits(T, H, G, splits):
+    # Causal query blocks see unequal key ranges: the planner splits the key
+    # ranges to at least 1.5 waves of workgroups and until each head has as
+    # many query blocks as an XCD runs workgroups at once.
+    plan = ga.attn_plan(T, T, heads=H, kvHeads=G, headDim=128)
+    assert plan["path"] == "prefill" and plan["splits"] == splits, plan
+    # Non-causal calls give every block the same keys: split only to fill
+    # one wave of workgroups (256 of them at 1024 rows: 2 parts).
+    nc = ga.attn_plan(T, T, heads=H, kvHeads=G, headDim=128, causal=False)["splits"]
+    assert nc == (2 if (T, H, G) == (1024, 32, 8) else 1), nc
+
+
 @pytest.mark.parametrize("G", [1, 2, 6, 8, 12, 16, 24])
 def test_decode_splits_fit_one_wave(G):
     # Two workgroups per CU on 256 CUs: splits x KV groups never passes 512,

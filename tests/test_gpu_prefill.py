@@ -176,3 +176,14 @@ def test_prefill_bias_entries_four_at_a_time(S, kind, causal, D, Dv, variant):
                            bias_mask_prob=0.1, seed=S + D)
     q, k, v, bias = w.tensors()
     compare(q, k, v, bias, w.params(), what=f"{kind} S={S} D={D}")
+
+
+@pytest.mark.parametrize("T, H, G", [(2048, 32, 32), (1024, 28, 4), (4096, 40, 8)])
+def test_causal_prefill_split_plans_sampled(T, H, G):
+    # Causal MHA and 7- or 5-heads-per-KV-head shapes (one head per
+    # workgroup) take key-split plans of 2-4 parts: sampled rows, the
+    # diagonal's included, against the oracle.
+    w = workloads.Workload("causal split plan", T=T, S=T, heads=H, kvHeads=G, headDim=128, seed=T + H)
+    plan = ga.attn_plan(w.T, w.S, **w.params())
+    assert plan["path"] == "prefill" and plan["splits"] > 1, plan
+    _check(w, rows=sample_rows(w.T, seed=H, n_random=24, edges=(w.T // 2, 127, 128)))
