@@ -32,23 +32,38 @@ __global__ __launch_bounds__(kThreads) void rope_vec_kernel(RopeArgs ra, const f
     const int rot_units = ra.interleaved ? ra.rd / 4 : ra.rd / 8;
     const int64_t row = blockIdx.x;
     const int64_t pos = ra.pos0 + row;
-    for (int i = threadIdx.x; i < ra.rd / 2; i += kThreads) rope_cos_sin(pos, ra.inv_freq[i], ra.af, s_cos[i], s_sin[i]);
-    __syncthreads();
     const int idx = (int)blockIdx.y * kThreads + (int)threadIdx.x;
-    if (idx >= heads * units) return;
+    const bool active = idx < heads * units;
     const bool in_place = x == out;
-    const int h = idx / units, u = idx - h * units;
+    const int h = active ? idx / units : 0, u = active ? idx - h * units : 0;
     const int64_t rh = row * heads + h;
     const float* xh = x + rh * D;
     float* oh = out + rh * D;
-    if (u >= rot_units) {
-        const int d = ra.rd + 4 * (u - rot_units);
-        if (!in_place) st4(oh + d, ld4(xh + d));
+    // The thread's channels are requested before the row's angles are
+    // worked out, so the memory latency overlaps that arithmetic.
+    const bool rot = active && u < rot_units;
+    const int dpass = ra.rd + 4 * (u - rot_units);
+    float4 va = make_float4(0.f, 0.f, 0.f, 0.f), vb = va;
+    if (active) {
+        if (!rot) {
+            if (!in_place) va = ld4(xh + dpass);  // pass-through channels: copied unless in place
+        }
+        else if (ra.interleaved) va = ld4(xh + 4 * u);
+        else {
+            va = ld4(xh + 4 * u);
+            vb = ld4(xh + ra.rd / 2 + 4 * u);
+        }
+    }
+    for (int i = threadIdx.x; i < ra.rd / 2; i += kThreads) rope_cos_sin(pos, ra.inv_freq[i], ra.af, s_cos[i], s_sin[i]);
+    __syncthreads();
+    if (!active) return;
+    if (!rot) {
+        if (!in_place) st4(oh + dpass, va);
         return;
     }
     {
         if (ra.interleaved) {
-            const float4 v = ld4(xh + 4 * u);
+            const float4 v = va;
             const float c0 = s_cos[2 * u], s0 = s_sin[2 * u], c1 = s_cos[2 * u + 1], s1 = s_sin[2 * u + 1];
             float4 o;
             o.x = fmaf(-v.y, s0, v.x * c0);
@@ -58,7 +73,7 @@ __global__ __launch_bounds__(kThreads) void rope_vec_kernel(RopeArgs ra, const f
             st4(oh + 4 * u, o);
         } else {
             const int half = ra.rd / 2;
-            const float4 a = ld4(xh + 4 * u), b = ld4(xh + half + 4 * u);
+            const float4 a = va, b = vb;
             float c[4], s[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
