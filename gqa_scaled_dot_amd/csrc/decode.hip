@@ -74,9 +74,11 @@ __device__ __forceinline__ float4 zero4() { return make_float4(0.f, 0.f, 0.f, 0.
 // key/value embeddings). 0: off. 1: on, for splits whose keys are all at the
 // tables' far end for every row (their terms are per-row constants). 2: on,
 // looked up per key (the split of keys near the query rows, the sink split,
-// and non-causal calls). RM > 0 implies EPI.
+// and non-causal calls). RM = 2 implies EPI.
 // EPI: whether softcap, ALiBi or a bias can be on; without them the score
-// is the scaled dot product and the code for the rest is left out.
+// is the scaled dot product and the code for the rest is left out (with
+// RM = 1, plus the per-row constants of the far splits and, in the near
+// split's loop, the relative-position terms, all in the scaled domain).
 // DEPTH: batches of U rows per row group held in registers. 1 (the default):
 // one batch at a time, the next fetched once the current one is used; 2 or
 // 3: a ring, DEPTH-1 batches in flight while one is used.
@@ -531,6 +533,16 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
 #pragma unroll
                 for (int r = 0; r < NQ; ++r) qrel0[r] = rel ? s_qrel[r * nrel] : 0.0f;
             }
+            if constexpr (FAR && !EPI) {
+                // No other epilogue term: a far split's scores are the scaled
+                // product (q carries scale * log2(e)) plus one constant per
+                // row in the same base-2 domain, the embedding-0 product
+                // (formed with the scaled q) and the last bucket's bias.
+                if (split_far) {
+#pragma unroll
+                    for (int r = 0; r < NQ; ++r) qrel0[r] += pbc[r] * kLog2e;
+                }
+            }
         }
         if constexpr (FAR) {
             if (near_loop) {
@@ -555,7 +567,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
                         if (p.ep.bias_kind == ATTN_BIAS_TS) b = p.bias[(int64_t)tt[r] * p.S + s];
                         else if (p.ep.bias_kind == ATTN_BIAS_HTS) b = p.bias[((int64_t)hh[r] * p.T + tt[r]) * p.S + s];
                         if (pb) b += position_bias_tab(p.ep, s_pbb, hh[r], pos[r], s);
-                        float xs = score_epilogue(dot, p.ep, slope[r], pos[r], s, b) * kLog2e;
+                        float xs;
+                        if constexpr (EPI) xs = score_epilogue(dot, p.ep, slope[r], pos[r], s, b) * kLog2e;
+                        else xs = dot + b * kLog2e;  // scaled q and embedding products; b: the position bias
                         xs = (live[r] & key_visible(p.ep, pos[r], s)) ? xs : -INFINITY;
                         if (xs > m[r] + kLazy) {
                             const float alpha = fast_exp2(m[r] - xs);
@@ -854,9 +868,16 @@ hipError_t launch_split_d(const Problem& p, const DecodePlan& plan, float* ws, c
         // walk for far splits, plain loop for the near one); otherwise every
         // split looks its terms up per key.
         const uint32_t lds_all = lds + (p.ep.pb_weight ? (uint32_t)((p.ep.pb_dt + 3) & ~3) : 0u);
-        if (plan.near_hi > plan.near_lo)
+        if (plan.near_hi > plan.near_lo) {
+            // Without softcap, ALiBi or a bias input the far splits run the
+            // epilogue-free walk (their terms are per-row constants).
+            const bool other = p.ep.softcap > 0.0f || p.ep.has_alibi || p.ep.bias_kind != ATTN_BIAS_NONE;
+            if (!other)
+                return launch_kernel(decode_split_kernel<D, DV, NQ, false, 1, DEPTH>, grid, dim3(kThreads), lds_all,
+                                     L, p, plan, ws);
             return launch_kernel(decode_split_kernel<D, DV, NQ, true, 1, DEPTH>, grid, dim3(kThreads), lds_all, L,
                                  p, plan, ws);
+        }
         return launch_kernel(decode_split_kernel<D, DV, NQ, true, 2, DEPTH>, grid, dim3(kThreads), lds_all, L, p,
                              plan, ws);
     }
