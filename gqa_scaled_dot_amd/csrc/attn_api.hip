@@ -689,11 +689,16 @@ int make_plan(const Resolved& r, Plan* plan, const AppendRows* app = nullptr) {
         // Measured on decode shapes from 8k to 128k keys: blocks of 256 rows
         // beat chunks where a chunk is 1024 keys or more (Llama-shaped
         // 128k-key decode 175-195 -> 166-176 us), and are no better below.
+        // decode_mfma takes blocks of 512 rows: against 256, 70B-shaped
+        // (64 heads over 8) 32768 keys 47.2 -> 46.5 us, 64-wide heads over
+        // 65536 keys 49.5 -> 47.3, Qwen2-shaped (28 over 4) 131072 keys
+        // 90.3 -> 84.9; decode_split measured the same with either.
         // Automatic blocks never lengthen the longest split.
         int64_t block = g_opt_decode_block;
         if (block == 0) {
             block = -1;
-            for (int64_t b = kDecodeBlock; b >= 64 && chunk >= 4 * kDecodeBlock; b /= 2) {
+            const int64_t widest = d.mfma ? 2 * kDecodeBlock : kDecodeBlock;
+            for (int64_t b = widest; b >= 64 && chunk >= 4 * kDecodeBlock; b /= 2) {
                 if ((n + b - 1) / b <= d.main_splits * (chunk / b)) {
                     block = b;
                     break;
