@@ -511,9 +511,10 @@ int attn_mla_forward(const attn_mla_params* p, const float* q, const float* stat
  *   "decode_block"   where every query row sees every key of the range, the
  *                    splits take interleaved blocks of this many rows (a power
  *                    of two in 32..4096) instead of one chunk each; -1 = always
- *                    chunks; 0 = automatic (256-row blocks where a split has
- *                    1024 keys or more and blocks keep the longest split as
- *                    short, else chunks)
+ *                    chunks; 0 = automatic (256-row blocks, 512-row ones on
+ *                    the matrix-core decode, where a split has 1024 keys or
+ *                    more and blocks keep the longest split as short, else
+ *                    chunks)
  *   "prefill_splits" force the prefill key-range split count (0 = automatic, max 16)
  *   "prefill_variant" force the prefill kernel: 32 (32x32x2 MFMA, 32-row waves) or
  *                    16 (16x16x4 MFMA, 16-row waves); 0 = automatic
