@@ -108,7 +108,7 @@ WALK_CASES = [
 ]
 
 
-@pytest.mark.parametrize("block", [-1, 32, 64, 1024])
+@pytest.mark.parametrize("block", [-1, 32, 64, 512, 1024])
 @pytest.mark.parametrize("case", range(len(WALK_CASES)))
 def test_mfma_walks_agree(block, case, mfma):
     w = _wl(**WALK_CASES[case], seed=case)
