@@ -557,6 +557,19 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
                     for (int j = 0; j < KJ; ++j) kf[j] = kin(j) ? ld4(kwg + row * kstride + koff(j)) : zero4();
 #pragma unroll
                     for (int j = 0; j < VJ; ++j) vf[j] = ld4(vwg + row * vstride + voff(j));
+                    // Each row's relative value embedding, requested with the
+                    // key's K and V rows (requested after the row's softmax,
+                    // each was a dependent round trip: the near split then
+                    // outlasted the far ones, Llama-shaped decode with
+                    // relative keys/values 47.9 -> 46.2 us).
+                    float4 rvr[NQ][VJ];
+#pragma unroll
+                    for (int r = 0; r < NQ; ++r)
+#pragma unroll
+                        for (int j = 0; j < VJ; ++j)
+                            rvr[r][j] = rel && p.ep.rel_v
+                                            ? ld4(p.ep.rel_v + (int64_t)rel_row(p.ep, pos[r], s) * DV + 4 * ln + voff(j))
+                                            : zero4();
 #pragma unroll
                     for (int r = 0; r < NQ; ++r) {
                         float dot = 0.0f;
@@ -588,10 +601,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
 #pragma unroll
                         for (int j = 0; j < VJ; ++j) {
                             float4 vv = vf[j];
-                            if (rel && p.ep.rel_v) {
-                                const float4 rv = ld4(p.ep.rel_v + (int64_t)jr * DV + 4 * ln + voff(j));
-                                vv.x += rv.x; vv.y += rv.y; vv.z += rv.z; vv.w += rv.w;
-                            }
+                            vv.x += rvr[r][j].x; vv.y += rvr[r][j].y; vv.z += rvr[r][j].z; vv.w += rvr[r][j].w;
                             acc[r][j].x = fmaf(pw, vv.x, acc[r][j].x);
                             acc[r][j].y = fmaf(pw, vv.y, acc[r][j].y);
                             acc[r][j].z = fmaf(pw, vv.z, acc[r][j].z);
@@ -603,28 +613,26 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
         }
         bool done = near_loop;
         if constexpr (DEPTH == 1 && FAR && !EPI) {
-            // Far splits with the bucketed position bias alone: still one
-            // batch in flight per lane, but the next one is requested as
-            // soon as the current one has arrived, before it is used (the
-            // two slots in turn; the wait drains this lane's only batch in
-            // flight). Llama-shaped T5-biased decode, one box, three rounds:
-            // 45.6-45.7 -> 44.5 us. The same walk measured 0.3 us slower on
-            // the plain Llama-shaped decode and 1 us slower on far splits
-            // with relative embeddings, which keep the loop below.
-            if (!rel) {
-                for (int st = 0; st < nsteps && !done; st += 2) {
-                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-                    if (st + 1 < nsteps) load(kr[1], vr[1], br[1], st + 1);
-                    __builtin_amdgcn_sched_barrier(0);
-                    process(kr[0], vr[0], br[0], st);
-                    if (st + 1 >= nsteps) break;
-                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-                    if (st + 2 < nsteps) load(kr[0], vr[0], br[0], st + 2);
-                    __builtin_amdgcn_sched_barrier(0);
-                    process(kr[1], vr[1], br[1], st + 1);
-                }
-                done = true;
+            // Far splits of the epilogue-free relative-position instance:
+            // still one batch in flight per lane, but the next one is
+            // requested as soon as the current one has arrived, before it is
+            // used (the two slots in turn; the wait drains this lane's only
+            // batch in flight). Llama-shaped decode, one box, two or three
+            // rounds: T5 bias 45.6-45.7 -> 44.5 us, relative keys/values
+            // 46.1-46.2 -> 45.1 us. The same walk measured 0.3 us slower on
+            // the plain decode, which keeps the loop below.
+            for (int st = 0; st < nsteps && !done; st += 2) {
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                if (st + 1 < nsteps) load(kr[1], vr[1], br[1], st + 1);
+                __builtin_amdgcn_sched_barrier(0);
+                process(kr[0], vr[0], br[0], st);
+                if (st + 1 >= nsteps) break;
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                if (st + 2 < nsteps) load(kr[0], vr[0], br[0], st + 2);
+                __builtin_amdgcn_sched_barrier(0);
+                process(kr[1], vr[1], br[1], st + 1);
             }
+            done = true;
         }
         if constexpr (DEPTH == 1) {
             // One batch per lane at a time: use it, then fetch the next into
