@@ -49,7 +49,7 @@ def _check_pb(w, th, weight, bidirectional, paths, variant=0, rows=None):
         assert_close(sel, ref, f"{w.name} {path} v{variant}")
 
 
-@pytest.mark.parametrize("D, H, G", [(128, 32, 8), (64, 8, 8), (192, 16, 16), (256, 8, 4)])
+@pytest.mark.parametrize("D, H, G", [(128, 32, 8), (128, 64, 8), (64, 8, 8), (192, 16, 16), (256, 8, 4)])
 def test_position_bias_decode(D, H, G):
     w = workloads.Workload("pb decode", T=1, S=3000, heads=H, kvHeads=G, headDim=D,
                            vHeadDim=128 if D == 192 else None, posOffset=2999, seed=D)
@@ -130,7 +130,7 @@ def _check_rkv(w, m, with_v, paths, seed=21, rows=None):
         assert_close(sel, ref, f"{w.name} m={m} {path}")
 
 
-@pytest.mark.parametrize("D, H, G", [(128, 32, 8), (64, 8, 8), (192, 16, 16), (256, 8, 4)])
+@pytest.mark.parametrize("D, H, G", [(128, 32, 8), (128, 64, 8), (64, 8, 8), (192, 16, 16), (256, 8, 4)])
 @pytest.mark.parametrize("m", [0, 1, 16, 200])
 def test_relative_kv_decode(D, H, G, m):
     w = workloads.Workload("rkv decode", T=1, S=3000, heads=H, kvHeads=G, headDim=D,
@@ -138,7 +138,8 @@ def test_relative_kv_decode(D, H, G, m):
     _check_rkv(w, m, True, ("decode", "generic"))
 
 
-@pytest.mark.parametrize("kw", [dict(T=2, heads=8, kvHeads=4), dict(T=1, causal=False, posOffset=900),
+@pytest.mark.parametrize("kw", [dict(T=2, heads=8, kvHeads=4), dict(T=2, heads=16, kvHeads=4),
+                                dict(T=1, causal=False, posOffset=900),
                                 dict(T=1, softcap=20.0, alibi=True), dict(T=1, window=300, sinks=2),
                                 dict(T=4, heads=4, kvHeads=4, posOffset=500)])
 def test_relative_kv_decode_features(kw):
