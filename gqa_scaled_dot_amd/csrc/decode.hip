@@ -561,13 +561,18 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
                     // key's K and V rows (requested after the row's softmax,
                     // each was a dependent round trip: the near split then
                     // outlasted the far ones, Llama-shaped decode with
-                    // relative keys/values 47.9 -> 46.2 us).
-                    float4 rvr[NQ][VJ];
+                    // relative keys/values 47.9 -> 46.2 us). Eight-row
+                    // instances keep one shared row, which serves every row
+                    // of a one-query call (all rows at one position); with
+                    // more query rows they load per row as the row needs it.
+                    constexpr int NRV = NQ > 4 ? 1 : NQ;
+                    const bool rv_early = rel && p.ep.rel_v && (NQ <= 4 || p.T == 1);
+                    float4 rvr[NRV][VJ];
 #pragma unroll
-                    for (int r = 0; r < NQ; ++r)
+                    for (int r = 0; r < NRV; ++r)
 #pragma unroll
                         for (int j = 0; j < VJ; ++j)
-                            rvr[r][j] = rel && p.ep.rel_v
+                            rvr[r][j] = rv_early
                                             ? ld4(p.ep.rel_v + (int64_t)rel_row(p.ep, pos[r], s) * DV + 4 * ln + voff(j))
                                             : zero4();
 #pragma unroll
@@ -601,7 +606,10 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
 #pragma unroll
                         for (int j = 0; j < VJ; ++j) {
                             float4 vv = vf[j];
-                            vv.x += rvr[r][j].x; vv.y += rvr[r][j].y; vv.z += rvr[r][j].z; vv.w += rvr[r][j].w;
+                            float4 rv = rvr[NRV > 1 ? r : 0][j];
+                            if (NQ > 4 && !rv_early && rel && p.ep.rel_v)
+                                rv = ld4(p.ep.rel_v + (int64_t)jr * DV + 4 * ln + voff(j));
+                            vv.x += rv.x; vv.y += rv.y; vv.z += rv.z; vv.w += rv.w;
                             acc[r][j].x = fmaf(pw, vv.x, acc[r][j].x);
                             acc[r][j].y = fmaf(pw, vv.y, acc[r][j].y);
                             acc[r][j].z = fmaf(pw, vv.z, acc[r][j].z);
