@@ -256,8 +256,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
         pbc[r] = 0.0f;
         if (pb_far) pbc[r] = p.ep.pb_weight[(p.ep.pb_n - 1) * p.ep.pb_heads + hh[r]];
     }
-    extern __shared__ float s_qrel[];  // [NQ][nrel], then the position-bias bucket of each distance
+    // [NQ][nrel], then the position-bias bucket of each distance, then (from
+    // a 4-byte boundary) each row's weight of each bucket, [buckets][NQ].
+    extern __shared__ float s_qrel[];
     uint8_t* s_pbb = reinterpret_cast<uint8_t*>(s_qrel + NQ * nrel);
+    float* s_pbw = reinterpret_cast<float*>(s_pbb + ((p.ep.pb_dt + 3) & ~3));
     float qrel0[NQ];
 #pragma unroll
     for (int r = 0; r < NQ; ++r) qrel0[r] = 0.0f;
@@ -267,6 +270,13 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
         // (before any batch is fetched: the fetches look buckets up).
         if (pb && !(FAR && split_far)) {
             for (int d = tid; d < p.ep.pb_dt; d += kThreads) s_pbb[d] = p.ep.pb_bucket[d];
+            // The weights too: a per-key lookup is then two LDS reads, not an
+            // LDS read and a dependent memory round trip per row.
+            const int nbw = (p.ep.pb_bidir ? 2 : 1) * p.ep.pb_n * NQ;
+            for (int i = tid; i < nbw; i += kThreads) {
+                const int b = i / NQ, r = i - b * NQ;
+                s_pbw[i] = p.ep.pb_weight[b * p.ep.pb_heads + g * hpg + (r < nrows ? r % hpg : 0)];
+            }
             __syncthreads();
         }
     }
@@ -298,7 +308,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
                     if constexpr (REL) {
                         if constexpr (FAR) b += pbc[r];
                         else if (pb_far) b += pbc[r];
-                        else if (pb) b += position_bias_tab(p.ep, s_pbb, hh[r], pos[r], sc);
+                        else if (pb) b += pb_row_tab_n<NQ>(p.ep, s_pbb, s_pbw, r, pos[r], sc);
                     }
                     bf[r][u] = b;
                 }
@@ -586,7 +596,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(Problem p, De
                         float b = 0.0f;
                         if (p.ep.bias_kind == ATTN_BIAS_TS) b = p.bias[(int64_t)tt[r] * p.S + s];
                         else if (p.ep.bias_kind == ATTN_BIAS_HTS) b = p.bias[((int64_t)hh[r] * p.T + tt[r]) * p.S + s];
-                        if (pb) b += position_bias_tab(p.ep, s_pbb, hh[r], pos[r], s);
+                        if (pb) b += pb_row_tab_n<NQ>(p.ep, s_pbb, s_pbw, r, pos[r], s);
                         float xs;
                         if constexpr (EPI) xs = score_epilogue(dot, p.ep, slope[r], pos[r], s, b) * kLog2e;
                         else xs = dot + b * kLog2e;  // scaled q and embedding products; b: the position bias
@@ -909,7 +919,10 @@ hipError_t launch_split_d(const Problem& p, const DecodePlan& plan, float* ws, c
         // Causal calls with a split of near keys: the far instance (batched
         // walk for far splits, plain loop for the near one); otherwise every
         // split looks its terms up per key.
-        const uint32_t lds_all = lds + (p.ep.pb_weight ? (uint32_t)((p.ep.pb_dt + 3) & ~3) : 0u);
+        const uint32_t lds_all =
+            lds + (p.ep.pb_weight ? (uint32_t)((p.ep.pb_dt + 3) & ~3) +
+                                        (uint32_t)(sizeof(float) * NQ * (p.ep.pb_bidir ? 2 : 1) * p.ep.pb_n)
+                                  : 0u);
         if (plan.near_hi > plan.near_lo) {
             // Without softcap, ALiBi or a bias input the far splits run the
             // epilogue-free walk (their terms are per-row constants).

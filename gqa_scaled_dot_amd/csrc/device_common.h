@@ -73,6 +73,17 @@ __device__ __forceinline__ float position_bias_tab(const Epilogue& e, const uint
     return e.pb_weight[b * e.pb_heads + h];
 }
 
+// The same for row r of a KV group with the weights in LDS as well
+// (w[bucket * NQ + r]: the row's head's weight of each bucket).
+template <int NQ>
+__device__ __forceinline__ float pb_row_tab_n(const Epilogue& e, const uint8_t* tab, const float* w, int r, int pos,
+                                              int s) {
+    const int d = abs(pos - s);
+    int b = d < e.pb_dt ? (int)tab[d] : e.pb_n - 1;
+    if (e.pb_bidir && s > pos) b += e.pb_n;
+    return w[b * NQ + r];
+}
+
 // tanh without branches or library calls. Below |x| = 1/4 its Taylor
 // series through x^9 (truncation error under 1e-8 relative there); above,
 // the identity tanh|x| = (1 - e^(-2|x|)) / (1 + e^(-2|x|)) with the hardware
